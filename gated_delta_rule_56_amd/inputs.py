@@ -1,0 +1,205 @@
+"""Seeded synthetic inputs for the KDA prefill and decode workloads.
+
+This module only draws random numbers and shapes them into the input
+distributions of the workloads; it holds none of the KDA arithmetic, so the
+oracle (under ``oracle/``) and the HIP path can both consume its output.
+
+Input recipe (per token and head):
+  * q, k ~ N(0, 1)^d_k, L2-normalised over d_k in float64 with no epsilon
+    (q and k are L2-normalised in the model: "Kimi Linear" notes, section
+    "Other Components").
+  * v ~ N(0, 1)^d_v.
+  * beta = sigmoid(N(0, 1))  (the step size is a sigmoid of a projection,
+    same section).
+  * g = -softplus(N(0, 1)) * 0.1, one value per key channel; alpha = exp(g).
+  * q, k, v are then rounded to bfloat16 (round to nearest even) for the
+    bf16 workloads, or kept as float32; g and beta stay float32.
+
+Seeds: numpy PCG64 ``default_rng``.  A workload that is generated whole uses
+``default_rng([workload_id, stream])``; streamed tensors (long sequences,
+repeated decode steps) use ``default_rng([workload_id, stream, index])``.
+"""
+from __future__ import annotations
+
+import dataclasses
+from typing import Optional
+
+import numpy as np
+
+# Stream ids inside one workload seed.
+_STREAM_TOKENS = 1
+_STREAM_STATE = 2
+_STREAM_DECODE_STEP = 3
+
+
+def bf16_round(x: np.ndarray) -> np.ndarray:
+    """Round float32/float64 values to the nearest bfloat16 (ties to even).
+
+    Returns float32 values that are exactly representable in bfloat16.
+    NaN stays NaN; values past the bf16 range become +-inf, as in hardware
+    conversion.
+    """
+    x32 = np.ascontiguousarray(x, dtype=np.float32)
+    u = x32.view(np.uint32).astype(np.uint64)
+    nan = np.isnan(x32)
+    lsb = (u >> 16) & 1
+    r = ((u + 0x7FFF + lsb) >> 16) << 16
+    out = (r & 0xFFFFFFFF).astype(np.uint32).view(np.float32)
+    if nan.any():
+        out = out.copy()
+        out[nan] = np.nan
+    return out
+
+
+def bf16_bits(x: np.ndarray) -> np.ndarray:
+    """bfloat16 bit patterns (uint16) of values that are already bf16-exact."""
+    x32 = np.ascontiguousarray(x, dtype=np.float32)
+    return (x32.view(np.uint32) >> 16).astype(np.uint16)
+
+
+def _l2norm(x: np.ndarray) -> np.ndarray:
+    n = np.sqrt(np.sum(x * x, axis=-1, keepdims=True))
+    return x / n
+
+
+def _sigmoid(x: np.ndarray) -> np.ndarray:
+    return 1.0 / (1.0 + np.exp(-x))
+
+
+def _softplus(x: np.ndarray) -> np.ndarray:
+    return np.logaddexp(0.0, x)
+
+
+@dataclasses.dataclass
+class TokenInputs:
+    """Per-token inputs, token-major ``[T, H, D]`` (float32 arrays).
+
+    For ``dtype == "bf16"`` the q/k/v arrays hold bf16-exact float32 values.
+    """
+    q: np.ndarray       # [T, H, Dk]
+    k: np.ndarray       # [T, H, Dk]
+    v: np.ndarray       # [T, H, Dv]
+    g: np.ndarray       # [T, H, Dk]  log-decay, <= 0
+    beta: np.ndarray    # [T, H]
+    dtype: str          # "bf16" or "f32"
+
+    @property
+    def T(self) -> int:
+        return self.q.shape[0]
+
+    def slice(self, t0: int, t1: int) -> "TokenInputs":
+        return TokenInputs(self.q[t0:t1], self.k[t0:t1], self.v[t0:t1],
+                           self.g[t0:t1], self.beta[t0:t1], self.dtype)
+
+
+def draw_tokens(rng: np.random.Generator, T: int, H: int, Dk: int, Dv: int,
+                dtype: str = "bf16", g_scale: float = 0.1) -> TokenInputs:
+    """Draw T tokens for H heads with the recipe in the module docstring.
+
+    ``g_scale`` multiplies the softplus term (0.1 in every workload; the
+    stress tests pass other values to reach strong or weak decay).
+    """
+    if dtype not in ("bf16", "f32"):
+        raise ValueError(f"dtype must be 'bf16' or 'f32', got {dtype!r}")
+    q = _l2norm(rng.standard_normal((T, H, Dk)))
+    k = _l2norm(rng.standard_normal((T, H, Dk)))
+    v = rng.standard_normal((T, H, Dv))
+    beta = _sigmoid(rng.standard_normal((T, H)))
+    g = -_softplus(rng.standard_normal((T, H, Dk))) * g_scale
+    if dtype == "bf16":
+        q, k, v = bf16_round(q), bf16_round(k), bf16_round(v)
+    else:
+        q, k, v = (a.astype(np.float32) for a in (q, k, v))
+    return TokenInputs(q, k, v, g.astype(np.float32), beta.astype(np.float32), dtype)
+
+
+def draw_states(rng: np.random.Generator, N: int, H: int, Dk: int, Dv: int,
+                std: float = 0.1) -> np.ndarray:
+    """Initial fast-weight states ``[N, H, Dk, Dv]`` ~ N(0, std^2), float32."""
+    return (rng.standard_normal((N, H, Dk, Dv)) * std).astype(np.float32)
+
+
+# --------------------------------------------------------------------------
+# The workloads.  Ids 0..4 are fixed; their sizes are stated in each entry.
+# --------------------------------------------------------------------------
+
+@dataclasses.dataclass(frozen=True)
+class Workload:
+    wid: int
+    name: str
+    H: int
+    Dk: int
+    Dv: int
+    dtype: str
+    chunk: int
+    T: int = 0                      # tokens per sequence (fixed-length cases)
+    B: int = 1
+    num_seqs: int = 0               # varlen: number of packed sequences
+    len_range: tuple = (0, 0)       # varlen: inclusive length range
+    init_state_std: float = 0.0     # 0 => zero initial state
+    decode_N: int = 0               # decode: concurrent sequences
+    decode_steps: int = 0
+
+
+WORKLOADS = {
+    0: Workload(0, "tiny_f32_T256_H1_d64", H=1, Dk=64, Dv=64, dtype="f32",
+                chunk=16, T=256),
+    1: Workload(1, "prefill_bf16_T4096_H32_d128", H=32, Dk=128, Dv=128,
+                dtype="bf16", chunk=64, T=4096),
+    2: Workload(2, "varlen_bf16_16seq_512-8192_H32_d128", H=32, Dk=128, Dv=128,
+                dtype="bf16", chunk=64, num_seqs=16, len_range=(512, 8192),
+                init_state_std=0.1),
+    3: Workload(3, "prefill_bf16_T1048576_H32_d128", H=32, Dk=128, Dv=128,
+                dtype="bf16", chunk=64, T=1 << 20),
+    4: Workload(4, "decode_bf16_N256_H32_d128_1000steps", H=32, Dk=128, Dv=128,
+                dtype="bf16", chunk=0, decode_N=256, decode_steps=1000,
+                init_state_std=0.1),
+}
+
+
+def varlen_lengths(w: Workload) -> np.ndarray:
+    """Sequence lengths, uniform integers on the inclusive range."""
+    lo, hi = w.len_range
+    return np.random.default_rng(w.wid).integers(lo, hi + 1, w.num_seqs)
+
+
+def cu_seqlens_from_lengths(lengths) -> np.ndarray:
+    lengths = np.asarray(lengths, dtype=np.int64)
+    cu = np.zeros(len(lengths) + 1, dtype=np.int64)
+    np.cumsum(lengths, out=cu[1:])
+    return cu.astype(np.int32)
+
+
+def workload_tokens(w: Workload, T: Optional[int] = None) -> TokenInputs:
+    """All tokens of a whole-generated prefill workload (ids 0, 1, 2).
+
+    For the varlen workload the sequences are packed back to back.
+    ``T`` overrides the token count (used to draw a prefix of a workload).
+    """
+    if T is None:
+        T = int(varlen_lengths(w).sum()) if w.num_seqs else w.T
+    rng = np.random.default_rng([w.wid, _STREAM_TOKENS])
+    return draw_tokens(rng, T, w.H, w.Dk, w.Dv, w.dtype)
+
+
+def workload_states(w: Workload, N: int) -> Optional[np.ndarray]:
+    if w.init_state_std == 0.0:
+        return None
+    rng = np.random.default_rng([w.wid, _STREAM_STATE])
+    return draw_states(rng, N, w.H, w.Dk, w.Dv, w.init_state_std)
+
+
+def long_block(w: Workload, block: int, block_tokens: int = 4096) -> TokenInputs:
+    """Block ``block`` of a streamed long sequence (``block_tokens`` tokens)."""
+    rng = np.random.default_rng([w.wid, _STREAM_TOKENS, block])
+    return draw_tokens(rng, block_tokens, w.H, w.Dk, w.Dv, w.dtype)
+
+
+def decode_step_inputs(w: Workload, step: int) -> TokenInputs:
+    """One new token for each of the ``decode_N`` sequences at ``step``.
+
+    Returned with the sequence axis in the token position: arrays are
+    ``[N, H, D]`` and ``beta`` is ``[N, H]``.
+    """
+    rng = np.random.default_rng([w.wid, _STREAM_DECODE_STEP, step])
+    return draw_tokens(rng, w.decode_N, w.H, w.Dk, w.Dv, w.dtype)

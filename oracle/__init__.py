@@ -1,0 +1,245 @@
+"""KDA oracle: plain, slow, float64 CPU evaluations of what KDA computes.
+
+TEST INFRASTRUCTURE ONLY.  Only the test suite, the smoke check and the
+CPU-baseline leg of the benchmark may import or call anything here; the HIP
+library never does, and this package never imports the HIP library.
+
+Functions
+---------
+``kda_recurrent``      the definition, token by token, in C (float64).
+``kda_recurrent_np``   the same definition as a numpy loop (tiny inputs).
+``kda_unrolled``       the unrolled transition-product form, brute force;
+                       works on float64 or on exact ``fractions.Fraction``.
+``kda_chunked``        the chunkwise WY / UT-transform algorithm in float64.
+
+Sources (pages this package follows):
+  * Recurrence: "Kimi Linear" notes (docsaid.org), section "KDA: Splitting
+    the Decay Across Channels"; greeksharifa.github.io summary, section 3
+    "Kimi Delta Attention" (decay applied before the delta-rule correction,
+    output o_t = S_t^T q_t).
+  * Unrolled form: zeroshot.it.com deep-dive, section 3.3 "The Learned
+    Position" (printed without beta_i and without the initial-state term;
+    the complete form used here is derived from the recurrence).
+  * Chunkwise algorithm: greeksharifa.github.io summary, section 3.1
+    "Hardware-Efficient Chunkwise Algorithm" and Appendix B/C notes (WY
+    representation, UT transform by forward substitution, output = state
+    term + causally masked intra-chunk term).
+
+Pins: every function here is checked in ``tests/test_oracle_pins.py`` against
+closed forms, special cases, the two-channel decay table printed on the
+docsaid.org page, exact rational arithmetic, and brute force.
+"""
+from __future__ import annotations
+
+import ctypes
+import os
+import subprocess
+from fractions import Fraction
+from typing import Optional, Sequence
+
+import numpy as np
+
+_HERE = os.path.dirname(os.path.abspath(__file__))
+_SRC = os.path.join(_HERE, "kda_oracle.c")
+_LIB = os.path.join(_HERE, "libkda_oracle.so")
+_lib = None
+
+
+def build(force: bool = True) -> str:
+    """Compile the C oracle with gcc (float64, no fast-math)."""
+    if force or not os.path.exists(_LIB):
+        tmp = _LIB + ".tmp"
+        subprocess.check_call(["gcc", "-O2", "-fopenmp", "-fPIC", "-shared",
+                               "-std=c99", _SRC, "-o", tmp, "-lm"])
+        os.replace(tmp, _LIB)
+    return _LIB
+
+
+def _load():
+    global _lib
+    if _lib is None:
+        if not os.path.exists(_LIB):
+            build()
+        lib = ctypes.CDLL(_LIB)
+        dp = ctypes.POINTER(ctypes.c_double)
+        lib.kda_oracle_prefill.argtypes = [dp, dp, dp, dp, dp, dp, dp, dp,
+                                           ctypes.POINTER(ctypes.c_int64),
+                                           ctypes.c_int, ctypes.c_int,
+                                           ctypes.c_int, ctypes.c_int,
+                                           ctypes.c_int]
+        lib.kda_oracle_prefill.restype = ctypes.c_int
+        lib.kda_oracle_threads.restype = ctypes.c_int
+        _lib = lib
+    return _lib
+
+
+def threads() -> int:
+    return _load().kda_oracle_threads()
+
+
+def _dptr(a: Optional[np.ndarray]):
+    if a is None:
+        return None
+    return a.ctypes.data_as(ctypes.POINTER(ctypes.c_double))
+
+
+def kda_recurrent(q, k, v, g, beta, initial_state=None, cu_seqlens=None,
+                  nthreads: int = 0):
+    """Token-by-token KDA in float64 (C).
+
+    q, k, g: [T, H, dk]; v: [T, H, dv]; beta: [T, H] (any float dtype; the
+    values are upcast exactly to float64).  ``cu_seqlens`` [N+1] packs N
+    sequences; None means one sequence of length T.  ``initial_state``
+    [N, H, dk, dv] or None (zeros).  Returns (o [T, H, dv], final [N, H, dk, dv]),
+    both float64.
+    """
+    q, k, v, g, beta = (np.ascontiguousarray(a, dtype=np.float64)
+                        for a in (q, k, v, g, beta))
+    T, H, dk = q.shape
+    dv = v.shape[2]
+    if cu_seqlens is None:
+        cu = np.array([0, T], dtype=np.int64)
+    else:
+        cu = np.ascontiguousarray(cu_seqlens, dtype=np.int64)
+    N = len(cu) - 1
+    if cu[-1] > T:
+        raise ValueError("cu_seqlens exceeds the token count")
+    s0 = None
+    if initial_state is not None:
+        s0 = np.ascontiguousarray(initial_state, dtype=np.float64)
+        if s0.shape != (N, H, dk, dv):
+            raise ValueError(f"initial_state shape {s0.shape} != {(N, H, dk, dv)}")
+    o = np.zeros((T, H, dv), dtype=np.float64)
+    fin = np.zeros((N, H, dk, dv), dtype=np.float64)
+    rc = _load().kda_oracle_prefill(
+        _dptr(q), _dptr(k), _dptr(v), _dptr(g), _dptr(beta), _dptr(s0),
+        _dptr(fin), _dptr(o), cu.ctypes.data_as(ctypes.POINTER(ctypes.c_int64)),
+        N, H, dk, dv, int(nthreads))
+    if rc != 0:
+        raise ValueError("kda_oracle_prefill rejected its arguments")
+    return o, fin
+
+
+def kda_recurrent_np(q, k, v, g, beta, S0=None):
+    """The same definition as ``kda_recurrent`` for ONE head, numpy loop.
+
+    q, k, g: [T, dk]; v: [T, dv]; beta: [T]; S0: [dk, dv] or None.
+    Returns (o [T, dv], S_T [dk, dv]).
+    """
+    q, k, v, g, beta = (np.asarray(a, dtype=np.float64) for a in (q, k, v, g, beta))
+    T, dk = q.shape
+    dv = v.shape[1]
+    S = np.zeros((dk, dv)) if S0 is None else np.array(S0, dtype=np.float64)
+    o = np.zeros((T, dv))
+    for t in range(T):
+        S = np.exp(g[t])[:, None] * S              # Diag(alpha_t) S
+        u = beta[t] * (v[t] - S.T @ k[t])          # pseudo-value
+        S = S + np.outer(k[t], u)                  # delta correction + write
+        o[t] = S.T @ q[t]                          # read after the update
+    return o, S
+
+
+def kda_unrolled(q, k, v, alpha, beta, S0):
+    """Brute-force unrolled KDA for ONE head (tiny inputs).
+
+    With transition A_j = (I - beta_j k_j k_j^T) Diag(alpha_j) and
+    Phi(t, i) = A_t A_{t-1} ... A_{i+1} (Phi(t, t) = I):
+
+        o_t = (Phi(t, 0) S0)^T q_t + sum_{i<=t} beta_i (q_t^T Phi(t, i) k_i) v_i
+        S_T = Phi(T, 0) S0 + sum_i beta_i Phi(T, i) k_i v_i^T
+
+    Every Phi is formed as an explicit d_k x d_k matrix product, so this
+    evaluates the position-dependent transition products directly rather
+    than the recurrence.  Inputs may be float64 arrays or object arrays of
+    ``fractions.Fraction`` (then the result is exact).  ``alpha`` is given
+    directly ([T, dk]), not as a log-decay.
+    """
+    q, k, v, alpha = (np.asarray(a) for a in (q, k, v, alpha))
+    beta = np.asarray(beta)
+    S0 = np.asarray(S0)
+    T, dk = q.shape
+    dv = v.shape[1]
+    exact = q.dtype == object
+    one = Fraction(1) if exact else 1.0
+    zero = Fraction(0) if exact else 0.0
+
+    def eye():
+        m = np.empty((dk, dk), dtype=object if exact else np.float64)
+        for a in range(dk):
+            for b in range(dk):
+                m[a, b] = one if a == b else zero
+        return m
+
+    A = []
+    for j in range(T):
+        kk = np.outer(k[j], k[j])
+        A.append((eye() - beta[j] * kk) @ np.diag(alpha[j]).astype(kk.dtype))
+
+    def phi(t, i):  # A_t ... A_{i+1}, 1-based t, i
+        m = eye()
+        for j in range(i + 1, t + 1):
+            m = A[j - 1] @ m
+        return m
+
+    o = np.empty((T, dv), dtype=object if exact else np.float64)
+    for t in range(1, T + 1):
+        acc = (phi(t, 0) @ S0).T @ q[t - 1]
+        for i in range(1, t + 1):
+            coef = beta[i - 1] * (q[t - 1] @ (phi(t, i) @ k[i - 1]))
+            acc = acc + coef * v[i - 1]
+        o[t - 1] = acc
+    S = phi(T, 0) @ S0
+    for i in range(1, T + 1):
+        S = S + beta[i - 1] * np.outer(phi(T, i) @ k[i - 1], v[i - 1])
+    return o, S
+
+
+def _forward_substitution_inverse(L: np.ndarray) -> np.ndarray:
+    """Inverse of a unit lower-triangular matrix, solved row by row."""
+    n = L.shape[0]
+    X = np.zeros_like(L)
+    for r in range(n):
+        X[r, r] = 1.0
+        for i in range(r):
+            # row r of L X = e_r  =>  X[r] = e_r - sum_{m<r} L[r, m] X[m]
+            X[r] -= L[r, i] * X[i]
+    return X
+
+
+def kda_chunked(q, k, v, g, beta, C: int, S0=None):
+    """Chunkwise KDA for ONE head in float64: WY representation + UT transform.
+
+    Per chunk of n <= C rows (the last one may be shorter), entering state S:
+      Gamma_r = sum_{s<=r} g_s (inclusive, per key channel);  gam_r = exp(Gamma_r)
+      A[r, i] = beta_r * sum_c k_rc k_ic exp(Gamma_rc - Gamma_ic)   for i < r
+      P[r, i] =          sum_c q_rc k_ic exp(Gamma_rc - Gamma_ic)   for i <= r
+      T       = (I + A)^{-1} Diag(beta)      (forward substitution)
+      W       = T (K * gam),  U0 = T V        (WY auxiliaries)
+      U       = U0 - W S                      (delta-rule pseudo-values)
+      O       = (Q * gam) S + P U             (state term + masked intra term)
+      S_next  = Diag(gam_n) S + (K * exp(Gamma_n - Gamma))^T U
+    The decay ratios are evaluated pairwise as exp of a difference, so no
+    reciprocal of a cumulative decay is ever formed.
+    """
+    q, k, v, g, beta = (np.asarray(a, dtype=np.float64) for a in (q, k, v, g, beta))
+    T, dk = q.shape
+    dv = v.shape[1]
+    S = np.zeros((dk, dv)) if S0 is None else np.array(S0, dtype=np.float64)
+    o = np.zeros((T, dv))
+    for c0 in range(0, T, C):
+        Q, K, V, G, B = q[c0:c0 + C], k[c0:c0 + C], v[c0:c0 + C], g[c0:c0 + C], beta[c0:c0 + C]
+        n = Q.shape[0]
+        Gam = np.cumsum(G, axis=0)                       # [n, dk]
+        E = np.exp(Gam[:, None, :] - Gam[None, :, :])    # E[r, i, c], used for i <= r
+        KK = np.einsum("rc,ic,ric->ri", K, K, E)
+        QK = np.einsum("rc,ic,ric->ri", Q, K, E)
+        A = np.tril(B[:, None] * KK, -1)
+        P = np.tril(QK, 0)
+        Tm = _forward_substitution_inverse(np.eye(n) + A) * B[None, :]
+        gam = np.exp(Gam)
+        W = Tm @ (K * gam)
+        U = Tm @ V - W @ S
+        o[c0:c0 + n] = (Q * gam) @ S + P @ U
+        Kbar = K * np.exp(Gam[-1][None, :] - Gam)
+        S = gam[-1][:, None] * S + Kbar.T @ U
+    return o, S
