@@ -1,0 +1,210 @@
+"""KDA benchmark on one MI355X: chunked prefill tokens/s and decode-step GB/s.
+
+One step = one pass of the whole hot path on synthetic resident inputs:
+  * kda_prefill on B=1, H=32, T=4096, d_k=d_v=128, bf16 q/k/v, fp32 g/beta,
+    chunk 64, fp32 output and final state (the prefill workload);
+  * kda_decode_step on 256 sequences x 32 heads, d=128, fp32 state
+    [256, 32, 128, 128] (the decode workload), one token per sequence.
+Three prefill input sets and two decode input sets rotate so the 256 MB
+Infinity Cache cannot hold a step's working set.
+
+Prints ONE JSON line.  ``value`` is prefill tokens/s; the decode rate and the
+per-call times are in ``decode`` / ``prefill``.  ``roofline`` describes the
+kernel that takes the most time per step (decided from the measured times);
+``prefill_roofline`` gives the prefill call against HBM and bf16-MFMA peaks.
+"""
+from __future__ import annotations
+
+import argparse
+import json
+import os
+import platform
+import sys
+import time
+
+import numpy as np
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+sys.path.insert(0, ROOT)
+
+HBM_PEAK_GBS = 8000.0          # MI355X HBM3E, GB/s
+BF16_PEAK_TFLOPS = 2500.0      # MI355X dense bf16 MFMA, TFLOP/s
+
+# Workload sizes (see gated_delta_rule_56_amd/inputs.py WORKLOADS[1] and [4]).
+P_T, P_H, P_D, P_C = 4096, 32, 128, 64
+D_N, D_H, D_D = 256, 32, 128
+
+
+def prefill_algorithmic_bytes(T=P_T, H=P_H, d=P_D):
+    # q, k, v bf16 + g fp32 + beta fp32 + o fp32 per token-head, + final state.
+    return T * H * (3 * 2 * d + 4 * d + 4 + 4 * d) + H * d * d * 4
+
+
+def prefill_flops(T=P_T, H=P_H, d=P_D, C=P_C):
+    # Per-head chunked-KDA FLOPs, 6Td^2 + 3TCd + TC^2 (zeroshot.it.com
+    # deep-dive, section 4; greeksharifa summary, section 6.3).
+    return H * (6 * T * d * d + 3 * T * C * d + T * C * C)
+
+
+def decode_algorithmic_bytes(N=D_N, H=D_H, d=D_D):
+    # state read + write (fp32), q/k/v bf16, g fp32, beta fp32, o fp32.
+    return N * H * (2 * d * d * 4 + 3 * 2 * d + 4 * d + 4 + 4 * d)
+
+
+def log(*a):
+    print(*a, file=sys.stderr, flush=True)
+
+
+def cpu_baseline(min_seconds=10.0, max_reps=5):
+    """The float64 oracle on the host cores, on the whole prefill workload."""
+    import oracle
+    from gated_delta_rule_56_amd import inputs as I
+    x = I.workload_tokens(I.WORKLOADS[1])
+    reps, t = 0, 0.0
+    while reps < max_reps and (t < min_seconds or reps == 0):
+        t0 = time.perf_counter()
+        oracle.kda_recurrent(x.q, x.k, x.v, x.g, x.beta)
+        t += time.perf_counter() - t0
+        reps += 1
+    return {"value": reps * P_T / t, "unit": "tokens/s", "cores": oracle.threads(),
+            "kind": "oracle",
+            "sample": f"whole prefill workload (B=1, H=32, T=4096, d=128), {reps} pass(es), "
+                      f"float64 token-by-token recurrence, {t:.1f} s",
+            "cpu": platform.processor() or platform.machine()}
+
+
+def main():
+    ap = argparse.ArgumentParser()
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=20)
+    ap.add_argument("--warmup", type=int, default=5)
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    args = ap.parse_args()
+    if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) != 1:
+        print("bench.py measures one GPU only: every configuration here fits one MI355X "
+              "and this build has no multi-GPU path (--gpus must be 1).", file=sys.stderr)
+        sys.exit(2)
+
+    import torch
+    from gated_delta_rule_56_amd import inputs as I
+    from gated_delta_rule_56_amd import kda
+
+    dev = torch.device("cuda:0")
+    torch.cuda.set_device(dev)
+    kda.load()
+
+    # ---- resident inputs ----
+    log("generating prefill inputs")
+    wp = I.WORKLOADS[1]
+    psets = []
+    for s in range(3):
+        rng = np.random.default_rng([wp.wid, 1, 1000 + s]) if s else None
+        x = I.workload_tokens(wp) if s == 0 else I.draw_tokens(rng, P_T, P_H, P_D, P_D, "bf16")
+        bf = lambda a: torch.from_numpy(a).to(torch.bfloat16).to(dev)[None]
+        f32 = lambda a: torch.from_numpy(np.ascontiguousarray(a)).to(dev)[None]
+        psets.append((bf(x.q), bf(x.k), bf(x.v), f32(x.g), f32(x.beta)))
+    o = torch.empty((1, P_T, P_H, P_D), dtype=torch.float32, device=dev)
+    fin = torch.empty((1, P_H, P_D, P_D), dtype=torch.float32, device=dev)
+    ws_bytes = kda.workspace_size(1, P_T, P_H, P_D, 1, P_C, kda.KDA_BF16)
+    ws = torch.empty(ws_bytes, dtype=torch.uint8, device=dev)
+
+    log("generating decode inputs")
+    wd = I.WORKLOADS[4]
+    state = torch.from_numpy(I.draw_states(np.random.default_rng([4, 2]), D_N, D_H, D_D, D_D)).to(dev)
+    dsets = []
+    for s in range(2):
+        x = I.decode_step_inputs(wd, s)
+        bf = lambda a: torch.from_numpy(a).to(torch.bfloat16).to(dev)
+        f32 = lambda a: torch.from_numpy(np.ascontiguousarray(a)).to(dev)
+        dsets.append((bf(x.q), bf(x.k), bf(x.v), f32(x.g), f32(x.beta)))
+    od = torch.empty((D_N, D_H, D_D), dtype=torch.float32, device=dev)
+    torch.cuda.synchronize()
+
+    def step(i, ev=None):
+        q, k, v, g, b = psets[i % 3]
+        if ev is not None:
+            ev[0].record()
+        kda.prefill(q, k, v, g, b, None, chunk_size=P_C, o=o, final_state=fin, workspace=ws)
+        if ev is not None:
+            ev[1].record()
+        q, k, v, g, b = dsets[i % 2]
+        kda.decode_step(q, k, v, g, b, state, o=od)
+        if ev is not None:
+            ev[2].record()
+
+    log("warmup")
+    for i in range(args.warmup):
+        step(i)
+    torch.cuda.synchronize()
+
+    evs = [[torch.cuda.Event(enable_timing=True) for _ in range(3)] for _ in range(args.steps)]
+    start, stop = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    torch.cuda.synchronize()
+    t_wall0 = time.perf_counter()
+    start.record()
+    for i in range(args.steps):
+        step(i, evs[i])
+    stop.record()
+    torch.cuda.synchronize()
+    t_wall = time.perf_counter() - t_wall0
+    total_ms = start.elapsed_time(stop)
+    pre_ms = np.array([e[0].elapsed_time(e[1]) for e in evs])
+    dec_ms = np.array([e[1].elapsed_time(e[2]) for e in evs])
+
+    pre_s = pre_ms.mean() / 1e3
+    dec_s = dec_ms.mean() / 1e3
+    p_bytes, p_flops = prefill_algorithmic_bytes(), prefill_flops()
+    d_bytes = decode_algorithmic_bytes()
+    prefill_tok_s = P_T / pre_s
+    dec_gbs = d_bytes / dec_s / 1e9
+
+    decode_roof = {"bound": "hbm", "achieved": round(dec_gbs, 1), "peak": HBM_PEAK_GBS,
+                   "unit": "GB/s", "frac": round(dec_gbs / HBM_PEAK_GBS, 4), "traffic": None,
+                   "kernel": "decode_step_kernel", "bytes_per_launch": d_bytes}
+    p_gbs = p_bytes / pre_s / 1e9
+    p_tfl = p_flops / pre_s / 1e12
+    prefill_roof = {"bound": "hbm", "achieved": round(p_gbs, 1), "peak": HBM_PEAK_GBS,
+                    "unit": "GB/s", "frac": round(p_gbs / HBM_PEAK_GBS, 4), "traffic": None,
+                    "kernels": "intra_chunk_kernel + inter_chunk_kernel (one kda_prefill call)",
+                    "bytes_per_call": p_bytes, "flops_per_call": p_flops,
+                    "mfma_tflops": round(p_tfl, 2),
+                    "mfma_frac_bf16": round(p_tfl / BF16_PEAK_TFLOPS, 4)}
+    roof = decode_roof if dec_s >= pre_s else prefill_roof
+
+    cpu = None
+    if not args.no_cpu_baseline:
+        log("timing the CPU oracle")
+        cpu = cpu_baseline()
+
+    line = {
+        "metric": "KDA prefill tokens/s (H=32, d=128) + decode-step HBM GB/s, 1 MI355X",
+        "value": round(prefill_tok_s, 1),
+        "unit": "tokens/s",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": round(total_ms / args.steps, 4),
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "bf16",
+        "data": "synthetic",
+        "config": {"workload": "kda_prefill B=1 H=32 T=4096 d=128 chunk=64 bf16 in / fp32 out "
+                               "+ kda_decode_step N=256 H=32 d=128 fp32 state",
+                   "prefill": {"B": 1, "H": P_H, "T": P_T, "d": P_D, "chunk": P_C},
+                   "decode": {"N": D_N, "H": D_H, "d": D_D}},
+        "prefill": {"us_per_call": round(pre_s * 1e6, 2), "tokens_per_s": round(prefill_tok_s, 1),
+                    "algorithmic_GBps": round(p_gbs, 1), "algorithmic_TFLOPs": round(p_tfl, 3)},
+        "decode": {"us_per_step": round(dec_s * 1e6, 2), "GBps": round(dec_gbs, 1),
+                   "tokens_per_s": round(D_N / dec_s, 1), "hbm_frac": round(dec_gbs / HBM_PEAK_GBS, 4)},
+        "roofline": roof,
+        "prefill_roofline": prefill_roof,
+        "decode_roofline": decode_roof,
+        "cpu_baseline": cpu,
+        "wall_s_timed_region": round(t_wall, 4),
+    }
+    print(json.dumps(line), flush=True)
+
+
+if __name__ == "__main__":
+    main()

@@ -1,0 +1,146 @@
+// C-ABI layer: argument validation, workspace sizing and dispatch.
+// Every check runs on the host before anything is enqueued.
+#include "../../include/kda.h"
+
+#include <hip/hip_runtime.h>
+
+#include "kda_launch.hpp"
+
+namespace {
+
+bool aligned(const void* p, size_t a) { return (reinterpret_cast<uintptr_t>(p) % a) == 0; }
+
+bool supported_head(int Dk, int Dv) { return Dk == Dv && (Dk == 64 || Dk == 128); }
+
+bool supported_chunk(int c) { return c == 16 || c == 32 || c == 64; }
+
+bool valid_dtype(kda_dtype d) { return d == KDA_BF16 || d == KDA_F32; }
+
+// Validates the sequence description and returns the chunk count.
+kda_status seq_layout(int B, int T, int num_seqs, const int32_t* cu_dev, const int32_t* cu_host,
+                      int chunk, int64_t* total_chunks) {
+  if (B < 1 || T < 0 || num_seqs < 1) return KDA_ERR_INVALID_ARG;
+  int64_t chunks = 0;
+  if (cu_dev == nullptr) {
+    if (cu_host != nullptr || num_seqs != B) return KDA_ERR_INVALID_ARG;
+    chunks = (int64_t)B * ((T + chunk - 1) / chunk);
+  } else {
+    if (cu_host == nullptr || B != 1) return KDA_ERR_INVALID_ARG;
+    if (cu_host[0] != 0 || cu_host[num_seqs] != T) return KDA_ERR_INVALID_ARG;
+    for (int n = 0; n < num_seqs; ++n) {
+      const int64_t len = (int64_t)cu_host[n + 1] - cu_host[n];
+      if (len < 0) return KDA_ERR_INVALID_ARG;
+      chunks += (len + chunk - 1) / chunk;
+    }
+  }
+  if ((int64_t)B * T > INT32_MAX || chunks > INT32_MAX) return KDA_ERR_INVALID_ARG;
+  *total_chunks = chunks;
+  return KDA_OK;
+}
+
+}  // namespace
+
+extern "C" {
+
+const char* kda_status_string(kda_status s) {
+  switch (s) {
+    case KDA_OK: return "KDA_OK";
+    case KDA_ERR_INVALID_ARG: return "KDA_ERR_INVALID_ARG: invalid argument";
+    case KDA_ERR_UNSUPPORTED: return "KDA_ERR_UNSUPPORTED: head size or chunk size not supported";
+    case KDA_ERR_WORKSPACE: return "KDA_ERR_WORKSPACE: workspace missing or too small";
+    case KDA_ERR_HIP: return "KDA_ERR_HIP: HIP runtime error";
+  }
+  return "KDA_ERR_UNKNOWN";
+}
+
+int kda_version(void) { return 100; }
+
+kda_status kda_prefill_workspace_size(int B, int T, int H, int Dk, int Dv, int num_seqs,
+                                      const int32_t* cu_seqlens_host, int chunk_size,
+                                      kda_dtype in_dtype, size_t* bytes) {
+  if (bytes == nullptr || H < 1 || !valid_dtype(in_dtype)) return KDA_ERR_INVALID_ARG;
+  if (!supported_head(Dk, Dv) || !supported_chunk(chunk_size)) return KDA_ERR_UNSUPPORTED;
+  int64_t chunks = 0;
+  // Any non-NULL host table stands for a device copy when sizing.
+  const int32_t* cu_dev = cu_seqlens_host;
+  kda_status st = seq_layout(B, T, num_seqs, cu_dev, cu_seqlens_host, chunk_size, &chunks);
+  if (st != KDA_OK) return st;
+  *bytes = kda::prefill_workspace_bytes(num_seqs, (int)chunks, H, Dk, chunk_size,
+                                        in_dtype == KDA_BF16);
+  return KDA_OK;
+}
+
+kda_status kda_prefill(const void* q, const void* k, const void* v, const float* g,
+                       const float* beta, void* o, const float* initial_state,
+                       float* final_state, const int32_t* cu_seqlens,
+                       const int32_t* cu_seqlens_host, int B, int T, int H, int Dk, int Dv,
+                       int num_seqs, int chunk_size, kda_dtype in_dtype, kda_dtype out_dtype,
+                       void* workspace, size_t workspace_bytes, void* stream) {
+  if (H < 1 || !valid_dtype(in_dtype) || !valid_dtype(out_dtype)) return KDA_ERR_INVALID_ARG;
+  if (!supported_head(Dk, Dv) || !supported_chunk(chunk_size)) return KDA_ERR_UNSUPPORTED;
+  const void* ptrs[] = {q, k, v, g, beta, o, initial_state, final_state, cu_seqlens};
+  for (const void* p : ptrs)
+    if (p && !aligned(p, 16)) return KDA_ERR_INVALID_ARG;
+  int64_t chunks = 0;
+  kda_status st = seq_layout(B, T, num_seqs, cu_seqlens, cu_seqlens_host, chunk_size, &chunks);
+  if (st != KDA_OK) return st;
+  // Token tensors may be empty (and then NULL) only when there are no tokens.
+  if ((int64_t)B * T > 0 && (!q || !k || !v || !g || !beta || !o)) return KDA_ERR_INVALID_ARG;
+  const size_t need = kda::prefill_workspace_bytes(num_seqs, (int)chunks, H, Dk, chunk_size,
+                                                   in_dtype == KDA_BF16);
+  if (need > 0 && (workspace == nullptr || workspace_bytes < need)) return KDA_ERR_WORKSPACE;
+  if (workspace && !aligned(workspace, 256)) return KDA_ERR_INVALID_ARG;
+
+  kda::PrefillArgs a;
+  a.q = q;
+  a.k = k;
+  a.v = v;
+  a.g = g;
+  a.beta = beta;
+  a.o = o;
+  a.initial_state = initial_state;
+  a.final_state = final_state;
+  a.cu_seqlens = cu_seqlens;
+  a.num_seqs = num_seqs;
+  a.seq_len = cu_seqlens ? 0 : T;
+  a.total_tokens = B * T;
+  a.total_chunks = (int)chunks;
+  a.H = H;
+  a.D = Dk;
+  a.chunk = chunk_size;
+  a.in_bf16 = in_dtype == KDA_BF16;
+  a.out_bf16 = out_dtype == KDA_BF16;
+  a.workspace = workspace;
+  a.stream = reinterpret_cast<hipStream_t>(stream);
+  return kda::launch_prefill(a) == hipSuccess ? KDA_OK : KDA_ERR_HIP;
+}
+
+kda_status kda_decode_step(const void* q, const void* k, const void* v, const float* g,
+                           const float* beta, float* state, void* o, int N, int H, int Dk,
+                           int Dv, kda_dtype in_dtype, kda_dtype out_dtype, void* stream) {
+  if (!q || !k || !v || !g || !beta || !state || !o) return KDA_ERR_INVALID_ARG;
+  if (N < 0 || H < 1 || !valid_dtype(in_dtype) || !valid_dtype(out_dtype))
+    return KDA_ERR_INVALID_ARG;
+  if (!supported_head(Dk, Dv)) return KDA_ERR_UNSUPPORTED;
+  const void* ptrs[] = {q, k, v, g, beta, state, o};
+  for (const void* p : ptrs)
+    if (!aligned(p, 16)) return KDA_ERR_INVALID_ARG;
+  if ((int64_t)N * H > INT32_MAX) return KDA_ERR_INVALID_ARG;
+  kda::DecodeArgs a;
+  a.q = q;
+  a.k = k;
+  a.v = v;
+  a.g = g;
+  a.beta = beta;
+  a.state = state;
+  a.o = o;
+  a.N = N;
+  a.H = H;
+  a.D = Dk;
+  a.in_bf16 = in_dtype == KDA_BF16;
+  a.out_bf16 = out_dtype == KDA_BF16;
+  a.stream = reinterpret_cast<hipStream_t>(stream);
+  return kda::launch_decode(a) == hipSuccess ? KDA_OK : KDA_ERR_HIP;
+}
+
+}  // extern "C"

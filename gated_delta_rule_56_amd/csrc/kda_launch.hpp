@@ -1,0 +1,53 @@
+// Internal launcher interface between the C-ABI layer (kda_api.cpp) and the
+// kernel translation units.  Arguments arrive validated.
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stddef.h>
+#include <stdint.h>
+
+namespace kda {
+
+struct DecodeArgs {
+  const void* q;
+  const void* k;
+  const void* v;
+  const float* g;
+  const float* beta;
+  float* state;
+  void* o;
+  int N, H, D;
+  bool in_bf16, out_bf16;
+  hipStream_t stream;
+};
+
+hipError_t launch_decode(const DecodeArgs& a);
+
+struct PrefillArgs {
+  const void* q;
+  const void* k;
+  const void* v;
+  const float* g;
+  const float* beta;
+  void* o;
+  const float* initial_state;
+  float* final_state;
+  const int32_t* cu_seqlens;  // device, or NULL => num_seqs sequences of seq_len
+  int num_seqs;
+  int seq_len;                // tokens per sequence when cu_seqlens == NULL
+  int total_tokens;
+  int total_chunks;           // sum over sequences of ceil(len / chunk)
+  int H, D, chunk;
+  bool in_bf16, out_bf16;
+  void* workspace;
+  hipStream_t stream;
+};
+
+// Bytes of intra-chunk operands stored per (chunk, head).
+size_t prefill_chunk_bytes(int D, int chunk, bool in_bf16);
+// Total workspace bytes (chunk table + operands), 256-byte aligned pieces.
+size_t prefill_workspace_bytes(int num_seqs, int total_chunks, int H, int D, int chunk,
+                               bool in_bf16);
+hipError_t launch_prefill(const PrefillArgs& a);
+
+}  // namespace kda

@@ -40,13 +40,13 @@ def bf16_round(x: np.ndarray) -> np.ndarray:
     conversion.
     """
     x32 = np.ascontiguousarray(x, dtype=np.float32)
-    u = x32.view(np.uint32).astype(np.uint64)
+    u = x32.view(np.uint32)
+    r = u + np.uint32(0x7FFF)          # wraps only for NaN payloads, fixed below
+    r += (u >> np.uint32(16)) & np.uint32(1)
+    r &= np.uint32(0xFFFF0000)
+    out = r.view(np.float32)
     nan = np.isnan(x32)
-    lsb = (u >> 16) & 1
-    r = ((u + 0x7FFF + lsb) >> 16) << 16
-    out = (r & 0xFFFFFFFF).astype(np.uint32).view(np.float32)
     if nan.any():
-        out = out.copy()
         out[nan] = np.nan
     return out
 
@@ -170,16 +170,34 @@ def cu_seqlens_from_lengths(lengths) -> np.ndarray:
     return cu.astype(np.int32)
 
 
-def workload_tokens(w: Workload, T: Optional[int] = None) -> TokenInputs:
+def workload_tokens(w: Workload, T: Optional[int] = None, workers: int = 8) -> TokenInputs:
     """All tokens of a whole-generated prefill workload (ids 0, 1, 2).
 
-    For the varlen workload the sequences are packed back to back.
-    ``T`` overrides the token count (used to draw a prefix of a workload).
+    Fixed-length workloads draw every token from one stream.  For the varlen
+    workload each sequence n has its own stream ``[wid, 1, n]`` (so any subset
+    can be drawn alone) and the sequences are packed back to back; ``workers``
+    threads draw them concurrently.  ``T`` overrides the token count of a
+    fixed-length workload (to draw a prefix).
     """
-    if T is None:
-        T = int(varlen_lengths(w).sum()) if w.num_seqs else w.T
-    rng = np.random.default_rng([w.wid, _STREAM_TOKENS])
-    return draw_tokens(rng, T, w.H, w.Dk, w.Dv, w.dtype)
+    if not w.num_seqs:
+        rng = np.random.default_rng([w.wid, _STREAM_TOKENS])
+        return draw_tokens(rng, w.T if T is None else T, w.H, w.Dk, w.Dv, w.dtype)
+    lens = varlen_lengths(w)
+    parts = [None] * len(lens)
+
+    def one(n):
+        rng = np.random.default_rng([w.wid, _STREAM_TOKENS, n])
+        parts[n] = draw_tokens(rng, int(lens[n]), w.H, w.Dk, w.Dv, w.dtype)
+
+    if workers > 1:
+        from concurrent.futures import ThreadPoolExecutor
+        with ThreadPoolExecutor(workers) as ex:
+            list(ex.map(one, range(len(lens))))
+    else:
+        for n in range(len(lens)):
+            one(n)
+    cat = lambda name: np.concatenate([getattr(p, name) for p in parts])
+    return TokenInputs(cat("q"), cat("k"), cat("v"), cat("g"), cat("beta"), w.dtype)
 
 
 def workload_states(w: Workload, N: int) -> Optional[np.ndarray]:

@@ -1,0 +1,182 @@
+"""Python binding of the KDA C ABI (include/kda.h).
+
+Argument marshalling only: every step of the computation runs in the HIP
+kernels of ``libkda.so``.  PyTorch provides device memory and the stream.
+The native library is required; if it is missing this module raises on first
+use instead of falling back to anything else.
+"""
+from __future__ import annotations
+
+import ctypes
+import os
+from typing import Optional, Sequence, Tuple, Union
+
+import numpy as np
+
+_HERE = os.path.dirname(os.path.abspath(__file__))
+LIB_PATH = os.path.join(_HERE, "libkda.so")
+
+KDA_BF16 = 0
+KDA_F32 = 1
+
+_lib = None
+
+
+class KDAError(RuntimeError):
+    pass
+
+
+def load() -> ctypes.CDLL:
+    """Load libkda.so (built in-tree by gated_delta_rule_56_amd.build)."""
+    global _lib
+    if _lib is not None:
+        return _lib
+    if not os.path.exists(LIB_PATH):
+        raise KDAError(f"{LIB_PATH} is missing: build it with "
+                       "`python -m gated_delta_rule_56_amd.build` first")
+    lib = ctypes.CDLL(LIB_PATH)
+    vp, i32, sz = ctypes.c_void_p, ctypes.c_int, ctypes.c_size_t
+    lib.kda_status_string.argtypes = [i32]
+    lib.kda_status_string.restype = ctypes.c_char_p
+    lib.kda_version.restype = i32
+    lib.kda_prefill_workspace_size.argtypes = [i32, i32, i32, i32, i32, i32, vp, i32, i32,
+                                               ctypes.POINTER(sz)]
+    lib.kda_prefill_workspace_size.restype = i32
+    lib.kda_prefill.argtypes = [vp, vp, vp, vp, vp, vp, vp, vp, vp, vp,
+                                i32, i32, i32, i32, i32, i32, i32, i32, i32,
+                                vp, sz, vp]
+    lib.kda_prefill.restype = i32
+    lib.kda_decode_step.argtypes = [vp, vp, vp, vp, vp, vp, vp, i32, i32, i32, i32, i32, i32, vp]
+    lib.kda_decode_step.restype = i32
+    _lib = lib
+    return lib
+
+
+def status_string(code: int) -> str:
+    return load().kda_status_string(code).decode()
+
+
+def _check(code: int, what: str):
+    if code != 0:
+        raise KDAError(f"{what}: {status_string(code)}")
+
+
+def _torch():
+    import torch
+    return torch
+
+
+def _dtype_code(dt) -> int:
+    torch = _torch()
+    if dt == torch.bfloat16:
+        return KDA_BF16
+    if dt == torch.float32:
+        return KDA_F32
+    raise KDAError(f"unsupported dtype {dt}; use torch.bfloat16 or torch.float32")
+
+
+def _ptr(t) -> Optional[int]:
+    return None if t is None else t.data_ptr()
+
+
+def _stream_ptr(device) -> int:
+    torch = _torch()
+    return torch.cuda.current_stream(device).cuda_stream
+
+
+def _host_cu(cu_seqlens, cu_seqlens_host) -> np.ndarray:
+    if cu_seqlens_host is not None:
+        return np.ascontiguousarray(np.asarray(cu_seqlens_host), dtype=np.int32)
+    return np.ascontiguousarray(cu_seqlens.detach().cpu().numpy(), dtype=np.int32)
+
+
+def workspace_size(B: int, T: int, H: int, D: int, num_seqs: int, chunk_size: int,
+                   in_dtype: int, cu_seqlens_host: Optional[np.ndarray] = None) -> int:
+    out = ctypes.c_size_t(0)
+    cu_p = None if cu_seqlens_host is None else cu_seqlens_host.ctypes.data
+    _check(load().kda_prefill_workspace_size(B, T, H, D, D, num_seqs, cu_p, chunk_size,
+                                             in_dtype, ctypes.byref(out)),
+           "kda_prefill_workspace_size")
+    return out.value
+
+
+def prefill(q, k, v, g, beta, initial_state=None, cu_seqlens=None, *,
+            cu_seqlens_host: Optional[Union[Sequence[int], np.ndarray]] = None,
+            chunk_size: int = 64, out_dtype=None, output_final_state: bool = True,
+            final_state=None, o=None, workspace=None):
+    """Chunked KDA forward (``kda_prefill``).
+
+    Shapes: q, k, g ``[B, T, H, Dk]``; v ``[B, T, H, Dv]``; beta ``[B, T, H]``.
+    With ``cu_seqlens`` (int32 device tensor ``[N+1]``), B must be 1 and the
+    N packed sequences share the T axis.  ``initial_state`` ``[N, H, Dk, Dv]``
+    float32 or None.  Returns ``(o, final_state)`` (final_state None unless
+    requested).  ``final_state`` may be passed (it may alias initial_state).
+    """
+    torch = _torch()
+    if q.dim() != 4:
+        raise KDAError("q must be [B, T, H, D]")
+    B, T, H, D = q.shape
+    Dv = v.shape[-1]
+    in_code = _dtype_code(q.dtype)
+    for name, t in (("k", k), ("v", v)):
+        if t.dtype != q.dtype:
+            raise KDAError(f"{name} must have the dtype of q")
+    if g.dtype != torch.float32 or beta.dtype != torch.float32:
+        raise KDAError("g and beta must be float32")
+    for name, t in (("q", q), ("k", k), ("v", v), ("g", g), ("beta", beta)):
+        if not t.is_contiguous():
+            raise KDAError(f"{name} must be contiguous")
+    if cu_seqlens is not None:
+        cu_h = _host_cu(cu_seqlens, cu_seqlens_host)
+        N = len(cu_h) - 1
+        if cu_seqlens.dtype != torch.int32:
+            raise KDAError("cu_seqlens must be int32")
+    else:
+        cu_h = None
+        N = B
+    out_dtype = out_dtype or torch.float32
+    out_code = _dtype_code(out_dtype)
+    if o is None:
+        o = torch.empty((B, T, H, Dv), dtype=out_dtype, device=q.device)
+    if output_final_state and final_state is None:
+        final_state = torch.empty((N, H, D, Dv), dtype=torch.float32, device=q.device)
+    if not output_final_state:
+        final_state = None
+    if initial_state is not None and (initial_state.dtype != torch.float32
+                                      or not initial_state.is_contiguous()):
+        raise KDAError("initial_state must be contiguous float32")
+    ws_bytes = workspace_size(B, T, H, D, N, chunk_size, in_code, cu_h)
+    if workspace is None or workspace.numel() < ws_bytes:
+        workspace = torch.empty(max(ws_bytes, 1), dtype=torch.uint8, device=q.device)
+    cu_hp = None if cu_h is None else cu_h.ctypes.data
+    _check(load().kda_prefill(
+        _ptr(q), _ptr(k), _ptr(v), _ptr(g), _ptr(beta), _ptr(o),
+        _ptr(initial_state), _ptr(final_state), _ptr(cu_seqlens), cu_hp,
+        B, T, H, D, Dv, N, chunk_size, in_code, out_code,
+        _ptr(workspace), workspace.numel(), _stream_ptr(q.device)), "kda_prefill")
+    return o, final_state
+
+
+def decode_step(q, k, v, g, beta, state, *, out_dtype=None, o=None):
+    """One recurrent KDA step (``kda_decode_step``); ``state`` updated in place.
+
+    Shapes: q, k, g ``[N, H, Dk]``; v ``[N, H, Dv]``; beta ``[N, H]``;
+    state ``[N, H, Dk, Dv]`` float32.  Returns o ``[N, H, Dv]``.
+    """
+    torch = _torch()
+    N, H, D = q.shape
+    Dv = v.shape[-1]
+    in_code = _dtype_code(q.dtype)
+    out_dtype = out_dtype or torch.float32
+    out_code = _dtype_code(out_dtype)
+    for name, t in (("q", q), ("k", k), ("v", v), ("g", g), ("beta", beta), ("state", state)):
+        if not t.is_contiguous():
+            raise KDAError(f"{name} must be contiguous")
+    if state.dtype != torch.float32 or g.dtype != torch.float32 or beta.dtype != torch.float32:
+        raise KDAError("state, g and beta must be float32")
+    if o is None:
+        o = torch.empty((N, H, Dv), dtype=out_dtype, device=q.device)
+    _check(load().kda_decode_step(
+        _ptr(q), _ptr(k), _ptr(v), _ptr(g), _ptr(beta), _ptr(state), _ptr(o),
+        N, H, D, Dv, in_code, out_code, _stream_ptr(q.device)), "kda_decode_step")
+    return o

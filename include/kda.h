@@ -1,0 +1,155 @@
+/*
+ * kda.h - Kimi Delta Attention (KDA) forward kernels for AMD MI355X (gfx950).
+ *
+ * KDA is the channel-wise gated delta rule.  Per head, a d_k x d_v fast-weight
+ * state evolves token by token as
+ *
+ *     S_t = (I - beta_t k_t k_t^T) Diag(alpha_t) S_{t-1} + beta_t k_t v_t^T,
+ *     o_t = S_t^T q_t,          alpha_t = exp(g_t)  (one factor per key channel)
+ *
+ * with the decay applied before the delta-rule correction and the output read
+ * from the updated state.  Sources: the "Kimi Linear" notes (docsaid.org),
+ * section "KDA: Splitting the Decay Across Channels"; the greeksharifa.github.io
+ * summary of the Kimi Linear report, section 3 "Kimi Delta Attention".  No query
+ * scale is applied (none appears on those pages); callers pre-scale q.
+ *
+ * Two entry points cover the two ways the pages say the operator runs
+ * (greeksharifa summary, section 6.3 "Complexity Analysis"): prompt processing
+ * uses the chunkwise algorithm (kda_prefill) and generation uses the recurrent
+ * single-token update (kda_decode_step).
+ *
+ * Conventions shared by every call
+ * --------------------------------
+ *  - All tensor pointers are DEVICE pointers owned by the caller.  The library
+ *    never allocates, frees or retains device memory.
+ *  - Layouts are contiguous and token-major: q, k, g are [tokens, H, Dk];
+ *    v and o are [tokens, H, Dv]; beta is [tokens, H].  States are
+ *    [N, H, Dk, Dv] float32 with Dv contiguous.
+ *  - in_dtype selects the element type of q, k, v (KDA_BF16 or KDA_F32);
+ *    g, beta and the states are always float32.  out_dtype selects o.
+ *  - g is the log-decay: finite and <= 0 (alpha in (0, 1]).  Values are not
+ *    checked; NaN/Inf propagate.  g > 0 is outside the supported domain.
+ *  - Work is enqueued asynchronously on `stream` (NULL = the default stream).
+ *    Argument errors are detected on the host, before anything is enqueued,
+ *    and are returned synchronously.  A launch failure returns KDA_ERR_HIP.
+ *  - No C++ exception crosses this interface.
+ *  - Pointers must be 16-byte aligned.
+ */
+#ifndef KDA_H_
+#define KDA_H_
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+typedef enum {
+  KDA_OK = 0,
+  KDA_ERR_INVALID_ARG = 1, /* null pointer, bad size, bad cu_seqlens, misaligned */
+  KDA_ERR_UNSUPPORTED = 2, /* head size or chunk size not built */
+  KDA_ERR_WORKSPACE = 3,   /* workspace missing or smaller than required */
+  KDA_ERR_HIP = 4          /* a HIP launch or runtime call failed */
+} kda_status;
+
+typedef enum { KDA_BF16 = 0, KDA_F32 = 1 } kda_dtype;
+
+/* Human-readable name of a status code (static string, never NULL). */
+const char* kda_status_string(kda_status s);
+
+/* Library version as MAJOR*10000 + MINOR*100 + PATCH. */
+int kda_version(void);
+
+/*
+ * Workspace bytes that kda_prefill needs for this problem.  Arguments have the
+ * same meaning as in kda_prefill.  Returns 0 and writes nothing to *bytes on
+ * an argument error (the status says which).
+ *
+ * The workspace holds the chunk table and, per (chunk, head), the intra-chunk
+ * operands that the inter-chunk pass consumes (128.5 KB per chunk and head at
+ * Dk = Dv = 128, C = 64).
+ */
+kda_status kda_prefill_workspace_size(int B, int T, int H, int Dk, int Dv,
+                                      int num_seqs,
+                                      const int32_t* cu_seqlens_host,
+                                      int chunk_size, kda_dtype in_dtype,
+                                      size_t* bytes);
+
+/*
+ * Chunked KDA forward pass (prompt processing).
+ *
+ * Computes o for every token and, optionally, the final state of every
+ * sequence, exactly as the token-by-token recurrence above, using the
+ * chunkwise algorithm of the Kimi Linear report: within each chunk of
+ * `chunk_size` tokens the work is parallel (WY representation of the rank-1
+ * updates, UT transform solved by forward substitution, causally masked
+ * intra-chunk term); between chunks the state is carried recurrently
+ * (greeksharifa summary, section 3.1 "Hardware-Efficient Chunkwise
+ * Algorithm"; zeroshot.it.com deep-dive, section 4 "Chunking and Kernels").
+ *
+ * Sequences:
+ *   - cu_seqlens == NULL: B sequences of T tokens each, tensors [B, T, H, *].
+ *     num_seqs must equal B.
+ *   - cu_seqlens != NULL (varlen packing): B must be 1; the tensors hold
+ *     T = cu_seqlens_host[num_seqs] tokens; sequence n is the token range
+ *     [cu_seqlens[n], cu_seqlens[n+1]).  Both the device copy (read by the
+ *     kernels) and an identical host copy (validated, sizes the launch) are
+ *     required.  Values must be non-decreasing from 0 and end at T.  Empty
+ *     sequences are allowed (their final state equals their initial state).
+ *   Chunks start at each sequence start and never cross sequences; the last
+ *   chunk of a sequence may be shorter than chunk_size.
+ *
+ * Arguments:
+ *   q, k          [B*T, H, Dk]  in_dtype
+ *   v             [B*T, H, Dv]  in_dtype
+ *   g             [B*T, H, Dk]  float32 log-decay (<= 0)
+ *   beta          [B*T, H]      float32
+ *   o             [B*T, H, Dv]  out_dtype (written)
+ *   initial_state [num_seqs, H, Dk, Dv] float32, or NULL for zeros
+ *   final_state   [num_seqs, H, Dk, Dv] float32, or NULL (not written);
+ *                 may alias initial_state
+ *   Dk, Dv        head sizes; supported: Dk == Dv in {64, 128}
+ *   chunk_size    16, 32 or 64
+ *   workspace     device buffer of at least kda_prefill_workspace_size bytes,
+ *                 256-byte aligned; contents need not be initialised and are
+ *                 garbage afterwards.  Must not be shared with a call that
+ *                 runs concurrently.
+ */
+kda_status kda_prefill(const void* q, const void* k, const void* v,
+                       const float* g, const float* beta, void* o,
+                       const float* initial_state, float* final_state,
+                       const int32_t* cu_seqlens, const int32_t* cu_seqlens_host,
+                       int B, int T, int H, int Dk, int Dv, int num_seqs,
+                       int chunk_size, kda_dtype in_dtype, kda_dtype out_dtype,
+                       void* workspace, size_t workspace_bytes,
+                       void* stream /* hipStream_t */);
+
+/*
+ * One recurrent KDA step for N independent sequences (generation).
+ *
+ * For every sequence n and head h, with one new token (q, k, v, g, beta):
+ *   S <- Diag(exp(g)) S;  u = beta (v - S^T k);  S <- S + k u^T;  o = S^T q
+ * (greeksharifa summary, section 3 and section 6.3: generation uses the
+ * recurrent update).  The state is read and written in place.
+ *
+ * Arguments:
+ *   q, k   [N, H, Dk]  in_dtype
+ *   v      [N, H, Dv]  in_dtype
+ *   g      [N, H, Dk]  float32 log-decay (<= 0)
+ *   beta   [N, H]      float32
+ *   state  [N, H, Dk, Dv] float32, updated in place
+ *   o      [N, H, Dv]  out_dtype (written)
+ *   Dk, Dv supported: Dk == Dv in {64, 128}
+ */
+kda_status kda_decode_step(const void* q, const void* k, const void* v,
+                           const float* g, const float* beta, float* state,
+                           void* o, int N, int H, int Dk, int Dv,
+                           kda_dtype in_dtype, kda_dtype out_dtype,
+                           void* stream /* hipStream_t */);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* KDA_H_ */

@@ -1,0 +1,113 @@
+"""The C ABI on the host: every declared symbol is exported, and argument
+validation returns the documented status codes before anything reaches a GPU
+(no call here passes validation, so nothing is launched)."""
+import ctypes
+import os
+import re
+
+import numpy as np
+import pytest
+
+from gated_delta_rule_56_amd import kda
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+HEADER = os.path.join(ROOT, "include", "kda.h")
+
+OK, INVALID, UNSUPPORTED, WORKSPACE, HIPERR = 0, 1, 2, 3, 4
+FAKE = 0x100000  # 16-byte aligned, never dereferenced (validation fails first)
+
+
+def declared_functions():
+    text = open(HEADER).read()
+    text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
+    return sorted(set(re.findall(r"\b(kda_\w+)\s*\(", text)))
+
+
+@pytest.fixture(scope="module")
+def lib():
+    if not os.path.exists(kda.LIB_PATH):
+        pytest.skip("libkda.so not built")
+    return kda.load()
+
+
+def test_exports_every_declared_symbol(lib):
+    names = declared_functions()
+    assert {"kda_prefill", "kda_decode_step", "kda_prefill_workspace_size",
+            "kda_status_string", "kda_version"} <= set(names)
+    for name in names:
+        assert hasattr(lib, name), f"{name} declared in kda.h but not exported"
+
+
+def test_status_strings(lib):
+    for code in range(5):
+        s = kda.status_string(code)
+        assert s.startswith("KDA_")
+    assert "UNKNOWN" in kda.status_string(99)
+    assert lib.kda_version() >= 100
+
+
+def _prefill(lib, **kw):
+    a = dict(q=FAKE, k=FAKE, v=FAKE, g=FAKE, beta=FAKE, o=FAKE, s0=None, s1=None,
+             cu=None, cu_host=None, B=1, T=128, H=2, Dk=128, Dv=128, N=1, C=64,
+             ind=0, outd=1, ws=FAKE, wsb=1 << 40, stream=None)
+    a.update(kw)
+    return lib.kda_prefill(a["q"], a["k"], a["v"], a["g"], a["beta"], a["o"], a["s0"], a["s1"],
+                           a["cu"], a["cu_host"], a["B"], a["T"], a["H"], a["Dk"], a["Dv"],
+                           a["N"], a["C"], a["ind"], a["outd"], a["ws"], a["wsb"], a["stream"])
+
+
+def test_prefill_validation(lib):
+    assert _prefill(lib, q=None) == INVALID
+    assert _prefill(lib, H=0) == INVALID
+    assert _prefill(lib, Dk=96, Dv=96) == UNSUPPORTED
+    assert _prefill(lib, Dk=128, Dv=64) == UNSUPPORTED
+    assert _prefill(lib, C=48) == UNSUPPORTED
+    assert _prefill(lib, ind=7) == INVALID
+    assert _prefill(lib, g=FAKE + 4) == INVALID            # misaligned
+    assert _prefill(lib, N=2) == INVALID                    # N must equal B without cu_seqlens
+    assert _prefill(lib, ws=None) == WORKSPACE
+    assert _prefill(lib, wsb=1024) == WORKSPACE
+    assert _prefill(lib, ws=FAKE + 16) == INVALID           # workspace not 256-aligned
+    assert _prefill(lib, T=-1) == INVALID
+
+
+def test_prefill_varlen_validation(lib):
+    good = np.array([0, 50, 50, 128], dtype=np.int32)
+    bad_order = np.array([0, 60, 50, 128], dtype=np.int32)
+    bad_end = np.array([0, 50, 60, 127], dtype=np.int32)
+    bad_start = np.array([4, 50, 60, 128], dtype=np.int32)
+    hp = lambda a: a.ctypes.data
+    # host copy required with a device copy, and B must be 1
+    assert _prefill(lib, cu=FAKE, cu_host=None, N=3) == INVALID
+    assert _prefill(lib, cu=FAKE, cu_host=hp(good), N=3, B=2) == INVALID
+    assert _prefill(lib, cu=FAKE, cu_host=hp(bad_order), N=3) == INVALID
+    assert _prefill(lib, cu=FAKE, cu_host=hp(bad_end), N=3) == INVALID
+    assert _prefill(lib, cu=FAKE, cu_host=hp(bad_start), N=3) == INVALID
+    # a valid table with a too-small workspace fails only on the workspace
+    assert _prefill(lib, cu=FAKE, cu_host=hp(good), N=3, wsb=16) == WORKSPACE
+
+
+def test_workspace_size(lib):
+    # B=1, T=4096, H=32, D=128, C=64, bf16: 64 chunks x 32 heads of 131584 B
+    # (Q*gam 32 KB, W 32 KB, K-bar 32 KB, P 16 KB, T 16 KB, gam_n 512 B, each
+    # precise matrix as bf16 hi + lo) plus the 256-byte-aligned chunk table.
+    n = kda.workspace_size(1, 4096, 32, 128, 1, 64, kda.KDA_BF16)
+    assert n == 2048 * 131584 + 256 + 256
+    cu = np.array([0, 100, 100, 300], dtype=np.int32)
+    m = kda.workspace_size(1, 300, 4, 64, 3, 16, kda.KDA_F32, cu)
+    assert m > 0 and m % 256 == 0
+    with pytest.raises(kda.KDAError):
+        kda.workspace_size(1, 300, 4, 80, 3, 16, kda.KDA_F32, cu)
+
+
+def test_decode_validation(lib):
+    d = lambda **kw: lib.kda_decode_step(
+        *[kw.get(n, FAKE) for n in ("q", "k", "v", "g", "beta", "state", "o")],
+        kw.get("N", 4), kw.get("H", 2), kw.get("Dk", 64), kw.get("Dv", 64),
+        kw.get("ind", 1), kw.get("outd", 1), None)
+    assert d(state=None) == INVALID
+    assert d(N=-1) == INVALID
+    assert d(H=0) == INVALID
+    assert d(Dk=32, Dv=32) == UNSUPPORTED
+    assert d(o=FAKE + 8) == INVALID
+    assert d(outd=5) == INVALID
