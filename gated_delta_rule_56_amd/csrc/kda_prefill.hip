@@ -39,6 +39,8 @@
 #include "kda_device.hpp"
 #include "kda_launch.hpp"
 
+#include <stdlib.h>
+
 namespace kda {
 
 constexpr float kSpanLimit = 40.f;
@@ -188,46 +190,48 @@ __device__ __forceinline__ f32x4 prod16(ModeF32, f32x4 acc, const float* A, int 
 }
 
 // ---------------------------------------------------------------------------
-// LDS plan of the intra-chunk kernel
+// LDS plan of the intra-chunk kernel.  One region is reused by the phases:
+//   A  (fast path, per half of the channels): Qt', Kt', Kh' precise [C x 64]
+//   S  (strong-decay path): Gamma fp32 [C x (D+1)]
+//   B  (after the Grams): X, Y scratch, A, P (fp32)
+//   C  (W product): X, KtT precise [D x KC]
+// plus the persistent scan totals, beta and a flag.
 // ---------------------------------------------------------------------------
 template <class M, int D, int C>
 struct IntraLds {
-  typedef typename M::in_t plain_t;  // element of a plain LDS operand (bf16 or fp32)
+  typedef typename M::in_t plain_t;  // element of one half of a precise matrix
   static constexpr int KC = Layout<M, D, C>::KC;
   static constexpr int NCG = D / 8;
   static constexpr int RPT = (C * NCG / 256) > 1 ? (C * NCG / 256) : 1;
   static constexpr int NRG = C / RPT;
-  static constexpr int SD = D + kPad;    // row stride of [C x D] operands
-  static constexpr int SK = KC + kPad;   // row stride of [D x KC] operands
-  static constexpr int SF = KC + 1;      // row stride of fp32 [C x KC] matrices
-  static constexpr int SG = D + 1;       // row stride of the fp32 Gamma array (slow path)
-  static constexpr size_t kPlainMat = (size_t)C * SD * sizeof(plain_t);
-  static constexpr size_t kPreciseMat = M::kSplit ? 2 * kPlainMat : kPlainMat;
-  // Phase A, fast path (cumsum .. Grams): Qt, Kt, Kh (all precise).
-  static constexpr size_t kPhaseA = 3 * kPreciseMat;
-  // Phase B (after Grams): A, P, X (fp32 [C x SF]), Y scratch, W staging (fp32).
-  static constexpr size_t kFMat = (size_t)C * SF * 4;
+  static constexpr int DH = 64;                      // channels per Gram pass
+  static constexpr int NHALF = D / DH;
+  static constexpr int SH = DH + kPad;               // row stride of [C x DH] operands
+  static constexpr int SK = KC + kPad;               // row stride of [D x KC] operands
+  static constexpr int SF = KC + 1;                  // row stride of fp32 [C x KC] matrices
+  static constexpr int SG = D + 1;                   // row stride of the fp32 Gamma array
+  static constexpr size_t kHalfPlain = (size_t)C * SH * sizeof(plain_t);
+  static constexpr size_t kHalfPrecise = M::kSplit ? 2 * kHalfPlain : kHalfPlain;
+  static constexpr size_t kPhaseA = 3 * kHalfPrecise;
+  static constexpr size_t kPhaseS = (size_t)C * SG * 4;
+  static constexpr size_t kFMat = ((size_t)C * SF * 4 + 15) / 16 * 16;
   static constexpr size_t kYsc = 4 * 16 * 17 * 4;
-  static constexpr size_t kWst = (size_t)C * SD * 4;
-  static constexpr size_t kPhaseB = 3 * kFMat + kYsc + kWst;
-  // Strong-decay path: the fp32 Gamma array sits after A and P (it is dead by
-  // the time X is formed there).
-  static constexpr size_t kGammaBytes = (size_t)C * SG * 4;
-  static constexpr size_t kPhaseS = 2 * kFMat + kGammaBytes;
-  static constexpr size_t kMax1 = kPhaseA > kPhaseB ? kPhaseA : kPhaseB;
-  static constexpr size_t kUnion = ((kMax1 > kPhaseS ? kMax1 : kPhaseS) + 15) / 16 * 16;
-  // Persistent: KtT (precise [D x SK]), scan totals, beta, flag.
+  static constexpr size_t kPhaseB = 3 * kFMat + kYsc;
   static constexpr size_t kKtTplain = ((size_t)D * SK * sizeof(plain_t) + 15) / 16 * 16;
   static constexpr size_t kKtT = M::kSplit ? 2 * kKtTplain : kKtTplain;
+  static constexpr size_t kPhaseC = kFMat + kKtT;
+  static constexpr size_t m1 = kPhaseA > kPhaseS ? kPhaseA : kPhaseS;
+  static constexpr size_t m2 = kPhaseB > kPhaseC ? kPhaseB : kPhaseC;
+  static constexpr size_t kUnion = ((m1 > m2 ? m1 : m2) + 15) / 16 * 16;
   static constexpr size_t kScan = (size_t)NRG * D * 4;
   static constexpr size_t kBeta = (size_t)KC * 4;
-  static constexpr size_t kTotal = kUnion + kKtT + kScan + kBeta + 16;
+  static constexpr size_t kTotal = kUnion + kScan + kBeta + 16;
   // offsets
-  static constexpr size_t oQt = 0, oKt = kPreciseMat, oKh = 2 * kPreciseMat;
-  static constexpr size_t oA = 0, oP = kFMat, oX = 2 * kFMat, oY = 3 * kFMat, oWs = 3 * kFMat + kYsc;
-  static constexpr size_t oG = 2 * kFMat;
-  static constexpr size_t oKtT = kUnion, oScan = kUnion + kKtT, oBeta = oScan + kScan,
-                          oFlag = oBeta + kBeta;
+  static constexpr size_t oQt = 0, oKt = kHalfPrecise, oKh = 2 * kHalfPrecise;  // phase A
+  static constexpr size_t oG = 0;                                              // phase S
+  static constexpr size_t oX = 0, oY = kFMat, oA = kFMat + kYsc, oP = 2 * kFMat + kYsc;  // B
+  static constexpr size_t oKtT = kFMat;                                        // phase C
+  static constexpr size_t oScan = kUnion, oBeta = oScan + kScan, oFlag = oBeta + kBeta;
 };
 
 template <class M>
@@ -243,11 +247,21 @@ struct LdsPrecise<ModeBF16> {
     hi[idx] = h;
     lo[idx] = f2bf(x - bf2f(h));
   }
+  // N consecutive elements starting at idx (idx a multiple of N).
+  template <int N>
+  __device__ void storeN(int idx, const float* x) {
+    typedef __bf16 vec_t __attribute__((ext_vector_type(N)));
+    vec_t h, l;
+#pragma unroll
+    for (int e = 0; e < N; ++e) {
+      h[e] = f2bf(x[e]);
+      l[e] = f2bf(x[e] - bf2f(h[e]));
+    }
+    *reinterpret_cast<vec_t*>(hi + idx) = h;
+    *reinterpret_cast<vec_t*>(lo + idx) = l;
+  }
   __device__ ModeBF16::PFrag pfrag(int stride, int row0, int k0) const {
     return lds_pfrag(ModeBF16{}, hi, lo, stride, row0, k0);
-  }
-  __device__ ModeBF16::Frag hifrag(int stride, int row0, int k0) const {
-    return lds_frag(ModeBF16{}, hi, stride, row0, k0);
   }
 };
 template <>
@@ -255,11 +269,16 @@ struct LdsPrecise<ModeF32> {
   float* v;
   __device__ LdsPrecise(char* base, size_t) : v(reinterpret_cast<float*>(base)) {}
   __device__ void store(int idx, float x) { v[idx] = x; }
+  template <int N>
+  __device__ void storeN(int idx, const float* x) {
+    typedef float vec_t __attribute__((ext_vector_type(N)));
+    vec_t t;
+#pragma unroll
+    for (int e = 0; e < N; ++e) t[e] = x[e];
+    *reinterpret_cast<vec_t*>(v + idx) = t;
+  }
   __device__ ModeF32::PFrag pfrag(int stride, int row0, int k0) const {
     return lds_pfrag(ModeF32{}, v, nullptr, stride, row0, k0);
-  }
-  __device__ ModeF32::Frag hifrag(int stride, int row0, int k0) const {
-    return lds_frag(ModeF32{}, v, stride, row0, k0);
   }
 };
 
@@ -281,30 +300,28 @@ __device__ __forceinline__ void gst_pfrag8(ModeF32, char* frag, int lane, const 
   for (int e = 0; e < 8; ++e) v[e] = x[e];
   *reinterpret_cast<f32x8*>(frag + lane * 32) = v;
 }
-__device__ __forceinline__ void gst_frag8(ModeBF16, char* frag, int lane, const float* x) {
-  bf16x8 h;
-#pragma unroll
-  for (int e = 0; e < 8; ++e) h[e] = f2bf(x[e]);
-  *reinterpret_cast<bf16x8*>(frag + lane * 16) = h;
-}
-__device__ __forceinline__ void gst_frag8(ModeF32, char* frag, int lane, const float* x) {
-  gst_pfrag8(ModeF32{}, frag, lane, x);
-}
-// Store a run of `n` (<= 8) consecutive k values starting at element e0 of a
-// lane's slot in a precise fragment.
+// Store a run of N (1, 2 or 4) consecutive k values starting at element e0
+// (a multiple of N) of a lane's slot in a precise fragment, as one store per
+// half.
 template <int N>
 __device__ __forceinline__ void gst_pfrag_run(ModeBF16, char* frag, int lane, int e0, const float* x) {
+  typedef __bf16 vec_t __attribute__((ext_vector_type(N)));
+  vec_t h, lo;
 #pragma unroll
   for (int e = 0; e < N; ++e) {
-    const bf16 h = f2bf(x[e]);
-    reinterpret_cast<bf16*>(frag + lane * 16)[e0 + e] = h;
-    reinterpret_cast<bf16*>(frag + 1024 + lane * 16)[e0 + e] = f2bf(x[e] - bf2f(h));
+    h[e] = f2bf(x[e]);
+    lo[e] = f2bf(x[e] - bf2f(h[e]));
   }
+  *reinterpret_cast<vec_t*>(frag + lane * 16 + e0 * 2) = h;
+  *reinterpret_cast<vec_t*>(frag + 1024 + lane * 16 + e0 * 2) = lo;
 }
 template <int N>
 __device__ __forceinline__ void gst_pfrag_run(ModeF32, char* frag, int lane, int e0, const float* x) {
+  typedef float vec_t __attribute__((ext_vector_type(N)));
+  vec_t v;
 #pragma unroll
-  for (int e = 0; e < N; ++e) reinterpret_cast<float*>(frag + lane * 32)[e0 + e] = x[e];
+  for (int e = 0; e < N; ++e) v[e] = x[e];
+  *reinterpret_cast<vec_t*>(frag + lane * 32 + e0 * 4) = v;
 }
 
 struct KernelPtrs {
@@ -320,16 +337,25 @@ struct KernelPtrs {
   int H;
 };
 
+// Lower-triangular 16x16 tile t (row-major order over b <= a) -> (a, b).
+__device__ __forceinline__ void tile_ab(int t, int& a, int& b) {
+  a = 0;
+  while ((a + 1) * (a + 2) / 2 <= t) ++a;
+  b = t - a * (a + 1) / 2;
+}
+
 // ---------------------------------------------------------------------------
-// Intra-chunk kernel: grid (total_chunks, H), 256 threads.
+// Intra-chunk kernel: grid (total_chunks, H), 256 threads, two per CU.
 // ---------------------------------------------------------------------------
 template <class M, int D, int C>
-__global__ __launch_bounds__(256) void intra_chunk_kernel(KernelPtrs kp, SeqInfo si) {
+__global__ __launch_bounds__(256, 2) void intra_chunk_kernel(KernelPtrs kp, SeqInfo si) {
   typedef typename M::in_t in_t;
   typedef Layout<M, D, C> LY;
   typedef IntraLds<M, D, C> L;
   constexpr int NRT = LY::NRT, KC = LY::KC, NKC = LY::NKC, NKD = LY::NKD, NDT = LY::NDT;
-  constexpr int NCG = L::NCG, RPT = L::RPT, NRG = L::NRG, SD = L::SD, SK = L::SK, SF = L::SF;
+  constexpr int NCG = L::NCG, RPT = L::RPT, NRG = L::NRG, SH = L::SH, SK = L::SK, SF = L::SF;
+  constexpr int NTILE = NRT * (NRT + 1) / 2;
+  constexpr int TPW = (NTILE + 3) / 4;  // Gram tiles per wave
   extern __shared__ __attribute__((aligned(16))) char smem[];
 
   const int cid = blockIdx.x;
@@ -359,42 +385,36 @@ __global__ __launch_bounds__(256) void intra_chunk_kernel(KernelPtrs kp, SeqInfo
 
   const in_t* qg = reinterpret_cast<const in_t*>(kp.q);
   const in_t* kg = reinterpret_cast<const in_t*>(kp.k);
-
   float* scan = reinterpret_cast<float*>(smem + L::oScan);
   float* beta_s = reinterpret_cast<float*>(smem + L::oBeta);
   int* flag = reinterpret_cast<int*>(smem + L::oFlag);
-  LdsPrecise<M> Qt(smem + L::oQt, L::kPlainMat);
-  LdsPrecise<M> Kt(smem + L::oKt, L::kPlainMat);
-  LdsPrecise<M> Kh(smem + L::oKh, L::kPlainMat);
-  LdsPrecise<M> KtT(smem + L::oKtT, L::kKtTplain);
 
-  // ---- step 1: cumulative decay and decayed operands ----
-  for (int i = tid; i < KC; i += 256) beta_s[i] = (i < len) ? kp.beta[(size_t)(t0 + i) * H + h] : 0.f;
-  if (tid == 0) *flag = 0;
-  // Zero the padded token columns of KtT (only when KC > C).
-  if (KC > C) {
-    for (int idx = tid; idx < D * (KC - C); idx += 256) {
-      const int c = idx / (KC - C), i = C + idx % (KC - C);
-      KtT.store(c * SK + i, 0.f);
-    }
-  }
+  // ---- step 1: loads (all issued up front), cumulative decay ----
   const bool active = tid < NCG * NRG;
   const int cg = tid % NCG, rg = tid / NCG;
-  float gam[RPT][8];
+  float gam[RPT][8], qv[RPT][8], kv[RPT][8];
   if (active) {
 #pragma unroll
     for (int p = 0; p < RPT; ++p) {
       const int r = rg * RPT + p;
-      float gv[8];
       if (r < len) {
-        load8(kp.g + ((size_t)(t0 + r) * H + h) * D + 8 * cg, gv);
+        const size_t base = ((size_t)(t0 + r) * H + h) * D + 8 * cg;
+        load8(kp.g + base, gam[p]);
+        load8(qg + base, qv[p]);
+        load8(kg + base, kv[p]);
       } else {
 #pragma unroll
-        for (int e = 0; e < 8; ++e) gv[e] = 0.f;
+        for (int e = 0; e < 8; ++e) { gam[p][e] = 0.f; qv[p][e] = 0.f; kv[p][e] = 0.f; }
       }
-#pragma unroll
-      for (int e = 0; e < 8; ++e) gam[p][e] = (p ? gam[p - 1][e] : 0.f) + gv[e];
     }
+  }
+  for (int i = tid; i < KC; i += 256) beta_s[i] = (i < len) ? kp.beta[(size_t)(t0 + i) * H + h] : 0.f;
+  if (tid == 0) *flag = 0;
+  if (active) {
+#pragma unroll
+    for (int p = 1; p < RPT; ++p)
+#pragma unroll
+      for (int e = 0; e < 8; ++e) gam[p][e] += gam[p - 1][e];
 #pragma unroll
     for (int e = 0; e < 8; ++e) scan[rg * D + 8 * cg + e] = gam[RPT - 1][e];
   }
@@ -412,71 +432,52 @@ __global__ __launch_bounds__(256) void intra_chunk_kernel(KernelPtrs kp, SeqInfo
         last[e] += s;
       }
     }
-#pragma unroll
-    for (int p = 0; p < RPT; ++p)
-#pragma unroll
-      for (int e = 0; e < 8; ++e) gam[p][e] += off[e];
     bool big = false;
 #pragma unroll
     for (int e = 0; e < 8; ++e) big |= (last[e] < -kSpanLimit);
     if (big) atomicOr(flag, 1);
+#pragma unroll
+    for (int p = 0; p < RPT; ++p)
+#pragma unroll
+      for (int e = 0; e < 8; ++e) gam[p][e] += off[e];
   }
   __syncthreads();
   const bool fast = (*flag == 0);
 
+  // ---- decayed operands.  Q*gam and K*exp(Gamma_n - Gamma) go straight to
+  // their global fragments; K*gam and K/gam stay in registers.
+  float kt[RPT][8], kh[RPT][8];
   if (active) {
-    // gam_n (chunk decay) for the state update
     if (rg == 0) {
 #pragma unroll
       for (int e = 0; e < 8; ++e) reinterpret_cast<float*>(blk + LY::kGam)[8 * cg + e] = __expf(last[e]);
     }
-    float* Gs = reinterpret_cast<float*>(smem + L::oG);  // strong-decay path only
+    float kb[8][RPT];
 #pragma unroll
     for (int p = 0; p < RPT; ++p) {
       const int r = rg * RPT + p;
-      float qv[8], kv[8];
-      if (r < len) {
-        load8(qg + ((size_t)(t0 + r) * H + h) * D + 8 * cg, qv);
-        load8(kg + ((size_t)(t0 + r) * H + h) * D + 8 * cg, kv);
-      } else {
-#pragma unroll
-        for (int e = 0; e < 8; ++e) { qv[e] = 0.f; kv[e] = 0.f; }
-      }
-      float qt[8], kt[8], kb[8];
 #pragma unroll
       for (int e = 0; e < 8; ++e) {
         const float ep = __expf(gam[p][e]);
-        qt[e] = qv[e] * ep;
-        kt[e] = kv[e] * ep;
-        kb[e] = kv[e] * __expf(last[e] - gam[p][e]);
+        qv[p][e] *= ep;                                   // now Q * gam
+        kt[p][e] = kv[p][e] * ep;
+        kh[p][e] = fast ? kv[p][e] * __expf(-gam[p][e]) : 0.f;
+        kb[e][p] = kv[p][e] * __expf(last[e] - gam[p][e]);
       }
-      // LDS operands
-#pragma unroll
-      for (int e = 0; e < 8; ++e) {
-        const int c = 8 * cg + e;
-        KtT.store(c * SK + r, kt[e]);
-        if (fast) {
-          Qt.store(r * SD + c, qt[e]);
-          Kt.store(r * SD + c, kt[e]);
-          Kh.store(r * SD + c, kv[e] * __expf(-gam[p][e]));
-        } else {
-          Gs[r * L::SG + c] = gam[p][e];
-        }
-      }
-      // Global Qt fragment: row r, k = 8cg..8cg+7 -> fragment (r/16, cg/4), lane (r%16)+16(cg%4).
+      // Q*gam fragment: row r, k = 8cg..8cg+7 -> fragment (r/16, cg/4), lane (r%16)+16(cg%4).
       gst_pfrag8(M{}, blk + LY::kQt + ((size_t)(r / 16) * NKD + cg / 4) * LY::PF,
-                 (r % 16) + 16 * (cg % 4), qt);
-      // Global KbT fragments: row c = 8cg+e, k = token r.
+                 (r % 16) + 16 * (cg % 4), qv[p]);
+    }
+    // K-bar^T fragments: row c = 8cg+e, k = tokens rg*RPT .. +RPT-1 (one run).
+    const int r0 = rg * RPT;
 #pragma unroll
-      for (int e = 0; e < 8; ++e) {
-        const int c = 8 * cg + e;
-        char* fr = blk + LY::kKb + ((size_t)(c / 16) * NKC + r / 32) * LY::PF;
-        gst_pfrag_run<1>(M{}, fr, (c % 16) + 16 * ((r % 32) / 8), r % 8, &kb[e]);
-      }
+    for (int e = 0; e < 8; ++e) {
+      const int c = 8 * cg + e;
+      char* fr = blk + LY::kKb + ((size_t)(c / 16) * NKC + r0 / 32) * LY::PF;
+      gst_pfrag_run<RPT>(M{}, fr, (c % 16) + 16 * ((r0 % 32) / 8), r0 % 8, kb[e]);
     }
   }
-  // Zero the padded token range of the KbT fragments (KC > C): lanes of
-  // k-groups C/8 .. 3 in each fragment.
+  // Zero the padded token range of the K-bar^T fragments (KC > C).
   if (KC > C) {
     for (int idx = tid; idx < NDT * 64; idx += 256) {
       const int rt = idx / 64, ln = idx % 64;
@@ -486,74 +487,103 @@ __global__ __launch_bounds__(256) void intra_chunk_kernel(KernelPtrs kp, SeqInfo
       }
     }
   }
-  __syncthreads();
 
   // ---- step 2: Grams A and P ----
-  float* As = reinterpret_cast<float*>(smem + L::oA);
-  float* Ps = reinterpret_cast<float*>(smem + L::oP);
-  constexpr int NTILE = NRT * (NRT + 1) / 2;
-  f32x4 accA[(NTILE + 3) / 4], accP[(NTILE + 3) / 4];
+  f32x4 accA[TPW], accP[TPW];
+#pragma unroll
+  for (int s = 0; s < TPW; ++s) { accA[s] = f32x4{0, 0, 0, 0}; accP[s] = accA[s]; }
   if (fast) {
+    LdsPrecise<M> Qh(smem + L::oQt, L::kHalfPlain);
+    LdsPrecise<M> Kth(smem + L::oKt, L::kHalfPlain);
+    LdsPrecise<M> Khh(smem + L::oKh, L::kHalfPlain);
 #pragma unroll
-    for (int s = 0; s < (NTILE + 3) / 4; ++s) {
-      const int t = w + 4 * s;
-      accA[s] = f32x4{0, 0, 0, 0};
-      accP[s] = f32x4{0, 0, 0, 0};
-      if (t < NTILE) {
-        int a = 0;
-        while ((a + 1) * (a + 2) / 2 <= t) ++a;
-        const int b = t - a * (a + 1) / 2;
+    for (int half = 0; half < L::NHALF; ++half) {
+      if (active && (cg * 8) / L::DH == half) {
+        const int c0 = 8 * cg - half * L::DH;
 #pragma unroll
-        for (int kb = 0; kb < NKD; ++kb) {
-          const auto kh = Kh.pfrag(SD, 16 * b, 32 * kb);
-          accP[s] = mma_pp(Qt.pfrag(SD, 16 * a, 32 * kb), kh, accP[s]);
-          accA[s] = mma_pp(Kt.pfrag(SD, 16 * a, 32 * kb), kh, accA[s]);
+        for (int p = 0; p < RPT; ++p) {
+          const int r = rg * RPT + p;
+          Qh.template storeN<8>(r * SH + c0, qv[p]);
+          Kth.template storeN<8>(r * SH + c0, kt[p]);
+          Khh.template storeN<8>(r * SH + c0, kh[p]);
         }
       }
+      __syncthreads();
+#pragma unroll
+      for (int s = 0; s < TPW; ++s) {
+        const int t = w + 4 * s;
+        if (t < NTILE) {
+          int a, b;
+          tile_ab(t, a, b);
+#pragma unroll
+          for (int kb = 0; kb < L::DH / 32; ++kb) {
+            const auto khf = Khh.pfrag(SH, 16 * b, 32 * kb);
+            accP[s] = mma_pp(Qh.pfrag(SH, 16 * a, 32 * kb), khf, accP[s]);
+            accA[s] = mma_pp(Kth.pfrag(SH, 16 * a, 32 * kb), khf, accA[s]);
+          }
+        }
+      }
+      __syncthreads();  // the next half (or phase B) overwrites the operands
     }
   } else {
-    // Exact pairwise evaluation for strong decay.  Thread tid handles rows
-    // r = tid / 4 and columns i = tid % 4, +4, ... <= r.
-    const float* Gs = reinterpret_cast<const float*>(smem + L::oG);
+    // Strong decay: exact pairwise evaluation.  Gamma goes to LDS; thread tid
+    // owns row r = tid / 4 and columns i = tid % 4, +4, ... <= r.
+    float* Gs = reinterpret_cast<float*>(smem + L::oG);
+    if (active) {
 #pragma unroll
-    for (int s = 0; s < (NTILE + 3) / 4; ++s) { accA[s] = f32x4{0, 0, 0, 0}; accP[s] = accA[s]; }
-    for (int idx = tid; idx < C * KC; idx += 256) {
-      As[(idx / KC) * SF + idx % KC] = 0.f;
-      Ps[(idx / KC) * SF + idx % KC] = 0.f;
+      for (int p = 0; p < RPT; ++p)
+#pragma unroll
+        for (int e = 0; e < 8; ++e) Gs[(rg * RPT + p) * L::SG + 8 * cg + e] = gam[p][e];
     }
     __syncthreads();
-    for (int r = tid / 4; r < C; r += 64) {
-      if (r >= len) continue;
-      for (int i = tid % 4; i <= r; i += 4) {
-        float sa = 0.f, sp = 0.f;
-        for (int c = 0; c < D; ++c) {
-          const float kr = (float)kg[((size_t)(t0 + r) * H + h) * D + c];
-          const float ki = (float)kg[((size_t)(t0 + i) * H + h) * D + c];
-          const float qr = (float)qg[((size_t)(t0 + r) * H + h) * D + c];
-          const float ex = __expf(Gs[r * L::SG + c] - Gs[i * L::SG + c]);
-          sa += kr * ki * ex;
-          sp += qr * ki * ex;
+  }
+  float* As = reinterpret_cast<float*>(smem + L::oA);
+  float* Ps = reinterpret_cast<float*>(smem + L::oP);
+  float* Xs = reinterpret_cast<float*>(smem + L::oX);
+  float* Ysc = reinterpret_cast<float*>(smem + L::oY);
+  constexpr int NPAIR = (C + 3) / 4;  // columns per thread in the pairwise path
+  float pa[NPAIR], pp[NPAIR];
+  if (!fast) {
+    const float* Gs = reinterpret_cast<const float*>(smem + L::oG);
+    const int r = tid >> 2;
+#pragma unroll
+    for (int m = 0; m < NPAIR; ++m) { pa[m] = 0.f; pp[m] = 0.f; }
+    if (r < len) {
+#pragma unroll
+      for (int m = 0; m < NPAIR; ++m) {
+        const int i = (tid & 3) + 4 * m;
+        if (i <= r) {
+          float sa = 0.f, sp = 0.f;
+          for (int c = 0; c < D; ++c) {
+            const float kr = (float)kg[((size_t)(t0 + r) * H + h) * D + c];
+            const float ki = (float)kg[((size_t)(t0 + i) * H + h) * D + c];
+            const float qr = (float)qg[((size_t)(t0 + r) * H + h) * D + c];
+            const float ex = __expf(Gs[r * L::SG + c] - Gs[i * L::SG + c]);
+            sa += kr * ki * ex;
+            sp += qr * ki * ex;
+          }
+          pa[m] = sa;
+          pp[m] = sp;
         }
-        if (i < r) As[r * SF + i] = beta_s[r] * sa;
-        Ps[r * SF + i] = sp;
       }
     }
+    __syncthreads();  // Gamma reads done before A/P overwrite it
   }
-  __syncthreads();  // Grams done reading Qt/Kt/Kh; As/Ps may overwrite them
+  // ---- A (strictly lower, times beta_r), P (lower), X cleared ----
+  for (int idx = tid; idx < C * KC; idx += 256) {
+    const int r = idx / KC, i = idx % KC;
+    As[r * SF + i] = 0.f;
+    Ps[r * SF + i] = 0.f;
+    Xs[r * SF + i] = 0.f;
+  }
+  __syncthreads();
   if (fast) {
-    // zero everything, then scatter the lower tiles
-    for (int idx = tid; idx < C * KC; idx += 256) {
-      As[(idx / KC) * SF + idx % KC] = 0.f;
-      Ps[(idx / KC) * SF + idx % KC] = 0.f;
-    }
-    __syncthreads();
 #pragma unroll
-    for (int s = 0; s < (NTILE + 3) / 4; ++s) {
+    for (int s = 0; s < TPW; ++s) {
       const int t = w + 4 * s;
       if (t < NTILE) {
-        int a = 0;
-        while ((a + 1) * (a + 2) / 2 <= t) ++a;
-        const int b = t - a * (a + 1) / 2;
+        int a, b;
+        tile_ab(t, a, b);
         const int i = 16 * b + (l & 15);
 #pragma unroll
         for (int x = 0; x < 4; ++x) {
@@ -563,16 +593,24 @@ __global__ __launch_bounds__(256) void intra_chunk_kernel(KernelPtrs kp, SeqInfo
         }
       }
     }
+  } else {
+    const int r = tid >> 2;
+    if (r < C) {
+#pragma unroll
+      for (int m = 0; m < NPAIR; ++m) {
+        const int i = (tid & 3) + 4 * m;
+        if (i <= r && r < len) {
+          if (i < r) As[r * SF + i] = beta_s[r] * pa[m];
+          Ps[r * SF + i] = pp[m];
+        }
+      }
+    }
   }
   __syncthreads();
 
   // ---- step 3: X = (I + A)^{-1} by blocked forward substitution ----
-  float* Xs = reinterpret_cast<float*>(smem + L::oX);
-  float* Ysc = reinterpret_cast<float*>(smem + L::oY);
-  for (int idx = tid; idx < C * KC; idx += 256) Xs[(idx / KC) * SF + idx % KC] = 0.f;
-  __syncthreads();
   if (w == 0) {
-    // diagonal 16x16 blocks: lane = 16*blk + column
+    // diagonal 16x16 blocks: lane = 16*block + column
     const int bk = l >> 4, j = l & 15;
     if (bk < NRT) {
       float x[16];
@@ -588,15 +626,15 @@ __global__ __launch_bounds__(256) void intra_chunk_kernel(KernelPtrs kp, SeqInfo
     }
   }
   __syncthreads();
-  // off-diagonal blocks, one level (a - b) at a time
+  // off-diagonal blocks, one level (a - b) at a time:
+  //   X_ab = -X_aa * sum_{m=b}^{a-1} A_am X_mb
 #pragma unroll
   for (int lev = 1; lev < NRT; ++lev) {
     const int a = lev + w, b = w;
     const bool mine = (w < NRT - lev);
     if (mine) {
       f32x4 y = {0, 0, 0, 0};
-      for (int m = b; m < a; ++m)
-        y = prod16(M{}, y, As, SF, 16 * a, 16 * m, Xs, SF, 16 * m, 16 * b);
+      for (int m = b; m < a; ++m) y = prod16(M{}, y, As, SF, 16 * a, 16 * m, Xs, SF, 16 * m, 16 * b);
       float* Yw = Ysc + w * 16 * 17;
 #pragma unroll
       for (int x = 0; x < 4; ++x) Yw[(4 * (l >> 4) + x) * 17 + (l & 15)] = y[x];
@@ -611,11 +649,9 @@ __global__ __launch_bounds__(256) void intra_chunk_kernel(KernelPtrs kp, SeqInfo
     __syncthreads();
   }
 
-  // ---- step 4: W = T (K * gam), T = X Diag(beta); write P, T, W ----
-  // T and P fragments: (row tile rt, token block kb), lane (row, k-group).
+  // ---- step 4: T = X Diag(beta) and P fragments (fragment (rt, kb)) ----
   for (int f = w; f < NRT * NKC; f += 4) {
-    const int rt = f / NKC, kb = f % NKC;
-    const int r = 16 * rt + (l & 15), i0 = 32 * kb + 8 * (l >> 4);
+    const int r = 16 * (f / NKC) + (l & 15), i0 = 32 * (f % NKC) + 8 * (l >> 4);
     float tv[8], pv[8];
 #pragma unroll
     for (int e = 0; e < 8; ++e) {
@@ -625,7 +661,27 @@ __global__ __launch_bounds__(256) void intra_chunk_kernel(KernelPtrs kp, SeqInfo
     gst_pfrag8(M{}, blk + LY::kT + (size_t)f * LY::PF, l, tv);
     gst_pfrag8(M{}, blk + LY::kP + (size_t)f * LY::PF, l, pv);
   }
-  float* Ws = reinterpret_cast<float*>(smem + L::oWs);
+  __syncthreads();  // A and P are dead; K*gam^T may overwrite them
+  LdsPrecise<M> KtT(smem + L::oKtT, L::kKtTplain);
+  if (active) {
+#pragma unroll
+    for (int e = 0; e < 8; ++e) {
+      float run[RPT];
+#pragma unroll
+      for (int p = 0; p < RPT; ++p) run[p] = kt[p][e];
+      KtT.template storeN<RPT>((8 * cg + e) * SK + rg * RPT, run);
+    }
+  }
+  if (KC > C) {
+    for (int idx = tid; idx < D * (KC - C); idx += 256) {
+      const int c = idx / (KC - C), i = C + idx % (KC - C);
+      KtT.store(c * SK + i, 0.f);
+    }
+  }
+  __syncthreads();
+  // ---- W^T = (K*gam)^T T^T, tile (channel tile ct, token tile rt).  The
+  // accumulator lane l holds W[16rt + (l&15)][16ct + 4(l>>4) + x], which is
+  // four consecutive k values of one lane slot of the W fragment (rt, ct/2).
   for (int t = w; t < NRT * NDT; t += 4) {
     const int rt = t / NDT, ct = t % NDT;
     f32x4 acc = {0, 0, 0, 0};
@@ -636,21 +692,18 @@ __global__ __launch_bounds__(256) void intra_chunk_kernel(KernelPtrs kp, SeqInfo
       float tv[8];
 #pragma unroll
       for (int e = 0; e < 8; ++e) tv[e] = Xs[r * SF + i0 + e] * beta_s[i0 + e];
-      acc = mma_pp(make_pfrag(M{}, tv), KtT.pfrag(SK, 16 * ct, 32 * kb), acc);
+      acc = mma_pp(KtT.pfrag(SK, 16 * ct, 32 * kb), make_pfrag(M{}, tv), acc);
     }
-#pragma unroll
-    for (int x = 0; x < 4; ++x) Ws[(16 * rt + 4 * (l >> 4) + x) * SD + 16 * ct + (l & 15)] = acc[x];
-  }
-  __syncthreads();
-  for (int f = w; f < NRT * NKD; f += 4) {
-    const int rt = f / NKD, kb = f % NKD;
-    const float* src = Ws + (16 * rt + (l & 15)) * SD + 32 * kb + 8 * (l >> 4);
-    gst_pfrag8(M{}, blk + LY::kW + (size_t)f * LY::PF, l, src);
+    const int q4 = l >> 4;
+    const int lane_w = (l & 15) + 16 * (2 * (ct & 1) + (q4 >> 1));
+    float wv[4] = {acc[0], acc[1], acc[2], acc[3]};
+    gst_pfrag_run<4>(M{}, blk + LY::kW + ((size_t)rt * NKD + ct / 2) * LY::PF, lane_w,
+                     4 * (q4 & 1), wv);
   }
 }
 
 // ---------------------------------------------------------------------------
-// Inter-chunk kernel: one workgroup per (sequence, head, 16 value columns).
+// Inter-chunk kernel: one workgroup per (sequence, head, block of value columns).
 // ---------------------------------------------------------------------------
 template <class M, int D, int C>
 struct ChunkFrags {
@@ -664,12 +717,17 @@ struct ChunkFrags {
   float gam[NST][4];
 };
 
+// Operands of one chunk are loaded in two groups: the phase-1 group (W, Q*gam,
+// T) is dead after the U product and the phase-2 group (P, K-bar^T, gam_n)
+// after the state update, so each group of the next chunk can be fetched into
+// the same registers as soon as its current use ends.
 template <class M, int D, int C>
-__device__ __forceinline__ void load_chunk_frags(ChunkFrags<M, D, C>& f, const char* blk, int w) {
+__device__ __forceinline__ void load_frags_phase1(ChunkFrags<M, D, C>& f, const char* blk, int w) {
   typedef Layout<M, D, C> LY;
-  constexpr int NST = ChunkFrags<M, D, C>::NST;
-  const int l = lane_id();
-  if (w < LY::NRT) {
+  // With four row tiles every wave has one; the test is then known true at
+  // compile time and the loads stay unconditional (which lets the compiler
+  // count outstanding loads instead of draining them).
+  if (LY::NRT == 4 || w < LY::NRT) {
     const int rt = w;
 #pragma unroll
     for (int kb = 0; kb < LY::NKD; ++kb) {
@@ -677,15 +735,26 @@ __device__ __forceinline__ void load_chunk_frags(ChunkFrags<M, D, C>& f, const c
       f.Qt[kb] = ld_pfrag(M{}, blk + LY::kQt + (size_t)(rt * LY::NKD + kb) * LY::PF);
     }
 #pragma unroll
-    for (int kb = 0; kb < LY::NKC; ++kb) {
+    for (int kb = 0; kb < LY::NKC; ++kb)
       f.Tm[kb] = ld_pfrag(M{}, blk + LY::kT + (size_t)(rt * LY::NKC + kb) * LY::PF);
+  }
+}
+
+template <class M, int D, int C>
+__device__ __forceinline__ void load_frags_phase2(ChunkFrags<M, D, C>& f, const char* blk, int w) {
+  typedef Layout<M, D, C> LY;
+  constexpr int NST = ChunkFrags<M, D, C>::NST;
+  const int l = lane_id();
+  if (LY::NRT == 4 || w < LY::NRT) {
+    const int rt = w;
+#pragma unroll
+    for (int kb = 0; kb < LY::NKC; ++kb)
       f.P[kb] = ld_pfrag(M{}, blk + LY::kP + (size_t)(rt * LY::NKC + kb) * LY::PF);
-    }
   }
 #pragma unroll
   for (int s = 0; s < NST; ++s) {
     const int st = w * NST + s;
-    if (st < LY::NDT) {
+    if (LY::NDT == 4 * NST || st < LY::NDT) {
 #pragma unroll
       for (int kb = 0; kb < LY::NKC; ++kb)
         f.Kb[s][kb] = ld_pfrag(M{}, blk + LY::kKb + (size_t)(st * LY::NKC + kb) * LY::PF);
@@ -697,29 +766,34 @@ __device__ __forceinline__ void load_chunk_frags(ChunkFrags<M, D, C>& f, const c
   }
 }
 
-template <class M, int D, int C>
+template <class M, int D, int C, int NCT>
 struct InterLds {
   typedef typename M::in_t plain_t;
   static constexpr int KC = Layout<M, D, C>::KC;
   static constexpr int SD = D + kPad;
   static constexpr int SK = KC + kPad;
-  static constexpr size_t kSTplain = (size_t)16 * SD * sizeof(plain_t);
-  static constexpr size_t kUTplain = (size_t)16 * SK * sizeof(plain_t);
+  static constexpr int DVB = 16 * NCT;  // value columns per workgroup
+  static constexpr size_t kSTplain = (size_t)DVB * SD * sizeof(plain_t);
+  static constexpr size_t kUTplain = (size_t)DVB * SK * sizeof(plain_t);
   static constexpr size_t oST = 0;
   static constexpr size_t oUT = oST + (M::kSplit ? 2 : 1) * kSTplain;
   static constexpr size_t oVT = oUT + (M::kSplit ? 2 : 1) * kUTplain;
   static constexpr size_t kTotal = oVT + kUTplain;
 };
 
-template <class M, int D, int C, bool OUT_BF16>
+// NCT = number of 16-column value tiles per workgroup (16, 32 or 64 columns).
+// Every wave applies each operand fragment it loads to all NCT tiles, so a
+// wider block divides the per-chunk operand traffic among fewer workgroups.
+template <class M, int D, int C, int NCT, bool OUT_BF16>
 __global__ __launch_bounds__(256) void inter_chunk_kernel(KernelPtrs kp, SeqInfo si, int num_pairs) {
   typedef typename M::in_t in_t;
   typedef Layout<M, D, C> LY;
-  typedef InterLds<M, D, C> L;
+  typedef InterLds<M, D, C, NCT> L;
   typedef typename L::plain_t plain_t;
   constexpr int NRT = LY::NRT, KC = LY::KC, NKC = LY::NKC, NKD = LY::NKD, NDT = LY::NDT;
   constexpr int NST = ChunkFrags<M, D, C>::NST;
-  constexpr int NVB = D / 16;
+  constexpr int DVB = L::DVB;
+  constexpr int NVB = D / DVB;
   constexpr int SD = L::SD, SK = L::SK;
   __shared__ __attribute__((aligned(16))) char smem[L::kTotal];
 
@@ -734,6 +808,7 @@ __global__ __launch_bounds__(256) void inter_chunk_kernel(KernelPtrs kp, SeqInfo
   const int H = kp.H;
   const int n = pair / H, h = pair % H;
   const int tid = threadIdx.x, w = wave_id(), l = lane_id();
+  const int col0 = DVB * vb;  // first value column of this block
 
   int bos, eos;
   seq_bounds(si, n, bos, eos);
@@ -746,136 +821,215 @@ __global__ __launch_bounds__(256) void inter_chunk_kernel(KernelPtrs kp, SeqInfo
   LdsPrecise<M> UT(smem + L::oUT, L::kUTplain);
   plain_t* VT = reinterpret_cast<plain_t*>(smem + L::oVT);
 
-  // ---- state block in accumulator layout: tile st rows 16st.., cols 16vb.. ----
-  f32x4 S[NST];
+  // ---- state block in accumulator layout: tile (st, ct) holds rows
+  // 16st.., columns col0 + 16ct.. ----
+  f32x4 S[NST][NCT];
   const size_t sbase = ((size_t)n * H + h) * D * D;
 #pragma unroll
   for (int s = 0; s < NST; ++s) {
     const int st = w * NST + s;
 #pragma unroll
-    for (int x = 0; x < 4; ++x) {
-      const int c = 16 * st + 4 * (l >> 4) + x;
-      S[s][x] = (kp.s0 && st < NDT) ? kp.s0[sbase + (size_t)c * D + 16 * vb + (l & 15)] : 0.f;
-    }
+    for (int ct = 0; ct < NCT; ++ct)
+#pragma unroll
+      for (int x = 0; x < 4; ++x) {
+        const int c = 16 * st + 4 * (l >> 4) + x;
+        S[s][ct][x] = (kp.s0 && st < NDT)
+                          ? kp.s0[sbase + (size_t)c * D + col0 + 16 * ct + (l & 15)] : 0.f;
+      }
   }
   auto write_state_lds = [&]() {
 #pragma unroll
     for (int s = 0; s < NST; ++s) {
       const int st = w * NST + s;
-      if (st < NDT) {
+      if (NDT == 4 * NST || st < NDT) {
 #pragma unroll
-        for (int x = 0; x < 4; ++x) ST.store((l & 15) * SD + 16 * st + 4 * (l >> 4) + x, S[s][x]);
+        for (int ct = 0; ct < NCT; ++ct) {
+          float v4[4] = {S[s][ct][0], S[s][ct][1], S[s][ct][2], S[s][ct][3]};
+          ST.template storeN<4>((16 * ct + (l & 15)) * SD + 16 * st + 4 * (l >> 4), v4);
+        }
       }
     }
   };
   write_state_lds();
 
-  // V tile loader: thread -> (token i, 4 columns)
+  // V tile loader: thread -> (token vi, columns 16ct + vj .. +3 for every ct).
+  // The prefetch keeps the raw elements; converting them at load time would
+  // make the wave wait for every earlier load right there.
+  typedef typename M::in_t vin_t;
+  typedef vin_t vraw_t __attribute__((ext_vector_type(4)));
   const in_t* vg = reinterpret_cast<const in_t*>(kp.v);
   const int vi = tid >> 2, vj = 4 * (tid & 3);
-  float vreg[4];
-  auto load_v = [&](int ci) {
+  // The load is unconditional: rows past the chunk re-read its last row
+  // (always a valid token) and are zeroed when stored.
+  auto load_v = [&](int ci, vraw_t* raw) {
     const int t0 = bos + ci * C;
-    const int len = eos - t0;
+    const int tr = min(t0 + min(vi, C - 1), eos - 1);
+    const in_t* p = vg + ((size_t)tr * H + h) * D + col0 + vj;
 #pragma unroll
-    for (int e = 0; e < 4; ++e) vreg[e] = 0.f;
-    if (vi < C && vi < len) {
-      const in_t* p = vg + ((size_t)(t0 + vi) * H + h) * D + 16 * vb + vj;
-#pragma unroll
-      for (int e = 0; e < 4; ++e) vreg[e] = (float)p[e];
-    }
+    for (int ct = 0; ct < NCT; ++ct) raw[ct] = *reinterpret_cast<const vraw_t*>(p + 16 * ct);
   };
-  auto store_v = [&]() {
-    if (vi < KC) {
+  auto store_v = [&](const vraw_t* raw, int len) {
+    if (C >= 64 || vi < KC) {
+      const bool live = vi < C && vi < len;
 #pragma unroll
-      for (int e = 0; e < 4; ++e) VT[(vj + e) * SK + vi] = (plain_t)vreg[e];
+      for (int ct = 0; ct < NCT; ++ct)
+#pragma unroll
+        for (int e = 0; e < 4; ++e)
+          VT[(16 * ct + vj + e) * SK + vi] = live ? raw[ct][e] : (vin_t)0.f;
     }
   };
   // Zero the padded token columns of VT and UT once (KC > C).
   if (KC > C) {
-    for (int idx = tid; idx < 16 * (KC - C); idx += 256) {
+    for (int idx = tid; idx < DVB * (KC - C); idx += 256) {
       const int j = idx / (KC - C), i = C + idx % (KC - C);
       VT[j * SK + i] = (plain_t)0.f;
       UT.store(j * SK + i, 0.f);
     }
   }
 
-  ChunkFrags<M, D, C> cur, nxt;
-  if (nch > 0) {
-    load_chunk_frags<M, D, C>(cur, kp.ops + ((size_t)cid0 * H + h) * LY::kBytes, w);
-    load_v(0);
-  }
-  for (int ci = 0; ci < nch; ++ci) {
+  auto blk_of = [&](int ci) { return kp.ops + ((size_t)(cid0 + ci) * H + h) * LY::kBytes; };
+  ChunkFrags<M, D, C> f;
+  vraw_t vr[NCT];
+
+  // One chunk of the recurrence.  The operands of chunk ci are in `f` and
+  // `vr`; the next chunk's are fetched into them as each group goes dead.
+  // Past the end the fetches re-read the last chunk: they stay
+  // unconditional, since a fetch under a branch makes the compiler drain
+  // every outstanding load where the paths join.
+  auto process = [&](int ci) {
     const int t0 = bos + ci * C;
     const int len = eos - t0 < C ? eos - t0 : C;
-    store_v();
+    const int nx = min(ci + 1, nch - 1);
+    store_v(vr, len);
     __syncthreads();  // VT and ST ready
-    if (ci + 1 < nch) {
-      load_chunk_frags<M, D, C>(nxt, kp.ops + ((size_t)(cid0 + ci + 1) * H + h) * LY::kBytes, w);
-      load_v(ci + 1);
-    }
-    f32x4 qs = {0, 0, 0, 0};
-    if (w < NRT) {
-      f32x4 ws = {0, 0, 0, 0}, u = {0, 0, 0, 0};
+    f32x4 qs[NCT];
 #pragma unroll
-      for (int kb = 0; kb < NKD; ++kb) {
-        const auto sf = ST.pfrag(SD, 0, 32 * kb);
-        ws = mma_pp(cur.W[kb], sf, ws);
-        qs = mma_pp(cur.Qt[kb], sf, qs);
+    for (int ct = 0; ct < NCT; ++ct) qs[ct] = f32x4{0, 0, 0, 0};
+    if (NRT == 4 || w < NRT) {
+      f32x4 ws[NCT], u[NCT];
+#pragma unroll
+      for (int ct = 0; ct < NCT; ++ct) { ws[ct] = f32x4{0, 0, 0, 0}; u[ct] = ws[ct]; }
+#pragma unroll
+      for (int kb = 0; kb < NKD; ++kb)
+#pragma unroll
+        for (int ct = 0; ct < NCT; ++ct) {
+          const auto sf = ST.pfrag(SD, 16 * ct, 32 * kb);
+          ws[ct] = mma_pp(f.W[kb], sf, ws[ct]);
+          qs[ct] = mma_pp(f.Qt[kb], sf, qs[ct]);
+        }
+#pragma unroll
+      for (int kb = 0; kb < NKC; ++kb)
+#pragma unroll
+        for (int ct = 0; ct < NCT; ++ct)
+          u[ct] = mma_pf(f.Tm[kb], lds_frag(M{}, VT, SK, 16 * ct, 32 * kb), u[ct]);
+#pragma unroll
+      for (int ct = 0; ct < NCT; ++ct) {
+        float v4[4] = {u[ct][0] - ws[ct][0], u[ct][1] - ws[ct][1], u[ct][2] - ws[ct][2],
+                       u[ct][3] - ws[ct][3]};
+        UT.template storeN<4>((16 * ct + (l & 15)) * SK + 16 * w + 4 * (l >> 4), v4);
       }
-#pragma unroll
-      for (int kb = 0; kb < NKC; ++kb) u = mma_pf(cur.Tm[kb], lds_frag(M{}, VT, SK, 0, 32 * kb), u);
-#pragma unroll
-      for (int x = 0; x < 4; ++x) UT.store((l & 15) * SK + 16 * w + 4 * (l >> 4) + x, u[x] - ws[x]);
     }
+    load_frags_phase1<M, D, C>(f, blk_of(nx), w);
+    load_v(nx, vr);
     __syncthreads();  // UT ready; ST/VT reads done
-    if (w < NRT) {
-      f32x4 o = qs;
+    if (NRT == 4 || w < NRT) {
 #pragma unroll
-      for (int kb = 0; kb < NKC; ++kb) {
-        if (32 * kb > 16 * w + 15) break;
-        o = mma_pp(cur.P[kb], UT.pfrag(SK, 0, 32 * kb), o);
-      }
+      for (int ct = 0; ct < NCT; ++ct) {
+        f32x4 o = qs[ct];
 #pragma unroll
-      for (int x = 0; x < 4; ++x) {
-        const int r = 16 * w + 4 * (l >> 4) + x;
-        if (r < len) {
-          const size_t oi = ((size_t)(t0 + r) * H + h) * D + 16 * vb + (l & 15);
-          if constexpr (OUT_BF16)
-            reinterpret_cast<bf16*>(kp.o)[oi] = f2bf(o[x]);
-          else
-            reinterpret_cast<float*>(kp.o)[oi] = o[x];
+        for (int kb = 0; kb < NKC; ++kb) {
+          if (32 * kb > 16 * w + 15) break;
+          o = mma_pp(f.P[kb], UT.pfrag(SK, 16 * ct, 32 * kb), o);
+        }
+#pragma unroll
+        for (int x = 0; x < 4; ++x) {
+          const int r = 16 * w + 4 * (l >> 4) + x;
+          if (r < len) {
+            const size_t oi = ((size_t)(t0 + r) * H + h) * D + col0 + 16 * ct + (l & 15);
+            if constexpr (OUT_BF16)
+              reinterpret_cast<bf16*>(kp.o)[oi] = f2bf(o[x]);
+            else
+              reinterpret_cast<float*>(kp.o)[oi] = o[x];
+          }
         }
       }
     }
 #pragma unroll
     for (int s = 0; s < NST; ++s) {
       const int st = w * NST + s;
-      if (st < NDT) {
+      if (NDT == 4 * NST || st < NDT) {
 #pragma unroll
-        for (int x = 0; x < 4; ++x) S[s][x] *= cur.gam[s][x];
+        for (int ct = 0; ct < NCT; ++ct)
 #pragma unroll
-        for (int kb = 0; kb < NKC; ++kb) S[s] = mma_pp(cur.Kb[s][kb], UT.pfrag(SK, 0, 32 * kb), S[s]);
+          for (int x = 0; x < 4; ++x) S[s][ct][x] *= f.gam[s][x];
+#pragma unroll
+        for (int kb = 0; kb < NKC; ++kb)
+#pragma unroll
+          for (int ct = 0; ct < NCT; ++ct)
+            S[s][ct] = mma_pp(f.Kb[s][kb], UT.pfrag(SK, 16 * ct, 32 * kb), S[s][ct]);
       }
     }
-    // ST is read again only after the next iteration's first barrier, and
-    // every read of this chunk's ST/VT happened before the second barrier.
+    load_frags_phase2<M, D, C>(f, blk_of(nx), w);
+    // ST is read again only after the next chunk's first barrier, and every
+    // read of this chunk's ST/VT happened before the second barrier.
     write_state_lds();
-    if (ci + 1 < nch) cur = nxt;
+  };
+
+  if (nch > 0) {
+    load_frags_phase1<M, D, C>(f, blk_of(0), w);
+    load_frags_phase2<M, D, C>(f, blk_of(0), w);
+    load_v(0, vr);
   }
+  for (int ci = 0; ci < nch; ++ci) process(ci);
   if (kp.s1) {
 #pragma unroll
     for (int s = 0; s < NST; ++s) {
       const int st = w * NST + s;
       if (st < NDT) {
 #pragma unroll
-        for (int x = 0; x < 4; ++x) {
-          const int c = 16 * st + 4 * (l >> 4) + x;
-          kp.s1[sbase + (size_t)c * D + 16 * vb + (l & 15)] = S[s][x];
-        }
+        for (int ct = 0; ct < NCT; ++ct)
+#pragma unroll
+          for (int x = 0; x < 4; ++x) {
+            const int c = 16 * st + 4 * (l >> 4) + x;
+            kp.s1[sbase + (size_t)c * D + col0 + 16 * ct + (l & 15)] = S[s][ct][x];
+          }
       }
     }
   }
+}
+
+// Value-column block width of the inter-chunk pass: wide blocks cut the
+// per-chunk operand traffic (each block re-reads the chunk's operands), narrow
+// ones give more workgroups.  Heuristic: keep at least ~2 workgroups per CU
+// of work available when there are many (sequence, head) pairs.
+// KDA_PREFILL_DVB (16, 32 or 64) overrides it, for tuning.
+static int choose_nct(int pairs, int D) {
+  static int env = -1;
+  if (env < 0) {
+    const char* e = getenv("KDA_PREFILL_DVB");
+    const int v = e ? atoi(e) : 0;
+    env = (v == 16 || v == 32 || v == 64) ? v / 16 : 0;
+  }
+  int nct = env;
+  if (nct == 0) {
+    const long long units16 = (long long)pairs * (D / 16);
+    nct = units16 >= 4096 ? 4 : (units16 >= 1024 ? 2 : 1);
+  }
+  while (nct > 1 && D / (16 * nct) < 1) nct >>= 1;
+  return nct;
+}
+
+template <class M, int D, int C, int NCT>
+static void launch_inter(const PrefillArgs& a, const KernelPtrs& kp, const SeqInfo& si) {
+  const int pairs = a.num_seqs * a.H;
+  const int nvb = D / (16 * NCT);
+  const int blocks = ((pairs + 7) / 8) * 8 * nvb;
+  if (a.out_bf16)
+    hipLaunchKernelGGL((inter_chunk_kernel<M, D, C, NCT, true>), dim3(blocks), dim3(256), 0, a.stream,
+                       kp, si, pairs);
+  else
+    hipLaunchKernelGGL((inter_chunk_kernel<M, D, C, NCT, false>), dim3(blocks), dim3(256), 0, a.stream,
+                       kp, si, pairs);
 }
 
 // ---------------------------------------------------------------------------
@@ -919,15 +1073,13 @@ static hipError_t launch_prefill_t(const PrefillArgs& a) {
     hipLaunchKernelGGL((intra_chunk_kernel<M, D, C>), dim3(a.total_chunks, a.H), dim3(256), lds,
                        a.stream, kp, si);
   }
-  const int pairs = a.num_seqs * a.H;
-  const int nvb = D / 16;
-  const int blocks = ((pairs + 7) / 8) * 8 * nvb;
-  if (a.out_bf16)
-    hipLaunchKernelGGL((inter_chunk_kernel<M, D, C, true>), dim3(blocks), dim3(256), 0, a.stream, kp,
-                       si, pairs);
+  const int nct = choose_nct(a.num_seqs * a.H, D);
+  if (nct == 4)
+    launch_inter<M, D, C, 4>(a, kp, si);
+  else if (nct == 2)
+    launch_inter<M, D, C, 2>(a, kp, si);
   else
-    hipLaunchKernelGGL((inter_chunk_kernel<M, D, C, false>), dim3(blocks), dim3(256), 0, a.stream, kp,
-                       si, pairs);
+    launch_inter<M, D, C, 1>(a, kp, si);
   return hipGetLastError();
 }
 

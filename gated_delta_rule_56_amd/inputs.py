@@ -221,3 +221,22 @@ def decode_step_inputs(w: Workload, step: int) -> TokenInputs:
     """
     rng = np.random.default_rng([w.wid, _STREAM_DECODE_STEP, step])
     return draw_tokens(rng, w.decode_N, w.H, w.Dk, w.Dv, w.dtype)
+
+
+def long_blocks(w: Workload, blocks, block_tokens: int = 4096, workers: int = 16):
+    """Yield ``(block, TokenInputs)`` for the given block indices, in order,
+    drawing up to ``workers`` blocks concurrently (each block has its own
+    stream, so the result does not depend on the thread count)."""
+    from concurrent.futures import ThreadPoolExecutor
+    blocks = list(blocks)
+    with ThreadPoolExecutor(max(1, workers)) as ex:
+        futs = {}
+        ahead = max(1, workers)
+        for i, b in enumerate(blocks[:ahead]):
+            futs[i] = ex.submit(long_block, w, b, block_tokens)
+        for i, b in enumerate(blocks):
+            x = futs.pop(i).result()
+            j = i + ahead
+            if j < len(blocks):
+                futs[j] = ex.submit(long_block, w, blocks[j], block_tokens)
+            yield b, x

@@ -1,0 +1,77 @@
+"""Long-context prefill: B=1, H=32, T=1,048,576, d=128, bf16, chunk 64.
+
+The sequence is drawn in 4096-token blocks (each with its own seed).  The GPU
+runs the whole sequence in one call.  The oracle carries the state of two
+sampled heads through all 1,048,576 tokens from a zero state, and the GPU
+output is compared on the first and last 4096-token windows, plus the final
+state of those heads.
+"""
+import os
+import sys
+import time
+
+import numpy as np
+import pytest
+
+import oracle
+from gated_delta_rule_56_amd import inputs as I
+
+torch = pytest.importorskip("torch")
+pytestmark = [pytest.mark.gpu, pytest.mark.slow]
+
+HEADS = (0, 31)
+
+
+def say(msg):
+    print(f"[gpu-case] {msg}", flush=True)
+
+
+def test_prefill_workload3_long_windows():
+    if not torch.cuda.is_available():
+        pytest.skip("no GPU")
+    from gated_delta_rule_56_amd import kda
+    kda.load()
+    w = I.WORKLOADS[3]
+    T, H, D, B = w.T, w.H, w.Dk, 4096
+    nblk = T // B
+    dev = "cuda:0"
+    say(f"long prefill T={T}: allocating device inputs")
+    q = torch.empty((1, T, H, D), dtype=torch.bfloat16, device=dev)
+    k = torch.empty_like(q)
+    v = torch.empty_like(q)
+    g = torch.empty((1, T, H, D), dtype=torch.float32, device=dev)
+    beta = torch.empty((1, T, H), dtype=torch.float32, device=dev)
+    hs = list(HEADS)
+    hq = np.empty((T, len(hs), D), np.float32)
+    hk, hv, hg = np.empty_like(hq), np.empty_like(hq), np.empty_like(hq)
+    hb = np.empty((T, len(hs)), np.float32)
+    t0 = time.time()
+    for b, x in I.long_blocks(w, range(nblk), B, workers=min(16, os.cpu_count() or 1)):
+        sl = slice(b * B, (b + 1) * B)
+        q[0, sl] = torch.from_numpy(x.q).to(torch.bfloat16).to(dev)
+        k[0, sl] = torch.from_numpy(x.k).to(torch.bfloat16).to(dev)
+        v[0, sl] = torch.from_numpy(x.v).to(torch.bfloat16).to(dev)
+        g[0, sl] = torch.from_numpy(x.g).to(dev)
+        beta[0, sl] = torch.from_numpy(x.beta).to(dev)
+        hq[sl], hk[sl], hv[sl], hg[sl] = x.q[:, hs], x.k[:, hs], x.v[:, hs], x.g[:, hs]
+        hb[sl] = x.beta[:, hs]
+        if b % 64 == 0:
+            say(f"  drew block {b}/{nblk} ({time.time() - t0:.0f} s)")
+    say("running kda_prefill on 1M tokens")
+    o, fin = kda.prefill(q, k, v, g, beta, None, chunk_size=64)
+    torch.cuda.synchronize()
+    del q, k, v, g, beta
+    o_first = o[0, :B][:, hs].float().cpu().numpy()
+    o_last = o[0, T - B:][:, hs].float().cpu().numpy()
+    fin_h = fin[0, hs].cpu().numpy()
+    del o
+    say("oracle over the full sequence for the sampled heads")
+    t1 = time.time()
+    eo, ef = oracle.kda_recurrent(hq, hk, hv, hg, hb)
+    say(f"  oracle {time.time() - t1:.0f} s")
+    rel = lambda x, y: float(np.abs(x - y).max() / np.abs(y).max())
+    e_first = rel(o_first, eo[:B])
+    e_last = rel(o_last, eo[T - B:])
+    e_state = rel(fin_h, ef[0])
+    say(f"  first window {e_first:.2e}  last window {e_last:.2e}  final state {e_state:.2e}")
+    assert max(e_first, e_last, e_state) <= 2e-3
