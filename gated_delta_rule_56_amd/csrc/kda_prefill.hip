@@ -44,6 +44,7 @@
 namespace kda {
 
 constexpr float kSpanLimit = 40.f;
+constexpr int kIntraThreads = 512;
 
 // ---------------------------------------------------------------------------
 // Workspace layout
@@ -62,7 +63,8 @@ struct Layout {
   static constexpr size_t kKb = kW + (size_t)NRT * NKD * PF;         // precise [D x KC]
   static constexpr size_t kP = kKb + (size_t)NDT * NKC * PF;         // precise [C x KC]
   static constexpr size_t kT = kP + (size_t)NRT * NKC * PF;          // precise [C x KC]
-  static constexpr size_t kGam = kT + (size_t)NRT * NKC * PF;        // fp32 [D]
+  static constexpr size_t kV = kT + (size_t)NRT * NKC * PF;          // plain   [D x KC] (V^T)
+  static constexpr size_t kGam = kV + (size_t)NDT * NKC * FF;        // fp32 [D]
   static constexpr size_t kBytes = ((kGam + D * 4) + 255) / 256 * 256;
 };
 
@@ -202,7 +204,7 @@ struct IntraLds {
   typedef typename M::in_t plain_t;  // element of one half of a precise matrix
   static constexpr int KC = Layout<M, D, C>::KC;
   static constexpr int NCG = D / 8;
-  static constexpr int RPT = (C * NCG / 256) > 1 ? (C * NCG / 256) : 1;
+  static constexpr int RPT = (C * NCG / kIntraThreads) > 1 ? (C * NCG / kIntraThreads) : 1;
   static constexpr int NRG = C / RPT;
   static constexpr int DH = 64;                      // channels per Gram pass
   static constexpr int NHALF = D / DH;
@@ -220,7 +222,11 @@ struct IntraLds {
   static constexpr size_t kKtTplain = ((size_t)D * SK * sizeof(plain_t) + 15) / 16 * 16;
   static constexpr size_t kKtT = M::kSplit ? 2 * kKtTplain : kKtTplain;
   static constexpr size_t kPhaseC = kFMat + kKtT;
-  static constexpr size_t m1 = kPhaseA > kPhaseS ? kPhaseA : kPhaseS;
+  // Phase K (before A): K-bar^T (precise) and V^T (plain) staged [D x KC]
+  // for the fragment copy-out.
+  static constexpr size_t kPhaseK = kKtT + kKtTplain;
+  static constexpr size_t m0 = kPhaseA > kPhaseK ? kPhaseA : kPhaseK;
+  static constexpr size_t m1 = m0 > kPhaseS ? m0 : kPhaseS;
   static constexpr size_t m2 = kPhaseB > kPhaseC ? kPhaseB : kPhaseC;
   static constexpr size_t kUnion = ((m1 > m2 ? m1 : m2) + 15) / 16 * 16;
   static constexpr size_t kScan = (size_t)NRG * D * 4;
@@ -231,6 +237,7 @@ struct IntraLds {
   static constexpr size_t oG = 0;                                              // phase S
   static constexpr size_t oX = 0, oY = kFMat, oA = kFMat + kYsc, oP = 2 * kFMat + kYsc;  // B
   static constexpr size_t oKtT = kFMat;                                        // phase C
+  static constexpr size_t oKbS = 0, oVS = kKtT;                                // phase K
   static constexpr size_t oScan = kUnion, oBeta = oScan + kScan, oFlag = oBeta + kBeta;
 };
 
@@ -315,6 +322,23 @@ __device__ __forceinline__ void gst_pfrag_run(ModeBF16, char* frag, int lane, in
   *reinterpret_cast<vec_t*>(frag + lane * 16 + e0 * 2) = h;
   *reinterpret_cast<vec_t*>(frag + 1024 + lane * 16 + e0 * 2) = lo;
 }
+// The same for a plain fragment (one bf16 or fp32 value per element).
+template <int N>
+__device__ __forceinline__ void gst_frag_run(ModeBF16, char* frag, int lane, int e0, const bf16* x) {
+  typedef __bf16 vec_t __attribute__((ext_vector_type(N)));
+  vec_t h;
+#pragma unroll
+  for (int e = 0; e < N; ++e) h[e] = x[e];
+  *reinterpret_cast<vec_t*>(frag + lane * 16 + e0 * 2) = h;
+}
+template <int N>
+__device__ __forceinline__ void gst_frag_run(ModeF32, char* frag, int lane, int e0, const float* x) {
+  typedef float vec_t __attribute__((ext_vector_type(N)));
+  vec_t v;
+#pragma unroll
+  for (int e = 0; e < N; ++e) v[e] = x[e];
+  *reinterpret_cast<vec_t*>(frag + lane * 32 + e0 * 4) = v;
+}
 template <int N>
 __device__ __forceinline__ void gst_pfrag_run(ModeF32, char* frag, int lane, int e0, const float* x) {
   typedef float vec_t __attribute__((ext_vector_type(N)));
@@ -345,17 +369,20 @@ __device__ __forceinline__ void tile_ab(int t, int& a, int& b) {
 }
 
 // ---------------------------------------------------------------------------
-// Intra-chunk kernel: grid (total_chunks, H), 256 threads, two per CU.
+// Intra-chunk kernel: grid (total_chunks, H), 512 threads (8 waves), two
+// workgroups per CU, so four waves share each SIMD to cover each other's
+// latency.
 // ---------------------------------------------------------------------------
 template <class M, int D, int C>
-__global__ __launch_bounds__(256, 2) void intra_chunk_kernel(KernelPtrs kp, SeqInfo si) {
+__global__ __launch_bounds__(kIntraThreads, 4) void intra_chunk_kernel(KernelPtrs kp, SeqInfo si) {
   typedef typename M::in_t in_t;
   typedef Layout<M, D, C> LY;
   typedef IntraLds<M, D, C> L;
   constexpr int NRT = LY::NRT, KC = LY::KC, NKC = LY::NKC, NKD = LY::NKD, NDT = LY::NDT;
   constexpr int NCG = L::NCG, RPT = L::RPT, NRG = L::NRG, SH = L::SH, SK = L::SK, SF = L::SF;
   constexpr int NTILE = NRT * (NRT + 1) / 2;
-  constexpr int TPW = (NTILE + 3) / 4;  // Gram tiles per wave
+  constexpr int NW = kIntraThreads / 64;
+  constexpr int TPW = (NTILE + NW - 1) / NW;  // Gram tiles per wave
   extern __shared__ __attribute__((aligned(16))) char smem[];
 
   const int cid = blockIdx.x;
@@ -385,14 +412,19 @@ __global__ __launch_bounds__(256, 2) void intra_chunk_kernel(KernelPtrs kp, SeqI
 
   const in_t* qg = reinterpret_cast<const in_t*>(kp.q);
   const in_t* kg = reinterpret_cast<const in_t*>(kp.k);
+  const in_t* vg = reinterpret_cast<const in_t*>(kp.v);
   float* scan = reinterpret_cast<float*>(smem + L::oScan);
   float* beta_s = reinterpret_cast<float*>(smem + L::oBeta);
   int* flag = reinterpret_cast<int*>(smem + L::oFlag);
+  typedef typename L::plain_t plain_t;
+  LdsPrecise<M> KbS(smem + L::oKbS, L::kKtTplain);
+  plain_t* VS = reinterpret_cast<plain_t*>(smem + L::oVS);
 
   // ---- step 1: loads (all issued up front), cumulative decay ----
   const bool active = tid < NCG * NRG;
   const int cg = tid % NCG, rg = tid / NCG;
   float gam[RPT][8], qv[RPT][8], kv[RPT][8];
+  in_t vv[8][RPT];  // V^T run: value column 8cg+e, tokens rg*RPT .. +RPT-1
   if (active) {
 #pragma unroll
     for (int p = 0; p < RPT; ++p) {
@@ -402,13 +434,17 @@ __global__ __launch_bounds__(256, 2) void intra_chunk_kernel(KernelPtrs kp, SeqI
         load8(kp.g + base, gam[p]);
         load8(qg + base, qv[p]);
         load8(kg + base, kv[p]);
+        float vtmp[8];
+        load8(vg + base, vtmp);
+#pragma unroll
+        for (int e = 0; e < 8; ++e) vv[e][p] = (in_t)vtmp[e];
       } else {
 #pragma unroll
-        for (int e = 0; e < 8; ++e) { gam[p][e] = 0.f; qv[p][e] = 0.f; kv[p][e] = 0.f; }
+        for (int e = 0; e < 8; ++e) { gam[p][e] = 0.f; qv[p][e] = 0.f; kv[p][e] = 0.f; vv[e][p] = (in_t)0.f; }
       }
     }
   }
-  for (int i = tid; i < KC; i += 256) beta_s[i] = (i < len) ? kp.beta[(size_t)(t0 + i) * H + h] : 0.f;
+  for (int i = tid; i < KC; i += kIntraThreads) beta_s[i] = (i < len) ? kp.beta[(size_t)(t0 + i) * H + h] : 0.f;
   if (tid == 0) *flag = 0;
   if (active) {
 #pragma unroll
@@ -424,12 +460,19 @@ __global__ __launch_bounds__(256, 2) void intra_chunk_kernel(KernelPtrs kp, SeqI
     float off[8];
 #pragma unroll
     for (int e = 0; e < 8; ++e) { off[e] = 0.f; last[e] = 0.f; }
+    // Partial unrolling only: a fully unrolled loop would hoist every
+    // load of the scan table into registers.
+#pragma unroll 2
     for (int j = 0; j < NRG; ++j) {
+      const f32x4 s0 = *reinterpret_cast<const f32x4*>(scan + j * D + 8 * cg);
+      const f32x4 s1 = *reinterpret_cast<const f32x4*>(scan + j * D + 8 * cg + 4);
+      const float m = j < rg ? 1.f : 0.f;
 #pragma unroll
-      for (int e = 0; e < 8; ++e) {
-        const float s = scan[j * D + 8 * cg + e];
-        if (j < rg) off[e] += s;
-        last[e] += s;
+      for (int e = 0; e < 4; ++e) {
+        off[e] += m * s0[e];
+        off[4 + e] += m * s1[e];
+        last[e] += s0[e];
+        last[4 + e] += s1[e];
       }
     }
     bool big = false;
@@ -468,25 +511,34 @@ __global__ __launch_bounds__(256, 2) void intra_chunk_kernel(KernelPtrs kp, SeqI
       gst_pfrag8(M{}, blk + LY::kQt + ((size_t)(r / 16) * NKD + cg / 4) * LY::PF,
                  (r % 16) + 16 * (cg % 4), qv[p]);
     }
-    // K-bar^T fragments: row c = 8cg+e, k = tokens rg*RPT .. +RPT-1 (one run).
+    // K-bar^T and V^T go to LDS transposed (row = channel c = 8cg+e, k =
+    // tokens rg*RPT .. +RPT-1), then out as whole fragments below: storing
+    // these short transposed runs straight to memory costs far more.
     const int r0 = rg * RPT;
 #pragma unroll
     for (int e = 0; e < 8; ++e) {
       const int c = 8 * cg + e;
-      char* fr = blk + LY::kKb + ((size_t)(c / 16) * NKC + r0 / 32) * LY::PF;
-      gst_pfrag_run<RPT>(M{}, fr, (c % 16) + 16 * ((r0 % 32) / 8), r0 % 8, kb[e]);
+      KbS.template storeN<RPT>(c * SK + r0, kb[e]);
+#pragma unroll
+      for (int p = 0; p < RPT; ++p) VS[c * SK + r0 + p] = vv[e][p];
     }
   }
-  // Zero the padded token range of the K-bar^T fragments (KC > C).
-  if (KC > C) {
-    for (int idx = tid; idx < NDT * 64; idx += 256) {
-      const int rt = idx / 64, ln = idx % 64;
-      if ((ln >> 4) >= C / 8) {
-        float z[8] = {0, 0, 0, 0, 0, 0, 0, 0};
-        gst_pfrag8(M{}, blk + LY::kKb + (size_t)rt * NKC * LY::PF, ln, z);
-      }
+  if (KC > C) {  // zero the padded tokens
+    for (int idx = tid; idx < D * (KC - C); idx += kIntraThreads) {
+      const int c = idx / (KC - C), i = C + idx % (KC - C);
+      KbS.store(c * SK + i, 0.f);
+      VS[c * SK + i] = (plain_t)0.f;
     }
   }
+  __syncthreads();
+  // Fragment (channel tile rt, token block kb): lane l reads row 16rt + (l&15),
+  // tokens 32kb + 8(l>>4) .. +7, and stores them as one contiguous slot.
+  for (int f = w; f < NDT * NKC; f += NW) {
+    const int rt = f / NKC, kb = f % NKC;
+    st_pfrag(M{}, blk + LY::kKb + (size_t)f * LY::PF, KbS.pfrag(SK, 16 * rt, 32 * kb));
+    st_frag(M{}, blk + LY::kV + (size_t)f * LY::FF, lds_frag(M{}, VS, SK, 16 * rt, 32 * kb));
+  }
+  __syncthreads();  // the Gram operands reuse this region
 
   // ---- step 2: Grams A and P ----
   f32x4 accA[TPW], accP[TPW];
@@ -511,7 +563,7 @@ __global__ __launch_bounds__(256, 2) void intra_chunk_kernel(KernelPtrs kp, SeqI
       __syncthreads();
 #pragma unroll
       for (int s = 0; s < TPW; ++s) {
-        const int t = w + 4 * s;
+        const int t = w + NW * s;
         if (t < NTILE) {
           int a, b;
           tile_ab(t, a, b);
@@ -527,7 +579,7 @@ __global__ __launch_bounds__(256, 2) void intra_chunk_kernel(KernelPtrs kp, SeqI
     }
   } else {
     // Strong decay: exact pairwise evaluation.  Gamma goes to LDS; thread tid
-    // owns row r = tid / 4 and columns i = tid % 4, +4, ... <= r.
+    // owns row r = tid / 8 and columns i = tid % 8, +8, ... <= r.
     float* Gs = reinterpret_cast<float*>(smem + L::oG);
     if (active) {
 #pragma unroll
@@ -541,17 +593,17 @@ __global__ __launch_bounds__(256, 2) void intra_chunk_kernel(KernelPtrs kp, SeqI
   float* Ps = reinterpret_cast<float*>(smem + L::oP);
   float* Xs = reinterpret_cast<float*>(smem + L::oX);
   float* Ysc = reinterpret_cast<float*>(smem + L::oY);
-  constexpr int NPAIR = (C + 3) / 4;  // columns per thread in the pairwise path
+  constexpr int NPAIR = (C + 7) / 8;  // columns per thread in the pairwise path
   float pa[NPAIR], pp[NPAIR];
   if (!fast) {
     const float* Gs = reinterpret_cast<const float*>(smem + L::oG);
-    const int r = tid >> 2;
+    const int r = tid >> 3;
 #pragma unroll
     for (int m = 0; m < NPAIR; ++m) { pa[m] = 0.f; pp[m] = 0.f; }
     if (r < len) {
 #pragma unroll
       for (int m = 0; m < NPAIR; ++m) {
-        const int i = (tid & 3) + 4 * m;
+        const int i = (tid & 7) + 8 * m;
         if (i <= r) {
           float sa = 0.f, sp = 0.f;
           for (int c = 0; c < D; ++c) {
@@ -570,7 +622,7 @@ __global__ __launch_bounds__(256, 2) void intra_chunk_kernel(KernelPtrs kp, SeqI
     __syncthreads();  // Gamma reads done before A/P overwrite it
   }
   // ---- A (strictly lower, times beta_r), P (lower), X cleared ----
-  for (int idx = tid; idx < C * KC; idx += 256) {
+  for (int idx = tid; idx < C * KC; idx += kIntraThreads) {
     const int r = idx / KC, i = idx % KC;
     As[r * SF + i] = 0.f;
     Ps[r * SF + i] = 0.f;
@@ -580,7 +632,7 @@ __global__ __launch_bounds__(256, 2) void intra_chunk_kernel(KernelPtrs kp, SeqI
   if (fast) {
 #pragma unroll
     for (int s = 0; s < TPW; ++s) {
-      const int t = w + 4 * s;
+      const int t = w + NW * s;
       if (t < NTILE) {
         int a, b;
         tile_ab(t, a, b);
@@ -594,11 +646,11 @@ __global__ __launch_bounds__(256, 2) void intra_chunk_kernel(KernelPtrs kp, SeqI
       }
     }
   } else {
-    const int r = tid >> 2;
+    const int r = tid >> 3;
     if (r < C) {
 #pragma unroll
       for (int m = 0; m < NPAIR; ++m) {
-        const int i = (tid & 3) + 4 * m;
+        const int i = (tid & 7) + 8 * m;
         if (i <= r && r < len) {
           if (i < r) As[r * SF + i] = beta_s[r] * pa[m];
           Ps[r * SF + i] = pp[m];
@@ -618,9 +670,13 @@ __global__ __launch_bounds__(256, 2) void intra_chunk_kernel(KernelPtrs kp, SeqI
       for (int s = 0; s < 16; ++s) x[s] = (s == j) ? 1.f : 0.f;
       const float* Ab = As + (16 * bk) * SF + 16 * bk;
 #pragma unroll
-      for (int r = 0; r < 16; ++r)
+      for (int r = 0; r < 16; ++r) {
 #pragma unroll
         for (int s = r + 1; s < 16; ++s) x[s] -= Ab[s * SF + r] * x[r];
+        // Keep each elimination step's LDS reads next to their use; hoisting
+        // all 120 of them would cost as many registers.
+        __builtin_amdgcn_sched_barrier(0);
+      }
 #pragma unroll
       for (int s = 0; s < 16; ++s) Xs[(16 * bk + s) * SF + 16 * bk + j] = x[s];
     }
@@ -650,7 +706,7 @@ __global__ __launch_bounds__(256, 2) void intra_chunk_kernel(KernelPtrs kp, SeqI
   }
 
   // ---- step 4: T = X Diag(beta) and P fragments (fragment (rt, kb)) ----
-  for (int f = w; f < NRT * NKC; f += 4) {
+  for (int f = w; f < NRT * NKC; f += NW) {
     const int r = 16 * (f / NKC) + (l & 15), i0 = 32 * (f % NKC) + 8 * (l >> 4);
     float tv[8], pv[8];
 #pragma unroll
@@ -673,7 +729,7 @@ __global__ __launch_bounds__(256, 2) void intra_chunk_kernel(KernelPtrs kp, SeqI
     }
   }
   if (KC > C) {
-    for (int idx = tid; idx < D * (KC - C); idx += 256) {
+    for (int idx = tid; idx < D * (KC - C); idx += kIntraThreads) {
       const int c = idx / (KC - C), i = C + idx % (KC - C);
       KtT.store(c * SK + i, 0.f);
     }
@@ -682,7 +738,7 @@ __global__ __launch_bounds__(256, 2) void intra_chunk_kernel(KernelPtrs kp, SeqI
   // ---- W^T = (K*gam)^T T^T, tile (channel tile ct, token tile rt).  The
   // accumulator lane l holds W[16rt + (l&15)][16ct + 4(l>>4) + x], which is
   // four consecutive k values of one lane slot of the W fragment (rt, ct/2).
-  for (int t = w; t < NRT * NDT; t += 4) {
+  for (int t = w; t < NRT * NDT; t += NW) {
     const int rt = t / NDT, ct = t % NDT;
     f32x4 acc = {0, 0, 0, 0};
 #pragma unroll
@@ -705,64 +761,67 @@ __global__ __launch_bounds__(256, 2) void intra_chunk_kernel(KernelPtrs kp, SeqI
 // ---------------------------------------------------------------------------
 // Inter-chunk kernel: one workgroup per (sequence, head, block of value columns).
 // ---------------------------------------------------------------------------
-template <class M, int D, int C>
+// Operands of one chunk, as held by one wave.  The phase-1 group (W, Q*gam,
+// T, V^T) feeds U = T V - W S and Q*gam S; the phase-2 group (P, K-bar^T,
+// gam_n) feeds the output and the state update.
+template <class M, int D, int C, int NCT>
 struct ChunkFrags {
   typedef Layout<M, D, C> LY;
   static constexpr int NST = LY::NDT / 4 > 0 ? LY::NDT / 4 : 1;  // state tiles per wave
   typename M::PFrag W[LY::NKD];
-  typename M::PFrag Tm[LY::NKC];
   typename M::PFrag Qt[LY::NKD];
+  typename M::PFrag Tm[LY::NKC];
+  typename M::Frag V[NCT][LY::NKC];
   typename M::PFrag P[LY::NKC];
   typename M::PFrag Kb[NST][LY::NKC];
   float gam[NST][4];
 };
 
-// Operands of one chunk are loaded in two groups: the phase-1 group (W, Q*gam,
-// T) is dead after the U product and the phase-2 group (P, K-bar^T, gam_n)
-// after the state update, so each group of the next chunk can be fetched into
-// the same registers as soon as its current use ends.
-template <class M, int D, int C>
-__device__ __forceinline__ void load_frags_phase1(ChunkFrags<M, D, C>& f, const char* blk, int w) {
+template <class M, int D, int C, int NCT>
+__device__ __forceinline__ void load_frags_phase1(ChunkFrags<M, D, C, NCT>& f, const char* blk, int w,
+                                                  int vt0) {
   typedef Layout<M, D, C> LY;
-  // With four row tiles every wave has one; the test is then known true at
-  // compile time and the loads stay unconditional (which lets the compiler
-  // count outstanding loads instead of draining them).
-  if (LY::NRT == 4 || w < LY::NRT) {
-    const int rt = w;
+  // Every wave issues the same loads.  With fewer than four row tiles the
+  // waves past the last one re-read it (their products are skipped): a load
+  // that only some waves issue leaves the compiler's count of outstanding
+  // loads wrong for the others, and a wait can then pass before the data
+  // it guards has arrived.
+  const int rt = LY::NRT == 4 ? w : min(w, LY::NRT - 1);
 #pragma unroll
-    for (int kb = 0; kb < LY::NKD; ++kb) {
-      f.W[kb] = ld_pfrag(M{}, blk + LY::kW + (size_t)(rt * LY::NKD + kb) * LY::PF);
-      f.Qt[kb] = ld_pfrag(M{}, blk + LY::kQt + (size_t)(rt * LY::NKD + kb) * LY::PF);
-    }
+  for (int kb = 0; kb < LY::NKD; ++kb) {
+    f.W[kb] = ld_pfrag(M{}, blk + LY::kW + (size_t)(rt * LY::NKD + kb) * LY::PF);
+    f.Qt[kb] = ld_pfrag(M{}, blk + LY::kQt + (size_t)(rt * LY::NKD + kb) * LY::PF);
+  }
 #pragma unroll
-    for (int kb = 0; kb < LY::NKC; ++kb)
-      f.Tm[kb] = ld_pfrag(M{}, blk + LY::kT + (size_t)(rt * LY::NKC + kb) * LY::PF);
+  for (int kb = 0; kb < LY::NKC; ++kb) {
+    f.Tm[kb] = ld_pfrag(M{}, blk + LY::kT + (size_t)(rt * LY::NKC + kb) * LY::PF);
+#pragma unroll
+    for (int ct = 0; ct < NCT; ++ct)
+      f.V[ct][kb] = ld_frag(M{}, blk + LY::kV + (size_t)((vt0 + ct) * LY::NKC + kb) * LY::FF);
   }
 }
 
-template <class M, int D, int C>
-__device__ __forceinline__ void load_frags_phase2(ChunkFrags<M, D, C>& f, const char* blk, int w) {
+template <class M, int D, int C, int NCT>
+__device__ __forceinline__ void load_frags_phase2(ChunkFrags<M, D, C, NCT>& f, const char* blk, int w) {
   typedef Layout<M, D, C> LY;
-  constexpr int NST = ChunkFrags<M, D, C>::NST;
+  constexpr int NST = ChunkFrags<M, D, C, NCT>::NST;
   const int l = lane_id();
-  if (LY::NRT == 4 || w < LY::NRT) {
-    const int rt = w;
+  // Unconditional for every wave, as in load_frags_phase1.
+  const int rt = LY::NRT == 4 ? w : min(w, LY::NRT - 1);
 #pragma unroll
-    for (int kb = 0; kb < LY::NKC; ++kb)
-      f.P[kb] = ld_pfrag(M{}, blk + LY::kP + (size_t)(rt * LY::NKC + kb) * LY::PF);
-  }
+  for (int kb = 0; kb < LY::NKC; ++kb)
+    f.P[kb] = ld_pfrag(M{}, blk + LY::kP + (size_t)(rt * LY::NKC + kb) * LY::PF);
+  static_assert(LY::NDT == 4 * NST, "every wave owns NST state tiles");
 #pragma unroll
   for (int s = 0; s < NST; ++s) {
     const int st = w * NST + s;
-    if (LY::NDT == 4 * NST || st < LY::NDT) {
 #pragma unroll
-      for (int kb = 0; kb < LY::NKC; ++kb)
-        f.Kb[s][kb] = ld_pfrag(M{}, blk + LY::kKb + (size_t)(st * LY::NKC + kb) * LY::PF);
-      const f32x4 gv = *reinterpret_cast<const f32x4*>(
-          reinterpret_cast<const float*>(blk + LY::kGam) + 16 * st + 4 * (l >> 4));
+    for (int kb = 0; kb < LY::NKC; ++kb)
+      f.Kb[s][kb] = ld_pfrag(M{}, blk + LY::kKb + (size_t)(st * LY::NKC + kb) * LY::PF);
+    const f32x4 gv = *reinterpret_cast<const f32x4*>(
+        reinterpret_cast<const float*>(blk + LY::kGam) + 16 * st + 4 * (l >> 4));
 #pragma unroll
-      for (int x = 0; x < 4; ++x) f.gam[s][x] = gv[x];
-    }
+    for (int x = 0; x < 4; ++x) f.gam[s][x] = gv[x];
   }
 }
 
@@ -777,21 +836,24 @@ struct InterLds {
   static constexpr size_t kUTplain = (size_t)DVB * SK * sizeof(plain_t);
   static constexpr size_t oST = 0;
   static constexpr size_t oUT = oST + (M::kSplit ? 2 : 1) * kSTplain;
-  static constexpr size_t oVT = oUT + (M::kSplit ? 2 : 1) * kUTplain;
-  static constexpr size_t kTotal = oVT + kUTplain;
+  static constexpr size_t kTotal = oUT + (M::kSplit ? 2 : 1) * kUTplain;
 };
 
 // NCT = number of 16-column value tiles per workgroup (16, 32 or 64 columns).
 // Every wave applies each operand fragment it loads to all NCT tiles, so a
 // wider block divides the per-chunk operand traffic among fewer workgroups.
+//
+// Pipeline: two operand sets alternate between even and odd chunks.  After
+// phase 1 of chunk c its set receives the phase-1 group of chunk c+2, and
+// after phase 2 the other set receives the phase-2 group of chunk c+1.  That
+// keeps about 55 loads per wave in flight, inside the 63-entry vmcnt range.
 template <class M, int D, int C, int NCT, bool OUT_BF16>
 __global__ __launch_bounds__(256) void inter_chunk_kernel(KernelPtrs kp, SeqInfo si, int num_pairs) {
-  typedef typename M::in_t in_t;
   typedef Layout<M, D, C> LY;
   typedef InterLds<M, D, C, NCT> L;
-  typedef typename L::plain_t plain_t;
+  typedef ChunkFrags<M, D, C, NCT> CF;
   constexpr int NRT = LY::NRT, KC = LY::KC, NKC = LY::NKC, NKD = LY::NKD, NDT = LY::NDT;
-  constexpr int NST = ChunkFrags<M, D, C>::NST;
+  constexpr int NST = CF::NST;
   constexpr int DVB = L::DVB;
   constexpr int NVB = D / DVB;
   constexpr int SD = L::SD, SK = L::SK;
@@ -819,7 +881,6 @@ __global__ __launch_bounds__(256) void inter_chunk_kernel(KernelPtrs kp, SeqInfo
 
   LdsPrecise<M> ST(smem + L::oST, L::kSTplain);
   LdsPrecise<M> UT(smem + L::oUT, L::kUTplain);
-  plain_t* VT = reinterpret_cast<plain_t*>(smem + L::oVT);
 
   // ---- state block in accumulator layout: tile (st, ct) holds rows
   // 16st.., columns col0 + 16ct.. ----
@@ -851,77 +912,47 @@ __global__ __launch_bounds__(256) void inter_chunk_kernel(KernelPtrs kp, SeqInfo
     }
   };
   write_state_lds();
-
-  // V tile loader: thread -> (token vi, columns 16ct + vj .. +3 for every ct).
-  // The prefetch keeps the raw elements; converting them at load time would
-  // make the wave wait for every earlier load right there.
-  typedef typename M::in_t vin_t;
-  typedef vin_t vraw_t __attribute__((ext_vector_type(4)));
-  const in_t* vg = reinterpret_cast<const in_t*>(kp.v);
-  const int vi = tid >> 2, vj = 4 * (tid & 3);
-  // The load is unconditional: rows past the chunk re-read its last row
-  // (always a valid token) and are zeroed when stored.
-  auto load_v = [&](int ci, vraw_t* raw) {
-    const int t0 = bos + ci * C;
-    const int tr = min(t0 + min(vi, C - 1), eos - 1);
-    const in_t* p = vg + ((size_t)tr * H + h) * D + col0 + vj;
-#pragma unroll
-    for (int ct = 0; ct < NCT; ++ct) raw[ct] = *reinterpret_cast<const vraw_t*>(p + 16 * ct);
-  };
-  auto store_v = [&](const vraw_t* raw, int len) {
-    if (C >= 64 || vi < KC) {
-      const bool live = vi < C && vi < len;
-#pragma unroll
-      for (int ct = 0; ct < NCT; ++ct)
-#pragma unroll
-        for (int e = 0; e < 4; ++e)
-          VT[(16 * ct + vj + e) * SK + vi] = live ? raw[ct][e] : (vin_t)0.f;
-    }
-  };
-  // Zero the padded token columns of VT and UT once (KC > C).
+  // Zero the padded token columns of UT once (KC > C); nothing writes them.
   if (KC > C) {
-    for (int idx = tid; idx < DVB * (KC - C); idx += 256) {
-      const int j = idx / (KC - C), i = C + idx % (KC - C);
-      VT[j * SK + i] = (plain_t)0.f;
-      UT.store(j * SK + i, 0.f);
-    }
+    for (int idx = tid; idx < DVB * (KC - C); idx += 256) UT.store((idx / (KC - C)) * SK + C + idx % (KC - C), 0.f);
   }
 
   auto blk_of = [&](int ci) { return kp.ops + ((size_t)(cid0 + ci) * H + h) * LY::kBytes; };
-  ChunkFrags<M, D, C> f;
-  vraw_t vr[NCT];
+  const int vt0 = col0 / 16;  // first V^T fragment row tile of this block
 
-  // One chunk of the recurrence.  The operands of chunk ci are in `f` and
-  // `vr`; the next chunk's are fetched into them as each group goes dead.
-  // Past the end the fetches re-read the last chunk: they stay
-  // unconditional, since a fetch under a branch makes the compiler drain
-  // every outstanding load where the paths join.
-  auto process = [&](int ci) {
+  // One chunk.  `f` holds chunk ci; `g` is the other set.  Fetches past the
+  // end re-read the last chunk: they stay unconditional, since a fetch under a
+  // branch makes the compiler drain every outstanding load where the paths
+  // join.
+  auto process = [&](CF& f, CF& g, int ci) {
     const int t0 = bos + ci * C;
     const int len = eos - t0 < C ? eos - t0 : C;
-    const int nx = min(ci + 1, nch - 1);
-    store_v(vr, len);
-    __syncthreads();  // VT and ST ready
+    __syncthreads();  // ST ready
     f32x4 qs[NCT];
 #pragma unroll
     for (int ct = 0; ct < NCT; ++ct) qs[ct] = f32x4{0, 0, 0, 0};
     if (NRT == 4 || w < NRT) {
+      // All B-operand fragments of this phase are read from LDS first, so
+      // their latency is paid once rather than in front of every product.
+      typename M::PFrag sf[NKD][NCT];
+#pragma unroll
+      for (int kb = 0; kb < NKD; ++kb)
+#pragma unroll
+        for (int ct = 0; ct < NCT; ++ct) sf[kb][ct] = ST.pfrag(SD, 16 * ct, 32 * kb);
       f32x4 ws[NCT], u[NCT];
 #pragma unroll
       for (int ct = 0; ct < NCT; ++ct) { ws[ct] = f32x4{0, 0, 0, 0}; u[ct] = ws[ct]; }
 #pragma unroll
+      for (int kb = 0; kb < NKC; ++kb)
+#pragma unroll
+        for (int ct = 0; ct < NCT; ++ct) u[ct] = mma_pf(f.Tm[kb], f.V[ct][kb], u[ct]);
+#pragma unroll
       for (int kb = 0; kb < NKD; ++kb)
 #pragma unroll
         for (int ct = 0; ct < NCT; ++ct) {
-          const auto sf = ST.pfrag(SD, 16 * ct, 32 * kb);
-          ws[ct] = mma_pp(f.W[kb], sf, ws[ct]);
-          qs[ct] = mma_pp(f.Qt[kb], sf, qs[ct]);
+          ws[ct] = mma_pp(f.W[kb], sf[kb][ct], ws[ct]);
+          qs[ct] = mma_pp(f.Qt[kb], sf[kb][ct], qs[ct]);
         }
-#pragma unroll
-      for (int kb = 0; kb < NKC; ++kb)
-#pragma unroll
-        for (int ct = 0; ct < NCT; ++ct)
-          u[ct] = mma_pf(f.Tm[kb], lds_frag(M{}, VT, SK, 16 * ct, 32 * kb), u[ct]);
 #pragma unroll
       for (int ct = 0; ct < NCT; ++ct) {
         float v4[4] = {u[ct][0] - ws[ct][0], u[ct][1] - ws[ct][1], u[ct][2] - ws[ct][2],
@@ -929,18 +960,21 @@ __global__ __launch_bounds__(256) void inter_chunk_kernel(KernelPtrs kp, SeqInfo
         UT.template storeN<4>((16 * ct + (l & 15)) * SK + 16 * w + 4 * (l >> 4), v4);
       }
     }
-    load_frags_phase1<M, D, C>(f, blk_of(nx), w);
-    load_v(nx, vr);
-    __syncthreads();  // UT ready; ST/VT reads done
+    load_frags_phase1<M, D, C, NCT>(f, blk_of(min(ci + 2, nch - 1)), w, vt0);
+    __syncthreads();  // UT ready; ST reads done
+    typename M::PFrag uf[NKC][NCT];
+#pragma unroll
+    for (int kb = 0; kb < NKC; ++kb)
+#pragma unroll
+      for (int ct = 0; ct < NCT; ++ct) uf[kb][ct] = UT.pfrag(SK, 16 * ct, 32 * kb);
     if (NRT == 4 || w < NRT) {
 #pragma unroll
       for (int ct = 0; ct < NCT; ++ct) {
         f32x4 o = qs[ct];
+        // P is lower triangular: token blocks past this row tile are zero.
 #pragma unroll
-        for (int kb = 0; kb < NKC; ++kb) {
-          if (32 * kb > 16 * w + 15) break;
-          o = mma_pp(f.P[kb], UT.pfrag(SK, 16 * ct, 32 * kb), o);
-        }
+        for (int kb = 0; kb < NKC; ++kb)
+          if (32 * kb <= 16 * w + 15) o = mma_pp(f.P[kb], uf[kb][ct], o);
 #pragma unroll
         for (int x = 0; x < 4; ++x) {
           const int r = 16 * w + 4 * (l >> 4) + x;
@@ -965,22 +999,26 @@ __global__ __launch_bounds__(256) void inter_chunk_kernel(KernelPtrs kp, SeqInfo
 #pragma unroll
         for (int kb = 0; kb < NKC; ++kb)
 #pragma unroll
-          for (int ct = 0; ct < NCT; ++ct)
-            S[s][ct] = mma_pp(f.Kb[s][kb], UT.pfrag(SK, 16 * ct, 32 * kb), S[s][ct]);
+          for (int ct = 0; ct < NCT; ++ct) S[s][ct] = mma_pp(f.Kb[s][kb], uf[kb][ct], S[s][ct]);
       }
     }
-    load_frags_phase2<M, D, C>(f, blk_of(nx), w);
+    load_frags_phase2<M, D, C, NCT>(g, blk_of(min(ci + 1, nch - 1)), w);
     // ST is read again only after the next chunk's first barrier, and every
-    // read of this chunk's ST/VT happened before the second barrier.
+    // read of this chunk's ST happened before the second barrier.
     write_state_lds();
   };
 
+  CF fa, fb;
   if (nch > 0) {
-    load_frags_phase1<M, D, C>(f, blk_of(0), w);
-    load_frags_phase2<M, D, C>(f, blk_of(0), w);
-    load_v(0, vr);
+    load_frags_phase1<M, D, C, NCT>(fa, blk_of(0), w, vt0);
+    load_frags_phase2<M, D, C, NCT>(fa, blk_of(0), w);
+    load_frags_phase1<M, D, C, NCT>(fb, blk_of(min(1, nch - 1)), w, vt0);
   }
-  for (int ci = 0; ci < nch; ++ci) process(ci);
+  for (int ci = 0; ci < nch; ci += 2) {
+    process(fa, fb, ci);
+    if (ci + 1 >= nch) break;
+    process(fb, fa, ci + 1);
+  }
   if (kp.s1) {
 #pragma unroll
     for (int s = 0; s < NST; ++s) {
@@ -1070,7 +1108,7 @@ static hipError_t launch_prefill_t(const PrefillArgs& a) {
     hipError_t e = hipFuncSetAttribute(reinterpret_cast<const void*>(&intra_chunk_kernel<M, D, C>),
                                        hipFuncAttributeMaxDynamicSharedMemorySize, (int)lds);
     if (e != hipSuccess) return e;
-    hipLaunchKernelGGL((intra_chunk_kernel<M, D, C>), dim3(a.total_chunks, a.H), dim3(256), lds,
+    hipLaunchKernelGGL((intra_chunk_kernel<M, D, C>), dim3(a.total_chunks, a.H), dim3(kIntraThreads), lds,
                        a.stream, kp, si);
   }
   const int nct = choose_nct(a.num_seqs * a.H, D);

@@ -67,7 +67,7 @@ int kda_version(void);
  * an argument error (the status says which).
  *
  * The workspace holds the chunk table and, per (chunk, head), the intra-chunk
- * operands that the inter-chunk pass consumes (128.5 KB per chunk and head at
+ * operands that the inter-chunk pass consumes (144.5 KB per chunk and head at
  * Dk = Dv = 128, C = 64).
  */
 kda_status kda_prefill_workspace_size(int B, int T, int H, int Dk, int Dv,

@@ -88,11 +88,11 @@ def test_prefill_varlen_validation(lib):
 
 
 def test_workspace_size(lib):
-    # B=1, T=4096, H=32, D=128, C=64, bf16: 64 chunks x 32 heads of 131584 B
-    # (Q*gam 32 KB, W 32 KB, K-bar 32 KB, P 16 KB, T 16 KB, gam_n 512 B, each
-    # precise matrix as bf16 hi + lo) plus the 256-byte-aligned chunk table.
+    # B=1, T=4096, H=32, D=128, C=64, bf16: 64 chunks x 32 heads of 147968 B
+    # (Q*gam 32 KB, W 32 KB, K-bar 32 KB, P 16 KB, T 16 KB as bf16 hi + lo;
+    # V^T 16 KB; gam_n 512 B) plus the 256-byte-aligned chunk table.
     n = kda.workspace_size(1, 4096, 32, 128, 1, 64, kda.KDA_BF16)
-    assert n == 2048 * 131584 + 256 + 256
+    assert n == 2048 * 147968 + 256 + 256
     cu = np.array([0, 100, 100, 300], dtype=np.int32)
     m = kda.workspace_size(1, 300, 4, 64, 3, 16, kda.KDA_F32, cu)
     assert m > 0 and m % 256 == 0

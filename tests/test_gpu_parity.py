@@ -173,6 +173,25 @@ def test_prefill_ragged_with_state(kda, dtype, D, C, T):
 
 
 @pytest.mark.parametrize("dtype", ["bf16", "f32"])
+@pytest.mark.parametrize("D", [64, 128])
+@pytest.mark.parametrize("C", [16, 32, 64])
+def test_prefill_every_variant_multichunk(kda, dtype, D, C):
+    """Every built (dtype, head size, chunk) variant over several chunks with a
+    ragged tail and an initial state: exercises the inter-chunk pipeline
+    (operands fetched one and two chunks ahead) for each instantiation."""
+    T = 3 * C + 5
+    say(f"prefill variant dtype={dtype} D={D} C={C} T={T}")
+    rng = np.random.default_rng([19, D, C])
+    x = I.draw_tokens(rng, T, 2, D, D, dtype)
+    s0 = I.draw_states(rng, 1, 2, D, D)
+    eo, ef = oracle.kda_recurrent(x.q, x.k, x.v, x.g, x.beta, s0)
+    o, fin = run_prefill(kda, x, C, s0=s0)
+    eo_, es_ = rel(o, eo), rel(fin, ef)
+    say(f"  o err {eo_:.2e}  state err {es_:.2e}")
+    assert eo_ <= TOL[dtype] and es_ <= TOL[dtype]
+
+
+@pytest.mark.parametrize("dtype", ["bf16", "f32"])
 def test_prefill_strong_decay(kda, dtype):
     """g scaled x50: chunk decay spans far past exp(-40), so the Grams take the
     exact pairwise path."""
