@@ -45,7 +45,10 @@ struct PrefillArgs {
 
 // Bytes of intra-chunk operands stored per (chunk, head).
 size_t prefill_chunk_bytes(int D, int chunk, bool in_bf16);
-// Total workspace bytes (chunk table + operands), 256-byte aligned pieces.
+// Chunks per prefill segment (the workspace holds one segment's operands).
+int prefill_segment_chunks(int total_chunks, int H, int D, int chunk, bool in_bf16);
+// Total workspace bytes (chunk table, state carry between segments, one
+// segment's operands), 256-byte aligned pieces.
 size_t prefill_workspace_bytes(int num_seqs, int total_chunks, int H, int D, int chunk,
                                bool in_bf16);
 hipError_t launch_prefill(const PrefillArgs& a);

@@ -91,10 +91,39 @@ static size_t table_bytes(int num_seqs, int total_chunks) {
          align256(sizeof(int32_t) * (size_t)total_chunks);
 }
 
+// The prefill runs in segments of consecutive chunks (in the packed chunk
+// order): the intra-chunk pass of a segment, then its inter-chunk pass, which
+// carries each sequence's state into the next segment.  The workspace holds
+// one segment's operands, so it stays bounded for long inputs and a segment's
+// operands are read back soon after they are written, while the 256 MB
+// Infinity Cache still holds them.  KDA_PREFILL_SEGMENT_KB (>= 1) overrides
+// the per-segment operand budget; it is read at every call, and a workspace
+// must be sized under the same setting as the call that uses it.
+static size_t segment_budget_bytes() {
+  const char* e = getenv("KDA_PREFILL_SEGMENT_KB");
+  const long long v = e ? atoll(e) : 0;
+  return (size_t)(v >= 1 ? v : 160 * 1024) << 10;
+}
+
+int prefill_segment_chunks(int total_chunks, int H, int D, int chunk, bool in_bf16) {
+  if (total_chunks <= 0) return 0;
+  const size_t per = (size_t)H * prefill_chunk_bytes(D, chunk, in_bf16);
+  size_t most = segment_budget_bytes() / per;
+  if (most < 1) most = 1;
+  // Equal segments rather than full ones and a short tail.
+  const size_t nseg = (total_chunks + most - 1) / most;
+  return (int)((total_chunks + nseg - 1) / nseg);
+}
+
+static size_t carry_bytes(int num_seqs, int total_chunks, int seg, int H, int D) {
+  return seg < total_chunks ? align256((size_t)num_seqs * H * D * D * sizeof(float)) : 0;
+}
+
 size_t prefill_workspace_bytes(int num_seqs, int total_chunks, int H, int D, int chunk,
                                bool in_bf16) {
-  return table_bytes(num_seqs, total_chunks) +
-         (size_t)total_chunks * H * prefill_chunk_bytes(D, chunk, in_bf16);
+  const int seg = prefill_segment_chunks(total_chunks, H, D, chunk, in_bf16);
+  return table_bytes(num_seqs, total_chunks) + carry_bytes(num_seqs, total_chunks, seg, H, D) +
+         (size_t)seg * H * prefill_chunk_bytes(D, chunk, in_bf16);
 }
 
 // ---------------------------------------------------------------------------
@@ -105,6 +134,7 @@ struct SeqInfo {
   const int32_t* chunk_off; // [num_seqs + 1] chunk offsets (varlen only)
   const int32_t* chunk_seq; // [total_chunks] sequence of each chunk (varlen only)
   int num_seqs, seq_len, total_tokens, total_chunks;
+  int seg_lo, seg_hi;       // chunks [seg_lo, seg_hi) of the packed order in this launch
 };
 
 __device__ __forceinline__ int clampi(int x, int lo, int hi) { return x < lo ? lo : (x > hi ? hi : x); }
@@ -192,53 +222,46 @@ __device__ __forceinline__ f32x4 prod16(ModeF32, f32x4 acc, const float* A, int 
 }
 
 // ---------------------------------------------------------------------------
-// LDS plan of the intra-chunk kernel.  One region is reused by the phases:
-//   A  (fast path, per half of the channels): Qt', Kt', Kh' precise [C x 64]
-//   S  (strong-decay path): Gamma fp32 [C x (D+1)]
-//   B  (after the Grams): X, Y scratch, A, P (fp32)
-//   C  (W product): X, KtT precise [D x KC]
-// plus the persistent scan totals, beta and a flag.
+// LDS plan of the intra-chunk kernel: two regions that the phases reuse,
+//   R0: K-bar^T staging (precise [D x KC])  ->  K/gam fragments (precise, in
+//       fragment order; on the strong-decay path Gamma fp32 [C x (D+1)])
+//       ->  X = (I + A)^{-1} (fp32 [C x (KC+1)]) and the solve scratch, then
+//       the T fragments
+//   R1: V^T staging ([D x KC])  ->  A and P (fp32 [C x (KC+1)])
+//       ->  (K*gam)^T staging (precise [D x KC])
+// plus the per-tile totals of the decay scan and beta.
 // ---------------------------------------------------------------------------
+constexpr size_t cmax(size_t a, size_t b) { return a > b ? a : b; }
+
 template <class M, int D, int C>
 struct IntraLds {
   typedef typename M::in_t plain_t;  // element of one half of a precise matrix
   static constexpr int KC = Layout<M, D, C>::KC;
-  static constexpr int NCG = D / 8;
-  static constexpr int RPT = (C * NCG / kIntraThreads) > 1 ? (C * NCG / kIntraThreads) : 1;
-  static constexpr int NRG = C / RPT;
-  static constexpr int DH = 64;                      // channels per Gram pass
-  static constexpr int NHALF = D / DH;
-  static constexpr int SH = DH + kPad;               // row stride of [C x DH] operands
-  static constexpr int SK = KC + kPad;               // row stride of [D x KC] operands
-  static constexpr int SF = KC + 1;                  // row stride of fp32 [C x KC] matrices
-  static constexpr int SG = D + 1;                   // row stride of the fp32 Gamma array
-  static constexpr size_t kHalfPlain = (size_t)C * SH * sizeof(plain_t);
-  static constexpr size_t kHalfPrecise = M::kSplit ? 2 * kHalfPlain : kHalfPlain;
-  static constexpr size_t kPhaseA = 3 * kHalfPrecise;
-  static constexpr size_t kPhaseS = (size_t)C * SG * 4;
+  static constexpr int NRT = C / 16;
+  static constexpr int SK = KC + kPad;  // row stride of [D x KC] staging
+  static constexpr int SF = KC + 1;     // row stride of fp32 [C x KC] matrices
+  static constexpr int SG = D + 1;      // row stride of the fp32 Gamma array
+  static constexpr size_t kStPlain = ((size_t)D * SK * sizeof(plain_t) + 15) / 16 * 16;
+  static constexpr size_t kStPrecise = M::kSplit ? 2 * kStPlain : kStPlain;
+  static constexpr size_t kKhFrags = (size_t)NRT * (D / 32) * M::kPFragBytes;
+  static constexpr size_t kGamma = ((size_t)C * SG * 4 + 15) / 16 * 16;
   static constexpr size_t kFMat = ((size_t)C * SF * 4 + 15) / 16 * 16;
   static constexpr size_t kYsc = 4 * 16 * 17 * 4;
-  static constexpr size_t kPhaseB = 3 * kFMat + kYsc;
-  static constexpr size_t kKtTplain = ((size_t)D * SK * sizeof(plain_t) + 15) / 16 * 16;
-  static constexpr size_t kKtT = M::kSplit ? 2 * kKtTplain : kKtTplain;
-  static constexpr size_t kPhaseC = kFMat + kKtT;
-  // Phase K (before A): K-bar^T (precise) and V^T (plain) staged [D x KC]
-  // for the fragment copy-out.
-  static constexpr size_t kPhaseK = kKtT + kKtTplain;
-  static constexpr size_t m0 = kPhaseA > kPhaseK ? kPhaseA : kPhaseK;
-  static constexpr size_t m1 = m0 > kPhaseS ? m0 : kPhaseS;
-  static constexpr size_t m2 = kPhaseB > kPhaseC ? kPhaseB : kPhaseC;
-  static constexpr size_t kUnion = ((m1 > m2 ? m1 : m2) + 15) / 16 * 16;
-  static constexpr size_t kScan = (size_t)NRG * D * 4;
-  static constexpr size_t kBeta = (size_t)KC * 4;
-  static constexpr size_t kTotal = kUnion + kScan + kBeta + 16;
-  // offsets
-  static constexpr size_t oQt = 0, oKt = kHalfPrecise, oKh = 2 * kHalfPrecise;  // phase A
-  static constexpr size_t oG = 0;                                              // phase S
-  static constexpr size_t oX = 0, oY = kFMat, oA = kFMat + kYsc, oP = 2 * kFMat + kYsc;  // B
-  static constexpr size_t oKtT = kFMat;                                        // phase C
-  static constexpr size_t oKbS = 0, oVS = kKtT;                                // phase K
-  static constexpr size_t oScan = kUnion, oBeta = oScan + kScan, oFlag = oBeta + kBeta;
+  static constexpr size_t kTFrags = (size_t)NRT * (KC / 32) * M::kPFragBytes;
+  static constexpr size_t kR0 = cmax(cmax(kStPrecise, kKhFrags),
+                                     cmax(kGamma, kFMat + cmax(kYsc, kTFrags)));
+  static constexpr size_t kR1 = cmax(cmax(kStPlain, 2 * kFMat), kStPrecise);
+  static constexpr size_t oR0 = 0, oR1 = kR0;
+  static constexpr size_t oTot = kR0 + kR1;              // fp32 [NRT][D]
+  static constexpr size_t oBeta = oTot + (size_t)NRT * D * 4;
+  static constexpr size_t kTotal = oBeta + (size_t)KC * 4;
+  // offsets inside the regions
+  static constexpr size_t oKbS = oR0, oVS = oR1;         // staging
+  static constexpr size_t oKh = oR0, oG = oR0;           // Gram operands / Gamma
+  static constexpr size_t oA = oR1, oP = oR1 + kFMat;    // Grams
+  static constexpr size_t oX = oR0, oY = oR0 + kFMat;    // solve
+  static constexpr size_t oTf = oR0 + kFMat;             // T fragments (after the solve)
+  static constexpr size_t oKtT = oR1;                    // W product
 };
 
 template <class M>
@@ -270,6 +293,11 @@ struct LdsPrecise<ModeBF16> {
   __device__ ModeBF16::PFrag pfrag(int stride, int row0, int k0) const {
     return lds_pfrag(ModeBF16{}, hi, lo, stride, row0, k0);
   }
+  // element e of a lane's precise fragment, already split
+  __device__ void put(int idx, const ModeBF16::PFrag& f, int e) {
+    hi[idx] = f.hi[e];
+    lo[idx] = f.lo[e];
+  }
 };
 template <>
 struct LdsPrecise<ModeF32> {
@@ -287,6 +315,7 @@ struct LdsPrecise<ModeF32> {
   __device__ ModeF32::PFrag pfrag(int stride, int row0, int k0) const {
     return lds_pfrag(ModeF32{}, v, nullptr, stride, row0, k0);
   }
+  __device__ void put(int idx, const ModeF32::PFrag& f, int e) { v[idx] = f.v[e]; }
 };
 
 // Write eight consecutive-k fp32 values of one lane into a global fragment.
@@ -357,39 +386,67 @@ struct KernelPtrs {
   void* o;
   const float* s0;
   float* s1;
-  char* ops;       // per-(chunk, head) operand blocks
+  float* carry;    // [num_seqs, H, D, D] state between segments, or nullptr
+  char* ops;       // per-(chunk, head) operand blocks of the current segment
   int H;
 };
 
-// Lower-triangular 16x16 tile t (row-major order over b <= a) -> (a, b).
-__device__ __forceinline__ void tile_ab(int t, int& a, int& b) {
-  a = 0;
-  while ((a + 1) * (a + 2) / 2 <= t) ++a;
-  b = t - a * (a + 1) / 2;
-}
+// Eight input elements of one row held as loaded (bf16 or fp32).
+template <class T>
+struct Raw8;
+template <>
+struct Raw8<bf16> {
+  bf16x8 v;
+  __device__ void load(const bf16* p) { v = *reinterpret_cast<const bf16x8*>(p); }
+  __device__ float get(int e) const { return bf2f(v[e]); }
+};
+template <>
+struct Raw8<float> {
+  f32x4 a, b;
+  __device__ void load(const float* p) {
+    a = *reinterpret_cast<const f32x4*>(p);
+    b = *reinterpret_cast<const f32x4*>(p + 4);
+  }
+  __device__ float get(int e) const { return e < 4 ? a[e] : b[e - 4]; }
+};
+
+// Precise fragment in LDS, stored as in global memory (hi: lane*16 B, lo:
+// 1024 + lane*16 B for bf16; lane*32 B for fp32).
+__device__ __forceinline__ void lds_st_pfrag(ModeBF16 m, char* p, const ModeBF16::PFrag& f) { st_pfrag(m, p, f); }
+__device__ __forceinline__ void lds_st_pfrag(ModeF32 m, char* p, const ModeF32::PFrag& f) { st_pfrag(m, p, f); }
 
 // ---------------------------------------------------------------------------
-// Intra-chunk kernel: grid (total_chunks, H), 512 threads (8 waves), two
-// workgroups per CU, so four waves share each SIMD to cover each other's
-// latency.
+// Intra-chunk kernel: grid (chunks of the segment, H), 512 threads (8 waves),
+// two workgroups per CU.
+//
+// Thread layout follows the MFMA fragments: the chunk's [C x D] token-by-
+// channel matrices are cut into 16-token x 32-channel fragments; wave w holds
+// fragments w, w + 8, ... (row tile f % NRT, channel block f / NRT), lane l
+// the eight channels 32 kb + 8 (l >> 4) .. + 7 of token 16 rt + (l & 15).  So
+// the decayed Q and K are Gram A-operands in registers, Q*gam goes out as
+// whole fragments, and the decay cumsum runs across the 16 lanes of a tile.
 // ---------------------------------------------------------------------------
 template <class M, int D, int C>
 __global__ __launch_bounds__(kIntraThreads, 4) void intra_chunk_kernel(KernelPtrs kp, SeqInfo si) {
   typedef typename M::in_t in_t;
+  typedef typename M::PFrag PFrag;
   typedef Layout<M, D, C> LY;
   typedef IntraLds<M, D, C> L;
+  typedef typename L::plain_t plain_t;
   constexpr int NRT = LY::NRT, KC = LY::KC, NKC = LY::NKC, NKD = LY::NKD, NDT = LY::NDT;
-  constexpr int NCG = L::NCG, RPT = L::RPT, NRG = L::NRG, SH = L::SH, SK = L::SK, SF = L::SF;
-  constexpr int NTILE = NRT * (NRT + 1) / 2;
+  constexpr int SK = L::SK, SF = L::SF, SG = L::SG;
   constexpr int NW = kIntraThreads / 64;
-  constexpr int TPW = (NTILE + NW - 1) / NW;  // Gram tiles per wave
+  constexpr int NFRAG = NRT * NKD;            // fragments of a [C x D] matrix
+  constexpr int FPW = (NFRAG + NW - 1) / NW;  // fragments per wave
+  static_assert(NW % NRT == 0, "a wave's fragments share one row tile");
   extern __shared__ __attribute__((aligned(16))) char smem[];
 
-  const int cid = blockIdx.x;
+  const int cid = si.seg_lo + blockIdx.x;  // chunk in the packed order
   const int h = blockIdx.y;
   const int H = kp.H;
   const int tid = threadIdx.x;
   const int w = wave_id(), l = lane_id();
+  const int lr = l & 15, lg = l >> 4;
 
   // ---- which sequence and token range ----
   int n, ci;
@@ -408,120 +465,137 @@ __global__ __launch_bounds__(kIntraThreads, 4) void intra_chunk_kernel(KernelPtr
   const long long t0l = (long long)bos + (long long)(ci < 0 ? 0 : ci) * C;
   const int t0 = (int)(t0l < eos ? t0l : eos);
   const int len = clampi(eos - t0, 0, C);
-  char* blk = kp.ops + ((size_t)cid * H + h) * LY::kBytes;
+  char* blk = kp.ops + ((size_t)blockIdx.x * H + h) * LY::kBytes;
 
-  const in_t* qg = reinterpret_cast<const in_t*>(kp.q);
-  const in_t* kg = reinterpret_cast<const in_t*>(kp.k);
-  const in_t* vg = reinterpret_cast<const in_t*>(kp.v);
-  float* scan = reinterpret_cast<float*>(smem + L::oScan);
+  float* tot = reinterpret_cast<float*>(smem + L::oTot);
   float* beta_s = reinterpret_cast<float*>(smem + L::oBeta);
-  int* flag = reinterpret_cast<int*>(smem + L::oFlag);
-  typedef typename L::plain_t plain_t;
-  LdsPrecise<M> KbS(smem + L::oKbS, L::kKtTplain);
-  plain_t* VS = reinterpret_cast<plain_t*>(smem + L::oVS);
 
-  // ---- step 1: loads (all issued up front), cumulative decay ----
-  const bool active = tid < NCG * NRG;
-  const int cg = tid % NCG, rg = tid / NCG;
-  float gam[RPT][8], qv[RPT][8], kv[RPT][8];
-  in_t vv[8][RPT];  // V^T run: value column 8cg+e, tokens rg*RPT .. +RPT-1
-  if (active) {
+  // ---- this wave's fragments (surplus waves repeat the last one, without
+  // storing anything: their loads stay unconditional) ----
+  bool fv[FPW];
+  int fkb[FPW];
+  const int rt = (w % NRT);  // row tile shared by every fragment of this wave
+  const int r = 16 * rt + lr;
+  const bool rv = r < len;
 #pragma unroll
-    for (int p = 0; p < RPT; ++p) {
-      const int r = rg * RPT + p;
-      if (r < len) {
-        const size_t base = ((size_t)(t0 + r) * H + h) * D + 8 * cg;
-        load8(kp.g + base, gam[p]);
-        load8(qg + base, qv[p]);
-        load8(kg + base, kv[p]);
-        float vtmp[8];
-        load8(vg + base, vtmp);
-#pragma unroll
-        for (int e = 0; e < 8; ++e) vv[e][p] = (in_t)vtmp[e];
-      } else {
-#pragma unroll
-        for (int e = 0; e < 8; ++e) { gam[p][e] = 0.f; qv[p][e] = 0.f; kv[p][e] = 0.f; vv[e][p] = (in_t)0.f; }
-      }
-    }
+  for (int j = 0; j < FPW; ++j) {
+    const int f = w + NW * j;
+    fv[j] = f < NFRAG;
+    fkb[j] = (f < NFRAG ? f : NFRAG - NRT + rt) / NRT;
   }
-  for (int i = tid; i < KC; i += kIntraThreads) beta_s[i] = (i < len) ? kp.beta[(size_t)(t0 + i) * H + h] : 0.f;
-  if (tid == 0) *flag = 0;
-  if (active) {
-#pragma unroll
-    for (int p = 1; p < RPT; ++p)
-#pragma unroll
-      for (int e = 0; e < 8; ++e) gam[p][e] += gam[p - 1][e];
-#pragma unroll
-    for (int e = 0; e < 8; ++e) scan[rg * D + 8 * cg + e] = gam[RPT - 1][e];
-  }
-  __syncthreads();
-  float last[8];
-  if (active) {
-    float off[8];
-#pragma unroll
-    for (int e = 0; e < 8; ++e) { off[e] = 0.f; last[e] = 0.f; }
-    // Partial unrolling only: a fully unrolled loop would hoist every
-    // load of the scan table into registers.
-#pragma unroll 2
-    for (int j = 0; j < NRG; ++j) {
-      const f32x4 s0 = *reinterpret_cast<const f32x4*>(scan + j * D + 8 * cg);
-      const f32x4 s1 = *reinterpret_cast<const f32x4*>(scan + j * D + 8 * cg + 4);
-      const float m = j < rg ? 1.f : 0.f;
-#pragma unroll
-      for (int e = 0; e < 4; ++e) {
-        off[e] += m * s0[e];
-        off[4 + e] += m * s1[e];
-        last[e] += s0[e];
-        last[4 + e] += s1[e];
-      }
-    }
-    bool big = false;
-#pragma unroll
-    for (int e = 0; e < 8; ++e) big |= (last[e] < -kSpanLimit);
-    if (big) atomicOr(flag, 1);
-#pragma unroll
-    for (int p = 0; p < RPT; ++p)
-#pragma unroll
-      for (int e = 0; e < 8; ++e) gam[p][e] += off[e];
-  }
-  __syncthreads();
-  const bool fast = (*flag == 0);
+  const bool any_frag = fv[0];
 
-  // ---- decayed operands.  Q*gam and K*exp(Gamma_n - Gamma) go straight to
-  // their global fragments; K*gam and K/gam stay in registers.
-  float kt[RPT][8], kh[RPT][8];
-  if (active) {
-    if (rg == 0) {
+  // ---- step 1: loads, all issued up front (rows past the chunk re-read a
+  // valid row and are zeroed at use) ----
+  const int tok = clampi(t0 + (r < len ? r : len - 1), 0, si.total_tokens - 1);
+  Raw8<float> graw[FPW];
+  Raw8<in_t> qraw[FPW], kraw[FPW], vraw[FPW];
 #pragma unroll
-      for (int e = 0; e < 8; ++e) reinterpret_cast<float*>(blk + LY::kGam)[8 * cg + e] = __expf(last[e]);
-    }
-    float kb[8][RPT];
+  for (int j = 0; j < FPW; ++j) {
+    const size_t base = ((size_t)tok * H + h) * D + 32 * fkb[j] + 8 * lg;
+    graw[j].load(kp.g + base);
+    qraw[j].load(reinterpret_cast<const in_t*>(kp.q) + base);
+    kraw[j].load(reinterpret_cast<const in_t*>(kp.k) + base);
+    vraw[j].load(reinterpret_cast<const in_t*>(kp.v) + base);
+  }
+  if (tid < KC) {
+    const int tb = clampi(t0 + (tid < len ? tid : 0), 0, si.total_tokens - 1);
+    const float bv = kp.beta[(size_t)tb * H + h];
+    beta_s[tid] = tid < len ? bv : 0.f;
+  }
+
+  // ---- step 2: cumulative decay.  Inclusive scan over the 16 tokens of the
+  // tile (lanes lr of one lane group), then the totals of earlier tiles ----
+  float G[FPW][8];
 #pragma unroll
-    for (int p = 0; p < RPT; ++p) {
-      const int r = rg * RPT + p;
-#pragma unroll
-      for (int e = 0; e < 8; ++e) {
-        const float ep = __expf(gam[p][e]);
-        qv[p][e] *= ep;                                   // now Q * gam
-        kt[p][e] = kv[p][e] * ep;
-        kh[p][e] = fast ? kv[p][e] * __expf(-gam[p][e]) : 0.f;
-        kb[e][p] = kv[p][e] * __expf(last[e] - gam[p][e]);
-      }
-      // Q*gam fragment: row r, k = 8cg..8cg+7 -> fragment (r/16, cg/4), lane (r%16)+16(cg%4).
-      gst_pfrag8(M{}, blk + LY::kQt + ((size_t)(r / 16) * NKD + cg / 4) * LY::PF,
-                 (r % 16) + 16 * (cg % 4), qv[p]);
-    }
-    // K-bar^T and V^T go to LDS transposed (row = channel c = 8cg+e, k =
-    // tokens rg*RPT .. +RPT-1), then out as whole fragments below: storing
-    // these short transposed runs straight to memory costs far more.
-    const int r0 = rg * RPT;
+  for (int j = 0; j < FPW; ++j)
 #pragma unroll
     for (int e = 0; e < 8; ++e) {
-      const int c = 8 * cg + e;
-      KbS.template storeN<RPT>(c * SK + r0, kb[e]);
+      float x = rv ? graw[j].get(e) : 0.f;
 #pragma unroll
-      for (int p = 0; p < RPT; ++p) VS[c * SK + r0 + p] = vv[e][p];
+      for (int d = 1; d < 16; d <<= 1) {
+        const float t = __shfl_up(x, d, 16);
+        x += lr >= d ? t : 0.f;
+      }
+      G[j][e] = x;
     }
+  if (lr == 15) {
+#pragma unroll
+    for (int j = 0; j < FPW; ++j)
+      if (fv[j]) {
+        f32x4 a = {G[j][0], G[j][1], G[j][2], G[j][3]}, b = {G[j][4], G[j][5], G[j][6], G[j][7]};
+        *reinterpret_cast<f32x4*>(tot + rt * D + 32 * fkb[j] + 8 * lg) = a;
+        *reinterpret_cast<f32x4*>(tot + rt * D + 32 * fkb[j] + 8 * lg + 4) = b;
+      }
+  }
+  __syncthreads();  // B1: tile totals, beta
+  float Gn[FPW][8];
+#pragma unroll
+  for (int j = 0; j < FPW; ++j)
+#pragma unroll
+    for (int e = 0; e < 8; ++e) Gn[j][e] = 0.f;
+#pragma unroll
+  for (int t = 0; t < NRT; ++t) {
+#pragma unroll
+    for (int j = 0; j < FPW; ++j) {
+      const f32x4 a = *reinterpret_cast<const f32x4*>(tot + t * D + 32 * fkb[j] + 8 * lg);
+      const f32x4 b = *reinterpret_cast<const f32x4*>(tot + t * D + 32 * fkb[j] + 8 * lg + 4);
+      const float m = t < rt ? 1.f : 0.f;
+#pragma unroll
+      for (int e = 0; e < 4; ++e) {
+        G[j][e] += m * a[e];
+        G[j][4 + e] += m * b[e];
+        Gn[j][e] += a[e];
+        Gn[j][4 + e] += b[e];
+      }
+    }
+  }
+  // Span check over all channels (every wave reaches the same verdict).
+  bool big = false;
+  for (int c = l; c < D; c += 64) {
+    float s = 0.f;
+#pragma unroll
+    for (int t = 0; t < NRT; ++t) s += tot[t * D + c];
+    big |= s < -kSpanLimit;
+  }
+  const bool fast = !__any(big);
+
+  // ---- step 3: decayed operands.  Q*gam leaves as whole fragments; K*gam
+  // and K/gam stay in registers; K-bar^T and V^T are staged transposed ----
+  PFrag qtf[FPW], ktf[FPW], khf[FPW];
+  LdsPrecise<M> KbS(smem + L::oKbS, L::kStPlain);
+  plain_t* VS = reinterpret_cast<plain_t*>(smem + L::oVS);
+#pragma unroll
+  for (int j = 0; j < FPW; ++j) {
+    float qt[8], kt[8], kh[8];
+#pragma unroll
+    for (int e = 0; e < 8; ++e) {
+      const float kv = rv ? kraw[j].get(e) : 0.f;
+      const float qv = rv ? qraw[j].get(e) : 0.f;
+      const float gm = __expf(G[j][e]);
+      qt[e] = qv * gm;
+      kt[e] = kv * gm;
+      kh[e] = fast ? kv * __expf(-G[j][e]) : 0.f;
+      const int c = 32 * fkb[j] + 8 * lg + e;
+      if (fv[j]) {
+        KbS.store(c * SK + r, kv * __expf(Gn[j][e] - G[j][e]));
+        VS[c * SK + r] = rv ? (plain_t)vraw[j].get(e) : (plain_t)0.f;
+      }
+    }
+    qtf[j] = make_pfrag(M{}, qt);
+    ktf[j] = make_pfrag(M{}, kt);
+    khf[j] = make_pfrag(M{}, kh);
+    if (fv[j]) st_pfrag(M{}, blk + LY::kQt + (size_t)(rt * NKD + fkb[j]) * LY::PF, qtf[j]);
+  }
+  if (any_frag && rt == 0 && lr == 0) {
+    // gam_n: channels 32 kb + 8 lg .. + 7 of each fragment of row tile 0
+#pragma unroll
+    for (int j = 0; j < FPW; ++j)
+      if (fv[j]) {
+#pragma unroll
+        for (int e = 0; e < 8; ++e)
+          reinterpret_cast<float*>(blk + LY::kGam)[32 * fkb[j] + 8 * lg + e] = __expf(Gn[j][e]);
+      }
   }
   if (KC > C) {  // zero the padded tokens
     for (int idx = tid; idx < D * (KC - C); idx += kIntraThreads) {
@@ -530,158 +604,151 @@ __global__ __launch_bounds__(kIntraThreads, 4) void intra_chunk_kernel(KernelPtr
       VS[c * SK + i] = (plain_t)0.f;
     }
   }
-  __syncthreads();
-  // Fragment (channel tile rt, token block kb): lane l reads row 16rt + (l&15),
+  __syncthreads();  // B2: staging complete
+  // Fragment (channel tile ct, token block kb): lane l reads row 16ct + (l&15),
   // tokens 32kb + 8(l>>4) .. +7, and stores them as one contiguous slot.
   for (int f = w; f < NDT * NKC; f += NW) {
-    const int rt = f / NKC, kb = f % NKC;
-    st_pfrag(M{}, blk + LY::kKb + (size_t)f * LY::PF, KbS.pfrag(SK, 16 * rt, 32 * kb));
-    st_frag(M{}, blk + LY::kV + (size_t)f * LY::FF, lds_frag(M{}, VS, SK, 16 * rt, 32 * kb));
+    const int ct = f / NKC, kb = f % NKC;
+    st_pfrag(M{}, blk + LY::kKb + (size_t)f * LY::PF, KbS.pfrag(SK, 16 * ct, 32 * kb));
+    st_frag(M{}, blk + LY::kV + (size_t)f * LY::FF, lds_frag(M{}, VS, SK, 16 * ct, 32 * kb));
   }
-  __syncthreads();  // the Gram operands reuse this region
+  __syncthreads();  // B3: staging regions free
 
-  // ---- step 2: Grams A and P ----
-  f32x4 accA[TPW], accP[TPW];
-#pragma unroll
-  for (int s = 0; s < TPW; ++s) { accA[s] = f32x4{0, 0, 0, 0}; accP[s] = accA[s]; }
-  if (fast) {
-    LdsPrecise<M> Qh(smem + L::oQt, L::kHalfPlain);
-    LdsPrecise<M> Kth(smem + L::oKt, L::kHalfPlain);
-    LdsPrecise<M> Khh(smem + L::oKh, L::kHalfPlain);
-#pragma unroll
-    for (int half = 0; half < L::NHALF; ++half) {
-      if (active && (cg * 8) / L::DH == half) {
-        const int c0 = 8 * cg - half * L::DH;
-#pragma unroll
-        for (int p = 0; p < RPT; ++p) {
-          const int r = rg * RPT + p;
-          Qh.template storeN<8>(r * SH + c0, qv[p]);
-          Kth.template storeN<8>(r * SH + c0, kt[p]);
-          Khh.template storeN<8>(r * SH + c0, kh[p]);
-        }
-      }
-      __syncthreads();
-#pragma unroll
-      for (int s = 0; s < TPW; ++s) {
-        const int t = w + NW * s;
-        if (t < NTILE) {
-          int a, b;
-          tile_ab(t, a, b);
-#pragma unroll
-          for (int kb = 0; kb < L::DH / 32; ++kb) {
-            const auto khf = Khh.pfrag(SH, 16 * b, 32 * kb);
-            accP[s] = mma_pp(Qh.pfrag(SH, 16 * a, 32 * kb), khf, accP[s]);
-            accA[s] = mma_pp(Kth.pfrag(SH, 16 * a, 32 * kb), khf, accA[s]);
-          }
-        }
-      }
-      __syncthreads();  // the next half (or phase B) overwrites the operands
-    }
-  } else {
-    // Strong decay: exact pairwise evaluation.  Gamma goes to LDS; thread tid
-    // owns row r = tid / 8 and columns i = tid % 8, +8, ... <= r.
-    float* Gs = reinterpret_cast<float*>(smem + L::oG);
-    if (active) {
-#pragma unroll
-      for (int p = 0; p < RPT; ++p)
-#pragma unroll
-        for (int e = 0; e < 8; ++e) Gs[(rg * RPT + p) * L::SG + 8 * cg + e] = gam[p][e];
-    }
-    __syncthreads();
-  }
+  // ---- step 4: Grams A and P ----
   float* As = reinterpret_cast<float*>(smem + L::oA);
   float* Ps = reinterpret_cast<float*>(smem + L::oP);
-  float* Xs = reinterpret_cast<float*>(smem + L::oX);
-  float* Ysc = reinterpret_cast<float*>(smem + L::oY);
-  constexpr int NPAIR = (C + 7) / 8;  // columns per thread in the pairwise path
-  float pa[NPAIR], pp[NPAIR];
-  if (!fast) {
-    const float* Gs = reinterpret_cast<const float*>(smem + L::oG);
-    const int r = tid >> 3;
-#pragma unroll
-    for (int m = 0; m < NPAIR; ++m) { pa[m] = 0.f; pp[m] = 0.f; }
-    if (r < len) {
-#pragma unroll
-      for (int m = 0; m < NPAIR; ++m) {
-        const int i = (tid & 7) + 8 * m;
-        if (i <= r) {
-          float sa = 0.f, sp = 0.f;
-          for (int c = 0; c < D; ++c) {
-            const float kr = (float)kg[((size_t)(t0 + r) * H + h) * D + c];
-            const float ki = (float)kg[((size_t)(t0 + i) * H + h) * D + c];
-            const float qr = (float)qg[((size_t)(t0 + r) * H + h) * D + c];
-            const float ex = __expf(Gs[r * L::SG + c] - Gs[i * L::SG + c]);
-            sa += kr * ki * ex;
-            sp += qr * ki * ex;
-          }
-          pa[m] = sa;
-          pp[m] = sp;
-        }
-      }
-    }
-    __syncthreads();  // Gamma reads done before A/P overwrite it
-  }
-  // ---- A (strictly lower, times beta_r), P (lower), X cleared ----
-  for (int idx = tid; idx < C * KC; idx += kIntraThreads) {
-    const int r = idx / KC, i = idx % KC;
-    As[r * SF + i] = 0.f;
-    Ps[r * SF + i] = 0.f;
-    Xs[r * SF + i] = 0.f;
-  }
-  __syncthreads();
+  for (int idx = 4 * tid; idx < 2 * (int)(L::kFMat / 4); idx += 4 * kIntraThreads)
+    *reinterpret_cast<f32x4*>(As + idx) = f32x4{0, 0, 0, 0};  // A and P are adjacent
   if (fast) {
 #pragma unroll
-    for (int s = 0; s < TPW; ++s) {
-      const int t = w + NW * s;
-      if (t < NTILE) {
-        int a, b;
-        tile_ab(t, a, b);
-        const int i = 16 * b + (l & 15);
+    for (int j = 0; j < FPW; ++j)
+      if (fv[j]) lds_st_pfrag(M{}, smem + L::oKh + (size_t)(rt * NKD + fkb[j]) * LY::PF, khf[j]);
+  } else {
+    float* Gs = reinterpret_cast<float*>(smem + L::oG);
 #pragma unroll
-        for (int x = 0; x < 4; ++x) {
-          const int r = 16 * a + 4 * (l >> 4) + x;
-          if (i < r) As[r * SF + i] = beta_s[r] * accA[s][x];
-          if (i <= r) Ps[r * SF + i] = accP[s][x];
+    for (int j = 0; j < FPW; ++j)
+      if (fv[j]) {
+#pragma unroll
+        for (int e = 0; e < 8; ++e) Gs[r * SG + 32 * fkb[j] + 8 * lg + e] = G[j][e];
+      }
+  }
+  __syncthreads();  // B4: K/gam fragments (or Gamma), zeroed A and P
+  // Partial Grams over this wave's channel blocks for every tile b <= rt.
+  // The NC waves that share a row tile add their parts into A and P in turn,
+  // one barrier apart (LDS float atomics are far slower).
+  constexpr int NC = (NFRAG < NW ? NFRAG : NW) / NRT;
+  f32x4 accA[NRT], accP[NRT];
+#pragma unroll
+  for (int b = 0; b < NRT; ++b) { accA[b] = f32x4{0, 0, 0, 0}; accP[b] = accA[b]; }
+  if (fast) {
+    if (any_frag) {
+#pragma unroll
+      for (int b = 0; b < NRT; ++b) {
+        if (b > rt) break;
+#pragma unroll
+        for (int j = 0; j < FPW; ++j) {
+          if (!fv[j]) continue;
+          const PFrag kbf = ld_pfrag(M{}, smem + L::oKh + (size_t)(b * NKD + fkb[j]) * LY::PF);
+          accP[b] = mma_pp(qtf[j], kbf, accP[b]);
+          accA[b] = mma_pp(ktf[j], kbf, accA[b]);
         }
       }
     }
   } else {
-    const int r = tid >> 3;
-    if (r < C) {
-#pragma unroll
-      for (int m = 0; m < NPAIR; ++m) {
-        const int i = (tid & 7) + 8 * m;
-        if (i <= r && r < len) {
-          if (i < r) As[r * SF + i] = beta_s[r] * pa[m];
-          Ps[r * SF + i] = pp[m];
+    // Strong decay: exact pairwise evaluation.  Thread tid owns row
+    // rr = tid / 8 and columns i = tid % 8, +8, ... <= rr.
+    const float* Gs = reinterpret_cast<const float*>(smem + L::oG);
+    const in_t* qg = reinterpret_cast<const in_t*>(kp.q);
+    const in_t* kg = reinterpret_cast<const in_t*>(kp.k);
+    const int rr = tid >> 3;
+    if (rr < len) {
+      for (int i = tid & 7; i <= rr; i += 8) {
+        float sa = 0.f, sp = 0.f;
+        for (int c = 0; c < D; ++c) {
+          const float kr = (float)kg[((size_t)(t0 + rr) * H + h) * D + c];
+          const float ki = (float)kg[((size_t)(t0 + i) * H + h) * D + c];
+          const float qr = (float)qg[((size_t)(t0 + rr) * H + h) * D + c];
+          const float ex = __expf(Gs[rr * SG + c] - Gs[i * SG + c]);
+          sa += kr * ki * ex;
+          sp += qr * ki * ex;
         }
+        if (i < rr) As[rr * SF + i] = beta_s[rr] * sa;
+        Ps[rr * SF + i] = sp;
       }
     }
   }
-  __syncthreads();
+  float brow[4];
+#pragma unroll
+  for (int x = 0; x < 4; ++x) brow[x] = beta_s[16 * rt + 4 * lg + x];
+  const int cix = w / NRT;  // this wave's turn among those sharing the row tile
+#pragma unroll
+  for (int c = 0; c < NC; ++c) {
+    if (fast && any_frag && cix == c) {
+      // all reads of earlier contributions first, then the writes
+      float po[NRT][4], ao[NRT][4];
+#pragma unroll
+      for (int b = 0; b < NRT; ++b)
+#pragma unroll
+        for (int x = 0; x < 4; ++x) {
+          const int rr = 16 * rt + 4 * lg + x, i = 16 * b + lr;
+          po[b][x] = (c > 0 && b <= rt) ? Ps[rr * SF + i] : 0.f;
+          ao[b][x] = (c > 0 && b <= rt) ? As[rr * SF + i] : 0.f;
+        }
+#pragma unroll
+      for (int b = 0; b < NRT; ++b) {
+        if (b > rt) break;
+        const int i = 16 * b + lr;
+#pragma unroll
+        for (int x = 0; x < 4; ++x) {
+          const int rr = 16 * rt + 4 * lg + x;
+          if (i <= rr) Ps[rr * SF + i] = accP[b][x] + po[b][x];
+          if (i < rr) As[rr * SF + i] = brow[x] * accA[b][x] + ao[b][x];
+        }
+      }
+    }
+    if (c + 1 < NC) __syncthreads();
+  }
+  __syncthreads();  // B5: A and P complete; R0 free
 
-  // ---- step 3: X = (I + A)^{-1} by blocked forward substitution ----
+  // ---- step 5: P fragments out; X = (I + A)^{-1} by blocked forward
+  // substitution ----
+  for (int f = w; f < NRT * NKC; f += NW) {
+    const int rr = 16 * (f / NKC) + lr, i0 = 32 * (f % NKC) + 8 * lg;
+    float pv[8];
+#pragma unroll
+    for (int e = 0; e < 8; ++e) pv[e] = Ps[rr * SF + i0 + e];
+    gst_pfrag8(M{}, blk + LY::kP + (size_t)f * LY::PF, l, pv);
+  }
+  float* Xs = reinterpret_cast<float*>(smem + L::oX);
+  float* Ysc = reinterpret_cast<float*>(smem + L::oY);
   if (w == 0) {
     // diagonal 16x16 blocks: lane = 16*block + column
-    const int bk = l >> 4, j = l & 15;
+    const int bk = lg, jc = lr;
     if (bk < NRT) {
       float x[16];
 #pragma unroll
-      for (int s = 0; s < 16; ++s) x[s] = (s == j) ? 1.f : 0.f;
+      for (int s = 0; s < 16; ++s) x[s] = (s == jc) ? 1.f : 0.f;
       const float* Ab = As + (16 * bk) * SF + 16 * bk;
+      // Column q of the block is read one elimination step ahead of its use;
+      // hoisting all 120 reads would cost as many registers.
+      float cur[16], nxt[16];
 #pragma unroll
-      for (int r = 0; r < 16; ++r) {
+      for (int s = 0; s < 16; ++s) { cur[s] = s > 0 ? Ab[s * SF] : 0.f; nxt[s] = 0.f; }
 #pragma unroll
-        for (int s = r + 1; s < 16; ++s) x[s] -= Ab[s * SF + r] * x[r];
-        // Keep each elimination step's LDS reads next to their use; hoisting
-        // all 120 of them would cost as many registers.
+      for (int q = 0; q < 16; ++q) {
+#pragma unroll
+        for (int s = q + 2; s < 16; ++s) nxt[s] = Ab[s * SF + q + 1];
+#pragma unroll
+        for (int s = q + 1; s < 16; ++s) x[s] -= cur[s] * x[q];
         __builtin_amdgcn_sched_barrier(0);
+#pragma unroll
+        for (int s = 0; s < 16; ++s) cur[s] = nxt[s];
       }
 #pragma unroll
-      for (int s = 0; s < 16; ++s) Xs[(16 * bk + s) * SF + 16 * bk + j] = x[s];
+      for (int s = 0; s < 16; ++s) Xs[(16 * bk + s) * SF + 16 * bk + jc] = x[s];
     }
   }
-  __syncthreads();
+  __syncthreads();  // B6
   // off-diagonal blocks, one level (a - b) at a time:
   //   X_ab = -X_aa * sum_{m=b}^{a-1} A_am X_mb
 #pragma unroll
@@ -693,105 +760,124 @@ __global__ __launch_bounds__(kIntraThreads, 4) void intra_chunk_kernel(KernelPtr
       for (int m = b; m < a; ++m) y = prod16(M{}, y, As, SF, 16 * a, 16 * m, Xs, SF, 16 * m, 16 * b);
       float* Yw = Ysc + w * 16 * 17;
 #pragma unroll
-      for (int x = 0; x < 4; ++x) Yw[(4 * (l >> 4) + x) * 17 + (l & 15)] = y[x];
+      for (int x = 0; x < 4; ++x) Yw[(4 * lg + x) * 17 + lr] = y[x];
+      // Yw is this wave's own scratch: wait for its writes, no block barrier.
+      __builtin_amdgcn_s_waitcnt(0xC07F);  // lgkmcnt(0)
+      __builtin_amdgcn_wave_barrier();
     }
-    __syncthreads();
     if (mine) {
       f32x4 xab = {0, 0, 0, 0};
       xab = prod16(M{}, xab, Xs, SF, 16 * a, 16 * a, Ysc + w * 16 * 17, 17, 0, 0);
 #pragma unroll
-      for (int x = 0; x < 4; ++x) Xs[(16 * a + 4 * (l >> 4) + x) * SF + 16 * b + (l & 15)] = -xab[x];
+      for (int x = 0; x < 4; ++x) Xs[(16 * a + 4 * lg + x) * SF + 16 * b + lr] = -xab[x];
     }
     __syncthreads();
   }
 
-  // ---- step 4: T = X Diag(beta) and P fragments (fragment (rt, kb)) ----
+  // ---- step 6: T = X Diag(beta) (lower triangle) out, and kept in LDS
+  // (over the solve scratch) for the W product; (K*gam)^T staged ----
   for (int f = w; f < NRT * NKC; f += NW) {
-    const int r = 16 * (f / NKC) + (l & 15), i0 = 32 * (f % NKC) + 8 * (l >> 4);
-    float tv[8], pv[8];
+    const int rr = 16 * (f / NKC) + lr, i0 = 32 * (f % NKC) + 8 * lg;
+    float tv[8];
 #pragma unroll
-    for (int e = 0; e < 8; ++e) {
-      tv[e] = Xs[r * SF + i0 + e] * beta_s[i0 + e];
-      pv[e] = Ps[r * SF + i0 + e];
-    }
-    gst_pfrag8(M{}, blk + LY::kT + (size_t)f * LY::PF, l, tv);
-    gst_pfrag8(M{}, blk + LY::kP + (size_t)f * LY::PF, l, pv);
+    for (int e = 0; e < 8; ++e) tv[e] = i0 + e <= rr ? Xs[rr * SF + i0 + e] * beta_s[i0 + e] : 0.f;
+    const PFrag tf = make_pfrag(M{}, tv);
+    st_pfrag(M{}, blk + LY::kT + (size_t)f * LY::PF, tf);
+    lds_st_pfrag(M{}, smem + L::oTf + (size_t)f * LY::PF, tf);
   }
-  __syncthreads();  // A and P are dead; K*gam^T may overwrite them
-  LdsPrecise<M> KtT(smem + L::oKtT, L::kKtTplain);
-  if (active) {
+  LdsPrecise<M> KtT(smem + L::oKtT, L::kStPlain);
 #pragma unroll
-    for (int e = 0; e < 8; ++e) {
-      float run[RPT];
+  for (int j = 0; j < FPW; ++j)
+    if (fv[j]) {
 #pragma unroll
-      for (int p = 0; p < RPT; ++p) run[p] = kt[p][e];
-      KtT.template storeN<RPT>((8 * cg + e) * SK + rg * RPT, run);
+      for (int e = 0; e < 8; ++e) KtT.put((32 * fkb[j] + 8 * lg + e) * SK + r, ktf[j], e);
     }
-  }
   if (KC > C) {
     for (int idx = tid; idx < D * (KC - C); idx += kIntraThreads) {
       const int c = idx / (KC - C), i = C + idx % (KC - C);
       KtT.store(c * SK + i, 0.f);
     }
   }
-  __syncthreads();
-  // ---- W^T = (K*gam)^T T^T, tile (channel tile ct, token tile rt).  The
-  // accumulator lane l holds W[16rt + (l&15)][16ct + 4(l>>4) + x], which is
-  // four consecutive k values of one lane slot of the W fragment (rt, ct/2).
-  for (int t = w; t < NRT * NDT; t += NW) {
-    const int rt = t / NDT, ct = t % NDT;
-    f32x4 acc = {0, 0, 0, 0};
+  __syncthreads();  // B: (K*gam)^T staged
+
+  // ---- step 7: W^T = (K*gam)^T T^T for a pair of channel tiles (one W
+  // fragment column block) and one token tile.  Accumulator lane (lg, lr)
+  // holds four channels 4lg.. of token lr; lanes lg and lg^1 swap halves so
+  // each ends with eight consecutive channels of one token: one lane slot
+  // of the W fragment, written as a whole ----
+  for (int u = w; u < (NDT / 2) * NRT; u += NW) {
+    const int cp = u % (NDT / 2), wt = u / (NDT / 2);
+    f32x4 acc0 = {0, 0, 0, 0}, acc1 = {0, 0, 0, 0};
 #pragma unroll
     for (int kb = 0; kb < NKC; ++kb) {
-      if (32 * kb > 16 * rt + 15) break;
-      const int r = 16 * rt + (l & 15), i0 = 32 * kb + 8 * (l >> 4);
-      float tv[8];
-#pragma unroll
-      for (int e = 0; e < 8; ++e) tv[e] = Xs[r * SF + i0 + e] * beta_s[i0 + e];
-      acc = mma_pp(KtT.pfrag(SK, 16 * ct, 32 * kb), make_pfrag(M{}, tv), acc);
+      if (32 * kb > 16 * wt + 15) break;
+      const PFrag tf = ld_pfrag(M{}, smem + L::oTf + (size_t)(wt * NKC + kb) * LY::PF);
+      acc0 = mma_pp(KtT.pfrag(SK, 32 * cp, 32 * kb), tf, acc0);
+      acc1 = mma_pp(KtT.pfrag(SK, 32 * cp + 16, 32 * kb), tf, acc1);
     }
-    const int q4 = l >> 4;
-    const int lane_w = (l & 15) + 16 * (2 * (ct & 1) + (q4 >> 1));
-    float wv[4] = {acc[0], acc[1], acc[2], acc[3]};
-    gst_pfrag_run<4>(M{}, blk + LY::kW + ((size_t)rt * NKD + ct / 2) * LY::PF, lane_w,
-                     4 * (q4 & 1), wv);
+    const bool even = (lg & 1) == 0;
+    float wv[8];
+#pragma unroll
+    for (int x = 0; x < 4; ++x) {
+      const float recv = __shfl_xor(even ? acc1[x] : acc0[x], 16);
+      wv[x] = even ? acc0[x] : recv;
+      wv[4 + x] = even ? recv : acc1[x];
+    }
+    // lane group lg -> k-group {0, 2, 1, 3}[lg] of the fragment
+    const int kgrp = ((lg & 1) << 1) | (lg >> 1);
+    gst_pfrag8(M{}, blk + LY::kW + (size_t)(wt * NKD + cp) * LY::PF, lr + 16 * kgrp, wv);
   }
 }
 
 // ---------------------------------------------------------------------------
-// Inter-chunk kernel: one workgroup per (sequence, head, block of value columns).
+// Inter-chunk kernel: one workgroup per (sequence, head, block of value
+// columns), 512 threads in two roles that share the chunk loop:
+//
+//   U-waves (0..3) carry the state.  Wave w owns row tile w of U and the
+//     NST state row tiles NST*w ..; per chunk it forms U = T V - W S,
+//     publishes U^T in LDS, then updates its state tiles
+//     S <- Diag(gam_n) S + K-bar^T U and publishes S^T in LDS.
+//   O-waves (4..7) produce the output.  Wave 4 + r forms Q*gam S for row
+//     tile r from the published state, then O = Q*gam S + P U from the
+//     published U, and stores it.  They also pull the chunk blocks a few
+//     chunks ahead into L2.
+//
+// Each SIMD runs one wave of each role, so one wave's operand loads overlap
+// the other's matrix products; the two roles split the per-chunk operands
+// (U-waves: W, T, V^T, K-bar^T, gam_n; O-waves: Q*gam, P).
 // ---------------------------------------------------------------------------
-// Operands of one chunk, as held by one wave.  The phase-1 group (W, Q*gam,
-// T, V^T) feeds U = T V - W S and Q*gam S; the phase-2 group (P, K-bar^T,
-// gam_n) feeds the output and the state update.
+constexpr int kInterThreads = 512;
+constexpr int kPrefetchAhead = 4;  // chunks between the L2 probe and use
+
 template <class M, int D, int C, int NCT>
-struct ChunkFrags {
+struct UFrags {
   typedef Layout<M, D, C> LY;
-  static constexpr int NST = LY::NDT / 4 > 0 ? LY::NDT / 4 : 1;  // state tiles per wave
+  static constexpr int NST = LY::NDT / 4;  // state tiles per U-wave
   typename M::PFrag W[LY::NKD];
-  typename M::PFrag Qt[LY::NKD];
   typename M::PFrag Tm[LY::NKC];
   typename M::Frag V[NCT][LY::NKC];
-  typename M::PFrag P[LY::NKC];
   typename M::PFrag Kb[NST][LY::NKC];
   float gam[NST][4];
 };
 
-template <class M, int D, int C, int NCT>
-__device__ __forceinline__ void load_frags_phase1(ChunkFrags<M, D, C, NCT>& f, const char* blk, int w,
-                                                  int vt0) {
+template <class M, int D, int C>
+struct OFrags {
   typedef Layout<M, D, C> LY;
-  // Every wave issues the same loads.  With fewer than four row tiles the
-  // waves past the last one re-read it (their products are skipped): a load
-  // that only some waves issue leaves the compiler's count of outstanding
-  // loads wrong for the others, and a wait can then pass before the data
-  // it guards has arrived.
-  const int rt = LY::NRT == 4 ? w : min(w, LY::NRT - 1);
+  typename M::PFrag Qt[LY::NKD];
+  typename M::PFrag P[LY::NKC];
+  float probe;
+};
+
+// Every wave of a role issues the same loads.  With fewer than four row
+// tiles the surplus waves re-read the last one (and skip its products): a
+// load that only some paths issue leaves the compiler's count of outstanding
+// loads wrong, and a later wait can pass before its data has arrived.
+template <class M, int D, int C, int NCT>
+__device__ __forceinline__ void load_u1(UFrags<M, D, C, NCT>& f, const char* blk, int rt, int vt0) {
+  typedef Layout<M, D, C> LY;
 #pragma unroll
-  for (int kb = 0; kb < LY::NKD; ++kb) {
+  for (int kb = 0; kb < LY::NKD; ++kb)
     f.W[kb] = ld_pfrag(M{}, blk + LY::kW + (size_t)(rt * LY::NKD + kb) * LY::PF);
-    f.Qt[kb] = ld_pfrag(M{}, blk + LY::kQt + (size_t)(rt * LY::NKD + kb) * LY::PF);
-  }
 #pragma unroll
   for (int kb = 0; kb < LY::NKC; ++kb) {
     f.Tm[kb] = ld_pfrag(M{}, blk + LY::kT + (size_t)(rt * LY::NKC + kb) * LY::PF);
@@ -800,18 +886,11 @@ __device__ __forceinline__ void load_frags_phase1(ChunkFrags<M, D, C, NCT>& f, c
       f.V[ct][kb] = ld_frag(M{}, blk + LY::kV + (size_t)((vt0 + ct) * LY::NKC + kb) * LY::FF);
   }
 }
-
 template <class M, int D, int C, int NCT>
-__device__ __forceinline__ void load_frags_phase2(ChunkFrags<M, D, C, NCT>& f, const char* blk, int w) {
+__device__ __forceinline__ void load_u2(UFrags<M, D, C, NCT>& f, const char* blk, int w) {
   typedef Layout<M, D, C> LY;
-  constexpr int NST = ChunkFrags<M, D, C, NCT>::NST;
+  constexpr int NST = UFrags<M, D, C, NCT>::NST;
   const int l = lane_id();
-  // Unconditional for every wave, as in load_frags_phase1.
-  const int rt = LY::NRT == 4 ? w : min(w, LY::NRT - 1);
-#pragma unroll
-  for (int kb = 0; kb < LY::NKC; ++kb)
-    f.P[kb] = ld_pfrag(M{}, blk + LY::kP + (size_t)(rt * LY::NKC + kb) * LY::PF);
-  static_assert(LY::NDT == 4 * NST, "every wave owns NST state tiles");
 #pragma unroll
   for (int s = 0; s < NST; ++s) {
     const int st = w * NST + s;
@@ -823,6 +902,20 @@ __device__ __forceinline__ void load_frags_phase2(ChunkFrags<M, D, C, NCT>& f, c
 #pragma unroll
     for (int x = 0; x < 4; ++x) f.gam[s][x] = gv[x];
   }
+}
+template <class M, int D, int C>
+__device__ __forceinline__ void load_o1(OFrags<M, D, C>& f, const char* blk, int rt) {
+  typedef Layout<M, D, C> LY;
+#pragma unroll
+  for (int kb = 0; kb < LY::NKD; ++kb)
+    f.Qt[kb] = ld_pfrag(M{}, blk + LY::kQt + (size_t)(rt * LY::NKD + kb) * LY::PF);
+}
+template <class M, int D, int C>
+__device__ __forceinline__ void load_o2(OFrags<M, D, C>& f, const char* blk, int rt) {
+  typedef Layout<M, D, C> LY;
+#pragma unroll
+  for (int kb = 0; kb < LY::NKC; ++kb)
+    f.P[kb] = ld_pfrag(M{}, blk + LY::kP + (size_t)(rt * LY::NKC + kb) * LY::PF);
 }
 
 template <class M, int D, int C, int NCT>
@@ -839,53 +932,40 @@ struct InterLds {
   static constexpr size_t kTotal = oUT + (M::kSplit ? 2 : 1) * kUTplain;
 };
 
-// NCT = number of 16-column value tiles per workgroup (16, 32 or 64 columns).
-// Every wave applies each operand fragment it loads to all NCT tiles, so a
-// wider block divides the per-chunk operand traffic among fewer workgroups.
-//
-// Pipeline: two operand sets alternate between even and odd chunks.  After
-// phase 1 of chunk c its set receives the phase-1 group of chunk c+2, and
-// after phase 2 the other set receives the phase-2 group of chunk c+1.  That
-// keeps about 55 loads per wave in flight, inside the 63-entry vmcnt range.
-template <class M, int D, int C, int NCT, bool OUT_BF16>
-__global__ __launch_bounds__(256) void inter_chunk_kernel(KernelPtrs kp, SeqInfo si, int num_pairs) {
+// Geometry of one inter-chunk workgroup.  This launch runs the sequence's
+// chunks [ci_lo, ci_hi); chunk ci's operand block is number cbase + ci of
+// the segment.  The state enters from s_in (nullptr = zeros) and leaves to
+// s_out (nullptr = not written).
+struct InterGeom {
+  int n, h, H, bos, eos, nch, col0, vb;
+  int ci_lo, ci_hi, cbase;
+  const float* s_in;
+  float* s_out;
+};
+
+// Pipeline (both roles): two operand sets alternate between even and odd
+// chunks.  After phase 1 of chunk c its set receives the phase-1 group of
+// chunk c+2; after phase 2 the other set receives the phase-2 group of chunk
+// c+1.  Loads past the last chunk re-read it: they stay unconditional.
+template <class M, int D, int C, int NCT>
+__device__ __forceinline__ void inter_u_role(const KernelPtrs& kp, const InterGeom& gm, char* smem,
+                                             int w) {
   typedef Layout<M, D, C> LY;
   typedef InterLds<M, D, C, NCT> L;
-  typedef ChunkFrags<M, D, C, NCT> CF;
-  constexpr int NRT = LY::NRT, KC = LY::KC, NKC = LY::NKC, NKD = LY::NKD, NDT = LY::NDT;
-  constexpr int NST = CF::NST;
-  constexpr int DVB = L::DVB;
-  constexpr int NVB = D / DVB;
+  typedef UFrags<M, D, C, NCT> UF;
+  constexpr int NRT = LY::NRT, NKC = LY::NKC, NKD = LY::NKD, NDT = LY::NDT;
+  constexpr int NST = UF::NST;
   constexpr int SD = L::SD, SK = L::SK;
-  __shared__ __attribute__((aligned(16))) char smem[L::kTotal];
-
-  // XCD-aware mapping: consecutive block ids rotate over the 8 XCDs, so the
-  // NVB column blocks of one (sequence, head) are given ids that land on the
-  // same XCD and share its L2 for the per-chunk operands.
-  const int bid = blockIdx.x;
-  const int xcd = bid & 7, slot = bid >> 3;
-  const int pair = (slot / NVB) * 8 + xcd;
-  const int vb = slot % NVB;
-  if (pair >= num_pairs) return;
-  const int H = kp.H;
-  const int n = pair / H, h = pair % H;
-  const int tid = threadIdx.x, w = wave_id(), l = lane_id();
-  const int col0 = DVB * vb;  // first value column of this block
-
-  int bos, eos;
-  seq_bounds(si, n, bos, eos);
-  const int cid0 = si.cu ? clampi(si.chunk_off[n], 0, si.total_chunks)
-                         : n * chunks_of<C>(si.seq_len);
-  // Never walk past the chunks the workspace was sized for.
-  const int nch = min(chunks_of<C>(eos - bos), si.total_chunks - cid0);
-
+  static_assert(NDT == 4 * NST, "every U-wave owns NST state tiles");
+  const int l = lane_id();
   LdsPrecise<M> ST(smem + L::oST, L::kSTplain);
   LdsPrecise<M> UT(smem + L::oUT, L::kUTplain);
+  const int rt = NRT == 4 ? w : min(w, NRT - 1);
+  const bool act = NRT == 4 || w < NRT;
+  const int vt0 = gm.col0 / 16;
 
-  // ---- state block in accumulator layout: tile (st, ct) holds rows
-  // 16st.., columns col0 + 16ct.. ----
   f32x4 S[NST][NCT];
-  const size_t sbase = ((size_t)n * H + h) * D * D;
+  const size_t sbase = ((size_t)gm.n * gm.H + gm.h) * D * D;
 #pragma unroll
   for (int s = 0; s < NST; ++s) {
     const int st = w * NST + s;
@@ -894,54 +974,30 @@ __global__ __launch_bounds__(256) void inter_chunk_kernel(KernelPtrs kp, SeqInfo
 #pragma unroll
       for (int x = 0; x < 4; ++x) {
         const int c = 16 * st + 4 * (l >> 4) + x;
-        S[s][ct][x] = (kp.s0 && st < NDT)
-                          ? kp.s0[sbase + (size_t)c * D + col0 + 16 * ct + (l & 15)] : 0.f;
+        S[s][ct][x] = gm.s_in ? gm.s_in[sbase + (size_t)c * D + gm.col0 + 16 * ct + (l & 15)] : 0.f;
       }
   }
-  auto write_state_lds = [&]() {
+  auto publish_state = [&]() {
 #pragma unroll
     for (int s = 0; s < NST; ++s) {
       const int st = w * NST + s;
-      if (NDT == 4 * NST || st < NDT) {
 #pragma unroll
-        for (int ct = 0; ct < NCT; ++ct) {
-          float v4[4] = {S[s][ct][0], S[s][ct][1], S[s][ct][2], S[s][ct][3]};
-          ST.template storeN<4>((16 * ct + (l & 15)) * SD + 16 * st + 4 * (l >> 4), v4);
-        }
+      for (int ct = 0; ct < NCT; ++ct) {
+        float v4[4] = {S[s][ct][0], S[s][ct][1], S[s][ct][2], S[s][ct][3]};
+        ST.template storeN<4>((16 * ct + (l & 15)) * SD + 16 * st + 4 * (l >> 4), v4);
       }
     }
   };
-  write_state_lds();
-  // Zero the padded token columns of UT once (KC > C); nothing writes them.
-  if (KC > C) {
-    for (int idx = tid; idx < DVB * (KC - C); idx += 256) UT.store((idx / (KC - C)) * SK + C + idx % (KC - C), 0.f);
-  }
+  publish_state();
 
-  auto blk_of = [&](int ci) { return kp.ops + ((size_t)(cid0 + ci) * H + h) * LY::kBytes; };
-  const int vt0 = col0 / 16;  // first V^T fragment row tile of this block
-
-  // One chunk.  `f` holds chunk ci; `g` is the other set.  Fetches past the
-  // end re-read the last chunk: they stay unconditional, since a fetch under a
-  // branch makes the compiler drain every outstanding load where the paths
-  // join.
-  auto process = [&](CF& f, CF& g, int ci) {
-    const int t0 = bos + ci * C;
-    const int len = eos - t0 < C ? eos - t0 : C;
-    __syncthreads();  // ST ready
-    f32x4 qs[NCT];
+  auto blk_of = [&](int ci) { return kp.ops + ((size_t)(gm.cbase + ci) * gm.H + gm.h) * LY::kBytes; };
+  const int last = gm.ci_hi - 1;
+  auto step = [&](UF& f, UF& g, int ci) {
+    __syncthreads();  // S^T published; last chunk's U^T reads done
+    if (act) {
+      f32x4 u[NCT], ws[NCT];
 #pragma unroll
-    for (int ct = 0; ct < NCT; ++ct) qs[ct] = f32x4{0, 0, 0, 0};
-    if (NRT == 4 || w < NRT) {
-      // All B-operand fragments of this phase are read from LDS first, so
-      // their latency is paid once rather than in front of every product.
-      typename M::PFrag sf[NKD][NCT];
-#pragma unroll
-      for (int kb = 0; kb < NKD; ++kb)
-#pragma unroll
-        for (int ct = 0; ct < NCT; ++ct) sf[kb][ct] = ST.pfrag(SD, 16 * ct, 32 * kb);
-      f32x4 ws[NCT], u[NCT];
-#pragma unroll
-      for (int ct = 0; ct < NCT; ++ct) { ws[ct] = f32x4{0, 0, 0, 0}; u[ct] = ws[ct]; }
+      for (int ct = 0; ct < NCT; ++ct) { u[ct] = f32x4{0, 0, 0, 0}; ws[ct] = u[ct]; }
 #pragma unroll
       for (int kb = 0; kb < NKC; ++kb)
 #pragma unroll
@@ -949,37 +1005,116 @@ __global__ __launch_bounds__(256) void inter_chunk_kernel(KernelPtrs kp, SeqInfo
 #pragma unroll
       for (int kb = 0; kb < NKD; ++kb)
 #pragma unroll
-        for (int ct = 0; ct < NCT; ++ct) {
-          ws[ct] = mma_pp(f.W[kb], sf[kb][ct], ws[ct]);
-          qs[ct] = mma_pp(f.Qt[kb], sf[kb][ct], qs[ct]);
-        }
+        for (int ct = 0; ct < NCT; ++ct) ws[ct] = mma_pp(f.W[kb], ST.pfrag(SD, 16 * ct, 32 * kb), ws[ct]);
 #pragma unroll
       for (int ct = 0; ct < NCT; ++ct) {
         float v4[4] = {u[ct][0] - ws[ct][0], u[ct][1] - ws[ct][1], u[ct][2] - ws[ct][2],
                        u[ct][3] - ws[ct][3]};
-        UT.template storeN<4>((16 * ct + (l & 15)) * SK + 16 * w + 4 * (l >> 4), v4);
+        UT.template storeN<4>((16 * ct + (l & 15)) * SK + 16 * rt + 4 * (l >> 4), v4);
       }
     }
-    load_frags_phase1<M, D, C, NCT>(f, blk_of(min(ci + 2, nch - 1)), w, vt0);
-    __syncthreads();  // UT ready; ST reads done
-    typename M::PFrag uf[NKC][NCT];
+    load_u1<M, D, C, NCT>(f, blk_of(min(ci + 2, last)), rt, vt0);
+    __syncthreads();  // U^T published; S^T reads done
+#pragma unroll
+    for (int s = 0; s < NST; ++s)
+#pragma unroll
+      for (int ct = 0; ct < NCT; ++ct)
+#pragma unroll
+        for (int x = 0; x < 4; ++x) S[s][ct][x] *= f.gam[s][x];
 #pragma unroll
     for (int kb = 0; kb < NKC; ++kb)
 #pragma unroll
-      for (int ct = 0; ct < NCT; ++ct) uf[kb][ct] = UT.pfrag(SK, 16 * ct, 32 * kb);
-    if (NRT == 4 || w < NRT) {
+      for (int ct = 0; ct < NCT; ++ct) {
+        const auto uf = UT.pfrag(SK, 16 * ct, 32 * kb);
+#pragma unroll
+        for (int s = 0; s < NST; ++s) S[s][ct] = mma_pp(f.Kb[s][kb], uf, S[s][ct]);
+      }
+    load_u2<M, D, C, NCT>(g, blk_of(min(ci + 1, last)), w);
+    publish_state();
+  };
+
+  UF fa, fb;
+  if (gm.ci_lo < gm.ci_hi) {
+    load_u1<M, D, C, NCT>(fa, blk_of(gm.ci_lo), rt, vt0);
+    load_u2<M, D, C, NCT>(fa, blk_of(gm.ci_lo), w);
+    load_u1<M, D, C, NCT>(fb, blk_of(min(gm.ci_lo + 1, last)), rt, vt0);
+  }
+  for (int ci = gm.ci_lo; ci < gm.ci_hi; ci += 2) {
+    step(fa, fb, ci);
+    if (ci + 1 >= gm.ci_hi) break;
+    step(fb, fa, ci + 1);
+  }
+  if (gm.s_out) {
+#pragma unroll
+    for (int s = 0; s < NST; ++s) {
+      const int st = w * NST + s;
+#pragma unroll
+      for (int ct = 0; ct < NCT; ++ct)
+#pragma unroll
+        for (int x = 0; x < 4; ++x) {
+          const int c = 16 * st + 4 * (l >> 4) + x;
+          gm.s_out[sbase + (size_t)c * D + gm.col0 + 16 * ct + (l & 15)] = S[s][ct][x];
+        }
+    }
+  }
+}
+
+template <class M, int D, int C, int NCT, bool OUT_BF16>
+__device__ __forceinline__ void inter_o_role(const KernelPtrs& kp, const InterGeom& gm, char* smem,
+                                             int r) {
+  typedef Layout<M, D, C> LY;
+  typedef InterLds<M, D, C, NCT> L;
+  typedef OFrags<M, D, C> OF;
+  constexpr int NRT = LY::NRT, NKC = LY::NKC, NKD = LY::NKD;
+  constexpr int NVB = D / L::DVB;
+  constexpr int SD = L::SD, SK = L::SK;
+  const int l = lane_id();
+  LdsPrecise<M> ST(smem + L::oST, L::kSTplain);
+  LdsPrecise<M> UT(smem + L::oUT, L::kUTplain);
+  const int rt = NRT == 4 ? r : min(r, NRT - 1);
+  const bool act = NRT == 4 || r < NRT;
+  const int H = gm.H;
+
+  auto blk_of = [&](int ci) { return kp.ops + ((size_t)(gm.cbase + ci) * H + gm.h) * LY::kBytes; };
+  const int last = gm.ci_hi - 1;
+  // L2 probe: the NVB workgroups of this (sequence, head) each touch one
+  // line in every 128 B of their 1/NVB share of a chunk block.
+  constexpr int kLines = (int)(LY::kBytes / 128);
+  constexpr int kShare = (kLines + NVB - 1) / NVB;
+  const int pline = min(gm.vb * kShare + min(64 * r + l, kShare - 1), kLines - 1);
+  float sink = 0.f;
+
+  auto step = [&](OF& f, OF& g, int ci) {
+    const int t0 = gm.bos + ci * C;
+    const int len = gm.eos - t0 < C ? gm.eos - t0 : C;
+    __syncthreads();  // S^T published
+    sink += f.probe;
+    f.probe = *reinterpret_cast<const float*>(blk_of(min(ci + kPrefetchAhead, last)) +
+                                              (size_t)pline * 128);
+    f32x4 qs[NCT];
+#pragma unroll
+    for (int ct = 0; ct < NCT; ++ct) qs[ct] = f32x4{0, 0, 0, 0};
+    if (act) {
+#pragma unroll
+      for (int kb = 0; kb < NKD; ++kb)
+#pragma unroll
+        for (int ct = 0; ct < NCT; ++ct) qs[ct] = mma_pp(f.Qt[kb], ST.pfrag(SD, 16 * ct, 32 * kb), qs[ct]);
+    }
+    load_o1<M, D, C>(f, blk_of(min(ci + 2, last)), rt);
+    __syncthreads();  // U^T published
+    if (act) {
 #pragma unroll
       for (int ct = 0; ct < NCT; ++ct) {
         f32x4 o = qs[ct];
         // P is lower triangular: token blocks past this row tile are zero.
 #pragma unroll
         for (int kb = 0; kb < NKC; ++kb)
-          if (32 * kb <= 16 * w + 15) o = mma_pp(f.P[kb], uf[kb][ct], o);
+          if (32 * kb <= 16 * rt + 15) o = mma_pp(f.P[kb], UT.pfrag(SK, 16 * ct, 32 * kb), o);
 #pragma unroll
         for (int x = 0; x < 4; ++x) {
-          const int r = 16 * w + 4 * (l >> 4) + x;
-          if (r < len) {
-            const size_t oi = ((size_t)(t0 + r) * H + h) * D + col0 + 16 * ct + (l & 15);
+          const int row = 16 * rt + 4 * (l >> 4) + x;
+          if (row < len) {
+            const size_t oi = ((size_t)(t0 + row) * H + gm.h) * D + gm.col0 + 16 * ct + (l & 15);
             if constexpr (OUT_BF16)
               reinterpret_cast<bf16*>(kp.o)[oi] = f2bf(o[x]);
             else
@@ -988,72 +1123,93 @@ __global__ __launch_bounds__(256) void inter_chunk_kernel(KernelPtrs kp, SeqInfo
         }
       }
     }
-#pragma unroll
-    for (int s = 0; s < NST; ++s) {
-      const int st = w * NST + s;
-      if (NDT == 4 * NST || st < NDT) {
-#pragma unroll
-        for (int ct = 0; ct < NCT; ++ct)
-#pragma unroll
-          for (int x = 0; x < 4; ++x) S[s][ct][x] *= f.gam[s][x];
-#pragma unroll
-        for (int kb = 0; kb < NKC; ++kb)
-#pragma unroll
-          for (int ct = 0; ct < NCT; ++ct) S[s][ct] = mma_pp(f.Kb[s][kb], uf[kb][ct], S[s][ct]);
-      }
-    }
-    load_frags_phase2<M, D, C, NCT>(g, blk_of(min(ci + 1, nch - 1)), w);
-    // ST is read again only after the next chunk's first barrier, and every
-    // read of this chunk's ST happened before the second barrier.
-    write_state_lds();
+    load_o2<M, D, C>(g, blk_of(min(ci + 1, last)), rt);
   };
 
-  CF fa, fb;
-  if (nch > 0) {
-    load_frags_phase1<M, D, C, NCT>(fa, blk_of(0), w, vt0);
-    load_frags_phase2<M, D, C, NCT>(fa, blk_of(0), w);
-    load_frags_phase1<M, D, C, NCT>(fb, blk_of(min(1, nch - 1)), w, vt0);
+  OF fa, fb;
+  fa.probe = 0.f;
+  fb.probe = 0.f;
+  if (gm.ci_lo < gm.ci_hi) {
+    load_o1<M, D, C>(fa, blk_of(gm.ci_lo), rt);
+    load_o2<M, D, C>(fa, blk_of(gm.ci_lo), rt);
+    load_o1<M, D, C>(fb, blk_of(min(gm.ci_lo + 1, last)), rt);
   }
-  for (int ci = 0; ci < nch; ci += 2) {
-    process(fa, fb, ci);
-    if (ci + 1 >= nch) break;
-    process(fb, fa, ci + 1);
+  for (int ci = gm.ci_lo; ci < gm.ci_hi; ci += 2) {
+    step(fa, fb, ci);
+    if (ci + 1 >= gm.ci_hi) break;
+    step(fb, fa, ci + 1);
   }
-  if (kp.s1) {
-#pragma unroll
-    for (int s = 0; s < NST; ++s) {
-      const int st = w * NST + s;
-      if (st < NDT) {
-#pragma unroll
-        for (int ct = 0; ct < NCT; ++ct)
-#pragma unroll
-          for (int x = 0; x < 4; ++x) {
-            const int c = 16 * st + 4 * (l >> 4) + x;
-            kp.s1[sbase + (size_t)c * D + col0 + 16 * ct + (l & 15)] = S[s][ct][x];
-          }
-      }
-    }
+  // The probes only warm L2; keep their loads alive without a visible effect
+  // (H is never negative).
+  sink += fa.probe + fb.probe;
+  if (H < 0) reinterpret_cast<float*>(kp.o)[0] = sink;
+}
+
+// NCT = number of 16-column value tiles per workgroup (16 or 32 columns).
+template <class M, int D, int C, int NCT, bool OUT_BF16>
+__global__ __launch_bounds__(kInterThreads, 2) void inter_chunk_kernel(KernelPtrs kp, SeqInfo si,
+                                                                       int num_pairs) {
+  typedef Layout<M, D, C> LY;
+  typedef InterLds<M, D, C, NCT> L;
+  constexpr int KC = LY::KC;
+  constexpr int DVB = L::DVB;
+  constexpr int NVB = D / DVB;
+  __shared__ __attribute__((aligned(16))) char smem[L::kTotal];
+
+  // XCD-aware mapping: consecutive block ids rotate over the 8 XCDs, so the
+  // NVB column blocks of one (sequence, head) are given ids that land on the
+  // same XCD and share its L2 for the per-chunk operands.
+  const int bid = blockIdx.x;
+  const int xcd = bid & 7, slot = bid >> 3;
+  const int pair = (slot / NVB) * 8 + xcd;
+  InterGeom gm;
+  gm.vb = slot % NVB;
+  if (pair >= num_pairs) return;
+  gm.H = kp.H;
+  gm.n = pair / gm.H;
+  gm.h = pair % gm.H;
+  gm.col0 = DVB * gm.vb;
+  seq_bounds(si, gm.n, gm.bos, gm.eos);
+  const int cid0 = si.cu ? clampi(si.chunk_off[gm.n], 0, si.total_chunks) : gm.n * chunks_of<C>(si.seq_len);
+  // Never walk past the chunks the workspace was sized for.
+  gm.nch = min(chunks_of<C>(gm.eos - gm.bos), si.total_chunks - cid0);
+  // This launch covers chunks [seg_lo, seg_hi) of the packed order.  A
+  // sequence without chunks is settled (final = initial state) by the first.
+  const int lo = max(cid0, si.seg_lo), hi = min(cid0 + gm.nch, si.seg_hi);
+  if (gm.nch > 0 ? lo >= hi : si.seg_lo != 0) return;
+  gm.ci_lo = gm.nch > 0 ? lo - cid0 : 0;
+  gm.ci_hi = gm.nch > 0 ? hi - cid0 : 0;
+  gm.cbase = cid0 - si.seg_lo;
+  gm.s_in = gm.ci_lo == 0 ? kp.s0 : kp.carry;
+  gm.s_out = gm.ci_hi == gm.nch ? kp.s1 : kp.carry;
+
+  // Zero the padded token columns of U^T once (KC > C); nothing writes them.
+  if (KC > C) {
+    LdsPrecise<M> UT(smem + L::oUT, L::kUTplain);
+    for (int idx = threadIdx.x; idx < DVB * (KC - C); idx += kInterThreads)
+      UT.store((idx / (KC - C)) * L::SK + C + idx % (KC - C), 0.f);
   }
+  const int w = wave_id();
+  if (w < 4)
+    inter_u_role<M, D, C, NCT>(kp, gm, smem, w);
+  else
+    inter_o_role<M, D, C, NCT, OUT_BF16>(kp, gm, smem, w - 4);
 }
 
 // Value-column block width of the inter-chunk pass: wide blocks cut the
-// per-chunk operand traffic (each block re-reads the chunk's operands), narrow
-// ones give more workgroups.  Heuristic: keep at least ~2 workgroups per CU
-// of work available when there are many (sequence, head) pairs.
-// KDA_PREFILL_DVB (16, 32 or 64) overrides it, for tuning.
+// per-chunk operand traffic (each block re-reads the chunk's operands),
+// narrow ones give more workgroups.  32 columns once there are enough
+// (sequence, head) pairs to fill the chip twice over with them.
+// KDA_PREFILL_DVB (16 or 32) overrides it, for tuning.
 static int choose_nct(int pairs, int D) {
   static int env = -1;
   if (env < 0) {
     const char* e = getenv("KDA_PREFILL_DVB");
     const int v = e ? atoi(e) : 0;
-    env = (v == 16 || v == 32 || v == 64) ? v / 16 : 0;
+    env = (v == 16 || v == 32) ? v / 16 : 0;
   }
   int nct = env;
-  if (nct == 0) {
-    const long long units16 = (long long)pairs * (D / 16);
-    nct = units16 >= 4096 ? 4 : (units16 >= 1024 ? 2 : 1);
-  }
-  while (nct > 1 && D / (16 * nct) < 1) nct >>= 1;
+  if (nct == 0) nct = (long long)pairs * (D / 32) >= 512 ? 2 : 1;
   return nct;
 }
 
@@ -1063,11 +1219,11 @@ static void launch_inter(const PrefillArgs& a, const KernelPtrs& kp, const SeqIn
   const int nvb = D / (16 * NCT);
   const int blocks = ((pairs + 7) / 8) * 8 * nvb;
   if (a.out_bf16)
-    hipLaunchKernelGGL((inter_chunk_kernel<M, D, C, NCT, true>), dim3(blocks), dim3(256), 0, a.stream,
-                       kp, si, pairs);
+    hipLaunchKernelGGL((inter_chunk_kernel<M, D, C, NCT, true>), dim3(blocks), dim3(kInterThreads), 0,
+                       a.stream, kp, si, pairs);
   else
-    hipLaunchKernelGGL((inter_chunk_kernel<M, D, C, NCT, false>), dim3(blocks), dim3(256), 0, a.stream,
-                       kp, si, pairs);
+    hipLaunchKernelGGL((inter_chunk_kernel<M, D, C, NCT, false>), dim3(blocks), dim3(kInterThreads), 0,
+                       a.stream, kp, si, pairs);
 }
 
 // ---------------------------------------------------------------------------
@@ -1075,8 +1231,8 @@ static void launch_inter(const PrefillArgs& a, const KernelPtrs& kp, const SeqIn
 // ---------------------------------------------------------------------------
 template <class M, int D, int C>
 static hipError_t launch_prefill_t(const PrefillArgs& a) {
-  typedef Layout<M, D, C> LY;
   char* ws = reinterpret_cast<char*>(a.workspace);
+  const int seg = prefill_segment_chunks(a.total_chunks, a.H, D, C, a.in_bf16);
   SeqInfo si;
   si.cu = a.cu_seqlens;
   si.num_seqs = a.num_seqs;
@@ -1094,7 +1250,10 @@ static hipError_t launch_prefill_t(const PrefillArgs& a) {
   kp.o = a.o;
   kp.s0 = a.initial_state;
   kp.s1 = a.final_state;
-  kp.ops = ws + table_bytes(a.num_seqs, a.total_chunks);
+  char* after_table = ws + table_bytes(a.num_seqs, a.total_chunks);
+  const size_t carry = carry_bytes(a.num_seqs, a.total_chunks, seg, a.H, D);
+  kp.carry = carry ? reinterpret_cast<float*>(after_table) : nullptr;
+  kp.ops = after_table + carry;
   kp.H = a.H;
 
   if (a.cu_seqlens) {
@@ -1102,22 +1261,30 @@ static hipError_t launch_prefill_t(const PrefillArgs& a) {
                        const_cast<int32_t*>(si.chunk_off), const_cast<int32_t*>(si.chunk_seq),
                        a.num_seqs, a.total_tokens, a.total_chunks, C);
   }
+  constexpr size_t lds = IntraLds<M, D, C>::kTotal;
+  static_assert(lds <= 160 * 1024, "intra-chunk LDS");
   if (a.total_chunks > 0) {
-    constexpr size_t lds = IntraLds<M, D, C>::kTotal;
-    static_assert(lds <= 160 * 1024, "intra-chunk LDS");
     hipError_t e = hipFuncSetAttribute(reinterpret_cast<const void*>(&intra_chunk_kernel<M, D, C>),
                                        hipFuncAttributeMaxDynamicSharedMemorySize, (int)lds);
     if (e != hipSuccess) return e;
-    hipLaunchKernelGGL((intra_chunk_kernel<M, D, C>), dim3(a.total_chunks, a.H), dim3(kIntraThreads), lds,
-                       a.stream, kp, si);
   }
   const int nct = choose_nct(a.num_seqs * a.H, D);
-  if (nct == 4)
-    launch_inter<M, D, C, 4>(a, kp, si);
-  else if (nct == 2)
-    launch_inter<M, D, C, 2>(a, kp, si);
-  else
-    launch_inter<M, D, C, 1>(a, kp, si);
+  // One pass when there are no chunks: sequences without tokens still
+  // copy their initial state to the final state.
+  int lo = 0;
+  do {
+    const int hi = lo + seg < a.total_chunks ? lo + seg : a.total_chunks;
+    si.seg_lo = lo;
+    si.seg_hi = hi;
+    if (hi > lo)
+      hipLaunchKernelGGL((intra_chunk_kernel<M, D, C>), dim3(hi - lo, a.H), dim3(kIntraThreads), lds,
+                         a.stream, kp, si);
+    if (nct == 2)
+      launch_inter<M, D, C, 2>(a, kp, si);
+    else
+      launch_inter<M, D, C, 1>(a, kp, si);
+    lo = hi;
+  } while (lo < a.total_chunks);
   return hipGetLastError();
 }
 

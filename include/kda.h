@@ -66,9 +66,14 @@ int kda_version(void);
  * same meaning as in kda_prefill.  Returns 0 and writes nothing to *bytes on
  * an argument error (the status says which).
  *
- * The workspace holds the chunk table and, per (chunk, head), the intra-chunk
- * operands that the inter-chunk pass consumes (144.5 KB per chunk and head at
- * Dk = Dv = 128, C = 64).
+ * The prefill runs in segments of consecutive chunks; the workspace holds the
+ * chunk table, the intra-chunk operands of one segment (144.5 KB per chunk
+ * and head at Dk = Dv = 128, C = 64; segments are sized to about 160 MiB of
+ * operands) and, when there is more than one segment, the fp32 state carried
+ * between them (num_seqs * H * Dk * Dv * 4 bytes).  So the size is bounded
+ * for any sequence length.  The environment variable KDA_PREFILL_SEGMENT_KB
+ * overrides the per-segment budget; a workspace must be sized under the same
+ * setting as the kda_prefill call that uses it.
  */
 kda_status kda_prefill_workspace_size(int B, int T, int H, int Dk, int Dv,
                                       int num_seqs,

@@ -236,6 +236,32 @@ def test_prefill_varlen(kda, C):
     np.testing.assert_array_equal(fin[2], s0[2])
 
 
+@pytest.mark.parametrize("dtype,C,seg_kb", [("bf16", 16, 1), ("f32", 32, 500), ("bf16", 64, 700)])
+def test_prefill_segments(kda, monkeypatch, dtype, C, seg_kb):
+    """A small per-segment operand budget makes the prefill run as many
+    intra/inter passes (one chunk each at 1 KB), with every sequence's state
+    carried between passes: packed sequences start and end inside segments,
+    one is empty, and the final state is written over the initial state."""
+    monkeypatch.setenv("KDA_PREFILL_SEGMENT_KB", str(seg_kb))
+    say(f"prefill segments dtype={dtype} C={C} budget={seg_kb} KB")
+    lens = [37, 0, 130, 5, 200, 64]
+    cu = np.concatenate([[0], np.cumsum(lens)]).astype(np.int32)
+    rng = np.random.default_rng([21, C])
+    H = 2
+    x = I.draw_tokens(rng, int(cu[-1]), H, 128, 128, dtype)
+    s0 = I.draw_states(rng, len(lens), H, 128, 128)
+    eo, ef = oracle.kda_recurrent(x.q, x.k, x.v, x.g, x.beta, s0, cu_seqlens=cu)
+    q, k, v, g, b = tok_to_dev(x)
+    st = torch.from_numpy(s0.copy()).to(DEV)
+    cud = torch.from_numpy(cu).to(DEV)
+    o, _ = kda.prefill(q, k, v, g, b, st, cud, cu_seqlens_host=cu, chunk_size=C, final_state=st)
+    torch.cuda.synchronize()
+    eo_, es_ = rel(host(o)[0], eo), rel(host(st), ef)
+    say(f"  o err {eo_:.2e}  state err {es_:.2e}")
+    assert eo_ <= TOL[dtype] and es_ <= TOL[dtype]
+    np.testing.assert_array_equal(host(st)[1], s0[1])
+
+
 def test_prefill_workload1_full(kda):
     """B=1, H=32, T=4096, d=128, bf16, chunk 64: every output vs the oracle."""
     say("prefill workload 1 full")
