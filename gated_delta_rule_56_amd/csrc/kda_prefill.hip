@@ -839,15 +839,13 @@ __global__ __launch_bounds__(kIntraThreads, 4) void intra_chunk_kernel(KernelPtr
 //     S <- Diag(gam_n) S + K-bar^T U and publishes S^T in LDS.
 //   O-waves (4..7) produce the output.  Wave 4 + r forms Q*gam S for row
 //     tile r from the published state, then O = Q*gam S + P U from the
-//     published U, and stores it.  They also pull the chunk blocks a few
-//     chunks ahead into L2.
+//     published U, and stores it.
 //
 // Each SIMD runs one wave of each role, so one wave's operand loads overlap
 // the other's matrix products; the two roles split the per-chunk operands
 // (U-waves: W, T, V^T, K-bar^T, gam_n; O-waves: Q*gam, P).
 // ---------------------------------------------------------------------------
 constexpr int kInterThreads = 512;
-constexpr int kPrefetchAhead = 4;  // chunks between the L2 probe and use
 
 template <class M, int D, int C, int NCT>
 struct UFrags {
@@ -865,7 +863,6 @@ struct OFrags {
   typedef Layout<M, D, C> LY;
   typename M::PFrag Qt[LY::NKD];
   typename M::PFrag P[LY::NKC];
-  float probe;
 };
 
 // Every wave of a role issues the same loads.  With fewer than four row
@@ -992,45 +989,74 @@ __device__ __forceinline__ void inter_u_role(const KernelPtrs& kp, const InterGe
 
   auto blk_of = [&](int ci) { return kp.ops + ((size_t)(gm.cbase + ci) * gm.H + gm.h) * LY::kBytes; };
   const int last = gm.ci_hi - 1;
+  // T V of the chunk about to run: independent of the state, so it is
+  // formed at the end of the previous step, off the S -> U -> S chain.
+  f32x4 u[NCT];
+  auto form_tv = [&](const UF& f) {
+#pragma unroll
+    for (int ct = 0; ct < NCT; ++ct) u[ct] = f32x4{0, 0, 0, 0};
+#pragma unroll
+    for (int kb = 0; kb < NKC; ++kb)
+#pragma unroll
+      for (int ct = 0; ct < NCT; ++ct) u[ct] = mma_pf(f.Tm[kb], f.V[ct][kb], u[ct]);
+  };
+  // The chain's products keep two partial sums (even and odd k blocks) so
+  // that consecutive MFMAs do not wait on each other's accumulator.
   auto step = [&](UF& f, UF& g, int ci) {
     __syncthreads();  // S^T published; last chunk's U^T reads done
     if (act) {
-      f32x4 u[NCT], ws[NCT];
+      f32x4 ws0[NCT], ws1[NCT];
 #pragma unroll
-      for (int ct = 0; ct < NCT; ++ct) { u[ct] = f32x4{0, 0, 0, 0}; ws[ct] = u[ct]; }
-#pragma unroll
-      for (int kb = 0; kb < NKC; ++kb)
-#pragma unroll
-        for (int ct = 0; ct < NCT; ++ct) u[ct] = mma_pf(f.Tm[kb], f.V[ct][kb], u[ct]);
+      for (int ct = 0; ct < NCT; ++ct) { ws0[ct] = f32x4{0, 0, 0, 0}; ws1[ct] = ws0[ct]; }
 #pragma unroll
       for (int kb = 0; kb < NKD; ++kb)
 #pragma unroll
-        for (int ct = 0; ct < NCT; ++ct) ws[ct] = mma_pp(f.W[kb], ST.pfrag(SD, 16 * ct, 32 * kb), ws[ct]);
+        for (int ct = 0; ct < NCT; ++ct) {
+          const auto sf = ST.pfrag(SD, 16 * ct, 32 * kb);
+          if (kb & 1)
+            ws1[ct] = mma_pp(f.W[kb], sf, ws1[ct]);
+          else
+            ws0[ct] = mma_pp(f.W[kb], sf, ws0[ct]);
+        }
 #pragma unroll
       for (int ct = 0; ct < NCT; ++ct) {
-        float v4[4] = {u[ct][0] - ws[ct][0], u[ct][1] - ws[ct][1], u[ct][2] - ws[ct][2],
-                       u[ct][3] - ws[ct][3]};
+        float v4[4];
+#pragma unroll
+        for (int x = 0; x < 4; ++x) v4[x] = u[ct][x] - (ws0[ct][x] + ws1[ct][x]);
         UT.template storeN<4>((16 * ct + (l & 15)) * SK + 16 * rt + 4 * (l >> 4), v4);
       }
     }
     load_u1<M, D, C, NCT>(f, blk_of(min(ci + 2, last)), rt, vt0);
     __syncthreads();  // U^T published; S^T reads done
+    f32x4 S1[NST][NCT];
 #pragma unroll
     for (int s = 0; s < NST; ++s)
 #pragma unroll
-      for (int ct = 0; ct < NCT; ++ct)
+      for (int ct = 0; ct < NCT; ++ct) {
+        S1[s][ct] = f32x4{0, 0, 0, 0};
 #pragma unroll
         for (int x = 0; x < 4; ++x) S[s][ct][x] *= f.gam[s][x];
+      }
 #pragma unroll
     for (int kb = 0; kb < NKC; ++kb)
 #pragma unroll
       for (int ct = 0; ct < NCT; ++ct) {
         const auto uf = UT.pfrag(SK, 16 * ct, 32 * kb);
 #pragma unroll
-        for (int s = 0; s < NST; ++s) S[s][ct] = mma_pp(f.Kb[s][kb], uf, S[s][ct]);
+        for (int s = 0; s < NST; ++s) {
+          if (kb & 1)
+            S1[s][ct] = mma_pp(f.Kb[s][kb], uf, S1[s][ct]);
+          else
+            S[s][ct] = mma_pp(f.Kb[s][kb], uf, S[s][ct]);
+        }
       }
+#pragma unroll
+    for (int s = 0; s < NST; ++s)
+#pragma unroll
+      for (int ct = 0; ct < NCT; ++ct) S[s][ct] += S1[s][ct];
     load_u2<M, D, C, NCT>(g, blk_of(min(ci + 1, last)), w);
     publish_state();
+    if (act) form_tv(g);
   };
 
   UF fa, fb;
@@ -1038,6 +1064,7 @@ __device__ __forceinline__ void inter_u_role(const KernelPtrs& kp, const InterGe
     load_u1<M, D, C, NCT>(fa, blk_of(gm.ci_lo), rt, vt0);
     load_u2<M, D, C, NCT>(fa, blk_of(gm.ci_lo), w);
     load_u1<M, D, C, NCT>(fb, blk_of(min(gm.ci_lo + 1, last)), rt, vt0);
+    if (act) form_tv(fa);
   }
   for (int ci = gm.ci_lo; ci < gm.ci_hi; ci += 2) {
     step(fa, fb, ci);
@@ -1066,7 +1093,6 @@ __device__ __forceinline__ void inter_o_role(const KernelPtrs& kp, const InterGe
   typedef InterLds<M, D, C, NCT> L;
   typedef OFrags<M, D, C> OF;
   constexpr int NRT = LY::NRT, NKC = LY::NKC, NKD = LY::NKD;
-  constexpr int NVB = D / L::DVB;
   constexpr int SD = L::SD, SK = L::SK;
   const int l = lane_id();
   LdsPrecise<M> ST(smem + L::oST, L::kSTplain);
@@ -1077,28 +1103,30 @@ __device__ __forceinline__ void inter_o_role(const KernelPtrs& kp, const InterGe
 
   auto blk_of = [&](int ci) { return kp.ops + ((size_t)(gm.cbase + ci) * H + gm.h) * LY::kBytes; };
   const int last = gm.ci_hi - 1;
-  // L2 probe: the NVB workgroups of this (sequence, head) each touch one
-  // line in every 128 B of their 1/NVB share of a chunk block.
-  constexpr int kLines = (int)(LY::kBytes / 128);
-  constexpr int kShare = (kLines + NVB - 1) / NVB;
-  const int pline = min(gm.vb * kShare + min(64 * r + l, kShare - 1), kLines - 1);
-  float sink = 0.f;
 
   auto step = [&](OF& f, OF& g, int ci) {
     const int t0 = gm.bos + ci * C;
     const int len = gm.eos - t0 < C ? gm.eos - t0 : C;
     __syncthreads();  // S^T published
-    sink += f.probe;
-    f.probe = *reinterpret_cast<const float*>(blk_of(min(ci + kPrefetchAhead, last)) +
-                                              (size_t)pline * 128);
     f32x4 qs[NCT];
 #pragma unroll
     for (int ct = 0; ct < NCT; ++ct) qs[ct] = f32x4{0, 0, 0, 0};
     if (act) {
+      f32x4 qs1[NCT];
+#pragma unroll
+      for (int ct = 0; ct < NCT; ++ct) qs1[ct] = f32x4{0, 0, 0, 0};
 #pragma unroll
       for (int kb = 0; kb < NKD; ++kb)
 #pragma unroll
-        for (int ct = 0; ct < NCT; ++ct) qs[ct] = mma_pp(f.Qt[kb], ST.pfrag(SD, 16 * ct, 32 * kb), qs[ct]);
+        for (int ct = 0; ct < NCT; ++ct) {
+          const auto sf = ST.pfrag(SD, 16 * ct, 32 * kb);
+          if (kb & 1)
+            qs1[ct] = mma_pp(f.Qt[kb], sf, qs1[ct]);
+          else
+            qs[ct] = mma_pp(f.Qt[kb], sf, qs[ct]);
+        }
+#pragma unroll
+      for (int ct = 0; ct < NCT; ++ct) qs[ct] += qs1[ct];
     }
     load_o1<M, D, C>(f, blk_of(min(ci + 2, last)), rt);
     __syncthreads();  // U^T published
@@ -1127,8 +1155,6 @@ __device__ __forceinline__ void inter_o_role(const KernelPtrs& kp, const InterGe
   };
 
   OF fa, fb;
-  fa.probe = 0.f;
-  fb.probe = 0.f;
   if (gm.ci_lo < gm.ci_hi) {
     load_o1<M, D, C>(fa, blk_of(gm.ci_lo), rt);
     load_o2<M, D, C>(fa, blk_of(gm.ci_lo), rt);
@@ -1139,10 +1165,6 @@ __device__ __forceinline__ void inter_o_role(const KernelPtrs& kp, const InterGe
     if (ci + 1 >= gm.ci_hi) break;
     step(fb, fa, ci + 1);
   }
-  // The probes only warm L2; keep their loads alive without a visible effect
-  // (H is never negative).
-  sink += fa.probe + fb.probe;
-  if (H < 0) reinterpret_cast<float*>(kp.o)[0] = sink;
 }
 
 // NCT = number of 16-column value tiles per workgroup (16 or 32 columns).
