@@ -10,12 +10,17 @@ Infinity Cache cannot hold a step's working set.
 
 Prints ONE JSON line.  ``value`` is prefill tokens/s; the decode rate and the
 per-call times are in ``decode`` / ``prefill``.  ``roofline`` describes the
-kernel that takes the most time per step (decided from the measured times);
+unit that takes the most time per step (decided from the measured times): the
+kda_prefill call (its intra- and inter-chunk launches) or the decode kernel;
 ``prefill_roofline`` gives the prefill call against HBM and bf16-MFMA peaks.
+``copy`` is a 1 GiB device-to-device copy timed in the same process: a
+measured bandwidth reference, and the kernel the HBM byte counters are
+calibrated on.
 """
 from __future__ import annotations
 
 import argparse
+import hashlib
 import json
 import os
 import platform
@@ -33,6 +38,7 @@ BF16_PEAK_TFLOPS = 2500.0      # MI355X dense bf16 MFMA, TFLOP/s
 # Workload sizes (see gated_delta_rule_56_amd/inputs.py WORKLOADS[1] and [4]).
 P_T, P_H, P_D, P_C = 4096, 32, 128, 64
 D_N, D_H, D_D = 256, 32, 128
+COPY_BYTES, COPY_REPS = 1 << 30, 5
 
 
 def prefill_algorithmic_bytes(T=P_T, H=P_H, d=P_D):
@@ -51,12 +57,54 @@ def decode_algorithmic_bytes(N=D_N, H=D_H, d=D_D):
     return N * H * (2 * d * d * 4 + 3 * 2 * d + 4 * d + 4 + 4 * d)
 
 
+# HBM bytes per call measured with rocprofv3 FETCH_SIZE and WRITE_SIZE (one
+# run each) on the command in profiles/hbm_traffic.md, each counter scaled by
+# the ratio of known bytes to counted bytes for the 1 GiB copy in the same
+# run.  A figure is reported only while the kernel sources still hash to the
+# values it was measured on.
+TRAFFIC = {
+    "prefill": {"sources": "78bcc62772fd0fb7", "bytes": 873218517},
+    "decode": {"sources": "9b282d3be22a2ead", "bytes": 1089484282},
+}
+
+
+def sources_digest(names):
+    h = hashlib.sha256()
+    for n in names:
+        with open(os.path.join(ROOT, "gated_delta_rule_56_amd", "csrc", n), "rb") as f:
+            h.update(f.read())
+    return h.hexdigest()[:16]
+
+
+PREFILL_SOURCES = ("kda_prefill.hip", "kda_device.hpp", "kda_launch.hpp")
+DECODE_SOURCES = ("kda_decode.hip", "kda_device.hpp", "kda_launch.hpp")
+
+
+def measured_traffic(unit, names):
+    t = TRAFFIC.get(unit)
+    if t is None or t["sources"] != sources_digest(names):
+        return None
+    return t["bytes"]
+
+
 def log(*a):
     print(*a, file=sys.stderr, flush=True)
 
 
-def cpu_baseline(min_seconds=10.0, max_reps=5):
-    """The float64 oracle on the host cores, on the whole prefill workload."""
+def cpu_model():
+    try:
+        with open("/proc/cpuinfo") as f:
+            for line in f:
+                if line.startswith("model name"):
+                    return line.split(":", 1)[1].strip()
+    except OSError:
+        pass
+    return platform.processor() or platform.machine()
+
+
+def cpu_baseline(min_seconds=10.0, max_reps=200):
+    """The float64 oracle on the host cores, on the whole prefill workload,
+    repeated until about ``min_seconds`` of CPU work have been timed."""
     import oracle
     from gated_delta_rule_56_amd import inputs as I
     x = I.workload_tokens(I.WORKLOADS[1])
@@ -70,7 +118,7 @@ def cpu_baseline(min_seconds=10.0, max_reps=5):
             "kind": "oracle",
             "sample": f"whole prefill workload (B=1, H=32, T=4096, d=128), {reps} pass(es), "
                       f"float64 token-by-token recurrence, {t:.1f} s",
-            "cpu": platform.processor() or platform.machine()}
+            "cpu": cpu_model()}
 
 
 def main():
@@ -118,6 +166,8 @@ def main():
         f32 = lambda a: torch.from_numpy(np.ascontiguousarray(a)).to(dev)
         dsets.append((bf(x.q), bf(x.k), bf(x.v), f32(x.g), f32(x.beta)))
     od = torch.empty((D_N, D_H, D_D), dtype=torch.float32, device=dev)
+    copy_src = torch.ones(COPY_BYTES // 4, dtype=torch.float32, device=dev)
+    copy_dst = torch.empty_like(copy_src)
     torch.cuda.synchronize()
 
     def step(i, ev=None):
@@ -151,6 +201,18 @@ def main():
     pre_ms = np.array([e[0].elapsed_time(e[1]) for e in evs])
     dec_ms = np.array([e[1].elapsed_time(e[2]) for e in evs])
 
+    # 1 GiB device copy: read + write bytes over the median time
+    cev = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
+           for _ in range(COPY_REPS)]
+    copy_dst.copy_(copy_src)
+    for a, b in cev:
+        a.record()
+        copy_dst.copy_(copy_src)
+        b.record()
+    torch.cuda.synchronize()
+    copy_s = float(np.median([a.elapsed_time(b) for a, b in cev])) / 1e3
+    copy_gbs = 2 * COPY_BYTES / copy_s / 1e9
+
     pre_s = pre_ms.mean() / 1e3
     dec_s = dec_ms.mean() / 1e3
     p_bytes, p_flops = prefill_algorithmic_bytes(), prefill_flops()
@@ -159,16 +221,21 @@ def main():
     dec_gbs = d_bytes / dec_s / 1e9
 
     decode_roof = {"bound": "hbm", "achieved": round(dec_gbs, 1), "peak": HBM_PEAK_GBS,
-                   "unit": "GB/s", "frac": round(dec_gbs / HBM_PEAK_GBS, 4), "traffic": None,
-                   "kernel": "decode_step_kernel", "bytes_per_launch": d_bytes}
+                   "unit": "GB/s", "frac": round(dec_gbs / HBM_PEAK_GBS, 4),
+                   "traffic": measured_traffic("decode", DECODE_SOURCES),
+                   "kernel": "decode_step_kernel", "bytes_per_launch": d_bytes,
+                   "frac_of_measured_copy": round(dec_gbs / copy_gbs, 4)}
     p_gbs = p_bytes / pre_s / 1e9
     p_tfl = p_flops / pre_s / 1e12
     prefill_roof = {"bound": "hbm", "achieved": round(p_gbs, 1), "peak": HBM_PEAK_GBS,
-                    "unit": "GB/s", "frac": round(p_gbs / HBM_PEAK_GBS, 4), "traffic": None,
-                    "kernels": "intra_chunk_kernel + inter_chunk_kernel (one kda_prefill call)",
+                    "unit": "GB/s", "frac": round(p_gbs / HBM_PEAK_GBS, 4),
+                    "traffic": measured_traffic("prefill", PREFILL_SOURCES),
+                    "kernels": "intra_chunk_kernel + inter_chunk_kernel per segment "
+                               "(one kda_prefill call)",
                     "bytes_per_call": p_bytes, "flops_per_call": p_flops,
                     "mfma_tflops": round(p_tfl, 2),
-                    "mfma_frac_bf16": round(p_tfl / BF16_PEAK_TFLOPS, 4)}
+                    "mfma_frac_bf16": round(p_tfl / BF16_PEAK_TFLOPS, 4),
+                    "frac_of_measured_copy": round(p_gbs / copy_gbs, 4)}
     roof = decode_roof if dec_s >= pre_s else prefill_roof
 
     cpu = None
@@ -197,6 +264,8 @@ def main():
                     "algorithmic_GBps": round(p_gbs, 1), "algorithmic_TFLOPs": round(p_tfl, 3)},
         "decode": {"us_per_step": round(dec_s * 1e6, 2), "GBps": round(dec_gbs, 1),
                    "tokens_per_s": round(D_N / dec_s, 1), "hbm_frac": round(dec_gbs / HBM_PEAK_GBS, 4)},
+        "copy": {"bytes_moved": 2 * COPY_BYTES, "us": round(copy_s * 1e6, 1),
+                 "GBps": round(copy_gbs, 1)},
         "roofline": roof,
         "prefill_roofline": prefill_roof,
         "decode_roofline": decode_roof,
