@@ -58,8 +58,11 @@ def test_prefill_workload3_long_windows():
         if b % 64 == 0:
             say(f"  drew block {b}/{nblk} ({time.time() - t0:.0f} s)")
     say("running kda_prefill on 1M tokens")
+    torch.cuda.synchronize()
+    t2 = time.time()
     o, fin = kda.prefill(q, k, v, g, beta, None, chunk_size=64)
     torch.cuda.synchronize()
+    say(f"  kda_prefill (workspace allocation included) {1e3 * (time.time() - t2):.1f} ms")
     del q, k, v, g, beta
     o_first = o[0, :B][:, hs].float().cpu().numpy()
     o_last = o[0, T - B:][:, hs].float().cpu().numpy()
