@@ -65,8 +65,8 @@ kda_status kda_prefill_workspace_size(int B, int T, int H, int Dk, int Dv, int n
   const int32_t* cu_dev = cu_seqlens_host;
   kda_status st = seq_layout(B, T, num_seqs, cu_dev, cu_seqlens_host, chunk_size, &chunks);
   if (st != KDA_OK) return st;
-  *bytes = kda::prefill_workspace_bytes(num_seqs, (int)chunks, H, Dk, chunk_size,
-                                        in_dtype == KDA_BF16);
+  *bytes = kda::prefill_workspace_bytes(num_seqs, cu_seqlens_host, cu_seqlens_host ? 0 : T, H, Dk,
+                                        chunk_size, in_dtype == KDA_BF16);
   return KDA_OK;
 }
 
@@ -86,8 +86,8 @@ kda_status kda_prefill(const void* q, const void* k, const void* v, const float*
   if (st != KDA_OK) return st;
   // Token tensors may be empty (and then NULL) only when there are no tokens.
   if ((int64_t)B * T > 0 && (!q || !k || !v || !g || !beta || !o)) return KDA_ERR_INVALID_ARG;
-  const size_t need = kda::prefill_workspace_bytes(num_seqs, (int)chunks, H, Dk, chunk_size,
-                                                   in_dtype == KDA_BF16);
+  const size_t need = kda::prefill_workspace_bytes(num_seqs, cu_seqlens_host, cu_seqlens ? 0 : T,
+                                                   H, Dk, chunk_size, in_dtype == KDA_BF16);
   if (need > 0 && (workspace == nullptr || workspace_bytes < need)) return KDA_ERR_WORKSPACE;
   if (workspace && !aligned(workspace, 256)) return KDA_ERR_INVALID_ARG;
 
@@ -101,10 +101,10 @@ kda_status kda_prefill(const void* q, const void* k, const void* v, const float*
   a.initial_state = initial_state;
   a.final_state = final_state;
   a.cu_seqlens = cu_seqlens;
+  a.cu_seqlens_host = cu_seqlens ? cu_seqlens_host : nullptr;
   a.num_seqs = num_seqs;
   a.seq_len = cu_seqlens ? 0 : T;
   a.total_tokens = B * T;
-  a.total_chunks = (int)chunks;
   a.H = H;
   a.D = Dk;
   a.chunk = chunk_size;

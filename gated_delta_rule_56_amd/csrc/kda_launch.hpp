@@ -33,10 +33,10 @@ struct PrefillArgs {
   const float* initial_state;
   float* final_state;
   const int32_t* cu_seqlens;  // device, or NULL => num_seqs sequences of seq_len
+  const int32_t* cu_seqlens_host;  // host copy of cu_seqlens (or NULL with it)
   int num_seqs;
   int seq_len;                // tokens per sequence when cu_seqlens == NULL
   int total_tokens;
-  int total_chunks;           // sum over sequences of ceil(len / chunk)
   int H, D, chunk;
   bool in_bf16, out_bf16;
   void* workspace;
@@ -45,12 +45,19 @@ struct PrefillArgs {
 
 // Bytes of intra-chunk operands stored per (chunk, head).
 size_t prefill_chunk_bytes(int D, int chunk, bool in_bf16);
-// Chunks per prefill segment (the workspace holds one segment's operands).
-int prefill_segment_chunks(int total_chunks, int H, int D, int chunk, bool in_bf16);
-// Total workspace bytes (chunk table, state carry between segments, one
-// segment's operands), 256-byte aligned pieces.
-size_t prefill_workspace_bytes(int num_seqs, int total_chunks, int H, int D, int chunk,
-                               bool in_bf16);
+// Prefill segments: segment s covers local chunks [s L, (s + 1) L) of every
+// sequence; the workspace holds the largest segment's operands.
+struct SegmentPlan {
+  int L = 0;          // local chunks per segment (0: no sequence has tokens)
+  int nseg = 1;       // segments (at least one inter-chunk pass runs)
+  int max_slots = 0;  // (sequence, chunk) slots of the largest segment, the first
+};
+SegmentPlan plan_segments(int num_seqs, const int32_t* cu_host, int seq_len, int H, int D,
+                          int chunk, bool in_bf16);
+// Total workspace bytes (segment slot table, state carry between segments,
+// one segment's operands), 256-byte aligned pieces.
+size_t prefill_workspace_bytes(int num_seqs, const int32_t* cu_host, int seq_len, int H, int D,
+                               int chunk, bool in_bf16);
 hipError_t launch_prefill(const PrefillArgs& a);
 
 }  // namespace kda

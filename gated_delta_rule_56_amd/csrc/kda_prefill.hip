@@ -86,44 +86,99 @@ size_t prefill_chunk_bytes(int D, int chunk, bool in_bf16) {
   return in_bf16 ? chunk_bytes_m<ModeBF16>(D, chunk) : chunk_bytes_m<ModeF32>(D, chunk);
 }
 
-static size_t table_bytes(int num_seqs, int total_chunks) {
-  return align256(sizeof(int32_t) * (size_t)(num_seqs + 1)) +
-         align256(sizeof(int32_t) * (size_t)total_chunks);
-}
-
-// The prefill runs in segments of consecutive chunks (in the packed chunk
-// order): the intra-chunk pass of a segment, then its inter-chunk pass, which
-// carries each sequence's state into the next segment.  The workspace holds
-// one segment's operands, so it stays bounded for long inputs and a segment's
-// operands are read back soon after they are written, while the 256 MB
-// Infinity Cache still holds them.  KDA_PREFILL_SEGMENT_KB (>= 1) overrides
-// the per-segment operand budget; it is read at every call, and a workspace
-// must be sized under the same setting as the call that uses it.
-static size_t segment_budget_bytes() {
+// The prefill runs in segments: segment s covers the local chunks
+// [s L, (s + 1) L) of every sequence (chunk 0 starts at the sequence's first
+// token), so all sequences advance together.  A segment is the intra-chunk
+// pass over its chunks, then the inter-chunk pass, which carries each
+// sequence's state into the next segment.  The workspace holds one segment's
+// operands, so it stays bounded for long inputs, and a segment's operands are
+// read back soon after they are written, while the 256 MB Infinity Cache
+// still holds them.  That pays when the inter-chunk pass is latency-bound,
+// with at most 512 workgroups (two per CU): then the budget is 160 MiB.  With
+// more (sequence, head) pairs the pass is throughput-bound, extra segments
+// only add start-up and tail time, and the budget is 8 GiB, which only bounds
+// the workspace.  L is the largest length (at least 16 chunks, to amortise
+// the passes' start-up) whose operands fit the budget, then evened out over
+// the segments.  KDA_PREFILL_SEGMENT_KB (>= 1) overrides the budget
+// and KDA_PREFILL_SEGMENT_CHUNKS (>= 1) fixes L instead; both are read at
+// every call, and a workspace must be sized under the same settings as the
+// call that uses it.
+static size_t segment_budget_bytes(long long inter_workgroups) {
   const char* e = getenv("KDA_PREFILL_SEGMENT_KB");
   const long long v = e ? atoll(e) : 0;
-  return (size_t)(v >= 1 ? v : 160 * 1024) << 10;
+  if (v >= 1) return (size_t)v << 10;
+  return inter_workgroups <= 512 ? (size_t)160 << 20 : (size_t)8 << 30;
 }
 
-int prefill_segment_chunks(int total_chunks, int H, int D, int chunk, bool in_bf16) {
-  if (total_chunks <= 0) return 0;
+static int segment_chunks_override() {
+  const char* e = getenv("KDA_PREFILL_SEGMENT_CHUNKS");
+  const long long v = e ? atoll(e) : 0;
+  return v >= 1 && v <= (1 << 30) ? (int)v : 0;
+}
+
+namespace {
+struct SeqCounts {  // chunk counts of the sequences, on the host
+  int num_seqs;
+  const int32_t* cu;  // host cu_seqlens or nullptr
+  int seq_len, C;
+  int nch(int n) const {
+    const long long len = cu ? (long long)cu[n + 1] - cu[n] : seq_len;
+    return (int)((len + C - 1) / C);
+  }
+  // chunk slots of the segment that starts at local chunk c0
+  long long slots(int c0, int L) const {
+    long long t = 0;
+    for (int n = 0; n < num_seqs; ++n) {
+      const int c = nch(n) - c0;
+      t += c <= 0 ? 0 : (c < L ? c : L);
+    }
+    return t;
+  }
+};
+}  // namespace
+
+SegmentPlan plan_segments(int num_seqs, const int32_t* cu_host, int seq_len, int H, int D,
+                          int chunk, bool in_bf16) {
+  const SeqCounts sc{num_seqs, cu_host, seq_len, chunk};
+  int max_nch = 0;
+  for (int n = 0; n < num_seqs; ++n) max_nch = max_nch > sc.nch(n) ? max_nch : sc.nch(n);
+  SegmentPlan p;
+  if (max_nch == 0) return p;  // one pass of the inter kernel settles the states
   const size_t per = (size_t)H * prefill_chunk_bytes(D, chunk, in_bf16);
-  size_t most = segment_budget_bytes() / per;
-  if (most < 1) most = 1;
-  // Equal segments rather than full ones and a short tail.
-  const size_t nseg = (total_chunks + most - 1) / most;
-  return (int)((total_chunks + nseg - 1) / nseg);
+  // inter-chunk workgroups at 16 value columns each
+  const size_t budget = segment_budget_bytes((long long)num_seqs * H * (D / 16));
+  int lo = max_nch < 16 ? max_nch : 16, hi = max_nch;
+  if (const int fixed = segment_chunks_override()) {
+    lo = fixed < max_nch ? fixed : max_nch;
+  } else if ((size_t)sc.slots(0, lo) * per <= budget) {
+    while (lo < hi) {  // largest L that fits (slots grow with L)
+      const int mid = lo + (hi - lo + 1) / 2;
+      if ((size_t)sc.slots(0, mid) * per <= budget)
+        lo = mid;
+      else
+        hi = mid - 1;
+    }
+  }
+  p.nseg = (max_nch + lo - 1) / lo;
+  p.L = (max_nch + p.nseg - 1) / p.nseg;
+  p.max_slots = sc.slots(0, p.L);
+  return p;
 }
 
-static size_t carry_bytes(int num_seqs, int total_chunks, int seg, int H, int D) {
-  return seg < total_chunks ? align256((size_t)num_seqs * H * D * D * sizeof(float)) : 0;
+// The slot table exists for varlen input only.
+static size_t table_bytes(int num_seqs, bool varlen) {
+  return varlen ? align256(sizeof(int32_t) * (size_t)(num_seqs + 1)) : 0;
 }
 
-size_t prefill_workspace_bytes(int num_seqs, int total_chunks, int H, int D, int chunk,
-                               bool in_bf16) {
-  const int seg = prefill_segment_chunks(total_chunks, H, D, chunk, in_bf16);
-  return table_bytes(num_seqs, total_chunks) + carry_bytes(num_seqs, total_chunks, seg, H, D) +
-         (size_t)seg * H * prefill_chunk_bytes(D, chunk, in_bf16);
+static size_t carry_bytes(const SegmentPlan& p, int num_seqs, int H, int D) {
+  return p.nseg > 1 ? align256((size_t)num_seqs * H * D * D * sizeof(float)) : 0;
+}
+
+size_t prefill_workspace_bytes(int num_seqs, const int32_t* cu_host, int seq_len, int H, int D,
+                               int chunk, bool in_bf16) {
+  const SegmentPlan p = plan_segments(num_seqs, cu_host, seq_len, H, D, chunk, in_bf16);
+  return table_bytes(num_seqs, cu_host != nullptr) + carry_bytes(p, num_seqs, H, D) +
+         (size_t)p.max_slots * H * prefill_chunk_bytes(D, chunk, in_bf16);
 }
 
 // ---------------------------------------------------------------------------
@@ -131,10 +186,11 @@ size_t prefill_workspace_bytes(int num_seqs, int total_chunks, int H, int D, int
 // ---------------------------------------------------------------------------
 struct SeqInfo {
   const int32_t* cu;        // device cu_seqlens or nullptr
-  const int32_t* chunk_off; // [num_seqs + 1] chunk offsets (varlen only)
-  const int32_t* chunk_seq; // [total_chunks] sequence of each chunk (varlen only)
-  int num_seqs, seq_len, total_tokens, total_chunks;
-  int seg_lo, seg_hi;       // chunks [seg_lo, seg_hi) of the packed order in this launch
+  const int32_t* slot_off;  // varlen: [num_seqs + 1] first workspace slot of each sequence
+  int num_seqs, seq_len, total_tokens;
+  int c0, L;                // this segment: local chunks [c0, c0 + L) of every sequence
+  int slot_cnt;             // fixed length: slots of each sequence in this segment
+  int max_slots;            // workspace capacity, in (chunk, all heads) slots
 };
 
 __device__ __forceinline__ int clampi(int x, int lo, int hi) { return x < lo ? lo : (x > hi ? hi : x); }
@@ -152,35 +208,37 @@ __device__ __forceinline__ void seq_bounds(const SeqInfo& s, int n, int& bos, in
 template <int C>
 __device__ __forceinline__ int chunks_of(int len) { return (len + C - 1) / C; }
 
-// Varlen chunk table: block n writes chunk_off[n] (and chunk_off[N] for the
-// last block) and chunk_seq[chunk_off[n] .. chunk_off[n+1]) = n.
-__global__ __launch_bounds__(256) void chunk_table_kernel(const int32_t* __restrict__ cu,
-                                                          int32_t* __restrict__ chunk_off,
-                                                          int32_t* __restrict__ chunk_seq,
-                                                          int num_seqs, int total_tokens,
-                                                          int total_chunks, int C) {
-  const int n = blockIdx.x;
-  __shared__ int part[256];
+// Varlen segment table: slot_off[n] = sum over m < n of the number of local
+// chunks of sequence m in [c0, c0 + L); slot_off[N] is the segment's total.
+// One workgroup; thread t handles a contiguous run of sequences.
+__global__ __launch_bounds__(1024) void segment_table_kernel(const int32_t* __restrict__ cu,
+                                                             int32_t* __restrict__ slot_off,
+                                                             int num_seqs, int total_tokens, int C,
+                                                             int c0, int L) {
+  __shared__ int part[1024];
+  const int t = threadIdx.x;
+  const int per = (num_seqs + 1023) / 1024;
+  const int n0 = t * per, n1 = min(num_seqs, n0 + per);
+  auto count = [&](int n) {
+    const int b = clampi(cu[n], 0, total_tokens), e = clampi(cu[n + 1], b, total_tokens);
+    return clampi((e - b + C - 1) / C - c0, 0, L);
+  };
   int acc = 0;
-  for (int m = threadIdx.x; m < n; m += 256) {
-    const int b = clampi(cu[m], 0, total_tokens), e = clampi(cu[m + 1], b, total_tokens);
-    acc += (e - b + C - 1) / C;
-  }
-  part[threadIdx.x] = acc;
+  for (int n = n0; n < n1; ++n) acc += count(n);
+  part[t] = acc;
   __syncthreads();
-  for (int s = 128; s > 0; s >>= 1) {
-    if (threadIdx.x < s) part[threadIdx.x] += part[threadIdx.x + s];
+  for (int d = 1; d < 1024; d <<= 1) {
+    const int v = t >= d ? part[t - d] : 0;
+    __syncthreads();
+    part[t] += v;
     __syncthreads();
   }
-  const int off = part[0];
-  const int b = clampi(cu[n], 0, total_tokens), e = clampi(cu[n + 1], b, total_tokens);
-  const int nc = (e - b + C - 1) / C;
-  if (threadIdx.x == 0) {
-    chunk_off[n] = off;
-    if (n == num_seqs - 1) chunk_off[num_seqs] = off + nc;
+  int off = part[t] - acc;
+  for (int n = n0; n < n1; ++n) {
+    slot_off[n] = off;
+    off += count(n);
   }
-  for (int c = threadIdx.x; c < nc; c += 256)
-    if (off + c < total_chunks) chunk_seq[off + c] = n;
+  if (t == 1023) slot_off[num_seqs] = part[1023];
 }
 
 // ---------------------------------------------------------------------------
@@ -441,7 +499,7 @@ __global__ __launch_bounds__(kIntraThreads, 4) void intra_chunk_kernel(KernelPtr
   static_assert(NW % NRT == 0, "a wave's fragments share one row tile");
   extern __shared__ __attribute__((aligned(16))) char smem[];
 
-  const int cid = si.seg_lo + blockIdx.x;  // chunk in the packed order
+  const int slot = blockIdx.x;  // (sequence, local chunk) slot of this segment
   const int h = blockIdx.y;
   const int H = kp.H;
   const int tid = threadIdx.x;
@@ -451,12 +509,19 @@ __global__ __launch_bounds__(kIntraThreads, 4) void intra_chunk_kernel(KernelPtr
   // ---- which sequence and token range ----
   int n, ci;
   if (si.cu) {
-    n = clampi(si.chunk_seq[cid], 0, si.num_seqs - 1);
-    ci = cid - si.chunk_off[n];
+    int lo = 0, hi = si.num_seqs - 1;  // last n with slot_off[n] <= slot
+    while (lo < hi) {
+      const int mid = (lo + hi + 1) >> 1;
+      if (si.slot_off[mid] <= slot)
+        lo = mid;
+      else
+        hi = mid - 1;
+    }
+    n = lo;
+    ci = si.c0 + (slot - si.slot_off[n]);
   } else {
-    const int per = chunks_of<C>(si.seq_len);
-    n = cid / per;
-    ci = cid % per;
+    n = clampi(slot / si.slot_cnt, 0, si.num_seqs - 1);
+    ci = si.c0 + slot % si.slot_cnt;
   }
   int bos, eos;
   seq_bounds(si, n, bos, eos);
@@ -465,7 +530,7 @@ __global__ __launch_bounds__(kIntraThreads, 4) void intra_chunk_kernel(KernelPtr
   const long long t0l = (long long)bos + (long long)(ci < 0 ? 0 : ci) * C;
   const int t0 = (int)(t0l < eos ? t0l : eos);
   const int len = clampi(eos - t0, 0, C);
-  char* blk = kp.ops + ((size_t)blockIdx.x * H + h) * LY::kBytes;
+  char* blk = kp.ops + ((size_t)slot * H + h) * LY::kBytes;
 
   float* tot = reinterpret_cast<float*>(smem + L::oTot);
   float* beta_s = reinterpret_cast<float*>(smem + L::oBeta);
@@ -1192,16 +1257,17 @@ __global__ __launch_bounds__(kInterThreads, 2) void inter_chunk_kernel(KernelPtr
   gm.h = pair % gm.H;
   gm.col0 = DVB * gm.vb;
   seq_bounds(si, gm.n, gm.bos, gm.eos);
-  const int cid0 = si.cu ? clampi(si.chunk_off[gm.n], 0, si.total_chunks) : gm.n * chunks_of<C>(si.seq_len);
-  // Never walk past the chunks the workspace was sized for.
-  gm.nch = min(chunks_of<C>(gm.eos - gm.bos), si.total_chunks - cid0);
-  // This launch covers chunks [seg_lo, seg_hi) of the packed order.  A
-  // sequence without chunks is settled (final = initial state) by the first.
-  const int lo = max(cid0, si.seg_lo), hi = min(cid0 + gm.nch, si.seg_hi);
-  if (gm.nch > 0 ? lo >= hi : si.seg_lo != 0) return;
-  gm.ci_lo = gm.nch > 0 ? lo - cid0 : 0;
-  gm.ci_hi = gm.nch > 0 ? hi - cid0 : 0;
-  gm.cbase = cid0 - si.seg_lo;
+  gm.nch = chunks_of<C>(gm.eos - gm.bos);
+  // This launch covers the sequence's local chunks [c0, c0 + L), held in the
+  // workspace slots base .. base + count - 1.  A sequence without chunks is
+  // settled (final = initial state) by the first segment.
+  const int base = si.cu ? clampi(si.slot_off[gm.n], 0, si.max_slots) : gm.n * si.slot_cnt;
+  gm.ci_lo = si.c0;
+  // Never walk past the slots the workspace was sized for.
+  gm.ci_hi = min(min(si.c0 + si.L, gm.nch), si.c0 + (si.max_slots - base));
+  if (gm.nch > 0 ? gm.ci_lo >= gm.ci_hi : si.c0 != 0) return;
+  if (gm.nch == 0) gm.ci_hi = gm.ci_lo;
+  gm.cbase = base - si.c0;
   gm.s_in = gm.ci_lo == 0 ? kp.s0 : kp.carry;
   gm.s_out = gm.ci_hi == gm.nch ? kp.s1 : kp.carry;
 
@@ -1254,15 +1320,17 @@ static void launch_inter(const PrefillArgs& a, const KernelPtrs& kp, const SeqIn
 template <class M, int D, int C>
 static hipError_t launch_prefill_t(const PrefillArgs& a) {
   char* ws = reinterpret_cast<char*>(a.workspace);
-  const int seg = prefill_segment_chunks(a.total_chunks, a.H, D, C, a.in_bf16);
+  const SegmentPlan plan =
+      plan_segments(a.num_seqs, a.cu_seqlens_host, a.seq_len, a.H, D, C, a.in_bf16);
+  const SeqCounts sc{a.num_seqs, a.cu_seqlens_host, a.seq_len, C};
   SeqInfo si;
   si.cu = a.cu_seqlens;
   si.num_seqs = a.num_seqs;
   si.seq_len = a.seq_len;
   si.total_tokens = a.total_tokens;
-  si.total_chunks = a.total_chunks;
-  si.chunk_off = reinterpret_cast<const int32_t*>(ws);
-  si.chunk_seq = reinterpret_cast<const int32_t*>(ws + align256(sizeof(int32_t) * (a.num_seqs + 1)));
+  si.slot_off = reinterpret_cast<const int32_t*>(ws);
+  si.max_slots = plan.max_slots;
+  si.L = plan.L;
   KernelPtrs kp;
   kp.q = a.q;
   kp.k = a.k;
@@ -1272,41 +1340,40 @@ static hipError_t launch_prefill_t(const PrefillArgs& a) {
   kp.o = a.o;
   kp.s0 = a.initial_state;
   kp.s1 = a.final_state;
-  char* after_table = ws + table_bytes(a.num_seqs, a.total_chunks);
-  const size_t carry = carry_bytes(a.num_seqs, a.total_chunks, seg, a.H, D);
+  char* after_table = ws + table_bytes(a.num_seqs, a.cu_seqlens != nullptr);
+  const size_t carry = carry_bytes(plan, a.num_seqs, a.H, D);
   kp.carry = carry ? reinterpret_cast<float*>(after_table) : nullptr;
   kp.ops = after_table + carry;
   kp.H = a.H;
 
-  if (a.cu_seqlens) {
-    hipLaunchKernelGGL(chunk_table_kernel, dim3(a.num_seqs), dim3(256), 0, a.stream, a.cu_seqlens,
-                       const_cast<int32_t*>(si.chunk_off), const_cast<int32_t*>(si.chunk_seq),
-                       a.num_seqs, a.total_tokens, a.total_chunks, C);
-  }
   constexpr size_t lds = IntraLds<M, D, C>::kTotal;
   static_assert(lds <= 160 * 1024, "intra-chunk LDS");
-  if (a.total_chunks > 0) {
+  if (plan.max_slots > 0) {
     hipError_t e = hipFuncSetAttribute(reinterpret_cast<const void*>(&intra_chunk_kernel<M, D, C>),
                                        hipFuncAttributeMaxDynamicSharedMemorySize, (int)lds);
     if (e != hipSuccess) return e;
   }
   const int nct = choose_nct(a.num_seqs * a.H, D);
-  // One pass when there are no chunks: sequences without tokens still
-  // copy their initial state to the final state.
-  int lo = 0;
-  do {
-    const int hi = lo + seg < a.total_chunks ? lo + seg : a.total_chunks;
-    si.seg_lo = lo;
-    si.seg_hi = hi;
-    if (hi > lo)
-      hipLaunchKernelGGL((intra_chunk_kernel<M, D, C>), dim3(hi - lo, a.H), dim3(kIntraThreads), lds,
-                         a.stream, kp, si);
+  for (int s = 0; s < plan.nseg; ++s) {
+    si.c0 = s * plan.L;
+    const long long slots = sc.slots(si.c0, plan.L);
+    if (a.cu_seqlens) {
+      hipLaunchKernelGGL(segment_table_kernel, dim3(1), dim3(1024), 0, a.stream, a.cu_seqlens,
+                         const_cast<int32_t*>(si.slot_off), a.num_seqs, a.total_tokens, C, si.c0,
+                         plan.L);
+      si.slot_cnt = 0;
+    } else {
+      const int c = sc.nch(0) - si.c0;
+      si.slot_cnt = c <= 0 ? 0 : (c < plan.L ? c : plan.L);
+    }
+    if (slots > 0)
+      hipLaunchKernelGGL((intra_chunk_kernel<M, D, C>), dim3((unsigned)slots, a.H), dim3(kIntraThreads),
+                         lds, a.stream, kp, si);
     if (nct == 2)
       launch_inter<M, D, C, 2>(a, kp, si);
     else
       launch_inter<M, D, C, 1>(a, kp, si);
-    lo = hi;
-  } while (lo < a.total_chunks);
+  }
   return hipGetLastError();
 }
 

@@ -91,34 +91,38 @@ def test_workspace_size(lib):
     # B=1, T=4096, H=32, D=128, C=64, bf16: 64 chunks of 32 heads x 147968 B
     # (Q*gam 32 KB, W 32 KB, K-bar 32 KB, P 16 KB, T 16 KB as bf16 hi + lo;
     # V^T 16 KB; gam_n 512 B).  The workspace holds one segment of chunks
-    # (a 160 MiB budget: at most 35 chunks, so 2 equal segments of 32), the
-    # fp32 state carried between segments (32 x 128 x 128 x 4 B) and the
-    # 256-byte-aligned chunk table.
+    # (a 160 MiB budget: at most 35 chunks, so 2 equal segments of 32) and the
+    # fp32 state carried between segments (32 x 128 x 128 x 4 B); fixed-length
+    # input needs no slot table.
     if "KDA_PREFILL_SEGMENT_KB" in os.environ:
         pytest.skip("segment budget overridden")
     n = kda.workspace_size(1, 4096, 32, 128, 1, 64, kda.KDA_BF16)
-    assert n == 32 * 32 * 147968 + 32 * 128 * 128 * 4 + 256 + 256
+    assert n == 32 * 32 * 147968 + 32 * 128 * 128 * 4
     # one segment: no carry buffer
     n1 = kda.workspace_size(1, 2048, 32, 128, 1, 64, kda.KDA_BF16)
-    assert n1 == 32 * 32 * 147968 + 256 + 256
+    assert n1 == 32 * 32 * 147968
+    # varlen, fp32, D=64, C=16, H=4: lengths 100, 0, 200 -> 7, 0, 13 chunks,
+    # one segment of 13 local chunks holding 7 + 13 slots of 4 x 28928 B
+    # (Q*gam 4 KB, W 4 KB, K-bar 8 KB, P 2 KB, T 2 KB, V^T 8 KB, gam_n 256 B,
+    # a multiple of 256 B), plus the 256-byte slot table.
+    cu = np.array([0, 100, 100, 300], dtype=np.int32)
+    m = kda.workspace_size(1, 300, 4, 64, 3, 16, kda.KDA_F32, cu)
+    assert m == 20 * 4 * 28928 + 256
+    with pytest.raises(kda.KDAError):
+        kda.workspace_size(1, 300, 4, 80, 3, 16, kda.KDA_F32, cu)
 
 
 def test_workspace_segments(monkeypatch):
-    # A 1000 KB budget holds 6 chunks of 32 heads (4.5 MiB per chunk would
-    # not fit, so use H=1): 64 chunks -> 11 segments of at most 6, equalised
-    # to ceil(64 / 11) = 6 chunks.
+    # Segments hold at least 16 local chunks: with a 1000 KB budget (less
+    # than 16 chunks of one head, 2.37 MB), T=4096 (64 chunks) runs as 4
+    # segments of 16, plus the carried state.
     monkeypatch.setenv("KDA_PREFILL_SEGMENT_KB", "1000")
     n = kda.workspace_size(1, 4096, 1, 128, 1, 64, kda.KDA_BF16)
-    assert n == 6 * 147968 + 128 * 128 * 4 + 256 + 256
-    # below one chunk per segment, segments hold one chunk
-    monkeypatch.setenv("KDA_PREFILL_SEGMENT_KB", "1")
+    assert n == 16 * 147968 + 128 * 128 * 4
+    # 4000 KB fits 27 chunks: 3 segments, evened out to 22 chunks each.
+    monkeypatch.setenv("KDA_PREFILL_SEGMENT_KB", "4000")
     n = kda.workspace_size(1, 4096, 1, 128, 1, 64, kda.KDA_BF16)
-    assert n == 147968 + 128 * 128 * 4 + 256 + 256
-    cu = np.array([0, 100, 100, 300], dtype=np.int32)
-    m = kda.workspace_size(1, 300, 4, 64, 3, 16, kda.KDA_F32, cu)
-    assert m > 0 and m % 256 == 0
-    with pytest.raises(kda.KDAError):
-        kda.workspace_size(1, 300, 4, 80, 3, 16, kda.KDA_F32, cu)
+    assert n == 22 * 147968 + 128 * 128 * 4
 
 
 def test_decode_validation(lib):

@@ -236,14 +236,15 @@ def test_prefill_varlen(kda, C):
     np.testing.assert_array_equal(fin[2], s0[2])
 
 
-@pytest.mark.parametrize("dtype,C,seg_kb", [("bf16", 16, 1), ("f32", 32, 500), ("bf16", 64, 700)])
-def test_prefill_segments(kda, monkeypatch, dtype, C, seg_kb):
-    """A small per-segment operand budget makes the prefill run as many
-    intra/inter passes (one chunk each at 1 KB), with every sequence's state
-    carried between passes: packed sequences start and end inside segments,
-    one is empty, and the final state is written over the initial state."""
-    monkeypatch.setenv("KDA_PREFILL_SEGMENT_KB", str(seg_kb))
-    say(f"prefill segments dtype={dtype} C={C} budget={seg_kb} KB")
+@pytest.mark.parametrize("dtype,C,seg", [("bf16", 16, 1), ("f32", 32, 2), ("bf16", 64, 3)])
+def test_prefill_segments(kda, monkeypatch, dtype, C, seg):
+    """Short segments (1, 2 or 3 local chunks of every sequence per pass) make
+    the prefill run as many intra/inter passes, each sequence's state carried
+    between passes: packed sequences of different lengths finish in different
+    segments, one is empty, and the final state is written over the initial
+    state."""
+    monkeypatch.setenv("KDA_PREFILL_SEGMENT_CHUNKS", str(seg))
+    say(f"prefill segments dtype={dtype} C={C} segment={seg} chunks")
     lens = [37, 0, 130, 5, 200, 64]
     cu = np.concatenate([[0], np.cumsum(lens)]).astype(np.int32)
     rng = np.random.default_rng([21, C])
@@ -260,6 +261,24 @@ def test_prefill_segments(kda, monkeypatch, dtype, C, seg_kb):
     say(f"  o err {eo_:.2e}  state err {es_:.2e}")
     assert eo_ <= TOL[dtype] and es_ <= TOL[dtype]
     np.testing.assert_array_equal(host(st)[1], s0[1])
+
+
+def test_prefill_fixed_length_segments(kda, monkeypatch):
+    """B=3 equal sequences (no cu_seqlens) in segments of 2 chunks, fp32."""
+    monkeypatch.setenv("KDA_PREFILL_SEGMENT_CHUNKS", "2")
+    say("prefill fixed-length segments B=3")
+    B, T, H = 3, 150, 2
+    rng = np.random.default_rng(22)
+    x = I.draw_tokens(rng, B * T, H, 64, 64, "f32")
+    s0 = I.draw_states(rng, B, H, 64, 64)
+    cu = np.arange(B + 1, dtype=np.int32) * T
+    eo, ef = oracle.kda_recurrent(x.q, x.k, x.v, x.g, x.beta, s0, cu_seqlens=cu)
+    q, k, v, g, b = tok_to_dev(x, B=B)
+    o, fin = kda.prefill(q, k, v, g, b, torch.from_numpy(s0).to(DEV), chunk_size=32)
+    torch.cuda.synchronize()
+    eo_, es_ = rel(host(o).reshape(B * T, H, 64), eo), rel(host(fin), ef)
+    say(f"  o err {eo_:.2e}  state err {es_:.2e}")
+    assert eo_ <= TOL["f32"] and es_ <= TOL["f32"]
 
 
 def test_prefill_workload1_full(kda):
