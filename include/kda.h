@@ -66,14 +66,17 @@ int kda_version(void);
  * same meaning as in kda_prefill.  Returns 0 and writes nothing to *bytes on
  * an argument error (the status says which).
  *
- * The prefill runs in segments of consecutive chunks; the workspace holds the
- * chunk table, the intra-chunk operands of one segment (144.5 KB per chunk
- * and head at Dk = Dv = 128, C = 64; segments are sized to about 160 MiB of
- * operands) and, when there is more than one segment, the fp32 state carried
- * between them (num_seqs * H * Dk * Dv * 4 bytes).  So the size is bounded
- * for any sequence length.  The environment variable KDA_PREFILL_SEGMENT_KB
- * overrides the per-segment budget; a workspace must be sized under the same
- * setting as the kda_prefill call that uses it.
+ * The prefill runs in segments, each covering the same range of local chunks
+ * of every sequence.  The workspace holds a per-segment slot table (varlen
+ * only), the intra-chunk operands of one segment (144.5 KB per chunk and head
+ * at Dk = Dv = 128, C = 64; about 160 MiB per segment when there are few
+ * (sequence, head) pairs, up to 8 GiB otherwise) and, when there is more
+ * than one segment, the fp32 state carried between them (num_seqs * H * Dk *
+ * Dv * 4 bytes).  So the size is bounded for any sequence length.  The
+ * environment variables KDA_PREFILL_SEGMENT_KB (operand budget) and
+ * KDA_PREFILL_SEGMENT_CHUNKS (segment length) override the choice; a
+ * workspace must be sized under the same settings as the kda_prefill call
+ * that uses it.
  */
 kda_status kda_prefill_workspace_size(int B, int T, int H, int Dk, int Dv,
                                       int num_seqs,
