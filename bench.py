@@ -87,6 +87,88 @@ def measured_traffic(unit, names):
     return t["bytes"]
 
 
+def prefill_bytes_general(tokens, H, d, num_seqs, states_in, states_out):
+    return tokens * H * (3 * 2 * d + 4 * d + 4 + 4 * d) + num_seqs * H * d * d * 4 * (
+        int(states_in) + int(states_out))
+
+
+def prefill_flops_general(tokens, H, d, C):
+    return H * (6 * tokens * d * d + 3 * tokens * C * d + tokens * C * C)
+
+
+def time_prefill(torch, kda, args, reps, **kw):
+    """Mean time (s) of kda.prefill over ``reps`` calls after one warm-up,
+    with the output, final state and workspace allocated once."""
+    q = args[0]
+    kda.prefill(*args, **kw)
+    torch.cuda.synchronize()
+    a, b = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    a.record()
+    for _ in range(reps):
+        kda.prefill(*args, **kw)
+    b.record()
+    torch.cuda.synchronize()
+    return a.elapsed_time(b) / reps / 1e3
+
+
+def other_workloads(torch, kda, I, dev):
+    """Throughput on the other synthetic workloads (secondary to ``value``)."""
+    out = {}
+    # varlen: 16 packed sequences, lengths U[512, 8192], initial states
+    w = I.WORKLOADS[2]
+    cu = I.cu_seqlens_from_lengths(I.varlen_lengths(w))
+    n_tok, N = int(cu[-1]), len(cu) - 1
+    q, k, v, g, b = I.device_tokens(torch, n_tok, w.H, w.Dk, w.Dv, 2002, dev)
+    s0 = torch.from_numpy(I.workload_states(w, N)).to(dev)
+    cud = torch.from_numpy(cu).to(dev)
+    fin = torch.empty_like(s0)
+    o = torch.empty((1, n_tok, w.H, w.Dv), dtype=torch.float32, device=dev)
+    ws = torch.empty(kda.workspace_size(1, n_tok, w.H, w.Dk, N, 64, kda.KDA_BF16, cu),
+                     dtype=torch.uint8, device=dev)
+    t = time_prefill(torch, kda, (q, k, v, g, b, s0, cud), 3, cu_seqlens_host=cu, chunk_size=64,
+                     o=o, final_state=fin, workspace=ws)
+    by = prefill_bytes_general(n_tok, w.H, w.Dk, N, True, True)
+    out["varlen"] = {"workload": f"kda_prefill 16 packed sequences ({n_tok} tokens), H=32, d=128, "
+                                 "chunk 64, bf16 in / fp32 out, initial and final states",
+                     "ms_per_call": round(t * 1e3, 3), "tokens_per_s": round(n_tok / t, 1),
+                     "algorithmic_GBps": round(by / t / 1e9, 1),
+                     "hbm_frac": round(by / t / 1e9 / HBM_PEAK_GBS, 4),
+                     "mfma_frac_bf16": round(prefill_flops_general(n_tok, w.H, w.Dk, 64) / t / 1e12
+                                             / BF16_PEAK_TFLOPS, 4)}
+    del q, k, v, g, b, o, ws, fin
+    torch.cuda.empty_cache()
+    # long context: one sequence of 1,048,576 tokens
+    w = I.WORKLOADS[3]
+    q, k, v, g, b = I.device_tokens(torch, w.T, w.H, w.Dk, w.Dv, 3003, dev)
+    o = torch.empty((1, w.T, w.H, w.Dv), dtype=torch.float32, device=dev)
+    fin = torch.empty((1, w.H, w.Dk, w.Dv), dtype=torch.float32, device=dev)
+    ws = torch.empty(kda.workspace_size(1, w.T, w.H, w.Dk, 1, 64, kda.KDA_BF16),
+                     dtype=torch.uint8, device=dev)
+    t = time_prefill(torch, kda, (q, k, v, g, b, None), 2, chunk_size=64, o=o, final_state=fin,
+                     workspace=ws)
+    by = prefill_bytes_general(w.T, w.H, w.Dk, 1, False, True)
+    out["long_context"] = {"workload": "kda_prefill B=1 H=32 T=1,048,576 d=128 chunk 64, bf16 in / "
+                                       "fp32 out, final state",
+                           "ms_per_call": round(t * 1e3, 3), "tokens_per_s": round(w.T / t, 1),
+                           "algorithmic_GBps": round(by / t / 1e9, 1),
+                           "hbm_frac": round(by / t / 1e9 / HBM_PEAK_GBS, 4),
+                           "workspace_bytes": int(ws.numel())}
+    del q, k, v, g, b, o, ws, fin
+    torch.cuda.empty_cache()
+    # tiny fp32 case (launch-bound; chunk 16 and 64)
+    w = I.WORKLOADS[0]
+    x = I.workload_tokens(w)
+    f32 = lambda a: torch.from_numpy(np.ascontiguousarray(a)).to(dev)[None]
+    args = (f32(x.q), f32(x.k), f32(x.v), f32(x.g), f32(x.beta), None)
+    tiny = {}
+    for C in (16, 64):
+        t = time_prefill(torch, kda, args, 20, chunk_size=C)
+        tiny[f"chunk{C}_us_per_call"] = round(t * 1e6, 2)
+        tiny[f"chunk{C}_tokens_per_s"] = round(w.T / t, 1)
+    out["tiny_fp32"] = {"workload": "kda_prefill B=1 H=1 T=256 d=64 fp32", **tiny}
+    return out
+
+
 def log(*a):
     print(*a, file=sys.stderr, flush=True)
 
@@ -127,6 +209,8 @@ def main():
     ap.add_argument("--steps", type=int, default=20)
     ap.add_argument("--warmup", type=int, default=5)
     ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--no-other-workloads", action="store_true",
+                    help="skip the secondary varlen / long-context / tiny measurements")
     args = ap.parse_args()
     if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) != 1:
         print("bench.py measures one GPU only: every configuration here fits one MI355X "
@@ -238,6 +322,11 @@ def main():
                     "frac_of_measured_copy": round(p_gbs / copy_gbs, 4)}
     roof = decode_roof if dec_s >= pre_s else prefill_roof
 
+    others = None
+    if not args.no_other_workloads:
+        log("timing the other workloads")
+        others = other_workloads(torch, kda, I, dev)
+
     cpu = None
     if not args.no_cpu_baseline:
         log("timing the CPU oracle")
@@ -270,6 +359,7 @@ def main():
         "prefill_roofline": prefill_roof,
         "decode_roofline": decode_roof,
         "cpu_baseline": cpu,
+        "other_workloads": others,
         "wall_s_timed_region": round(t_wall, 4),
     }
     print(json.dumps(line), flush=True)

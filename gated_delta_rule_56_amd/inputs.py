@@ -240,3 +240,35 @@ def long_blocks(w: Workload, blocks, block_tokens: int = 4096, workers: int = 16
             if j < len(blocks):
                 futs[j] = ex.submit(long_block, w, blocks[j], block_tokens)
             yield b, x
+
+
+def device_tokens(torch, T: int, H: int, Dk: int, Dv: int, seed: int, device,
+                  dtype: str = "bf16", chunk_tokens: int = 65536):
+    """The same input recipe drawn on the GPU with torch's seeded generator.
+
+    For throughput measurements at sizes where drawing on the host would
+    dominate (the million-token workload): the values follow the recipe above
+    but come from torch's generator, so they differ from ``draw_tokens``.
+    The L2 normalisation runs in float32 here.  Returns device tensors q, k, v
+    ``[1, T, H, D]`` (bf16 or float32), g ``[1, T, H, Dk]`` and beta
+    ``[1, T, H]`` (float32), filled ``chunk_tokens`` tokens at a time.
+    """
+    gen = torch.Generator(device=device)
+    gen.manual_seed(seed)
+    dt = torch.bfloat16 if dtype == "bf16" else torch.float32
+    q = torch.empty((1, T, H, Dk), dtype=dt, device=device)
+    k = torch.empty_like(q)
+    v = torch.empty((1, T, H, Dv), dtype=dt, device=device)
+    g = torch.empty((1, T, H, Dk), dtype=torch.float32, device=device)
+    beta = torch.empty((1, T, H), dtype=torch.float32, device=device)
+    for t0 in range(0, T, chunk_tokens):
+        n = min(chunk_tokens, T - t0)
+        sl = slice(t0, t0 + n)
+        for dst, d in ((q, Dk), (k, Dk)):
+            x = torch.randn((n, H, d), generator=gen, device=device)
+            dst[0, sl] = (x / x.norm(dim=-1, keepdim=True)).to(dt)
+        v[0, sl] = torch.randn((n, H, Dv), generator=gen, device=device).to(dt)
+        g[0, sl] = -torch.nn.functional.softplus(
+            torch.randn((n, H, Dk), generator=gen, device=device)) * 0.1
+        beta[0, sl] = torch.sigmoid(torch.randn((n, H), generator=gen, device=device))
+    return q, k, v, g, beta
