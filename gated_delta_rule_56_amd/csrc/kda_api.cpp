@@ -70,12 +70,13 @@ kda_status kda_prefill_workspace_size(int B, int T, int H, int Dk, int Dv, int n
   return KDA_OK;
 }
 
-kda_status kda_prefill(const void* q, const void* k, const void* v, const float* g,
-                       const float* beta, void* o, const float* initial_state,
-                       float* final_state, const int32_t* cu_seqlens,
-                       const int32_t* cu_seqlens_host, int B, int T, int H, int Dk, int Dv,
-                       int num_seqs, int chunk_size, kda_dtype in_dtype, kda_dtype out_dtype,
-                       void* workspace, size_t workspace_bytes, void* stream) {
+static kda_status prefill_impl(bool scalar_g, const void* q, const void* k, const void* v,
+                               const float* g, const float* beta, void* o,
+                               const float* initial_state, float* final_state,
+                               const int32_t* cu_seqlens, const int32_t* cu_seqlens_host,
+                               int B, int T, int H, int Dk, int Dv, int num_seqs,
+                               int chunk_size, kda_dtype in_dtype, kda_dtype out_dtype,
+                               void* workspace, size_t workspace_bytes, void* stream) {
   if (H < 1 || !valid_dtype(in_dtype) || !valid_dtype(out_dtype)) return KDA_ERR_INVALID_ARG;
   if (!supported_head(Dk, Dv) || !supported_chunk(chunk_size)) return KDA_ERR_UNSUPPORTED;
   const void* ptrs[] = {q, k, v, g, beta, o, initial_state, final_state, cu_seqlens};
@@ -110,14 +111,16 @@ kda_status kda_prefill(const void* q, const void* k, const void* v, const float*
   a.chunk = chunk_size;
   a.in_bf16 = in_dtype == KDA_BF16;
   a.out_bf16 = out_dtype == KDA_BF16;
+  a.scalar_g = scalar_g;
   a.workspace = workspace;
   a.stream = reinterpret_cast<hipStream_t>(stream);
   return kda::launch_prefill(a) == hipSuccess ? KDA_OK : KDA_ERR_HIP;
 }
 
-kda_status kda_decode_step(const void* q, const void* k, const void* v, const float* g,
-                           const float* beta, float* state, void* o, int N, int H, int Dk,
-                           int Dv, kda_dtype in_dtype, kda_dtype out_dtype, void* stream) {
+static kda_status decode_impl(bool scalar_g, const void* q, const void* k, const void* v,
+                              const float* g, const float* beta, float* state, void* o, int N,
+                              int H, int Dk, int Dv, kda_dtype in_dtype, kda_dtype out_dtype,
+                              void* stream) {
   if (!q || !k || !v || !g || !beta || !state || !o) return KDA_ERR_INVALID_ARG;
   if (N < 0 || H < 1 || !valid_dtype(in_dtype) || !valid_dtype(out_dtype))
     return KDA_ERR_INVALID_ARG;
@@ -139,8 +142,43 @@ kda_status kda_decode_step(const void* q, const void* k, const void* v, const fl
   a.D = Dk;
   a.in_bf16 = in_dtype == KDA_BF16;
   a.out_bf16 = out_dtype == KDA_BF16;
+  a.scalar_g = scalar_g;
   a.stream = reinterpret_cast<hipStream_t>(stream);
   return kda::launch_decode(a) == hipSuccess ? KDA_OK : KDA_ERR_HIP;
+}
+
+kda_status kda_prefill(const void* q, const void* k, const void* v, const float* g,
+                       const float* beta, void* o, const float* initial_state,
+                       float* final_state, const int32_t* cu_seqlens,
+                       const int32_t* cu_seqlens_host, int B, int T, int H, int Dk, int Dv,
+                       int num_seqs, int chunk_size, kda_dtype in_dtype, kda_dtype out_dtype,
+                       void* workspace, size_t workspace_bytes, void* stream) {
+  return prefill_impl(false, q, k, v, g, beta, o, initial_state, final_state, cu_seqlens,
+                      cu_seqlens_host, B, T, H, Dk, Dv, num_seqs, chunk_size, in_dtype, out_dtype,
+                      workspace, workspace_bytes, stream);
+}
+
+kda_status gdn_prefill(const void* q, const void* k, const void* v, const float* g,
+                       const float* beta, void* o, const float* initial_state,
+                       float* final_state, const int32_t* cu_seqlens,
+                       const int32_t* cu_seqlens_host, int B, int T, int H, int Dk, int Dv,
+                       int num_seqs, int chunk_size, kda_dtype in_dtype, kda_dtype out_dtype,
+                       void* workspace, size_t workspace_bytes, void* stream) {
+  return prefill_impl(true, q, k, v, g, beta, o, initial_state, final_state, cu_seqlens,
+                      cu_seqlens_host, B, T, H, Dk, Dv, num_seqs, chunk_size, in_dtype, out_dtype,
+                      workspace, workspace_bytes, stream);
+}
+
+kda_status kda_decode_step(const void* q, const void* k, const void* v, const float* g,
+                           const float* beta, float* state, void* o, int N, int H, int Dk,
+                           int Dv, kda_dtype in_dtype, kda_dtype out_dtype, void* stream) {
+  return decode_impl(false, q, k, v, g, beta, state, o, N, H, Dk, Dv, in_dtype, out_dtype, stream);
+}
+
+kda_status gdn_decode_step(const void* q, const void* k, const void* v, const float* g,
+                           const float* beta, float* state, void* o, int N, int H, int Dk,
+                           int Dv, kda_dtype in_dtype, kda_dtype out_dtype, void* stream) {
+  return decode_impl(true, q, k, v, g, beta, state, o, N, H, Dk, Dv, in_dtype, out_dtype, stream);
 }
 
 }  // extern "C"

@@ -23,7 +23,8 @@
 
 namespace kda {
 
-template <typename in_t, int DK, int DV, bool OUT_BF16>
+// SG: scalar gate (Gated DeltaNet): g holds one log-decay per (n, h).
+template <typename in_t, int DK, int DV, bool OUT_BF16, bool SG>
 __global__ __launch_bounds__(256) void decode_step_kernel(
     const in_t* __restrict__ q, const in_t* __restrict__ k, const in_t* __restrict__ v,
     const float* __restrict__ g, const float* __restrict__ beta, float* __restrict__ state,
@@ -43,7 +44,8 @@ __global__ __launch_bounds__(256) void decode_step_kernel(
   const size_t tok = (size_t)nh;
   const in_t* qp = q + tok * DK;
   const in_t* kp = k + tok * DK;
-  const float* gp = g + tok * DK;
+  const float* gp = g + tok * (SG ? 1 : DK);
+  const float ag = SG ? __expf(gp[0]) : 0.f;
   float* sp = state + tok * (size_t)DK * DV;
 
   float kk[RPT], qq[RPT];
@@ -60,7 +62,7 @@ __global__ __launch_bounds__(256) void decode_step_kernel(
     const int i = rg + RG * m;
     kk[m] = (float)kp[i];
     qq[m] = (float)qp[i];
-    const float a = __expf(gp[i]);
+    const float a = SG ? ag : __expf(gp[i]);
 #pragma unroll
     for (int c = 0; c < 4; ++c) {
       s[m][c] *= a;
@@ -126,18 +128,26 @@ __global__ __launch_bounds__(256) void decode_step_kernel(
   }
 }
 
-template <typename in_t, int D>
-static hipError_t launch_decode_t(const DecodeArgs& a) {
+template <typename in_t, int D, bool OUT_BF16>
+static void launch_decode_o(const DecodeArgs& a) {
   const int NH = a.N * a.H;
   dim3 grid(NH), block(256);
-  if (a.out_bf16)
-    hipLaunchKernelGGL((decode_step_kernel<in_t, D, D, true>), grid, block, 0, a.stream,
+  if (a.scalar_g)
+    hipLaunchKernelGGL((decode_step_kernel<in_t, D, D, OUT_BF16, true>), grid, block, 0, a.stream,
                        (const in_t*)a.q, (const in_t*)a.k, (const in_t*)a.v, a.g, a.beta,
                        a.state, a.o, NH);
   else
-    hipLaunchKernelGGL((decode_step_kernel<in_t, D, D, false>), grid, block, 0, a.stream,
+    hipLaunchKernelGGL((decode_step_kernel<in_t, D, D, OUT_BF16, false>), grid, block, 0, a.stream,
                        (const in_t*)a.q, (const in_t*)a.k, (const in_t*)a.v, a.g, a.beta,
                        a.state, a.o, NH);
+}
+
+template <typename in_t, int D>
+static hipError_t launch_decode_t(const DecodeArgs& a) {
+  if (a.out_bf16)
+    launch_decode_o<in_t, D, true>(a);
+  else
+    launch_decode_o<in_t, D, false>(a);
   return hipGetLastError();
 }
 

@@ -18,6 +18,7 @@ struct DecodeArgs {
   void* o;
   int N, H, D;
   bool in_bf16, out_bf16;
+  bool scalar_g;  // g holds one log-decay per (sequence, head)
   hipStream_t stream;
 };
 
@@ -39,6 +40,7 @@ struct PrefillArgs {
   int total_tokens;
   int H, D, chunk;
   bool in_bf16, out_bf16;
+  bool scalar_g;              // g holds one log-decay per (token, head)
   void* workspace;
   hipStream_t stream;
 };

@@ -484,7 +484,9 @@ __device__ __forceinline__ void lds_st_pfrag(ModeF32 m, char* p, const ModeF32::
 // the decayed Q and K are Gram A-operands in registers, Q*gam goes out as
 // whole fragments, and the decay cumsum runs across the 16 lanes of a tile.
 // ---------------------------------------------------------------------------
-template <class M, int D, int C>
+// SDEC: scalar decay (Gated DeltaNet), one log-decay per token and head, g
+// [tokens, H]; otherwise one per key channel, g [tokens, H, D].
+template <class M, int D, int C, bool SDEC>
 __global__ __launch_bounds__(kIntraThreads, 4) void intra_chunk_kernel(KernelPtrs kp, SeqInfo si) {
   typedef typename M::in_t in_t;
   typedef typename M::PFrag PFrag;
@@ -555,10 +557,12 @@ __global__ __launch_bounds__(kIntraThreads, 4) void intra_chunk_kernel(KernelPtr
   const int tok = clampi(t0 + (r < len ? r : len - 1), 0, si.total_tokens - 1);
   Raw8<float> graw[FPW];
   Raw8<in_t> qraw[FPW], kraw[FPW], vraw[FPW];
+  float gscalar = 0.f;
+  if constexpr (SDEC) gscalar = kp.g[(size_t)tok * H + h];
 #pragma unroll
   for (int j = 0; j < FPW; ++j) {
     const size_t base = ((size_t)tok * H + h) * D + 32 * fkb[j] + 8 * lg;
-    graw[j].load(kp.g + base);
+    if constexpr (!SDEC) graw[j].load(kp.g + base);
     qraw[j].load(reinterpret_cast<const in_t*>(kp.q) + base);
     kraw[j].load(reinterpret_cast<const in_t*>(kp.k) + base);
     vraw[j].load(reinterpret_cast<const in_t*>(kp.v) + base);
@@ -572,18 +576,31 @@ __global__ __launch_bounds__(kIntraThreads, 4) void intra_chunk_kernel(KernelPtr
   // ---- step 2: cumulative decay.  Inclusive scan over the 16 tokens of the
   // tile (lanes lr of one lane group), then the totals of earlier tiles ----
   float G[FPW][8];
+  if constexpr (SDEC) {
+    float x = rv ? gscalar : 0.f;  // one scan serves every channel
 #pragma unroll
-  for (int j = 0; j < FPW; ++j)
-#pragma unroll
-    for (int e = 0; e < 8; ++e) {
-      float x = rv ? graw[j].get(e) : 0.f;
-#pragma unroll
-      for (int d = 1; d < 16; d <<= 1) {
-        const float t = __shfl_up(x, d, 16);
-        x += lr >= d ? t : 0.f;
-      }
-      G[j][e] = x;
+    for (int d = 1; d < 16; d <<= 1) {
+      const float t = __shfl_up(x, d, 16);
+      x += lr >= d ? t : 0.f;
     }
+#pragma unroll
+    for (int j = 0; j < FPW; ++j)
+#pragma unroll
+      for (int e = 0; e < 8; ++e) G[j][e] = x;
+  } else {
+#pragma unroll
+    for (int j = 0; j < FPW; ++j)
+#pragma unroll
+      for (int e = 0; e < 8; ++e) {
+        float x = rv ? graw[j].get(e) : 0.f;
+#pragma unroll
+        for (int d = 1; d < 16; d <<= 1) {
+          const float t = __shfl_up(x, d, 16);
+          x += lr >= d ? t : 0.f;
+        }
+        G[j][e] = x;
+      }
+  }
   if (lr == 15) {
 #pragma unroll
     for (int j = 0; j < FPW; ++j)
@@ -1317,7 +1334,7 @@ static void launch_inter(const PrefillArgs& a, const KernelPtrs& kp, const SeqIn
 // ---------------------------------------------------------------------------
 // Host launch
 // ---------------------------------------------------------------------------
-template <class M, int D, int C>
+template <class M, int D, int C, bool SDEC>
 static hipError_t launch_prefill_t(const PrefillArgs& a) {
   char* ws = reinterpret_cast<char*>(a.workspace);
   const SegmentPlan plan =
@@ -1349,7 +1366,7 @@ static hipError_t launch_prefill_t(const PrefillArgs& a) {
   constexpr size_t lds = IntraLds<M, D, C>::kTotal;
   static_assert(lds <= 160 * 1024, "intra-chunk LDS");
   if (plan.max_slots > 0) {
-    hipError_t e = hipFuncSetAttribute(reinterpret_cast<const void*>(&intra_chunk_kernel<M, D, C>),
+    hipError_t e = hipFuncSetAttribute(reinterpret_cast<const void*>(&intra_chunk_kernel<M, D, C, SDEC>),
                                        hipFuncAttributeMaxDynamicSharedMemorySize, (int)lds);
     if (e != hipSuccess) return e;
   }
@@ -1367,7 +1384,7 @@ static hipError_t launch_prefill_t(const PrefillArgs& a) {
       si.slot_cnt = c <= 0 ? 0 : (c < plan.L ? c : plan.L);
     }
     if (slots > 0)
-      hipLaunchKernelGGL((intra_chunk_kernel<M, D, C>), dim3((unsigned)slots, a.H), dim3(kIntraThreads),
+      hipLaunchKernelGGL((intra_chunk_kernel<M, D, C, SDEC>), dim3((unsigned)slots, a.H), dim3(kIntraThreads),
                          lds, a.stream, kp, si);
     if (nct == 2)
       launch_inter<M, D, C, 2>(a, kp, si);
@@ -1377,20 +1394,22 @@ static hipError_t launch_prefill_t(const PrefillArgs& a) {
   return hipGetLastError();
 }
 
-template <class M>
+template <class M, bool SG>
 static hipError_t launch_prefill_m(const PrefillArgs& a) {
   if (a.D == 64) {
-    if (a.chunk == 16) return launch_prefill_t<M, 64, 16>(a);
-    if (a.chunk == 32) return launch_prefill_t<M, 64, 32>(a);
-    return launch_prefill_t<M, 64, 64>(a);
+    if (a.chunk == 16) return launch_prefill_t<M, 64, 16, SG>(a);
+    if (a.chunk == 32) return launch_prefill_t<M, 64, 32, SG>(a);
+    return launch_prefill_t<M, 64, 64, SG>(a);
   }
-  if (a.chunk == 16) return launch_prefill_t<M, 128, 16>(a);
-  if (a.chunk == 32) return launch_prefill_t<M, 128, 32>(a);
-  return launch_prefill_t<M, 128, 64>(a);
+  if (a.chunk == 16) return launch_prefill_t<M, 128, 16, SG>(a);
+  if (a.chunk == 32) return launch_prefill_t<M, 128, 32, SG>(a);
+  return launch_prefill_t<M, 128, 64, SG>(a);
 }
 
 hipError_t launch_prefill(const PrefillArgs& a) {
-  return a.in_bf16 ? launch_prefill_m<ModeBF16>(a) : launch_prefill_m<ModeF32>(a);
+  if (a.scalar_g)
+    return a.in_bf16 ? launch_prefill_m<ModeBF16, true>(a) : launch_prefill_m<ModeF32, true>(a);
+  return a.in_bf16 ? launch_prefill_m<ModeBF16, false>(a) : launch_prefill_m<ModeF32, false>(a);
 }
 
 }  // namespace kda

@@ -48,6 +48,10 @@ def load() -> ctypes.CDLL:
     lib.kda_prefill.restype = i32
     lib.kda_decode_step.argtypes = [vp, vp, vp, vp, vp, vp, vp, i32, i32, i32, i32, i32, i32, vp]
     lib.kda_decode_step.restype = i32
+    lib.gdn_prefill.argtypes = lib.kda_prefill.argtypes
+    lib.gdn_prefill.restype = i32
+    lib.gdn_decode_step.argtypes = lib.kda_decode_step.argtypes
+    lib.gdn_decode_step.restype = i32
     _lib = lib
     return lib
 
@@ -100,6 +104,11 @@ def workspace_size(B: int, T: int, H: int, D: int, num_seqs: int, chunk_size: in
     return out.value
 
 
+def _expect(name, t, shape):
+    if t is not None and tuple(t.shape) != tuple(shape):
+        raise KDAError(f"{name} must have shape {tuple(shape)}, got {tuple(t.shape)}")
+
+
 def prefill(q, k, v, g, beta, initial_state=None, cu_seqlens=None, *,
             cu_seqlens_host: Optional[Union[Sequence[int], np.ndarray]] = None,
             chunk_size: int = 64, out_dtype=None, output_final_state: bool = True,
@@ -107,16 +116,23 @@ def prefill(q, k, v, g, beta, initial_state=None, cu_seqlens=None, *,
     """Chunked KDA forward (``kda_prefill``).
 
     Shapes: q, k, g ``[B, T, H, Dk]``; v ``[B, T, H, Dv]``; beta ``[B, T, H]``.
-    With ``cu_seqlens`` (int32 device tensor ``[N+1]``), B must be 1 and the
-    N packed sequences share the T axis.  ``initial_state`` ``[N, H, Dk, Dv]``
-    float32 or None.  Returns ``(o, final_state)`` (final_state None unless
-    requested).  ``final_state`` may be passed (it may alias initial_state).
+    A g of shape ``[B, T, H]`` (one log-decay per token and head) selects the
+    scalar-decay Gated DeltaNet form (``gdn_prefill``).  With ``cu_seqlens``
+    (int32 device tensor ``[N+1]``), B must be 1 and the N packed sequences
+    share the T axis.  ``initial_state`` ``[N, H, Dk, Dv]`` float32 or None.
+    Returns ``(o, final_state)`` (final_state None unless requested).
+    ``final_state`` may be passed (it may alias initial_state).
     """
     torch = _torch()
     if q.dim() != 4:
         raise KDAError("q must be [B, T, H, D]")
     B, T, H, D = q.shape
     Dv = v.shape[-1]
+    scalar_g = g.dim() == 3
+    _expect("k", k, (B, T, H, D))
+    _expect("v", v, (B, T, H, Dv))
+    _expect("g", g, (B, T, H) if scalar_g else (B, T, H, D))
+    _expect("beta", beta, (B, T, H))
     in_code = _dtype_code(q.dtype)
     for name, t in (("k", k), ("v", v)):
         if t.dtype != q.dtype:
@@ -145,15 +161,23 @@ def prefill(q, k, v, g, beta, initial_state=None, cu_seqlens=None, *,
     if initial_state is not None and (initial_state.dtype != torch.float32
                                       or not initial_state.is_contiguous()):
         raise KDAError("initial_state must be contiguous float32")
+    _expect("o", o, (B, T, H, Dv))
+    _expect("initial_state", initial_state, (N, H, D, Dv))
+    _expect("final_state", final_state, (N, H, D, Dv))
+    if final_state is not None and (final_state.dtype != torch.float32
+                                    or not final_state.is_contiguous()):
+        raise KDAError("final_state must be contiguous float32")
     ws_bytes = workspace_size(B, T, H, D, N, chunk_size, in_code, cu_h)
     if workspace is None or workspace.numel() < ws_bytes:
         workspace = torch.empty(max(ws_bytes, 1), dtype=torch.uint8, device=q.device)
     cu_hp = None if cu_h is None else cu_h.ctypes.data
-    _check(load().kda_prefill(
+    fn = load().gdn_prefill if scalar_g else load().kda_prefill
+    _check(fn(
         _ptr(q), _ptr(k), _ptr(v), _ptr(g), _ptr(beta), _ptr(o),
         _ptr(initial_state), _ptr(final_state), _ptr(cu_seqlens), cu_hp,
         B, T, H, D, Dv, N, chunk_size, in_code, out_code,
-        _ptr(workspace), workspace.numel(), _stream_ptr(q.device)), "kda_prefill")
+        _ptr(workspace), workspace.numel(), _stream_ptr(q.device)),
+        "gdn_prefill" if scalar_g else "kda_prefill")
     return o, final_state
 
 
@@ -161,11 +185,20 @@ def decode_step(q, k, v, g, beta, state, *, out_dtype=None, o=None):
     """One recurrent KDA step (``kda_decode_step``); ``state`` updated in place.
 
     Shapes: q, k, g ``[N, H, Dk]``; v ``[N, H, Dv]``; beta ``[N, H]``;
-    state ``[N, H, Dk, Dv]`` float32.  Returns o ``[N, H, Dv]``.
+    state ``[N, H, Dk, Dv]`` float32.  A g of shape ``[N, H]`` selects the
+    scalar-decay Gated DeltaNet form (``gdn_decode_step``).  Returns o
+    ``[N, H, Dv]``.
     """
     torch = _torch()
     N, H, D = q.shape
     Dv = v.shape[-1]
+    scalar_g = g.dim() == 2
+    _expect("k", k, (N, H, D))
+    _expect("v", v, (N, H, Dv))
+    _expect("g", g, (N, H) if scalar_g else (N, H, D))
+    _expect("beta", beta, (N, H))
+    _expect("state", state, (N, H, D, Dv))
+    _expect("o", o, (N, H, Dv))
     in_code = _dtype_code(q.dtype)
     out_dtype = out_dtype or torch.float32
     out_code = _dtype_code(out_dtype)
@@ -176,7 +209,9 @@ def decode_step(q, k, v, g, beta, state, *, out_dtype=None, o=None):
         raise KDAError("state, g and beta must be float32")
     if o is None:
         o = torch.empty((N, H, Dv), dtype=out_dtype, device=q.device)
-    _check(load().kda_decode_step(
+    fn = load().gdn_decode_step if scalar_g else load().kda_decode_step
+    _check(fn(
         _ptr(q), _ptr(k), _ptr(v), _ptr(g), _ptr(beta), _ptr(state), _ptr(o),
-        N, H, D, Dv, in_code, out_code, _stream_ptr(q.device)), "kda_decode_step")
+        N, H, D, Dv, in_code, out_code, _stream_ptr(q.device)),
+        "gdn_decode_step" if scalar_g else "kda_decode_step")
     return o

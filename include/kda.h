@@ -156,6 +156,37 @@ kda_status kda_decode_step(const void* q, const void* k, const void* v,
                            kda_dtype in_dtype, kda_dtype out_dtype,
                            void* stream /* hipStream_t */);
 
+/*
+ * Gated DeltaNet: the scalar-decay special case of KDA, with one log-decay
+ * per token and head shared by all key channels,
+ *
+ *     S_t = alpha_t (I - beta_t k_t k_t^T) S_{t-1} + beta_t k_t v_t^T
+ *
+ * (zeroshot.it.com deep-dive, section 2.3; the docsaid.org "Kimi Linear"
+ * notes, section "KDA: Splitting the Decay Across Channels", give it as the
+ * form KDA refines).  It equals kda_prefill / kda_decode_step with g
+ * broadcast over the key channels, runs through the same kernels, and reads
+ * Dk times fewer decay values.
+ *
+ * Arguments and behaviour are those of kda_prefill / kda_decode_step except:
+ *   g   [B*T, H] (prefill) or [N, H] (decode) float32 log-decay (<= 0)
+ * kda_prefill_workspace_size gives the workspace size for gdn_prefill too.
+ */
+kda_status gdn_prefill(const void* q, const void* k, const void* v,
+                       const float* g, const float* beta, void* o,
+                       const float* initial_state, float* final_state,
+                       const int32_t* cu_seqlens, const int32_t* cu_seqlens_host,
+                       int B, int T, int H, int Dk, int Dv, int num_seqs,
+                       int chunk_size, kda_dtype in_dtype, kda_dtype out_dtype,
+                       void* workspace, size_t workspace_bytes,
+                       void* stream /* hipStream_t */);
+
+kda_status gdn_decode_step(const void* q, const void* k, const void* v,
+                           const float* g, const float* beta, float* state,
+                           void* o, int N, int H, int Dk, int Dv,
+                           kda_dtype in_dtype, kda_dtype out_dtype,
+                           void* stream /* hipStream_t */);
+
 #ifdef __cplusplus
 }
 #endif
