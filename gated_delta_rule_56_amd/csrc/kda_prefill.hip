@@ -23,9 +23,10 @@
 //
 //  intra_chunk_kernel  one workgroup per (chunk, head), all in parallel:
 //                      decay cumsum, decayed operands, the two Grams A and P,
-//                      the UT-transform solve, W.  It writes Q*gam, W,
-//                      (K*exp(Gamma_n-Gamma))^T, P, T and gam_n to the
-//                      workspace, already in MFMA fragment order.
+//                      the UT-transform solve, W and U0.  It writes Q*gam, W,
+//                      (K*exp(Gamma_n-Gamma))^T, P, U0 and gam_n to the
+//                      workspace, already in the layouts the MFMA products
+//                      of the inter-chunk pass consume.
 //  inter_chunk_kernel  one workgroup per (sequence, head, 16 value columns):
 //                      the serial loop over the sequence's chunks, with the
 //                      state block held in MFMA accumulator registers.
@@ -62,9 +63,10 @@ struct Layout {
   static constexpr size_t kW = kQt + (size_t)NRT * NKD * PF;         // precise [C x D]
   static constexpr size_t kKb = kW + (size_t)NRT * NKD * PF;         // precise [D x KC]
   static constexpr size_t kP = kKb + (size_t)NDT * NKC * PF;         // precise [C x KC]
-  static constexpr size_t kT = kP + (size_t)NRT * NKC * PF;          // precise [C x KC]
-  static constexpr size_t kV = kT + (size_t)NRT * NKC * PF;          // plain   [D x KC] (V^T)
-  static constexpr size_t kGam = kV + (size_t)NDT * NKC * FF;        // fp32 [D]
+  // U0 = T V, fp32 [C x D] as 16x16 accumulator tiles (row tile, column
+  // tile): lane l holds rows 4(l>>4)..+3 of column l&15, 16 B per lane.
+  static constexpr size_t kU0 = kP + (size_t)NRT * NKC * PF;
+  static constexpr size_t kGam = kU0 + (size_t)NRT * NDT * 1024;      // fp32 [D]
   static constexpr size_t kBytes = ((kGam + D * 4) + 255) / 256 * 256;
 };
 
@@ -285,8 +287,8 @@ __device__ __forceinline__ f32x4 prod16(ModeF32, f32x4 acc, const float* A, int 
 //       fragment order; on the strong-decay path Gamma fp32 [C x (D+1)])
 //       ->  X = (I + A)^{-1} (fp32 [C x (KC+1)]) and the solve scratch, then
 //       the T fragments
-//   R1: V^T staging ([D x KC])  ->  A and P (fp32 [C x (KC+1)])
-//       ->  (K*gam)^T staging (precise [D x KC])
+//   R1: A and P (fp32 [C x (KC+1)])  ->  (K*gam)^T staging (precise
+//       [D x KC])  ->  V^T staging (precise [D x KC])
 // plus the per-tile totals of the decay scan and beta.
 // ---------------------------------------------------------------------------
 constexpr size_t cmax(size_t a, size_t b) { return a > b ? a : b; }
@@ -308,18 +310,19 @@ struct IntraLds {
   static constexpr size_t kTFrags = (size_t)NRT * (KC / 32) * M::kPFragBytes;
   static constexpr size_t kR0 = cmax(cmax(kStPrecise, kKhFrags),
                                      cmax(kGamma, kFMat + cmax(kYsc, kTFrags)));
-  static constexpr size_t kR1 = cmax(cmax(kStPlain, 2 * kFMat), kStPrecise);
+  static constexpr size_t kR1 = cmax(2 * kFMat, kStPrecise);
   static constexpr size_t oR0 = 0, oR1 = kR0;
   static constexpr size_t oTot = kR0 + kR1;              // fp32 [NRT][D]
   static constexpr size_t oBeta = oTot + (size_t)NRT * D * 4;
   static constexpr size_t kTotal = oBeta + (size_t)KC * 4;
   // offsets inside the regions
-  static constexpr size_t oKbS = oR0, oVS = oR1;         // staging
+  static constexpr size_t oKbS = oR0;                    // staging
   static constexpr size_t oKh = oR0, oG = oR0;           // Gram operands / Gamma
   static constexpr size_t oA = oR1, oP = oR1 + kFMat;    // Grams
   static constexpr size_t oX = oR0, oY = oR0 + kFMat;    // solve
   static constexpr size_t oTf = oR0 + kFMat;             // T fragments (after the solve)
   static constexpr size_t oKtT = oR1;                    // W product
+  static constexpr size_t oVT = oR1;                     // U0 product (after W)
 };
 
 template <class M>
@@ -556,7 +559,7 @@ __global__ __launch_bounds__(kIntraThreads, 4) void intra_chunk_kernel(KernelPtr
   // valid row and are zeroed at use) ----
   const int tok = clampi(t0 + (r < len ? r : len - 1), 0, si.total_tokens - 1);
   Raw8<float> graw[FPW];
-  Raw8<in_t> qraw[FPW], kraw[FPW], vraw[FPW];
+  Raw8<in_t> qraw[FPW], kraw[FPW];
   float gscalar = 0.f;
   if constexpr (SDEC) gscalar = kp.g[(size_t)tok * H + h];
 #pragma unroll
@@ -565,7 +568,6 @@ __global__ __launch_bounds__(kIntraThreads, 4) void intra_chunk_kernel(KernelPtr
     if constexpr (!SDEC) graw[j].load(kp.g + base);
     qraw[j].load(reinterpret_cast<const in_t*>(kp.q) + base);
     kraw[j].load(reinterpret_cast<const in_t*>(kp.k) + base);
-    vraw[j].load(reinterpret_cast<const in_t*>(kp.v) + base);
   }
   if (tid < KC) {
     const int tb = clampi(t0 + (tid < len ? tid : 0), 0, si.total_tokens - 1);
@@ -643,10 +645,9 @@ __global__ __launch_bounds__(kIntraThreads, 4) void intra_chunk_kernel(KernelPtr
   const bool fast = !__any(big);
 
   // ---- step 3: decayed operands.  Q*gam leaves as whole fragments; K*gam
-  // and K/gam stay in registers; K-bar^T and V^T are staged transposed ----
+  // and K/gam stay in registers; K-bar^T is staged transposed ----
   PFrag qtf[FPW], ktf[FPW], khf[FPW];
   LdsPrecise<M> KbS(smem + L::oKbS, L::kStPlain);
-  plain_t* VS = reinterpret_cast<plain_t*>(smem + L::oVS);
 #pragma unroll
   for (int j = 0; j < FPW; ++j) {
     float qt[8], kt[8], kh[8];
@@ -661,7 +662,6 @@ __global__ __launch_bounds__(kIntraThreads, 4) void intra_chunk_kernel(KernelPtr
       const int c = 32 * fkb[j] + 8 * lg + e;
       if (fv[j]) {
         KbS.store(c * SK + r, kv * __expf(Gn[j][e] - G[j][e]));
-        VS[c * SK + r] = rv ? (plain_t)vraw[j].get(e) : (plain_t)0.f;
       }
     }
     qtf[j] = make_pfrag(M{}, qt);
@@ -683,7 +683,6 @@ __global__ __launch_bounds__(kIntraThreads, 4) void intra_chunk_kernel(KernelPtr
     for (int idx = tid; idx < D * (KC - C); idx += kIntraThreads) {
       const int c = idx / (KC - C), i = C + idx % (KC - C);
       KbS.store(c * SK + i, 0.f);
-      VS[c * SK + i] = (plain_t)0.f;
     }
   }
   __syncthreads();  // B2: staging complete
@@ -692,7 +691,6 @@ __global__ __launch_bounds__(kIntraThreads, 4) void intra_chunk_kernel(KernelPtr
   for (int f = w; f < NDT * NKC; f += NW) {
     const int ct = f / NKC, kb = f % NKC;
     st_pfrag(M{}, blk + LY::kKb + (size_t)f * LY::PF, KbS.pfrag(SK, 16 * ct, 32 * kb));
-    st_frag(M{}, blk + LY::kV + (size_t)f * LY::FF, lds_frag(M{}, VS, SK, 16 * ct, 32 * kb));
   }
   __syncthreads();  // B3: staging regions free
 
@@ -856,16 +854,19 @@ __global__ __launch_bounds__(kIntraThreads, 4) void intra_chunk_kernel(KernelPtr
     __syncthreads();
   }
 
-  // ---- step 6: T = X Diag(beta) (lower triangle) out, and kept in LDS
-  // (over the solve scratch) for the W product; (K*gam)^T staged ----
+  // ---- step 6: T = X Diag(beta) (lower triangle) kept in LDS as
+  // fragments (over the solve scratch) for the W and U0 products; (K*gam)^T
+  // staged.  V is fetched here for step 8 ----
+  Raw8<in_t> vraw[FPW];
+#pragma unroll
+  for (int j = 0; j < FPW; ++j)
+    vraw[j].load(reinterpret_cast<const in_t*>(kp.v) + ((size_t)tok * H + h) * D + 32 * fkb[j] + 8 * lg);
   for (int f = w; f < NRT * NKC; f += NW) {
     const int rr = 16 * (f / NKC) + lr, i0 = 32 * (f % NKC) + 8 * lg;
     float tv[8];
 #pragma unroll
     for (int e = 0; e < 8; ++e) tv[e] = i0 + e <= rr ? Xs[rr * SF + i0 + e] * beta_s[i0 + e] : 0.f;
-    const PFrag tf = make_pfrag(M{}, tv);
-    st_pfrag(M{}, blk + LY::kT + (size_t)f * LY::PF, tf);
-    lds_st_pfrag(M{}, smem + L::oTf + (size_t)f * LY::PF, tf);
+    lds_st_pfrag(M{}, smem + L::oTf + (size_t)f * LY::PF, make_pfrag(M{}, tv));
   }
   LdsPrecise<M> KtT(smem + L::oKtT, L::kStPlain);
 #pragma unroll
@@ -909,6 +910,39 @@ __global__ __launch_bounds__(kIntraThreads, 4) void intra_chunk_kernel(KernelPtr
     const int kgrp = ((lg & 1) << 1) | (lg >> 1);
     gst_pfrag8(M{}, blk + LY::kW + (size_t)(wt * NKD + cp) * LY::PF, lr + 16 * kgrp, wv);
   }
+  __syncthreads();  // (K*gam)^T reads done
+
+  // ---- step 8: U0 = T V, tile (token tile ut, value tile ct), stored in the
+  // accumulator layout the inter-chunk pass adds to.  V^T is staged (split
+  // into hi + lo, so V need not be bf16-exact) over (K*gam)^T ----
+  LdsPrecise<M> VT(smem + L::oVT, L::kStPlain);
+#pragma unroll
+  for (int j = 0; j < FPW; ++j)
+    if (fv[j]) {
+#pragma unroll
+      for (int e = 0; e < 8; ++e) VT.store((32 * fkb[j] + 8 * lg + e) * SK + r, rv ? vraw[j].get(e) : 0.f);
+    }
+  if (KC > C) {
+    for (int idx = tid; idx < D * (KC - C); idx += kIntraThreads) {
+      const int c = idx / (KC - C), i = C + idx % (KC - C);
+      VT.store(c * SK + i, 0.f);
+    }
+  }
+  __syncthreads();  // V^T staged
+  for (int u = w; u < NRT * NDT; u += NW) {
+    const int ut = u / NDT, ct = u % NDT;
+    f32x4 acc0 = {0, 0, 0, 0}, acc1 = {0, 0, 0, 0};
+#pragma unroll
+    for (int kb = 0; kb < NKC; ++kb) {
+      if (32 * kb > 16 * ut + 15) break;
+      const PFrag tf = ld_pfrag(M{}, smem + L::oTf + (size_t)(ut * NKC + kb) * LY::PF);
+      if (kb & 1)
+        acc1 = mma_pp(tf, VT.pfrag(SK, 16 * ct, 32 * kb), acc1);
+      else
+        acc0 = mma_pp(tf, VT.pfrag(SK, 16 * ct, 32 * kb), acc0);
+    }
+    *reinterpret_cast<f32x4*>(blk + LY::kU0 + (size_t)u * 1024 + l * 16) = acc0 + acc1;
+  }
 }
 
 // ---------------------------------------------------------------------------
@@ -916,7 +950,7 @@ __global__ __launch_bounds__(kIntraThreads, 4) void intra_chunk_kernel(KernelPtr
 // columns), 512 threads in two roles that share the chunk loop:
 //
 //   U-waves (0..3) carry the state.  Wave w owns row tile w of U and the
-//     NST state row tiles NST*w ..; per chunk it forms U = T V - W S,
+//     NST state row tiles NST*w ..; per chunk it forms U = U0 - W S,
 //     publishes U^T in LDS, then updates its state tiles
 //     S <- Diag(gam_n) S + K-bar^T U and publishes S^T in LDS.
 //   O-waves (4..7) produce the output.  Wave 4 + r forms Q*gam S for row
@@ -925,7 +959,7 @@ __global__ __launch_bounds__(kIntraThreads, 4) void intra_chunk_kernel(KernelPtr
 //
 // Each SIMD runs one wave of each role, so one wave's operand loads overlap
 // the other's matrix products; the two roles split the per-chunk operands
-// (U-waves: W, T, V^T, K-bar^T, gam_n; O-waves: Q*gam, P).
+// (U-waves: W, U0, K-bar^T, gam_n; O-waves: Q*gam, P).
 // ---------------------------------------------------------------------------
 constexpr int kInterThreads = 512;
 
@@ -934,8 +968,7 @@ struct UFrags {
   typedef Layout<M, D, C> LY;
   static constexpr int NST = LY::NDT / 4;  // state tiles per U-wave
   typename M::PFrag W[LY::NKD];
-  typename M::PFrag Tm[LY::NKC];
-  typename M::Frag V[NCT][LY::NKC];
+  f32x4 U0[NCT];                           // T V tiles of this row tile
   typename M::PFrag Kb[NST][LY::NKC];
   float gam[NST][4];
 };
@@ -958,12 +991,9 @@ __device__ __forceinline__ void load_u1(UFrags<M, D, C, NCT>& f, const char* blk
   for (int kb = 0; kb < LY::NKD; ++kb)
     f.W[kb] = ld_pfrag(M{}, blk + LY::kW + (size_t)(rt * LY::NKD + kb) * LY::PF);
 #pragma unroll
-  for (int kb = 0; kb < LY::NKC; ++kb) {
-    f.Tm[kb] = ld_pfrag(M{}, blk + LY::kT + (size_t)(rt * LY::NKC + kb) * LY::PF);
-#pragma unroll
-    for (int ct = 0; ct < NCT; ++ct)
-      f.V[ct][kb] = ld_frag(M{}, blk + LY::kV + (size_t)((vt0 + ct) * LY::NKC + kb) * LY::FF);
-  }
+  for (int ct = 0; ct < NCT; ++ct)
+    f.U0[ct] = *reinterpret_cast<const f32x4*>(blk + LY::kU0 + (size_t)(rt * LY::NDT + vt0 + ct) * 1024 +
+                                               lane_id() * 16);
 }
 template <class M, int D, int C, int NCT>
 __device__ __forceinline__ void load_u2(UFrags<M, D, C, NCT>& f, const char* blk, int w) {
@@ -1071,17 +1101,6 @@ __device__ __forceinline__ void inter_u_role(const KernelPtrs& kp, const InterGe
 
   auto blk_of = [&](int ci) { return kp.ops + ((size_t)(gm.cbase + ci) * gm.H + gm.h) * LY::kBytes; };
   const int last = gm.ci_hi - 1;
-  // T V of the chunk about to run: independent of the state, so it is
-  // formed at the end of the previous step, off the S -> U -> S chain.
-  f32x4 u[NCT];
-  auto form_tv = [&](const UF& f) {
-#pragma unroll
-    for (int ct = 0; ct < NCT; ++ct) u[ct] = f32x4{0, 0, 0, 0};
-#pragma unroll
-    for (int kb = 0; kb < NKC; ++kb)
-#pragma unroll
-      for (int ct = 0; ct < NCT; ++ct) u[ct] = mma_pf(f.Tm[kb], f.V[ct][kb], u[ct]);
-  };
   // The chain's products keep two partial sums (even and odd k blocks) so
   // that consecutive MFMAs do not wait on each other's accumulator.
   auto step = [&](UF& f, UF& g, int ci) {
@@ -1104,7 +1123,7 @@ __device__ __forceinline__ void inter_u_role(const KernelPtrs& kp, const InterGe
       for (int ct = 0; ct < NCT; ++ct) {
         float v4[4];
 #pragma unroll
-        for (int x = 0; x < 4; ++x) v4[x] = u[ct][x] - (ws0[ct][x] + ws1[ct][x]);
+        for (int x = 0; x < 4; ++x) v4[x] = f.U0[ct][x] - (ws0[ct][x] + ws1[ct][x]);
         UT.template storeN<4>((16 * ct + (l & 15)) * SK + 16 * rt + 4 * (l >> 4), v4);
       }
     }
@@ -1138,7 +1157,6 @@ __device__ __forceinline__ void inter_u_role(const KernelPtrs& kp, const InterGe
       for (int ct = 0; ct < NCT; ++ct) S[s][ct] += S1[s][ct];
     load_u2<M, D, C, NCT>(g, blk_of(min(ci + 1, last)), w);
     publish_state();
-    if (act) form_tv(g);
   };
 
   UF fa, fb;
@@ -1146,7 +1164,6 @@ __device__ __forceinline__ void inter_u_role(const KernelPtrs& kp, const InterGe
     load_u1<M, D, C, NCT>(fa, blk_of(gm.ci_lo), rt, vt0);
     load_u2<M, D, C, NCT>(fa, blk_of(gm.ci_lo), w);
     load_u1<M, D, C, NCT>(fb, blk_of(min(gm.ci_lo + 1, last)), rt, vt0);
-    if (act) form_tv(fa);
   }
   for (int ci = gm.ci_lo; ci < gm.ci_hi; ci += 2) {
     step(fa, fb, ci);

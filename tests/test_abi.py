@@ -89,8 +89,8 @@ def test_prefill_varlen_validation(lib):
 
 def test_workspace_size(lib):
     # B=1, T=4096, H=32, D=128, C=64, bf16: 64 chunks of 32 heads x 147968 B
-    # (Q*gam 32 KB, W 32 KB, K-bar 32 KB, P 16 KB, T 16 KB as bf16 hi + lo;
-    # V^T 16 KB; gam_n 512 B).  The workspace holds one segment of chunks
+    # (Q*gam 32 KB, W 32 KB, K-bar 32 KB, P 16 KB as bf16 hi + lo; U0 = T V
+    # 32 KB fp32; gam_n 512 B).  The workspace holds one segment of chunks
     # (a 160 MiB budget: at most 35 chunks, so 2 equal segments of 32) and the
     # fp32 state carried between segments (32 x 128 x 128 x 4 B); fixed-length
     # input needs no slot table.
@@ -102,12 +102,12 @@ def test_workspace_size(lib):
     n1 = kda.workspace_size(1, 2048, 32, 128, 1, 64, kda.KDA_BF16)
     assert n1 == 32 * 32 * 147968
     # varlen, fp32, D=64, C=16, H=4: lengths 100, 0, 200 -> 7, 0, 13 chunks,
-    # one segment of 13 local chunks holding 7 + 13 slots of 4 x 28928 B
-    # (Q*gam 4 KB, W 4 KB, K-bar 8 KB, P 2 KB, T 2 KB, V^T 8 KB, gam_n 256 B,
-    # a multiple of 256 B), plus the 256-byte slot table.
+    # one segment of 13 local chunks holding 7 + 13 slots of 4 x 22784 B
+    # (Q*gam 4 KB, W 4 KB, K-bar 8 KB, P 2 KB, U0 4 KB, gam_n 256 B, a
+    # multiple of 256 B), plus the 256-byte slot table.
     cu = np.array([0, 100, 100, 300], dtype=np.int32)
     m = kda.workspace_size(1, 300, 4, 64, 3, 16, kda.KDA_F32, cu)
-    assert m == 20 * 4 * 28928 + 256
+    assert m == 20 * 4 * 22784 + 256
     with pytest.raises(kda.KDAError):
         kda.workspace_size(1, 300, 4, 80, 3, 16, kda.KDA_F32, cu)
 
