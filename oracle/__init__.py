@@ -11,6 +11,10 @@ Functions
 ``kda_unrolled``       the unrolled transition-product form, brute force;
                        works on float64 or on exact ``fractions.Fraction``.
 ``kda_chunked``        the chunkwise WY / UT-transform algorithm in float64.
+``layer_prologue``     the per-head input transforms of a KDA layer: Swish and
+                       L2 normalisation of q and k, Swish of v, sigmoid of beta.
+``layer_epilogue``     head-wise RMSNorm of o times a sigmoid output gate.
+``kda_layer``          prologue, recurrence, epilogue.
 
 Sources (pages this package follows):
   * Recurrence: "Kimi Linear" notes (docsaid.org), section "KDA: Splitting
@@ -24,6 +28,11 @@ Sources (pages this package follows):
     "Hardware-Efficient Chunkwise Algorithm" and Appendix B/C notes (WY
     representation, UT transform by forward substitution, output = state
     term + causally masked intra-chunk term).
+  * Layer prologue and epilogue: "Kimi Linear" notes (docsaid.org), section
+    "Other Components" (q, k: Swish then L2 normalisation; v: Swish; beta:
+    sigmoid; output: per-head RMSNorm, then a data-dependent sigmoid gate);
+    greeksharifa.github.io summary, section 4 (head-wise RMSNorm followed by
+    a sigmoid gate; queries and keys normalised to unit length).
 
 Pins: every function here is checked in ``tests/test_oracle_pins.py`` against
 closed forms, special cases, the two-channel decay table printed on the
@@ -243,3 +252,56 @@ def kda_chunked(q, k, v, g, beta, C: int, S0=None):
         Kbar = K * np.exp(Gam[-1][None, :] - Gam)
         S = gam[-1][:, None] * S + Kbar.T @ U
     return o, S
+
+
+# ---------------------------------------------------------------------------
+# Layer prologue / epilogue (docsaid.org notes, "Other Components")
+# ---------------------------------------------------------------------------
+
+L2_FLOOR = 1e-12  # norms below this are treated as this (zero vectors stay 0)
+
+
+def swish(x):
+    """Swish (SiLU): x * sigmoid(x)."""
+    x = np.asarray(x, dtype=np.float64)
+    return x / (1.0 + np.exp(-x))
+
+
+def sigmoid(x):
+    x = np.asarray(x, dtype=np.float64)
+    return 1.0 / (1.0 + np.exp(-x))
+
+
+def l2_normalize(x, axis=-1):
+    """x / ||x|| over ``axis`` (unit length), with the norm floored at
+    L2_FLOOR."""
+    x = np.asarray(x, dtype=np.float64)
+    n = np.sqrt((x * x).sum(axis=axis, keepdims=True))
+    return x / np.maximum(n, L2_FLOOR)
+
+
+def layer_prologue(q_pre, k_pre, v_pre, beta_pre):
+    """q = l2(swish(q_pre)), k = l2(swish(k_pre)) over d_k; v = swish(v_pre);
+    beta = sigmoid(beta_pre).  Arrays are [T, H, D] / [T, H]."""
+    return (l2_normalize(swish(q_pre)), l2_normalize(swish(k_pre)), swish(v_pre),
+            sigmoid(beta_pre))
+
+
+def layer_epilogue(o, gate, weight, eps):
+    """Head-wise RMSNorm with a per-channel weight, times sigmoid(gate):
+    y[t, h, c] = o[t, h, c] / sqrt(mean_c' o[t, h, c']^2 + eps) * weight[c]
+                 * sigmoid(gate[t, h, c])."""
+    o = np.asarray(o, dtype=np.float64)
+    rms = np.sqrt((o * o).mean(axis=-1, keepdims=True) + eps)
+    return o / rms * np.asarray(weight, dtype=np.float64) * sigmoid(gate)
+
+
+def kda_layer(q_pre, k_pre, v_pre, g, beta_pre, gate=None, weight=None, eps=1e-6,
+              initial_state=None, cu_seqlens=None):
+    """Prologue, token-by-token recurrence (kda_recurrent), then the
+    epilogue when ``gate`` is given.  Returns (y, final_state)."""
+    q, k, v, beta = layer_prologue(q_pre, k_pre, v_pre, beta_pre)
+    o, fin = kda_recurrent(q, k, v, g, beta, initial_state, cu_seqlens)
+    if gate is not None:
+        o = layer_epilogue(o, gate, weight, eps)
+    return o, fin
