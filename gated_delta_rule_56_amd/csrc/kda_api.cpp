@@ -4,6 +4,8 @@
 
 #include <hip/hip_runtime.h>
 
+#include <math.h>
+
 #include "kda_launch.hpp"
 
 namespace {
@@ -38,6 +40,30 @@ kda_status seq_layout(int B, int T, int num_seqs, const int32_t* cu_dev, const i
   return KDA_OK;
 }
 
+// The layer epilogue needs a weight with the gate and a finite eps >= 0.
+kda_status check_layer(const kda::Layer& L) {
+  if (!L.gate) return KDA_OK;
+  if (!L.norm_weight || !aligned(L.gate, 16) || !aligned(L.norm_weight, 16))
+    return KDA_ERR_INVALID_ARG;
+  if (!(L.norm_eps >= 0.f) || !isfinite(L.norm_eps)) return KDA_ERR_INVALID_ARG;
+  return KDA_OK;
+}
+
+kda_status workspace_size(int B, int T, int H, int Dk, int Dv, int num_seqs,
+                          const int32_t* cu_seqlens_host, int chunk_size, kda_dtype in_dtype,
+                          bool epilogue, size_t* bytes) {
+  if (bytes == nullptr || H < 1 || !valid_dtype(in_dtype)) return KDA_ERR_INVALID_ARG;
+  if (!supported_head(Dk, Dv) || !supported_chunk(chunk_size)) return KDA_ERR_UNSUPPORTED;
+  int64_t chunks = 0;
+  // Any non-NULL host table stands for a device copy when sizing.
+  const int32_t* cu_dev = cu_seqlens_host;
+  kda_status st = seq_layout(B, T, num_seqs, cu_dev, cu_seqlens_host, chunk_size, &chunks);
+  if (st != KDA_OK) return st;
+  *bytes = kda::prefill_workspace_bytes(num_seqs, cu_seqlens_host, cu_seqlens_host ? 0 : T, H, Dk,
+                                        chunk_size, in_dtype == KDA_BF16, epilogue);
+  return KDA_OK;
+}
+
 }  // namespace
 
 extern "C" {
@@ -58,19 +84,18 @@ int kda_version(void) { return 100; }
 kda_status kda_prefill_workspace_size(int B, int T, int H, int Dk, int Dv, int num_seqs,
                                       const int32_t* cu_seqlens_host, int chunk_size,
                                       kda_dtype in_dtype, size_t* bytes) {
-  if (bytes == nullptr || H < 1 || !valid_dtype(in_dtype)) return KDA_ERR_INVALID_ARG;
-  if (!supported_head(Dk, Dv) || !supported_chunk(chunk_size)) return KDA_ERR_UNSUPPORTED;
-  int64_t chunks = 0;
-  // Any non-NULL host table stands for a device copy when sizing.
-  const int32_t* cu_dev = cu_seqlens_host;
-  kda_status st = seq_layout(B, T, num_seqs, cu_dev, cu_seqlens_host, chunk_size, &chunks);
-  if (st != KDA_OK) return st;
-  *bytes = kda::prefill_workspace_bytes(num_seqs, cu_seqlens_host, cu_seqlens_host ? 0 : T, H, Dk,
-                                        chunk_size, in_dtype == KDA_BF16);
-  return KDA_OK;
+  return workspace_size(B, T, H, Dk, Dv, num_seqs, cu_seqlens_host, chunk_size, in_dtype, false,
+                        bytes);
 }
 
-static kda_status prefill_impl(bool scalar_g, const void* q, const void* k, const void* v,
+kda_status kda_prefill_layer_workspace_size(int B, int T, int H, int Dk, int Dv, int num_seqs,
+                                            const int32_t* cu_seqlens_host, int chunk_size,
+                                            kda_dtype in_dtype, int with_gate, size_t* bytes) {
+  return workspace_size(B, T, H, Dk, Dv, num_seqs, cu_seqlens_host, chunk_size, in_dtype,
+                        with_gate != 0, bytes);
+}
+
+static kda_status prefill_impl(bool scalar_g, const kda::Layer& layer, const void* q, const void* k, const void* v,
                                const float* g, const float* beta, void* o,
                                const float* initial_state, float* final_state,
                                const int32_t* cu_seqlens, const int32_t* cu_seqlens_host,
@@ -79,6 +104,7 @@ static kda_status prefill_impl(bool scalar_g, const void* q, const void* k, cons
                                void* workspace, size_t workspace_bytes, void* stream) {
   if (H < 1 || !valid_dtype(in_dtype) || !valid_dtype(out_dtype)) return KDA_ERR_INVALID_ARG;
   if (!supported_head(Dk, Dv) || !supported_chunk(chunk_size)) return KDA_ERR_UNSUPPORTED;
+  if (check_layer(layer) != KDA_OK) return KDA_ERR_INVALID_ARG;
   const void* ptrs[] = {q, k, v, g, beta, o, initial_state, final_state, cu_seqlens};
   for (const void* p : ptrs)
     if (p && !aligned(p, 16)) return KDA_ERR_INVALID_ARG;
@@ -87,8 +113,9 @@ static kda_status prefill_impl(bool scalar_g, const void* q, const void* k, cons
   if (st != KDA_OK) return st;
   // Token tensors may be empty (and then NULL) only when there are no tokens.
   if ((int64_t)B * T > 0 && (!q || !k || !v || !g || !beta || !o)) return KDA_ERR_INVALID_ARG;
-  const size_t need = kda::prefill_workspace_bytes(num_seqs, cu_seqlens_host, cu_seqlens ? 0 : T,
-                                                   H, Dk, chunk_size, in_dtype == KDA_BF16);
+  const size_t need =
+      kda::prefill_workspace_bytes(num_seqs, cu_seqlens_host, cu_seqlens ? 0 : T, H, Dk,
+                                   chunk_size, in_dtype == KDA_BF16, layer.gate != nullptr);
   if (need > 0 && (workspace == nullptr || workspace_bytes < need)) return KDA_ERR_WORKSPACE;
   if (workspace && !aligned(workspace, 256)) return KDA_ERR_INVALID_ARG;
 
@@ -112,12 +139,13 @@ static kda_status prefill_impl(bool scalar_g, const void* q, const void* k, cons
   a.in_bf16 = in_dtype == KDA_BF16;
   a.out_bf16 = out_dtype == KDA_BF16;
   a.scalar_g = scalar_g;
+  a.layer = layer;
   a.workspace = workspace;
   a.stream = reinterpret_cast<hipStream_t>(stream);
   return kda::launch_prefill(a) == hipSuccess ? KDA_OK : KDA_ERR_HIP;
 }
 
-static kda_status decode_impl(bool scalar_g, const void* q, const void* k, const void* v,
+static kda_status decode_impl(bool scalar_g, const kda::Layer& layer, const void* q, const void* k, const void* v,
                               const float* g, const float* beta, float* state, void* o, int N,
                               int H, int Dk, int Dv, kda_dtype in_dtype, kda_dtype out_dtype,
                               void* stream) {
@@ -125,6 +153,7 @@ static kda_status decode_impl(bool scalar_g, const void* q, const void* k, const
   if (N < 0 || H < 1 || !valid_dtype(in_dtype) || !valid_dtype(out_dtype))
     return KDA_ERR_INVALID_ARG;
   if (!supported_head(Dk, Dv)) return KDA_ERR_UNSUPPORTED;
+  if (check_layer(layer) != KDA_OK) return KDA_ERR_INVALID_ARG;
   const void* ptrs[] = {q, k, v, g, beta, state, o};
   for (const void* p : ptrs)
     if (!aligned(p, 16)) return KDA_ERR_INVALID_ARG;
@@ -143,6 +172,7 @@ static kda_status decode_impl(bool scalar_g, const void* q, const void* k, const
   a.in_bf16 = in_dtype == KDA_BF16;
   a.out_bf16 = out_dtype == KDA_BF16;
   a.scalar_g = scalar_g;
+  a.layer = layer;
   a.stream = reinterpret_cast<hipStream_t>(stream);
   return kda::launch_decode(a) == hipSuccess ? KDA_OK : KDA_ERR_HIP;
 }
@@ -153,9 +183,9 @@ kda_status kda_prefill(const void* q, const void* k, const void* v, const float*
                        const int32_t* cu_seqlens_host, int B, int T, int H, int Dk, int Dv,
                        int num_seqs, int chunk_size, kda_dtype in_dtype, kda_dtype out_dtype,
                        void* workspace, size_t workspace_bytes, void* stream) {
-  return prefill_impl(false, q, k, v, g, beta, o, initial_state, final_state, cu_seqlens,
-                      cu_seqlens_host, B, T, H, Dk, Dv, num_seqs, chunk_size, in_dtype, out_dtype,
-                      workspace, workspace_bytes, stream);
+  return prefill_impl(false, kda::Layer(), q, k, v, g, beta, o, initial_state, final_state,
+                      cu_seqlens, cu_seqlens_host, B, T, H, Dk, Dv, num_seqs, chunk_size,
+                      in_dtype, out_dtype, workspace, workspace_bytes, stream);
 }
 
 kda_status gdn_prefill(const void* q, const void* k, const void* v, const float* g,
@@ -164,21 +194,55 @@ kda_status gdn_prefill(const void* q, const void* k, const void* v, const float*
                        const int32_t* cu_seqlens_host, int B, int T, int H, int Dk, int Dv,
                        int num_seqs, int chunk_size, kda_dtype in_dtype, kda_dtype out_dtype,
                        void* workspace, size_t workspace_bytes, void* stream) {
-  return prefill_impl(true, q, k, v, g, beta, o, initial_state, final_state, cu_seqlens,
-                      cu_seqlens_host, B, T, H, Dk, Dv, num_seqs, chunk_size, in_dtype, out_dtype,
-                      workspace, workspace_bytes, stream);
+  return prefill_impl(true, kda::Layer(), q, k, v, g, beta, o, initial_state, final_state,
+                      cu_seqlens, cu_seqlens_host, B, T, H, Dk, Dv, num_seqs, chunk_size,
+                      in_dtype, out_dtype, workspace, workspace_bytes, stream);
 }
 
 kda_status kda_decode_step(const void* q, const void* k, const void* v, const float* g,
                            const float* beta, float* state, void* o, int N, int H, int Dk,
                            int Dv, kda_dtype in_dtype, kda_dtype out_dtype, void* stream) {
-  return decode_impl(false, q, k, v, g, beta, state, o, N, H, Dk, Dv, in_dtype, out_dtype, stream);
+  return decode_impl(false, kda::Layer(), q, k, v, g, beta, state, o, N, H, Dk, Dv, in_dtype,
+                     out_dtype, stream);
 }
 
 kda_status gdn_decode_step(const void* q, const void* k, const void* v, const float* g,
                            const float* beta, float* state, void* o, int N, int H, int Dk,
                            int Dv, kda_dtype in_dtype, kda_dtype out_dtype, void* stream) {
-  return decode_impl(true, q, k, v, g, beta, state, o, N, H, Dk, Dv, in_dtype, out_dtype, stream);
+  return decode_impl(true, kda::Layer(), q, k, v, g, beta, state, o, N, H, Dk, Dv, in_dtype,
+                     out_dtype, stream);
+}
+
+static kda::Layer make_layer(const void* gate, const float* norm_weight, float norm_eps) {
+  kda::Layer L;
+  L.prologue = true;
+  L.gate = gate;
+  L.norm_weight = gate ? norm_weight : nullptr;
+  L.norm_eps = norm_eps;
+  return L;
+}
+
+kda_status kda_prefill_layer(const void* q_pre, const void* k_pre, const void* v_pre,
+                             const float* g, const float* beta_logit, const void* gate,
+                             const float* norm_weight, float norm_eps, void* o,
+                             const float* initial_state, float* final_state,
+                             const int32_t* cu_seqlens, const int32_t* cu_seqlens_host, int B,
+                             int T, int H, int Dk, int Dv, int num_seqs, int chunk_size,
+                             kda_dtype in_dtype, kda_dtype out_dtype, void* workspace,
+                             size_t workspace_bytes, void* stream) {
+  return prefill_impl(false, make_layer(gate, norm_weight, norm_eps), q_pre, k_pre, v_pre, g,
+                      beta_logit, o, initial_state, final_state, cu_seqlens, cu_seqlens_host, B, T,
+                      H, Dk, Dv, num_seqs, chunk_size, in_dtype, out_dtype, workspace,
+                      workspace_bytes, stream);
+}
+
+kda_status kda_decode_step_layer(const void* q_pre, const void* k_pre, const void* v_pre,
+                                 const float* g, const float* beta_logit, const void* gate,
+                                 const float* norm_weight, float norm_eps, float* state, void* o,
+                                 int N, int H, int Dk, int Dv, kda_dtype in_dtype,
+                                 kda_dtype out_dtype, void* stream) {
+  return decode_impl(false, make_layer(gate, norm_weight, norm_eps), q_pre, k_pre, v_pre, g,
+                     beta_logit, state, o, N, H, Dk, Dv, in_dtype, out_dtype, stream);
 }
 
 }  // extern "C"

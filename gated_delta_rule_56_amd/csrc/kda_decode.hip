@@ -18,17 +18,34 @@
 // bytes per (n, h) plus the small per-token vectors.  The column reductions
 // over rows run in registers, then across the lanes of a wave with xor
 // shuffles, then across the four waves through LDS.
+//
+// LAYER adds the layer's elementwise work (the "Kimi Linear" notes,
+// docsaid.org, section "Other Components"): Swish and L2 normalisation of q
+// and k, Swish of v and the sigmoid of beta on the way in, and with a gate the
+// head-wise RMSNorm times sigmoid(gate) on the way out.  The norms of q and k
+// are scalars per (n, h), so the reductions run on the un-normalised values
+// and are rescaled once the norms are known.
 #include "kda_device.hpp"
 #include "kda_launch.hpp"
 
 namespace kda {
 
+struct LayerPtrs {
+  int prologue;
+  const void* gate;  // nullptr: no epilogue
+  const float* norm_weight;
+  float norm_eps;
+};
+
+__device__ __forceinline__ float swish_d(float x) { return x / (1.f + __expf(-x)); }
+__device__ __forceinline__ float sigmoid_d(float x) { return 1.f / (1.f + __expf(-x)); }
+
 // SG: scalar gate (Gated DeltaNet): g holds one log-decay per (n, h).
-template <typename in_t, int DK, int DV, bool OUT_BF16, bool SG>
+template <typename in_t, int DK, int DV, bool OUT_BF16, bool SG, bool LAYER>
 __global__ __launch_bounds__(256) void decode_step_kernel(
     const in_t* __restrict__ q, const in_t* __restrict__ k, const in_t* __restrict__ v,
     const float* __restrict__ g, const float* __restrict__ beta, float* __restrict__ state,
-    void* __restrict__ o, int NH) {
+    void* __restrict__ o, int NH, LayerPtrs lp) {
   constexpr int TPR = DV / 4;          // threads per state row
   constexpr int RG = 256 / TPR;        // row groups
   constexpr int RPT = DK / RG;         // rows per thread
@@ -56,12 +73,18 @@ __global__ __launch_bounds__(256) void decode_step_kernel(
     const int i = rg + RG * m;
     s[m] = __builtin_nontemporal_load(reinterpret_cast<const f32x4*>(sp + (size_t)i * DV + 4 * cg));
   }
-  float r[4] = {0, 0, 0, 0}, p[4] = {0, 0, 0, 0}, kq = 0.f;
+  float r[4] = {0, 0, 0, 0}, p[4] = {0, 0, 0, 0}, kq = 0.f, nq = 0.f, nk = 0.f;
 #pragma unroll
   for (int m = 0; m < RPT; ++m) {
     const int i = rg + RG * m;
     kk[m] = (float)kp[i];
     qq[m] = (float)qp[i];
+    if (LAYER && lp.prologue) {
+      kk[m] = swish_d(kk[m]);
+      qq[m] = swish_d(qq[m]);
+      nk += kk[m] * kk[m];
+      nq += qq[m] * qq[m];
+    }
     const float a = SG ? ag : __expf(gp[i]);
 #pragma unroll
     for (int c = 0; c < 4; ++c) {
@@ -81,8 +104,13 @@ __global__ __launch_bounds__(256) void decode_step_kernel(
       p[c] += __shfl_xor(p[c], off);
     }
     kq += __shfl_xor(kq, off);
+    if (LAYER) {
+      nq += __shfl_xor(nq, off);
+      nk += __shfl_xor(nk, off);
+    }
   }
-  __shared__ float red[4][TPR][9];
+  constexpr int NRED = LAYER ? 11 : 9;
+  __shared__ float red[4][TPR][NRED];
   const int w = t >> 6;
   if ((t & 63) < TPR) {
 #pragma unroll
@@ -91,6 +119,10 @@ __global__ __launch_bounds__(256) void decode_step_kernel(
       red[w][cg][4 + c] = p[c];
     }
     red[w][cg][8] = kq;
+    if (LAYER) {
+      red[w][cg][9] = nq;
+      red[w][cg][10] = nk;
+    }
   }
   __syncthreads();
 #pragma unroll
@@ -100,11 +132,30 @@ __global__ __launch_bounds__(256) void decode_step_kernel(
   }
   kq = red[0][cg][8] + red[1][cg][8] + red[2][cg][8] + red[3][cg][8];
 
-  const float b = beta[tok];
+  float b = beta[tok];
   const in_t* vp = v + tok * DV + 4 * cg;
+  float vv[4];
+#pragma unroll
+  for (int c = 0; c < 4; ++c) vv[c] = (float)vp[c];
+  if (LAYER && lp.prologue) {
+    // L2 normalisation: scale the reductions by 1/|q|, 1/|k| (floored).
+    nq = red[0][cg][9] + red[1][cg][9] + red[2][cg][9] + red[3][cg][9];
+    nk = red[0][cg][10] + red[1][cg][10] + red[2][cg][10] + red[3][cg][10];
+    const float iq = 1.f / fmaxf(sqrtf(nq), 1e-12f), ik = 1.f / fmaxf(sqrtf(nk), 1e-12f);
+#pragma unroll
+    for (int m = 0; m < RPT; ++m) kk[m] *= ik;
+#pragma unroll
+    for (int c = 0; c < 4; ++c) {
+      r[c] *= ik;
+      p[c] *= iq;
+      vv[c] = swish_d(vv[c]);
+    }
+    kq *= ik * iq;
+    b = sigmoid_d(b);
+  }
   float u[4];
 #pragma unroll
-  for (int c = 0; c < 4; ++c) u[c] = b * ((float)vp[c] - r[c]);
+  for (int c = 0; c < 4; ++c) u[c] = b * (vv[c] - r[c]);
 
 #pragma unroll
   for (int m = 0; m < RPT; ++m) {
@@ -114,32 +165,55 @@ __global__ __launch_bounds__(256) void decode_step_kernel(
     __builtin_nontemporal_store(s[m], reinterpret_cast<f32x4*>(sp + (size_t)i * DV + 4 * cg));
   }
   if (rg == 0) {
+    float y[4];
+#pragma unroll
+    for (int c = 0; c < 4; ++c) y[c] = p[c] + kq * u[c];
+    if (LAYER && lp.gate) {
+      // RMSNorm over the Dv outputs of this (n, h): lanes 0 .. TPR-1 of wave 0.
+      float ss = y[0] * y[0] + y[1] * y[1] + y[2] * y[2] + y[3] * y[3];
+#pragma unroll
+      for (int off = 1; off < TPR; off <<= 1) ss += __shfl_xor(ss, off);
+      const float inv = 1.f / sqrtf(ss / DV + lp.norm_eps);
+      const in_t* gt = reinterpret_cast<const in_t*>(lp.gate) + tok * DV + 4 * cg;
+#pragma unroll
+      for (int c = 0; c < 4; ++c)
+        y[c] = y[c] * inv * lp.norm_weight[4 * cg + c] * sigmoid_d((float)gt[c]);
+    }
     if constexpr (OUT_BF16) {
       bf16x4 ov;
 #pragma unroll
-      for (int c = 0; c < 4; ++c) ov[c] = f2bf(p[c] + kq * u[c]);
+      for (int c = 0; c < 4; ++c) ov[c] = f2bf(y[c]);
       *reinterpret_cast<bf16x4*>(reinterpret_cast<bf16*>(o) + tok * DV + 4 * cg) = ov;
     } else {
       f32x4 ov;
 #pragma unroll
-      for (int c = 0; c < 4; ++c) ov[c] = p[c] + kq * u[c];
+      for (int c = 0; c < 4; ++c) ov[c] = y[c];
       *reinterpret_cast<f32x4*>(reinterpret_cast<float*>(o) + tok * DV + 4 * cg) = ov;
     }
   }
 }
 
-template <typename in_t, int D, bool OUT_BF16>
-static void launch_decode_o(const DecodeArgs& a) {
+template <typename in_t, int D, bool OUT_BF16, bool LAYER>
+static void launch_decode_l(const DecodeArgs& a) {
   const int NH = a.N * a.H;
   dim3 grid(NH), block(256);
+  const LayerPtrs lp{a.layer.prologue ? 1 : 0, a.layer.gate, a.layer.norm_weight, a.layer.norm_eps};
   if (a.scalar_g)
-    hipLaunchKernelGGL((decode_step_kernel<in_t, D, D, OUT_BF16, true>), grid, block, 0, a.stream,
-                       (const in_t*)a.q, (const in_t*)a.k, (const in_t*)a.v, a.g, a.beta,
-                       a.state, a.o, NH);
+    hipLaunchKernelGGL((decode_step_kernel<in_t, D, D, OUT_BF16, true, LAYER>), grid, block, 0,
+                       a.stream, (const in_t*)a.q, (const in_t*)a.k, (const in_t*)a.v, a.g, a.beta,
+                       a.state, a.o, NH, lp);
   else
-    hipLaunchKernelGGL((decode_step_kernel<in_t, D, D, OUT_BF16, false>), grid, block, 0, a.stream,
-                       (const in_t*)a.q, (const in_t*)a.k, (const in_t*)a.v, a.g, a.beta,
-                       a.state, a.o, NH);
+    hipLaunchKernelGGL((decode_step_kernel<in_t, D, D, OUT_BF16, false, LAYER>), grid, block, 0,
+                       a.stream, (const in_t*)a.q, (const in_t*)a.k, (const in_t*)a.v, a.g, a.beta,
+                       a.state, a.o, NH, lp);
+}
+
+template <typename in_t, int D, bool OUT_BF16>
+static void launch_decode_o(const DecodeArgs& a) {
+  if (a.layer.prologue || a.layer.gate)
+    launch_decode_l<in_t, D, OUT_BF16, true>(a);
+  else
+    launch_decode_l<in_t, D, OUT_BF16, false>(a);
 }
 
 template <typename in_t, int D>

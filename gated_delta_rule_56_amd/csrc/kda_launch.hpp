@@ -8,6 +8,18 @@
 
 namespace kda {
 
+// The layer's own elementwise work around the recurrence.  prologue: q and k
+// pass through Swish then L2 normalisation per (token, head), v through
+// Swish, beta through the sigmoid.  gate != nullptr: the output becomes the
+// head-wise RMSNorm of o times norm_weight (per value channel) times
+// sigmoid(gate); gate has the element type and layout of v.
+struct Layer {
+  bool prologue = false;
+  const void* gate = nullptr;
+  const float* norm_weight = nullptr;
+  float norm_eps = 0.f;
+};
+
 struct DecodeArgs {
   const void* q;
   const void* k;
@@ -19,6 +31,7 @@ struct DecodeArgs {
   int N, H, D;
   bool in_bf16, out_bf16;
   bool scalar_g;  // g holds one log-decay per (sequence, head)
+  Layer layer;
   hipStream_t stream;
 };
 
@@ -41,6 +54,7 @@ struct PrefillArgs {
   int H, D, chunk;
   bool in_bf16, out_bf16;
   bool scalar_g;              // g holds one log-decay per (token, head)
+  Layer layer;
   void* workspace;
   hipStream_t stream;
 };
@@ -57,9 +71,10 @@ struct SegmentPlan {
 SegmentPlan plan_segments(int num_seqs, const int32_t* cu_host, int seq_len, int H, int D,
                           int chunk, bool in_bf16);
 // Total workspace bytes (segment slot table, state carry between segments,
-// one segment's operands), 256-byte aligned pieces.
+// one segment's operands, and with the layer epilogue one segment's raw
+// fp32 output), 256-byte aligned pieces.
 size_t prefill_workspace_bytes(int num_seqs, const int32_t* cu_host, int seq_len, int H, int D,
-                               int chunk, bool in_bf16);
+                               int chunk, bool in_bf16, bool epilogue);
 hipError_t launch_prefill(const PrefillArgs& a);
 
 }  // namespace kda

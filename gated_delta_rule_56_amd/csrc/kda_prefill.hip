@@ -176,11 +176,17 @@ static size_t carry_bytes(const SegmentPlan& p, int num_seqs, int H, int D) {
   return p.nseg > 1 ? align256((size_t)num_seqs * H * D * D * sizeof(float)) : 0;
 }
 
+// Raw o of one segment for the layer epilogue: fp32 [slot][H][C][D].
+static size_t raw_o_bytes(const SegmentPlan& p, int H, int D, int chunk, bool epilogue) {
+  return epilogue ? align256((size_t)p.max_slots * H * chunk * D * sizeof(float)) : 0;
+}
+
 size_t prefill_workspace_bytes(int num_seqs, const int32_t* cu_host, int seq_len, int H, int D,
-                               int chunk, bool in_bf16) {
+                               int chunk, bool in_bf16, bool epilogue) {
   const SegmentPlan p = plan_segments(num_seqs, cu_host, seq_len, H, D, chunk, in_bf16);
   return table_bytes(num_seqs, cu_host != nullptr) + carry_bytes(p, num_seqs, H, D) +
-         (size_t)p.max_slots * H * prefill_chunk_bytes(D, chunk, in_bf16);
+         (size_t)p.max_slots * H * prefill_chunk_bytes(D, chunk, in_bf16) +
+         raw_o_bytes(p, H, D, chunk, epilogue);
 }
 
 // ---------------------------------------------------------------------------
@@ -289,7 +295,8 @@ __device__ __forceinline__ f32x4 prod16(ModeF32, f32x4 acc, const float* A, int 
 //       the T fragments
 //   R1: A and P (fp32 [C x (KC+1)])  ->  (K*gam)^T staging (precise
 //       [D x KC])  ->  V^T staging (precise [D x KC])
-// plus the per-tile totals of the decay scan and beta.
+// plus the per-tile totals of the decay scan, beta, and the layer prologue's
+// norm partials and per-token factors.
 // ---------------------------------------------------------------------------
 constexpr size_t cmax(size_t a, size_t b) { return a > b ? a : b; }
 
@@ -314,7 +321,9 @@ struct IntraLds {
   static constexpr size_t oR0 = 0, oR1 = kR0;
   static constexpr size_t oTot = kR0 + kR1;              // fp32 [NRT][D]
   static constexpr size_t oBeta = oTot + (size_t)NRT * D * 4;
-  static constexpr size_t kTotal = oBeta + (size_t)KC * 4;
+  static constexpr size_t oNrm = oBeta + (size_t)KC * 4;      // fp32 [8 waves][16][2]
+  static constexpr size_t oRn = oNrm + 8 * 16 * 2 * 4;         // fp32 [C][2]
+  static constexpr size_t kTotal = oRn + (size_t)C * 2 * 4;
   // offsets inside the regions
   static constexpr size_t oKbS = oR0;                    // staging
   static constexpr size_t oKh = oR0, oG = oR0;           // Gram operands / Gamma
@@ -449,8 +458,18 @@ struct KernelPtrs {
   float* s1;
   float* carry;    // [num_seqs, H, D, D] state between segments, or nullptr
   char* ops;       // per-(chunk, head) operand blocks of the current segment
+  float* o_slots;  // with the layer epilogue: raw o, fp32 [slot][H][C][D]; else nullptr
+  const void* gate;          // layer epilogue: sigmoid gate [tokens, H, D] (in dtype)
+  const float* norm_weight;  // layer epilogue: RMSNorm weight [D]
+  float norm_eps;
   int H;
 };
+
+// Layer prologue pieces (the "Kimi Linear" notes, docsaid.org, section
+// "Other Components"): Swish of the projected q, k, v; sigmoid of beta.
+__device__ __forceinline__ float swishf(float x) { return x / (1.f + __expf(-x)); }
+__device__ __forceinline__ float sigmoidf(float x) { return 1.f / (1.f + __expf(-x)); }
+constexpr float kL2Floor = 1e-12f;  // L2 norms below this count as this
 
 // Eight input elements of one row held as loaded (bf16 or fp32).
 template <class T>
@@ -476,42 +495,21 @@ struct Raw8<float> {
 __device__ __forceinline__ void lds_st_pfrag(ModeBF16 m, char* p, const ModeBF16::PFrag& f) { st_pfrag(m, p, f); }
 __device__ __forceinline__ void lds_st_pfrag(ModeF32 m, char* p, const ModeF32::PFrag& f) { st_pfrag(m, p, f); }
 
-// ---------------------------------------------------------------------------
-// Intra-chunk kernel: grid (chunks of the segment, H), 512 threads (8 waves),
-// two workgroups per CU.
-//
-// Thread layout follows the MFMA fragments: the chunk's [C x D] token-by-
-// channel matrices are cut into 16-token x 32-channel fragments; wave w holds
-// fragments w, w + 8, ... (row tile f % NRT, channel block f / NRT), lane l
-// the eight channels 32 kb + 8 (l >> 4) .. + 7 of token 16 rt + (l & 15).  So
-// the decayed Q and K are Gram A-operands in registers, Q*gam goes out as
-// whole fragments, and the decay cumsum runs across the 16 lanes of a tile.
-// ---------------------------------------------------------------------------
-// SDEC: scalar decay (Gated DeltaNet), one log-decay per token and head, g
-// [tokens, H]; otherwise one per key channel, g [tokens, H, D].
-template <class M, int D, int C, bool SDEC>
-__global__ __launch_bounds__(kIntraThreads, 4) void intra_chunk_kernel(KernelPtrs kp, SeqInfo si) {
-  typedef typename M::in_t in_t;
-  typedef typename M::PFrag PFrag;
-  typedef Layout<M, D, C> LY;
-  typedef IntraLds<M, D, C> L;
-  typedef typename L::plain_t plain_t;
-  constexpr int NRT = LY::NRT, KC = LY::KC, NKC = LY::NKC, NKD = LY::NKD, NDT = LY::NDT;
-  constexpr int SK = L::SK, SF = L::SF, SG = L::SG;
-  constexpr int NW = kIntraThreads / 64;
-  constexpr int NFRAG = NRT * NKD;            // fragments of a [C x D] matrix
-  constexpr int FPW = (NFRAG + NW - 1) / NW;  // fragments per wave
-  static_assert(NW % NRT == 0, "a wave's fragments share one row tile");
-  extern __shared__ __attribute__((aligned(16))) char smem[];
+// One (slot, head) item of a segment: its token range and operand block.
+// item = slot * H + head; slot indexes the segment's (sequence, local chunk)
+// pairs (varlen: through the segment table).
+struct Item {
+  int h, t0, len;
+  char* blk;
+};
 
-  const int slot = blockIdx.x;  // (sequence, local chunk) slot of this segment
-  const int h = blockIdx.y;
+template <int C>
+__device__ __forceinline__ Item intra_item(const SeqInfo& si, const KernelPtrs& kp, int item,
+                                           size_t block_bytes) {
   const int H = kp.H;
-  const int tid = threadIdx.x;
-  const int w = wave_id(), l = lane_id();
-  const int lr = l & 15, lg = l >> 4;
-
-  // ---- which sequence and token range ----
+  const int slot = item / H;
+  Item x;
+  x.h = item - slot * H;
   int n, ci;
   if (si.cu) {
     int lo = 0, hi = si.num_seqs - 1;  // last n with slot_off[n] <= slot
@@ -533,9 +531,50 @@ __global__ __launch_bounds__(kIntraThreads, 4) void intra_chunk_kernel(KernelPtr
   // A device table that disagrees with the host one can only shorten chunks,
   // never move them outside [bos, eos].
   const long long t0l = (long long)bos + (long long)(ci < 0 ? 0 : ci) * C;
-  const int t0 = (int)(t0l < eos ? t0l : eos);
-  const int len = clampi(eos - t0, 0, C);
-  char* blk = kp.ops + ((size_t)slot * H + h) * LY::kBytes;
+  x.t0 = (int)(t0l < eos ? t0l : eos);
+  x.len = clampi(eos - x.t0, 0, C);
+  x.blk = kp.ops + ((size_t)slot * H + x.h) * block_bytes;
+  return x;
+}
+
+// ---------------------------------------------------------------------------
+// Intra-chunk kernel: grid (slots of the segment, H), 512 threads (8 waves),
+// two workgroups per CU.
+//
+// Thread layout follows the MFMA fragments: the chunk's [C x D] token-by-
+// channel matrices are cut into 16-token x 32-channel fragments; wave w holds
+// fragments w, w + 8, ... (row tile f % NRT, channel block f / NRT), lane l
+// the eight channels 32 kb + 8 (l >> 4) .. + 7 of token 16 rt + (l & 15).  So
+// the decayed Q and K are Gram A-operands in registers, Q*gam goes out as
+// whole fragments, and the decay cumsum runs across the 16 lanes of a tile.
+// ---------------------------------------------------------------------------
+// SDEC: scalar decay (Gated DeltaNet), one log-decay per token and head, g
+// [tokens, H]; otherwise one per key channel, g [tokens, H, D].
+// SDEC: scalar decay (one g per token and head).  PRO: the layer prologue
+// (Swish + L2 norm of q and k, Swish of v, sigmoid of beta) is applied to the
+// inputs as they are read.
+template <class M, int D, int C, bool SDEC, bool PRO>
+__global__ __launch_bounds__(kIntraThreads, 4) void intra_chunk_kernel(KernelPtrs kp, SeqInfo si) {
+  typedef typename M::in_t in_t;
+  typedef typename M::PFrag PFrag;
+  typedef Layout<M, D, C> LY;
+  typedef IntraLds<M, D, C> L;
+  typedef typename L::plain_t plain_t;
+  constexpr int NRT = LY::NRT, KC = LY::KC, NKC = LY::NKC, NKD = LY::NKD, NDT = LY::NDT;
+  constexpr int SK = L::SK, SF = L::SF, SG = L::SG;
+  constexpr int NW = kIntraThreads / 64;
+  constexpr int NFRAG = NRT * NKD;            // fragments of a [C x D] matrix
+  constexpr int FPW = (NFRAG + NW - 1) / NW;  // fragments per wave
+  static_assert(NW % NRT == 0, "a wave's fragments share one row tile");
+  extern __shared__ __attribute__((aligned(16))) char smem[];
+
+  const int H = kp.H;
+  const Item it = intra_item<C>(si, kp, blockIdx.x * H + blockIdx.y, LY::kBytes);
+  const int h = it.h, t0 = it.t0, len = it.len;
+  char* blk = it.blk;
+  const int tid = threadIdx.x;
+  const int w = wave_id(), l = lane_id();
+  const int lr = l & 15, lg = l >> 4;
 
   float* tot = reinterpret_cast<float*>(smem + L::oTot);
   float* beta_s = reinterpret_cast<float*>(smem + L::oBeta);
@@ -572,7 +611,7 @@ __global__ __launch_bounds__(kIntraThreads, 4) void intra_chunk_kernel(KernelPtr
   if (tid < KC) {
     const int tb = clampi(t0 + (tid < len ? tid : 0), 0, si.total_tokens - 1);
     const float bv = kp.beta[(size_t)tb * H + h];
-    beta_s[tid] = tid < len ? bv : 0.f;
+    beta_s[tid] = tid < len ? (PRO ? sigmoidf(bv) : bv) : 0.f;
   }
 
   // ---- step 2: cumulative decay.  Inclusive scan over the 16 tokens of the
@@ -612,7 +651,50 @@ __global__ __launch_bounds__(kIntraThreads, 4) void intra_chunk_kernel(KernelPtr
         *reinterpret_cast<f32x4*>(tot + rt * D + 32 * fkb[j] + 8 * lg + 4) = b;
       }
   }
-  __syncthreads();  // B1: tile totals, beta
+  // Layer prologue: this wave's part of |swish(q)|^2 and |swish(k)|^2 for
+  // its token, summed over its lane groups; the waves sharing the row tile
+  // hold the other channels.
+  constexpr int NCW = (NFRAG < NW ? NFRAG : NW) / NRT;  // waves per row tile
+  float* nrm = reinterpret_cast<float*>(smem + L::oNrm);
+  if (PRO) {
+    float sq = 0.f, sk = 0.f;
+#pragma unroll
+    for (int j = 0; j < FPW; ++j)
+      if (fv[j]) {
+#pragma unroll
+        for (int e = 0; e < 8; ++e) {
+          const float a = swishf(qraw[j].get(e)), b = swishf(kraw[j].get(e));
+          sq += a * a;
+          sk += b * b;
+        }
+      }
+    sq += __shfl_xor(sq, 16);
+    sk += __shfl_xor(sk, 16);
+    sq += __shfl_xor(sq, 32);
+    sk += __shfl_xor(sk, 32);
+    if (lg == 0) {
+      nrm[(w * 16 + lr) * 2] = sq;
+      nrm[(w * 16 + lr) * 2 + 1] = sk;
+    }
+  }
+  __syncthreads();  // B1: tile totals, beta, prologue norms
+  float iq = 1.f, ik = 1.f;
+  if (PRO) {
+    float sq = 0.f, sk = 0.f;
+#pragma unroll
+    for (int c = 0; c < NCW; ++c) {
+      sq += nrm[((rt + c * NRT) * 16 + lr) * 2];
+      sk += nrm[((rt + c * NRT) * 16 + lr) * 2 + 1];
+    }
+    iq = 1.f / fmaxf(sqrtf(sq), kL2Floor);
+    ik = 1.f / fmaxf(sqrtf(sk), kL2Floor);
+    // per-token factors for the strong-decay path, which re-reads q and k
+    float* rn = reinterpret_cast<float*>(smem + L::oRn);
+    if (w < NRT && lg == 0) {
+      rn[r * 2] = iq;
+      rn[r * 2 + 1] = ik;
+    }
+  }
   float Gn[FPW][8];
 #pragma unroll
   for (int j = 0; j < FPW; ++j)
@@ -653,8 +735,8 @@ __global__ __launch_bounds__(kIntraThreads, 4) void intra_chunk_kernel(KernelPtr
     float qt[8], kt[8], kh[8];
 #pragma unroll
     for (int e = 0; e < 8; ++e) {
-      const float kv = rv ? kraw[j].get(e) : 0.f;
-      const float qv = rv ? qraw[j].get(e) : 0.f;
+      const float kv = rv ? (PRO ? swishf(kraw[j].get(e)) * ik : kraw[j].get(e)) : 0.f;
+      const float qv = rv ? (PRO ? swishf(qraw[j].get(e)) * iq : qraw[j].get(e)) : 0.f;
       const float gm = __expf(G[j][e]);
       qt[e] = qv * gm;
       kt[e] = kv * gm;
@@ -740,14 +822,19 @@ __global__ __launch_bounds__(kIntraThreads, 4) void intra_chunk_kernel(KernelPtr
     const float* Gs = reinterpret_cast<const float*>(smem + L::oG);
     const in_t* qg = reinterpret_cast<const in_t*>(kp.q);
     const in_t* kg = reinterpret_cast<const in_t*>(kp.k);
+    const float* rn = reinterpret_cast<const float*>(smem + L::oRn);
+    auto in = [&](const in_t* p, int t, int c, float f) {
+      const float x = (float)p[((size_t)(t0 + t) * H + h) * D + c];
+      return PRO ? swishf(x) * f : x;
+    };
     const int rr = tid >> 3;
     if (rr < len) {
       for (int i = tid & 7; i <= rr; i += 8) {
         float sa = 0.f, sp = 0.f;
         for (int c = 0; c < D; ++c) {
-          const float kr = (float)kg[((size_t)(t0 + rr) * H + h) * D + c];
-          const float ki = (float)kg[((size_t)(t0 + i) * H + h) * D + c];
-          const float qr = (float)qg[((size_t)(t0 + rr) * H + h) * D + c];
+          const float kr = in(kg, rr, c, rn[rr * 2 + 1]);
+          const float ki = in(kg, i, c, rn[i * 2 + 1]);
+          const float qr = in(qg, rr, c, rn[rr * 2]);
           const float ex = __expf(Gs[rr * SG + c] - Gs[i * SG + c]);
           sa += kr * ki * ex;
           sp += qr * ki * ex;
@@ -920,7 +1007,10 @@ __global__ __launch_bounds__(kIntraThreads, 4) void intra_chunk_kernel(KernelPtr
   for (int j = 0; j < FPW; ++j)
     if (fv[j]) {
 #pragma unroll
-      for (int e = 0; e < 8; ++e) VT.store((32 * fkb[j] + 8 * lg + e) * SK + r, rv ? vraw[j].get(e) : 0.f);
+      for (int e = 0; e < 8; ++e) {
+        const float x = vraw[j].get(e);
+        VT.store((32 * fkb[j] + 8 * lg + e) * SK + r, rv ? (PRO ? swishf(x) : x) : 0.f);
+      }
     }
   if (KC > C) {
     for (int idx = tid; idx < D * (KC - C); idx += kIntraThreads) {
@@ -1241,11 +1331,16 @@ __device__ __forceinline__ void inter_o_role(const KernelPtrs& kp, const InterGe
         for (int x = 0; x < 4; ++x) {
           const int row = 16 * rt + 4 * (l >> 4) + x;
           if (row < len) {
-            const size_t oi = ((size_t)(t0 + row) * H + gm.h) * D + gm.col0 + 16 * ct + (l & 15);
-            if constexpr (OUT_BF16)
-              reinterpret_cast<bf16*>(kp.o)[oi] = f2bf(o[x]);
-            else
-              reinterpret_cast<float*>(kp.o)[oi] = o[x];
+            const int col = gm.col0 + 16 * ct + (l & 15);
+            if (kp.o_slots) {  // raw o for the layer epilogue
+              kp.o_slots[(((size_t)(gm.cbase + ci) * H + gm.h) * C + row) * D + col] = o[x];
+            } else {
+              const size_t oi = ((size_t)(t0 + row) * H + gm.h) * D + col;
+              if constexpr (OUT_BF16)
+                reinterpret_cast<bf16*>(kp.o)[oi] = f2bf(o[x]);
+              else
+                reinterpret_cast<float*>(kp.o)[oi] = o[x];
+            }
           }
         }
       }
@@ -1263,6 +1358,51 @@ __device__ __forceinline__ void inter_o_role(const KernelPtrs& kp, const InterGe
     step(fa, fb, ci);
     if (ci + 1 >= gm.ci_hi) break;
     step(fb, fa, ci + 1);
+  }
+}
+
+// ---------------------------------------------------------------------------
+// Layer epilogue (the "Kimi Linear" notes, docsaid.org, section "Other
+// Components"; greeksharifa.github.io summary, section 4): per token and
+// head, y = o / sqrt(mean_c o_c^2 + eps) * weight * sigmoid(gate).  The norm
+// spans all D value columns, which the inter-chunk pass splits over
+// workgroups, so it runs after that pass, per segment, on the raw o it left
+// in the workspace.  One workgroup per (slot, head); one wave per token row,
+// D/64 columns per lane.
+// ---------------------------------------------------------------------------
+template <class M, int D, int C, bool OUT_BF16>
+__global__ __launch_bounds__(256) void layer_epilogue_kernel(KernelPtrs kp, SeqInfo si) {
+  typedef typename M::in_t in_t;
+  constexpr int CPL = D / 64;  // columns per lane
+  const Item it = intra_item<C>(si, kp, blockIdx.x, 0);
+  const int slot = blockIdx.x / kp.H;
+  const int w = wave_id(), l = lane_id();
+  const in_t* gate = reinterpret_cast<const in_t*>(kp.gate);
+  float wt[CPL];
+#pragma unroll
+  for (int e = 0; e < CPL; ++e) wt[e] = kp.norm_weight[CPL * l + e];
+  for (int row = w; row < it.len; row += 4) {
+    const float* src = kp.o_slots + (((size_t)slot * kp.H + it.h) * C + row) * D + CPL * l;
+    const size_t ti = ((size_t)(it.t0 + row) * kp.H + it.h) * D + CPL * l;
+    float x[CPL], gv[CPL];
+    float ss = 0.f;
+#pragma unroll
+    for (int e = 0; e < CPL; ++e) {
+      x[e] = src[e];
+      gv[e] = (float)gate[ti + e];
+      ss += x[e] * x[e];
+    }
+#pragma unroll
+    for (int off = 32; off > 0; off >>= 1) ss += __shfl_xor(ss, off);
+    const float inv = 1.f / sqrtf(ss / D + kp.norm_eps);
+#pragma unroll
+    for (int e = 0; e < CPL; ++e) {
+      const float y = x[e] * inv * wt[e] * sigmoidf(gv[e]);
+      if constexpr (OUT_BF16)
+        reinterpret_cast<bf16*>(kp.o)[ti + e] = f2bf(y);
+      else
+        reinterpret_cast<float*>(kp.o)[ti + e] = y;
+    }
   }
 }
 
@@ -1353,6 +1493,7 @@ static void launch_inter(const PrefillArgs& a, const KernelPtrs& kp, const SeqIn
 // ---------------------------------------------------------------------------
 template <class M, int D, int C, bool SDEC>
 static hipError_t launch_prefill_t(const PrefillArgs& a) {
+  typedef Layout<M, D, C> LY;
   char* ws = reinterpret_cast<char*>(a.workspace);
   const SegmentPlan plan =
       plan_segments(a.num_seqs, a.cu_seqlens_host, a.seq_len, a.H, D, C, a.in_bf16);
@@ -1379,12 +1520,23 @@ static hipError_t launch_prefill_t(const PrefillArgs& a) {
   kp.carry = carry ? reinterpret_cast<float*>(after_table) : nullptr;
   kp.ops = after_table + carry;
   kp.H = a.H;
+  const bool epi = a.layer.gate != nullptr;
+  kp.o_slots = epi ? reinterpret_cast<float*>(kp.ops + (size_t)plan.max_slots * a.H * LY::kBytes)
+                   : nullptr;
+  kp.gate = a.layer.gate;
+  kp.norm_weight = a.layer.norm_weight;
+  kp.norm_eps = a.layer.norm_eps;
 
   constexpr size_t lds = IntraLds<M, D, C>::kTotal;
   static_assert(lds <= 160 * 1024, "intra-chunk LDS");
+  // The prologue is built for the per-channel decay only.
+  constexpr bool kPro = !SDEC;
+  if (SDEC && a.layer.prologue) return hipErrorInvalidValue;
+  const bool pro = kPro && a.layer.prologue;
+  const void* intra_fn = pro ? reinterpret_cast<const void*>(&intra_chunk_kernel<M, D, C, SDEC, kPro>)
+                             : reinterpret_cast<const void*>(&intra_chunk_kernel<M, D, C, SDEC, false>);
   if (plan.max_slots > 0) {
-    hipError_t e = hipFuncSetAttribute(reinterpret_cast<const void*>(&intra_chunk_kernel<M, D, C, SDEC>),
-                                       hipFuncAttributeMaxDynamicSharedMemorySize, (int)lds);
+    hipError_t e = hipFuncSetAttribute(intra_fn, hipFuncAttributeMaxDynamicSharedMemorySize, (int)lds);
     if (e != hipSuccess) return e;
   }
   const int nct = choose_nct(a.num_seqs * a.H, D);
@@ -1400,13 +1552,24 @@ static hipError_t launch_prefill_t(const PrefillArgs& a) {
       const int c = sc.nch(0) - si.c0;
       si.slot_cnt = c <= 0 ? 0 : (c < plan.L ? c : plan.L);
     }
-    if (slots > 0)
-      hipLaunchKernelGGL((intra_chunk_kernel<M, D, C, SDEC>), dim3((unsigned)slots, a.H), dim3(kIntraThreads),
-                         lds, a.stream, kp, si);
+    if (slots > 0 && pro)
+      hipLaunchKernelGGL((intra_chunk_kernel<M, D, C, SDEC, kPro>), dim3((unsigned)slots, a.H),
+                         dim3(kIntraThreads), lds, a.stream, kp, si);
+    else if (slots > 0)
+      hipLaunchKernelGGL((intra_chunk_kernel<M, D, C, SDEC, false>), dim3((unsigned)slots, a.H),
+                         dim3(kIntraThreads), lds, a.stream, kp, si);
     if (nct == 2)
       launch_inter<M, D, C, 2>(a, kp, si);
     else
       launch_inter<M, D, C, 1>(a, kp, si);
+    if (epi && slots > 0) {
+      const dim3 grid((unsigned)(slots * a.H));
+      if (a.out_bf16)
+        hipLaunchKernelGGL((layer_epilogue_kernel<M, D, C, true>), grid, dim3(256), 0, a.stream, kp, si);
+      else
+        hipLaunchKernelGGL((layer_epilogue_kernel<M, D, C, false>), grid, dim3(256), 0, a.stream, kp,
+                           si);
+    }
   }
   return hipGetLastError();
 }

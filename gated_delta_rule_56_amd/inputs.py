@@ -113,6 +113,40 @@ def draw_tokens(rng: np.random.Generator, T: int, H: int, Dk: int, Dv: int,
     return TokenInputs(q, k, v, g.astype(np.float32), beta.astype(np.float32), dtype)
 
 
+@dataclasses.dataclass
+class LayerInputs:
+    """Inputs of the fused layer: the projections before their activations.
+
+    q_pre, k_pre, v_pre, gate ~ N(0, 1) (bf16-exact for ``"bf16"``);
+    beta_logit ~ N(0, 1) float32; g as in :func:`draw_tokens`; norm_weight
+    ``[Dv]`` = 1 + 0.1 N(0, 1) float32.
+    """
+    q_pre: np.ndarray       # [T, H, Dk]
+    k_pre: np.ndarray       # [T, H, Dk]
+    v_pre: np.ndarray       # [T, H, Dv]
+    g: np.ndarray           # [T, H, Dk]
+    beta_logit: np.ndarray  # [T, H]
+    gate: np.ndarray        # [T, H, Dv]
+    norm_weight: np.ndarray  # [Dv]
+    dtype: str
+
+
+def draw_layer_tokens(rng: np.random.Generator, T: int, H: int, Dk: int, Dv: int,
+                      dtype: str = "bf16", g_scale: float = 0.1) -> LayerInputs:
+    if dtype not in ("bf16", "f32"):
+        raise ValueError(f"dtype must be 'bf16' or 'f32', got {dtype!r}")
+    q = rng.standard_normal((T, H, Dk))
+    k = rng.standard_normal((T, H, Dk))
+    v = rng.standard_normal((T, H, Dv))
+    gate = rng.standard_normal((T, H, Dv))
+    beta = rng.standard_normal((T, H))
+    g = -_softplus(rng.standard_normal((T, H, Dk))) * g_scale
+    w = 1.0 + 0.1 * rng.standard_normal(Dv)
+    rnd = bf16_round if dtype == "bf16" else (lambda a: a.astype(np.float32))
+    return LayerInputs(rnd(q), rnd(k), rnd(v), g.astype(np.float32), beta.astype(np.float32),
+                       rnd(gate), w.astype(np.float32), dtype)
+
+
 def draw_states(rng: np.random.Generator, N: int, H: int, Dk: int, Dv: int,
                 std: float = 0.1) -> np.ndarray:
     """Initial fast-weight states ``[N, H, Dk, Dv]`` ~ N(0, std^2), float32."""

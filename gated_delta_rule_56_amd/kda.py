@@ -52,6 +52,17 @@ def load() -> ctypes.CDLL:
     lib.gdn_prefill.restype = i32
     lib.gdn_decode_step.argtypes = lib.kda_decode_step.argtypes
     lib.gdn_decode_step.restype = i32
+    f32 = ctypes.c_float
+    lib.kda_prefill_layer_workspace_size.argtypes = [i32, i32, i32, i32, i32, i32, vp, i32, i32,
+                                                     i32, ctypes.POINTER(sz)]
+    lib.kda_prefill_layer_workspace_size.restype = i32
+    lib.kda_prefill_layer.argtypes = [vp, vp, vp, vp, vp, vp, vp, f32, vp, vp, vp, vp, vp,
+                                      i32, i32, i32, i32, i32, i32, i32, i32, i32,
+                                      vp, sz, vp]
+    lib.kda_prefill_layer.restype = i32
+    lib.kda_decode_step_layer.argtypes = [vp, vp, vp, vp, vp, vp, vp, f32, vp, vp,
+                                          i32, i32, i32, i32, i32, i32, vp]
+    lib.kda_decode_step_layer.restype = i32
     _lib = lib
     return lib
 
@@ -95,12 +106,21 @@ def _host_cu(cu_seqlens, cu_seqlens_host) -> np.ndarray:
 
 
 def workspace_size(B: int, T: int, H: int, D: int, num_seqs: int, chunk_size: int,
-                   in_dtype: int, cu_seqlens_host: Optional[np.ndarray] = None) -> int:
+                   in_dtype: int, cu_seqlens_host: Optional[np.ndarray] = None,
+                   layer_gate: Optional[bool] = None) -> int:
+    """Workspace bytes of kda_prefill (``layer_gate`` None) or of
+    kda_prefill_layer with (True) or without (False) the gated epilogue."""
     out = ctypes.c_size_t(0)
     cu_p = None if cu_seqlens_host is None else cu_seqlens_host.ctypes.data
-    _check(load().kda_prefill_workspace_size(B, T, H, D, D, num_seqs, cu_p, chunk_size,
-                                             in_dtype, ctypes.byref(out)),
-           "kda_prefill_workspace_size")
+    if layer_gate is None:
+        _check(load().kda_prefill_workspace_size(B, T, H, D, D, num_seqs, cu_p, chunk_size,
+                                                 in_dtype, ctypes.byref(out)),
+               "kda_prefill_workspace_size")
+    else:
+        _check(load().kda_prefill_layer_workspace_size(B, T, H, D, D, num_seqs, cu_p,
+                                                       chunk_size, in_dtype, int(layer_gate),
+                                                       ctypes.byref(out)),
+               "kda_prefill_layer_workspace_size")
     return out.value
 
 
@@ -123,12 +143,51 @@ def prefill(q, k, v, g, beta, initial_state=None, cu_seqlens=None, *,
     Returns ``(o, final_state)`` (final_state None unless requested).
     ``final_state`` may be passed (it may alias initial_state).
     """
+    return _prefill(q, k, v, g, beta, initial_state, cu_seqlens, cu_seqlens_host, chunk_size,
+                    out_dtype, output_final_state, final_state, o, workspace, None)
+
+
+def layer_prefill(q_pre, k_pre, v_pre, g, beta_logit, gate=None, norm_weight=None,
+                  norm_eps: float = 1e-6, initial_state=None, cu_seqlens=None, *,
+                  cu_seqlens_host: Optional[Union[Sequence[int], np.ndarray]] = None,
+                  chunk_size: int = 64, out_dtype=None, output_final_state: bool = True,
+                  final_state=None, o=None, workspace=None):
+    """KDA layer forward with the fused prologue and epilogue
+    (``kda_prefill_layer``): Swish + L2 norm of q and k, Swish of v, sigmoid
+    of beta, the recurrence, then with ``gate`` ``[B, T, H, Dv]`` (dtype of
+    q) the head-wise RMSNorm times ``norm_weight`` ``[Dv]`` float32 times
+    sigmoid(gate).  Shapes and the rest as in :func:`prefill` (KDA decay g
+    ``[B, T, H, Dk]`` only)."""
+    return _prefill(q_pre, k_pre, v_pre, g, beta_logit, initial_state, cu_seqlens,
+                    cu_seqlens_host, chunk_size, out_dtype, output_final_state, final_state, o,
+                    workspace, (gate, norm_weight, float(norm_eps)))
+
+
+def _check_layer_args(layer, q, out_shape, Dv):
+    torch = _torch()
+    gate, weight, _ = layer
+    if gate is None:
+        return
+    _expect("gate", gate, out_shape)
+    if gate.dtype != q.dtype or not gate.is_contiguous():
+        raise KDAError("gate must be contiguous with the dtype of q")
+    if weight is None:
+        raise KDAError("norm_weight is required with gate")
+    _expect("norm_weight", weight, (Dv,))
+    if weight.dtype != torch.float32 or not weight.is_contiguous():
+        raise KDAError("norm_weight must be contiguous float32")
+
+
+def _prefill(q, k, v, g, beta, initial_state, cu_seqlens, cu_seqlens_host, chunk_size,
+             out_dtype, output_final_state, final_state, o, workspace, layer):
     torch = _torch()
     if q.dim() != 4:
         raise KDAError("q must be [B, T, H, D]")
     B, T, H, D = q.shape
     Dv = v.shape[-1]
     scalar_g = g.dim() == 3
+    if layer is not None and scalar_g:
+        raise KDAError("the fused layer takes the per-channel decay g [B, T, H, Dk]")
     _expect("k", k, (B, T, H, D))
     _expect("v", v, (B, T, H, Dv))
     _expect("g", g, (B, T, H) if scalar_g else (B, T, H, D))
@@ -167,10 +226,22 @@ def prefill(q, k, v, g, beta, initial_state=None, cu_seqlens=None, *,
     if final_state is not None and (final_state.dtype != torch.float32
                                     or not final_state.is_contiguous()):
         raise KDAError("final_state must be contiguous float32")
-    ws_bytes = workspace_size(B, T, H, D, N, chunk_size, in_code, cu_h)
+    if layer is not None:
+        _check_layer_args(layer, q, (B, T, H, Dv), Dv)
+    ws_bytes = workspace_size(B, T, H, D, N, chunk_size, in_code, cu_h,
+                              None if layer is None else layer[0] is not None)
     if workspace is None or workspace.numel() < ws_bytes:
         workspace = torch.empty(max(ws_bytes, 1), dtype=torch.uint8, device=q.device)
     cu_hp = None if cu_h is None else cu_h.ctypes.data
+    if layer is not None:
+        gate, weight, eps = layer
+        _check(load().kda_prefill_layer(
+            _ptr(q), _ptr(k), _ptr(v), _ptr(g), _ptr(beta), _ptr(gate), _ptr(weight), eps,
+            _ptr(o), _ptr(initial_state), _ptr(final_state), _ptr(cu_seqlens), cu_hp,
+            B, T, H, D, Dv, N, chunk_size, in_code, out_code,
+            _ptr(workspace), workspace.numel(), _stream_ptr(q.device)),
+            "kda_prefill_layer")
+        return o, final_state
     fn = load().gdn_prefill if scalar_g else load().kda_prefill
     _check(fn(
         _ptr(q), _ptr(k), _ptr(v), _ptr(g), _ptr(beta), _ptr(o),
@@ -189,10 +260,25 @@ def decode_step(q, k, v, g, beta, state, *, out_dtype=None, o=None):
     scalar-decay Gated DeltaNet form (``gdn_decode_step``).  Returns o
     ``[N, H, Dv]``.
     """
+    return _decode(q, k, v, g, beta, state, out_dtype, o, None)
+
+
+def layer_decode_step(q_pre, k_pre, v_pre, g, beta_logit, state, gate=None, norm_weight=None,
+                      norm_eps: float = 1e-6, *, out_dtype=None, o=None):
+    """One KDA layer step with the fused prologue and epilogue
+    (``kda_decode_step_layer``); see :func:`layer_prefill`.  gate
+    ``[N, H, Dv]``; ``state`` updated in place."""
+    return _decode(q_pre, k_pre, v_pre, g, beta_logit, state, out_dtype, o,
+                   (gate, norm_weight, float(norm_eps)))
+
+
+def _decode(q, k, v, g, beta, state, out_dtype, o, layer):
     torch = _torch()
     N, H, D = q.shape
     Dv = v.shape[-1]
     scalar_g = g.dim() == 2
+    if layer is not None and scalar_g:
+        raise KDAError("the fused layer takes the per-channel decay g [N, H, Dk]")
     _expect("k", k, (N, H, D))
     _expect("v", v, (N, H, Dv))
     _expect("g", g, (N, H) if scalar_g else (N, H, D))
@@ -209,6 +295,14 @@ def decode_step(q, k, v, g, beta, state, *, out_dtype=None, o=None):
         raise KDAError("state, g and beta must be float32")
     if o is None:
         o = torch.empty((N, H, Dv), dtype=out_dtype, device=q.device)
+    if layer is not None:
+        _check_layer_args(layer, q, (N, H, Dv), Dv)
+        gate, weight, eps = layer
+        _check(load().kda_decode_step_layer(
+            _ptr(q), _ptr(k), _ptr(v), _ptr(g), _ptr(beta), _ptr(gate), _ptr(weight), eps,
+            _ptr(state), _ptr(o), N, H, D, Dv, in_code, out_code, _stream_ptr(q.device)),
+            "kda_decode_step_layer")
+        return o
     fn = load().gdn_decode_step if scalar_g else load().kda_decode_step
     _check(fn(
         _ptr(q), _ptr(k), _ptr(v), _ptr(g), _ptr(beta), _ptr(state), _ptr(o),

@@ -187,6 +187,66 @@ kda_status gdn_decode_step(const void* q, const void* k, const void* v,
                            kda_dtype in_dtype, kda_dtype out_dtype,
                            void* stream /* hipStream_t */);
 
+/*
+ * The KDA layer's elementwise work fused around the recurrence (the docsaid.org
+ * "Kimi Linear" notes, section "Other Components"; the greeksharifa.github.io
+ * summary, section 4 "Model Architecture").  The inputs are the projections
+ * before their activations:
+ *
+ *   q = L2norm(Swish(q_pre)),  k = L2norm(Swish(k_pre))   per (token, head)
+ *   v = Swish(v_pre),          beta = sigmoid(beta_logit)
+ *
+ * with Swish(x) = x * sigmoid(x) and L2norm(x) = x / max(|x|_2, 1e-12).  The
+ * recurrence then runs as in kda_prefill / kda_decode_step.  When gate is not
+ * NULL the output is
+ *
+ *   y[t, h, c] = o[t, h, c] / sqrt(mean_c' o[t, h, c']^2 + norm_eps)
+ *                * norm_weight[c] * sigmoid(gate[t, h, c])
+ *
+ * (head-wise RMSNorm with a per-channel weight shared by the heads, times the
+ * output gate); when gate is NULL, o itself is written and norm_weight and
+ * norm_eps are ignored.  The final states are those of the recurrence.
+ *
+ * Arguments are those of kda_prefill / kda_decode_step, plus:
+ *   q_pre, k_pre, v_pre  as q, k, v (in_dtype)
+ *   beta_logit  [tokens, H] float32 (sigmoid applied inside)
+ *   gate        [tokens, H, Dv] in_dtype, or NULL
+ *   norm_weight [Dv] float32 (required with gate)
+ *   norm_eps    finite, >= 0
+ * kda_prefill_layer's workspace must be at least
+ * kda_prefill_layer_workspace_size(..., with_gate = gate != NULL) bytes: with
+ * the gate it also holds one segment's raw fp32 output (chunk * Dv * 4 bytes
+ * per chunk and head), because the norm spans value columns that the
+ * inter-chunk pass computes in separate workgroups.
+ */
+kda_status kda_prefill_layer_workspace_size(int B, int T, int H, int Dk, int Dv,
+                                            int num_seqs,
+                                            const int32_t* cu_seqlens_host,
+                                            int chunk_size, kda_dtype in_dtype,
+                                            int with_gate, size_t* bytes);
+
+kda_status kda_prefill_layer(const void* q_pre, const void* k_pre,
+                             const void* v_pre, const float* g,
+                             const float* beta_logit, const void* gate,
+                             const float* norm_weight, float norm_eps, void* o,
+                             const float* initial_state, float* final_state,
+                             const int32_t* cu_seqlens,
+                             const int32_t* cu_seqlens_host, int B, int T,
+                             int H, int Dk, int Dv, int num_seqs,
+                             int chunk_size, kda_dtype in_dtype,
+                             kda_dtype out_dtype, void* workspace,
+                             size_t workspace_bytes,
+                             void* stream /* hipStream_t */);
+
+kda_status kda_decode_step_layer(const void* q_pre, const void* k_pre,
+                                 const void* v_pre, const float* g,
+                                 const float* beta_logit, const void* gate,
+                                 const float* norm_weight, float norm_eps,
+                                 float* state, void* o, int N, int H, int Dk,
+                                 int Dv, kda_dtype in_dtype,
+                                 kda_dtype out_dtype,
+                                 void* stream /* hipStream_t */);
+
 #ifdef __cplusplus
 }
 #endif

@@ -136,3 +136,46 @@ def test_decode_validation(lib):
     assert d(Dk=32, Dv=32) == UNSUPPORTED
     assert d(o=FAKE + 8) == INVALID
     assert d(outd=5) == INVALID
+
+
+def test_layer_workspace_size(lib):
+    # Without the gate the layer call needs exactly the plain workspace; with
+    # it, one segment's raw fp32 output as well: 32 slots x 32 heads x 64 x
+    # 128 x 4 B at T=4096 (two segments of 32 chunks).
+    if "KDA_PREFILL_SEGMENT_KB" in os.environ or "KDA_PREFILL_SEGMENT_CHUNKS" in os.environ:
+        pytest.skip("segment plan overridden")
+    plain = kda.workspace_size(1, 4096, 32, 128, 1, 64, kda.KDA_BF16)
+    assert kda.workspace_size(1, 4096, 32, 128, 1, 64, kda.KDA_BF16, layer_gate=False) == plain
+    gated = kda.workspace_size(1, 4096, 32, 128, 1, 64, kda.KDA_BF16, layer_gate=True)
+    assert gated == plain + 32 * 32 * 64 * 128 * 4
+
+
+def _layer_prefill(lib, **kw):
+    a = dict(q=FAKE, k=FAKE, v=FAKE, g=FAKE, beta=FAKE, gate=FAKE, w=FAKE, eps=1e-6, o=FAKE,
+             s0=None, s1=None, cu=None, cu_host=None, B=1, T=128, H=2, Dk=128, Dv=128, N=1,
+             C=64, ind=0, outd=1, ws=FAKE, wsb=1 << 40, stream=None)
+    a.update(kw)
+    return lib.kda_prefill_layer(a["q"], a["k"], a["v"], a["g"], a["beta"], a["gate"], a["w"],
+                                 a["eps"], a["o"], a["s0"], a["s1"], a["cu"], a["cu_host"],
+                                 a["B"], a["T"], a["H"], a["Dk"], a["Dv"], a["N"], a["C"],
+                                 a["ind"], a["outd"], a["ws"], a["wsb"], a["stream"])
+
+
+def test_layer_validation(lib):
+    # Every call fails validation; the first check that fails decides.
+    assert _layer_prefill(lib, w=None, ws=None) == INVALID       # gate without weight
+    assert _layer_prefill(lib, eps=-1.0, ws=None) == INVALID
+    assert _layer_prefill(lib, eps=float("inf"), ws=None) == INVALID
+    assert _layer_prefill(lib, eps=float("nan"), ws=None) == INVALID
+    assert _layer_prefill(lib, gate=FAKE + 2, ws=None) == INVALID  # misaligned gate
+    assert _layer_prefill(lib, ws=None) == WORKSPACE
+    assert _layer_prefill(lib, gate=None, w=None, ws=None) == WORKSPACE
+    assert _layer_prefill(lib, Dk=96, Dv=96) == UNSUPPORTED
+    d = lambda **kw: lib.kda_decode_step_layer(
+        *[kw.get(n, FAKE) for n in ("q", "k", "v", "g", "beta", "gate", "w")], kw.get("eps", 1e-6),
+        kw.get("state", FAKE), kw.get("o", FAKE), kw.get("N", 4), kw.get("H", 2),
+        kw.get("Dk", 64), kw.get("Dv", 64), kw.get("ind", 1), kw.get("outd", 1), None)
+    assert d(w=None) == INVALID
+    assert d(eps=-0.5) == INVALID
+    assert d(state=None) == INVALID
+    assert d(Dk=32, Dv=32) == UNSUPPORTED
