@@ -63,8 +63,8 @@ def decode_algorithmic_bytes(N=D_N, H=D_H, d=D_D):
 # run.  A figure is reported only while the kernel sources still hash to the
 # values it was measured on.
 TRAFFIC = {
-    "prefill": {"sources": "78bcc62772fd0fb7", "bytes": 873218517},
-    "decode": {"sources": "9b282d3be22a2ead", "bytes": 1089484282},
+    "prefill": {"sources": "37b508b660850da4", "bytes": 870272448},
+    "decode": {"sources": "e2a4b5474702cdbd", "bytes": 1089482400},
 }
 
 
@@ -166,7 +166,64 @@ def other_workloads(torch, kda, I, dev):
         tiny[f"chunk{C}_us_per_call"] = round(t * 1e6, 2)
         tiny[f"chunk{C}_tokens_per_s"] = round(w.T / t, 1)
     out["tiny_fp32"] = {"workload": "kda_prefill B=1 H=1 T=256 d=64 fp32", **tiny}
+    out["layer"] = layer_workloads(torch, kda, I, dev)
     return out
+
+
+def layer_workloads(torch, kda, I, dev):
+    """The fused layer entry points on the headline shapes: prologue (Swish,
+    L2 norm, sigmoid) and gated RMSNorm epilogue in the kernels."""
+    T, H, d, N = P_T, P_H, P_D, D_N
+    # two input sets, alternated, so the inputs do not stay in the Infinity Cache
+    sets = [I.device_layer_tokens(torch, T, H, d, d, 4004 + i, dev) for i in range(2)]
+    w = sets[0][6]
+    o = torch.empty((1, T, H, d), dtype=torch.float32, device=dev)
+    fin = torch.empty((1, H, d, d), dtype=torch.float32, device=dev)
+    ws = torch.empty(kda.workspace_size(1, T, H, d, 1, P_C, kda.KDA_BF16, layer_gate=True),
+                     dtype=torch.uint8, device=dev)
+    calls = [0]
+
+    def run():
+        q, k, v, gate, g, b, _ = sets[calls[0] % 2]
+        calls[0] += 1
+        kda.layer_prefill(q, k, v, g, b, gate, w, 1e-6, chunk_size=P_C, o=o, final_state=fin,
+                          workspace=ws)
+
+    t = time_calls(torch, run, 20)
+    # q, k, v, gate bf16 + g fp32 + beta fp32 + o fp32 per token-head, + final state
+    by = T * H * (4 * 2 * d + 4 * d + 4 + 4 * d) + H * d * d * 4 + d * 4
+    res = {"prefill_workload": f"kda_prefill_layer B=1 H={H} T={T} d={d} chunk {P_C}, bf16 in / "
+                               "fp32 out, gated RMSNorm epilogue, final state",
+           "prefill_us_per_call": round(t * 1e6, 2), "prefill_tokens_per_s": round(T / t, 1),
+           "prefill_algorithmic_GBps": round(by / t / 1e9, 1)}
+    del sets, o, fin, ws
+    qd, kd, vd, gd, gtd, bd = (torch.randn((N, H, d), device=dev).to(torch.bfloat16)
+                               for _ in range(6))
+    gd = -torch.nn.functional.softplus(gd.float()) * 0.1
+    bd = torch.randn((N, H), device=dev)
+    st = torch.randn((N, H, d, d), device=dev) * 0.1
+    od = torch.empty((N, H, d), dtype=torch.float32, device=dev)
+    t = time_calls(torch, lambda: kda.layer_decode_step(qd, kd, vd, gd, bd, st, gtd, w, 1e-6,
+                                                         o=od), 20)
+    by = N * H * (2 * d * d * 4 + 4 * 2 * d + 4 * d + 4 + 4 * d) + d * 4
+    res.update({"decode_workload": f"kda_decode_step_layer N={N} H={H} d={d}, bf16 in / fp32 out, "
+                                   "gated RMSNorm epilogue",
+                "decode_us_per_step": round(t * 1e6, 2), "decode_GBps": round(by / t / 1e9, 1),
+                "decode_hbm_frac": round(by / t / 1e9 / HBM_PEAK_GBS, 4)})
+    return res
+
+
+def time_calls(torch, fn, reps):
+    """Mean time (s) of ``fn()`` over ``reps`` calls after one warm-up."""
+    fn()
+    torch.cuda.synchronize()
+    a, b = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    a.record()
+    for _ in range(reps):
+        fn()
+    b.record()
+    torch.cuda.synchronize()
+    return a.elapsed_time(b) / reps / 1e3
 
 
 def log(*a):

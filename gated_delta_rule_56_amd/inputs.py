@@ -306,3 +306,23 @@ def device_tokens(torch, T: int, H: int, Dk: int, Dv: int, seed: int, device,
             torch.randn((n, H, Dk), generator=gen, device=device)) * 0.1
         beta[0, sl] = torch.sigmoid(torch.randn((n, H), generator=gen, device=device))
     return q, k, v, g, beta
+
+
+def device_layer_tokens(torch, T: int, H: int, Dk: int, Dv: int, seed: int, device,
+                        dtype: str = "bf16"):
+    """The fused layer's inputs (recipe of :class:`LayerInputs`) drawn on the
+    GPU with torch's seeded generator.  Returns q_pre, k_pre, v_pre, gate
+    ``[1, T, H, D]`` (bf16 or float32), g ``[1, T, H, Dk]``, beta_logit
+    ``[1, T, H]`` and norm_weight ``[Dv]`` (float32)."""
+    gen = torch.Generator(device=device)
+    gen.manual_seed(seed)
+    dt = torch.bfloat16 if dtype == "bf16" else torch.float32
+    rn = lambda *s: torch.randn(s, generator=gen, device=device)
+    q = rn(1, T, H, Dk).to(dt)
+    k = rn(1, T, H, Dk).to(dt)
+    v = rn(1, T, H, Dv).to(dt)
+    gate = rn(1, T, H, Dv).to(dt)
+    beta = rn(1, T, H)
+    g = -torch.nn.functional.softplus(rn(1, T, H, Dk)) * 0.1
+    w = 1.0 + 0.1 * rn(Dv)
+    return q, k, v, gate, g, beta, w
