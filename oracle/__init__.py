@@ -15,6 +15,9 @@ Functions
                        L2 normalisation of q and k, Swish of v, sigmoid of beta.
 ``layer_epilogue``     head-wise RMSNorm of o times a sigmoid output gate.
 ``kda_layer``          prologue, recurrence, epilogue.
+``short_conv``         causal depthwise convolution over the tokens of each
+                       sequence, with a carried state of the last inputs.
+``kda_layer_conv``     short convolution of q, k, v, then ``kda_layer``.
 
 Sources (pages this package follows):
   * Recurrence: "Kimi Linear" notes (docsaid.org), section "KDA: Splitting
@@ -33,6 +36,13 @@ Sources (pages this package follows):
     sigmoid; output: per-head RMSNorm, then a data-dependent sigmoid gate);
     greeksharifa.github.io summary, section 4 (head-wise RMSNorm followed by
     a sigmoid gate; queries and keys normalised to unit length).
+  * Short convolution: same docsaid.org section (q, k and v each pass through
+    a short convolution after their projection, before Swish); the
+    deepstudy.best introduction (short convolutions capture local token
+    dependencies).  The pages give neither the width nor the padding; the
+    reading taken is a causal, depthwise (per channel) convolution of width
+    W <= 4 with no bias, restarted at every sequence start from a carried
+    state (zeros when none is given).
 
 Pins: every function here is checked in ``tests/test_oracle_pins.py`` against
 closed forms, special cases, the two-channel decay table printed on the
@@ -305,3 +315,49 @@ def kda_layer(q_pre, k_pre, v_pre, g, beta_pre, gate=None, weight=None, eps=1e-6
     if gate is not None:
         o = layer_epilogue(o, gate, weight, eps)
     return o, fin
+
+
+def short_conv(x, weight, state=None, cu_seqlens=None):
+    """Causal depthwise convolution over tokens, per sequence.
+
+    x ``[T, H, D]``; weight ``[H, D, W]``; state ``[N, H, W-1, D]`` or None.
+    For token t of sequence n (tokens bos..eos-1):
+        y[t, h, c] = sum_{i=0}^{W-1} weight[h, c, i] * x(t - (W-1) + i)[h, c]
+    where x(s) for s < bos is state[n, h, (W-1) + (s - bos)] (zero without a
+    state): weight[..., W-1] multiplies the current token.  Returns y
+    ``[T, H, D]`` and the final state, the last W-1 inputs of each sequence
+    (state rows where the sequence is shorter than W-1), float64.
+    """
+    x = np.asarray(x, dtype=np.float64)
+    w = np.asarray(weight, dtype=np.float64)
+    T, H, D = x.shape
+    W = w.shape[-1]
+    cu = np.array([0, T]) if cu_seqlens is None else np.asarray(cu_seqlens, dtype=np.int64)
+    N = len(cu) - 1
+    st = (np.zeros((N, H, W - 1, D)) if state is None
+          else np.asarray(state, dtype=np.float64).reshape(N, H, W - 1, D))
+    y = np.zeros_like(x)
+    fin = np.zeros((N, H, W - 1, D))
+    for n in range(N):
+        bos, eos = int(cu[n]), int(cu[n + 1])
+        # the sequence's inputs preceded by its state rows: position p of
+        # ext holds x(bos - (W-1) + p)
+        ext = np.concatenate([st[n].transpose(1, 0, 2), x[bos:eos]], axis=0)  # [W-1+len, H, D]
+        for t in range(eos - bos):
+            for i in range(W):
+                y[bos + t] += w[:, :, i] * ext[t + i]
+        fin[n] = ext[len(ext) - (W - 1):].transpose(1, 0, 2) if W > 1 else fin[n]
+    return y, fin
+
+
+def kda_layer_conv(q_pre, k_pre, v_pre, g, beta_pre, conv_weight, conv_state=None, gate=None,
+                   weight=None, eps=1e-6, initial_state=None, cu_seqlens=None):
+    """Short convolution of q_pre, k_pre, v_pre (``conv_weight`` = (w_q, w_k,
+    w_v), ``conv_state`` = (s_q, s_k, s_v) or None), then :func:`kda_layer`.
+    Returns (y, final_state, (conv state of q, k, v))."""
+    states = (None, None, None) if conv_state is None else conv_state
+    conv = [short_conv(x, w, s, cu_seqlens) for x, w, s in
+            zip((q_pre, k_pre, v_pre), conv_weight, states)]
+    y, fin = kda_layer(conv[0][0], conv[1][0], conv[2][0], g, beta_pre, gate, weight, eps,
+                       initial_state, cu_seqlens)
+    return y, fin, tuple(c[1] for c in conv)
