@@ -171,8 +171,9 @@ def other_workloads(torch, kda, I, dev):
 
 
 def layer_workloads(torch, kda, I, dev):
-    """The fused layer entry points on the headline shapes: prologue (Swish,
-    L2 norm, sigmoid) and gated RMSNorm epilogue in the kernels."""
+    """The fused layer entry points on the headline shapes: prologue (short
+    convolution of width 4, Swish, L2 norm, sigmoid) and gated RMSNorm
+    epilogue in the kernels."""
     T, H, d, N = P_T, P_H, P_D, D_N
     # two input sets, alternated, so the inputs do not stay in the Infinity Cache
     sets = [I.device_layer_tokens(torch, T, H, d, d, 4004 + i, dev) for i in range(2)]
@@ -182,18 +183,23 @@ def layer_workloads(torch, kda, I, dev):
     ws = torch.empty(kda.workspace_size(1, T, H, d, 1, P_C, kda.KDA_BF16, layer_gate=True),
                      dtype=torch.uint8, device=dev)
     calls = [0]
+    W = 4
+    cw = tuple(torch.randn((H, d, W), device=dev) / W ** 0.5 for _ in range(3))
+    cs = tuple(torch.randn((1, H, W - 1, d), device=dev).to(torch.bfloat16) for _ in range(3))
+    cs_out = tuple(torch.empty_like(c) for c in cs)
 
     def run():
         q, k, v, gate, g, b, _ = sets[calls[0] % 2]
         calls[0] += 1
         kda.layer_prefill(q, k, v, g, b, gate, w, 1e-6, chunk_size=P_C, o=o, final_state=fin,
-                          workspace=ws)
+                          workspace=ws, conv_weight=cw, conv_state=cs, conv_state_out=cs_out)
 
     t = time_calls(torch, run, 20)
     # q, k, v, gate bf16 + g fp32 + beta fp32 + o fp32 per token-head, + final state
     by = T * H * (4 * 2 * d + 4 * d + 4 + 4 * d) + H * d * d * 4 + d * 4
     res = {"prefill_workload": f"kda_prefill_layer B=1 H={H} T={T} d={d} chunk {P_C}, bf16 in / "
-                               "fp32 out, gated RMSNorm epilogue, final state",
+                               "fp32 out, short convolution W=4, gated RMSNorm epilogue, "
+                               "final state",
            "prefill_us_per_call": round(t * 1e6, 2), "prefill_tokens_per_s": round(T / t, 1),
            "prefill_algorithmic_GBps": round(by / t / 1e9, 1)}
     del sets, o, fin, ws
@@ -203,11 +209,13 @@ def layer_workloads(torch, kda, I, dev):
     bd = torch.randn((N, H), device=dev)
     st = torch.randn((N, H, d, d), device=dev) * 0.1
     od = torch.empty((N, H, d), dtype=torch.float32, device=dev)
+    csd = tuple(torch.randn((N, H, W - 1, d), device=dev).to(torch.bfloat16) for _ in range(3))
     t = time_calls(torch, lambda: kda.layer_decode_step(qd, kd, vd, gd, bd, st, gtd, w, 1e-6,
+                                                         conv_weight=cw, conv_state=csd,
                                                          o=od), 20)
     by = N * H * (2 * d * d * 4 + 4 * 2 * d + 4 * d + 4 + 4 * d) + d * 4
     res.update({"decode_workload": f"kda_decode_step_layer N={N} H={H} d={d}, bf16 in / fp32 out, "
-                                   "gated RMSNorm epilogue",
+                                   "short convolution W=4, gated RMSNorm epilogue",
                 "decode_us_per_step": round(t * 1e6, 2), "decode_GBps": round(by / t / 1e9, 1),
                 "decode_hbm_frac": round(by / t / 1e9 / HBM_PEAK_GBS, 4)})
     return res

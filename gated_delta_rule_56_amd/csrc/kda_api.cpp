@@ -40,13 +40,40 @@ kda_status seq_layout(int B, int T, int num_seqs, const int32_t* cu_dev, const i
   return KDA_OK;
 }
 
-// The layer epilogue needs a weight with the gate and a finite eps >= 0.
+// The layer epilogue needs a weight with the gate and a finite eps >= 0; the
+// convolution a width of 1..4 and its three weights.
 kda_status check_layer(const kda::Layer& L) {
+  if (L.conv_w < 0 || L.conv_w > 4) return KDA_ERR_INVALID_ARG;
+  for (int x = 0; x < 3; ++x) {
+    if (L.conv_w > 0 && !L.conv_weight[x]) return KDA_ERR_INVALID_ARG;
+    if (!aligned(L.conv_weight[x], 4) || !aligned(L.conv_state_in[x], 16) ||
+        !aligned(L.conv_state_out[x], 16))
+      return KDA_ERR_INVALID_ARG;
+  }
   if (!L.gate) return KDA_OK;
   if (!L.norm_weight || !aligned(L.gate, 16) || !aligned(L.norm_weight, 16))
     return KDA_ERR_INVALID_ARG;
   if (!(L.norm_eps >= 0.f) || !isfinite(L.norm_eps)) return KDA_ERR_INVALID_ARG;
   return KDA_OK;
+}
+
+// The prologue always runs; epilogue and convolution as the caller asks.
+kda::Layer make_layer(const kda_layer_params* p) {
+  kda::Layer L;
+  L.prologue = true;
+  if (!p) return L;
+  L.gate = p->gate;
+  L.norm_weight = p->gate ? p->norm_weight : nullptr;
+  L.norm_eps = p->norm_eps;
+  L.conv_w = p->conv_width;
+  if (p->conv_width > 0) {
+    for (int x = 0; x < 3; ++x) {
+      L.conv_weight[x] = p->conv_weight[x];
+      L.conv_state_in[x] = p->conv_state_in[x];
+      L.conv_state_out[x] = p->conv_state_out[x];
+    }
+  }
+  return L;
 }
 
 kda_status workspace_size(int B, int T, int H, int Dk, int Dv, int num_seqs,
@@ -90,9 +117,10 @@ kda_status kda_prefill_workspace_size(int B, int T, int H, int Dk, int Dv, int n
 
 kda_status kda_prefill_layer_workspace_size(int B, int T, int H, int Dk, int Dv, int num_seqs,
                                             const int32_t* cu_seqlens_host, int chunk_size,
-                                            kda_dtype in_dtype, int with_gate, size_t* bytes) {
+                                            kda_dtype in_dtype, const kda_layer_params* layer,
+                                            size_t* bytes) {
   return workspace_size(B, T, H, Dk, Dv, num_seqs, cu_seqlens_host, chunk_size, in_dtype,
-                        with_gate != 0, bytes);
+                        layer != nullptr && layer->gate != nullptr, bytes);
 }
 
 static kda_status prefill_impl(bool scalar_g, const kda::Layer& layer, const void* q, const void* k, const void* v,
@@ -213,36 +241,27 @@ kda_status gdn_decode_step(const void* q, const void* k, const void* v, const fl
                      out_dtype, stream);
 }
 
-static kda::Layer make_layer(const void* gate, const float* norm_weight, float norm_eps) {
-  kda::Layer L;
-  L.prologue = true;
-  L.gate = gate;
-  L.norm_weight = gate ? norm_weight : nullptr;
-  L.norm_eps = norm_eps;
-  return L;
-}
-
 kda_status kda_prefill_layer(const void* q_pre, const void* k_pre, const void* v_pre,
-                             const float* g, const float* beta_logit, const void* gate,
-                             const float* norm_weight, float norm_eps, void* o,
-                             const float* initial_state, float* final_state,
-                             const int32_t* cu_seqlens, const int32_t* cu_seqlens_host, int B,
-                             int T, int H, int Dk, int Dv, int num_seqs, int chunk_size,
-                             kda_dtype in_dtype, kda_dtype out_dtype, void* workspace,
-                             size_t workspace_bytes, void* stream) {
-  return prefill_impl(false, make_layer(gate, norm_weight, norm_eps), q_pre, k_pre, v_pre, g,
-                      beta_logit, o, initial_state, final_state, cu_seqlens, cu_seqlens_host, B, T,
-                      H, Dk, Dv, num_seqs, chunk_size, in_dtype, out_dtype, workspace,
-                      workspace_bytes, stream);
+                             const float* g, const float* beta_logit,
+                             const kda_layer_params* layer, void* o, const float* initial_state,
+                             float* final_state, const int32_t* cu_seqlens,
+                             const int32_t* cu_seqlens_host, int B, int T, int H, int Dk, int Dv,
+                             int num_seqs, int chunk_size, kda_dtype in_dtype,
+                             kda_dtype out_dtype, void* workspace, size_t workspace_bytes,
+                             void* stream) {
+  return prefill_impl(false, make_layer(layer), q_pre, k_pre, v_pre, g, beta_logit, o,
+                      initial_state, final_state, cu_seqlens, cu_seqlens_host, B, T, H, Dk, Dv,
+                      num_seqs, chunk_size, in_dtype, out_dtype, workspace, workspace_bytes,
+                      stream);
 }
 
 kda_status kda_decode_step_layer(const void* q_pre, const void* k_pre, const void* v_pre,
-                                 const float* g, const float* beta_logit, const void* gate,
-                                 const float* norm_weight, float norm_eps, float* state, void* o,
-                                 int N, int H, int Dk, int Dv, kda_dtype in_dtype,
-                                 kda_dtype out_dtype, void* stream) {
-  return decode_impl(false, make_layer(gate, norm_weight, norm_eps), q_pre, k_pre, v_pre, g,
-                     beta_logit, state, o, N, H, Dk, Dv, in_dtype, out_dtype, stream);
+                                 const float* g, const float* beta_logit,
+                                 const kda_layer_params* layer, float* state, void* o, int N,
+                                 int H, int Dk, int Dv, kda_dtype in_dtype, kda_dtype out_dtype,
+                                 void* stream) {
+  return decode_impl(false, make_layer(layer), q_pre, k_pre, v_pre, g, beta_logit, state, o, N,
+                     H, Dk, Dv, in_dtype, out_dtype, stream);
 }
 
 }  // extern "C"

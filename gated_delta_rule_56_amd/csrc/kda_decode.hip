@@ -20,11 +20,14 @@
 // shuffles, then across the four waves through LDS.
 //
 // LAYER adds the layer's elementwise work (the "Kimi Linear" notes,
-// docsaid.org, section "Other Components"): Swish and L2 normalisation of q
-// and k, Swish of v and the sigmoid of beta on the way in, and with a gate the
-// head-wise RMSNorm times sigmoid(gate) on the way out.  The norms of q and k
-// are scalars per (n, h), so the reductions run on the un-normalised values
-// and are rescaled once the norms are known.
+// docsaid.org, section "Other Components"): the short causal convolution of
+// q, k and v (weight W-1 on the new token, the others on the carried inputs),
+// Swish and L2 normalisation of q and k, Swish of v and the sigmoid of beta on
+// the way in, and with a gate the head-wise RMSNorm times sigmoid(gate) on the
+// way out.  The norms of q and k are scalars per (n, h), so the reductions run
+// on the un-normalised values and are rescaled once the norms are known.  The
+// carried convolution inputs are read before the block barrier and shifted
+// after it, by one thread per row (q, k) or column (v).
 #include "kda_device.hpp"
 #include "kda_launch.hpp"
 
@@ -35,6 +38,13 @@ struct LayerPtrs {
   const void* gate;  // nullptr: no epilogue
   const float* norm_weight;
   float norm_eps;
+  // short convolution of q, k, v before Swish: width (0 = none), weights
+  // [H][D][conv_w], carried inputs [N][H][conv_w - 1][D] read from cs_in
+  // and shifted into cs_out (either may be nullptr; they may be equal)
+  int conv_w, H;
+  const float* cw[3];
+  const void* cs_in[3];
+  void* cs_out[3];
 };
 
 __device__ __forceinline__ float swish_d(float x) { return x / (1.f + __expf(-x)); }
@@ -74,11 +84,26 @@ __global__ __launch_bounds__(256) void decode_step_kernel(
     s[m] = __builtin_nontemporal_load(reinterpret_cast<const f32x4*>(sp + (size_t)i * DV + 4 * cg));
   }
   float r[4] = {0, 0, 0, 0}, p[4] = {0, 0, 0, 0}, kq = 0.f, nq = 0.f, nk = 0.f;
+  const int W1 = LAYER ? lp.conv_w - 1 : -1;
+  const int hh = LAYER ? nh % lp.H : 0;
+  // convolved input at row / column i of tensor x, new value xn
+  auto conv = [&](int x, int i, float xn) {
+    const float* wr = lp.cw[x] + ((size_t)hh * DK + i) * (W1 + 1);
+    const in_t* st = reinterpret_cast<const in_t*>(lp.cs_in[x]);
+    float acc = wr[W1] * xn;
+    for (int j = 0; j < W1; ++j)
+      acc += wr[j] * (st ? (float)st[((size_t)nh * W1 + j) * DK + i] : 0.f);
+    return acc;
+  };
 #pragma unroll
   for (int m = 0; m < RPT; ++m) {
     const int i = rg + RG * m;
     kk[m] = (float)kp[i];
     qq[m] = (float)qp[i];
+    if (LAYER && W1 >= 0) {
+      kk[m] = conv(1, i, kk[m]);
+      qq[m] = conv(0, i, qq[m]);
+    }
     if (LAYER && lp.prologue) {
       kk[m] = swish_d(kk[m]);
       qq[m] = swish_d(qq[m]);
@@ -111,6 +136,13 @@ __global__ __launch_bounds__(256) void decode_step_kernel(
   }
   constexpr int NRED = LAYER ? 11 : 9;
   __shared__ float red[4][TPR][NRED];
+  const in_t* vp = v + tok * DV + 4 * cg;
+  float vv[4];
+#pragma unroll
+  for (int c = 0; c < 4; ++c) {
+    vv[c] = (float)vp[c];
+    if (LAYER && W1 >= 0) vv[c] = conv(2, 4 * cg + c, vv[c]);
+  }
   const int w = t >> 6;
   if ((t & 63) < TPR) {
 #pragma unroll
@@ -132,11 +164,29 @@ __global__ __launch_bounds__(256) void decode_step_kernel(
   }
   kq = red[0][cg][8] + red[1][cg][8] + red[2][cg][8] + red[3][cg][8];
 
-  float b = beta[tok];
-  const in_t* vp = v + tok * DV + 4 * cg;
-  float vv[4];
+  if (LAYER && W1 > 0) {
+    // Every read of the carried inputs happened before the barrier above.
+    auto shift = [&](int x, int i, const in_t* src) {
+      in_t* out = reinterpret_cast<in_t*>(lp.cs_out[x]);
+      if (!out) return;
+      const in_t* in = reinterpret_cast<const in_t*>(lp.cs_in[x]);
+      const size_t b0 = (size_t)nh * W1 * DK + i;
+      for (int j = 0; j + 1 < W1; ++j) out[b0 + (size_t)j * DK] = in ? in[b0 + (size_t)(j + 1) * DK] : in_t(0.f);
+      out[b0 + (size_t)(W1 - 1) * DK] = src[i];
+    };
+    if (cg == 0) {
 #pragma unroll
-  for (int c = 0; c < 4; ++c) vv[c] = (float)vp[c];
+      for (int m = 0; m < RPT; ++m) {
+        shift(0, rg + RG * m, qp);
+        shift(1, rg + RG * m, kp);
+      }
+    }
+    if (rg == 0) {
+#pragma unroll
+      for (int c = 0; c < 4; ++c) shift(2, 4 * cg + c, v + tok * DV);
+    }
+  }
+  float b = beta[tok];
   if (LAYER && lp.prologue) {
     // L2 normalisation: scale the reductions by 1/|q|, 1/|k| (floored).
     nq = red[0][cg][9] + red[1][cg][9] + red[2][cg][9] + red[3][cg][9];
@@ -197,7 +247,13 @@ template <typename in_t, int D, bool OUT_BF16, bool LAYER>
 static void launch_decode_l(const DecodeArgs& a) {
   const int NH = a.N * a.H;
   dim3 grid(NH), block(256);
-  const LayerPtrs lp{a.layer.prologue ? 1 : 0, a.layer.gate, a.layer.norm_weight, a.layer.norm_eps};
+  LayerPtrs lp{a.layer.prologue ? 1 : 0, a.layer.gate, a.layer.norm_weight, a.layer.norm_eps,
+               a.layer.prologue ? a.layer.conv_w : 0, a.H};
+  for (int x = 0; x < 3; ++x) {
+    lp.cw[x] = a.layer.conv_weight[x];
+    lp.cs_in[x] = a.layer.conv_state_in[x];
+    lp.cs_out[x] = a.layer.conv_state_out[x];
+  }
   if (a.scalar_g)
     hipLaunchKernelGGL((decode_step_kernel<in_t, D, D, OUT_BF16, true, LAYER>), grid, block, 0,
                        a.stream, (const in_t*)a.q, (const in_t*)a.k, (const in_t*)a.v, a.g, a.beta,

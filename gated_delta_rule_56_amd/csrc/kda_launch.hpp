@@ -18,6 +18,14 @@ struct Layer {
   const void* gate = nullptr;
   const float* norm_weight = nullptr;
   float norm_eps = 0.f;
+  // Short causal convolution of q, k, v before Swish (prologue only):
+  // conv_w = 0 for none, else the width (1..4); weights [H][D][conv_w]
+  // float32; carried inputs [num_seqs][H][conv_w - 1][D] in the input dtype
+  // (state_in nullptr: zeros; state_out nullptr: not written).
+  int conv_w = 0;
+  const float* conv_weight[3] = {nullptr, nullptr, nullptr};
+  const void* conv_state_in[3] = {nullptr, nullptr, nullptr};
+  void* conv_state_out[3] = {nullptr, nullptr, nullptr};
 };
 
 struct DecodeArgs {

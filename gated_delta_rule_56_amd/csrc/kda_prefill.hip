@@ -462,6 +462,9 @@ struct KernelPtrs {
   const void* gate;          // layer epilogue: sigmoid gate [tokens, H, D] (in dtype)
   const float* norm_weight;  // layer epilogue: RMSNorm weight [D]
   float norm_eps;
+  const float* cw[3];  // short convolution of q, k, v: weights [H][D][conv_w]
+  const void* cs[3];   // their carried inputs [num_seqs][H][conv_w - 1][D] (in dtype), or nullptr
+  int conv_w;          // convolution width (1..4) when the prologue convolves
   int H;
 };
 
@@ -478,6 +481,7 @@ template <>
 struct Raw8<bf16> {
   bf16x8 v;
   __device__ void load(const bf16* p) { v = *reinterpret_cast<const bf16x8*>(p); }
+  __device__ void zero() { v = bf16x8{}; }
   __device__ float get(int e) const { return bf2f(v[e]); }
 };
 template <>
@@ -487,6 +491,7 @@ struct Raw8<float> {
     a = *reinterpret_cast<const f32x4*>(p);
     b = *reinterpret_cast<const f32x4*>(p + 4);
   }
+  __device__ void zero() { a = b = f32x4{0, 0, 0, 0}; }
   __device__ float get(int e) const { return e < 4 ? a[e] : b[e - 4]; }
 };
 
@@ -500,6 +505,7 @@ __device__ __forceinline__ void lds_st_pfrag(ModeF32 m, char* p, const ModeF32::
 // pairs (varlen: through the segment table).
 struct Item {
   int h, t0, len;
+  int n, bos;  // sequence and its first token
   char* blk;
 };
 
@@ -528,6 +534,8 @@ __device__ __forceinline__ Item intra_item(const SeqInfo& si, const KernelPtrs& 
   }
   int bos, eos;
   seq_bounds(si, n, bos, eos);
+  x.n = n;
+  x.bos = bos;
   // A device table that disagrees with the host one can only shorten chunks,
   // never move them outside [bos, eos].
   const long long t0l = (long long)bos + (long long)(ci < 0 ? 0 : ci) * C;
@@ -535,6 +543,56 @@ __device__ __forceinline__ Item intra_item(const SeqInfo& si, const KernelPtrs& 
   x.len = clampi(eos - x.t0, 0, C);
   x.blk = kp.ops + ((size_t)slot * H + x.h) * block_bytes;
   return x;
+}
+
+// ---------------------------------------------------------------------------
+// Short convolution of the layer prologue (the "Kimi Linear" notes,
+// docsaid.org, section "Other Components": q, k and v pass through a short
+// convolution before Swish).  Causal and depthwise: for token t of a sequence
+// starting at bos, y_c = sum_{i<W} w[c][i] x_c(t - (W-1) + i), where inputs
+// before bos come from the carried state (row (W-1) + (s - bos)), or are zero.
+// ---------------------------------------------------------------------------
+constexpr int kMaxConv = 4;
+
+// The inputs one lane needs besides its own token row r = 16 rt + lr: lanes
+// lr >= 16 - (kMaxConv - 1) load the rows 16 rt - 3 .. 16 rt - 1 of the chunk
+// (earlier tokens of the sequence, or state rows before its start).
+template <class T, int D>
+__device__ __forceinline__ void load_halo(Raw8<T>& ext, const KernelPtrs& kp, int x, const Item& it,
+                                          int rt, int lr, int c0, int total_tokens) {
+  ext.zero();
+  if (lr < 16 - (kMaxConv - 1)) return;
+  const int W = kp.conv_w, H = kp.H;
+  const int te = it.t0 + 16 * rt + lr - 16;
+  const T* src = x == 0 ? (const T*)kp.q : x == 1 ? (const T*)kp.k : (const T*)kp.v;
+  if (te >= it.bos) {
+    ext.load(src + ((size_t)clampi(te, 0, total_tokens - 1) * H + it.h) * D + c0);
+  } else {
+    const int j = (W - 1) + (te - it.bos);
+    if (j >= 0 && kp.cs[x])
+      ext.load(reinterpret_cast<const T*>(kp.cs[x]) + (((size_t)it.n * H + it.h) * (W - 1) + j) * D + c0);
+  }
+}
+
+// Convolved values of one lane's 8 channels (c0 .. c0 + 7) of row 16 rt + lr,
+// from the lane's own row and the halo rows of lanes 13..15 of its 16-lane
+// group (shuffles stay inside the group).
+template <class T>
+__device__ __forceinline__ void conv8(const Raw8<T>& own, const Raw8<T>& ext, const float* wrow,
+                                      int W, int lr, float out[8]) {
+#pragma unroll
+  for (int e = 0; e < 8; ++e) {
+    const float xo = own.get(e), xe = ext.get(e);
+    float acc = wrow[e * W + W - 1] * xo;
+#pragma unroll
+    for (int i = 1; i < kMaxConv; ++i) {
+      const int src = lr - i;
+      const float a = __shfl(xo, src < 0 ? 0 : src, 16);
+      const float b = __shfl(xe, src < 0 ? src + 16 : 0, 16);
+      if (i < W) acc += wrow[e * W + W - 1 - i] * (src >= 0 ? a : b);
+    }
+    out[e] = acc;
+  }
 }
 
 // ---------------------------------------------------------------------------
@@ -551,9 +609,10 @@ __device__ __forceinline__ Item intra_item(const SeqInfo& si, const KernelPtrs& 
 // SDEC: scalar decay (Gated DeltaNet), one log-decay per token and head, g
 // [tokens, H]; otherwise one per key channel, g [tokens, H, D].
 // SDEC: scalar decay (one g per token and head).  PRO: the layer prologue
-// (Swish + L2 norm of q and k, Swish of v, sigmoid of beta) is applied to the
-// inputs as they are read.
-template <class M, int D, int C, bool SDEC, bool PRO>
+// is applied to the inputs as they are read: 1 = Swish + L2 norm of q and k,
+// Swish of v, sigmoid of beta; 2 = the same after the short convolution of
+// q, k and v.
+template <class M, int D, int C, bool SDEC, int PRO>
 __global__ __launch_bounds__(kIntraThreads, 4) void intra_chunk_kernel(KernelPtrs kp, SeqInfo si) {
   typedef typename M::in_t in_t;
   typedef typename M::PFrag PFrag;
@@ -613,6 +672,23 @@ __global__ __launch_bounds__(kIntraThreads, 4) void intra_chunk_kernel(KernelPtr
     const float bv = kp.beta[(size_t)tb * H + h];
     beta_s[tid] = tid < len ? (PRO ? sigmoidf(bv) : bv) : 0.f;
   }
+  // Layer prologue inputs before Swish: the raw q, k, or their short
+  // convolution (PRO == 2), computed once here.
+  float qc[PRO == 2 ? FPW : 1][8], kc[PRO == 2 ? FPW : 1][8];
+  if constexpr (PRO == 2) {
+#pragma unroll
+    for (int j = 0; j < FPW; ++j) {
+      const int c0 = 32 * fkb[j] + 8 * lg;
+      Raw8<in_t> qe, ke;
+      load_halo<in_t, D>(qe, kp, 0, it, rt, lr, c0, si.total_tokens);
+      load_halo<in_t, D>(ke, kp, 1, it, rt, lr, c0, si.total_tokens);
+      const int W = kp.conv_w;
+      conv8(qraw[j], qe, kp.cw[0] + ((size_t)h * D + c0) * W, W, lr, qc[j]);
+      conv8(kraw[j], ke, kp.cw[1] + ((size_t)h * D + c0) * W, W, lr, kc[j]);
+    }
+  }
+  auto qin = [&](int j, int e) { if constexpr (PRO == 2) return qc[j][e]; else return qraw[j].get(e); };
+  auto kin = [&](int j, int e) { if constexpr (PRO == 2) return kc[j][e]; else return kraw[j].get(e); };
 
   // ---- step 2: cumulative decay.  Inclusive scan over the 16 tokens of the
   // tile (lanes lr of one lane group), then the totals of earlier tiles ----
@@ -663,7 +739,7 @@ __global__ __launch_bounds__(kIntraThreads, 4) void intra_chunk_kernel(KernelPtr
       if (fv[j]) {
 #pragma unroll
         for (int e = 0; e < 8; ++e) {
-          const float a = swishf(qraw[j].get(e)), b = swishf(kraw[j].get(e));
+          const float a = swishf(qin(j, e)), b = swishf(kin(j, e));
           sq += a * a;
           sk += b * b;
         }
@@ -735,8 +811,8 @@ __global__ __launch_bounds__(kIntraThreads, 4) void intra_chunk_kernel(KernelPtr
     float qt[8], kt[8], kh[8];
 #pragma unroll
     for (int e = 0; e < 8; ++e) {
-      const float kv = rv ? (PRO ? swishf(kraw[j].get(e)) * ik : kraw[j].get(e)) : 0.f;
-      const float qv = rv ? (PRO ? swishf(qraw[j].get(e)) * iq : qraw[j].get(e)) : 0.f;
+      const float kv = rv ? (PRO ? swishf(kin(j, e)) * ik : kraw[j].get(e)) : 0.f;
+      const float qv = rv ? (PRO ? swishf(qin(j, e)) * iq : qraw[j].get(e)) : 0.f;
       const float gm = __expf(G[j][e]);
       qt[e] = qv * gm;
       kt[e] = kv * gm;
@@ -823,18 +899,37 @@ __global__ __launch_bounds__(kIntraThreads, 4) void intra_chunk_kernel(KernelPtr
     const in_t* qg = reinterpret_cast<const in_t*>(kp.q);
     const in_t* kg = reinterpret_cast<const in_t*>(kp.k);
     const float* rn = reinterpret_cast<const float*>(smem + L::oRn);
-    auto in = [&](const in_t* p, int t, int c, float f) {
-      const float x = (float)p[((size_t)(t0 + t) * H + h) * D + c];
-      return PRO ? swishf(x) * f : x;
+    // token t of the chunk, channel c of q (x = 0) or k (x = 1), after the
+    // prologue scaled by the token's norm factor f
+    auto in = [&](const in_t* p, int x, int t, int c, float f) {
+      float y = 0.f;
+      if constexpr (PRO == 2) {
+        const int W = kp.conv_w;
+        const float* wr = kp.cw[x] + ((size_t)h * D + c) * W;
+        for (int i = 0; i < W; ++i) {
+          const int s = t0 + t - (W - 1) + i;
+          float xv = 0.f;
+          if (s >= it.bos) {
+            xv = (float)p[((size_t)s * H + h) * D + c];
+          } else if (kp.cs[x] && (W - 1) + (s - it.bos) >= 0) {
+            xv = (float)reinterpret_cast<const in_t*>(kp.cs[x])
+                     [(((size_t)it.n * H + h) * (W - 1) + (W - 1) + (s - it.bos)) * D + c];
+          }
+          y += wr[i] * xv;
+        }
+      } else {
+        y = (float)p[((size_t)(t0 + t) * H + h) * D + c];
+      }
+      return PRO ? swishf(y) * f : y;
     };
     const int rr = tid >> 3;
     if (rr < len) {
       for (int i = tid & 7; i <= rr; i += 8) {
         float sa = 0.f, sp = 0.f;
         for (int c = 0; c < D; ++c) {
-          const float kr = in(kg, rr, c, rn[rr * 2 + 1]);
-          const float ki = in(kg, i, c, rn[i * 2 + 1]);
-          const float qr = in(qg, rr, c, rn[rr * 2]);
+          const float kr = in(kg, 1, rr, c, rn[rr * 2 + 1]);
+          const float ki = in(kg, 1, i, c, rn[i * 2 + 1]);
+          const float qr = in(qg, 0, rr, c, rn[rr * 2]);
           const float ex = __expf(Gs[rr * SG + c] - Gs[i * SG + c]);
           sa += kr * ki * ex;
           sp += qr * ki * ex;
@@ -944,10 +1039,12 @@ __global__ __launch_bounds__(kIntraThreads, 4) void intra_chunk_kernel(KernelPtr
   // ---- step 6: T = X Diag(beta) (lower triangle) kept in LDS as
   // fragments (over the solve scratch) for the W and U0 products; (K*gam)^T
   // staged.  V is fetched here for step 8 ----
-  Raw8<in_t> vraw[FPW];
+  Raw8<in_t> vraw[FPW], vext[PRO == 2 ? FPW : 1];
 #pragma unroll
-  for (int j = 0; j < FPW; ++j)
+  for (int j = 0; j < FPW; ++j) {
     vraw[j].load(reinterpret_cast<const in_t*>(kp.v) + ((size_t)tok * H + h) * D + 32 * fkb[j] + 8 * lg);
+    if constexpr (PRO == 2) load_halo<in_t, D>(vext[j], kp, 2, it, rt, lr, 32 * fkb[j] + 8 * lg, si.total_tokens);
+  }
   for (int f = w; f < NRT * NKC; f += NW) {
     const int rr = 16 * (f / NKC) + lr, i0 = 32 * (f % NKC) + 8 * lg;
     float tv[8];
@@ -1006,11 +1103,17 @@ __global__ __launch_bounds__(kIntraThreads, 4) void intra_chunk_kernel(KernelPtr
 #pragma unroll
   for (int j = 0; j < FPW; ++j)
     if (fv[j]) {
+      float vx[8];
+      if constexpr (PRO == 2) {
+        const int W = kp.conv_w, c0 = 32 * fkb[j] + 8 * lg;
+        conv8(vraw[j], vext[j], kp.cw[2] + ((size_t)h * D + c0) * W, W, lr, vx);
+      } else {
 #pragma unroll
-      for (int e = 0; e < 8; ++e) {
-        const float x = vraw[j].get(e);
-        VT.store((32 * fkb[j] + 8 * lg + e) * SK + r, rv ? (PRO ? swishf(x) : x) : 0.f);
+        for (int e = 0; e < 8; ++e) vx[e] = vraw[j].get(e);
       }
+#pragma unroll
+      for (int e = 0; e < 8; ++e)
+        VT.store((32 * fkb[j] + 8 * lg + e) * SK + r, rv ? (PRO ? swishf(vx[e]) : vx[e]) : 0.f);
     }
   if (KC > C) {
     for (int idx = tid; idx < D * (KC - C); idx += kIntraThreads) {
@@ -1458,6 +1561,41 @@ __global__ __launch_bounds__(kInterThreads, 2) void inter_chunk_kernel(KernelPtr
     inter_o_role<M, D, C, NCT, OUT_BF16>(kp, gm, smem, w - 4);
 }
 
+// The carried inputs of the short convolution after the call: the last W-1
+// inputs of each sequence (of its state rows where it is shorter).  One
+// workgroup per (sequence, head) and tensor, one thread per channel; each
+// thread reads state row len + j before it writes row j, so the output may
+// overwrite the input state in place.
+struct ConvStateArgs {
+  const void* x[3];
+  const void* in[3];
+  void* out[3];
+  int W, H;
+};
+
+template <class T, int D>
+__global__ __launch_bounds__(D) void conv_state_kernel(ConvStateArgs ca, SeqInfo si) {
+  const int x = blockIdx.y;
+  if (!ca.out[x]) return;
+  const int n = blockIdx.x / ca.H, h = blockIdx.x % ca.H, c = threadIdx.x;
+  int bos, eos;
+  seq_bounds(si, n, bos, eos);
+  const int W1 = ca.W - 1, len = eos - bos;
+  const T* src = reinterpret_cast<const T*>(ca.x[x]);
+  const T* in = reinterpret_cast<const T*>(ca.in[x]);
+  T* out = reinterpret_cast<T*>(ca.out[x]);
+  const size_t sb = ((size_t)n * ca.H + h) * W1 * D + c;
+  for (int j = 0; j < W1; ++j) {
+    const int te = eos - W1 + j;
+    T v;
+    if (te >= bos)
+      v = src[((size_t)te * ca.H + h) * D + c];
+    else
+      v = in ? in[sb + (size_t)(len + j) * D] : T(0.f);
+    out[sb + (size_t)j * D] = v;
+  }
+}
+
 // Value-column block width of the inter-chunk pass: wide blocks cut the
 // per-chunk operand traffic (each block re-reads the chunk's operands),
 // narrow ones give more workgroups.  32 columns once there are enough
@@ -1526,15 +1664,22 @@ static hipError_t launch_prefill_t(const PrefillArgs& a) {
   kp.gate = a.layer.gate;
   kp.norm_weight = a.layer.norm_weight;
   kp.norm_eps = a.layer.norm_eps;
+  kp.conv_w = a.layer.conv_w;
+  for (int x = 0; x < 3; ++x) {
+    kp.cw[x] = a.layer.conv_weight[x];
+    kp.cs[x] = a.layer.conv_state_in[x];
+  }
 
   constexpr size_t lds = IntraLds<M, D, C>::kTotal;
   static_assert(lds <= 160 * 1024, "intra-chunk LDS");
   // The prologue is built for the per-channel decay only.
-  constexpr bool kPro = !SDEC;
+  constexpr int P1 = SDEC ? 0 : 1, P2 = SDEC ? 0 : 2;
   if (SDEC && a.layer.prologue) return hipErrorInvalidValue;
-  const bool pro = kPro && a.layer.prologue;
-  const void* intra_fn = pro ? reinterpret_cast<const void*>(&intra_chunk_kernel<M, D, C, SDEC, kPro>)
-                             : reinterpret_cast<const void*>(&intra_chunk_kernel<M, D, C, SDEC, false>);
+  const int pro = !a.layer.prologue ? 0 : a.layer.conv_w > 0 ? 2 : 1;
+  const void* intra_fn =
+      pro == 2   ? reinterpret_cast<const void*>(&intra_chunk_kernel<M, D, C, SDEC, P2>)
+      : pro == 1 ? reinterpret_cast<const void*>(&intra_chunk_kernel<M, D, C, SDEC, P1>)
+                 : reinterpret_cast<const void*>(&intra_chunk_kernel<M, D, C, SDEC, 0>);
   if (plan.max_slots > 0) {
     hipError_t e = hipFuncSetAttribute(intra_fn, hipFuncAttributeMaxDynamicSharedMemorySize, (int)lds);
     if (e != hipSuccess) return e;
@@ -1552,12 +1697,16 @@ static hipError_t launch_prefill_t(const PrefillArgs& a) {
       const int c = sc.nch(0) - si.c0;
       si.slot_cnt = c <= 0 ? 0 : (c < plan.L ? c : plan.L);
     }
-    if (slots > 0 && pro)
-      hipLaunchKernelGGL((intra_chunk_kernel<M, D, C, SDEC, kPro>), dim3((unsigned)slots, a.H),
-                         dim3(kIntraThreads), lds, a.stream, kp, si);
+    const dim3 igrid((unsigned)slots, a.H);
+    if (slots > 0 && pro == 2)
+      hipLaunchKernelGGL((intra_chunk_kernel<M, D, C, SDEC, P2>), igrid, dim3(kIntraThreads), lds,
+                         a.stream, kp, si);
+    else if (slots > 0 && pro == 1)
+      hipLaunchKernelGGL((intra_chunk_kernel<M, D, C, SDEC, P1>), igrid, dim3(kIntraThreads), lds,
+                         a.stream, kp, si);
     else if (slots > 0)
-      hipLaunchKernelGGL((intra_chunk_kernel<M, D, C, SDEC, false>), dim3((unsigned)slots, a.H),
-                         dim3(kIntraThreads), lds, a.stream, kp, si);
+      hipLaunchKernelGGL((intra_chunk_kernel<M, D, C, SDEC, 0>), igrid, dim3(kIntraThreads), lds,
+                         a.stream, kp, si);
     if (nct == 2)
       launch_inter<M, D, C, 2>(a, kp, si);
     else
@@ -1570,6 +1719,22 @@ static hipError_t launch_prefill_t(const PrefillArgs& a) {
         hipLaunchKernelGGL((layer_epilogue_kernel<M, D, C, false>), grid, dim3(256), 0, a.stream, kp,
                            si);
     }
+  }
+  // The carried convolution inputs, after every pass that reads the old ones
+  // (they may share memory).
+  const bool conv_out = a.layer.conv_state_out[0] || a.layer.conv_state_out[1] ||
+                        a.layer.conv_state_out[2];
+  if (pro == 2 && a.layer.conv_w > 1 && conv_out && a.num_seqs > 0) {
+    ConvStateArgs ca;
+    ca.W = a.layer.conv_w;
+    ca.H = a.H;
+    for (int x = 0; x < 3; ++x) {
+      ca.x[x] = x == 0 ? a.q : x == 1 ? a.k : a.v;
+      ca.in[x] = a.layer.conv_state_in[x];
+      ca.out[x] = a.layer.conv_state_out[x];
+    }
+    hipLaunchKernelGGL((conv_state_kernel<typename M::in_t, D>), dim3(a.num_seqs * a.H, 3), dim3(D),
+                       0, a.stream, ca, si);
   }
   return hipGetLastError();
 }

@@ -326,3 +326,15 @@ def device_layer_tokens(torch, T: int, H: int, Dk: int, Dv: int, seed: int, devi
     g = -torch.nn.functional.softplus(rn(1, T, H, Dk)) * 0.1
     w = 1.0 + 0.1 * rn(Dv)
     return q, k, v, gate, g, beta, w
+
+
+def draw_conv(rng: np.random.Generator, N: int, H: int, D: int, W: int,
+              dtype: str = "bf16"):
+    """Short-convolution weights and carried inputs for the fused layer:
+    three weights ``[H, D, W]`` ~ N(0, 1/W) float32 (q, k, v) and three
+    states ``[N, H, W-1, D]`` ~ N(0, 1) (bf16-exact for ``"bf16"``)."""
+    rnd = bf16_round if dtype == "bf16" else (lambda a: a.astype(np.float32))
+    ws = tuple((rng.standard_normal((H, D, W)) / np.sqrt(W)).astype(np.float32)
+               for _ in range(3))
+    ss = tuple(rnd(rng.standard_normal((N, H, W - 1, D))) for _ in range(3))
+    return ws, ss

@@ -193,12 +193,19 @@ kda_status gdn_decode_step(const void* q, const void* k, const void* v,
  * summary, section 4 "Model Architecture").  The inputs are the projections
  * before their activations:
  *
- *   q = L2norm(Swish(q_pre)),  k = L2norm(Swish(k_pre))   per (token, head)
- *   v = Swish(v_pre),          beta = sigmoid(beta_logit)
+ *   q = L2norm(Swish(conv_q(q_pre))),  k = L2norm(Swish(conv_k(k_pre)))
+ *   v = Swish(conv_v(v_pre)),          beta = sigmoid(beta_logit)
  *
- * with Swish(x) = x * sigmoid(x) and L2norm(x) = x / max(|x|_2, 1e-12).  The
- * recurrence then runs as in kda_prefill / kda_decode_step.  When gate is not
- * NULL the output is
+ * per (token, head), with Swish(x) = x * sigmoid(x) and L2norm(x) =
+ * x / max(|x|_2, 1e-12).  conv_x is the short convolution: causal and
+ * depthwise over the tokens of each sequence, of width W (1..4), no bias:
+ *
+ *   conv(x)[t, h, c] = sum_{i<W} weight[h, c, i] * x[t - (W-1) + i, h, c]
+ *
+ * where inputs before the sequence's first token come from the carried
+ * state (row (W-1) + (s - first token); zeros when the state is NULL).  With
+ * conv_width = 0 the convolution is skipped.  The recurrence then runs as in
+ * kda_prefill / kda_decode_step.  When gate is not NULL the output is
  *
  *   y[t, h, c] = o[t, h, c] / sqrt(mean_c' o[t, h, c']^2 + norm_eps)
  *                * norm_weight[c] * sigmoid(gate[t, h, c])
@@ -206,29 +213,48 @@ kda_status gdn_decode_step(const void* q, const void* k, const void* v,
  * (head-wise RMSNorm with a per-channel weight shared by the heads, times the
  * output gate); when gate is NULL, o itself is written and norm_weight and
  * norm_eps are ignored.  The final states are those of the recurrence.
- *
- * Arguments are those of kda_prefill / kda_decode_step, plus:
- *   q_pre, k_pre, v_pre  as q, k, v (in_dtype)
- *   beta_logit  [tokens, H] float32 (sigmoid applied inside)
- *   gate        [tokens, H, Dv] in_dtype, or NULL
- *   norm_weight [Dv] float32 (required with gate)
- *   norm_eps    finite, >= 0
- * kda_prefill_layer's workspace must be at least
- * kda_prefill_layer_workspace_size(..., with_gate = gate != NULL) bytes: with
- * the gate it also holds one segment's raw fp32 output (chunk * Dv * 4 bytes
- * per chunk and head), because the norm spans value columns that the
+ */
+typedef struct {
+  const void* gate;           /* [tokens, H, Dv] in_dtype, or NULL: no epilogue */
+  const float* norm_weight;   /* [Dv] float32; required with gate */
+  float norm_eps;             /* finite, >= 0 */
+  int conv_width;             /* 0: no short convolution; else 1..4 */
+  const float* conv_weight[3]; /* q, k, v: [H, D, conv_width] float32 (with conv) */
+  /* Carried convolution inputs of q, k, v: [num_seqs (or N), H, conv_width-1,
+   * D] in_dtype, row conv_width-2 the most recent.  conv_state_in NULL: zeros.
+   * conv_state_out receives the last conv_width-1 inputs of each sequence
+   * after the call (NULL: not written); it may alias conv_state_in. */
+  const void* conv_state_in[3];
+  void* conv_state_out[3];
+} kda_layer_params;
+
+/*
+ * Workspace bytes of kda_prefill_layer (layer may be NULL: no epilogue).  With
+ * a gate the workspace also holds one segment's raw fp32 output (chunk * Dv *
+ * 4 bytes per chunk and head), because the norm spans value columns that the
  * inter-chunk pass computes in separate workgroups.
  */
 kda_status kda_prefill_layer_workspace_size(int B, int T, int H, int Dk, int Dv,
                                             int num_seqs,
                                             const int32_t* cu_seqlens_host,
                                             int chunk_size, kda_dtype in_dtype,
-                                            int with_gate, size_t* bytes);
+                                            const kda_layer_params* layer,
+                                            size_t* bytes);
 
+/*
+ * Arguments are those of kda_prefill / kda_decode_step, plus:
+ *   q_pre, k_pre, v_pre  as q, k, v (in_dtype)
+ *   beta_logit  [tokens, H] float32 (sigmoid applied inside)
+ *   layer       gate, RMSNorm weight and eps, short convolution; NULL means
+ *               no convolution and no epilogue (the prologue still runs)
+ * For kda_decode_step_layer the convolution states are [N, H, conv_width-1,
+ * D]: one step reads conv_state_in and writes the shifted inputs (the new
+ * token last) to conv_state_out, which is normally the same buffer.
+ */
 kda_status kda_prefill_layer(const void* q_pre, const void* k_pre,
                              const void* v_pre, const float* g,
-                             const float* beta_logit, const void* gate,
-                             const float* norm_weight, float norm_eps, void* o,
+                             const float* beta_logit,
+                             const kda_layer_params* layer, void* o,
                              const float* initial_state, float* final_state,
                              const int32_t* cu_seqlens,
                              const int32_t* cu_seqlens_host, int B, int T,
@@ -240,11 +266,10 @@ kda_status kda_prefill_layer(const void* q_pre, const void* k_pre,
 
 kda_status kda_decode_step_layer(const void* q_pre, const void* k_pre,
                                  const void* v_pre, const float* g,
-                                 const float* beta_logit, const void* gate,
-                                 const float* norm_weight, float norm_eps,
-                                 float* state, void* o, int N, int H, int Dk,
-                                 int Dv, kda_dtype in_dtype,
-                                 kda_dtype out_dtype,
+                                 const float* beta_logit,
+                                 const kda_layer_params* layer, float* state,
+                                 void* o, int N, int H, int Dk, int Dv,
+                                 kda_dtype in_dtype, kda_dtype out_dtype,
                                  void* stream /* hipStream_t */);
 
 #ifdef __cplusplus

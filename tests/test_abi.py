@@ -150,32 +150,48 @@ def test_layer_workspace_size(lib):
     assert gated == plain + 32 * 32 * 64 * 128 * 4
 
 
-def _layer_prefill(lib, **kw):
-    a = dict(q=FAKE, k=FAKE, v=FAKE, g=FAKE, beta=FAKE, gate=FAKE, w=FAKE, eps=1e-6, o=FAKE,
+def _params(gate=FAKE, w=FAKE, eps=1e-6, cw=0, cwt=(FAKE, FAKE, FAKE), csin=(None,) * 3,
+            csout=(None,) * 3):
+    lp = kda.LayerParams()
+    lp.gate, lp.norm_weight, lp.norm_eps, lp.conv_width = gate, w, eps, cw
+    for x in range(3):
+        lp.conv_weight[x], lp.conv_state_in[x], lp.conv_state_out[x] = cwt[x], csin[x], csout[x]
+    return lp
+
+
+def _layer_prefill(lib, layer=None, **kw):
+    a = dict(q=FAKE, k=FAKE, v=FAKE, g=FAKE, beta=FAKE, o=FAKE,
              s0=None, s1=None, cu=None, cu_host=None, B=1, T=128, H=2, Dk=128, Dv=128, N=1,
              C=64, ind=0, outd=1, ws=FAKE, wsb=1 << 40, stream=None)
     a.update(kw)
-    return lib.kda_prefill_layer(a["q"], a["k"], a["v"], a["g"], a["beta"], a["gate"], a["w"],
-                                 a["eps"], a["o"], a["s0"], a["s1"], a["cu"], a["cu_host"],
+    lp = _params() if layer is None else layer
+    return lib.kda_prefill_layer(a["q"], a["k"], a["v"], a["g"], a["beta"], ctypes.byref(lp),
+                                 a["o"], a["s0"], a["s1"], a["cu"], a["cu_host"],
                                  a["B"], a["T"], a["H"], a["Dk"], a["Dv"], a["N"], a["C"],
                                  a["ind"], a["outd"], a["ws"], a["wsb"], a["stream"])
 
 
 def test_layer_validation(lib):
     # Every call fails validation; the first check that fails decides.
-    assert _layer_prefill(lib, w=None, ws=None) == INVALID       # gate without weight
-    assert _layer_prefill(lib, eps=-1.0, ws=None) == INVALID
-    assert _layer_prefill(lib, eps=float("inf"), ws=None) == INVALID
-    assert _layer_prefill(lib, eps=float("nan"), ws=None) == INVALID
-    assert _layer_prefill(lib, gate=FAKE + 2, ws=None) == INVALID  # misaligned gate
-    assert _layer_prefill(lib, ws=None) == WORKSPACE
-    assert _layer_prefill(lib, gate=None, w=None, ws=None) == WORKSPACE
-    assert _layer_prefill(lib, Dk=96, Dv=96) == UNSUPPORTED
-    d = lambda **kw: lib.kda_decode_step_layer(
-        *[kw.get(n, FAKE) for n in ("q", "k", "v", "g", "beta", "gate", "w")], kw.get("eps", 1e-6),
+    assert _layer_prefill(lib, _params(w=None), ws=None) == INVALID      # gate without weight
+    assert _layer_prefill(lib, _params(eps=-1.0), ws=None) == INVALID
+    assert _layer_prefill(lib, _params(eps=float("inf")), ws=None) == INVALID
+    assert _layer_prefill(lib, _params(eps=float("nan")), ws=None) == INVALID
+    assert _layer_prefill(lib, _params(gate=FAKE + 2), ws=None) == INVALID  # misaligned gate
+    assert _layer_prefill(lib, _params(cw=5), ws=None) == INVALID         # width beyond 4
+    assert _layer_prefill(lib, _params(cw=-1), ws=None) == INVALID
+    assert _layer_prefill(lib, _params(cw=4, cwt=(FAKE, None, FAKE)), ws=None) == INVALID
+    assert _layer_prefill(lib, _params(cw=4, csin=(FAKE + 8, None, None)), ws=None) == INVALID
+    assert _layer_prefill(lib, _params(), ws=None) == WORKSPACE
+    assert _layer_prefill(lib, _params(cw=4), ws=None) == WORKSPACE
+    assert _layer_prefill(lib, _params(gate=None, w=None), ws=None) == WORKSPACE
+    assert _layer_prefill(lib, _params(), Dk=96, Dv=96) == UNSUPPORTED
+    d = lambda lp, **kw: lib.kda_decode_step_layer(
+        *[kw.get(n, FAKE) for n in ("q", "k", "v", "g", "beta")], ctypes.byref(lp),
         kw.get("state", FAKE), kw.get("o", FAKE), kw.get("N", 4), kw.get("H", 2),
         kw.get("Dk", 64), kw.get("Dv", 64), kw.get("ind", 1), kw.get("outd", 1), None)
-    assert d(w=None) == INVALID
-    assert d(eps=-0.5) == INVALID
-    assert d(state=None) == INVALID
-    assert d(Dk=32, Dv=32) == UNSUPPORTED
+    assert d(_params(w=None)) == INVALID
+    assert d(_params(eps=-0.5)) == INVALID
+    assert d(_params(cw=7)) == INVALID
+    assert d(_params(), state=None) == INVALID
+    assert d(_params(), Dk=32, Dv=32) == UNSUPPORTED

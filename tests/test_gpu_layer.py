@@ -198,3 +198,153 @@ def test_layer_decode_continues_layer_prefill(kda):
     es = rel(host(st), ef)
     say(f"  o err {worst:.2e}  state err {es:.2e}")
     assert worst <= TOL["bf16"] and es <= TOL["bf16"]
+
+
+# --------------------------------------------------------------------------
+# short convolution (causal, depthwise, carried inputs) in the prologue
+# --------------------------------------------------------------------------
+
+def conv_to_dev(ws, ss, dt):
+    return (tuple(tdev(w, torch.float32) for w in ws),
+            None if ss is None else tuple(tdev(s, dt) for s in ss))
+
+
+@pytest.mark.parametrize("dtype,D,C,T,W,with_state", [
+    ("bf16", 128, 64, 300, 4, True), ("f32", 64, 16, 131, 2, False),
+    ("bf16", 64, 32, 70, 3, True), ("f32", 128, 64, 77, 1, False),
+    ("bf16", 128, 64, 2, 4, True)])
+def test_layer_prefill_conv_matches_oracle(kda, dtype, D, C, T, W, with_state):
+    say(f"layer prefill conv dtype={dtype} D={D} C={C} T={T} W={W} state={with_state}")
+    rng = np.random.default_rng([37, D, C, T, W])
+    H = 3
+    x = I.draw_layer_tokens(rng, T, H, D, D, dtype)
+    s0 = I.draw_states(rng, 1, H, D, D)
+    ws, ss = I.draw_conv(rng, 1, H, D, W, dtype)
+    ss = ss if with_state else None
+    eo, ef, ecs = oracle.kda_layer_conv(x.q_pre, x.k_pre, x.v_pre, x.g, x.beta_logit, ws, ss,
+                                        x.gate, x.norm_weight, EPS, s0)
+    dt = torch.bfloat16 if dtype == "bf16" else torch.float32
+    q, k, v, g, b, gt = layer_to_dev(x)
+    wd, sd = conv_to_dev(ws, ss, dt)
+    o, fin, cs = kda.layer_prefill(q, k, v, g, b, gt, tdev(x.norm_weight, torch.float32), EPS,
+                                   torch.from_numpy(s0).to(DEV), conv_weight=wd, conv_state=sd,
+                                   chunk_size=C)
+    torch.cuda.synchronize()
+    eo_, es_ = rel(host(o)[0], eo), rel(host(fin), ef)
+    say(f"  o err {eo_:.2e}  state err {es_:.2e}")
+    assert eo_ <= TOL[dtype] and es_ <= TOL[dtype]
+    for a, e in zip(cs, ecs):  # carried inputs are copies: bit-exact
+        np.testing.assert_array_equal(host(a), e.astype(np.float32))
+
+
+@pytest.mark.parametrize("seg", [None, 1])
+def test_layer_prefill_conv_varlen_in_place(kda, monkeypatch, seg):
+    """Packed sequences, some shorter than the convolution's reach (0, 1 and
+    2 tokens), carried inputs and recurrent state updated in place, in one
+    pass or in one-chunk segments."""
+    if seg is not None:
+        monkeypatch.setenv("KDA_PREFILL_SEGMENT_CHUNKS", str(seg))
+    say(f"layer prefill conv varlen in place segments={seg}")
+    lens = [37, 0, 130, 1, 200, 2, 64]
+    cu = np.concatenate([[0], np.cumsum(lens)]).astype(np.int32)
+    N, H, D, W = len(lens), 2, 128, 4
+    rng = np.random.default_rng([38, 0 if seg is None else seg])
+    x = I.draw_layer_tokens(rng, int(cu[-1]), H, D, D, "bf16")
+    s0 = I.draw_states(rng, N, H, D, D)
+    ws, ss = I.draw_conv(rng, N, H, D, W, "bf16")
+    eo, ef, ecs = oracle.kda_layer_conv(x.q_pre, x.k_pre, x.v_pre, x.g, x.beta_logit, ws, ss,
+                                        x.gate, x.norm_weight, EPS, s0, cu)
+    q, k, v, g, b, gt = layer_to_dev(x)
+    wd, sd = conv_to_dev(ws, ss, torch.bfloat16)
+    st = torch.from_numpy(s0.copy()).to(DEV)
+    cud = torch.from_numpy(cu).to(DEV)
+    o, _, cs = kda.layer_prefill(q, k, v, g, b, gt, tdev(x.norm_weight, torch.float32), EPS, st,
+                                 cud, conv_weight=wd, conv_state=sd, conv_state_out=sd,
+                                 cu_seqlens_host=cu, chunk_size=64, final_state=st)
+    torch.cuda.synchronize()
+    eo_, es_ = rel(host(o)[0], eo), rel(host(st), ef)
+    say(f"  o err {eo_:.2e}  state err {es_:.2e}")
+    assert eo_ <= TOL["bf16"] and es_ <= TOL["bf16"]
+    for a, e in zip(sd, ecs):
+        np.testing.assert_array_equal(host(a), e.astype(np.float32))
+
+
+def test_layer_prefill_conv_strong_decay(kda):
+    """The pairwise Gram path convolves q and k itself."""
+    say("layer prefill conv strong decay")
+    rng = np.random.default_rng(39)
+    T, H, D, W = 150, 2, 128, 4
+    x = I.draw_layer_tokens(rng, T, H, D, D, "f32", g_scale=5.0)
+    ws, ss = I.draw_conv(rng, 1, H, D, W, "f32")
+    eo, ef, _ = oracle.kda_layer_conv(x.q_pre, x.k_pre, x.v_pre, x.g, x.beta_logit, ws, ss,
+                                      x.gate, x.norm_weight, EPS)
+    q, k, v, g, b, gt = layer_to_dev(x)
+    wd, sd = conv_to_dev(ws, ss, torch.float32)
+    o, fin, _ = kda.layer_prefill(q, k, v, g, b, gt, tdev(x.norm_weight, torch.float32), EPS,
+                                  conv_weight=wd, conv_state=sd, chunk_size=64)
+    torch.cuda.synchronize()
+    eo_, es_ = rel(host(o)[0], eo), rel(host(fin), ef)
+    say(f"  o err {eo_:.2e}  state err {es_:.2e}")
+    assert eo_ <= TOL["f32"] and es_ <= TOL["f32"]
+
+
+@pytest.mark.parametrize("dtype,D,W", [("bf16", 128, 4), ("f32", 64, 3), ("bf16", 64, 1)])
+def test_layer_decode_conv_matches_oracle(kda, dtype, D, W):
+    """Decode steps with the convolution: its carried inputs and the state
+    are updated in place, step after step."""
+    say(f"layer decode conv dtype={dtype} D={D} W={W}")
+    N, H, steps = 3, 2, 24
+    rng = np.random.default_rng([40, D, W])
+    x = I.draw_layer_tokens(rng, N * steps, H, D, D, dtype)
+    s0 = I.draw_states(rng, N, H, D, D)
+    ws, ss = I.draw_conv(rng, N, H, D, W, dtype)
+    cu = np.arange(N + 1) * steps
+    eo, ef, ecs = oracle.kda_layer_conv(x.q_pre, x.k_pre, x.v_pre, x.g, x.beta_logit, ws, ss,
+                                        x.gate, x.norm_weight, EPS, s0, cu)
+    dt = torch.bfloat16 if dtype == "bf16" else torch.float32
+    state = torch.from_numpy(s0.copy()).to(DEV)
+    wd, sd = conv_to_dev(ws, ss, dt)
+    w = tdev(x.norm_weight, torch.float32)
+    worst = 0.0
+    for t in range(steps):
+        rows = np.arange(N) * steps + t
+        o = kda.layer_decode_step(tdev(x.q_pre[rows], dt), tdev(x.k_pre[rows], dt),
+                                  tdev(x.v_pre[rows], dt), tdev(x.g[rows], torch.float32),
+                                  tdev(x.beta_logit[rows], torch.float32), state,
+                                  tdev(x.gate[rows], dt), w, EPS, conv_weight=wd, conv_state=sd)
+        worst = max(worst, rel(host(o), eo[rows]))
+    torch.cuda.synchronize()
+    es = rel(host(state), ef)
+    say(f"  o err {worst:.2e}  state err {es:.2e}")
+    assert worst <= TOL[dtype] and es <= TOL[dtype]
+    for a, e in zip(sd, ecs):
+        np.testing.assert_array_equal(host(a), e.astype(np.float32))
+
+
+def test_layer_conv_decode_continues_prefill(kda):
+    """Prefill with the convolution hands both states to decode steps."""
+    say("layer conv prefill then decode")
+    rng = np.random.default_rng(41)
+    T, H, D, W, steps = 130, 2, 128, 4, 5
+    x = I.draw_layer_tokens(rng, T + steps, H, D, D, "bf16")
+    ws, _ = I.draw_conv(rng, 1, H, D, W, "bf16")
+    eo, ef, ecs = oracle.kda_layer_conv(x.q_pre, x.k_pre, x.v_pre, x.g, x.beta_logit, ws, None,
+                                        x.gate, x.norm_weight, EPS)
+    q, k, v, g, b, gt = layer_to_dev(x)
+    wd, _ = conv_to_dev(ws, None, torch.bfloat16)
+    w = tdev(x.norm_weight, torch.float32)
+    o, st, cs = kda.layer_prefill(q[:, :T].clone(), k[:, :T].clone(), v[:, :T].clone(),
+                                  g[:, :T].clone(), b[:, :T].clone(), gt[:, :T].clone(), w, EPS,
+                                  conv_weight=wd, chunk_size=64)
+    worst = rel(host(o)[0], eo[:T])
+    for t in range(T, T + steps):
+        od = kda.layer_decode_step(q[:, t].clone(), k[:, t].clone(), v[:, t].clone(),
+                                   g[:, t].clone(), b[:, t].clone(), st, gt[:, t].clone(), w, EPS,
+                                   conv_weight=wd, conv_state=cs)
+        worst = max(worst, rel(host(od)[0], eo[t]))
+    torch.cuda.synchronize()
+    es = rel(host(st), ef)
+    say(f"  o err {worst:.2e}  state err {es:.2e}")
+    assert worst <= TOL["bf16"] and es <= TOL["bf16"]
+    for a, e in zip(cs, ecs):
+        np.testing.assert_array_equal(host(a), e.astype(np.float32))
