@@ -18,6 +18,9 @@ Functions
 ``short_conv``         causal depthwise convolution over the tokens of each
                        sequence, with a carried state of the last inputs.
 ``kda_layer_conv``     short convolution of q, k, v, then ``kda_layer``.
+``kda_backward``       gradients of <dO, o> + <dS_N, S_N> with respect to q, k,
+                       v, g, beta and the initial state: reverse-mode through
+                       the token recurrence, written out by hand (float64).
 
 Sources (pages this package follows):
   * Recurrence: "Kimi Linear" notes (docsaid.org), section "KDA: Splitting
@@ -43,6 +46,11 @@ Sources (pages this package follows):
     reading taken is a causal, depthwise (per channel) convolution of width
     W <= 4 with no bias, restarted at every sequence start from a carried
     state (zeros when none is given).
+
+  * Backward pass: the pages only say the chunkwise form also serves training
+    (greeksharifa.github.io summary, sections 3.1 and 6.3; zeroshot.it.com
+    deep-dive, section 4); the gradients here are the chain rule applied to
+    the recurrence above, step by step in reverse token order.
 
 Pins: every function here is checked in ``tests/test_oracle_pins.py`` against
 closed forms, special cases, the two-channel decay table printed on the
@@ -361,3 +369,78 @@ def kda_layer_conv(q_pre, k_pre, v_pre, g, beta_pre, conv_weight, conv_state=Non
     y, fin = kda_layer(conv[0][0], conv[1][0], conv[2][0], g, beta_pre, gate, weight, eps,
                        initial_state, cu_seqlens)
     return y, fin, tuple(c[1] for c in conv)
+
+
+def kda_backward(q, k, v, g, beta, do, dfinal=None, initial_state=None, cu_seqlens=None,
+                 block: int = 64):
+    """Gradients of  L = sum(do * o) + sum(dfinal * S_N)  for the token
+    recurrence (kda_recurrent): per token t, with S the state before it,
+
+        Sp = Diag(exp g_t) S;  r = Sp^T k_t;  u = beta_t (v_t - r)
+        S' = Sp + k_t u^T;     o_t = S'^T q_t
+
+    and in reverse order (dS the gradient of the state after token t):
+
+        dS += q_t do_t^T;        dq_t = S' do_t
+        du = dS^T k_t;           dk_t = dS u
+        dbeta_t = du . (v_t - r);  dv_t = beta_t du;  dr = -beta_t du
+        dSp = dS + k_t dr^T;     dk_t += Sp dr
+        dg_t = exp(g_t) * rowsum(dSp * S);  dS <- Diag(exp g_t) dSp
+
+    Shapes as in kda_recurrent; do [T, H, dv]; dfinal and initial_state
+    [N, H, dk, dv] or None.  States are recomputed from checkpoints every
+    ``block`` tokens.  Returns (dq, dk, dv, dg, dbeta, dS0), float64.
+    """
+    q, k, v, g, beta, do = (np.asarray(a, dtype=np.float64) for a in (q, k, v, g, beta, do))
+    T, H, dk = q.shape
+    dvv = v.shape[2]
+    cu = np.array([0, T]) if cu_seqlens is None else np.asarray(cu_seqlens, dtype=np.int64)
+    N = len(cu) - 1
+    S0 = (np.zeros((N, H, dk, dvv)) if initial_state is None
+          else np.asarray(initial_state, dtype=np.float64))
+    dF = (np.zeros((N, H, dk, dvv)) if dfinal is None
+          else np.asarray(dfinal, dtype=np.float64))
+    dq, dk_, dv_, dg = (np.zeros_like(a) for a in (q, k, v, g))
+    db = np.zeros_like(beta)
+    dS0 = np.zeros((N, H, dk, dvv))
+    alpha = np.exp(g)
+
+    def step(S, t):  # one token for all heads; returns (Sp, r, u, S')
+        Sp = alpha[t][:, :, None] * S
+        r = np.einsum("hij,hi->hj", Sp, k[t])
+        u = beta[t][:, None] * (v[t] - r)
+        return Sp, r, u, Sp + k[t][:, :, None] * u[:, None, :]
+
+    for n in range(N):
+        bos, eos = int(cu[n]), int(cu[n + 1])
+        # forward: checkpoints at block starts
+        ck = {}
+        S = S0[n].copy()
+        for t in range(bos, eos):
+            if (t - bos) % block == 0:
+                ck[t] = S.copy()
+            S = step(S, t)[3]
+        dS = dF[n].copy()
+        starts = sorted(ck)
+        for b0 in reversed(starts):
+            b1 = min(b0 + block, eos)
+            states = [ck[b0]]  # state before each token of the block
+            for t in range(b0, b1 - 1):
+                states.append(step(states[-1], t)[3])
+            for t in range(b1 - 1, b0 - 1, -1):
+                Sprev = states[t - b0]
+                Sp, r, u, Sn = step(Sprev, t)
+                dS = dS + q[t][:, :, None] * do[t][:, None, :]
+                dq[t] = np.einsum("hij,hj->hi", Sn, do[t])
+                du = np.einsum("hij,hi->hj", dS, k[t])
+                dkt = np.einsum("hij,hj->hi", dS, u)
+                db[t] = np.einsum("hj,hj->h", du, v[t] - r)
+                dv_[t] = beta[t][:, None] * du
+                dr = -beta[t][:, None] * du
+                dSp = dS + k[t][:, :, None] * dr[:, None, :]
+                dkt += np.einsum("hij,hj->hi", Sp, dr)
+                dk_[t] = dkt
+                dg[t] = alpha[t] * np.einsum("hij,hij->hi", dSp, Sprev)
+                dS = alpha[t][:, :, None] * dSp
+        dS0[n] = dS
+    return dq, dk_, dv_, dg, db, dS0
