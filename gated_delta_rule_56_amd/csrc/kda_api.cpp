@@ -264,4 +264,68 @@ kda_status kda_decode_step_layer(const void* q_pre, const void* k_pre, const voi
                      H, Dk, Dv, in_dtype, out_dtype, stream);
 }
 
+kda_status kda_backward_workspace_size(int B, int T, int H, int Dk, int Dv, int num_seqs,
+                                       const int32_t* cu_seqlens_host, int chunk_size,
+                                       size_t* bytes) {
+  if (bytes == nullptr || H < 1) return KDA_ERR_INVALID_ARG;
+  if (!supported_head(Dk, Dv) || !supported_chunk(chunk_size)) return KDA_ERR_UNSUPPORTED;
+  int64_t chunks = 0;
+  kda_status st = seq_layout(B, T, num_seqs, cu_seqlens_host, cu_seqlens_host, chunk_size, &chunks);
+  if (st != KDA_OK) return st;
+  *bytes = kda::backward_workspace_bytes(chunks, num_seqs, H, Dk, chunk_size);
+  return KDA_OK;
+}
+
+kda_status kda_backward(const void* q, const void* k, const void* v, const float* g,
+                        const float* beta, const float* initial_state, const float* d_o,
+                        const float* d_final_state, float* dq, float* dk, float* dv, float* dg,
+                        float* dbeta, float* d_initial_state, const int32_t* cu_seqlens,
+                        const int32_t* cu_seqlens_host, int B, int T, int H, int Dk, int Dv,
+                        int num_seqs, int chunk_size, kda_dtype in_dtype, void* workspace,
+                        size_t workspace_bytes, void* stream) {
+  if (H < 1 || !valid_dtype(in_dtype)) return KDA_ERR_INVALID_ARG;
+  if (!supported_head(Dk, Dv) || !supported_chunk(chunk_size)) return KDA_ERR_UNSUPPORTED;
+  const void* ptrs[] = {q, k, v, g, beta, initial_state, d_o, d_final_state, dq, dk, dv, dg,
+                        dbeta, d_initial_state, cu_seqlens};
+  for (const void* p : ptrs)
+    if (p && !aligned(p, 16)) return KDA_ERR_INVALID_ARG;
+  int64_t chunks = 0;
+  kda_status st = seq_layout(B, T, num_seqs, cu_seqlens, cu_seqlens_host, chunk_size, &chunks);
+  if (st != KDA_OK) return st;
+  if ((int64_t)B * T > 0 &&
+      (!q || !k || !v || !g || !beta || !d_o || !dq || !dk || !dv || !dg || !dbeta))
+    return KDA_ERR_INVALID_ARG;
+  if (chunks * (int64_t)H > INT32_MAX) return KDA_ERR_INVALID_ARG;
+  const size_t need = kda::backward_workspace_bytes(chunks, num_seqs, H, Dk, chunk_size);
+  if (workspace == nullptr || workspace_bytes < need) return KDA_ERR_WORKSPACE;
+  if (!aligned(workspace, 256)) return KDA_ERR_INVALID_ARG;
+  kda::BackwardArgs a;
+  a.q = q;
+  a.k = k;
+  a.v = v;
+  a.g = g;
+  a.beta = beta;
+  a.initial_state = initial_state;
+  a.d_o = d_o;
+  a.d_final_state = d_final_state;
+  a.dq = dq;
+  a.dk = dk;
+  a.dv = dv;
+  a.dg = dg;
+  a.dbeta = dbeta;
+  a.d_initial_state = d_initial_state;
+  a.cu_seqlens = cu_seqlens;
+  a.num_seqs = num_seqs;
+  a.seq_len = cu_seqlens ? 0 : T;
+  a.total_tokens = B * T;
+  a.total_chunks = (int)chunks;
+  a.H = H;
+  a.D = Dk;
+  a.chunk = chunk_size;
+  a.in_bf16 = in_dtype == KDA_BF16;
+  a.workspace = workspace;
+  a.stream = reinterpret_cast<hipStream_t>(stream);
+  return kda::launch_backward(a) == hipSuccess ? KDA_OK : KDA_ERR_HIP;
+}
+
 }  // extern "C"

@@ -85,4 +85,28 @@ size_t prefill_workspace_bytes(int num_seqs, const int32_t* cu_host, int seq_len
                                int chunk, bool in_bf16, bool epilogue);
 hipError_t launch_prefill(const PrefillArgs& a);
 
+struct BackwardArgs {
+  const void* q;
+  const void* k;
+  const void* v;
+  const float* g;
+  const float* beta;
+  const float* initial_state;  // or nullptr (zeros)
+  const float* d_o;            // [tokens, H, D] gradient of o
+  const float* d_final_state;  // or nullptr (zeros)
+  float *dq, *dk, *dv, *dg, *dbeta;
+  float* d_initial_state;      // or nullptr (not written)
+  const int32_t* cu_seqlens;   // device, or nullptr => num_seqs sequences of seq_len
+  int num_seqs, seq_len, total_tokens, total_chunks;
+  int H, D, chunk;
+  bool in_bf16;
+  void* workspace;
+  hipStream_t stream;
+};
+
+// Workspace of the backward pass: the first chunk of each sequence, then the
+// fp32 per-(chunk, head) planes of every chunk (no segmenting).
+size_t backward_workspace_bytes(long long total_chunks, int num_seqs, int H, int D, int chunk);
+hipError_t launch_backward(const BackwardArgs& a);
+
 }  // namespace kda

@@ -71,6 +71,11 @@ def load() -> ctypes.CDLL:
     lib.kda_decode_step_layer.argtypes = [vp, vp, vp, vp, vp, lp, vp, vp,
                                           i32, i32, i32, i32, i32, i32, vp]
     lib.kda_decode_step_layer.restype = i32
+    lib.kda_backward_workspace_size.argtypes = [i32, i32, i32, i32, i32, i32, vp, i32,
+                                                ctypes.POINTER(sz)]
+    lib.kda_backward_workspace_size.restype = i32
+    lib.kda_backward.argtypes = [vp] * 16 + [i32] * 8 + [vp, sz, vp]
+    lib.kda_backward.restype = i32
     _lib = lib
     return lib
 
@@ -375,3 +380,79 @@ def _decode(q, k, v, g, beta, state, out_dtype, o, layer):
         N, H, D, Dv, in_code, out_code, _stream_ptr(q.device)),
         "gdn_decode_step" if scalar_g else "kda_decode_step")
     return o
+
+
+def backward_workspace_size(B: int, T: int, H: int, D: int, num_seqs: int, chunk_size: int,
+                            cu_seqlens_host: Optional[np.ndarray] = None) -> int:
+    out = ctypes.c_size_t(0)
+    cu_p = None if cu_seqlens_host is None else cu_seqlens_host.ctypes.data
+    _check(load().kda_backward_workspace_size(B, T, H, D, D, num_seqs, cu_p, chunk_size,
+                                              ctypes.byref(out)), "kda_backward_workspace_size")
+    return out.value
+
+
+def backward(q, k, v, g, beta, d_o, initial_state=None, d_final_state=None, cu_seqlens=None, *,
+             cu_seqlens_host: Optional[Union[Sequence[int], np.ndarray]] = None,
+             chunk_size: int = 64, output_d_initial_state: bool = True, workspace=None,
+             out=None):
+    """Backward of :func:`prefill` (``kda_backward``): gradients of
+    ``sum(d_o * o) + sum(d_final_state * final_state)`` with respect to q, k,
+    v, g, beta and the initial state.  Shapes as in :func:`prefill`; d_o
+    ``[B, T, H, Dv]`` float32.  Returns ``(dq, dk, dv, dg, dbeta, d_initial_state)``
+    (float32; the last is None unless requested).  ``out`` may pass the six
+    output tensors to write."""
+    torch = _torch()
+    if q.dim() != 4:
+        raise KDAError("q must be [B, T, H, D]")
+    B, T, H, D = q.shape
+    Dv = v.shape[-1]
+    _expect("k", k, (B, T, H, D))
+    _expect("v", v, (B, T, H, Dv))
+    _expect("g", g, (B, T, H, D))
+    _expect("beta", beta, (B, T, H))
+    _expect("d_o", d_o, (B, T, H, Dv))
+    in_code = _dtype_code(q.dtype)
+    for name, t in (("k", k), ("v", v)):
+        if t.dtype != q.dtype:
+            raise KDAError(f"{name} must have the dtype of q")
+    for name, t in (("g", g), ("beta", beta), ("d_o", d_o)):
+        if t.dtype != torch.float32:
+            raise KDAError(f"{name} must be float32")
+    for name, t in (("q", q), ("k", k), ("v", v), ("g", g), ("beta", beta), ("d_o", d_o)):
+        if not t.is_contiguous():
+            raise KDAError(f"{name} must be contiguous")
+    if cu_seqlens is not None:
+        cu_h = _host_cu(cu_seqlens, cu_seqlens_host)
+        N = len(cu_h) - 1
+        if cu_seqlens.dtype != torch.int32:
+            raise KDAError("cu_seqlens must be int32")
+    else:
+        cu_h = None
+        N = B
+    for name, t in (("initial_state", initial_state), ("d_final_state", d_final_state)):
+        _expect(name, t, (N, H, D, Dv))
+        if t is not None and (t.dtype != torch.float32 or not t.is_contiguous()):
+            raise KDAError(f"{name} must be contiguous float32")
+    if out is None:
+        f32 = dict(dtype=torch.float32, device=q.device)
+        out = (torch.empty((B, T, H, D), **f32), torch.empty((B, T, H, D), **f32),
+               torch.empty((B, T, H, Dv), **f32), torch.empty((B, T, H, D), **f32),
+               torch.empty((B, T, H), **f32),
+               torch.empty((N, H, D, Dv), **f32) if output_d_initial_state else None)
+    dq, dk, dv, dg, db, ds0 = out
+    for name, t, shp in (("dq", dq, (B, T, H, D)), ("dk", dk, (B, T, H, D)),
+                         ("dv", dv, (B, T, H, Dv)), ("dg", dg, (B, T, H, D)),
+                         ("dbeta", db, (B, T, H)), ("d_initial_state", ds0, (N, H, D, Dv))):
+        _expect(name, t, shp)
+        if t is not None and (t.dtype != torch.float32 or not t.is_contiguous()):
+            raise KDAError(f"{name} must be contiguous float32")
+    ws_bytes = backward_workspace_size(B, T, H, D, N, chunk_size, cu_h)
+    if workspace is None or workspace.numel() < ws_bytes:
+        workspace = torch.empty(max(ws_bytes, 256), dtype=torch.uint8, device=q.device)
+    cu_hp = None if cu_h is None else cu_h.ctypes.data
+    _check(load().kda_backward(
+        _ptr(q), _ptr(k), _ptr(v), _ptr(g), _ptr(beta), _ptr(initial_state), _ptr(d_o),
+        _ptr(d_final_state), _ptr(dq), _ptr(dk), _ptr(dv), _ptr(dg), _ptr(db), _ptr(ds0),
+        _ptr(cu_seqlens), cu_hp, B, T, H, D, Dv, N, chunk_size, in_code,
+        _ptr(workspace), workspace.numel(), _stream_ptr(q.device)), "kda_backward")
+    return dq, dk, dv, dg, db, ds0

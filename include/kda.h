@@ -272,6 +272,47 @@ kda_status kda_decode_step_layer(const void* q_pre, const void* k_pre,
                                  kda_dtype in_dtype, kda_dtype out_dtype,
                                  void* stream /* hipStream_t */);
 
+/*
+ * Backward pass of kda_prefill: the gradients of
+ *
+ *     L = sum(d_o * o) + sum(d_final_state * final_state)
+ *
+ * with respect to q, k, v, g, beta and the initial state, for the same
+ * inputs and sequence description as the forward call (the pages say the
+ * chunkwise form serves training: greeksharifa summary, sections 3.1 and
+ * 6.3; the gradients are the chain rule through the chunk form of the
+ * recurrence).  The forward pass is recomputed inside; o is not needed.
+ * Arithmetic is fp32; the decay enters every intra-chunk pair through the
+ * exact exponent of its difference, so any decay strength is handled.
+ *
+ * Arguments (others as in kda_prefill):
+ *   d_o            [B*T, H, Dv] float32
+ *   d_final_state  [num_seqs, H, Dk, Dv] float32, or NULL (zero)
+ *   dq, dk, dg     [B*T, H, Dk] float32 (written)
+ *   dv             [B*T, H, Dv] float32 (written)
+ *   dbeta          [B*T, H] float32 (written)
+ *   d_initial_state [num_seqs, H, Dk, Dv] float32, or NULL (not written)
+ *   workspace      at least kda_backward_workspace_size bytes, 256-byte
+ *                  aligned: about 737 KB of fp32 intermediates per chunk and
+ *                  head at Dk = Dv = 128, C = 64, for every chunk (the
+ *                  backward does not run in segments).
+ */
+kda_status kda_backward_workspace_size(int B, int T, int H, int Dk, int Dv,
+                                       int num_seqs,
+                                       const int32_t* cu_seqlens_host,
+                                       int chunk_size, size_t* bytes);
+
+kda_status kda_backward(const void* q, const void* k, const void* v,
+                        const float* g, const float* beta,
+                        const float* initial_state, const float* d_o,
+                        const float* d_final_state, float* dq, float* dk,
+                        float* dv, float* dg, float* dbeta,
+                        float* d_initial_state, const int32_t* cu_seqlens,
+                        const int32_t* cu_seqlens_host, int B, int T, int H,
+                        int Dk, int Dv, int num_seqs, int chunk_size,
+                        kda_dtype in_dtype, void* workspace,
+                        size_t workspace_bytes, void* stream /* hipStream_t */);
+
 #ifdef __cplusplus
 }
 #endif
