@@ -167,7 +167,35 @@ def other_workloads(torch, kda, I, dev):
         tiny[f"chunk{C}_tokens_per_s"] = round(w.T / t, 1)
     out["tiny_fp32"] = {"workload": "kda_prefill B=1 H=1 T=256 d=64 fp32", **tiny}
     out["layer"] = layer_workloads(torch, kda, I, dev)
+    out["backward"] = backward_workload(torch, kda, I, dev)
     return out
+
+
+def backward_workload(torch, kda, I, dev):
+    """kda_backward on the headline prefill shape, initial state and
+    final-state gradient included."""
+    T, H, d = P_T, P_H, P_D
+    q, k, v, g, b = I.device_tokens(torch, T, H, d, d, 5005, dev)
+    do = torch.randn((1, T, H, d), device=dev)
+    s0 = torch.randn((1, H, d, d), device=dev) * 0.1
+    dF = torch.randn((1, H, d, d), device=dev)
+    f32 = dict(dtype=torch.float32, device=dev)
+    outs = (torch.empty((1, T, H, d), **f32), torch.empty((1, T, H, d), **f32),
+            torch.empty((1, T, H, d), **f32), torch.empty((1, T, H, d), **f32),
+            torch.empty((1, T, H), **f32), torch.empty((1, H, d, d), **f32))
+    ws = torch.empty(kda.backward_workspace_size(1, T, H, d, 1, P_C), dtype=torch.uint8,
+                     device=dev)
+    t = time_calls(torch, lambda: kda.backward(q, k, v, g, b, do, s0, dF, chunk_size=P_C,
+                                               workspace=ws, out=outs), 5)
+    # inputs q, k, v bf16, g, beta, d_o fp32; outputs dq, dk, dv, dg, dbeta
+    # fp32; initial state, final-state gradient and its result
+    by = T * H * (3 * 2 * d + 4 * d + 4 + 4 * d + 4 * 4 * d + 4) + 3 * H * d * d * 4
+    return {"workload": f"kda_backward B=1 H={H} T={T} d={d} chunk {P_C}, bf16 q/k/v, fp32 "
+                        "gradients, initial state and final-state gradient",
+            "ms_per_call": round(t * 1e3, 3), "tokens_per_s": round(T / t, 1),
+            "algorithmic_GBps": round(by / t / 1e9, 1),
+            "hbm_frac": round(by / t / 1e9 / HBM_PEAK_GBS, 4),
+            "workspace_bytes": int(ws.numel())}
 
 
 def layer_workloads(torch, kda, I, dev):

@@ -27,18 +27,31 @@
 //   then the exact pairwise terms of Bm and P, the decays, and dg as the
 //   reverse cumulative sum of dGamma over the chunk.
 //
+// Decay factorisation.  When the chunk's total decay is moderate (max over
+// channels of -Gamma_{C-1} <= 40), exp(Gamma_r - Gamma_i) = gam_r / gam_i
+// holds to rounding in fp32, and every pairwise sum is a product with
+// Kh = K*exp(-Gamma): Bm = strict_tril(Kt Kh^T), P = tril(Qt Kh^T), and the
+// pairwise gradient terms come from Y1 = dBm Kh, Y2 = dP Kh and
+// Y3 = dBm^T Kt + dP^T Qt.  Other chunks evaluate every pair with the exact
+// exponent of its difference.
+//
 // Kernels (one launch each, in order):
 //   bwd_table_kernel      first global chunk of each packed sequence
-//   bwd_prep_kernel       per (chunk, head): padded fp32 copies, Gamma, Qt, Kt, Kb
-//   bwd_gram_kernel       per (chunk, head): Bm and P pair by pair (exact exps)
+//   bwd_prep_kernel       per (chunk, head): padded fp32 copies, Gamma, Qt, Kt,
+//                         Kb, Kh and the span verdict
+//   bwd_gemm_kernel       batched fp32 products (Grams, contractions over value
+//                         columns, pairwise gradient terms)
+//   bwd_gram_kernel       per strong-decay (chunk, head): Bm and P pair by pair
 //   bwd_solve_kernel      per (chunk, head): M by forward substitution, T
 //   bwd_fwd_states_kernel per (sequence, head, 16 value columns), serial over
 //                         chunks: the entering state S of every chunk, R, U
 //   bwd_bwd_states_kernel the same, reverse: dS' of every chunk, dU, dR, dS0
 //   bwd_nt_gemm_kernel    batched fp32 products over value columns
 //   bwd_cc_kernel         per (chunk, head): the C x C algebra of M and A
-//   bwd_final_kernel      per (chunk, head): pairwise gradients, decays,
-//                         reverse cumsum, scatter to the token-major outputs
+//   bwd_final_fast_kernel per moderate-decay (chunk, head): decays, reverse
+//                         cumsum, scatter to the token-major outputs
+//   bwd_final_kernel      the same for strong-decay chunks, with the pairwise
+//                         gradient terms evaluated pair by pair
 #include "kda_device.hpp"
 #include "kda_launch.hpp"
 
@@ -47,27 +60,31 @@ namespace kda {
 namespace {
 
 constexpr int kCols = 16;  // value columns per serial workgroup
+constexpr float kSpan = 40.f;  // decay span up to which exp(-Gamma) is factored out
 
 // fp32 planes, each [NB][size] with NB = chunks x heads.
+// R, U and dU are dead once the value-column contractions are done and then
+// hold Y1, Y2 and Y3.
 struct Planes {
-  float *Q, *K, *V, *dO, *Gam, *Qt, *Kt, *Kb, *R, *U, *dU, *dR, *dQt, *dKb, *dKt;  // [C][D]
+  float *Q, *K, *V, *dO, *Gam, *Qt, *Kt, *Kb, *Kh, *R, *U, *dU, *dR, *dQt, *dKb, *dKt;  // [C][D]
   float *P, *Bm, *M, *T, *dP, *dT, *dBm;                                          // [C][C]
   float *S, *dSn;                                                                 // [D][D]
   float *beta, *db;                                                               // [C]
   float *gn;                                                                      // [D]
+  int32_t* fast;                                                                  // [1] per (chunk, head)
 };
 
 size_t a256(size_t x) { return (x + 255) / 256 * 256; }
 
 size_t plane_bytes(size_t NB, int C, int D) {
   const size_t cd = a256(NB * C * D * 4), cc = a256(NB * C * C * 4), dd = a256(NB * D * D * 4);
-  return 15 * cd + 7 * cc + 2 * dd + 2 * a256(NB * C * 4) + a256(NB * D * 4);
+  return 16 * cd + 7 * cc + 2 * dd + 2 * a256(NB * C * 4) + a256(NB * D * 4) + a256(NB * 4);
 }
 
 Planes carve(char* p, size_t NB, int C, int D) {
   const size_t cd = a256(NB * C * D * 4), cc = a256(NB * C * C * 4), dd = a256(NB * D * D * 4);
   Planes x;
-  float** cdp[] = {&x.Q, &x.K, &x.V, &x.dO, &x.Gam, &x.Qt, &x.Kt, &x.Kb,
+  float** cdp[] = {&x.Q, &x.K, &x.V, &x.dO, &x.Gam, &x.Qt, &x.Kt, &x.Kb, &x.Kh,
                    &x.R, &x.U, &x.dU, &x.dR, &x.dQt, &x.dKb, &x.dKt};
   for (float** f : cdp) { *f = reinterpret_cast<float*>(p); p += cd; }
   float** ccp[] = {&x.P, &x.Bm, &x.M, &x.T, &x.dP, &x.dT, &x.dBm};
@@ -77,6 +94,8 @@ Planes carve(char* p, size_t NB, int C, int D) {
   x.beta = reinterpret_cast<float*>(p); p += a256(NB * C * 4);
   x.db = reinterpret_cast<float*>(p); p += a256(NB * C * 4);
   x.gn = reinterpret_cast<float*>(p);
+  p += a256(NB * D * 4);
+  x.fast = reinterpret_cast<int32_t*>(p);
   return x;
 }
 
@@ -197,6 +216,12 @@ __global__ __launch_bounds__(256) void bwd_prep_kernel(BwdIn in, Planes p, Geo g
     p.gn[(size_t)b * D + c] = __expf(s);
   }
   __syncthreads();
+  if (threadIdx.x < 64) {  // span verdict over all channels (one wave)
+    bool big = false;
+    for (int c = threadIdx.x; c < D; c += 64) big |= G[C - 1][c] < -kSpan;
+    big = __any(big);
+    if (threadIdx.x == 0) p.fast[b] = big ? 0 : 1;
+  }
   for (int idx = threadIdx.x; idx < C * D; idx += 256) {
     const int r = idx / D, c = idx % D;
     const float gm = G[r][c], ga = __expf(gm);
@@ -205,10 +230,12 @@ __global__ __launch_bounds__(256) void bwd_prep_kernel(BwdIn in, Planes p, Geo g
     p.Qt[pcd + idx] = p.Q[pcd + idx] * ga;
     p.Kt[pcd + idx] = kv * ga;
     p.Kb[pcd + idx] = kv * __expf(G[C - 1][c] - gm);
+    p.Kh[pcd + idx] = kv * __expf(-gm);  // finite where the chunk is factored
   }
 }
 
-// Bm (strictly lower) and P (lower) with the exact exponent of every pair.
+// Bm (strictly lower) and P (lower) with the exact exponent of every pair,
+// for strong-decay chunks.
 // Lane = row r; the four waves step through the columns i.
 template <int D, int C>
 __global__ __launch_bounds__(256) void bwd_gram_kernel(Planes p, int NB) {
@@ -217,6 +244,7 @@ __global__ __launch_bounds__(256) void bwd_gram_kernel(Planes p, int NB) {
   float* Qs = Ks + C * (D + 1);
   float* Gs = Qs + C * (D + 1);
   const int b = blockIdx.x;
+  if (p.fast[b]) return;  // formed as a product
   const size_t pcd = (size_t)b * C * D;
   for (int idx = threadIdx.x; idx < C * D; idx += 256) {
     const int r = idx / D, c = idx % D;
@@ -272,184 +300,257 @@ __global__ __launch_bounds__(64) void bwd_solve_kernel(Planes p) {
   }
 }
 
-// Serial forward over a sequence's chunks for 16 value columns: the state
-// entering every chunk, R = V - Kt S and U = T R.
+// The serial passes run their products on v_mfma_f32_16x16x4f32 (fp32
+// operands): lane l supplies A[m = l & 15][k = l >> 4] and B[k = l >> 4][n =
+// l & 15] and receives D rows 4 (l >> 4) + i of column l & 15.  Operands are
+// staged in LDS; a matrix read as A[m][k] = X[m][k] has row stride +4 floats,
+// one read transposed (A[m][k] = X[k][m]) +16, so the 64 lanes of a read hit
+// 64 different banks; 16-column blocks have stride 16.
+__device__ __forceinline__ f32x4 mfma4(float a, float b, f32x4 c) {
+  return __builtin_amdgcn_mfma_f32_16x16x4f32(a, b, c, 0, 0, 0);
+}
+
+// Stage ROWS x COLS floats (row-major) into LDS with row stride LD: every
+// load of the thread is issued before the first LDS store.
+template <int ROWS, int COLS, int LD>
+__device__ __forceinline__ void stage(float* dst, const float* __restrict__ src) {
+  constexpr int C4 = COLS / 4, N = (ROWS * C4 + 255) / 256;
+  static_assert(COLS % 4 == 0, "float4 rows");
+  f32x4 v[N];
+#pragma unroll
+  for (int x = 0; x < N; ++x) {
+    const int idx = threadIdx.x + 256 * x;
+    if (idx < ROWS * C4)
+      v[x] = *reinterpret_cast<const f32x4*>(src + (size_t)(idx / C4) * COLS + 4 * (idx % C4));
+  }
+#pragma unroll
+  for (int x = 0; x < N; ++x) {
+    const int idx = threadIdx.x + 256 * x;
+    if (idx < ROWS * C4) {
+      const int r = idx / C4, c = 4 * (idx % C4);
+#pragma unroll
+      for (int e = 0; e < 4; ++e) dst[r * LD + c + e] = v[x][e];
+    }
+  }
+}
+
 template <int D, int C>
 struct FwdLds {
-  float Ks[C][D + 1];  // Kt, then Kb
-  float Ts[C][C + 1];
-  float Ss[D][kCols + 1];
-  float Rs[C][kCols + 1];
-  float Us[C][kCols + 1];
+  float Kt[C][D + 4];
+  float Kb[C][D + 16];
+  float T[C][C + 4];
+  float S[D][kCols];
+  float R[C][kCols];
+  float U[C][kCols];
 };
 
+// Serial forward over a sequence's chunks for 16 value columns: the state
+// entering every chunk, R = V - Kt S and U = T R.
 template <int D, int C>
 __global__ __launch_bounds__(256) void bwd_fwd_states_kernel(Planes p, Geo geo,
                                                              const float* __restrict__ s0) {
   extern __shared__ float sm[];
   FwdLds<D, C>& L = *reinterpret_cast<FwdLds<D, C>*>(sm);
-  auto& Ks = L.Ks;
-  auto& Ts = L.Ts;
-  auto& Ss = L.Ss;
-  auto& Rs = L.Rs;
-  auto& Us = L.Us;
   constexpr int NVB = D / kCols;
   const int H = geo.H;
-  const int blk = blockIdx.x;
-  const int vb = blk % NVB, nh = blk / NVB;
+  const int vb = blockIdx.x % NVB, nh = blockIdx.x / NVB;
   const int n = nh / H, h = nh % H, col0 = vb * kCols;
-  const int tid = threadIdx.x;
+  const int tid = threadIdx.x, w = tid >> 6, l = tid & 63, m = l & 15, g = l >> 4;
   int bos, eos, base;
   seq_of<C>(geo, n, bos, eos, base);
   const int nch = (eos - bos + C - 1) / C;
   for (int idx = tid; idx < D * kCols; idx += 256) {
     const int i = idx / kCols, j = idx % kCols;
-    Ss[i][j] = s0 ? s0[(((size_t)n * H + h) * D + i) * D + col0 + j] : 0.f;
+    L.S[i][j] = s0 ? s0[(((size_t)n * H + h) * D + i) * D + col0 + j] : 0.f;
   }
   for (int ci = 0; ci < nch; ++ci) {
     const size_t b = (size_t)(base + ci) * H + h;
     const size_t pcd = b * C * D, pcc = b * C * C;
     __syncthreads();
-    for (int idx = tid; idx < C * D; idx += 256) Ks[idx / D][idx % D] = p.Kt[pcd + idx];
-    for (int idx = tid; idx < C * C; idx += 256) Ts[idx / C][idx % C] = p.T[pcc + idx];
+    stage<C, D, D + 4>(&L.Kt[0][0], p.Kt + pcd);
+    stage<C, D, D + 16>(&L.Kb[0][0], p.Kb + pcd);
+    stage<C, C, C + 4>(&L.T[0][0], p.T + pcc);
     for (int idx = tid; idx < D * kCols; idx += 256) {
       const int i = idx / kCols, j = idx % kCols;
-      p.S[(b * D + i) * D + col0 + j] = Ss[i][j];
+      p.S[(b * D + i) * D + col0 + j] = L.S[i][j];
     }
     __syncthreads();
-    for (int idx = tid; idx < C * kCols; idx += 256) {  // R = V - Kt S
-      const int r = idx / kCols, j = idx % kCols;
-      float s = p.V[pcd + r * D + col0 + j];
-      for (int c = 0; c < D; ++c) s -= Ks[r][c] * Ss[c][j];
-      Rs[r][j] = s;
-      p.R[pcd + r * D + col0 + j] = s;
+    for (int rt = w; rt < C / 16; rt += 4) {  // R = V - Kt S
+      f32x4 acc = {0, 0, 0, 0}, acc1 = {0, 0, 0, 0};
+#pragma unroll 8
+      for (int k0 = 0; k0 < D; k0 += 8) {
+        acc = mfma4(L.Kt[16 * rt + m][k0 + g], L.S[k0 + g][m], acc);
+        acc1 = mfma4(L.Kt[16 * rt + m][k0 + 4 + g], L.S[k0 + 4 + g][m], acc1);
+      }
+      acc += acc1;
+#pragma unroll
+      for (int i = 0; i < 4; ++i) {
+        const int r = 16 * rt + 4 * g + i;
+        const float x = p.V[pcd + r * D + col0 + m] - acc[i];
+        L.R[r][m] = x;
+        p.R[pcd + r * D + col0 + m] = x;
+      }
     }
     __syncthreads();
-    for (int idx = tid; idx < C * kCols; idx += 256) {  // U = T R
-      const int r = idx / kCols, j = idx % kCols;
-      float s = 0.f;
-      for (int i = 0; i <= r; ++i) s += Ts[r][i] * Rs[i][j];
-      Us[r][j] = s;
-      p.U[pcd + r * D + col0 + j] = s;
+    for (int rt = w; rt < C / 16; rt += 4) {  // U = T R (T lower triangular)
+      f32x4 acc = {0, 0, 0, 0};
+      for (int k0 = 0; k0 < 16 * (rt + 1); k0 += 4) acc = mfma4(L.T[16 * rt + m][k0 + g], L.R[k0 + g][m], acc);
+#pragma unroll
+      for (int i = 0; i < 4; ++i) {
+        const int r = 16 * rt + 4 * g + i;
+        L.U[r][m] = acc[i];
+        p.U[pcd + r * D + col0 + m] = acc[i];
+      }
     }
     __syncthreads();
-    for (int idx = tid; idx < C * D; idx += 256) Ks[idx / D][idx % D] = p.Kb[pcd + idx];
-    __syncthreads();
-    for (int idx = tid; idx < D * kCols; idx += 256) {  // S = gam_n S + Kb^T U
-      const int c = idx / kCols, j = idx % kCols;
-      float s = p.gn[b * D + c] * Ss[c][j];
-      for (int r = 0; r < C; ++r) s += Ks[r][c] * Us[r][j];
-      Ss[c][j] = s;  // each (c, j) read and written by this thread only
+    for (int t = w; t < D / 16; t += 4) {  // S = gam_n S + Kb^T U, tile t of each wave
+      f32x4 acc;
+#pragma unroll
+      for (int i = 0; i < 4; ++i) {
+        const int c = 16 * t + 4 * g + i;
+        acc[i] = p.gn[b * D + c] * L.S[c][m];
+      }
+      f32x4 acc1 = {0, 0, 0, 0};
+#pragma unroll 8
+      for (int k0 = 0; k0 < C; k0 += 8) {
+        acc = mfma4(L.Kb[k0 + g][16 * t + m], L.U[k0 + g][m], acc);
+        acc1 = mfma4(L.Kb[k0 + 4 + g][16 * t + m], L.U[k0 + 4 + g][m], acc1);
+      }
+      acc += acc1;
+#pragma unroll
+      for (int i = 0; i < 4; ++i) L.S[16 * t + 4 * g + i][m] = acc[i];
     }
   }
 }
 
+template <int D, int C>
+struct BwdLds {
+  union {
+    struct {
+      float P[C][C + 16];   // read transposed
+      float T[C][C + 16];   // read transposed
+      float Kb[C][D + 4];
+    } a;
+    struct {
+      float Qt[C][D + 16];  // read transposed
+      float Kt[C][D + 16];  // read transposed
+    } b;
+  } u;
+  float X[D][kCols];     // dS'
+  float dO[C][kCols];
+  float dU[C][kCols];
+  float ndR[C][kCols];   // -dR
+};
+
 // Serial backward over a sequence's chunks for 16 value columns: dS' of
 // every chunk, dU = P^T dO + Kb dS', dR = T^T dU, and the carried
 // dS = gam_n dS' + Qt^T dO - Kt^T dR; the last one is dS0.
-template <int D, int C>
-struct BwdLds {
-  float Xs[C][D + 1];  // Kb, then Qt
-  float Ys[C][D + 1];  // Kt
-  float Ps[C][C + 1];
-  float Ts[C][C + 1];
-  float Ds[D][kCols + 1];
-  float Os[C][kCols + 1];
-  float dUs[C][kCols + 1];
-  float dRs[C][kCols + 1];
-};
-
 template <int D, int C>
 __global__ __launch_bounds__(256) void bwd_bwd_states_kernel(Planes p, Geo geo,
                                                              const float* __restrict__ dfin,
                                                              float* __restrict__ ds0) {
   extern __shared__ float sm[];
   BwdLds<D, C>& L = *reinterpret_cast<BwdLds<D, C>*>(sm);
-  auto& Xs = L.Xs;
-  auto& Ys = L.Ys;
-  auto& Ps = L.Ps;
-  auto& Ts = L.Ts;
-  auto& Ds = L.Ds;
-  auto& Os = L.Os;
-  auto& dUs = L.dUs;
-  auto& dRs = L.dRs;
   constexpr int NVB = D / kCols;
   const int H = geo.H;
-  const int blk = blockIdx.x;
-  const int vb = blk % NVB, nh = blk / NVB;
+  const int vb = blockIdx.x % NVB, nh = blockIdx.x / NVB;
   const int n = nh / H, h = nh % H, col0 = vb * kCols;
-  const int tid = threadIdx.x;
+  const int tid = threadIdx.x, w = tid >> 6, l = tid & 63, m = l & 15, g = l >> 4;
   int bos, eos, base;
   seq_of<C>(geo, n, bos, eos, base);
   const int nch = (eos - bos + C - 1) / C;
   for (int idx = tid; idx < D * kCols; idx += 256) {
     const int i = idx / kCols, j = idx % kCols;
-    Ds[i][j] = dfin ? dfin[(((size_t)n * H + h) * D + i) * D + col0 + j] : 0.f;
+    L.X[i][j] = dfin ? dfin[(((size_t)n * H + h) * D + i) * D + col0 + j] : 0.f;
   }
   for (int ci = nch - 1; ci >= 0; --ci) {
     const size_t b = (size_t)(base + ci) * H + h;
     const size_t pcd = b * C * D, pcc = b * C * C;
     __syncthreads();
-    for (int idx = tid; idx < C * D; idx += 256) Xs[idx / D][idx % D] = p.Kb[pcd + idx];
-    for (int idx = tid; idx < C * C; idx += 256) {
-      Ps[idx / C][idx % C] = p.P[pcc + idx];
-      Ts[idx / C][idx % C] = p.T[pcc + idx];
-    }
+    stage<C, C, C + 16>(&L.u.a.P[0][0], p.P + pcc);
+    stage<C, C, C + 16>(&L.u.a.T[0][0], p.T + pcc);
+    stage<C, D, D + 4>(&L.u.a.Kb[0][0], p.Kb + pcd);
     for (int idx = tid; idx < C * kCols; idx += 256) {
       const int r = idx / kCols, j = idx % kCols;
-      Os[r][j] = p.dO[pcd + r * D + col0 + j];
+      L.dO[r][j] = p.dO[pcd + r * D + col0 + j];
     }
     for (int idx = tid; idx < D * kCols; idx += 256) {
       const int i = idx / kCols, j = idx % kCols;
-      p.dSn[(b * D + i) * D + col0 + j] = Ds[i][j];
+      p.dSn[(b * D + i) * D + col0 + j] = L.X[i][j];
     }
     __syncthreads();
-    for (int idx = tid; idx < C * kCols; idx += 256) {  // dU = P^T dO + Kb dS'
-      const int r = idx / kCols, j = idx % kCols;
-      float s = 0.f;
-      for (int i = r; i < C; ++i) s += Ps[i][r] * Os[i][j];
-      for (int c = 0; c < D; ++c) s += Xs[r][c] * Ds[c][j];
-      dUs[r][j] = s;
-      p.dU[pcd + r * D + col0 + j] = s;
+    for (int rt = w; rt < C / 16; rt += 4) {  // dU = P^T dO + Kb dS'
+      f32x4 acc = {0, 0, 0, 0};
+      for (int k0 = 16 * rt; k0 < C; k0 += 4) acc = mfma4(L.u.a.P[k0 + g][16 * rt + m], L.dO[k0 + g][m], acc);
+      f32x4 acc1 = {0, 0, 0, 0};
+#pragma unroll 8
+      for (int k0 = 0; k0 < D; k0 += 8) {
+        acc1 = mfma4(L.u.a.Kb[16 * rt + m][k0 + g], L.X[k0 + g][m], acc1);
+        acc = mfma4(L.u.a.Kb[16 * rt + m][k0 + 4 + g], L.X[k0 + 4 + g][m], acc);
+      }
+      acc += acc1;
+#pragma unroll
+      for (int i = 0; i < 4; ++i) {
+        const int r = 16 * rt + 4 * g + i;
+        L.dU[r][m] = acc[i];
+        p.dU[pcd + r * D + col0 + m] = acc[i];
+      }
     }
     __syncthreads();
-    for (int idx = tid; idx < C * kCols; idx += 256) {  // dR = T^T dU
-      const int r = idx / kCols, j = idx % kCols;
-      float s = 0.f;
-      for (int i = r; i < C; ++i) s += Ts[i][r] * dUs[i][j];
-      dRs[r][j] = s;
-      p.dR[pcd + r * D + col0 + j] = s;
+    for (int rt = w; rt < C / 16; rt += 4) {  // dR = T^T dU
+      f32x4 acc = {0, 0, 0, 0};
+      for (int k0 = 16 * rt; k0 < C; k0 += 4) acc = mfma4(L.u.a.T[k0 + g][16 * rt + m], L.dU[k0 + g][m], acc);
+#pragma unroll
+      for (int i = 0; i < 4; ++i) {
+        const int r = 16 * rt + 4 * g + i;
+        L.ndR[r][m] = -acc[i];
+        p.dR[pcd + r * D + col0 + m] = acc[i];
+      }
     }
     __syncthreads();
-    for (int idx = tid; idx < C * D; idx += 256) {
-      Xs[idx / D][idx % D] = p.Qt[pcd + idx];
-      Ys[idx / D][idx % D] = p.Kt[pcd + idx];
-    }
+    stage<C, D, D + 16>(&L.u.b.Qt[0][0], p.Qt + pcd);
+    stage<C, D, D + 16>(&L.u.b.Kt[0][0], p.Kt + pcd);
     __syncthreads();
-    for (int idx = tid; idx < D * kCols; idx += 256) {  // dS = gam_n dS' + Qt^T dO - Kt^T dR
-      const int c = idx / kCols, j = idx % kCols;
-      float s = p.gn[b * D + c] * Ds[c][j];
-      for (int r = 0; r < C; ++r) s += Xs[r][c] * Os[r][j] - Ys[r][c] * dRs[r][j];
-      Ds[c][j] = s;
+    for (int t = w; t < D / 16; t += 4) {  // dS = gam_n dS' + Qt^T dO - Kt^T dR
+      f32x4 acc;
+#pragma unroll
+      for (int i = 0; i < 4; ++i) {
+        const int c = 16 * t + 4 * g + i;
+        acc[i] = p.gn[b * D + c] * L.X[c][m];
+      }
+      f32x4 acc1 = {0, 0, 0, 0};
+#pragma unroll 8
+      for (int k0 = 0; k0 < C; k0 += 4) {
+        acc = mfma4(L.u.b.Qt[k0 + g][16 * t + m], L.dO[k0 + g][m], acc);
+        acc1 = mfma4(L.u.b.Kt[k0 + g][16 * t + m], L.ndR[k0 + g][m], acc1);
+      }
+      acc += acc1;
+#pragma unroll
+      for (int i = 0; i < 4; ++i) L.X[16 * t + 4 * g + i][m] = acc[i];
     }
   }
   __syncthreads();
   if (ds0) {
     for (int idx = tid; idx < D * kCols; idx += 256) {
       const int i = idx / kCols, j = idx % kCols;
-      ds0[(((size_t)n * H + h) * D + i) * D + col0 + j] = Ds[i][j];
+      ds0[(((size_t)n * H + h) * D + i) * D + col0 + j] = L.X[i][j];
     }
   }
 }
 
-// Batched C = alpha * A B^T (row-major A [M][K], B [N][K], C [M][N]) with an
-// optional lower-triangular mask on C.  64 x 64 tile, 256 threads, 4 x 4
-// outputs each; M, N, K multiples of 16.
-__global__ __launch_bounds__(256) void bwd_nt_gemm_kernel(const float* __restrict__ A,
-                                                          const float* __restrict__ B,
-                                                          float* __restrict__ Cm, int M, int N,
-                                                          int K, size_t sa, size_t sb, size_t sc,
-                                                          float alpha, int lower) {
+// Batched C = alpha op(A) op(B) (+ C when acc) with op(A) [M x K] stored as
+// A[m][k] (TA = false) or A[k][m] (TA = true), op(B) [K x N] stored as B[k][n]
+// (TB = false) or B[n][k] (TB = true), leading dimensions lda, ldb, ldc, and
+// an optional mask on C (1: keep n <= m, 2: keep n < m).  64 x 64 tile, 256
+// threads with 4 x 4 outputs each; the tile loads stay coalesced for either
+// storage; K a multiple of 16.
+template <bool TA, bool TB>
+__global__ __launch_bounds__(256) void bwd_gemm_kernel(const float* __restrict__ A,
+                                                       const float* __restrict__ B,
+                                                       float* __restrict__ Cm, int M, int N, int K,
+                                                       int lda, int ldb, int ldc, size_t sa,
+                                                       size_t sb, size_t sc, float alpha, int acc_c,
+                                                       int mask) {
   __shared__ float As[16][64 + 4];
   __shared__ float Bs[16][64 + 4];
   const int bt = blockIdx.x;  // batch on x: up to 2^31 - 1 blocks
@@ -460,9 +561,14 @@ __global__ __launch_bounds__(256) void bwd_nt_gemm_kernel(const float* __restric
   float acc[4][4] = {};
   for (int k0 = 0; k0 < K; k0 += 16) {
     for (int idx = threadIdx.x; idx < 64 * 16; idx += 256) {
-      const int rr = idx / 16, kk = idx % 16;
-      As[kk][rr] = m0 + rr < M ? a[(size_t)(m0 + rr) * K + k0 + kk] : 0.f;
-      Bs[kk][rr] = n0 + rr < N ? bb[(size_t)(n0 + rr) * K + k0 + kk] : 0.f;
+      int mm, kk;
+      if (TA) { kk = idx / 64; mm = idx % 64; } else { mm = idx / 16; kk = idx % 16; }
+      As[kk][mm] = m0 + mm < M ? (TA ? a[(size_t)(k0 + kk) * lda + m0 + mm]
+                                     : a[(size_t)(m0 + mm) * lda + k0 + kk]) : 0.f;
+      int nn;
+      if (TB) { nn = idx / 16; kk = idx % 16; } else { kk = idx / 64; nn = idx % 64; }
+      Bs[kk][nn] = n0 + nn < N ? (TB ? bb[(size_t)(n0 + nn) * ldb + k0 + kk]
+                                     : bb[(size_t)(k0 + kk) * ldb + n0 + nn]) : 0.f;
     }
     __syncthreads();
 #pragma unroll
@@ -486,7 +592,11 @@ __global__ __launch_bounds__(256) void bwd_nt_gemm_kernel(const float* __restric
 #pragma unroll
     for (int y = 0; y < 4; ++y) {
       const int m = m0 + ty * 4 + x, nn = n0 + tx * 4 + y;
-      if (m < M && nn < N) c[(size_t)m * N + nn] = (lower && nn > m) ? 0.f : alpha * acc[x][y];
+      if (m < M && nn < N) {
+        const bool keep = mask == 0 || (mask == 1 ? nn <= m : nn < m);
+        const float v = keep ? alpha * acc[x][y] : 0.f;
+        c[(size_t)m * ldc + nn] = acc_c ? c[(size_t)m * ldc + nn] + v : v;
+      }
     }
 }
 
@@ -534,77 +644,150 @@ struct BwdOut {
   float *dq, *dk, *dv, *dg, *dbeta;
 };
 
-// One thread per channel c: the pairwise terms of Bm and P (row-i parts
-// accumulated in this thread's own LDS column), the decays, the reverse
-// cumulative sum of dGamma, and the scatter to token-major outputs.
+// The pairwise terms of Bm and P, the decays, the reverse cumulative sum of
+// dGamma, and the scatter to token-major outputs.  2 D threads: thread c < D
+// walks the pairs (r, i <= r) row by row and keeps the row-r terms of channel
+// c in registers; thread D + c walks them column by column and keeps the
+// row-i terms, which it hands over through LDS (the row-i term of dGamma is
+// minus that of dk times k_i).  Each exponent is evaluated by both.
 template <int D, int C>
-__global__ __launch_bounds__(D) void bwd_final_kernel(Planes p, Geo geo, BwdOut out) {
+__global__ __launch_bounds__(2 * D) void bwd_final_kernel(Planes p, Geo geo, BwdOut out) {
   extern __shared__ float sm[];
   float* Ks = sm;               // [C][D]
   float* Gs = Ks + C * D;       // [C][D]
-  float* aK = Gs + C * D;       // [C][D] row-i terms of dk
-  float* aG = aK + C * D;       // [C][D] row-i terms of dGamma
-  const int b = blockIdx.x, c = threadIdx.x, H = geo.H;
+  float* Qs = Gs + C * D;       // [C][D]
+  float* xK = Qs + C * D;       // [C][D] row-i terms of dk
+  float* dBm = xK + C * D;      // [C][C]
+  float* dP = dBm + C * C;      // [C][C]
+  const int b = blockIdx.x, H = geo.H;
+  if (p.fast[b]) return;  // bwd_final_fast_kernel
+  const int c = threadIdx.x % D, half = threadIdx.x / D;
   const int gch = b / H, h = b % H;
   int n, t0, len;
   chunk_of<C>(geo, gch, n, t0, len);
   const size_t pcd = (size_t)b * C * D, pcc = (size_t)b * C * C;
-  for (int r = 0; r < C; ++r) {
-    Ks[r * D + c] = p.K[pcd + r * D + c];
-    Gs[r * D + c] = p.Gam[pcd + r * D + c];
-    aK[r * D + c] = 0.f;
-    aG[r * D + c] = 0.f;
+  for (int idx = threadIdx.x; idx < C * D; idx += 2 * D) {
+    Ks[idx] = p.K[pcd + idx];
+    Gs[idx] = p.Gam[pcd + idx];
+    Qs[idx] = p.Q[pcd + idx];
   }
-  const float* dBm = p.dBm + pcc;
-  const float* dP = p.dP + pcc;
-  const float gn = p.gn[(size_t)b * D + c];
-  float dgn = 0.f;  // rowsum(dS' * S) for channel c
+  for (int idx = threadIdx.x; idx < C * C; idx += 2 * D) {
+    dBm[idx] = p.dBm[pcc + idx];
+    dP[idx] = p.dP[pcc + idx];
+  }
+  __syncthreads();
+  if (half == 1) {
+    // column i: dk_i += sum_{r >= i} (dBm[r,i] k_r + dP[r,i] q_r) e_ri,
+    // dGamma_i -= sum_{r >= i} (dBm[r,i] k_r + dP[r,i] q_r) k_i e_ri
+    for (int i = 0; i < C; ++i) {
+      const float gi = Gs[i * D + c];
+      float ak0 = 0.f, ak1 = 0.f;
+      int r = i;
+      for (; r + 1 < C; r += 2) {
+        ak0 += (dBm[r * C + i] * Ks[r * D + c] + dP[r * C + i] * Qs[r * D + c]) *
+               __expf(Gs[r * D + c] - gi);
+        ak1 += (dBm[(r + 1) * C + i] * Ks[(r + 1) * D + c] + dP[(r + 1) * C + i] * Qs[(r + 1) * D + c]) *
+               __expf(Gs[(r + 1) * D + c] - gi);
+      }
+      if (r < C) ak0 += (dBm[r * C + i] * Ks[r * D + c] + dP[r * C + i] * Qs[r * D + c]) * __expf(Gs[r * D + c] - gi);
+      xK[i * D + c] = ak0 + ak1;
+    }
+  }
+  // Row-r terms go to dk and dg of the token (padded rows carry none), and
+  // are completed after the barrier by the same thread.
+  float kbsum = 0.f, dgn = 0.f;
+  if (half == 0) {
+    {
+      const float* S = p.S + ((size_t)b * D + c) * D;
+      const float* dS = p.dSn + ((size_t)b * D + c) * D;
+      for (int j = 0; j < D; ++j) dgn += S[j] * dS[j];
+    }
+    for (int r = 0; r < C; ++r) {
+      const float kr = Ks[r * D + c], qr = Qs[r * D + c], gr = Gs[r * D + c];
+      float dkr = 0.f, dqr = 0.f, dgr = 0.f;
+      for (int i = 0; i <= r; ++i) {
+        const float e = __expf(gr - Gs[i * D + c]);
+        const float ki = Ks[i * D + c];
+        const float wb = dBm[r * C + i] * e, wp = dP[r * C + i] * e;
+        dkr += wb * ki;
+        dqr += wp * ki;
+        dgr += (wb * kr + wp * qr) * ki;
+      }
+      const float ga = __expf(gr);
+      const size_t e0 = pcd + r * D + c;
+      const float dqt = p.dQt[e0], dkt = p.dKt[e0], dkb = p.dKb[e0];
+      const float kb = p.Kb[e0];
+      kbsum += dkb * kb;
+      if (r < len) {
+        const size_t ti = ((size_t)(t0 + r) * H + h) * D + c;
+        out.dq[ti] = dqt * ga + dqr;
+        out.dk[ti] = dkr + dkt * ga + dkb * __expf(Gs[(C - 1) * D + c] - gr);
+        out.dg[ti] = dgr + dqt * p.Qt[e0] + dkt * p.Kt[e0] - dkb * kb;
+      }
+    }
+  }
+  __syncthreads();
+  if (half == 0) {
+    const float gn = p.gn[(size_t)b * D + c];
+    float run = kbsum + dgn * gn;  // dGamma_n lands on the last row
+    for (int r = C - 1; r >= 0; --r) {
+      run -= xK[r * D + c] * Ks[r * D + c];
+      if (r < len) {
+        const size_t ti = ((size_t)(t0 + r) * H + h) * D + c;
+        run += out.dg[ti];
+        out.dg[ti] = run;
+        out.dk[ti] += xK[r * D + c];
+        out.dv[ti] = p.dR[pcd + r * D + c];
+      }
+    }
+    if (c < len) out.dbeta[(size_t)(t0 + c) * H + h] = p.db[(size_t)b * C + c];
+  }
+}
+
+// Moderate-decay chunks: the pairwise gradient terms are the products
+// Y1 = dBm Kh, Y2 = dP Kh, Y3 = dBm^T Kt + dP^T Qt (in the R, U, dU planes):
+// dq += gam Y2, dk += gam Y1 + exp(-Gamma) Y3, dGamma += Kt Y1 + Qt Y2 - Kh Y3.
+// One thread per channel.
+template <int D, int C>
+__global__ __launch_bounds__(D) void bwd_final_fast_kernel(Planes p, Geo geo, BwdOut out) {
+  const int b = blockIdx.x, c = threadIdx.x, H = geo.H;
+  if (!p.fast[b]) return;  // bwd_final_kernel
+  const int gch = b / H, h = b % H;
+  int n, t0, len;
+  chunk_of<C>(geo, gch, n, t0, len);
+  const size_t pcd = (size_t)b * C * D;
+  const float* Y1 = p.R + pcd;
+  const float* Y2 = p.U + pcd;
+  const float* Y3 = p.dU + pcd;
+  float dgn = 0.f, kbsum = 0.f;
   {
     const float* S = p.S + ((size_t)b * D + c) * D;
     const float* dS = p.dSn + ((size_t)b * D + c) * D;
     for (int j = 0; j < D; ++j) dgn += S[j] * dS[j];
   }
-  float kbsum = 0.f;  // sum_r dKb * Kb
-  for (int r = 0; r < C; ++r) {
-    const float kr = Ks[r * D + c], qr = p.Q[pcd + r * D + c], gr = Gs[r * D + c];
-    float dkr = 0.f, dqr = 0.f, dgr = 0.f;
-    for (int i = 0; i <= r; ++i) {
-      const float e = __expf(gr - Gs[i * D + c]);
-      const float ki = Ks[i * D + c];
-      const float wb = dBm[r * C + i] * e, wp = dP[r * C + i] * e;
-      dkr += wb * ki;
-      dqr += wp * ki;
-      const float t = wb * kr + wp * qr;
-      aK[i * D + c] += t;
-      const float z = t * ki;
-      dgr += z;
-      aG[i * D + c] -= z;
-    }
-    const float ga = __expf(gr);
-    const size_t e0 = pcd + r * D + c;
-    const float dqt = p.dQt[e0], dkt = p.dKt[e0], dkb = p.dKb[e0];
-    const float kb = p.Kb[e0];
-    kbsum += dkb * kb;
-    aK[r * D + c] += dkr + dkt * ga + dkb * __expf(Gs[(C - 1) * D + c] - gr);
-    aG[r * D + c] += dgr + dqt * p.Qt[e0] + dkt * p.Kt[e0] - dkb * kb;
-    if (r < len) out.dq[((size_t)(t0 + r) * H + h) * D + c] = dqt * ga + dqr;
-  }
-  aG[(C - 1) * D + c] += kbsum + dgn * gn;
-  float run = 0.f;
+  for (int r = 0; r < C; ++r) kbsum += p.dKb[pcd + r * D + c] * p.Kb[pcd + r * D + c];
+  const float gl = p.Gam[pcd + (C - 1) * D + c];
+  float run = kbsum + dgn * p.gn[(size_t)b * D + c];  // dGamma_n lands on the last row
   for (int r = C - 1; r >= 0; --r) {
-    run += aG[r * D + c];
+    const size_t e0 = pcd + r * D + c;
+    const float gr = p.Gam[e0], ga = __expf(gr);
+    const float dqt = p.dQt[e0], dkt = p.dKt[e0], dkb = p.dKb[e0];
+    const float y1 = Y1[r * D + c], y2 = Y2[r * D + c], y3 = Y3[r * D + c];
+    run += dqt * p.Qt[e0] + dkt * p.Kt[e0] - dkb * p.Kb[e0] + p.Kt[e0] * y1 + p.Qt[e0] * y2 -
+           p.Kh[e0] * y3;
     if (r < len) {
       const size_t ti = ((size_t)(t0 + r) * H + h) * D + c;
+      out.dq[ti] = (dqt + y2) * ga;
+      out.dk[ti] = (dkt + y1) * ga + dkb * __expf(gl - gr) + __expf(-gr) * y3;
       out.dg[ti] = run;
-      out.dk[ti] = aK[r * D + c];
-      out.dv[ti] = p.dR[pcd + r * D + c];
+      out.dv[ti] = p.dR[e0];
     }
   }
   if (c < len) out.dbeta[(size_t)(t0 + c) * H + h] = p.db[(size_t)b * C + c];
 }
 
 template <int D, int C>
-size_t final_lds() { return (size_t)4 * C * D * sizeof(float); }
+size_t final_lds() { return ((size_t)4 * C * D + 2 * C * C) * sizeof(float); }
 
 template <class in_t, int D, int C>
 hipError_t launch_backward_t(const BackwardArgs& a) {
@@ -638,37 +821,50 @@ hipError_t launch_backward_t(const BackwardArgs& a) {
     return hipGetLastError();
   }
   BwdIn in{a.q, a.k, a.v, a.g, a.beta, a.d_o};
+  BwdOut out{a.dq, a.dk, a.dv, a.dg, a.dbeta};
   hipLaunchKernelGGL((bwd_prep_kernel<in_t, D, C>), dim3(NB), dim3(256), 0, a.stream, in, p, geo);
   const size_t glds = (size_t)3 * C * (D + 1) * sizeof(float);
   e = hipFuncSetAttribute(reinterpret_cast<const void*>(&bwd_gram_kernel<D, C>),
                                      hipFuncAttributeMaxDynamicSharedMemorySize, (int)glds);
   if (e != hipSuccess) return e;
+  auto gemm = [&](auto kern, const float* A, const float* B, float* Cm, int M, int N, int K,
+                  int lda, int ldb, size_t sa, size_t sb, float alpha, int acc_c, int mask) {
+    const dim3 grid((unsigned)NB, (N + 63) / 64, (M + 63) / 64);
+    hipLaunchKernelGGL(kern, grid, dim3(256), 0, a.stream, A, B, Cm, M, N, K, lda, ldb, N, sa, sb,
+                       (size_t)M * N, alpha, acc_c, mask);
+  };
+  const size_t scd = (size_t)C * D, scc = (size_t)C * C, sdd = (size_t)D * D;
+  auto NT = bwd_gemm_kernel<false, true>;
+  auto NN = bwd_gemm_kernel<false, false>;
+  auto TN = bwd_gemm_kernel<true, false>;
+  // Grams of the moderate-decay chunks, then the others pair by pair.
+  gemm(NT, p.Kt, p.Kh, p.Bm, C, C, D, D, D, scd, scd, 1.f, 0, 2);  // strict_tril(Kt Kh^T)
+  gemm(NT, p.Qt, p.Kh, p.P, C, C, D, D, D, scd, scd, 1.f, 0, 1);   // tril(Qt Kh^T)
   hipLaunchKernelGGL((bwd_gram_kernel<D, C>), dim3(NB), dim3(256), glds, a.stream, p, (int)NB);
   hipLaunchKernelGGL((bwd_solve_kernel<C>), dim3(NB), dim3(64), 0, a.stream, p);
   hipLaunchKernelGGL((bwd_fwd_states_kernel<D, C>), dim3(serial), dim3(256), flds_s, a.stream, p,
                      geo, a.initial_state);
   hipLaunchKernelGGL((bwd_bwd_states_kernel<D, C>), dim3(serial), dim3(256), blds_s, a.stream, p,
                      geo, a.d_final_state, a.d_initial_state);
-  auto gemm = [&](const float* A, const float* B, float* Cm, int M, int N, float alpha,
-                  int lower) {
-    const dim3 grid((unsigned)NB, (N + 63) / 64, (M + 63) / 64);
-    hipLaunchKernelGGL(bwd_nt_gemm_kernel, grid, dim3(256), 0, a.stream, A, B, Cm, M, N, D,
-                       (size_t)M * D, (size_t)N * D, (size_t)M * N, alpha, lower);
-  };
   // p.S and p.dSn are [D][D] per chunk and head: the B operand "rows" are the
   // key channels, contracted over the value columns.
-  gemm(p.dO, p.S, p.dQt, C, D, 1.f, 0);    // dQt = dO S^T
-  gemm(p.U, p.dSn, p.dKb, C, D, 1.f, 0);   // dKb = U dS'^T
-  gemm(p.dR, p.S, p.dKt, C, D, -1.f, 0);   // dKt = -dR S^T
-  gemm(p.dU, p.R, p.dT, C, C, 1.f, 0);     // dT = dU R^T
-  gemm(p.dO, p.U, p.dP, C, C, 1.f, 1);     // dP = tril(dO U^T)
+  gemm(NT, p.dO, p.S, p.dQt, C, D, D, D, D, scd, sdd, 1.f, 0, 0);   // dQt = dO S^T
+  gemm(NT, p.U, p.dSn, p.dKb, C, D, D, D, D, scd, sdd, 1.f, 0, 0);  // dKb = U dS'^T
+  gemm(NT, p.dR, p.S, p.dKt, C, D, D, D, D, scd, sdd, -1.f, 0, 0);  // dKt = -dR S^T
+  gemm(NT, p.dU, p.R, p.dT, C, C, D, D, D, scd, scd, 1.f, 0, 0);    // dT = dU R^T
+  gemm(NT, p.dO, p.U, p.dP, C, C, D, D, D, scd, scd, 1.f, 0, 1);    // dP = tril(dO U^T)
   hipLaunchKernelGGL((bwd_cc_kernel<C>), dim3(NB), dim3(256), 0, a.stream, p);
+  // Pairwise gradient terms of the moderate-decay chunks (R, U, dU are free).
+  gemm(NN, p.dBm, p.Kh, p.R, C, D, C, C, D, scc, scd, 1.f, 0, 0);   // Y1 = dBm Kh
+  gemm(NN, p.dP, p.Kh, p.U, C, D, C, C, D, scc, scd, 1.f, 0, 0);    // Y2 = dP Kh
+  gemm(TN, p.dBm, p.Kt, p.dU, C, D, C, C, D, scc, scd, 1.f, 0, 0);  // Y3 = dBm^T Kt
+  gemm(TN, p.dP, p.Qt, p.dU, C, D, C, C, D, scc, scd, 1.f, 1, 0);   //    + dP^T Qt
+  hipLaunchKernelGGL((bwd_final_fast_kernel<D, C>), dim3(NB), dim3(D), 0, a.stream, p, geo, out);
   const size_t flds = final_lds<D, C>();
   e = hipFuncSetAttribute(reinterpret_cast<const void*>(&bwd_final_kernel<D, C>),
                           hipFuncAttributeMaxDynamicSharedMemorySize, (int)flds);
   if (e != hipSuccess) return e;
-  BwdOut out{a.dq, a.dk, a.dv, a.dg, a.dbeta};
-  hipLaunchKernelGGL((bwd_final_kernel<D, C>), dim3(NB), dim3(D), flds, a.stream, p, geo, out);
+  hipLaunchKernelGGL((bwd_final_kernel<D, C>), dim3(NB), dim3(2 * D), flds, a.stream, p, geo, out);
   return hipGetLastError();
 }
 

@@ -25,9 +25,9 @@
 // Swish and L2 normalisation of q and k, Swish of v and the sigmoid of beta on
 // the way in, and with a gate the head-wise RMSNorm times sigmoid(gate) on the
 // way out.  The norms of q and k are scalars per (n, h), so the reductions run
-// on the un-normalised values and are rescaled once the norms are known.  The
-// carried convolution inputs are read before the block barrier and shifted
-// after it, by one thread per row (q, k) or column (v).
+// on the un-normalised values and are rescaled once the norms are known.  One
+// thread per (tensor, channel) convolves and shifts that channel's carried
+// inputs; the results reach the other threads through LDS.
 #include "kda_device.hpp"
 #include "kda_launch.hpp"
 
@@ -85,25 +85,47 @@ __global__ __launch_bounds__(256) void decode_step_kernel(
   }
   float r[4] = {0, 0, 0, 0}, p[4] = {0, 0, 0, 0}, kq = 0.f, nq = 0.f, nk = 0.f;
   const int W1 = LAYER ? lp.conv_w - 1 : -1;
-  const int hh = LAYER ? nh % lp.H : 0;
-  // convolved input at row / column i of tensor x, new value xn
-  auto conv = [&](int x, int i, float xn) {
-    const float* wr = lp.cw[x] + ((size_t)hh * DK + i) * (W1 + 1);
-    const in_t* st = reinterpret_cast<const in_t*>(lp.cs_in[x]);
-    float acc = wr[W1] * xn;
-    for (int j = 0; j < W1; ++j)
-      acc += wr[j] * (st ? (float)st[((size_t)nh * W1 + j) * DK + i] : 0.f);
-    return acc;
-  };
+  // Short convolution: each (tensor, channel) of this (n, h) is convolved by
+  // one thread, which also shifts that channel's carried inputs (it alone
+  // reads them), and published through LDS.
+  __shared__ float cv[LAYER ? 3 : 1][LAYER ? DK : 1];
+  if (LAYER && W1 >= 0) {
+    const int hh = nh % lp.H;
+    for (int item = t; item < 3 * DK; item += 256) {
+      const int x = item / DK, i = item % DK;
+      const in_t* src = (x == 0 ? q : x == 1 ? k : v) + tok * DK;
+      const float xn = (float)src[i];
+      const float* wr = lp.cw[x] + ((size_t)hh * DK + i) * (W1 + 1);
+      const in_t* in = reinterpret_cast<const in_t*>(lp.cs_in[x]);
+      in_t* out = reinterpret_cast<in_t*>(lp.cs_out[x]);
+      const size_t b0 = (size_t)nh * W1 * DK + i;
+      float old[3];
+#pragma unroll
+      for (int j = 0; j < 3; ++j) old[j] = (j < W1 && in) ? (float)in[b0 + (size_t)j * DK] : 0.f;
+      float acc = wr[W1] * xn;
+#pragma unroll
+      for (int j = 0; j < 3; ++j)
+        if (j < W1) acc += wr[j] * old[j];
+      cv[x][i] = acc;
+      if (out && W1 > 0) {
+#pragma unroll
+        for (int j = 0; j < 2; ++j)
+          if (j + 1 < W1) out[b0 + (size_t)j * DK] = (in_t)old[j + 1];  // exact: old came from in_t
+        out[b0 + (size_t)(W1 - 1) * DK] = src[i];
+      }
+    }
+    __syncthreads();
+  }
+  const bool conv = LAYER && W1 >= 0;
 #pragma unroll
   for (int m = 0; m < RPT; ++m) {
     const int i = rg + RG * m;
-    kk[m] = (float)kp[i];
-    qq[m] = (float)qp[i];
-    if (LAYER && W1 >= 0) {
-      kk[m] = conv(1, i, kk[m]);
-      qq[m] = conv(0, i, qq[m]);
-    }
+    kk[m] = conv ? cv[LAYER ? 1 : 0][i] : (float)kp[i];
+    qq[m] = conv ? cv[0][i] : (float)qp[i];
+  }
+#pragma unroll
+  for (int m = 0; m < RPT; ++m) {
+    const int i = rg + RG * m;
     if (LAYER && lp.prologue) {
       kk[m] = swish_d(kk[m]);
       qq[m] = swish_d(qq[m]);
@@ -139,10 +161,7 @@ __global__ __launch_bounds__(256) void decode_step_kernel(
   const in_t* vp = v + tok * DV + 4 * cg;
   float vv[4];
 #pragma unroll
-  for (int c = 0; c < 4; ++c) {
-    vv[c] = (float)vp[c];
-    if (LAYER && W1 >= 0) vv[c] = conv(2, 4 * cg + c, vv[c]);
-  }
+  for (int c = 0; c < 4; ++c) vv[c] = conv ? cv[LAYER ? 2 : 0][4 * cg + c] : (float)vp[c];
   const int w = t >> 6;
   if ((t & 63) < TPR) {
 #pragma unroll
@@ -164,28 +183,6 @@ __global__ __launch_bounds__(256) void decode_step_kernel(
   }
   kq = red[0][cg][8] + red[1][cg][8] + red[2][cg][8] + red[3][cg][8];
 
-  if (LAYER && W1 > 0) {
-    // Every read of the carried inputs happened before the barrier above.
-    auto shift = [&](int x, int i, const in_t* src) {
-      in_t* out = reinterpret_cast<in_t*>(lp.cs_out[x]);
-      if (!out) return;
-      const in_t* in = reinterpret_cast<const in_t*>(lp.cs_in[x]);
-      const size_t b0 = (size_t)nh * W1 * DK + i;
-      for (int j = 0; j + 1 < W1; ++j) out[b0 + (size_t)j * DK] = in ? in[b0 + (size_t)(j + 1) * DK] : in_t(0.f);
-      out[b0 + (size_t)(W1 - 1) * DK] = src[i];
-    };
-    if (cg == 0) {
-#pragma unroll
-      for (int m = 0; m < RPT; ++m) {
-        shift(0, rg + RG * m, qp);
-        shift(1, rg + RG * m, kp);
-      }
-    }
-    if (rg == 0) {
-#pragma unroll
-      for (int c = 0; c < 4; ++c) shift(2, 4 * cg + c, v + tok * DV);
-    }
-  }
   float b = beta[tok];
   if (LAYER && lp.prologue) {
     // L2 normalisation: scale the reductions by 1/|q|, 1/|k| (floored).

@@ -110,3 +110,30 @@ def test_backward_strong_decay(kda):
     x = I.draw_tokens(rng, 150, 2, 64, 64, "f32", g_scale=5.0)
     errs = run_case(kda, x, 64, seed=2)
     assert max(errs.values()) <= TOL["f32"], errs
+
+
+def test_backward_full_size_sampled_heads(kda):
+    """The headline shape (B=1, T=4096, H=32, d=128, bf16, chunk 64, initial
+    state and final-state gradient), all heads on the GPU; the oracle
+    replays two sampled heads over the whole sequence."""
+    say("backward full size T=4096 H=32, sampled heads 0 and 19")
+    T, H, D = 4096, 32, 128
+    rng = np.random.default_rng(54)
+    x = I.draw_tokens(rng, T, H, D, D, "bf16")
+    s0 = I.draw_states(rng, 1, H, D, D)
+    do = rng.standard_normal((T, H, D)).astype(np.float32)
+    dF = rng.standard_normal((1, H, D, D)).astype(np.float32)
+    got = kda.backward(tdev(x.q, torch.bfloat16)[None], tdev(x.k, torch.bfloat16)[None],
+                       tdev(x.v, torch.bfloat16)[None], tdev(x.g)[None], tdev(x.beta)[None],
+                       tdev(do)[None], tdev(s0), tdev(dF), chunk_size=64)
+    torch.cuda.synchronize()
+    hs = [0, 19]
+    ref = oracle.kda_backward(x.q[:, hs], x.k[:, hs], x.v[:, hs], x.g[:, hs], x.beta[:, hs],
+                              do[:, hs], dF[:, hs], s0[:, hs])
+    errs = {}
+    for name, a, r in zip(NAMES, got, ref):
+        a = host(a)
+        a = a[:, hs] if name == "dS0" else a[0][:, hs]
+        errs[name] = rel(a, r)
+    say("  " + "  ".join(f"{k} {v:.2e}" for k, v in errs.items()))
+    assert max(errs.values()) <= TOL["bf16"], errs
