@@ -18,6 +18,9 @@ Functions
 ``short_conv``         causal depthwise convolution over the tokens of each
                        sequence, with a carried state of the last inputs.
 ``kda_layer_conv``     short convolution of q, k, v, then ``kda_layer``.
+``dplr_recurrent``     the general diagonal-plus-low-rank recurrence
+                       S_t = (Diag(exp g_t) - a_t b_t^T) S_{t-1} + k_t v_t^T.
+``dplr_explicit``      the same by explicit d_k x d_k transition matrices.
 ``kda_backward``       gradients of <dO, o> + <dS_N, S_N> with respect to q, k,
                        v, g, beta and the initial state: reverse-mode through
                        the token recurrence, written out by hand (float64).
@@ -47,6 +50,10 @@ Sources (pages this package follows):
     W <= 4 with no bias, restarted at every sequence start from a carried
     state (zeros when none is given).
 
+  * General DPLR: zeroshot.it.com deep-dive, section 3.2 "DPLR Structure"
+    (the update (D_t - a_t b_t^T) S_{t-1} + k_t v_t^T, with KDA the case
+    a_t = beta_t k_t, b_t = k_t * alpha_t); greeksharifa.github.io summary,
+    section 6.2 "Relation to DPLR".
   * Backward pass: the pages only say the chunkwise form also serves training
     (greeksharifa.github.io summary, sections 3.1 and 6.3; zeroshot.it.com
     deep-dive, section 4); the gradients here are the chain rule applied to
@@ -444,3 +451,53 @@ def kda_backward(q, k, v, g, beta, do, dfinal=None, initial_state=None, cu_seqle
                 dS = alpha[t][:, :, None] * dSp
         dS0[n] = dS
     return dq, dk_, dv_, dg, db, dS0
+
+
+def dplr_recurrent(q, k, v, a, b, g, initial_state=None, cu_seqlens=None):
+    """General DPLR recurrence, token by token, float64, all heads at once:
+
+        S_t = Diag(exp g_t) S_{t-1} - a_t (b_t^T S_{t-1}) + k_t v_t^T,
+        o_t = S_t^T q_t
+
+    q, k, a, b, g: [T, H, dk]; v: [T, H, dv]; initial_state [N, H, dk, dv] or
+    None.  Returns (o [T, H, dv], final [N, H, dk, dv])."""
+    q, k, v, a, b, g = (np.asarray(x, dtype=np.float64) for x in (q, k, v, a, b, g))
+    T, H, dk = q.shape
+    dv = v.shape[2]
+    cu = np.array([0, T]) if cu_seqlens is None else np.asarray(cu_seqlens, dtype=np.int64)
+    N = len(cu) - 1
+    S0 = (np.zeros((N, H, dk, dv)) if initial_state is None
+          else np.asarray(initial_state, dtype=np.float64))
+    o = np.zeros((T, H, dv))
+    fin = np.zeros((N, H, dk, dv))
+    for n in range(N):
+        S = S0[n].copy()
+        for t in range(int(cu[n]), int(cu[n + 1])):
+            bS = np.einsum("hi,hij->hj", b[t], S)
+            S = (np.exp(g[t])[:, :, None] * S - a[t][:, :, None] * bS[:, None, :]
+                 + k[t][:, :, None] * v[t][:, None, :])
+            o[t] = np.einsum("hij,hi->hj", S, q[t])
+        fin[n] = S
+    return o, fin
+
+
+def dplr_explicit(q, k, v, a, b, g, S0):
+    """The same for ONE head by explicit transition matrices
+    A_t = Diag(alpha_t) - a_t b_t^T:  S_t = A_t S_{t-1} + k_t v_t^T,
+    o_t = S_t^T q_t.  ``g`` is the log-decay for float input; for exact
+    evaluation pass object arrays of fractions.Fraction and ``g`` holding
+    alpha itself (exp of a rational is not rational)."""
+    T, dk = q.shape
+    dv = v.shape[1]
+    exact = np.asarray(g).dtype == object
+    S = np.array(S0, dtype=object if exact else np.float64)
+    o = np.empty((T, dv), dtype=S.dtype)
+    for t in range(T):
+        alpha = g[t] if exact else np.exp(np.asarray(g[t], dtype=np.float64))
+        A = np.empty((dk, dk), dtype=S.dtype)
+        for i in range(dk):
+            for j in range(dk):
+                A[i, j] = (alpha[i] if i == j else 0) - a[t][i] * b[t][j]
+        S = A.dot(S) + np.outer(k[t], v[t])
+        o[t] = S.T.dot(q[t])
+    return o, S
