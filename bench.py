@@ -168,7 +168,47 @@ def other_workloads(torch, kda, I, dev):
     out["tiny_fp32"] = {"workload": "kda_prefill B=1 H=1 T=256 d=64 fp32", **tiny}
     out["layer"] = layer_workloads(torch, kda, I, dev)
     out["backward"] = backward_workload(torch, kda, I, dev)
+    out["dplr"] = dplr_workloads(torch, kda, I, dev)
     return out
+
+
+def dplr_workloads(torch, kda, I, dev):
+    """General DPLR against KDA on the same KDA inputs (a = beta k,
+    b = exp(g) k): dplr_prefill (four intra-chunk matrices), KDA through the
+    same fp32 chunk pipeline (kda_prefill_chunk_fp32, two matrices) and the
+    optimized kda_prefill.  B=1, 16 heads (the setting of the pages' kernel
+    comparison) at 4K and 64K tokens, and the headline 32-head 4K shape."""
+    res = []
+    for T, H in ((4096, 16), (65536, 16), (4096, 32)):
+        d = P_D
+        q, k, v, g, b = I.device_tokens(torch, T, H, d, d, 6006 + T + H, dev)
+        a = (b[..., None] * k.float()).to(torch.bfloat16)
+        bb = (torch.exp(g) * k.float()).to(torch.bfloat16)
+        o = torch.empty((1, T, H, d), dtype=torch.float32, device=dev)
+        fin = torch.empty((1, H, d, d), dtype=torch.float32, device=dev)
+        ws = torch.empty(kda.dplr_workspace_size(1, T, H, d, 1, P_C), dtype=torch.uint8,
+                         device=dev)
+        reps = 3 if T > 8192 else 10
+        t_dplr = time_calls(torch, lambda: kda.dplr_prefill(q, a, v, a, bb, g, None, chunk_size=P_C,
+                                                            o=o, final_state=fin, workspace=ws),
+                            reps)
+        t_tied = time_calls(torch, lambda: kda.prefill_chunk_fp32(q, k, v, g, b, None,
+                                                                  chunk_size=P_C, o=o,
+                                                                  final_state=fin, workspace=ws),
+                            reps)
+        del ws
+        ws2 = torch.empty(kda.workspace_size(1, T, H, d, 1, P_C, kda.KDA_BF16), dtype=torch.uint8,
+                          device=dev)
+        t_kda = time_calls(torch, lambda: kda.prefill(q, k, v, g, b, None, chunk_size=P_C, o=o,
+                                                      final_state=fin, workspace=ws2), reps)
+        res.append({"T": T, "H": H, "d": d, "dplr_ms": round(t_dplr * 1e3, 3),
+                    "kda_chunk_fp32_ms": round(t_tied * 1e3, 3),
+                    "kda_prefill_ms": round(t_kda * 1e3, 3),
+                    "dplr_over_kda_same_pipeline": round(t_dplr / t_tied, 2),
+                    "dplr_over_kda_prefill": round(t_dplr / t_kda, 2)})
+        del q, k, v, g, b, a, bb, o, fin, ws2
+        torch.cuda.empty_cache()
+    return {"workload": "general DPLR vs KDA on the same inputs, bf16, chunk 64", "cases": res}
 
 
 def backward_workload(torch, kda, I, dev):

@@ -328,4 +328,85 @@ kda_status kda_backward(const void* q, const void* k, const void* v, const float
   return kda::launch_backward(a) == hipSuccess ? KDA_OK : KDA_ERR_HIP;
 }
 
+kda_status dplr_prefill_workspace_size(int B, int T, int H, int Dk, int Dv, int num_seqs,
+                                       const int32_t* cu_seqlens_host, int chunk_size,
+                                       size_t* bytes) {
+  if (bytes == nullptr || H < 1) return KDA_ERR_INVALID_ARG;
+  if (!supported_head(Dk, Dv) || !supported_chunk(chunk_size)) return KDA_ERR_UNSUPPORTED;
+  int64_t chunks = 0;
+  kda_status st = seq_layout(B, T, num_seqs, cu_seqlens_host, cu_seqlens_host, chunk_size, &chunks);
+  if (st != KDA_OK) return st;
+  *bytes = kda::dplr_workspace_bytes(chunks, num_seqs, H, Dk, chunk_size);
+  return KDA_OK;
+}
+
+static kda_status dplr_impl(bool tied, const void* q, const void* k, const void* v,
+                            const void* a_, const void* b_, const float* g, const float* beta,
+                            float* o, const float* initial_state, float* final_state,
+                            const int32_t* cu_seqlens, const int32_t* cu_seqlens_host, int B,
+                            int T, int H, int Dk, int Dv, int num_seqs, int chunk_size,
+                            kda_dtype in_dtype, void* workspace, size_t workspace_bytes,
+                            void* stream) {
+  if (H < 1 || !valid_dtype(in_dtype)) return KDA_ERR_INVALID_ARG;
+  if (!supported_head(Dk, Dv) || !supported_chunk(chunk_size)) return KDA_ERR_UNSUPPORTED;
+  const void* ptrs[] = {q, k, v, a_, b_, g, beta, o, initial_state, final_state, cu_seqlens};
+  for (const void* p : ptrs)
+    if (p && !aligned(p, 16)) return KDA_ERR_INVALID_ARG;
+  int64_t chunks = 0;
+  kda_status st = seq_layout(B, T, num_seqs, cu_seqlens, cu_seqlens_host, chunk_size, &chunks);
+  if (st != KDA_OK) return st;
+  if ((int64_t)B * T > 0 && (!q || !k || !v || !g || !o || (tied ? !beta : (!a_ || !b_))))
+    return KDA_ERR_INVALID_ARG;
+  if (chunks * (int64_t)H > INT32_MAX) return KDA_ERR_INVALID_ARG;
+  const size_t need = kda::dplr_workspace_bytes(chunks, num_seqs, H, Dk, chunk_size);
+  if (workspace == nullptr || workspace_bytes < need) return KDA_ERR_WORKSPACE;
+  if (!aligned(workspace, 256)) return KDA_ERR_INVALID_ARG;
+  kda::DplrArgs a;
+  a.q = q;
+  a.k = k;
+  a.v = v;
+  a.a = a_;
+  a.b = b_;
+  a.g = g;
+  a.beta = beta;
+  a.o = o;
+  a.initial_state = initial_state;
+  a.final_state = final_state;
+  a.cu_seqlens = cu_seqlens;
+  a.num_seqs = num_seqs;
+  a.seq_len = cu_seqlens ? 0 : T;
+  a.total_tokens = B * T;
+  a.total_chunks = (int)chunks;
+  a.H = H;
+  a.D = Dk;
+  a.chunk = chunk_size;
+  a.in_bf16 = in_dtype == KDA_BF16;
+  a.tied = tied;
+  a.workspace = workspace;
+  a.stream = reinterpret_cast<hipStream_t>(stream);
+  return kda::launch_dplr(a) == hipSuccess ? KDA_OK : KDA_ERR_HIP;
+}
+
+kda_status dplr_prefill(const void* q, const void* k, const void* v, const void* a,
+                        const void* b, const float* g, float* o, const float* initial_state,
+                        float* final_state, const int32_t* cu_seqlens,
+                        const int32_t* cu_seqlens_host, int B, int T, int H, int Dk, int Dv,
+                        int num_seqs, int chunk_size, kda_dtype in_dtype, void* workspace,
+                        size_t workspace_bytes, void* stream) {
+  return dplr_impl(false, q, k, v, a, b, g, nullptr, o, initial_state, final_state, cu_seqlens,
+                   cu_seqlens_host, B, T, H, Dk, Dv, num_seqs, chunk_size, in_dtype, workspace,
+                   workspace_bytes, stream);
+}
+
+kda_status kda_prefill_chunk_fp32(const void* q, const void* k, const void* v, const float* g,
+                                  const float* beta, float* o, const float* initial_state,
+                                  float* final_state, const int32_t* cu_seqlens,
+                                  const int32_t* cu_seqlens_host, int B, int T, int H, int Dk,
+                                  int Dv, int num_seqs, int chunk_size, kda_dtype in_dtype,
+                                  void* workspace, size_t workspace_bytes, void* stream) {
+  return dplr_impl(true, q, k, v, nullptr, nullptr, g, beta, o, initial_state, final_state,
+                   cu_seqlens, cu_seqlens_host, B, T, H, Dk, Dv, num_seqs, chunk_size, in_dtype,
+                   workspace, workspace_bytes, stream);
+}
+
 }  // extern "C"

@@ -36,23 +36,23 @@
 // exponent of its difference.
 //
 // Kernels (one launch each, in order):
-//   bwd_table_kernel      first global chunk of each packed sequence
+//   chunk_table_kernel    first global chunk of each packed sequence
 //   bwd_prep_kernel       per (chunk, head): padded fp32 copies, Gamma, Qt, Kt,
 //                         Kb, Kh and the span verdict
-//   bwd_gemm_kernel       batched fp32 products (Grams, contractions over value
+//   fp32_gemm_kernel      batched fp32 products (Grams, contractions over value
 //                         columns, pairwise gradient terms)
 //   bwd_gram_kernel       per strong-decay (chunk, head): Bm and P pair by pair
 //   bwd_solve_kernel      per (chunk, head): M by forward substitution, T
 //   bwd_fwd_states_kernel per (sequence, head, 16 value columns), serial over
 //                         chunks: the entering state S of every chunk, R, U
 //   bwd_bwd_states_kernel the same, reverse: dS' of every chunk, dU, dR, dS0
-//   bwd_nt_gemm_kernel    batched fp32 products over value columns
 //   bwd_cc_kernel         per (chunk, head): the C x C algebra of M and A
 //   bwd_final_fast_kernel per moderate-decay (chunk, head): decays, reverse
 //                         cumsum, scatter to the token-major outputs
 //   bwd_final_kernel      the same for strong-decay chunks, with the pairwise
 //                         gradient terms evaluated pair by pair
 #include "kda_device.hpp"
+#include "kda_fp32_chunks.hpp"
 #include "kda_launch.hpp"
 
 namespace kda {
@@ -73,8 +73,6 @@ struct Planes {
   float *gn;                                                                      // [D]
   int32_t* fast;                                                                  // [1] per (chunk, head)
 };
-
-size_t a256(size_t x) { return (x + 255) / 256 * 256; }
 
 size_t plane_bytes(size_t NB, int C, int D) {
   const size_t cd = a256(NB * C * D * 4), cc = a256(NB * C * C * 4), dd = a256(NB * D * D * 4);
@@ -97,81 +95,6 @@ Planes carve(char* p, size_t NB, int C, int D) {
   p += a256(NB * D * 4);
   x.fast = reinterpret_cast<int32_t*>(p);
   return x;
-}
-
-// Sequence geometry.  Fixed length: num_seqs sequences of seq_len tokens;
-// varlen: cu (device) and off[n] = first global chunk of sequence n.
-struct Geo {
-  const int32_t* cu;
-  const int32_t* off;  // varlen only
-  int num_seqs, seq_len, total_tokens, H, nchunks;
-};
-
-__device__ __forceinline__ int clampi(int x, int lo, int hi) { return x < lo ? lo : (x > hi ? hi : x); }
-
-template <int C>
-__device__ __forceinline__ void seq_of(const Geo& g, int n, int& bos, int& eos, int& base) {
-  if (g.cu) {
-    bos = clampi(g.cu[n], 0, g.total_tokens);
-    eos = clampi(g.cu[n + 1], bos, g.total_tokens);
-    base = g.off[n];
-  } else {
-    bos = n * g.seq_len;
-    eos = bos + g.seq_len;
-    base = n * ((g.seq_len + C - 1) / C);
-  }
-}
-
-// Global chunk -> (sequence, first token, length).
-template <int C>
-__device__ __forceinline__ void chunk_of(const Geo& g, int gch, int& n, int& t0, int& len) {
-  if (g.cu) {
-    int lo = 0, hi = g.num_seqs - 1;  // last n with off[n] <= gch
-    while (lo < hi) {
-      const int mid = (lo + hi + 1) >> 1;
-      if (g.off[mid] <= gch)
-        lo = mid;
-      else
-        hi = mid - 1;
-    }
-    n = lo;
-  } else {
-    n = clampi(gch / ((g.seq_len + C - 1) / C), 0, g.num_seqs - 1);
-  }
-  int bos, eos, base;
-  seq_of<C>(g, n, bos, eos, base);
-  t0 = clampi(bos + (gch - base) * C, bos, eos);
-  len = clampi(eos - t0, 0, C);
-}
-
-// off[n] = sum of the chunk counts of the sequences before n (block scan).
-__global__ __launch_bounds__(1024) void bwd_table_kernel(const int32_t* __restrict__ cu,
-                                                         int32_t* __restrict__ off, int num_seqs,
-                                                         int total_tokens, int C) {
-  __shared__ int part[1024];
-  const int t = threadIdx.x;
-  const int per = (num_seqs + 1023) / 1024;
-  const int n0 = t * per, n1 = min(n0 + per, num_seqs);
-  auto nch = [&](int n) {
-    const int b = clampi(cu[n], 0, total_tokens), e = clampi(cu[n + 1], b, total_tokens);
-    return (e - b + C - 1) / C;
-  };
-  int s = 0;
-  for (int n = n0; n < n1; ++n) s += nch(n);
-  part[t] = s;
-  __syncthreads();
-  for (int d = 1; d < 1024; d <<= 1) {  // inclusive scan
-    const int x = t >= d ? part[t - d] : 0;
-    __syncthreads();
-    part[t] += x;
-    __syncthreads();
-  }
-  int run = t ? part[t - 1] : 0;
-  for (int n = n0; n < n1; ++n) {
-    off[n] = run;
-    run += nch(n);
-  }
-  if (t == 1023) off[num_seqs] = part[1023];
 }
 
 struct BwdIn {
@@ -297,40 +220,6 @@ __global__ __launch_bounds__(64) void bwd_solve_kernel(Planes p) {
     const int r = idx / C, i = idx % C;
     p.M[pcc + idx] = X[r][i];
     p.T[pcc + idx] = X[r][i] * beta[i];
-  }
-}
-
-// The serial passes run their products on v_mfma_f32_16x16x4f32 (fp32
-// operands): lane l supplies A[m = l & 15][k = l >> 4] and B[k = l >> 4][n =
-// l & 15] and receives D rows 4 (l >> 4) + i of column l & 15.  Operands are
-// staged in LDS; a matrix read as A[m][k] = X[m][k] has row stride +4 floats,
-// one read transposed (A[m][k] = X[k][m]) +16, so the 64 lanes of a read hit
-// 64 different banks; 16-column blocks have stride 16.
-__device__ __forceinline__ f32x4 mfma4(float a, float b, f32x4 c) {
-  return __builtin_amdgcn_mfma_f32_16x16x4f32(a, b, c, 0, 0, 0);
-}
-
-// Stage ROWS x COLS floats (row-major) into LDS with row stride LD: every
-// load of the thread is issued before the first LDS store.
-template <int ROWS, int COLS, int LD>
-__device__ __forceinline__ void stage(float* dst, const float* __restrict__ src) {
-  constexpr int C4 = COLS / 4, N = (ROWS * C4 + 255) / 256;
-  static_assert(COLS % 4 == 0, "float4 rows");
-  f32x4 v[N];
-#pragma unroll
-  for (int x = 0; x < N; ++x) {
-    const int idx = threadIdx.x + 256 * x;
-    if (idx < ROWS * C4)
-      v[x] = *reinterpret_cast<const f32x4*>(src + (size_t)(idx / C4) * COLS + 4 * (idx % C4));
-  }
-#pragma unroll
-  for (int x = 0; x < N; ++x) {
-    const int idx = threadIdx.x + 256 * x;
-    if (idx < ROWS * C4) {
-      const int r = idx / C4, c = 4 * (idx % C4);
-#pragma unroll
-      for (int e = 0; e < 4; ++e) dst[r * LD + c + e] = v[x][e];
-    }
   }
 }
 
@@ -538,68 +427,6 @@ __global__ __launch_bounds__(256) void bwd_bwd_states_kernel(Planes p, Geo geo,
   }
 }
 
-// Batched C = alpha op(A) op(B) (+ C when acc) with op(A) [M x K] stored as
-// A[m][k] (TA = false) or A[k][m] (TA = true), op(B) [K x N] stored as B[k][n]
-// (TB = false) or B[n][k] (TB = true), leading dimensions lda, ldb, ldc, and
-// an optional mask on C (1: keep n <= m, 2: keep n < m).  64 x 64 tile, 256
-// threads with 4 x 4 outputs each; the tile loads stay coalesced for either
-// storage; K a multiple of 16.
-template <bool TA, bool TB>
-__global__ __launch_bounds__(256) void bwd_gemm_kernel(const float* __restrict__ A,
-                                                       const float* __restrict__ B,
-                                                       float* __restrict__ Cm, int M, int N, int K,
-                                                       int lda, int ldb, int ldc, size_t sa,
-                                                       size_t sb, size_t sc, float alpha, int acc_c,
-                                                       int mask) {
-  __shared__ float As[16][64 + 4];
-  __shared__ float Bs[16][64 + 4];
-  const int bt = blockIdx.x;  // batch on x: up to 2^31 - 1 blocks
-  const int m0 = blockIdx.z * 64, n0 = blockIdx.y * 64;
-  const float* a = A + bt * sa;
-  const float* bb = B + bt * sb;
-  const int tx = threadIdx.x % 16, ty = threadIdx.x / 16;
-  float acc[4][4] = {};
-  for (int k0 = 0; k0 < K; k0 += 16) {
-    for (int idx = threadIdx.x; idx < 64 * 16; idx += 256) {
-      int mm, kk;
-      if (TA) { kk = idx / 64; mm = idx % 64; } else { mm = idx / 16; kk = idx % 16; }
-      As[kk][mm] = m0 + mm < M ? (TA ? a[(size_t)(k0 + kk) * lda + m0 + mm]
-                                     : a[(size_t)(m0 + mm) * lda + k0 + kk]) : 0.f;
-      int nn;
-      if (TB) { nn = idx / 16; kk = idx % 16; } else { kk = idx / 64; nn = idx % 64; }
-      Bs[kk][nn] = n0 + nn < N ? (TB ? bb[(size_t)(n0 + nn) * ldb + k0 + kk]
-                                     : bb[(size_t)(k0 + kk) * ldb + n0 + nn]) : 0.f;
-    }
-    __syncthreads();
-#pragma unroll
-    for (int kk = 0; kk < 16; ++kk) {
-      float av[4], bv[4];
-#pragma unroll
-      for (int x = 0; x < 4; ++x) {
-        av[x] = As[kk][ty * 4 + x];
-        bv[x] = Bs[kk][tx * 4 + x];
-      }
-#pragma unroll
-      for (int x = 0; x < 4; ++x)
-#pragma unroll
-        for (int y = 0; y < 4; ++y) acc[x][y] += av[x] * bv[y];
-    }
-    __syncthreads();
-  }
-  float* c = Cm + bt * sc;
-#pragma unroll
-  for (int x = 0; x < 4; ++x)
-#pragma unroll
-    for (int y = 0; y < 4; ++y) {
-      const int m = m0 + ty * 4 + x, nn = n0 + tx * 4 + y;
-      if (m < M && nn < N) {
-        const bool keep = mask == 0 || (mask == 1 ? nn <= m : nn < m);
-        const float v = keep ? alpha * acc[x][y] : 0.f;
-        c[(size_t)m * ldc + nn] = acc_c ? c[(size_t)m * ldc + nn] + v : v;
-      }
-    }
-}
-
 // dM = dT Diag(beta); dbeta = colsum(M * dT) + rowsum(dA * Bm) with
 // dA = strict_tril(-M^T dM M^T); dBm = Diag(beta) dA.
 template <int C>
@@ -803,7 +630,7 @@ hipError_t launch_backward_t(const BackwardArgs& a) {
   geo.nchunks = a.total_chunks;
   Planes p = carve(ws + a256(sizeof(int32_t) * (a.num_seqs + 1)), NB, C, D);
   if (a.cu_seqlens)
-    hipLaunchKernelGGL(bwd_table_kernel, dim3(1), dim3(1024), 0, a.stream, a.cu_seqlens,
+    hipLaunchKernelGGL(chunk_table_kernel, dim3(1), dim3(1024), 0, a.stream, a.cu_seqlens,
                        const_cast<int32_t*>(geo.off), a.num_seqs, a.total_tokens, C);
   const int serial = a.num_seqs * a.H * (D / kCols);
   const size_t flds_s = sizeof(FwdLds<D, C>), blds_s = sizeof(BwdLds<D, C>);
@@ -834,9 +661,9 @@ hipError_t launch_backward_t(const BackwardArgs& a) {
                        (size_t)M * N, alpha, acc_c, mask);
   };
   const size_t scd = (size_t)C * D, scc = (size_t)C * C, sdd = (size_t)D * D;
-  auto NT = bwd_gemm_kernel<false, true>;
-  auto NN = bwd_gemm_kernel<false, false>;
-  auto TN = bwd_gemm_kernel<true, false>;
+  auto NT = fp32_gemm_kernel<false, true>;
+  auto NN = fp32_gemm_kernel<false, false>;
+  auto TN = fp32_gemm_kernel<true, false>;
   // Grams of the moderate-decay chunks, then the others pair by pair.
   gemm(NT, p.Kt, p.Kh, p.Bm, C, C, D, D, D, scd, scd, 1.f, 0, 2);  // strict_tril(Kt Kh^T)
   gemm(NT, p.Qt, p.Kh, p.P, C, C, D, D, D, scd, scd, 1.f, 0, 1);   // tril(Qt Kh^T)

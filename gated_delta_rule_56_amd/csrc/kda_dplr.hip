@@ -1,0 +1,394 @@
+// General diagonal-plus-low-rank (DPLR) chunked forward pass, gfx950, fp32.
+//
+//   S_t = (Diag(exp g_t) - a_t b_t^T) S_{t-1} + k_t v_t^T,   o_t = S_t^T q_t
+//
+// (zeroshot.it.com deep-dive, section 3.2 "DPLR Structure"; greeksharifa
+// summary, section 6.2 "Relation to DPLR": KDA is the case a = beta k,
+// b = k * alpha with the write beta k v^T, and needs two of the general
+// form's four intra-chunk matrices).  For a chunk of C rows (zero-padded; g = 0
+// on padded rows) entering with state S, Gamma = cumsum(g), Gamma' = Gamma - g
+// (decay up to the previous row), gam_n = exp(Gamma_{C-1}):
+//
+//   Qt = q e^Gamma,  Bt = b e^Gamma',  Ah = a e^-Gamma,  Kh = k e^-Gamma,
+//   Ab = a e^(Gamma_n - Gamma),  Kb = k e^(Gamma_n - Gamma)
+//   Aba = strict_tril(Bt Ah^T), Abk = strict_tril(Bt Kh^T),
+//   Aqa = tril(Qt Ah^T),        Aqk = tril(Qt Kh^T)
+//   M = (I + Aba)^{-1}
+//   U = -M (Bt S + Abk V)        (U row r = -b_r^T S_{r-1})
+//   O = Qt S + Aqa U + Aqk V,    S' = Diag(gam_n) S + Ab^T U + Kb^T V
+//
+// With the tied (KDA) structure a = k_w = beta k, b = alpha k, so Aba = Abk,
+// Aqa = Aqk and Ab = Kb; then U~ = U + V = M (V - Bt S) and O = Qt S + Aqa U~,
+// S' = Diag(gam_n) S + Ab^T U~: two Grams and two products fewer.  The tied
+// mode runs KDA through this same pipeline, the like-for-like baseline for the
+// general form's extra work.
+//
+// Grams of chunks whose decay span (max -Gamma_{C-1}) is at most 40 are
+// products of the factored operands; others are evaluated pair by pair with
+// the exact exponent of each difference.
+//
+// Kernels: chunk_table_kernel (varlen), dplr_prep_kernel, fp32_gemm_kernel
+// (Grams, then Wb = M Bt, the V terms), dplr_gram_kernel (strong decay),
+// dplr_solve_kernel (M), dplr_states_kernel (serial over chunks per
+// (sequence, head, 16 value columns), fp32 MFMA, writes o and the final state).
+#include "kda_device.hpp"
+#include "kda_fp32_chunks.hpp"
+#include "kda_launch.hpp"
+
+namespace kda {
+namespace {
+
+constexpr int kColsD = 16;
+constexpr float kSpanD = 40.f;
+
+struct DPlanes {
+  float *Q, *K, *V, *A, *B, *Gam, *G;   // padded inputs (A, B: the low-rank factors), Gamma, g
+  float *Qt, *Bt, *Ah, *Kh, *Ab, *Kb;   // decayed operands
+  float *Wb, *Y, *OV, *X;               // Wb = M Bt; Y = M V (tied) or -M Abk V; OV = Aqk V
+  float *Aba, *Abk, *Aqa, *Aqk, *M;     // [C][C]
+  float* gn;                            // [D]
+  int32_t* fast;
+};
+
+size_t dplr_plane_bytes(size_t NB, int C, int D) {
+  const size_t cd = a256(NB * C * D * 4), cc = a256(NB * C * C * 4);
+  return 17 * cd + 5 * cc + a256(NB * D * 4) + a256(NB * 4);
+}
+
+DPlanes dcarve(char* p, size_t NB, int C, int D) {
+  const size_t cd = a256(NB * C * D * 4), cc = a256(NB * C * C * 4);
+  DPlanes x;
+  float** cdp[] = {&x.Q, &x.K, &x.V, &x.A, &x.B, &x.Gam, &x.G, &x.Qt, &x.Bt,
+                   &x.Ah, &x.Kh, &x.Ab, &x.Kb, &x.Wb, &x.Y, &x.OV, &x.X};
+  for (float** f : cdp) { *f = reinterpret_cast<float*>(p); p += cd; }
+  float** ccp[] = {&x.Aba, &x.Abk, &x.Aqa, &x.Aqk, &x.M};
+  for (float** f : ccp) { *f = reinterpret_cast<float*>(p); p += cc; }
+  x.gn = reinterpret_cast<float*>(p);
+  p += a256(NB * D * 4);
+  x.fast = reinterpret_cast<int32_t*>(p);
+  return x;
+}
+
+struct DIn {
+  const void *q, *k, *v, *a, *b;  // a, b unused when tied
+  const float *g, *beta;          // beta used when tied
+};
+
+// Padded fp32 inputs, Gamma, the decayed operands and the span verdict.
+template <class in_t, int D, int C, bool TIED>
+__global__ __launch_bounds__(256) void dplr_prep_kernel(DIn in, DPlanes p, Geo geo) {
+  __shared__ float Gs[C][D + 1];
+  const int b = blockIdx.x, H = geo.H;
+  const int gch = b / H, h = b % H;
+  int n, t0, len;
+  chunk_of<C>(geo, gch, n, t0, len);
+  const size_t pcd = (size_t)b * C * D;
+  auto ld = [&](const void* ptr, size_t ti) { return (float)reinterpret_cast<const in_t*>(ptr)[ti]; };
+  for (int idx = threadIdx.x; idx < C * D; idx += 256) {
+    const int r = idx / D, c = idx % D;
+    const bool ok = r < len;
+    const size_t ti = ((size_t)(t0 + r) * H + h) * D + c;
+    const float kv = ok ? ld(in.k, ti) : 0.f;
+    const float gv = ok ? in.g[ti] : 0.f;
+    float av, bv;
+    if (TIED) {
+      const float be = ok ? in.beta[(size_t)(t0 + r) * H + h] : 0.f;
+      av = be * kv;                 // a = write key = beta k
+      bv = __expf(gv) * kv;         // b = alpha k
+    } else {
+      av = ok ? ld(in.a, ti) : 0.f;
+      bv = ok ? ld(in.b, ti) : 0.f;
+    }
+    p.Q[pcd + idx] = ok ? ld(in.q, ti) : 0.f;
+    p.K[pcd + idx] = TIED ? av : kv;  // the key that writes v
+    p.V[pcd + idx] = ok ? ld(in.v, ti) : 0.f;
+    p.A[pcd + idx] = av;
+    p.B[pcd + idx] = bv;
+    p.G[pcd + idx] = gv;
+    Gs[r][c] = gv;
+  }
+  __syncthreads();
+  if (threadIdx.x < D) {
+    const int c = threadIdx.x;
+    float s = 0.f;
+    for (int r = 0; r < C; ++r) {
+      s += Gs[r][c];
+      Gs[r][c] = s;
+    }
+    p.gn[(size_t)b * D + c] = __expf(s);
+  }
+  __syncthreads();
+  if (threadIdx.x < 64) {
+    bool big = false;
+    for (int c = threadIdx.x; c < D; c += 64) big |= Gs[C - 1][c] < -kSpanD;
+    big = __any(big);
+    if (threadIdx.x == 0) p.fast[b] = big ? 0 : 1;
+  }
+  for (int idx = threadIdx.x; idx < C * D; idx += 256) {
+    const int r = idx / D, c = idx % D;
+    const float gm = Gs[r][c], gl = Gs[C - 1][c];
+    const float ea = __expf(gm), eh = __expf(-gm), eb = __expf(gl - gm);
+    const float av = p.A[pcd + idx], kv = p.K[pcd + idx];
+    p.Gam[pcd + idx] = gm;
+    p.Qt[pcd + idx] = p.Q[pcd + idx] * ea;
+    p.Bt[pcd + idx] = p.B[pcd + idx] * __expf(gm - p.G[pcd + idx]);
+    p.Ah[pcd + idx] = av * eh;  // finite where the chunk is factored
+    p.Kh[pcd + idx] = kv * eh;
+    p.Ab[pcd + idx] = av * eb;
+    p.Kb[pcd + idx] = kv * eb;
+  }
+}
+
+// Strong-decay chunks: the four (tied: two) Grams pair by pair with the
+// exact exponent of each difference.  Lane = row r; waves step through i.
+template <int D, int C, bool TIED>
+__global__ __launch_bounds__(256) void dplr_gram_kernel(DPlanes p) {
+  const int b = blockIdx.x;
+  if (p.fast[b]) return;
+  const size_t pcd = (size_t)b * C * D, pcc = (size_t)b * C * C;
+  const int r = threadIdx.x & 63, w = threadIdx.x >> 6;
+  if (r >= C) return;
+  const float* Q = p.Q + pcd;
+  const float* K = p.K + pcd;
+  const float* A = p.A + pcd;
+  const float* Bv = p.B + pcd;
+  const float* G = p.Gam + pcd;
+  const float* g = p.G + pcd;
+  for (int i = w; i < C; i += 4) {
+    float ba = 0.f, bk = 0.f, qa = 0.f, qk = 0.f;
+    if (i <= r) {
+      for (int c = 0; c < D; ++c) {
+        const float gi = G[i * D + c], gr = G[r * D + c];
+        const float eq = __expf(gr - gi), eb = __expf(gr - g[r * D + c] - gi);
+        const float ai = A[i * D + c], ki = K[i * D + c];
+        ba += Bv[r * D + c] * ai * eb;
+        qa += Q[r * D + c] * ai * eq;
+        if (!TIED) {
+          bk += Bv[r * D + c] * ki * eb;
+          qk += Q[r * D + c] * ki * eq;
+        }
+      }
+    }
+    p.Aba[pcc + r * C + i] = i < r ? ba : 0.f;
+    p.Aqa[pcc + r * C + i] = i <= r ? qa : 0.f;
+    if (!TIED) {
+      p.Abk[pcc + r * C + i] = i < r ? bk : 0.f;
+      p.Aqk[pcc + r * C + i] = i <= r ? qk : 0.f;
+    }
+  }
+}
+
+// M = (I + Aba)^{-1} by forward substitution, one column per thread.
+template <int C>
+__global__ __launch_bounds__(64) void dplr_solve_kernel(DPlanes p) {
+  __shared__ float Am[C][C + 1];
+  __shared__ float Xm[C][C + 1];
+  const int b = blockIdx.x, j = threadIdx.x;
+  const size_t pcc = (size_t)b * C * C;
+  for (int idx = j; idx < C * C; idx += 64) Am[idx / C][idx % C] = p.Aba[pcc + idx];
+  __syncthreads();
+  if (j < C) {
+    for (int i = 0; i < C; ++i) {
+      float s = i == j ? 1.f : 0.f;
+      for (int l = j; l < i; ++l) s -= Am[i][l] * Xm[l][j];
+      Xm[i][j] = i < j ? 0.f : s;
+    }
+  }
+  __syncthreads();
+  for (int idx = j; idx < C * C; idx += 64) p.M[pcc + idx] = Xm[idx / C][idx % C];
+}
+
+template <int D, int C>
+struct StLds {
+  union {
+    struct {
+      float Wb[C][D + 4];
+      float Qt[C][D + 4];
+      float Aqa[C][C + 4];
+    } a;
+    struct {
+      float Ab[C][D + 16];   // read transposed
+      float Kb[C][D + 16];   // read transposed
+    } b;
+  } u;
+  float S[D][kColsD];
+  float U[C][kColsD];
+  float Yb[C][kColsD];
+  float Vb[C][kColsD];
+};
+
+// Serial pass over a sequence's chunks for 16 value columns:
+//   U~ = Y - Wb S;  O = Qt S + Aqa U~ (+ Aqk V);  S' = gam_n S + Ab^T U~ (+ Kb^T V)
+// (general form: U~ = U, Y = -M Abk V; tied: U~ = U + V, Y = M V).
+template <int D, int C, bool TIED>
+__global__ __launch_bounds__(256) void dplr_states_kernel(DPlanes p, Geo geo,
+                                                          const float* __restrict__ s0,
+                                                          float* __restrict__ s1,
+                                                          float* __restrict__ o) {
+  extern __shared__ float sm[];
+  StLds<D, C>& L = *reinterpret_cast<StLds<D, C>*>(sm);
+  constexpr int NVB = D / kColsD;
+  const int H = geo.H;
+  const int vb = blockIdx.x % NVB, nh = blockIdx.x / NVB;
+  const int n = nh / H, h = nh % H, col0 = vb * kColsD;
+  const int tid = threadIdx.x, w = tid >> 6, l = tid & 63, m = l & 15, g = l >> 4;
+  int bos, eos, base;
+  seq_of<C>(geo, n, bos, eos, base);
+  const int nch = (eos - bos + C - 1) / C;
+  for (int idx = tid; idx < D * kColsD; idx += 256) {
+    const int i = idx / kColsD, j = idx % kColsD;
+    L.S[i][j] = s0 ? s0[(((size_t)n * H + h) * D + i) * D + col0 + j] : 0.f;
+  }
+  for (int ci = 0; ci < nch; ++ci) {
+    const size_t b = (size_t)(base + ci) * H + h;
+    const size_t pcd = b * C * D, pcc = b * C * C;
+    const int t0 = bos + ci * C, len = min(C, eos - t0);
+    __syncthreads();
+    stage<C, D, D + 4>(&L.u.a.Wb[0][0], p.Wb + pcd);
+    stage<C, D, D + 4>(&L.u.a.Qt[0][0], p.Qt + pcd);
+    stage<C, C, C + 4>(&L.u.a.Aqa[0][0], p.Aqa + pcc);
+    for (int idx = tid; idx < C * kColsD; idx += 256) {
+      const int r = idx / kColsD, j = idx % kColsD;
+      L.Yb[r][j] = p.Y[pcd + r * D + col0 + j];
+      if (!TIED) L.Vb[r][j] = p.V[pcd + r * D + col0 + j];
+    }
+    __syncthreads();
+    for (int rt = w; rt < C / 16; rt += 4) {  // U~ = Y - Wb S
+      f32x4 acc = {0, 0, 0, 0}, acc1 = {0, 0, 0, 0};
+#pragma unroll 8
+      for (int k0 = 0; k0 < D; k0 += 8) {
+        acc = mfma4(L.u.a.Wb[16 * rt + m][k0 + g], L.S[k0 + g][m], acc);
+        acc1 = mfma4(L.u.a.Wb[16 * rt + m][k0 + 4 + g], L.S[k0 + 4 + g][m], acc1);
+      }
+#pragma unroll
+      for (int i = 0; i < 4; ++i) {
+        const int r = 16 * rt + 4 * g + i;
+        L.U[r][m] = L.Yb[r][m] - acc[i] - acc1[i];
+      }
+    }
+    __syncthreads();
+    for (int rt = w; rt < C / 16; rt += 4) {  // O = Qt S + Aqa U~ (+ OV)
+      f32x4 acc = {0, 0, 0, 0}, acc1 = {0, 0, 0, 0};
+#pragma unroll 8
+      for (int k0 = 0; k0 < D; k0 += 4) acc = mfma4(L.u.a.Qt[16 * rt + m][k0 + g], L.S[k0 + g][m], acc);
+      for (int k0 = 0; k0 < 16 * (rt + 1); k0 += 4) acc1 = mfma4(L.u.a.Aqa[16 * rt + m][k0 + g], L.U[k0 + g][m], acc1);
+#pragma unroll
+      for (int i = 0; i < 4; ++i) {
+        const int r = 16 * rt + 4 * g + i;
+        float x = acc[i] + acc1[i];
+        if (!TIED) x += p.OV[pcd + r * D + col0 + m];
+        if (r < len) o[((size_t)(t0 + r) * H + h) * D + col0 + m] = x;
+      }
+    }
+    __syncthreads();
+    stage<C, D, D + 16>(&L.u.b.Ab[0][0], p.Ab + pcd);
+    if (!TIED) stage<C, D, D + 16>(&L.u.b.Kb[0][0], p.Kb + pcd);
+    __syncthreads();
+    for (int t = w; t < D / 16; t += 4) {  // S = gam_n S + Ab^T U~ (+ Kb^T V)
+      f32x4 acc, acc1 = {0, 0, 0, 0};
+#pragma unroll
+      for (int i = 0; i < 4; ++i) {
+        const int c = 16 * t + 4 * g + i;
+        acc[i] = p.gn[b * D + c] * L.S[c][m];
+      }
+#pragma unroll 8
+      for (int k0 = 0; k0 < C; k0 += 4) {
+        acc = mfma4(L.u.b.Ab[k0 + g][16 * t + m], L.U[k0 + g][m], acc);
+        if (!TIED) acc1 = mfma4(L.u.b.Kb[k0 + g][16 * t + m], L.Vb[k0 + g][m], acc1);
+      }
+#pragma unroll
+      for (int i = 0; i < 4; ++i) L.S[16 * t + 4 * g + i][m] = acc[i] + acc1[i];
+    }
+  }
+  __syncthreads();
+  if (s1) {
+    for (int idx = tid; idx < D * kColsD; idx += 256) {
+      const int i = idx / kColsD, j = idx % kColsD;
+      s1[(((size_t)n * H + h) * D + i) * D + col0 + j] = L.S[i][j];
+    }
+  }
+}
+
+template <class in_t, int D, int C, bool TIED>
+hipError_t launch_dplr_t(const DplrArgs& a) {
+  const size_t NB = (size_t)a.total_chunks * a.H;
+  char* ws = reinterpret_cast<char*>(a.workspace);
+  Geo geo;
+  geo.cu = a.cu_seqlens;
+  geo.off = reinterpret_cast<const int32_t*>(ws);
+  geo.num_seqs = a.num_seqs;
+  geo.seq_len = a.seq_len;
+  geo.total_tokens = a.total_tokens;
+  geo.H = a.H;
+  geo.nchunks = a.total_chunks;
+  DPlanes p = dcarve(ws + a256(sizeof(int32_t) * (a.num_seqs + 1)), NB, C, D);
+  if (a.cu_seqlens)
+    hipLaunchKernelGGL(chunk_table_kernel, dim3(1), dim3(1024), 0, a.stream, a.cu_seqlens,
+                       const_cast<int32_t*>(geo.off), a.num_seqs, a.total_tokens, C);
+  const int serial = a.num_seqs * a.H * (D / kColsD);
+  const size_t slds = sizeof(StLds<D, C>);
+  hipError_t e = hipFuncSetAttribute(reinterpret_cast<const void*>(&dplr_states_kernel<D, C, TIED>),
+                                     hipFuncAttributeMaxDynamicSharedMemorySize, (int)slds);
+  if (e != hipSuccess) return e;
+  if (NB > 0) {
+    DIn in{a.q, a.k, a.v, a.a, a.b, a.g, a.beta};
+    hipLaunchKernelGGL((dplr_prep_kernel<in_t, D, C, TIED>), dim3(NB), dim3(256), 0, a.stream, in,
+                       p, geo);
+    auto gemm = [&](auto kern, const float* A, const float* B, float* Cm, int M, int N, int K,
+                    int lda, int ldb, size_t sa, size_t sb, float alpha, int mask) {
+      const dim3 grid((unsigned)NB, (N + 63) / 64, (M + 63) / 64);
+      hipLaunchKernelGGL(kern, grid, dim3(256), 0, a.stream, A, B, Cm, M, N, K, lda, ldb, N, sa,
+                         sb, (size_t)M * N, alpha, 0, mask);
+    };
+    const size_t scd = (size_t)C * D, scc = (size_t)C * C;
+    auto NT = fp32_gemm_kernel<false, true>;
+    auto NN = fp32_gemm_kernel<false, false>;
+    gemm(NT, p.Bt, p.Ah, p.Aba, C, C, D, D, D, scd, scd, 1.f, 2);  // strict_tril(Bt Ah^T)
+    gemm(NT, p.Qt, p.Ah, p.Aqa, C, C, D, D, D, scd, scd, 1.f, 1);  // tril(Qt Ah^T)
+    if (!TIED) {
+      gemm(NT, p.Bt, p.Kh, p.Abk, C, C, D, D, D, scd, scd, 1.f, 2);  // strict_tril(Bt Kh^T)
+      gemm(NT, p.Qt, p.Kh, p.Aqk, C, C, D, D, D, scd, scd, 1.f, 1);  // tril(Qt Kh^T)
+    }
+    hipLaunchKernelGGL((dplr_gram_kernel<D, C, TIED>), dim3(NB), dim3(256), 0, a.stream, p);
+    hipLaunchKernelGGL((dplr_solve_kernel<C>), dim3(NB), dim3(64), 0, a.stream, p);
+    gemm(NN, p.M, p.Bt, p.Wb, C, D, C, C, D, scc, scd, 1.f, 0);      // Wb = M Bt
+    if (TIED) {
+      gemm(NN, p.M, p.V, p.Y, C, D, C, C, D, scc, scd, 1.f, 0);      // Y = M V
+    } else {
+      gemm(NN, p.Abk, p.V, p.X, C, D, C, C, D, scc, scd, 1.f, 0);    // X = Abk V
+      gemm(NN, p.M, p.X, p.Y, C, D, C, C, D, scc, scd, -1.f, 0);     // Y = -M X
+      gemm(NN, p.Aqk, p.V, p.OV, C, D, C, C, D, scc, scd, 1.f, 0);   // OV = Aqk V
+    }
+  }
+  if (serial > 0)
+    hipLaunchKernelGGL((dplr_states_kernel<D, C, TIED>), dim3(serial), dim3(256), slds, a.stream,
+                       p, geo, a.initial_state, a.final_state, a.o);
+  return hipGetLastError();
+}
+
+template <class in_t, bool TIED>
+hipError_t launch_dplr_i(const DplrArgs& a) {
+  if (a.D == 64) {
+    if (a.chunk == 16) return launch_dplr_t<in_t, 64, 16, TIED>(a);
+    if (a.chunk == 32) return launch_dplr_t<in_t, 64, 32, TIED>(a);
+    return launch_dplr_t<in_t, 64, 64, TIED>(a);
+  }
+  if (a.chunk == 16) return launch_dplr_t<in_t, 128, 16, TIED>(a);
+  if (a.chunk == 32) return launch_dplr_t<in_t, 128, 32, TIED>(a);
+  return launch_dplr_t<in_t, 128, 64, TIED>(a);
+}
+
+}  // namespace
+
+size_t dplr_workspace_bytes(long long total_chunks, int num_seqs, int H, int D, int chunk) {
+  return a256(sizeof(int32_t) * (size_t)(num_seqs + 1)) +
+         dplr_plane_bytes((size_t)total_chunks * H, chunk, D);
+}
+
+hipError_t launch_dplr(const DplrArgs& a) {
+  if (a.tied)
+    return a.in_bf16 ? launch_dplr_i<bf16, true>(a) : launch_dplr_i<float, true>(a);
+  return a.in_bf16 ? launch_dplr_i<bf16, false>(a) : launch_dplr_i<float, false>(a);
+}
+
+}  // namespace kda

@@ -109,4 +109,28 @@ struct BackwardArgs {
 size_t backward_workspace_bytes(long long total_chunks, int num_seqs, int H, int D, int chunk);
 hipError_t launch_backward(const BackwardArgs& a);
 
+// General DPLR forward (fp32 chunk pipeline); tied = KDA through the same
+// pipeline (a = k_write = beta k, b = exp(g) k).
+struct DplrArgs {
+  const void* q;
+  const void* k;
+  const void* v;
+  const void* a;       // general form only
+  const void* b;       // general form only
+  const float* g;
+  const float* beta;   // tied form only
+  float* o;
+  const float* initial_state;
+  float* final_state;
+  const int32_t* cu_seqlens;
+  int num_seqs, seq_len, total_tokens, total_chunks;
+  int H, D, chunk;
+  bool in_bf16, tied;
+  void* workspace;
+  hipStream_t stream;
+};
+
+size_t dplr_workspace_bytes(long long total_chunks, int num_seqs, int H, int D, int chunk);
+hipError_t launch_dplr(const DplrArgs& a);
+
 }  // namespace kda

@@ -338,3 +338,20 @@ def draw_conv(rng: np.random.Generator, N: int, H: int, D: int, W: int,
                for _ in range(3))
     ss = tuple(rnd(rng.standard_normal((N, H, W - 1, D))) for _ in range(3))
     return ws, ss
+
+
+def draw_dplr_tokens(rng: np.random.Generator, T: int, H: int, Dk: int, Dv: int,
+                     dtype: str = "bf16", g_scale: float = 0.1):
+    """Inputs of the general DPLR recurrence: q, k as in :func:`draw_tokens`;
+    a = sigmoid(N(0, 1)) u and b = exp(g) * 0.5 w with u, w independent unit
+    vectors (so the low-rank term has norm below 1/2); v ~ N(0, 1); g as in
+    :func:`draw_tokens`.  Returns (q, k, v, a, b, g) float32 arrays
+    (q, k, v, a, b bf16-exact for ``"bf16"``)."""
+    q = _l2norm(rng.standard_normal((T, H, Dk)))
+    k = _l2norm(rng.standard_normal((T, H, Dk)))
+    v = rng.standard_normal((T, H, Dv))
+    g = -_softplus(rng.standard_normal((T, H, Dk))) * g_scale
+    a = _sigmoid(rng.standard_normal((T, H, 1))) * _l2norm(rng.standard_normal((T, H, Dk)))
+    b = np.exp(g) * 0.5 * _l2norm(rng.standard_normal((T, H, Dk)))
+    rnd = bf16_round if dtype == "bf16" else (lambda x: x.astype(np.float32))
+    return rnd(q), rnd(k), rnd(v), rnd(a), rnd(b), g.astype(np.float32)

@@ -76,6 +76,13 @@ def load() -> ctypes.CDLL:
     lib.kda_backward_workspace_size.restype = i32
     lib.kda_backward.argtypes = [vp] * 16 + [i32] * 8 + [vp, sz, vp]
     lib.kda_backward.restype = i32
+    lib.dplr_prefill_workspace_size.argtypes = [i32, i32, i32, i32, i32, i32, vp, i32,
+                                                ctypes.POINTER(sz)]
+    lib.dplr_prefill_workspace_size.restype = i32
+    lib.dplr_prefill.argtypes = [vp] * 11 + [i32] * 8 + [vp, sz, vp]
+    lib.dplr_prefill.restype = i32
+    lib.kda_prefill_chunk_fp32.argtypes = [vp] * 10 + [i32] * 8 + [vp, sz, vp]
+    lib.kda_prefill_chunk_fp32.restype = i32
     _lib = lib
     return lib
 
@@ -456,3 +463,96 @@ def backward(q, k, v, g, beta, d_o, initial_state=None, d_final_state=None, cu_s
         _ptr(cu_seqlens), cu_hp, B, T, H, D, Dv, N, chunk_size, in_code,
         _ptr(workspace), workspace.numel(), _stream_ptr(q.device)), "kda_backward")
     return dq, dk, dv, dg, db, ds0
+
+
+def dplr_workspace_size(B: int, T: int, H: int, D: int, num_seqs: int, chunk_size: int,
+                        cu_seqlens_host: Optional[np.ndarray] = None) -> int:
+    out = ctypes.c_size_t(0)
+    cu_p = None if cu_seqlens_host is None else cu_seqlens_host.ctypes.data
+    _check(load().dplr_prefill_workspace_size(B, T, H, D, D, num_seqs, cu_p, chunk_size,
+                                              ctypes.byref(out)), "dplr_prefill_workspace_size")
+    return out.value
+
+
+def _dplr_call(tied, q, k, v, a, b, g, beta, initial_state, cu_seqlens, cu_seqlens_host,
+               chunk_size, output_final_state, final_state, o, workspace):
+    torch = _torch()
+    if q.dim() != 4:
+        raise KDAError("q must be [B, T, H, D]")
+    B, T, H, D = q.shape
+    Dv = v.shape[-1]
+    _expect("k", k, (B, T, H, D))
+    _expect("v", v, (B, T, H, Dv))
+    _expect("g", g, (B, T, H, D))
+    in_code = _dtype_code(q.dtype)
+    named = [("q", q), ("k", k), ("v", v)]
+    if tied:
+        _expect("beta", beta, (B, T, H))
+        f32s = [("g", g), ("beta", beta)]
+    else:
+        _expect("a", a, (B, T, H, D))
+        _expect("b", b, (B, T, H, D))
+        named += [("a", a), ("b", b)]
+        f32s = [("g", g)]
+    for name, t in named:
+        if t.dtype != q.dtype or not t.is_contiguous():
+            raise KDAError(f"{name} must be contiguous with the dtype of q")
+    for name, t in f32s:
+        if t.dtype != torch.float32 or not t.is_contiguous():
+            raise KDAError(f"{name} must be contiguous float32")
+    if cu_seqlens is not None:
+        cu_h = _host_cu(cu_seqlens, cu_seqlens_host)
+        N = len(cu_h) - 1
+    else:
+        cu_h = None
+        N = B
+    if o is None:
+        o = torch.empty((B, T, H, Dv), dtype=torch.float32, device=q.device)
+    if output_final_state and final_state is None:
+        final_state = torch.empty((N, H, D, Dv), dtype=torch.float32, device=q.device)
+    if not output_final_state:
+        final_state = None
+    for name, t in (("o", o), ("initial_state", initial_state), ("final_state", final_state)):
+        if t is not None and (t.dtype != torch.float32 or not t.is_contiguous()):
+            raise KDAError(f"{name} must be contiguous float32")
+    _expect("o", o, (B, T, H, Dv))
+    _expect("initial_state", initial_state, (N, H, D, Dv))
+    _expect("final_state", final_state, (N, H, D, Dv))
+    ws_bytes = dplr_workspace_size(B, T, H, D, N, chunk_size, cu_h)
+    if workspace is None or workspace.numel() < ws_bytes:
+        workspace = torch.empty(max(ws_bytes, 256), dtype=torch.uint8, device=q.device)
+    cu_hp = None if cu_h is None else cu_h.ctypes.data
+    if tied:
+        code = load().kda_prefill_chunk_fp32(
+            _ptr(q), _ptr(k), _ptr(v), _ptr(g), _ptr(beta), _ptr(o), _ptr(initial_state),
+            _ptr(final_state), _ptr(cu_seqlens), cu_hp, B, T, H, D, Dv, N, chunk_size, in_code,
+            _ptr(workspace), workspace.numel(), _stream_ptr(q.device))
+    else:
+        code = load().dplr_prefill(
+            _ptr(q), _ptr(k), _ptr(v), _ptr(a), _ptr(b), _ptr(g), _ptr(o), _ptr(initial_state),
+            _ptr(final_state), _ptr(cu_seqlens), cu_hp, B, T, H, D, Dv, N, chunk_size, in_code,
+            _ptr(workspace), workspace.numel(), _stream_ptr(q.device))
+    _check(code, "kda_prefill_chunk_fp32" if tied else "dplr_prefill")
+    return o, final_state
+
+
+def dplr_prefill(q, k, v, a, b, g, initial_state=None, cu_seqlens=None, *,
+                 cu_seqlens_host: Optional[Union[Sequence[int], np.ndarray]] = None,
+                 chunk_size: int = 64, output_final_state: bool = True, final_state=None,
+                 o=None, workspace=None):
+    """General DPLR forward (``dplr_prefill``):
+    S_t = (Diag(exp g_t) - a_t b_t^T) S_{t-1} + k_t v_t^T, o_t = S_t^T q_t.
+    q, k, a, b, g ``[B, T, H, Dk]``; v ``[B, T, H, Dv]``.  Returns (o float32,
+    final_state)."""
+    return _dplr_call(False, q, k, v, a, b, g, None, initial_state, cu_seqlens,
+                      cu_seqlens_host, chunk_size, output_final_state, final_state, o, workspace)
+
+
+def prefill_chunk_fp32(q, k, v, g, beta, initial_state=None, cu_seqlens=None, *,
+                       cu_seqlens_host: Optional[Union[Sequence[int], np.ndarray]] = None,
+                       chunk_size: int = 64, output_final_state: bool = True, final_state=None,
+                       o=None, workspace=None):
+    """KDA through the DPLR pipeline's fp32 chunk planes (``kda_prefill_chunk_fp32``);
+    arguments as :func:`prefill`, o float32."""
+    return _dplr_call(True, q, k, v, None, None, g, beta, initial_state, cu_seqlens,
+                      cu_seqlens_host, chunk_size, output_final_state, final_state, o, workspace)

@@ -313,6 +313,54 @@ kda_status kda_backward(const void* q, const void* k, const void* v,
                         kda_dtype in_dtype, void* workspace,
                         size_t workspace_bytes, void* stream /* hipStream_t */);
 
+/*
+ * General diagonal-plus-low-rank (DPLR) recurrence, chunked forward pass:
+ *
+ *     S_t = (Diag(exp g_t) - a_t b_t^T) S_{t-1} + k_t v_t^T,   o_t = S_t^T q_t
+ *
+ * (zeroshot.it.com deep-dive, section 3.2 "DPLR Structure"; greeksharifa
+ * summary, section 6.2 "Relation to DPLR").  KDA is the case a = beta k,
+ * b = exp(g) k with the write beta k v^T; the general form needs four
+ * intra-chunk matrices where KDA needs two.  fp32 arithmetic in per-chunk
+ * planes (the same pipeline as kda_prefill_chunk_fp32), exact for any decay
+ * strength (chunks whose decay span exceeds 40 evaluate their intra-chunk
+ * matrices pair by pair).
+ *
+ * Arguments as in kda_prefill, plus a, b [B*T, H, Dk] in_dtype; o is float32.
+ * The workspace (dplr_prefill_workspace_size) holds fp32 planes of every
+ * chunk: about 624 KB per chunk and head at Dk = Dv = 128, C = 64.
+ */
+kda_status dplr_prefill_workspace_size(int B, int T, int H, int Dk, int Dv,
+                                       int num_seqs,
+                                       const int32_t* cu_seqlens_host,
+                                       int chunk_size, size_t* bytes);
+
+kda_status dplr_prefill(const void* q, const void* k, const void* v,
+                        const void* a, const void* b, const float* g, float* o,
+                        const float* initial_state, float* final_state,
+                        const int32_t* cu_seqlens,
+                        const int32_t* cu_seqlens_host, int B, int T, int H,
+                        int Dk, int Dv, int num_seqs, int chunk_size,
+                        kda_dtype in_dtype, void* workspace,
+                        size_t workspace_bytes, void* stream /* hipStream_t */);
+
+/*
+ * KDA through the same fp32 chunk pipeline as dplr_prefill, with its tied
+ * structure (two intra-chunk matrices): the like-for-like baseline for the
+ * general form, and an fp32-arithmetic KDA forward.  Arguments as in
+ * kda_prefill (o float32); workspace: dplr_prefill_workspace_size.
+ */
+kda_status kda_prefill_chunk_fp32(const void* q, const void* k, const void* v,
+                                  const float* g, const float* beta, float* o,
+                                  const float* initial_state,
+                                  float* final_state,
+                                  const int32_t* cu_seqlens,
+                                  const int32_t* cu_seqlens_host, int B,
+                                  int T, int H, int Dk, int Dv, int num_seqs,
+                                  int chunk_size, kda_dtype in_dtype,
+                                  void* workspace, size_t workspace_bytes,
+                                  void* stream /* hipStream_t */);
+
 #ifdef __cplusplus
 }
 #endif

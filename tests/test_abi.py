@@ -20,7 +20,7 @@ FAKE = 0x100000  # 16-byte aligned, never dereferenced (validation fails first)
 def declared_functions():
     text = open(HEADER).read()
     text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
-    return sorted(set(re.findall(r"\b(kda_\w+)\s*\(", text)))
+    return sorted(set(re.findall(r"\b((?:kda|gdn|dplr)_\w+)\s*\(", text)))
 
 
 @pytest.fixture(scope="module")
@@ -33,7 +33,9 @@ def lib():
 def test_exports_every_declared_symbol(lib):
     names = declared_functions()
     assert {"kda_prefill", "kda_decode_step", "kda_prefill_workspace_size",
-            "kda_status_string", "kda_version"} <= set(names)
+            "kda_status_string", "kda_version", "gdn_prefill", "gdn_decode_step",
+            "kda_prefill_layer", "kda_decode_step_layer", "kda_backward", "dplr_prefill",
+            "kda_prefill_chunk_fp32"} <= set(names)
     for name in names:
         assert hasattr(lib, name), f"{name} declared in kda.h but not exported"
 
