@@ -233,14 +233,17 @@ struct FwdLds {
   float U[C][kCols];
 };
 
+constexpr int kSerThreads = 512;
+
 // Serial forward over a sequence's chunks for 16 value columns: the state
-// entering every chunk, R = V - Kt S and U = T R.
+// entering every chunk, R = V - Kt S and U = T R.  Eight waves; the next
+// chunk's Kt, Kb, T are loaded into registers while this chunk computes.
 template <int D, int C>
-__global__ __launch_bounds__(256) void bwd_fwd_states_kernel(Planes p, Geo geo,
-                                                             const float* __restrict__ s0) {
+__global__ __launch_bounds__(kSerThreads) void bwd_fwd_states_kernel(Planes p, Geo geo,
+                                                                     const float* __restrict__ s0) {
   extern __shared__ float sm[];
   FwdLds<D, C>& L = *reinterpret_cast<FwdLds<D, C>*>(sm);
-  constexpr int NVB = D / kCols;
+  constexpr int NVB = D / kCols, NT = kSerThreads, NW = NT / 64;
   const int H = geo.H;
   const int vb = blockIdx.x % NVB, nh = blockIdx.x / NVB;
   const int n = nh / H, h = nh % H, col0 = vb * kCols;
@@ -248,40 +251,54 @@ __global__ __launch_bounds__(256) void bwd_fwd_states_kernel(Planes p, Geo geo,
   int bos, eos, base;
   seq_of<C>(geo, n, bos, eos, base);
   const int nch = (eos - bos + C - 1) / C;
-  for (int idx = tid; idx < D * kCols; idx += 256) {
+  for (int idx = tid; idx < D * kCols; idx += NT) {
     const int i = idx / kCols, j = idx % kCols;
     L.S[i][j] = s0 ? s0[(((size_t)n * H + h) * D + i) * D + col0 + j] : 0.f;
   }
+  Prefetch<C, D, NT> pKt, pKb;
+  Prefetch<C, C, NT> pT;
+  auto blk = [&](int ci) { return (size_t)(base + ci) * H + h; };
+  if (nch > 0) {
+    const size_t b0 = blk(0);
+    pKt.load(p.Kt + b0 * C * D);
+    pKb.load(p.Kb + b0 * C * D);
+    pT.load(p.T + b0 * C * C);
+  }
   for (int ci = 0; ci < nch; ++ci) {
-    const size_t b = (size_t)(base + ci) * H + h;
-    const size_t pcd = b * C * D, pcc = b * C * C;
+    const size_t b = blk(ci);
+    const size_t pcd = b * C * D;
     __syncthreads();
-    stage<C, D, D + 4>(&L.Kt[0][0], p.Kt + pcd);
-    stage<C, D, D + 16>(&L.Kb[0][0], p.Kb + pcd);
-    stage<C, C, C + 4>(&L.T[0][0], p.T + pcc);
-    for (int idx = tid; idx < D * kCols; idx += 256) {
+    pKt.template store<D + 4>(&L.Kt[0][0]);
+    pKb.template store<D + 16>(&L.Kb[0][0]);
+    pT.template store<C + 4>(&L.T[0][0]);
+    for (int idx = tid; idx < D * kCols; idx += NT) {
       const int i = idx / kCols, j = idx % kCols;
       p.S[(b * D + i) * D + col0 + j] = L.S[i][j];
     }
     __syncthreads();
-    for (int rt = w; rt < C / 16; rt += 4) {  // R = V - Kt S
+    if (ci + 1 < nch) {
+      const size_t bn = blk(ci + 1);
+      pKt.load(p.Kt + bn * C * D);
+      pKb.load(p.Kb + bn * C * D);
+      pT.load(p.T + bn * C * C);
+    }
+    for (int rt = w; rt < C / 16; rt += NW) {  // R = V - Kt S
       f32x4 acc = {0, 0, 0, 0}, acc1 = {0, 0, 0, 0};
 #pragma unroll 8
       for (int k0 = 0; k0 < D; k0 += 8) {
         acc = mfma4(L.Kt[16 * rt + m][k0 + g], L.S[k0 + g][m], acc);
         acc1 = mfma4(L.Kt[16 * rt + m][k0 + 4 + g], L.S[k0 + 4 + g][m], acc1);
       }
-      acc += acc1;
 #pragma unroll
       for (int i = 0; i < 4; ++i) {
         const int r = 16 * rt + 4 * g + i;
-        const float x = p.V[pcd + r * D + col0 + m] - acc[i];
+        const float x = p.V[pcd + r * D + col0 + m] - acc[i] - acc1[i];
         L.R[r][m] = x;
         p.R[pcd + r * D + col0 + m] = x;
       }
     }
     __syncthreads();
-    for (int rt = w; rt < C / 16; rt += 4) {  // U = T R (T lower triangular)
+    for (int rt = w; rt < C / 16; rt += NW) {  // U = T R (T lower triangular)
       f32x4 acc = {0, 0, 0, 0};
       for (int k0 = 0; k0 < 16 * (rt + 1); k0 += 4) acc = mfma4(L.T[16 * rt + m][k0 + g], L.R[k0 + g][m], acc);
 #pragma unroll
@@ -292,22 +309,20 @@ __global__ __launch_bounds__(256) void bwd_fwd_states_kernel(Planes p, Geo geo,
       }
     }
     __syncthreads();
-    for (int t = w; t < D / 16; t += 4) {  // S = gam_n S + Kb^T U, tile t of each wave
-      f32x4 acc;
+    for (int t = w; t < D / 16; t += NW) {  // S = gam_n S + Kb^T U, one tile per wave
+      f32x4 acc, acc1 = {0, 0, 0, 0};
 #pragma unroll
       for (int i = 0; i < 4; ++i) {
         const int c = 16 * t + 4 * g + i;
         acc[i] = p.gn[b * D + c] * L.S[c][m];
       }
-      f32x4 acc1 = {0, 0, 0, 0};
 #pragma unroll 8
       for (int k0 = 0; k0 < C; k0 += 8) {
         acc = mfma4(L.Kb[k0 + g][16 * t + m], L.U[k0 + g][m], acc);
         acc1 = mfma4(L.Kb[k0 + 4 + g][16 * t + m], L.U[k0 + 4 + g][m], acc1);
       }
-      acc += acc1;
 #pragma unroll
-      for (int i = 0; i < 4; ++i) L.S[16 * t + 4 * g + i][m] = acc[i];
+      for (int i = 0; i < 4; ++i) L.S[16 * t + 4 * g + i][m] = acc[i] + acc1[i];
     }
   }
 }
@@ -333,14 +348,15 @@ struct BwdLds {
 
 // Serial backward over a sequence's chunks for 16 value columns: dS' of
 // every chunk, dU = P^T dO + Kb dS', dR = T^T dU, and the carried
-// dS = gam_n dS' + Qt^T dO - Kt^T dR; the last one is dS0.
+// dS = gam_n dS' + Qt^T dO - Kt^T dR; the last one is dS0.  Eight waves; the
+// next chunk's P, T, Kb and this chunk's Qt, Kt load while earlier work runs.
 template <int D, int C>
-__global__ __launch_bounds__(256) void bwd_bwd_states_kernel(Planes p, Geo geo,
-                                                             const float* __restrict__ dfin,
-                                                             float* __restrict__ ds0) {
+__global__ __launch_bounds__(kSerThreads) void bwd_bwd_states_kernel(Planes p, Geo geo,
+                                                                     const float* __restrict__ dfin,
+                                                                     float* __restrict__ ds0) {
   extern __shared__ float sm[];
   BwdLds<D, C>& L = *reinterpret_cast<BwdLds<D, C>*>(sm);
-  constexpr int NVB = D / kCols;
+  constexpr int NVB = D / kCols, NT = kSerThreads, NW = NT / 64;
   const int H = geo.H;
   const int vb = blockIdx.x % NVB, nh = blockIdx.x / NVB;
   const int n = nh / H, h = nh % H, col0 = vb * kCols;
@@ -348,30 +364,46 @@ __global__ __launch_bounds__(256) void bwd_bwd_states_kernel(Planes p, Geo geo,
   int bos, eos, base;
   seq_of<C>(geo, n, bos, eos, base);
   const int nch = (eos - bos + C - 1) / C;
-  for (int idx = tid; idx < D * kCols; idx += 256) {
+  for (int idx = tid; idx < D * kCols; idx += NT) {
     const int i = idx / kCols, j = idx % kCols;
     L.X[i][j] = dfin ? dfin[(((size_t)n * H + h) * D + i) * D + col0 + j] : 0.f;
   }
+  Prefetch<C, C, NT> pP, pT;
+  Prefetch<C, D, NT> pKb, pQt, pKt;
+  auto blk = [&](int ci) { return (size_t)(base + ci) * H + h; };
+  if (nch > 0) {
+    const size_t b0 = blk(nch - 1);
+    pP.load(p.P + b0 * C * C);
+    pT.load(p.T + b0 * C * C);
+    pKb.load(p.Kb + b0 * C * D);
+  }
   for (int ci = nch - 1; ci >= 0; --ci) {
-    const size_t b = (size_t)(base + ci) * H + h;
-    const size_t pcd = b * C * D, pcc = b * C * C;
+    const size_t b = blk(ci);
+    const size_t pcd = b * C * D;
     __syncthreads();
-    stage<C, C, C + 16>(&L.u.a.P[0][0], p.P + pcc);
-    stage<C, C, C + 16>(&L.u.a.T[0][0], p.T + pcc);
-    stage<C, D, D + 4>(&L.u.a.Kb[0][0], p.Kb + pcd);
-    for (int idx = tid; idx < C * kCols; idx += 256) {
+    pP.template store<C + 16>(&L.u.a.P[0][0]);
+    pT.template store<C + 16>(&L.u.a.T[0][0]);
+    pKb.template store<D + 4>(&L.u.a.Kb[0][0]);
+    pQt.load(p.Qt + pcd);
+    pKt.load(p.Kt + pcd);
+    for (int idx = tid; idx < C * kCols; idx += NT) {
       const int r = idx / kCols, j = idx % kCols;
       L.dO[r][j] = p.dO[pcd + r * D + col0 + j];
     }
-    for (int idx = tid; idx < D * kCols; idx += 256) {
+    for (int idx = tid; idx < D * kCols; idx += NT) {
       const int i = idx / kCols, j = idx % kCols;
       p.dSn[(b * D + i) * D + col0 + j] = L.X[i][j];
     }
     __syncthreads();
-    for (int rt = w; rt < C / 16; rt += 4) {  // dU = P^T dO + Kb dS'
-      f32x4 acc = {0, 0, 0, 0};
+    if (ci > 0) {
+      const size_t bn = blk(ci - 1);
+      pP.load(p.P + bn * C * C);
+      pT.load(p.T + bn * C * C);
+      pKb.load(p.Kb + bn * C * D);
+    }
+    for (int rt = w; rt < C / 16; rt += NW) {  // dU = P^T dO + Kb dS'
+      f32x4 acc = {0, 0, 0, 0}, acc1 = {0, 0, 0, 0};
       for (int k0 = 16 * rt; k0 < C; k0 += 4) acc = mfma4(L.u.a.P[k0 + g][16 * rt + m], L.dO[k0 + g][m], acc);
-      f32x4 acc1 = {0, 0, 0, 0};
 #pragma unroll 8
       for (int k0 = 0; k0 < D; k0 += 8) {
         acc1 = mfma4(L.u.a.Kb[16 * rt + m][k0 + g], L.X[k0 + g][m], acc1);
@@ -386,7 +418,7 @@ __global__ __launch_bounds__(256) void bwd_bwd_states_kernel(Planes p, Geo geo,
       }
     }
     __syncthreads();
-    for (int rt = w; rt < C / 16; rt += 4) {  // dR = T^T dU
+    for (int rt = w; rt < C / 16; rt += NW) {  // dR = T^T dU
       f32x4 acc = {0, 0, 0, 0};
       for (int k0 = 16 * rt; k0 < C; k0 += 4) acc = mfma4(L.u.a.T[k0 + g][16 * rt + m], L.dU[k0 + g][m], acc);
 #pragma unroll
@@ -397,30 +429,28 @@ __global__ __launch_bounds__(256) void bwd_bwd_states_kernel(Planes p, Geo geo,
       }
     }
     __syncthreads();
-    stage<C, D, D + 16>(&L.u.b.Qt[0][0], p.Qt + pcd);
-    stage<C, D, D + 16>(&L.u.b.Kt[0][0], p.Kt + pcd);
+    pQt.template store<D + 16>(&L.u.b.Qt[0][0]);
+    pKt.template store<D + 16>(&L.u.b.Kt[0][0]);
     __syncthreads();
-    for (int t = w; t < D / 16; t += 4) {  // dS = gam_n dS' + Qt^T dO - Kt^T dR
-      f32x4 acc;
+    for (int t = w; t < D / 16; t += NW) {  // dS = gam_n dS' + Qt^T dO - Kt^T dR
+      f32x4 acc, acc1 = {0, 0, 0, 0};
 #pragma unroll
       for (int i = 0; i < 4; ++i) {
         const int c = 16 * t + 4 * g + i;
         acc[i] = p.gn[b * D + c] * L.X[c][m];
       }
-      f32x4 acc1 = {0, 0, 0, 0};
 #pragma unroll 8
       for (int k0 = 0; k0 < C; k0 += 4) {
         acc = mfma4(L.u.b.Qt[k0 + g][16 * t + m], L.dO[k0 + g][m], acc);
         acc1 = mfma4(L.u.b.Kt[k0 + g][16 * t + m], L.ndR[k0 + g][m], acc1);
       }
-      acc += acc1;
 #pragma unroll
-      for (int i = 0; i < 4; ++i) L.X[16 * t + 4 * g + i][m] = acc[i];
+      for (int i = 0; i < 4; ++i) L.X[16 * t + 4 * g + i][m] = acc[i] + acc1[i];
     }
   }
   __syncthreads();
   if (ds0) {
-    for (int idx = tid; idx < D * kCols; idx += 256) {
+    for (int idx = tid; idx < D * kCols; idx += NT) {
       const int i = idx / kCols, j = idx % kCols;
       ds0[(((size_t)n * H + h) * D + i) * D + col0 + j] = L.X[i][j];
     }
@@ -643,7 +673,7 @@ hipError_t launch_backward_t(const BackwardArgs& a) {
   if (NB == 0) {
     // No tokens: dS0 = dS_N.
     if (a.d_initial_state && serial > 0)
-      hipLaunchKernelGGL((bwd_bwd_states_kernel<D, C>), dim3(serial), dim3(256), blds_s, a.stream,
+      hipLaunchKernelGGL((bwd_bwd_states_kernel<D, C>), dim3(serial), dim3(kSerThreads), blds_s, a.stream,
                          p, geo, a.d_final_state, a.d_initial_state);
     return hipGetLastError();
   }
@@ -669,9 +699,9 @@ hipError_t launch_backward_t(const BackwardArgs& a) {
   gemm(NT, p.Qt, p.Kh, p.P, C, C, D, D, D, scd, scd, 1.f, 0, 1);   // tril(Qt Kh^T)
   hipLaunchKernelGGL((bwd_gram_kernel<D, C>), dim3(NB), dim3(256), glds, a.stream, p, (int)NB);
   hipLaunchKernelGGL((bwd_solve_kernel<C>), dim3(NB), dim3(64), 0, a.stream, p);
-  hipLaunchKernelGGL((bwd_fwd_states_kernel<D, C>), dim3(serial), dim3(256), flds_s, a.stream, p,
+  hipLaunchKernelGGL((bwd_fwd_states_kernel<D, C>), dim3(serial), dim3(kSerThreads), flds_s, a.stream, p,
                      geo, a.initial_state);
-  hipLaunchKernelGGL((bwd_bwd_states_kernel<D, C>), dim3(serial), dim3(256), blds_s, a.stream, p,
+  hipLaunchKernelGGL((bwd_bwd_states_kernel<D, C>), dim3(serial), dim3(kSerThreads), blds_s, a.stream, p,
                      geo, a.d_final_state, a.d_initial_state);
   // p.S and p.dSn are [D][D] per chunk and head: the B operand "rows" are the
   // key channels, contracted over the value columns.

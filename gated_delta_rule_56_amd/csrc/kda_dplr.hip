@@ -217,17 +217,21 @@ struct StLds {
   float Vb[C][kColsD];
 };
 
+constexpr int kStThreads = 512;
+
 // Serial pass over a sequence's chunks for 16 value columns:
 //   U~ = Y - Wb S;  O = Qt S + Aqa U~ (+ Aqk V);  S' = gam_n S + Ab^T U~ (+ Kb^T V)
-// (general form: U~ = U, Y = -M Abk V; tied: U~ = U + V, Y = M V).
+// (general form: U~ = U, Y = -M Abk V; tied: U~ = U + V, Y = M V).  Eight
+// waves; the next chunk's Wb, Qt, Aqa are loaded into registers while this
+// chunk computes, and this chunk's Ab, Kb while its first half computes.
 template <int D, int C, bool TIED>
-__global__ __launch_bounds__(256) void dplr_states_kernel(DPlanes p, Geo geo,
-                                                          const float* __restrict__ s0,
-                                                          float* __restrict__ s1,
-                                                          float* __restrict__ o) {
+__global__ __launch_bounds__(kStThreads) void dplr_states_kernel(DPlanes p, Geo geo,
+                                                                 const float* __restrict__ s0,
+                                                                 float* __restrict__ s1,
+                                                                 float* __restrict__ o) {
   extern __shared__ float sm[];
   StLds<D, C>& L = *reinterpret_cast<StLds<D, C>*>(sm);
-  constexpr int NVB = D / kColsD;
+  constexpr int NVB = D / kColsD, NT = kStThreads, NW = NT / 64;
   const int H = geo.H;
   const int vb = blockIdx.x % NVB, nh = blockIdx.x / NVB;
   const int n = nh / H, h = nh % H, col0 = vb * kColsD;
@@ -235,25 +239,42 @@ __global__ __launch_bounds__(256) void dplr_states_kernel(DPlanes p, Geo geo,
   int bos, eos, base;
   seq_of<C>(geo, n, bos, eos, base);
   const int nch = (eos - bos + C - 1) / C;
-  for (int idx = tid; idx < D * kColsD; idx += 256) {
+  for (int idx = tid; idx < D * kColsD; idx += NT) {
     const int i = idx / kColsD, j = idx % kColsD;
     L.S[i][j] = s0 ? s0[(((size_t)n * H + h) * D + i) * D + col0 + j] : 0.f;
   }
+  Prefetch<C, D, NT> pW, pQ, pA, pK;
+  Prefetch<C, C, NT> pP;
+  auto blk = [&](int ci) { return (size_t)(base + ci) * H + h; };
+  if (nch > 0) {
+    const size_t b0 = blk(0);
+    pW.load(p.Wb + b0 * C * D);
+    pQ.load(p.Qt + b0 * C * D);
+    pP.load(p.Aqa + b0 * C * C);
+  }
   for (int ci = 0; ci < nch; ++ci) {
-    const size_t b = (size_t)(base + ci) * H + h;
-    const size_t pcd = b * C * D, pcc = b * C * C;
+    const size_t b = blk(ci);
+    const size_t pcd = b * C * D;
     const int t0 = bos + ci * C, len = min(C, eos - t0);
-    __syncthreads();
-    stage<C, D, D + 4>(&L.u.a.Wb[0][0], p.Wb + pcd);
-    stage<C, D, D + 4>(&L.u.a.Qt[0][0], p.Qt + pcd);
-    stage<C, C, C + 4>(&L.u.a.Aqa[0][0], p.Aqa + pcc);
-    for (int idx = tid; idx < C * kColsD; idx += 256) {
+    __syncthreads();  // the previous chunk's reads of the union are done
+    pW.template store<D + 4>(&L.u.a.Wb[0][0]);
+    pQ.template store<D + 4>(&L.u.a.Qt[0][0]);
+    pP.template store<C + 4>(&L.u.a.Aqa[0][0]);
+    pA.load(p.Ab + pcd);
+    if (!TIED) pK.load(p.Kb + pcd);
+    for (int idx = tid; idx < C * kColsD; idx += NT) {
       const int r = idx / kColsD, j = idx % kColsD;
       L.Yb[r][j] = p.Y[pcd + r * D + col0 + j];
       if (!TIED) L.Vb[r][j] = p.V[pcd + r * D + col0 + j];
     }
     __syncthreads();
-    for (int rt = w; rt < C / 16; rt += 4) {  // U~ = Y - Wb S
+    if (ci + 1 < nch) {  // the next chunk's first-half operands
+      const size_t bn = blk(ci + 1);
+      pW.load(p.Wb + bn * C * D);
+      pQ.load(p.Qt + bn * C * D);
+      pP.load(p.Aqa + bn * C * C);
+    }
+    for (int rt = w; rt < C / 16; rt += NW) {  // U~ = Y - Wb S
       f32x4 acc = {0, 0, 0, 0}, acc1 = {0, 0, 0, 0};
 #pragma unroll 8
       for (int k0 = 0; k0 < D; k0 += 8) {
@@ -267,7 +288,7 @@ __global__ __launch_bounds__(256) void dplr_states_kernel(DPlanes p, Geo geo,
       }
     }
     __syncthreads();
-    for (int rt = w; rt < C / 16; rt += 4) {  // O = Qt S + Aqa U~ (+ OV)
+    for (int rt = w; rt < C / 16; rt += NW) {  // O = Qt S + Aqa U~ (+ OV)
       f32x4 acc = {0, 0, 0, 0}, acc1 = {0, 0, 0, 0};
 #pragma unroll 8
       for (int k0 = 0; k0 < D; k0 += 4) acc = mfma4(L.u.a.Qt[16 * rt + m][k0 + g], L.S[k0 + g][m], acc);
@@ -281,10 +302,10 @@ __global__ __launch_bounds__(256) void dplr_states_kernel(DPlanes p, Geo geo,
       }
     }
     __syncthreads();
-    stage<C, D, D + 16>(&L.u.b.Ab[0][0], p.Ab + pcd);
-    if (!TIED) stage<C, D, D + 16>(&L.u.b.Kb[0][0], p.Kb + pcd);
+    pA.template store<D + 16>(&L.u.b.Ab[0][0]);
+    if (!TIED) pK.template store<D + 16>(&L.u.b.Kb[0][0]);
     __syncthreads();
-    for (int t = w; t < D / 16; t += 4) {  // S = gam_n S + Ab^T U~ (+ Kb^T V)
+    for (int t = w; t < D / 16; t += NW) {  // S = gam_n S + Ab^T U~ (+ Kb^T V)
       f32x4 acc, acc1 = {0, 0, 0, 0};
 #pragma unroll
       for (int i = 0; i < 4; ++i) {
@@ -302,7 +323,7 @@ __global__ __launch_bounds__(256) void dplr_states_kernel(DPlanes p, Geo geo,
   }
   __syncthreads();
   if (s1) {
-    for (int idx = tid; idx < D * kColsD; idx += 256) {
+    for (int idx = tid; idx < D * kColsD; idx += NT) {
       const int i = idx / kColsD, j = idx % kColsD;
       s1[(((size_t)n * H + h) * D + i) * D + col0 + j] = L.S[i][j];
     }
@@ -361,7 +382,7 @@ hipError_t launch_dplr_t(const DplrArgs& a) {
     }
   }
   if (serial > 0)
-    hipLaunchKernelGGL((dplr_states_kernel<D, C, TIED>), dim3(serial), dim3(256), slds, a.stream,
+    hipLaunchKernelGGL((dplr_states_kernel<D, C, TIED>), dim3(serial), dim3(kStThreads), slds, a.stream,
                        p, geo, a.initial_state, a.final_state, a.o);
   return hipGetLastError();
 }

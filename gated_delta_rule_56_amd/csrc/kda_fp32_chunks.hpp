@@ -96,29 +96,6 @@ __device__ __forceinline__ f32x4 mfma4(float a, float b, f32x4 c) {
   return __builtin_amdgcn_mfma_f32_16x16x4f32(a, b, c, 0, 0, 0);
 }
 
-// Stage ROWS x COLS floats (row-major) into LDS with row stride LD: every
-// load of the thread is issued before the first LDS store.
-template <int ROWS, int COLS, int LD>
-__device__ __forceinline__ void stage(float* dst, const float* __restrict__ src) {
-  constexpr int C4 = COLS / 4, N = (ROWS * C4 + 255) / 256;
-  static_assert(COLS % 4 == 0, "float4 rows");
-  f32x4 v[N];
-#pragma unroll
-  for (int x = 0; x < N; ++x) {
-    const int idx = threadIdx.x + 256 * x;
-    if (idx < ROWS * C4)
-      v[x] = *reinterpret_cast<const f32x4*>(src + (size_t)(idx / C4) * COLS + 4 * (idx % C4));
-  }
-#pragma unroll
-  for (int x = 0; x < N; ++x) {
-    const int idx = threadIdx.x + 256 * x;
-    if (idx < ROWS * C4) {
-      const int r = idx / C4, c = 4 * (idx % C4);
-#pragma unroll
-      for (int e = 0; e < 4; ++e) dst[r * LD + c + e] = v[x][e];
-    }
-  }
-}
 
 // Batched C = alpha op(A) op(B) (+ C when acc) with op(A) [M x K] stored as
 // A[m][k] (TA = false) or A[k][m] (TA = true), op(B) [K x N] stored as B[k][n]
@@ -181,6 +158,35 @@ __global__ __launch_bounds__(256) void fp32_gemm_kernel(const float* __restrict_
       }
     }
 }
+
+// Register-staged copy of a ROWS x COLS fp32 block (row-major in global
+// memory) spread over NT threads: load() issues every load of the thread,
+// store<LD>() writes the block into LDS with row stride LD (a multiple of 4,
+// so each write is one 16-byte LDS store).  Loading the next chunk's
+// operands while the current chunk computes hides their latency.
+template <int ROWS, int COLS, int NT>
+struct Prefetch {
+  static constexpr int C4 = COLS / 4, N = (ROWS * C4 + NT - 1) / NT;
+  static_assert(COLS % 4 == 0, "float4 rows");
+  f32x4 v[N];
+  __device__ __forceinline__ void load(const float* __restrict__ src) {
+#pragma unroll
+    for (int x = 0; x < N; ++x) {
+      const int idx = threadIdx.x + NT * x;
+      if (idx < ROWS * C4)
+        v[x] = *reinterpret_cast<const f32x4*>(src + (size_t)(idx / C4) * COLS + 4 * (idx % C4));
+    }
+  }
+  template <int LD>
+  __device__ __forceinline__ void store(float* dst) const {
+    static_assert(LD % 4 == 0, "16-byte LDS rows");
+#pragma unroll
+    for (int x = 0; x < N; ++x) {
+      const int idx = threadIdx.x + NT * x;
+      if (idx < ROWS * C4) *reinterpret_cast<f32x4*>(dst + (idx / C4) * LD + 4 * (idx % C4)) = v[x];
+    }
+  }
+};
 
 }  // namespace
 }  // namespace kda
