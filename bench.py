@@ -63,8 +63,8 @@ def decode_algorithmic_bytes(N=D_N, H=D_H, d=D_D):
 # run.  A figure is reported only while the kernel sources still hash to the
 # values it was measured on.
 TRAFFIC = {
-    "prefill": {"sources": "37b508b660850da4", "bytes": 870272448},
-    "decode": {"sources": "e2a4b5474702cdbd", "bytes": 1089482400},
+    "prefill": {"sources": "3ee9db3a1c1f75a2", "bytes": 871665664},
+    "decode": {"sources": "e646a7258292501a", "bytes": 1089498080},
 }
 
 
@@ -76,8 +76,10 @@ def sources_digest(names):
     return h.hexdigest()[:16]
 
 
-PREFILL_SOURCES = ("kda_prefill.hip", "kda_device.hpp", "kda_launch.hpp")
-DECODE_SOURCES = ("kda_decode.hip", "kda_device.hpp", "kda_launch.hpp")
+# The files that define the measured kernels (launch arguments are plain
+# structs declared elsewhere and do not change the kernels' memory traffic).
+PREFILL_SOURCES = ("kda_prefill.hip", "kda_device.hpp")
+DECODE_SOURCES = ("kda_decode.hip", "kda_device.hpp")
 
 
 def measured_traffic(unit, names):
