@@ -42,7 +42,7 @@
 //   fp32_gemm_kernel      batched fp32 products (Grams, contractions over value
 //                         columns, pairwise gradient terms)
 //   bwd_gram_kernel       per strong-decay (chunk, head): Bm and P pair by pair
-//   bwd_solve_kernel      per (chunk, head): M by forward substitution, T
+//   unit_lower_inverse_kernel per (chunk, head): M = (I + Diag(beta) Bm)^-1, T
 //   bwd_fwd_states_kernel per (sequence, head, 16 value columns), serial over
 //                         chunks: the entering state S of every chunk, R, U
 //   bwd_bwd_states_kernel the same, reverse: dS' of every chunk, dU, dR, dS0
@@ -194,34 +194,6 @@ __global__ __launch_bounds__(256) void bwd_gram_kernel(Planes p, int NB) {
   }
 }
 
-// M = (I + Diag(beta) Bm)^{-1} by forward substitution, one column per
-// thread; T = M Diag(beta).
-template <int C>
-__global__ __launch_bounds__(64) void bwd_solve_kernel(Planes p) {
-  __shared__ float A[C][C + 1];
-  __shared__ float X[C][C + 1];
-  const int b = blockIdx.x, j = threadIdx.x;
-  const size_t pcc = (size_t)b * C * C;
-  const float* beta = p.beta + (size_t)b * C;
-  for (int idx = j; idx < C * C; idx += 64) {
-    const int r = idx / C, i = idx % C;
-    A[r][i] = beta[r] * p.Bm[pcc + idx];
-  }
-  __syncthreads();
-  if (j < C) {
-    for (int i = 0; i < C; ++i) {
-      float s = i == j ? 1.f : 0.f;
-      for (int l = j; l < i; ++l) s -= A[i][l] * X[l][j];
-      X[i][j] = i < j ? 0.f : s;
-    }
-  }
-  __syncthreads();
-  for (int idx = j; idx < C * C; idx += 64) {
-    const int r = idx / C, i = idx % C;
-    p.M[pcc + idx] = X[r][i];
-    p.T[pcc + idx] = X[r][i] * beta[i];
-  }
-}
 
 template <int D, int C>
 struct FwdLds {
@@ -698,7 +670,8 @@ hipError_t launch_backward_t(const BackwardArgs& a) {
   gemm(NT, p.Kt, p.Kh, p.Bm, C, C, D, D, D, scd, scd, 1.f, 0, 2);  // strict_tril(Kt Kh^T)
   gemm(NT, p.Qt, p.Kh, p.P, C, C, D, D, D, scd, scd, 1.f, 0, 1);   // tril(Qt Kh^T)
   hipLaunchKernelGGL((bwd_gram_kernel<D, C>), dim3(NB), dim3(256), glds, a.stream, p, (int)NB);
-  hipLaunchKernelGGL((bwd_solve_kernel<C>), dim3(NB), dim3(64), 0, a.stream, p);
+  hipLaunchKernelGGL((unit_lower_inverse_kernel<C>), dim3(NB), dim3(256), 0, a.stream, p.Bm, p.beta,
+                     p.M, p.T);
   hipLaunchKernelGGL((bwd_fwd_states_kernel<D, C>), dim3(serial), dim3(kSerThreads), flds_s, a.stream, p,
                      geo, a.initial_state);
   hipLaunchKernelGGL((bwd_bwd_states_kernel<D, C>), dim3(serial), dim3(kSerThreads), blds_s, a.stream, p,

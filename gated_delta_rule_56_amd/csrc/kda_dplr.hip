@@ -29,7 +29,7 @@
 //
 // Kernels: chunk_table_kernel (varlen), dplr_prep_kernel, fp32_gemm_kernel
 // (Grams, then Wb = M Bt, the V terms), dplr_gram_kernel (strong decay),
-// dplr_solve_kernel (M), dplr_states_kernel (serial over chunks per
+// unit_lower_inverse_kernel (M), dplr_states_kernel (serial over chunks per
 // (sequence, head, 16 value columns), fp32 MFMA, writes o and the final state).
 #include "kda_device.hpp"
 #include "kda_fp32_chunks.hpp"
@@ -178,25 +178,6 @@ __global__ __launch_bounds__(256) void dplr_gram_kernel(DPlanes p) {
   }
 }
 
-// M = (I + Aba)^{-1} by forward substitution, one column per thread.
-template <int C>
-__global__ __launch_bounds__(64) void dplr_solve_kernel(DPlanes p) {
-  __shared__ float Am[C][C + 1];
-  __shared__ float Xm[C][C + 1];
-  const int b = blockIdx.x, j = threadIdx.x;
-  const size_t pcc = (size_t)b * C * C;
-  for (int idx = j; idx < C * C; idx += 64) Am[idx / C][idx % C] = p.Aba[pcc + idx];
-  __syncthreads();
-  if (j < C) {
-    for (int i = 0; i < C; ++i) {
-      float s = i == j ? 1.f : 0.f;
-      for (int l = j; l < i; ++l) s -= Am[i][l] * Xm[l][j];
-      Xm[i][j] = i < j ? 0.f : s;
-    }
-  }
-  __syncthreads();
-  for (int idx = j; idx < C * C; idx += 64) p.M[pcc + idx] = Xm[idx / C][idx % C];
-}
 
 template <int D, int C>
 struct StLds {
@@ -371,7 +352,8 @@ hipError_t launch_dplr_t(const DplrArgs& a) {
       gemm(NT, p.Qt, p.Kh, p.Aqk, C, C, D, D, D, scd, scd, 1.f, 1);  // tril(Qt Kh^T)
     }
     hipLaunchKernelGGL((dplr_gram_kernel<D, C, TIED>), dim3(NB), dim3(256), 0, a.stream, p);
-    hipLaunchKernelGGL((dplr_solve_kernel<C>), dim3(NB), dim3(64), 0, a.stream, p);
+    hipLaunchKernelGGL((unit_lower_inverse_kernel<C>), dim3(NB), dim3(256), 0, a.stream, p.Aba,
+                       (const float*)nullptr, p.M, (float*)nullptr);
     gemm(NN, p.M, p.Bt, p.Wb, C, D, C, C, D, scc, scd, 1.f, 0);      // Wb = M Bt
     if (TIED) {
       gemm(NN, p.M, p.V, p.Y, C, D, C, C, D, scc, scd, 1.f, 0);      // Y = M V

@@ -188,5 +188,62 @@ struct Prefetch {
   }
 };
 
+// M = (I + Diag(rs) A)^{-1} for a strictly lower-triangular C x C block A
+// per item (rs: a row scale, or nullptr for none), and optionally
+// T = M Diag(rs).  Blocked: the 16 x 16 diagonal blocks by forward
+// substitution (one thread per column), then the off-diagonal blocks level by
+// level, M_ij = -M_ii sum_{j <= k < i} A_ik M_kj, as 16 x 16 x 16 products
+// spread over 256 threads.
+template <int C>
+__global__ __launch_bounds__(256) void unit_lower_inverse_kernel(const float* __restrict__ A,
+                                                                 const float* __restrict__ rs,
+                                                                 float* __restrict__ M,
+                                                                 float* __restrict__ Tm) {
+  constexpr int NB = C / 16;
+  __shared__ float As[C][C + 1];
+  __shared__ float Xs[C][C + 1];
+  __shared__ float Ys[NB][16][17];
+  const int b = blockIdx.x, tid = threadIdx.x;
+  const size_t pcc = (size_t)b * C * C;
+  const float* r = rs ? rs + (size_t)b * C : nullptr;
+  for (int idx = tid; idx < C * C; idx += 256) {
+    const int i = idx / C, j = idx % C;
+    As[i][j] = j < i ? (r ? r[i] : 1.f) * A[pcc + idx] : 0.f;
+    Xs[i][j] = 0.f;
+  }
+  __syncthreads();
+  if (tid < 16 * NB) {  // diagonal blocks
+    const int base = 16 * (tid / 16), j = tid % 16;
+    for (int i = j; i < 16; ++i) {
+      float s = i == j ? 1.f : 0.f;
+      for (int l = j; l < i; ++l) s -= As[base + i][base + l] * Xs[base + l][base + j];
+      Xs[base + i][base + j] = s;
+    }
+  }
+  __syncthreads();
+  for (int d = 1; d < NB; ++d) {
+    // Y_i = sum_{k = j .. i-1} A_ik X_kj for the block pairs (i, j = i - d)
+    for (int e = tid; e < (NB - d) * 256; e += 256) {
+      const int bi = d + e / 256, bj = bi - d, rr = (e % 256) / 16, cc = e % 16;
+      float s = 0.f;
+      for (int k = 16 * bj; k < 16 * bi; ++k) s += As[16 * bi + rr][k] * Xs[k][16 * bj + cc];
+      Ys[bi][rr][cc] = s;
+    }
+    __syncthreads();
+    for (int e = tid; e < (NB - d) * 256; e += 256) {  // X_ij = -X_ii Y_i
+      const int bi = d + e / 256, bj = bi - d, rr = (e % 256) / 16, cc = e % 16;
+      float s = 0.f;
+      for (int k = 0; k <= rr; ++k) s -= Xs[16 * bi + rr][16 * bi + k] * Ys[bi][k][cc];
+      Xs[16 * bi + rr][16 * bj + cc] = s;
+    }
+    __syncthreads();
+  }
+  for (int idx = tid; idx < C * C; idx += 256) {
+    const int i = idx / C, j = idx % C;
+    M[pcc + idx] = Xs[i][j];
+    if (Tm) Tm[pcc + idx] = Xs[i][j] * (r ? r[j] : 1.f);
+  }
+}
+
 }  // namespace
 }  // namespace kda
