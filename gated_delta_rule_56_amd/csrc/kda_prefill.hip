@@ -574,9 +574,18 @@ __device__ __forceinline__ void load_halo(Raw8<T>& ext, const KernelPtrs& kp, in
   }
 }
 
+// Rotate a value right by N lanes within each 16-lane row (DPP row_ror):
+// lane lr receives the value of lane (lr - N) mod 16 of its row.
+template <int N>
+__device__ __forceinline__ float row_ror(float x) {
+  return __builtin_bit_cast(float, __builtin_amdgcn_update_dpp(0, __builtin_bit_cast(int, x),
+                                                               0x120 + N, 0xF, 0xF, false));
+}
+
 // Convolved values of one lane's 8 channels (c0 .. c0 + 7) of row 16 rt + lr,
 // from the lane's own row and the halo rows of lanes 13..15 of its 16-lane
-// group (shuffles stay inside the group).
+// group: tap i reads row lr - i, the own value of lane lr - i, or for
+// lr < i the halo value of lane lr - i + 16 (both one row rotation).
 template <class T>
 __device__ __forceinline__ void conv8(const Raw8<T>& own, const Raw8<T>& ext, const float* wrow,
                                       int W, int lr, float out[8]) {
@@ -584,13 +593,16 @@ __device__ __forceinline__ void conv8(const Raw8<T>& own, const Raw8<T>& ext, co
   for (int e = 0; e < 8; ++e) {
     const float xo = own.get(e), xe = ext.get(e);
     float acc = wrow[e * W + W - 1] * xo;
-#pragma unroll
-    for (int i = 1; i < kMaxConv; ++i) {
-      const int src = lr - i;
-      const float a = __shfl(xo, src < 0 ? 0 : src, 16);
-      const float b = __shfl(xe, src < 0 ? src + 16 : 0, 16);
-      if (i < W) acc += wrow[e * W + W - 1 - i] * (src >= 0 ? a : b);
-    }
+    // Both rotations run on every lane (a conditional operator would run
+    // only one, under a divergent branch, and read inactive lanes).
+    const float o1 = row_ror<1>(xo), e1 = row_ror<1>(xe);
+    const float o2 = row_ror<2>(xo), e2 = row_ror<2>(xe);
+    const float o3 = row_ror<3>(xo), e3 = row_ror<3>(xe);
+    const float t1 = lr >= 1 ? o1 : e1, t2 = lr >= 2 ? o2 : e2, t3 = lr >= 3 ? o3 : e3;
+    static_assert(kMaxConv == 4, "three taps before the current row");
+    if (W > 1) acc += wrow[e * W + W - 2] * t1;
+    if (W > 2) acc += wrow[e * W + W - 3] * t2;
+    if (W > 3) acc += wrow[e * W + W - 4] * t3;
     out[e] = acc;
   }
 }
@@ -672,9 +684,13 @@ __global__ __launch_bounds__(kIntraThreads, 4) void intra_chunk_kernel(KernelPtr
     const float bv = kp.beta[(size_t)tb * H + h];
     beta_s[tid] = tid < len ? (PRO ? sigmoidf(bv) : bv) : 0.f;
   }
-  // Layer prologue inputs before Swish: the raw q, k, or their short
-  // convolution (PRO == 2), computed once here.
-  float qc[PRO == 2 ? FPW : 1][8], kc[PRO == 2 ? FPW : 1][8];
+  // Layer prologue: Swish of q and k, after their short convolution when
+  // PRO == 2.  Where the Gram region (unused until step 4) holds 32 B per
+  // lane and fragment, the convolved, activated k waits there instead of in
+  // registers.
+  constexpr bool kPark = PRO == 2 && (size_t)kIntraThreads * FPW * 32 <= L::kR1;
+  float qc[PRO == 2 ? FPW : 1][8], kc_reg[PRO == 2 && !kPark ? FPW : 1][8];
+  f32x4* kpark = reinterpret_cast<f32x4*>(smem + L::oR1) + 2 * (64 * (FPW * w) + l);
   if constexpr (PRO == 2) {
 #pragma unroll
     for (int j = 0; j < FPW; ++j) {
@@ -683,12 +699,29 @@ __global__ __launch_bounds__(kIntraThreads, 4) void intra_chunk_kernel(KernelPtr
       load_halo<in_t, D>(qe, kp, 0, it, rt, lr, c0, si.total_tokens);
       load_halo<in_t, D>(ke, kp, 1, it, rt, lr, c0, si.total_tokens);
       const int W = kp.conv_w;
+      float kc[8];
       conv8(qraw[j], qe, kp.cw[0] + ((size_t)h * D + c0) * W, W, lr, qc[j]);
-      conv8(kraw[j], ke, kp.cw[1] + ((size_t)h * D + c0) * W, W, lr, kc[j]);
+      conv8(kraw[j], ke, kp.cw[1] + ((size_t)h * D + c0) * W, W, lr, kc);
+#pragma unroll
+      for (int e = 0; e < 8; ++e) qc[j][e] = swishf(qc[j][e]);
+      if constexpr (kPark) {
+        kpark[128 * j] = f32x4{swishf(kc[0]), swishf(kc[1]), swishf(kc[2]), swishf(kc[3])};
+        kpark[128 * j + 1] = f32x4{swishf(kc[4]), swishf(kc[5]), swishf(kc[6]), swishf(kc[7])};
+      } else {
+#pragma unroll
+        for (int e = 0; e < 8; ++e) kc_reg[j][e] = swishf(kc[e]);
+      }
     }
   }
-  auto qin = [&](int j, int e) { if constexpr (PRO == 2) return qc[j][e]; else return qraw[j].get(e); };
-  auto kin = [&](int j, int e) { if constexpr (PRO == 2) return kc[j][e]; else return kraw[j].get(e); };
+  // activated (Swish, before the L2 norm) inputs of the prologue
+  auto qact = [&](int j, int e) {
+    if constexpr (PRO == 2) return qc[j][e]; else return swishf(qraw[j].get(e));
+  };
+  auto kact = [&](int j, int e) {
+    if constexpr (kPark) return kpark[128 * j + (e >> 2)][e & 3];
+    else if constexpr (PRO == 2) return kc_reg[j][e];
+    else return swishf(kraw[j].get(e));
+  };
 
   // ---- step 2: cumulative decay.  Inclusive scan over the 16 tokens of the
   // tile (lanes lr of one lane group), then the totals of earlier tiles ----
@@ -739,7 +772,7 @@ __global__ __launch_bounds__(kIntraThreads, 4) void intra_chunk_kernel(KernelPtr
       if (fv[j]) {
 #pragma unroll
         for (int e = 0; e < 8; ++e) {
-          const float a = swishf(qin(j, e)), b = swishf(kin(j, e));
+          const float a = qact(j, e), b = kact(j, e);
           sq += a * a;
           sk += b * b;
         }
@@ -811,8 +844,8 @@ __global__ __launch_bounds__(kIntraThreads, 4) void intra_chunk_kernel(KernelPtr
     float qt[8], kt[8], kh[8];
 #pragma unroll
     for (int e = 0; e < 8; ++e) {
-      const float kv = rv ? (PRO ? swishf(kin(j, e)) * ik : kraw[j].get(e)) : 0.f;
-      const float qv = rv ? (PRO ? swishf(qin(j, e)) * iq : qraw[j].get(e)) : 0.f;
+      const float kv = rv ? (PRO ? kact(j, e) * ik : kraw[j].get(e)) : 0.f;
+      const float qv = rv ? (PRO ? qact(j, e) * iq : qraw[j].get(e)) : 0.f;
       const float gm = __expf(G[j][e]);
       qt[e] = qv * gm;
       kt[e] = kv * gm;
