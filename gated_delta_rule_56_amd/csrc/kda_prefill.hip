@@ -582,6 +582,24 @@ __device__ __forceinline__ float row_ror(float x) {
                                                                0x120 + N, 0xF, 0xF, false));
 }
 
+// Shift a value right by N lanes within each 16-lane row (DPP row_shr): lane
+// lr receives the value of lane lr - N, lanes lr < N receive 0.  Every lane
+// of the wave must execute it.
+template <int N>
+__device__ __forceinline__ float row_shr(float x) {
+  return __builtin_bit_cast(float, __builtin_amdgcn_update_dpp(0, __builtin_bit_cast(int, x),
+                                                               0x110 + N, 0xF, 0xF, false));
+}
+
+// Inclusive prefix sum over the 16 lanes of each row.
+__device__ __forceinline__ float row_scan16(float x) {
+  x += row_shr<1>(x);
+  x += row_shr<2>(x);
+  x += row_shr<4>(x);
+  x += row_shr<8>(x);
+  return x;
+}
+
 // Convolved values of one lane's 8 channels (c0 .. c0 + 7) of row 16 rt + lr,
 // from the lane's own row and the halo rows of lanes 13..15 of its 16-lane
 // group: tap i reads row lr - i, the own value of lane lr - i, or for
@@ -727,12 +745,7 @@ __global__ __launch_bounds__(kIntraThreads, 4) void intra_chunk_kernel(KernelPtr
   // tile (lanes lr of one lane group), then the totals of earlier tiles ----
   float G[FPW][8];
   if constexpr (SDEC) {
-    float x = rv ? gscalar : 0.f;  // one scan serves every channel
-#pragma unroll
-    for (int d = 1; d < 16; d <<= 1) {
-      const float t = __shfl_up(x, d, 16);
-      x += lr >= d ? t : 0.f;
-    }
+    const float x = row_scan16(rv ? gscalar : 0.f);  // one scan serves every channel
 #pragma unroll
     for (int j = 0; j < FPW; ++j)
 #pragma unroll
@@ -741,15 +754,7 @@ __global__ __launch_bounds__(kIntraThreads, 4) void intra_chunk_kernel(KernelPtr
 #pragma unroll
     for (int j = 0; j < FPW; ++j)
 #pragma unroll
-      for (int e = 0; e < 8; ++e) {
-        float x = rv ? graw[j].get(e) : 0.f;
-#pragma unroll
-        for (int d = 1; d < 16; d <<= 1) {
-          const float t = __shfl_up(x, d, 16);
-          x += lr >= d ? t : 0.f;
-        }
-        G[j][e] = x;
-      }
+      for (int e = 0; e < 8; ++e) G[j][e] = row_scan16(rv ? graw[j].get(e) : 0.f);
   }
   if (lr == 15) {
 #pragma unroll
