@@ -210,7 +210,19 @@ def dplr_workloads(torch, kda, I, dev):
                     "dplr_over_kda_prefill": round(t_dplr / t_kda, 2)})
         del q, k, v, g, b, a, bb, o, fin, ws2
         torch.cuda.empty_cache()
-    return {"workload": "general DPLR vs KDA on the same inputs, bf16, chunk 64", "cases": res}
+    # one general DPLR decode step on the decode workload's shape
+    N, H, d = D_N, D_H, D_D
+    qd, kd, vd, ad, bd = (torch.randn((N, H, d), device=dev).to(torch.bfloat16) for _ in range(5))
+    gd = -torch.nn.functional.softplus(torch.randn((N, H, d), device=dev)) * 0.1
+    st = torch.randn((N, H, d, d), device=dev) * 0.1
+    od = torch.empty((N, H, d), dtype=torch.float32, device=dev)
+    t = time_calls(torch, lambda: kda.dplr_decode_step(qd, kd, vd, ad, bd, gd, st, o=od), 20)
+    by = N * H * (2 * d * d * 4 + 5 * 2 * d + 4 * d + 4 * d)
+    dec = {"workload": f"dplr_decode_step N={N} H={H} d={d}, bf16 in / fp32 out",
+           "us_per_step": round(t * 1e6, 2), "GBps": round(by / t / 1e9, 1),
+           "hbm_frac": round(by / t / 1e9 / HBM_PEAK_GBS, 4)}
+    return {"workload": "general DPLR vs KDA on the same inputs, bf16, chunk 64", "cases": res,
+            "decode": dec}
 
 
 def backward_workload(torch, kda, I, dev):

@@ -409,4 +409,21 @@ kda_status kda_prefill_chunk_fp32(const void* q, const void* k, const void* v, c
                    workspace, workspace_bytes, stream);
 }
 
+kda_status dplr_decode_step(const void* q, const void* k, const void* v, const void* a_,
+                            const void* b_, const float* g, float* state, void* o, int N, int H,
+                            int Dk, int Dv, kda_dtype in_dtype, kda_dtype out_dtype,
+                            void* stream) {
+  if (!q || !k || !v || !a_ || !b_ || !g || !state || !o) return KDA_ERR_INVALID_ARG;
+  if (N < 0 || H < 1 || !valid_dtype(in_dtype) || !valid_dtype(out_dtype))
+    return KDA_ERR_INVALID_ARG;
+  if (!supported_head(Dk, Dv)) return KDA_ERR_UNSUPPORTED;
+  const void* ptrs[] = {q, k, v, a_, b_, g, state, o};
+  for (const void* p : ptrs)
+    if (!aligned(p, 16)) return KDA_ERR_INVALID_ARG;
+  if ((int64_t)N * H > INT32_MAX) return KDA_ERR_INVALID_ARG;
+  kda::DplrDecodeArgs a{q, k, v, a_, b_, g, state, o, N, H, Dk, in_dtype == KDA_BF16,
+                        out_dtype == KDA_BF16, reinterpret_cast<hipStream_t>(stream)};
+  return kda::launch_dplr_decode(a) == hipSuccess ? KDA_OK : KDA_ERR_HIP;
+}
+
 }  // extern "C"

@@ -278,6 +278,119 @@ static hipError_t launch_decode_t(const DecodeArgs& a) {
   return hipGetLastError();
 }
 
+// General DPLR single-token step (zeroshot.it.com deep-dive, section 3.2
+// "DPLR Structure"): S' = Diag(alpha) S - a (b^T S) + k v^T, o = S'^T q,
+// alpha = exp(g).  One pass over the state as in decode_step_kernel: the row
+// reductions r = S^T b and p = (Diag(alpha) S)^T q, with a.q and k.q, give
+// o = p - (a.q) r + (k.q) v before the state is rewritten.
+template <typename in_t, int D, bool OUT_BF16>
+__global__ __launch_bounds__(256) void dplr_decode_step_kernel(
+    const in_t* __restrict__ q, const in_t* __restrict__ k, const in_t* __restrict__ v,
+    const in_t* __restrict__ av, const in_t* __restrict__ bv, const float* __restrict__ g,
+    float* __restrict__ state, void* __restrict__ o, int NH) {
+  constexpr int TPR = D / 4, RG = 256 / TPR, RPT = D / RG;
+  const int nh = blockIdx.x;
+  if (nh >= NH) return;
+  const int t = threadIdx.x, cg = t % TPR, rg = t / TPR;
+  const size_t tok = (size_t)nh;
+  float* sp = state + tok * (size_t)D * D;
+  f32x4 s[RPT];
+  float al[RPT], aa[RPT], kk[RPT];
+#pragma unroll
+  for (int m = 0; m < RPT; ++m)
+    s[m] = __builtin_nontemporal_load(reinterpret_cast<const f32x4*>(sp + (size_t)(rg + RG * m) * D + 4 * cg));
+  float r[4] = {0, 0, 0, 0}, p[4] = {0, 0, 0, 0}, aq = 0.f, kq = 0.f;
+#pragma unroll
+  for (int m = 0; m < RPT; ++m) {
+    const int i = rg + RG * m;
+    const float qi = (float)q[tok * D + i], bi = (float)bv[tok * D + i];
+    al[m] = __expf(g[tok * D + i]);
+    aa[m] = (float)av[tok * D + i];
+    kk[m] = (float)k[tok * D + i];
+#pragma unroll
+    for (int c = 0; c < 4; ++c) {
+      r[c] += bi * s[m][c];
+      p[c] += qi * al[m] * s[m][c];
+    }
+    aq += aa[m] * qi;
+    kq += kk[m] * qi;
+  }
+#pragma unroll
+  for (int off = TPR; off < 64; off <<= 1) {
+#pragma unroll
+    for (int c = 0; c < 4; ++c) {
+      r[c] += __shfl_xor(r[c], off);
+      p[c] += __shfl_xor(p[c], off);
+    }
+    aq += __shfl_xor(aq, off);
+    kq += __shfl_xor(kq, off);
+  }
+  __shared__ float red[4][TPR][10];
+  const int w = t >> 6;
+  if ((t & 63) < TPR) {
+#pragma unroll
+    for (int c = 0; c < 4; ++c) {
+      red[w][cg][c] = r[c];
+      red[w][cg][4 + c] = p[c];
+    }
+    red[w][cg][8] = aq;
+    red[w][cg][9] = kq;
+  }
+  __syncthreads();
+#pragma unroll
+  for (int c = 0; c < 4; ++c) {
+    r[c] = red[0][cg][c] + red[1][cg][c] + red[2][cg][c] + red[3][cg][c];
+    p[c] = red[0][cg][4 + c] + red[1][cg][4 + c] + red[2][cg][4 + c] + red[3][cg][4 + c];
+  }
+  aq = red[0][cg][8] + red[1][cg][8] + red[2][cg][8] + red[3][cg][8];
+  kq = red[0][cg][9] + red[1][cg][9] + red[2][cg][9] + red[3][cg][9];
+  float vv[4];
+#pragma unroll
+  for (int c = 0; c < 4; ++c) vv[c] = (float)v[tok * D + 4 * cg + c];
+#pragma unroll
+  for (int m = 0; m < RPT; ++m) {
+#pragma unroll
+    for (int c = 0; c < 4; ++c) s[m][c] = al[m] * s[m][c] - aa[m] * r[c] + kk[m] * vv[c];
+    __builtin_nontemporal_store(s[m], reinterpret_cast<f32x4*>(sp + (size_t)(rg + RG * m) * D + 4 * cg));
+  }
+  if (rg == 0) {
+    float y[4];
+#pragma unroll
+    for (int c = 0; c < 4; ++c) y[c] = p[c] - aq * r[c] + kq * vv[c];
+    if constexpr (OUT_BF16) {
+      bf16x4 ov;
+#pragma unroll
+      for (int c = 0; c < 4; ++c) ov[c] = f2bf(y[c]);
+      *reinterpret_cast<bf16x4*>(reinterpret_cast<bf16*>(o) + tok * D + 4 * cg) = ov;
+    } else {
+      *reinterpret_cast<f32x4*>(reinterpret_cast<float*>(o) + tok * D + 4 * cg) = f32x4{y[0], y[1], y[2], y[3]};
+    }
+  }
+}
+
+template <typename in_t, int D>
+static void launch_dplr_decode_t(const DplrDecodeArgs& a) {
+  const int NH = a.N * a.H;
+  const dim3 grid(NH), block(256);
+  if (a.out_bf16)
+    hipLaunchKernelGGL((dplr_decode_step_kernel<in_t, D, true>), grid, block, 0, a.stream,
+                       (const in_t*)a.q, (const in_t*)a.k, (const in_t*)a.v, (const in_t*)a.a,
+                       (const in_t*)a.b, a.g, a.state, a.o, NH);
+  else
+    hipLaunchKernelGGL((dplr_decode_step_kernel<in_t, D, false>), grid, block, 0, a.stream,
+                       (const in_t*)a.q, (const in_t*)a.k, (const in_t*)a.v, (const in_t*)a.a,
+                       (const in_t*)a.b, a.g, a.state, a.o, NH);
+}
+
+hipError_t launch_dplr_decode(const DplrDecodeArgs& a) {
+  if (a.N * a.H == 0) return hipSuccess;
+  if (a.in_bf16)
+    a.D == 128 ? launch_dplr_decode_t<bf16, 128>(a) : launch_dplr_decode_t<bf16, 64>(a);
+  else
+    a.D == 128 ? launch_dplr_decode_t<float, 128>(a) : launch_dplr_decode_t<float, 64>(a);
+  return hipGetLastError();
+}
+
 hipError_t launch_decode(const DecodeArgs& a) {
   if (a.N * a.H == 0) return hipSuccess;
   if (a.in_bf16) {

@@ -133,4 +133,16 @@ struct DplrArgs {
 size_t dplr_workspace_bytes(long long total_chunks, int num_seqs, int H, int D, int chunk);
 hipError_t launch_dplr(const DplrArgs& a);
 
+struct DplrDecodeArgs {
+  const void *q, *k, *v, *a, *b;
+  const float* g;
+  float* state;
+  void* o;
+  int N, H, D;
+  bool in_bf16, out_bf16;
+  hipStream_t stream;
+};
+
+hipError_t launch_dplr_decode(const DplrDecodeArgs& a);
+
 }  // namespace kda

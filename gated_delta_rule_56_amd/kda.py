@@ -83,6 +83,8 @@ def load() -> ctypes.CDLL:
     lib.dplr_prefill.restype = i32
     lib.kda_prefill_chunk_fp32.argtypes = [vp] * 10 + [i32] * 8 + [vp, sz, vp]
     lib.kda_prefill_chunk_fp32.restype = i32
+    lib.dplr_decode_step.argtypes = [vp] * 8 + [i32] * 6 + [vp]
+    lib.dplr_decode_step.restype = i32
     _lib = lib
     return lib
 
@@ -556,3 +558,33 @@ def prefill_chunk_fp32(q, k, v, g, beta, initial_state=None, cu_seqlens=None, *,
     arguments as :func:`prefill`, o float32."""
     return _dplr_call(True, q, k, v, None, None, g, beta, initial_state, cu_seqlens,
                       cu_seqlens_host, chunk_size, output_final_state, final_state, o, workspace)
+
+
+def dplr_decode_step(q, k, v, a, b, g, state, *, out_dtype=None, o=None):
+    """One general DPLR step (``dplr_decode_step``); ``state`` updated in place.
+    q, k, a, b, g ``[N, H, Dk]`` (g float32); v ``[N, H, Dv]``; state
+    ``[N, H, Dk, Dv]`` float32.  Returns o ``[N, H, Dv]``."""
+    torch = _torch()
+    N, H, D = q.shape
+    Dv = v.shape[-1]
+    for name, t in (("k", k), ("a", a), ("b", b)):
+        _expect(name, t, (N, H, D))
+        if t.dtype != q.dtype or not t.is_contiguous():
+            raise KDAError(f"{name} must be contiguous with the dtype of q")
+    _expect("v", v, (N, H, Dv))
+    _expect("g", g, (N, H, D))
+    _expect("state", state, (N, H, D, Dv))
+    if v.dtype != q.dtype or not v.is_contiguous() or not q.is_contiguous():
+        raise KDAError("q and v must be contiguous with one dtype")
+    for name, t in (("g", g), ("state", state)):
+        if t.dtype != torch.float32 or not t.is_contiguous():
+            raise KDAError(f"{name} must be contiguous float32")
+    out_dtype = out_dtype or torch.float32
+    if o is None:
+        o = torch.empty((N, H, Dv), dtype=out_dtype, device=q.device)
+    _expect("o", o, (N, H, Dv))
+    _check(load().dplr_decode_step(
+        _ptr(q), _ptr(k), _ptr(v), _ptr(a), _ptr(b), _ptr(g), _ptr(state), _ptr(o),
+        N, H, D, Dv, _dtype_code(q.dtype), _dtype_code(out_dtype), _stream_ptr(q.device)),
+        "dplr_decode_step")
+    return o

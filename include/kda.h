@@ -345,6 +345,19 @@ kda_status dplr_prefill(const void* q, const void* k, const void* v,
                         size_t workspace_bytes, void* stream /* hipStream_t */);
 
 /*
+ * One general DPLR step for N independent sequences (generation):
+ *   S <- Diag(exp g) S - a (b^T S) + k v^T;   o = S^T q
+ * q, k, a, b, g [N, H, Dk] (g float32, the others in_dtype); v [N, H, Dv];
+ * state [N, H, Dk, Dv] float32, updated in place; o [N, H, Dv] out_dtype.
+ * Dk == Dv in {64, 128}.
+ */
+kda_status dplr_decode_step(const void* q, const void* k, const void* v,
+                            const void* a, const void* b, const float* g,
+                            float* state, void* o, int N, int H, int Dk, int Dv,
+                            kda_dtype in_dtype, kda_dtype out_dtype,
+                            void* stream /* hipStream_t */);
+
+/*
  * KDA through the same fp32 chunk pipeline as dplr_prefill, with its tied
  * structure (two intra-chunk matrices): the like-for-like baseline for the
  * general form, and an fp32-arithmetic KDA forward.  Arguments as in

@@ -124,3 +124,49 @@ def test_dplr_full_size_sampled_heads(kda):
     eo_, es_ = rel(o[:, hs], eo), rel(fin[0, hs], ef[0])
     say(f"  o err {eo_:.2e}  state err {es_:.2e}")
     assert eo_ <= TOL["bf16"] and es_ <= TOL["bf16"]
+
+
+@pytest.mark.parametrize("dtype,D", [("bf16", 128), ("f32", 64)])
+def test_dplr_decode_steps_match_oracle(kda, dtype, D):
+    say(f"dplr decode dtype={dtype} D={D}")
+    N, H, steps = 3, 2, 40
+    rng = np.random.default_rng([64, D])
+    x = I.draw_dplr_tokens(rng, N * steps, H, D, D, dtype)
+    s0 = I.draw_states(rng, N, H, D, D)
+    cu = np.arange(N + 1) * steps
+    eo, ef = oracle.dplr_recurrent(*x, s0, cu)
+    dt = torch.bfloat16 if dtype == "bf16" else torch.float32
+    state = torch.from_numpy(s0.copy()).to(DEV)
+    q, k, v, a, b, g = x
+    worst = 0.0
+    for t in range(steps):
+        rows = np.arange(N) * steps + t
+        o = kda.dplr_decode_step(tdev(q[rows], dt), tdev(k[rows], dt), tdev(v[rows], dt),
+                                 tdev(a[rows], dt), tdev(b[rows], dt), tdev(g[rows]), state)
+        worst = max(worst, rel(host(o), eo[rows]))
+    torch.cuda.synchronize()
+    es = rel(host(state), ef)
+    say(f"  o err {worst:.2e}  state err {es:.2e}")
+    assert worst <= TOL[dtype] and es <= TOL[dtype]
+
+
+def test_dplr_decode_continues_prefill(kda):
+    say("dplr prefill then decode")
+    rng = np.random.default_rng(65)
+    T, H, D, steps = 130, 2, 128, 4
+    x = I.draw_dplr_tokens(rng, T + steps, H, D, D, "bf16")
+    eo, ef = oracle.dplr_recurrent(*x)
+    o, st = run_dplr(kda, tuple(a[:T] for a in x), "bf16", 64)
+    stt = torch.from_numpy(st).to(DEV)
+    worst = rel(o, eo[:T])
+    dt = torch.bfloat16
+    q, k, v, a, b, g = x
+    for t in range(T, T + steps):
+        od = kda.dplr_decode_step(tdev(q[t:t + 1], dt), tdev(k[t:t + 1], dt), tdev(v[t:t + 1], dt),
+                                  tdev(a[t:t + 1], dt), tdev(b[t:t + 1], dt), tdev(g[t:t + 1]),
+                                  stt)
+        worst = max(worst, rel(host(od)[0], eo[t]))
+    torch.cuda.synchronize()
+    es = rel(host(stt)[0], ef[0])
+    say(f"  o err {worst:.2e}  state err {es:.2e}")
+    assert worst <= TOL["bf16"] and es <= TOL["bf16"]
