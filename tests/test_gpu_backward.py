@@ -137,3 +137,18 @@ def test_backward_full_size_sampled_heads(kda):
         errs[name] = rel(a, r)
     say("  " + "  ".join(f"{k} {v:.2e}" for k, v in errs.items()))
     assert max(errs.values()) <= TOL["bf16"], errs
+
+
+def test_backward_no_tokens(kda):
+    """T = 0: every token gradient is empty and dS0 equals dS_N."""
+    say("backward T=0")
+    H, D = 2, 64
+    rng = np.random.default_rng(55)
+    dF = rng.standard_normal((1, H, D, D)).astype(np.float32)
+    z = lambda *s: torch.zeros(s, dtype=torch.float32, device=DEV)
+    got = kda.backward(z(1, 0, H, D), z(1, 0, H, D), z(1, 0, H, D), z(1, 0, H, D), z(1, 0, H),
+                       z(1, 0, H, D), tdev(I.draw_states(rng, 1, H, D, D)), tdev(dF),
+                       chunk_size=64)
+    torch.cuda.synchronize()
+    np.testing.assert_array_equal(host(got[5]), dF)
+    assert got[0].numel() == 0

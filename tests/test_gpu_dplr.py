@@ -170,3 +170,17 @@ def test_dplr_decode_continues_prefill(kda):
     es = rel(host(stt)[0], ef[0])
     say(f"  o err {worst:.2e}  state err {es:.2e}")
     assert worst <= TOL["bf16"] and es <= TOL["bf16"]
+
+
+def test_dplr_no_tokens(kda):
+    """T = 0: the final state is the initial state."""
+    say("dplr T=0")
+    H, D = 2, 64
+    rng = np.random.default_rng(66)
+    s0 = I.draw_states(rng, 1, H, D, D)
+    z = lambda *s: torch.zeros(s, dtype=torch.float32, device=DEV)
+    o, fin = kda.dplr_prefill(z(1, 0, H, D), z(1, 0, H, D), z(1, 0, H, D), z(1, 0, H, D),
+                              z(1, 0, H, D), z(1, 0, H, D), tdev(s0), chunk_size=64)
+    torch.cuda.synchronize()
+    np.testing.assert_array_equal(host(fin), s0)
+    assert o.numel() == 0
