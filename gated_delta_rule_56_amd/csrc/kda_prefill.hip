@@ -250,40 +250,48 @@ __global__ __launch_bounds__(1024) void segment_table_kernel(const int32_t* __re
 }
 
 // ---------------------------------------------------------------------------
-// Precise 16x16x16 product from fp32 LDS matrices (used by the block solve).
-// acc += A[ra.., ca..] (16x16) * B[rb.., cb..] (16x16); row-major, strides sa/sb.
+// Block forward substitution on 16x16 tiles.  A chain operand is a 16x16
+// block in the A-operand layout of the 16x16x16 products: lane l holds
+// A[l & 15][4 (l >> 4) + e], e = 0..3, kept in LDS as 16 B per lane (split
+// hi + lo for bf16, fp32 otherwise).  The right operand is an accumulator
+// tile itself (lane l holds Y[4 (l >> 4) + i][l & 15]), which is exactly the
+// B-operand layout of those products, so a chain of them never moves data
+// between lanes.
 // ---------------------------------------------------------------------------
-__device__ __forceinline__ f32x4 prod16(ModeBF16, f32x4 acc, const float* A, int sa, int ra, int ca,
-                                        const float* B, int sb, int rb, int cb) {
-  const int l = lane_id();
-  const int g = l >> 4, r = l & 15;
-  // MFMA 1: [A_hi | A_lo] x [B_hi ; B_hi]; MFMA 2: [A_hi | 0] x [B_lo ; 0].
-  const int kbase = 8 * (g & 1);
-  bf16x8 a1, b1, a2, b2;
+__device__ __forceinline__ void cfrag_store(ModeBF16, char* p, const float* x) {
+  bf16x4 h, lo;
 #pragma unroll
-  for (int e = 0; e < 8; ++e) {
-    const float av = A[(ra + r) * sa + ca + kbase + e];
-    const float bv = B[(rb + kbase + e) * sb + cb + r];
-    const bf16 ah = f2bf(av), bh = f2bf(bv);
-    const bf16 al = f2bf(av - bf2f(ah)), bl = f2bf(bv - bf2f(bh));
-    a1[e] = g < 2 ? ah : al;
-    b1[e] = bh;
-    a2[e] = g < 2 ? ah : f2bf(0.f);
-    b2[e] = g < 2 ? bl : f2bf(0.f);
+  for (int e = 0; e < 4; ++e) {
+    h[e] = f2bf(x[e]);
+    lo[e] = f2bf(x[e] - bf2f(h[e]));
   }
-  acc = mfma_bf16(a2, b2, acc);
-  return mfma_bf16(a1, b1, acc);
+  bf16x4* q = reinterpret_cast<bf16x4*>(p + 16 * lane_id());
+  q[0] = h;
+  q[1] = lo;
 }
-__device__ __forceinline__ f32x4 prod16(ModeF32, f32x4 acc, const float* A, int sa, int ra, int ca,
-                                        const float* B, int sb, int rb, int cb) {
-  const int l = lane_id();
-  const int g = l >> 4, r = l & 15;
+__device__ __forceinline__ void cfrag_store(ModeF32, char* p, const float* x) {
+  *reinterpret_cast<f32x4*>(p + 16 * lane_id()) = f32x4{x[0], x[1], x[2], x[3]};
+}
+// acc += A Y for a chain operand A at p and an accumulator-layout tile Y.
+__device__ __forceinline__ f32x4 chain_mma(ModeBF16, const char* p, f32x4 y, f32x4 acc) {
+  const bf16x4* q = reinterpret_cast<const bf16x4*>(p + 16 * lane_id());
+  const bf16x4 ah = q[0], al = q[1];
+  bf16x4 yh, yl;
 #pragma unroll
-  for (int s = 0; s < 4; ++s) {
-    const int kk = 4 * s + g;
-    acc = __builtin_amdgcn_mfma_f32_16x16x4f32(A[(ra + r) * sa + ca + kk],
-                                               B[(rb + kk) * sb + cb + r], acc, 0, 0, 0);
+  for (int e = 0; e < 4; ++e) {
+    yh[e] = f2bf(y[e]);
+    yl[e] = f2bf(y[e] - bf2f(yh[e]));
   }
+  acc = __builtin_amdgcn_mfma_f32_16x16x16bf16_1k(al, yh, acc, 0, 0, 0);
+  acc = __builtin_amdgcn_mfma_f32_16x16x16bf16_1k(ah, yl, acc, 0, 0, 0);
+  return __builtin_amdgcn_mfma_f32_16x16x16bf16_1k(ah, yh, acc, 0, 0, 0);
+}
+// fp32: four 16x16x4 products; the s-th takes k = 4 (l >> 4) + s, which is
+// element s of both the lane's chain operand and its accumulator.
+__device__ __forceinline__ f32x4 chain_mma(ModeF32, const char* p, f32x4 y, f32x4 acc) {
+  const f32x4 a = *reinterpret_cast<const f32x4*>(p + 16 * lane_id());
+#pragma unroll
+  for (int s = 0; s < 4; ++s) acc = __builtin_amdgcn_mfma_f32_16x16x4f32(a[s], y[s], acc, 0, 0, 0);
   return acc;
 }
 
@@ -291,10 +299,11 @@ __device__ __forceinline__ f32x4 prod16(ModeF32, f32x4 acc, const float* A, int 
 // LDS plan of the intra-chunk kernel: two regions that the phases reuse,
 //   R0: K-bar^T staging (precise [D x KC])  ->  K/gam fragments (precise, in
 //       fragment order; on the strong-decay path Gamma fp32 [C x (D+1)])
-//       ->  X = (I + A)^{-1} (fp32 [C x (KC+1)]) and the solve scratch, then
-//       the T fragments
+//       ->  the solve's operands: inverses of the diagonal blocks of I + A
+//       (fp32 [NRT][16][17]) and the chain operands (the blocks A_am below
+//       the diagonal, then the inverses)
 //   R1: A and P (fp32 [C x (KC+1)])  ->  (K*gam)^T staging (precise
-//       [D x KC])  ->  V^T staging (precise [D x KC])
+//       [D x KC]), overwritten in place by W^T  ->  V^T staging
 // plus the per-tile totals of the decay scan, beta, and the layer prologue's
 // norm partials and per-token factors.
 // ---------------------------------------------------------------------------
@@ -305,6 +314,7 @@ struct IntraLds {
   typedef typename M::in_t plain_t;  // element of one half of a precise matrix
   static constexpr int KC = Layout<M, D, C>::KC;
   static constexpr int NRT = C / 16;
+  static constexpr int NOFF = NRT * (NRT - 1) / 2;  // blocks below the diagonal
   static constexpr int SK = KC + kPad;  // row stride of [D x KC] staging
   static constexpr int SF = KC + 1;     // row stride of fp32 [C x KC] matrices
   static constexpr int SG = D + 1;      // row stride of the fp32 Gamma array
@@ -313,10 +323,9 @@ struct IntraLds {
   static constexpr size_t kKhFrags = (size_t)NRT * (D / 32) * M::kPFragBytes;
   static constexpr size_t kGamma = ((size_t)C * SG * 4 + 15) / 16 * 16;
   static constexpr size_t kFMat = ((size_t)C * SF * 4 + 15) / 16 * 16;
-  static constexpr size_t kYsc = 4 * 16 * 17 * 4;
-  static constexpr size_t kTFrags = (size_t)NRT * (KC / 32) * M::kPFragBytes;
-  static constexpr size_t kR0 = cmax(cmax(kStPrecise, kKhFrags),
-                                     cmax(kGamma, kFMat + cmax(kYsc, kTFrags)));
+  static constexpr size_t kXD = ((size_t)NRT * 16 * 17 * 4 + 15) / 16 * 16;
+  static constexpr size_t kSolve = kXD + (size_t)(NOFF + NRT) * 1024;
+  static constexpr size_t kR0 = cmax(cmax(kStPrecise, kKhFrags), cmax(kGamma, kSolve));
   static constexpr size_t kR1 = cmax(2 * kFMat, kStPrecise);
   static constexpr size_t oR0 = 0, oR1 = kR0;
   static constexpr size_t oTot = kR0 + kR1;              // fp32 [NRT][D]
@@ -328,10 +337,9 @@ struct IntraLds {
   static constexpr size_t oKbS = oR0;                    // staging
   static constexpr size_t oKh = oR0, oG = oR0;           // Gram operands / Gamma
   static constexpr size_t oA = oR1, oP = oR1 + kFMat;    // Grams
-  static constexpr size_t oX = oR0, oY = oR0 + kFMat;    // solve
-  static constexpr size_t oTf = oR0 + kFMat;             // T fragments (after the solve)
-  static constexpr size_t oKtT = oR1;                    // W product
-  static constexpr size_t oVT = oR1;                     // U0 product (after W)
+  static constexpr size_t oXD = oR0, oCF = oR0 + kXD;    // solve
+  static constexpr size_t oKtT = oR1;                    // W
+  static constexpr size_t oVT = oR1;                     // U0 (after W)
 };
 
 template <class M>
@@ -368,6 +376,14 @@ struct LdsPrecise<ModeBF16> {
     hi[idx] = f.hi[e];
     lo[idx] = f.lo[e];
   }
+  __device__ float get(int idx) const { return bf2f(hi[idx]) + bf2f(lo[idx]); }
+  // four consecutive elements starting at idx (a multiple of 4)
+  __device__ void get4(int idx, float* x) const {
+    const bf16x4 h = *reinterpret_cast<const bf16x4*>(hi + idx);
+    const bf16x4 l = *reinterpret_cast<const bf16x4*>(lo + idx);
+#pragma unroll
+    for (int e = 0; e < 4; ++e) x[e] = bf2f(h[e]) + bf2f(l[e]);
+  }
 };
 template <>
 struct LdsPrecise<ModeF32> {
@@ -386,6 +402,12 @@ struct LdsPrecise<ModeF32> {
     return lds_pfrag(ModeF32{}, v, nullptr, stride, row0, k0);
   }
   __device__ void put(int idx, const ModeF32::PFrag& f, int e) { v[idx] = f.v[e]; }
+  __device__ float get(int idx) const { return v[idx]; }
+  __device__ void get4(int idx, float* x) const {
+    const f32x4 t = *reinterpret_cast<const f32x4*>(v + idx);
+#pragma unroll
+    for (int e = 0; e < 4; ++e) x[e] = t[e];
+  }
 };
 
 // Write eight consecutive-k fp32 values of one lane into a global fragment.
@@ -655,6 +677,7 @@ __global__ __launch_bounds__(kIntraThreads, 4) void intra_chunk_kernel(KernelPtr
   constexpr int NFRAG = NRT * NKD;            // fragments of a [C x D] matrix
   constexpr int FPW = (NFRAG + NW - 1) / NW;  // fragments per wave
   static_assert(NW % NRT == 0, "a wave's fragments share one row tile");
+  static_assert(NDT <= NW, "one wave per column tile in the solve");
   extern __shared__ __attribute__((aligned(16))) char smem[];
 
   const int H = kp.H;
@@ -1010,8 +1033,12 @@ __global__ __launch_bounds__(kIntraThreads, 4) void intra_chunk_kernel(KernelPtr
   }
   __syncthreads();  // B5: A and P complete; R0 free
 
-  // ---- step 5: P fragments out; X = (I + A)^{-1} by blocked forward
-  // substitution ----
+  // ---- step 5: P fragments out, and the operands of the solve.  T =
+  // (I + A)^{-1} Diag(beta) is never formed: W = T (K*gam) and U0 = T V come
+  // from block forward substitution on the right-hand sides beta (K*gam)
+  // and beta V, one row block a at a time,
+  //   Y_a = X_a (R_a - sum_{m<a} A_am Y_m),  X_a = (I + A_aa)^{-1},
+  // with each wave carrying one 16-column tile of Y in accumulators ----
   for (int f = w; f < NRT * NKC; f += NW) {
     const int rr = 16 * (f / NKC) + lr, i0 = 32 * (f % NKC) + 8 * lg;
     float pv[8];
@@ -1019,8 +1046,9 @@ __global__ __launch_bounds__(kIntraThreads, 4) void intra_chunk_kernel(KernelPtr
     for (int e = 0; e < 8; ++e) pv[e] = Ps[rr * SF + i0 + e];
     gst_pfrag8(M{}, blk + LY::kP + (size_t)f * LY::PF, l, pv);
   }
-  float* Xs = reinterpret_cast<float*>(smem + L::oX);
-  float* Ysc = reinterpret_cast<float*>(smem + L::oY);
+  constexpr int NOFF = L::NOFF;
+  float* XD = reinterpret_cast<float*>(smem + L::oXD);  // X_a, fp32 [NRT][16][17]
+  char* CF = smem + L::oCF;  // chain operands: A_am (a > m) in order, then X_a
   if (w == 0) {
     // diagonal 16x16 blocks: lane = 16*block + column
     const int bk = lg, jc = lr;
@@ -1045,50 +1073,35 @@ __global__ __launch_bounds__(kIntraThreads, 4) void intra_chunk_kernel(KernelPtr
         for (int s = 0; s < 16; ++s) cur[s] = nxt[s];
       }
 #pragma unroll
-      for (int s = 0; s < 16; ++s) Xs[(16 * bk + s) * SF + 16 * bk + jc] = x[s];
+      for (int s = 0; s < 16; ++s) XD[(16 * bk + s) * 17 + jc] = x[s];
+    }
+  } else {
+    // block p = a (a - 1) / 2 + m below the diagonal
+    for (int p = w - 1; p < NOFF; p += NW - 1) {
+      int a = 1;
+      while ((a + 1) * a / 2 <= p) ++a;
+      const int m = p - a * (a - 1) / 2;
+      float x[4];
+#pragma unroll
+      for (int e = 0; e < 4; ++e) x[e] = As[(16 * a + lr) * SF + 16 * m + 4 * lg + e];
+      cfrag_store(M{}, CF + (size_t)p * 1024, x);
     }
   }
-  __syncthreads();  // B6
-  // off-diagonal blocks, one level (a - b) at a time:
-  //   X_ab = -X_aa * sum_{m=b}^{a-1} A_am X_mb
-#pragma unroll
-  for (int lev = 1; lev < NRT; ++lev) {
-    const int a = lev + w, b = w;
-    const bool mine = (w < NRT - lev);
-    if (mine) {
-      f32x4 y = {0, 0, 0, 0};
-      for (int m = b; m < a; ++m) y = prod16(M{}, y, As, SF, 16 * a, 16 * m, Xs, SF, 16 * m, 16 * b);
-      float* Yw = Ysc + w * 16 * 17;
-#pragma unroll
-      for (int x = 0; x < 4; ++x) Yw[(4 * lg + x) * 17 + lr] = y[x];
-      // Yw is this wave's own scratch: wait for its writes, no block barrier.
-      __builtin_amdgcn_s_waitcnt(0xC07F);  // lgkmcnt(0)
-      __builtin_amdgcn_wave_barrier();
-    }
-    if (mine) {
-      f32x4 xab = {0, 0, 0, 0};
-      xab = prod16(M{}, xab, Xs, SF, 16 * a, 16 * a, Ysc + w * 16 * 17, 17, 0, 0);
-#pragma unroll
-      for (int x = 0; x < 4; ++x) Xs[(16 * a + 4 * lg + x) * SF + 16 * b + lr] = -xab[x];
-    }
-    __syncthreads();
-  }
+  __syncthreads();  // B6: A consumed; X_a in fp32
 
-  // ---- step 6: T = X Diag(beta) (lower triangle) kept in LDS as
-  // fragments (over the solve scratch) for the W and U0 products; (K*gam)^T
-  // staged.  V is fetched here for step 8 ----
+  // ---- step 6: X_a as chain operands; (K*gam)^T staged over A and P.  V
+  // is fetched here for step 8 ----
   Raw8<in_t> vraw[FPW], vext[PRO == 2 ? FPW : 1];
 #pragma unroll
   for (int j = 0; j < FPW; ++j) {
     vraw[j].load(reinterpret_cast<const in_t*>(kp.v) + ((size_t)tok * H + h) * D + 32 * fkb[j] + 8 * lg);
     if constexpr (PRO == 2) load_halo<in_t, D>(vext[j], kp, 2, it, rt, lr, 32 * fkb[j] + 8 * lg, si.total_tokens);
   }
-  for (int f = w; f < NRT * NKC; f += NW) {
-    const int rr = 16 * (f / NKC) + lr, i0 = 32 * (f % NKC) + 8 * lg;
-    float tv[8];
+  if (w < NRT) {
+    float x[4];
 #pragma unroll
-    for (int e = 0; e < 8; ++e) tv[e] = i0 + e <= rr ? Xs[rr * SF + i0 + e] * beta_s[i0 + e] : 0.f;
-    lds_st_pfrag(M{}, smem + L::oTf + (size_t)f * LY::PF, make_pfrag(M{}, tv));
+    for (int e = 0; e < 4; ++e) x[e] = XD[(16 * w + lr) * 17 + 4 * lg + e];
+    cfrag_store(M{}, CF + (size_t)(NOFF + w) * 1024, x);
   }
   LdsPrecise<M> KtT(smem + L::oKtT, L::kStPlain);
 #pragma unroll
@@ -1103,40 +1116,52 @@ __global__ __launch_bounds__(kIntraThreads, 4) void intra_chunk_kernel(KernelPtr
       KtT.store(c * SK + i, 0.f);
     }
   }
-  __syncthreads();  // B: (K*gam)^T staged
+  __syncthreads();  // B7: chain operands ready, (K*gam)^T staged
 
-  // ---- step 7: W^T = (K*gam)^T T^T for a pair of channel tiles (one W
-  // fragment column block) and one token tile.  Accumulator lane (lg, lr)
-  // holds four channels 4lg.. of token lr; lanes lg and lg^1 swap halves so
-  // each ends with eight consecutive channels of one token: one lane slot
-  // of the W fragment, written as a whole ----
-  for (int u = w; u < (NDT / 2) * NRT; u += NW) {
-    const int cp = u % (NDT / 2), wt = u / (NDT / 2);
-    f32x4 acc0 = {0, 0, 0, 0}, acc1 = {0, 0, 0, 0};
+  // The substitution for column tile ct of a right-hand side staged
+  // transposed in Rs ([columns x KC]): lane (lg, lr) reads tokens 16a +
+  // 4lg .. +3 of column 16ct + lr, the B-operand slot of its tile.
+  auto substitute = [&](const LdsPrecise<M>& Rs, int ct, f32x4 (&Y)[NRT]) {
 #pragma unroll
-    for (int kb = 0; kb < NKC; ++kb) {
-      if (32 * kb > 16 * wt + 15) break;
-      const PFrag tf = ld_pfrag(M{}, smem + L::oTf + (size_t)(wt * NKC + kb) * LY::PF);
-      acc0 = mma_pp(KtT.pfrag(SK, 32 * cp, 32 * kb), tf, acc0);
-      acc1 = mma_pp(KtT.pfrag(SK, 32 * cp + 16, 32 * kb), tf, acc1);
+    for (int a = 0; a < NRT; ++a) {
+      f32x4 acc = {0, 0, 0, 0};
+#pragma unroll
+      for (int m = 0; m < a; ++m) acc = chain_mma(M{}, CF + (size_t)(a * (a - 1) / 2 + m) * 1024, Y[m], acc);
+      float rh[4];
+      Rs.get4((16 * ct + lr) * SK + 16 * a + 4 * lg, rh);
+      f32x4 rhs;
+#pragma unroll
+      for (int e = 0; e < 4; ++e) rhs[e] = beta_s[16 * a + 4 * lg + e] * rh[e] - acc[e];
+      Y[a] = chain_mma(M{}, CF + (size_t)(NOFF + a) * 1024, rhs, f32x4{0, 0, 0, 0});
     }
-    const bool even = (lg & 1) == 0;
+  };
+
+  // ---- step 7: W.  Each wave solves one channel tile and writes it back
+  // over the columns of (K*gam)^T it alone read; W fragments then leave in
+  // the layout of the inter-chunk pass (lane slot: one token, eight
+  // consecutive channels) ----
+  if (w < NDT) {
+    f32x4 Y[NRT];
+    substitute(KtT, w, Y);
+#pragma unroll
+    for (int a = 0; a < NRT; ++a) {
+      const float y4[4] = {Y[a][0], Y[a][1], Y[a][2], Y[a][3]};
+      KtT.template storeN<4>((16 * w + lr) * SK + 16 * a + 4 * lg, y4);
+    }
+  }
+  __syncthreads();  // B8: W^T staged
+  for (int f = w; f < NRT * NKD; f += NW) {
+    const int wt = f / NKD, cb = f % NKD;
     float wv[8];
 #pragma unroll
-    for (int x = 0; x < 4; ++x) {
-      const float recv = __shfl_xor(even ? acc1[x] : acc0[x], 16);
-      wv[x] = even ? acc0[x] : recv;
-      wv[4 + x] = even ? recv : acc1[x];
-    }
-    // lane group lg -> k-group {0, 2, 1, 3}[lg] of the fragment
-    const int kgrp = ((lg & 1) << 1) | (lg >> 1);
-    gst_pfrag8(M{}, blk + LY::kW + (size_t)(wt * NKD + cp) * LY::PF, lr + 16 * kgrp, wv);
+    for (int e = 0; e < 8; ++e) wv[e] = KtT.get((32 * cb + 8 * lg + e) * SK + 16 * wt + lr);
+    gst_pfrag8(M{}, blk + LY::kW + (size_t)f * LY::PF, l, wv);
   }
-  __syncthreads();  // (K*gam)^T reads done
+  __syncthreads();  // B9: W^T reads done
 
-  // ---- step 8: U0 = T V, tile (token tile ut, value tile ct), stored in the
+  // ---- step 8: U0 = T V, tile (token tile a, value tile ct), stored in the
   // accumulator layout the inter-chunk pass adds to.  V^T is staged (split
-  // into hi + lo, so V need not be bf16-exact) over (K*gam)^T ----
+  // into hi + lo, so V need not be bf16-exact) over W^T ----
   LdsPrecise<M> VT(smem + L::oVT, L::kStPlain);
 #pragma unroll
   for (int j = 0; j < FPW; ++j)
@@ -1159,20 +1184,13 @@ __global__ __launch_bounds__(kIntraThreads, 4) void intra_chunk_kernel(KernelPtr
       VT.store(c * SK + i, 0.f);
     }
   }
-  __syncthreads();  // V^T staged
-  for (int u = w; u < NRT * NDT; u += NW) {
-    const int ut = u / NDT, ct = u % NDT;
-    f32x4 acc0 = {0, 0, 0, 0}, acc1 = {0, 0, 0, 0};
+  __syncthreads();  // B10: V^T staged
+  if (w < NDT) {
+    f32x4 Y[NRT];
+    substitute(VT, w, Y);
 #pragma unroll
-    for (int kb = 0; kb < NKC; ++kb) {
-      if (32 * kb > 16 * ut + 15) break;
-      const PFrag tf = ld_pfrag(M{}, smem + L::oTf + (size_t)(ut * NKC + kb) * LY::PF);
-      if (kb & 1)
-        acc1 = mma_pp(tf, VT.pfrag(SK, 16 * ct, 32 * kb), acc1);
-      else
-        acc0 = mma_pp(tf, VT.pfrag(SK, 16 * ct, 32 * kb), acc0);
-    }
-    *reinterpret_cast<f32x4*>(blk + LY::kU0 + (size_t)u * 1024 + l * 16) = acc0 + acc1;
+    for (int a = 0; a < NRT; ++a)
+      *reinterpret_cast<f32x4*>(blk + LY::kU0 + (size_t)(a * NDT + w) * 1024 + l * 16) = Y[a];
   }
 }
 
