@@ -1352,14 +1352,21 @@ __device__ __forceinline__ void inter_u_role(const KernelPtrs& kp, const InterGe
   const int last = gm.ci_hi - 1;
   // The chain's products keep two partial sums (even and odd k blocks) so
   // that consecutive MFMAs do not wait on each other's accumulator.
+  // The loads of later chunks are spread over the products: a fragment of
+  // this chunk is replaced by the one two chunks ahead right after its last
+  // use (W, U0), and the next chunk's K-bar and gam go into the other set
+  // between the K-bar^T U products, so the load path stays busy through the
+  // step instead of taking bursts that stall the issuing wave.
   auto step = [&](UF& f, UF& g, int ci) {
+    const char* b2 = blk_of(min(ci + 2, last));
+    const char* b1 = blk_of(min(ci + 1, last));
     __syncthreads();  // S^T published; last chunk's U^T reads done
-    if (act) {
-      f32x4 ws0[NCT], ws1[NCT];
+    f32x4 ws0[NCT], ws1[NCT];
 #pragma unroll
-      for (int ct = 0; ct < NCT; ++ct) { ws0[ct] = f32x4{0, 0, 0, 0}; ws1[ct] = ws0[ct]; }
+    for (int ct = 0; ct < NCT; ++ct) { ws0[ct] = f32x4{0, 0, 0, 0}; ws1[ct] = ws0[ct]; }
 #pragma unroll
-      for (int kb = 0; kb < NKD; ++kb)
+    for (int kb = 0; kb < NKD; ++kb) {
+      if (act) {
 #pragma unroll
         for (int ct = 0; ct < NCT; ++ct) {
           const auto sf = ST.pfrag(SD, 16 * ct, 32 * kb);
@@ -1368,6 +1375,10 @@ __device__ __forceinline__ void inter_u_role(const KernelPtrs& kp, const InterGe
           else
             ws0[ct] = mma_pp(f.W[kb], sf, ws0[ct]);
         }
+      }
+      f.W[kb] = ld_pfrag(M{}, b2 + LY::kW + (size_t)(rt * NKD + kb) * LY::PF);
+    }
+    if (act) {
 #pragma unroll
       for (int ct = 0; ct < NCT; ++ct) {
         float v4[4];
@@ -1376,7 +1387,10 @@ __device__ __forceinline__ void inter_u_role(const KernelPtrs& kp, const InterGe
         UT.template storeN<4>((16 * ct + (l & 15)) * SK + 16 * rt + 4 * (l >> 4), v4);
       }
     }
-    load_u1<M, D, C, NCT>(f, blk_of(min(ci + 2, last)), rt, vt0);
+#pragma unroll
+    for (int ct = 0; ct < NCT; ++ct)
+      f.U0[ct] = *reinterpret_cast<const f32x4*>(b2 + LY::kU0 + (size_t)(rt * NDT + vt0 + ct) * 1024 +
+                                                 l * 16);
     __syncthreads();  // U^T published; S^T reads done
     f32x4 S1[NST][NCT];
 #pragma unroll
@@ -1388,7 +1402,14 @@ __device__ __forceinline__ void inter_u_role(const KernelPtrs& kp, const InterGe
         for (int x = 0; x < 4; ++x) S[s][ct][x] *= f.gam[s][x];
       }
 #pragma unroll
-    for (int kb = 0; kb < NKC; ++kb)
+    for (int s = 0; s < NST; ++s) {
+      const f32x4 gv = *reinterpret_cast<const f32x4*>(
+          reinterpret_cast<const float*>(b1 + LY::kGam) + 16 * (w * NST + s) + 4 * (l >> 4));
+#pragma unroll
+      for (int x = 0; x < 4; ++x) g.gam[s][x] = gv[x];
+    }
+#pragma unroll
+    for (int kb = 0; kb < NKC; ++kb) {
 #pragma unroll
       for (int ct = 0; ct < NCT; ++ct) {
         const auto uf = UT.pfrag(SK, 16 * ct, 32 * kb);
@@ -1401,10 +1422,13 @@ __device__ __forceinline__ void inter_u_role(const KernelPtrs& kp, const InterGe
         }
       }
 #pragma unroll
+      for (int s = 0; s < NST; ++s)
+        g.Kb[s][kb] = ld_pfrag(M{}, b1 + LY::kKb + (size_t)((w * NST + s) * NKC + kb) * LY::PF);
+    }
+#pragma unroll
     for (int s = 0; s < NST; ++s)
 #pragma unroll
       for (int ct = 0; ct < NCT; ++ct) S[s][ct] += S1[s][ct];
-    load_u2<M, D, C, NCT>(g, blk_of(min(ci + 1, last)), w);
     publish_state();
   };
 
@@ -1452,19 +1476,21 @@ __device__ __forceinline__ void inter_o_role(const KernelPtrs& kp, const InterGe
   auto blk_of = [&](int ci) { return kp.ops + ((size_t)(gm.cbase + ci) * H + gm.h) * LY::kBytes; };
   const int last = gm.ci_hi - 1;
 
+  // Loads spread over the products as in the U-waves: Q*gam fragments two
+  // chunks ahead replace this chunk's right after use; the next chunk's P
+  // fragments go into the other set between the P U products.
   auto step = [&](OF& f, OF& g, int ci) {
     const int t0 = gm.bos + ci * C;
     const int len = gm.eos - t0 < C ? gm.eos - t0 : C;
+    const char* b2 = blk_of(min(ci + 2, last));
+    const char* b1 = blk_of(min(ci + 1, last));
     __syncthreads();  // S^T published
-    f32x4 qs[NCT];
+    f32x4 qs[NCT], qs1[NCT];
 #pragma unroll
-    for (int ct = 0; ct < NCT; ++ct) qs[ct] = f32x4{0, 0, 0, 0};
-    if (act) {
-      f32x4 qs1[NCT];
+    for (int ct = 0; ct < NCT; ++ct) { qs[ct] = f32x4{0, 0, 0, 0}; qs1[ct] = qs[ct]; }
 #pragma unroll
-      for (int ct = 0; ct < NCT; ++ct) qs1[ct] = f32x4{0, 0, 0, 0};
-#pragma unroll
-      for (int kb = 0; kb < NKD; ++kb)
+    for (int kb = 0; kb < NKD; ++kb) {
+      if (act) {
 #pragma unroll
         for (int ct = 0; ct < NCT; ++ct) {
           const auto sf = ST.pfrag(SD, 16 * ct, 32 * kb);
@@ -1473,19 +1499,25 @@ __device__ __forceinline__ void inter_o_role(const KernelPtrs& kp, const InterGe
           else
             qs[ct] = mma_pp(f.Qt[kb], sf, qs[ct]);
         }
-#pragma unroll
-      for (int ct = 0; ct < NCT; ++ct) qs[ct] += qs1[ct];
+      }
+      f.Qt[kb] = ld_pfrag(M{}, b2 + LY::kQt + (size_t)(rt * NKD + kb) * LY::PF);
     }
-    load_o1<M, D, C>(f, blk_of(min(ci + 2, last)), rt);
+#pragma unroll
+    for (int ct = 0; ct < NCT; ++ct) qs[ct] += qs1[ct];
     __syncthreads();  // U^T published
+#pragma unroll
+    for (int kb = 0; kb < NKC; ++kb) {
+      // P is lower triangular: token blocks past this row tile are zero.
+      if (act && 32 * kb <= 16 * rt + 15) {
+#pragma unroll
+        for (int ct = 0; ct < NCT; ++ct) qs[ct] = mma_pp(f.P[kb], UT.pfrag(SK, 16 * ct, 32 * kb), qs[ct]);
+      }
+      g.P[kb] = ld_pfrag(M{}, b1 + LY::kP + (size_t)(rt * NKC + kb) * LY::PF);
+    }
     if (act) {
 #pragma unroll
       for (int ct = 0; ct < NCT; ++ct) {
-        f32x4 o = qs[ct];
-        // P is lower triangular: token blocks past this row tile are zero.
-#pragma unroll
-        for (int kb = 0; kb < NKC; ++kb)
-          if (32 * kb <= 16 * rt + 15) o = mma_pp(f.P[kb], UT.pfrag(SK, 16 * ct, 32 * kb), o);
+        const f32x4 o = qs[ct];
 #pragma unroll
         for (int x = 0; x < 4; ++x) {
           const int row = 16 * rt + 4 * (l >> 4) + x;
@@ -1504,7 +1536,6 @@ __device__ __forceinline__ void inter_o_role(const KernelPtrs& kp, const InterGe
         }
       }
     }
-    load_o2<M, D, C>(g, blk_of(min(ci + 1, last)), rt);
   };
 
   OF fa, fb;
