@@ -613,6 +613,30 @@ __device__ __forceinline__ float row_shr(float x) {
                                                                0x110 + N, 0xF, 0xF, false));
 }
 
+// Exchange with the lane whose index differs in bit 0 (X = 1) or bit 1
+// (X = 2), by a DPP quad permutation.  Every lane of the wave must execute it.
+template <int X>
+__device__ __forceinline__ float quad_xor(float x) {
+  constexpr int ctrl = X == 1 ? 0xB1 : 0x4E;  // quad_perm [1,0,3,2] / [2,3,0,1]
+  return __builtin_bit_cast(float, __builtin_amdgcn_update_dpp(0, __builtin_bit_cast(int, x), ctrl,
+                                                               0xF, 0xF, false));
+}
+
+// 4x4 transpose within each quad of lanes: if lane j of the quad holds
+// a[i] = M[i][j], lane r ends with M[r][0..3].  Two butterfly rounds: the
+// off-diagonal 2x2 blocks swap between lanes r and r^2, then the elements
+// of each 2x2 block between lanes r and r^1.  Every lane must execute it.
+__device__ __forceinline__ f32x4 quad_transpose(f32x4 a) {
+  const int r = lane_id() & 3;
+  const bool h2 = (r & 2) != 0, h1 = (r & 1) != 0;
+  float w0 = quad_xor<2>(h2 ? a[0] : a[2]), w1 = quad_xor<2>(h2 ? a[1] : a[3]);
+  if (h2) { a[0] = w0; a[1] = w1; } else { a[2] = w0; a[3] = w1; }
+  w0 = quad_xor<1>(h1 ? a[0] : a[1]);
+  w1 = quad_xor<1>(h1 ? a[2] : a[3]);
+  if (h1) { a[0] = w0; a[2] = w1; } else { a[1] = w0; a[3] = w1; }
+  return a;
+}
+
 // Inclusive prefix sum over the 16 lanes of each row.
 __device__ __forceinline__ float row_scan16(float x) {
   x += row_shr<1>(x);
@@ -1515,22 +1539,27 @@ __device__ __forceinline__ void inter_o_role(const KernelPtrs& kp, const InterGe
       g.P[kb] = ld_pfrag(M{}, b1 + LY::kP + (size_t)(rt * NKC + kb) * LY::PF);
     }
     if (act) {
+      // After a transpose inside each lane quad, lane l holds four
+      // consecutive columns 4((l & 15) >> 2) .. of row 4(l >> 4) + (l & 3):
+      // one vector store per lane and tile.
+      const int row = 16 * rt + 4 * (l >> 4) + (l & 3);
 #pragma unroll
       for (int ct = 0; ct < NCT; ++ct) {
-        const f32x4 o = qs[ct];
+        const f32x4 o = quad_transpose(qs[ct]);
+        const int col = gm.col0 + 16 * ct + 4 * ((l & 15) >> 2);
+        if (row < len) {
+          if (kp.o_slots) {  // raw o for the layer epilogue
+            *reinterpret_cast<f32x4*>(kp.o_slots + (((size_t)(gm.cbase + ci) * H + gm.h) * C + row) * D +
+                                      col) = o;
+          } else {
+            const size_t oi = ((size_t)(t0 + row) * H + gm.h) * D + col;
+            if constexpr (OUT_BF16) {
+              bf16x4 ob;
 #pragma unroll
-        for (int x = 0; x < 4; ++x) {
-          const int row = 16 * rt + 4 * (l >> 4) + x;
-          if (row < len) {
-            const int col = gm.col0 + 16 * ct + (l & 15);
-            if (kp.o_slots) {  // raw o for the layer epilogue
-              kp.o_slots[(((size_t)(gm.cbase + ci) * H + gm.h) * C + row) * D + col] = o[x];
+              for (int x = 0; x < 4; ++x) ob[x] = f2bf(o[x]);
+              *reinterpret_cast<bf16x4*>(reinterpret_cast<bf16*>(kp.o) + oi) = ob;
             } else {
-              const size_t oi = ((size_t)(t0 + row) * H + gm.h) * D + col;
-              if constexpr (OUT_BF16)
-                reinterpret_cast<bf16*>(kp.o)[oi] = f2bf(o[x]);
-              else
-                reinterpret_cast<float*>(kp.o)[oi] = o[x];
+              *reinterpret_cast<f32x4*>(reinterpret_cast<float*>(kp.o) + oi) = o;
             }
           }
         }
