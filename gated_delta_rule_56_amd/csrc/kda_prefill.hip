@@ -1063,7 +1063,10 @@ __global__ __launch_bounds__(kIntraThreads, 4) void intra_chunk_kernel(KernelPtr
   // and beta V, one row block a at a time,
   //   Y_a = X_a (R_a - sum_{m<a} A_am Y_m),  X_a = (I + A_aa)^{-1},
   // with each wave carrying one 16-column tile of Y in accumulators ----
+  // P fragments above the diagonal are zero: they are neither written nor
+  // read.
   for (int f = w; f < NRT * NKC; f += NW) {
+    if (32 * (f % NKC) > 16 * (f / NKC) + 15) continue;
     const int rr = 16 * (f / NKC) + lr, i0 = 32 * (f % NKC) + 8 * lg;
     float pv[8];
 #pragma unroll
@@ -1292,11 +1295,12 @@ __device__ __forceinline__ void load_o1(OFrags<M, D, C>& f, const char* blk, int
   for (int kb = 0; kb < LY::NKD; ++kb)
     f.Qt[kb] = ld_pfrag(M{}, blk + LY::kQt + (size_t)(rt * LY::NKD + kb) * LY::PF);
 }
-template <class M, int D, int C>
+// The first NP token blocks of P (the rest of the row tile is zero).
+template <class M, int D, int C, int NP>
 __device__ __forceinline__ void load_o2(OFrags<M, D, C>& f, const char* blk, int rt) {
   typedef Layout<M, D, C> LY;
 #pragma unroll
-  for (int kb = 0; kb < LY::NKC; ++kb)
+  for (int kb = 0; kb < NP; ++kb)
     f.P[kb] = ld_pfrag(M{}, blk + LY::kP + (size_t)(rt * LY::NKC + kb) * LY::PF);
 }
 
@@ -1482,7 +1486,8 @@ __device__ __forceinline__ void inter_u_role(const KernelPtrs& kp, const InterGe
   }
 }
 
-template <class M, int D, int C, int NCT, bool OUT_BF16>
+// NP: token blocks of P that are not zero for this wave's row tile.
+template <class M, int D, int C, int NCT, bool OUT_BF16, int NP>
 __device__ __forceinline__ void inter_o_role(const KernelPtrs& kp, const InterGeom& gm, char* smem,
                                              int r) {
   typedef Layout<M, D, C> LY;
@@ -1530,9 +1535,8 @@ __device__ __forceinline__ void inter_o_role(const KernelPtrs& kp, const InterGe
     for (int ct = 0; ct < NCT; ++ct) qs[ct] += qs1[ct];
     __syncthreads();  // U^T published
 #pragma unroll
-    for (int kb = 0; kb < NKC; ++kb) {
-      // P is lower triangular: token blocks past this row tile are zero.
-      if (act && 32 * kb <= 16 * rt + 15) {
+    for (int kb = 0; kb < NP; ++kb) {
+      if (act) {
 #pragma unroll
         for (int ct = 0; ct < NCT; ++ct) qs[ct] = mma_pp(f.P[kb], UT.pfrag(SK, 16 * ct, 32 * kb), qs[ct]);
       }
@@ -1570,7 +1574,7 @@ __device__ __forceinline__ void inter_o_role(const KernelPtrs& kp, const InterGe
   OF fa, fb;
   if (gm.ci_lo < gm.ci_hi) {
     load_o1<M, D, C>(fa, blk_of(gm.ci_lo), rt);
-    load_o2<M, D, C>(fa, blk_of(gm.ci_lo), rt);
+    load_o2<M, D, C, NP>(fa, blk_of(gm.ci_lo), rt);
     load_o1<M, D, C>(fb, blk_of(min(gm.ci_lo + 1, last)), rt);
   }
   for (int ci = gm.ci_lo; ci < gm.ci_hi; ci += 2) {
@@ -1671,10 +1675,18 @@ __global__ __launch_bounds__(kInterThreads, 2) void inter_chunk_kernel(KernelPtr
       UT.store((idx / (KC - C)) * L::SK + C + idx % (KC - C), 0.f);
   }
   const int w = wave_id();
-  if (w < 4)
+  constexpr int NRT = LY::NRT, NKC = LY::NKC;
+  static_assert(NKC <= 2, "P spans at most two token blocks");
+  if (w < 4) {
     inter_u_role<M, D, C, NCT>(kp, gm, smem, w);
-  else
-    inter_o_role<M, D, C, NCT, OUT_BF16>(kp, gm, smem, w - 4);
+  } else {
+    // P is lower triangular: row tiles 0 and 1 use only its first 32 tokens.
+    const int rt = NRT == 4 ? w - 4 : min(w - 4, NRT - 1);
+    if (NKC == 2 && 16 * rt + 15 >= 32)
+      inter_o_role<M, D, C, NCT, OUT_BF16, NKC>(kp, gm, smem, w - 4);
+    else
+      inter_o_role<M, D, C, NCT, OUT_BF16, 1>(kp, gm, smem, w - 4);
+  }
 }
 
 // The carried inputs of the short convolution after the call: the last W-1
