@@ -203,6 +203,8 @@ struct FwdLds {
   float S[D][kCols];
   float R[C][kCols];
   float U[C][kCols];
+  float V[C][kCols];
+  float gn[D];
 };
 
 constexpr int kSerThreads = 512;
@@ -229,13 +231,17 @@ __global__ __launch_bounds__(kSerThreads) void bwd_fwd_states_kernel(Planes p, G
   }
   Prefetch<C, D, NT> pKt, pKb;
   Prefetch<C, C, NT> pT;
+  Prefetch<C, kCols, NT, D> pV;  // this workgroup's value columns
+  Prefetch<1, D, NT> pG;         // gam_n
   auto blk = [&](int ci) { return (size_t)(base + ci) * H + h; };
-  if (nch > 0) {
-    const size_t b0 = blk(0);
-    pKt.load(p.Kt + b0 * C * D);
-    pKb.load(p.Kb + b0 * C * D);
-    pT.load(p.T + b0 * C * C);
-  }
+  auto fetch = [&](size_t b) {
+    pKt.load(p.Kt + b * C * D);
+    pKb.load(p.Kb + b * C * D);
+    pT.load(p.T + b * C * C);
+    pV.load(p.V + b * C * D + col0);
+    pG.load(p.gn + b * D);
+  };
+  if (nch > 0) fetch(blk(0));
   for (int ci = 0; ci < nch; ++ci) {
     const size_t b = blk(ci);
     const size_t pcd = b * C * D;
@@ -243,17 +249,14 @@ __global__ __launch_bounds__(kSerThreads) void bwd_fwd_states_kernel(Planes p, G
     pKt.template store<D + 4>(&L.Kt[0][0]);
     pKb.template store<D + 16>(&L.Kb[0][0]);
     pT.template store<C + 4>(&L.T[0][0]);
+    pV.template store<kCols>(&L.V[0][0]);
+    pG.template store<D>(&L.gn[0]);
     for (int idx = tid; idx < D * kCols; idx += NT) {
       const int i = idx / kCols, j = idx % kCols;
       p.S[(b * D + i) * D + col0 + j] = L.S[i][j];
     }
     __syncthreads();
-    if (ci + 1 < nch) {
-      const size_t bn = blk(ci + 1);
-      pKt.load(p.Kt + bn * C * D);
-      pKb.load(p.Kb + bn * C * D);
-      pT.load(p.T + bn * C * C);
-    }
+    if (ci + 1 < nch) fetch(blk(ci + 1));
     for (int rt = w; rt < C / 16; rt += NW) {  // R = V - Kt S
       f32x4 acc = {0, 0, 0, 0}, acc1 = {0, 0, 0, 0};
 #pragma unroll 8
@@ -264,7 +267,7 @@ __global__ __launch_bounds__(kSerThreads) void bwd_fwd_states_kernel(Planes p, G
 #pragma unroll
       for (int i = 0; i < 4; ++i) {
         const int r = 16 * rt + 4 * g + i;
-        const float x = p.V[pcd + r * D + col0 + m] - acc[i] - acc1[i];
+        const float x = L.V[r][m] - acc[i] - acc1[i];
         L.R[r][m] = x;
         p.R[pcd + r * D + col0 + m] = x;
       }
@@ -286,7 +289,7 @@ __global__ __launch_bounds__(kSerThreads) void bwd_fwd_states_kernel(Planes p, G
 #pragma unroll
       for (int i = 0; i < 4; ++i) {
         const int c = 16 * t + 4 * g + i;
-        acc[i] = p.gn[b * D + c] * L.S[c][m];
+        acc[i] = L.gn[c] * L.S[c][m];
       }
 #pragma unroll 8
       for (int k0 = 0; k0 < C; k0 += 8) {
@@ -316,6 +319,7 @@ struct BwdLds {
   float dO[C][kCols];
   float dU[C][kCols];
   float ndR[C][kCols];   // -dR
+  float gn[D];
 };
 
 // Serial backward over a sequence's chunks for 16 value columns: dS' of
@@ -342,12 +346,25 @@ __global__ __launch_bounds__(kSerThreads) void bwd_bwd_states_kernel(Planes p, G
   }
   Prefetch<C, C, NT> pP, pT;
   Prefetch<C, D, NT> pKb, pQt, pKt;
+  Prefetch<C, kCols, NT, D> pdO;  // this workgroup's value columns
+  Prefetch<1, D, NT> pG;          // gam_n
   auto blk = [&](int ci) { return (size_t)(base + ci) * H + h; };
+  // P, T, K-bar, dO and gam_n of a chunk load a step ahead, Q*gam and K*gam
+  // half a step ahead (after the previous chunk's copies are stored).
+  auto fetch_a = [&](size_t b) {
+    pP.load(p.P + b * C * C);
+    pT.load(p.T + b * C * C);
+    pKb.load(p.Kb + b * C * D);
+    pdO.load(p.dO + b * C * D + col0);
+    pG.load(p.gn + b * D);
+  };
+  auto fetch_b = [&](size_t b) {
+    pQt.load(p.Qt + b * C * D);
+    pKt.load(p.Kt + b * C * D);
+  };
   if (nch > 0) {
-    const size_t b0 = blk(nch - 1);
-    pP.load(p.P + b0 * C * C);
-    pT.load(p.T + b0 * C * C);
-    pKb.load(p.Kb + b0 * C * D);
+    fetch_a(blk(nch - 1));
+    fetch_b(blk(nch - 1));
   }
   for (int ci = nch - 1; ci >= 0; --ci) {
     const size_t b = blk(ci);
@@ -356,23 +373,14 @@ __global__ __launch_bounds__(kSerThreads) void bwd_bwd_states_kernel(Planes p, G
     pP.template store<C + 16>(&L.u.a.P[0][0]);
     pT.template store<C + 16>(&L.u.a.T[0][0]);
     pKb.template store<D + 4>(&L.u.a.Kb[0][0]);
-    pQt.load(p.Qt + pcd);
-    pKt.load(p.Kt + pcd);
-    for (int idx = tid; idx < C * kCols; idx += NT) {
-      const int r = idx / kCols, j = idx % kCols;
-      L.dO[r][j] = p.dO[pcd + r * D + col0 + j];
-    }
+    pdO.template store<kCols>(&L.dO[0][0]);
+    pG.template store<D>(&L.gn[0]);
     for (int idx = tid; idx < D * kCols; idx += NT) {
       const int i = idx / kCols, j = idx % kCols;
       p.dSn[(b * D + i) * D + col0 + j] = L.X[i][j];
     }
     __syncthreads();
-    if (ci > 0) {
-      const size_t bn = blk(ci - 1);
-      pP.load(p.P + bn * C * C);
-      pT.load(p.T + bn * C * C);
-      pKb.load(p.Kb + bn * C * D);
-    }
+    if (ci > 0) fetch_a(blk(ci - 1));
     for (int rt = w; rt < C / 16; rt += NW) {  // dU = P^T dO + Kb dS'
       f32x4 acc = {0, 0, 0, 0}, acc1 = {0, 0, 0, 0};
       for (int k0 = 16 * rt; k0 < C; k0 += 4) acc = mfma4(L.u.a.P[k0 + g][16 * rt + m], L.dO[k0 + g][m], acc);
@@ -403,13 +411,14 @@ __global__ __launch_bounds__(kSerThreads) void bwd_bwd_states_kernel(Planes p, G
     __syncthreads();
     pQt.template store<D + 16>(&L.u.b.Qt[0][0]);
     pKt.template store<D + 16>(&L.u.b.Kt[0][0]);
+    if (ci > 0) fetch_b(blk(ci - 1));
     __syncthreads();
     for (int t = w; t < D / 16; t += NW) {  // dS = gam_n dS' + Qt^T dO - Kt^T dR
       f32x4 acc, acc1 = {0, 0, 0, 0};
 #pragma unroll
       for (int i = 0; i < 4; ++i) {
         const int c = 16 * t + 4 * g + i;
-        acc[i] = p.gn[b * D + c] * L.X[c][m];
+        acc[i] = L.gn[c] * L.X[c][m];
       }
 #pragma unroll 8
       for (int k0 = 0; k0 < C; k0 += 4) {

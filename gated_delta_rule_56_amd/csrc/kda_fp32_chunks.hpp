@@ -160,21 +160,22 @@ __global__ __launch_bounds__(256) void fp32_gemm_kernel(const float* __restrict_
 }
 
 // Register-staged copy of a ROWS x COLS fp32 block (row-major in global
-// memory) spread over NT threads: load() issues every load of the thread,
-// store<LD>() writes the block into LDS with row stride LD (a multiple of 4,
-// so each write is one 16-byte LDS store).  Loading the next chunk's
-// operands while the current chunk computes hides their latency.
-template <int ROWS, int COLS, int NT>
+// memory with row stride SLD, COLS by default) spread over NT threads:
+// load() issues every load of the thread, store<LD>() writes the block into
+// LDS with row stride LD (a multiple of 4, so each write is one 16-byte LDS
+// store).  Loading the next chunk's operands while the current chunk
+// computes hides their latency.
+template <int ROWS, int COLS, int NT, int SLD = COLS>
 struct Prefetch {
   static constexpr int C4 = COLS / 4, N = (ROWS * C4 + NT - 1) / NT;
-  static_assert(COLS % 4 == 0, "float4 rows");
+  static_assert(COLS % 4 == 0 && SLD % 4 == 0, "float4 rows");
   f32x4 v[N];
   __device__ __forceinline__ void load(const float* __restrict__ src) {
 #pragma unroll
     for (int x = 0; x < N; ++x) {
       const int idx = threadIdx.x + NT * x;
       if (idx < ROWS * C4)
-        v[x] = *reinterpret_cast<const f32x4*>(src + (size_t)(idx / C4) * COLS + 4 * (idx % C4));
+        v[x] = *reinterpret_cast<const f32x4*>(src + (size_t)(idx / C4) * SLD + 4 * (idx % C4));
     }
   }
   template <int LD>
