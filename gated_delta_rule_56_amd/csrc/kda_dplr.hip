@@ -196,6 +196,8 @@ struct StLds {
   float U[C][kColsD];
   float Yb[C][kColsD];
   float Vb[C][kColsD];
+  float OV[C][kColsD];
+  float gn[D];
 };
 
 constexpr int kStThreads = 512;
@@ -226,13 +228,23 @@ __global__ __launch_bounds__(kStThreads) void dplr_states_kernel(DPlanes p, Geo 
   }
   Prefetch<C, D, NT> pW, pQ, pA, pK;
   Prefetch<C, C, NT> pP;
+  Prefetch<C, kColsD, NT, D> pY, pV, pOV;  // this workgroup's value columns
+  Prefetch<1, D, NT> pG;                   // gam_n
   auto blk = [&](int ci) { return (size_t)(base + ci) * H + h; };
-  if (nch > 0) {
-    const size_t b0 = blk(0);
-    pW.load(p.Wb + b0 * C * D);
-    pQ.load(p.Qt + b0 * C * D);
-    pP.load(p.Aqa + b0 * C * C);
-  }
+  // The first-half operands of a chunk (and its value-column slices and
+  // gam_n) load a step ahead; Ab and Kb at the start of their chunk.
+  auto fetch = [&](size_t b) {
+    pW.load(p.Wb + b * C * D);
+    pQ.load(p.Qt + b * C * D);
+    pP.load(p.Aqa + b * C * C);
+    pY.load(p.Y + b * C * D + col0);
+    if (!TIED) {
+      pV.load(p.V + b * C * D + col0);
+      pOV.load(p.OV + b * C * D + col0);
+    }
+    pG.load(p.gn + b * D);
+  };
+  if (nch > 0) fetch(blk(0));
   for (int ci = 0; ci < nch; ++ci) {
     const size_t b = blk(ci);
     const size_t pcd = b * C * D;
@@ -241,20 +253,16 @@ __global__ __launch_bounds__(kStThreads) void dplr_states_kernel(DPlanes p, Geo 
     pW.template store<D + 4>(&L.u.a.Wb[0][0]);
     pQ.template store<D + 4>(&L.u.a.Qt[0][0]);
     pP.template store<C + 4>(&L.u.a.Aqa[0][0]);
+    pY.template store<kColsD>(&L.Yb[0][0]);
+    if (!TIED) {
+      pV.template store<kColsD>(&L.Vb[0][0]);
+      pOV.template store<kColsD>(&L.OV[0][0]);
+    }
+    pG.template store<D>(&L.gn[0]);
     pA.load(p.Ab + pcd);
     if (!TIED) pK.load(p.Kb + pcd);
-    for (int idx = tid; idx < C * kColsD; idx += NT) {
-      const int r = idx / kColsD, j = idx % kColsD;
-      L.Yb[r][j] = p.Y[pcd + r * D + col0 + j];
-      if (!TIED) L.Vb[r][j] = p.V[pcd + r * D + col0 + j];
-    }
     __syncthreads();
-    if (ci + 1 < nch) {  // the next chunk's first-half operands
-      const size_t bn = blk(ci + 1);
-      pW.load(p.Wb + bn * C * D);
-      pQ.load(p.Qt + bn * C * D);
-      pP.load(p.Aqa + bn * C * C);
-    }
+    if (ci + 1 < nch) fetch(blk(ci + 1));
     for (int rt = w; rt < C / 16; rt += NW) {  // U~ = Y - Wb S
       f32x4 acc = {0, 0, 0, 0}, acc1 = {0, 0, 0, 0};
 #pragma unroll 8
@@ -278,7 +286,7 @@ __global__ __launch_bounds__(kStThreads) void dplr_states_kernel(DPlanes p, Geo 
       for (int i = 0; i < 4; ++i) {
         const int r = 16 * rt + 4 * g + i;
         float x = acc[i] + acc1[i];
-        if (!TIED) x += p.OV[pcd + r * D + col0 + m];
+        if (!TIED) x += L.OV[r][m];
         if (r < len) o[((size_t)(t0 + r) * H + h) * D + col0 + m] = x;
       }
     }
@@ -291,7 +299,7 @@ __global__ __launch_bounds__(kStThreads) void dplr_states_kernel(DPlanes p, Geo 
 #pragma unroll
       for (int i = 0; i < 4; ++i) {
         const int c = 16 * t + 4 * g + i;
-        acc[i] = p.gn[b * D + c] * L.S[c][m];
+        acc[i] = L.gn[c] * L.S[c][m];
       }
 #pragma unroll 8
       for (int k0 = 0; k0 < C; k0 += 4) {
