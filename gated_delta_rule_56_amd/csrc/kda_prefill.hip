@@ -309,6 +309,8 @@ __device__ __forceinline__ f32x4 chain_mma(ModeF32, const char* p, f32x4 y, f32x
 // ---------------------------------------------------------------------------
 constexpr size_t cmax(size_t a, size_t b) { return a > b ? a : b; }
 
+constexpr int kMaxConv = 4;  // widest short convolution
+
 template <class M, int D, int C>
 struct IntraLds {
   typedef typename M::in_t plain_t;  // element of one half of a precise matrix
@@ -333,6 +335,10 @@ struct IntraLds {
   static constexpr size_t oNrm = oBeta + (size_t)KC * 4;      // fp32 [8 waves][16][2]
   static constexpr size_t oRn = oNrm + 8 * 16 * 2 * 4;         // fp32 [C][2]
   static constexpr size_t kTotal = oRn + (size_t)C * 2 * 4;
+  // With the convolution: v's weights, [D][kMaxConv] fp32, taps from the
+  // current row back (q's and k's sit in R0 while the prologue runs).
+  static constexpr size_t oCWv = kTotal;
+  static constexpr size_t kTotalConv = oCWv + (size_t)D * kMaxConv * 4;
   // offsets inside the regions
   static constexpr size_t oKbS = oR0;                    // staging
   static constexpr size_t oKh = oR0, oG = oR0;           // Gram operands / Gamma
@@ -574,7 +580,6 @@ __device__ __forceinline__ Item intra_item(const SeqInfo& si, const KernelPtrs& 
 // starting at bos, y_c = sum_{i<W} w[c][i] x_c(t - (W-1) + i), where inputs
 // before bos come from the carried state (row (W-1) + (s - bos)), or are zero.
 // ---------------------------------------------------------------------------
-constexpr int kMaxConv = 4;
 
 // The inputs one lane needs besides its own token row r = 16 rt + lr: lanes
 // lr >= 16 - (kMaxConv - 1) load the rows 16 rt - 3 .. 16 rt - 1 of the chunk
@@ -648,26 +653,37 @@ __device__ __forceinline__ float row_scan16(float x) {
 
 // Convolved values of one lane's 8 channels (c0 .. c0 + 7) of row 16 rt + lr,
 // from the lane's own row and the halo rows of lanes 13..15 of its 16-lane
-// group: tap i reads row lr - i, the own value of lane lr - i, or for
-// lr < i the halo value of lane lr - i + 16 (both one row rotation).
+// group: tap j reads row lr - j, the own value of lane lr - j, or for
+// lr < j the halo value of lane lr - j + 16 (both one row rotation).  w4
+// holds the channels' weights in LDS, [8][kMaxConv], w4[4e + j] the weight
+// of row lr - j; taps at or past the width W are skipped.
 template <class T>
-__device__ __forceinline__ void conv8(const Raw8<T>& own, const Raw8<T>& ext, const float* wrow,
+__device__ __forceinline__ void conv8(const Raw8<T>& own, const Raw8<T>& ext, const float* w4,
                                       int W, int lr, float out[8]) {
+  static_assert(kMaxConv == 4, "three taps before the current row");
 #pragma unroll
   for (int e = 0; e < 8; ++e) {
     const float xo = own.get(e), xe = ext.get(e);
-    float acc = wrow[e * W + W - 1] * xo;
+    float acc = w4[4 * e] * xo;
     // Both rotations run on every lane (a conditional operator would run
     // only one, under a divergent branch, and read inactive lanes).
     const float o1 = row_ror<1>(xo), e1 = row_ror<1>(xe);
     const float o2 = row_ror<2>(xo), e2 = row_ror<2>(xe);
     const float o3 = row_ror<3>(xo), e3 = row_ror<3>(xe);
     const float t1 = lr >= 1 ? o1 : e1, t2 = lr >= 2 ? o2 : e2, t3 = lr >= 3 ? o3 : e3;
-    static_assert(kMaxConv == 4, "three taps before the current row");
-    if (W > 1) acc += wrow[e * W + W - 2] * t1;
-    if (W > 2) acc += wrow[e * W + W - 3] * t2;
-    if (W > 3) acc += wrow[e * W + W - 4] * t3;
+    if (W > 1) acc += w4[4 * e + 1] * t1;
+    if (W > 2) acc += w4[4 * e + 2] * t2;
+    if (W > 3) acc += w4[4 * e + 3] * t3;
     out[e] = acc;
+  }
+}
+
+// One head's convolution weights [D][W] (global) into LDS as [D][kMaxConv],
+// taps reordered from the current row back and zero past W.
+__device__ __forceinline__ void stage_conv_weights(float* dst, const float* src, int D, int W) {
+  for (int idx = threadIdx.x; idx < D * kMaxConv; idx += blockDim.x) {
+    const int c = idx / kMaxConv, j = idx % kMaxConv;
+    dst[idx] = j < W ? src[(size_t)c * W + (W - 1 - j)] : 0.f;
   }
 }
 
@@ -757,16 +773,24 @@ __global__ __launch_bounds__(kIntraThreads, 4) void intra_chunk_kernel(KernelPtr
   float qc[PRO == 2 ? FPW : 1][8], kc_reg[PRO == 2 && !kPark ? FPW : 1][8];
   f32x4* kpark = reinterpret_cast<f32x4*>(smem + L::oR1) + 2 * (64 * (FPW * w) + l);
   if constexpr (PRO == 2) {
+    // The head's weights into LDS first (q's and k's in R0, unused until
+    // step 3; v's in their own region, used in step 8).
+    float* cwq = reinterpret_cast<float*>(smem + L::oR0);
+    float* cwk = cwq + D * kMaxConv;
+    const int W = kp.conv_w;
+    stage_conv_weights(cwq, kp.cw[0] + (size_t)h * D * W, D, W);
+    stage_conv_weights(cwk, kp.cw[1] + (size_t)h * D * W, D, W);
+    stage_conv_weights(reinterpret_cast<float*>(smem + L::oCWv), kp.cw[2] + (size_t)h * D * W, D, W);
+    __syncthreads();  // weights staged
 #pragma unroll
     for (int j = 0; j < FPW; ++j) {
       const int c0 = 32 * fkb[j] + 8 * lg;
       Raw8<in_t> qe, ke;
       load_halo<in_t, D>(qe, kp, 0, it, rt, lr, c0, si.total_tokens);
       load_halo<in_t, D>(ke, kp, 1, it, rt, lr, c0, si.total_tokens);
-      const int W = kp.conv_w;
       float kc[8];
-      conv8(qraw[j], qe, kp.cw[0] + ((size_t)h * D + c0) * W, W, lr, qc[j]);
-      conv8(kraw[j], ke, kp.cw[1] + ((size_t)h * D + c0) * W, W, lr, kc);
+      conv8(qraw[j], qe, cwq + c0 * kMaxConv, W, lr, qc[j]);
+      conv8(kraw[j], ke, cwk + c0 * kMaxConv, W, lr, kc);
 #pragma unroll
       for (int e = 0; e < 8; ++e) qc[j][e] = swishf(qc[j][e]);
       if constexpr (kPark) {
@@ -1195,8 +1219,8 @@ __global__ __launch_bounds__(kIntraThreads, 4) void intra_chunk_kernel(KernelPtr
     if (fv[j]) {
       float vx[8];
       if constexpr (PRO == 2) {
-        const int W = kp.conv_w, c0 = 32 * fkb[j] + 8 * lg;
-        conv8(vraw[j], vext[j], kp.cw[2] + ((size_t)h * D + c0) * W, W, lr, vx);
+        const int c0 = 32 * fkb[j] + 8 * lg;
+        conv8(vraw[j], vext[j], reinterpret_cast<const float*>(smem + L::oCWv) + c0 * kMaxConv, kp.conv_w, lr, vx);
       } else {
 #pragma unroll
         for (int e = 0; e < 8; ++e) vx[e] = vraw[j].get(e);
@@ -1798,12 +1822,13 @@ static hipError_t launch_prefill_t(const PrefillArgs& a) {
     kp.cs[x] = a.layer.conv_state_in[x];
   }
 
-  constexpr size_t lds = IntraLds<M, D, C>::kTotal;
-  static_assert(lds <= 160 * 1024, "intra-chunk LDS");
+  constexpr size_t lds0 = IntraLds<M, D, C>::kTotal, lds_conv = IntraLds<M, D, C>::kTotalConv;
+  static_assert(lds_conv <= 80 * 1024, "two intra-chunk workgroups per compute unit");
   // The prologue is built for the per-channel decay only.
   constexpr int P1 = SDEC ? 0 : 1, P2 = SDEC ? 0 : 2;
   if (SDEC && a.layer.prologue) return hipErrorInvalidValue;
   const int pro = !a.layer.prologue ? 0 : a.layer.conv_w > 0 ? 2 : 1;
+  const size_t lds = pro == 2 ? lds_conv : lds0;
   const void* intra_fn =
       pro == 2   ? reinterpret_cast<const void*>(&intra_chunk_kernel<M, D, C, SDEC, P2>)
       : pro == 1 ? reinterpret_cast<const void*>(&intra_chunk_kernel<M, D, C, SDEC, P1>)
