@@ -678,14 +678,6 @@ __device__ __forceinline__ void conv8(const Raw8<T>& own, const Raw8<T>& ext, co
   }
 }
 
-// One head's convolution weights [D][W] (global) into LDS as [D][kMaxConv],
-// taps reordered from the current row back and zero past W.
-__device__ __forceinline__ void stage_conv_weights(float* dst, const float* src, int D, int W) {
-  for (int idx = threadIdx.x; idx < D * kMaxConv; idx += blockDim.x) {
-    const int c = idx / kMaxConv, j = idx % kMaxConv;
-    dst[idx] = j < W ? src[(size_t)c * W + (W - 1 - j)] : 0.f;
-  }
-}
 
 // ---------------------------------------------------------------------------
 // Intra-chunk kernel: grid (slots of the segment, H), 512 threads (8 waves),
@@ -747,8 +739,20 @@ __global__ __launch_bounds__(kIntraThreads, 4) void intra_chunk_kernel(KernelPtr
   const bool any_frag = fv[0];
 
   // ---- step 1: loads, all issued up front (rows past the chunk re-read a
-  // valid row and are zeroed at use) ----
+  // valid row and are zeroed at use).  With the convolution its weights come
+  // first: a wait for them then covers no other load ----
   const int tok = clampi(t0 + (r < len ? r : len - 1), 0, si.total_tokens - 1);
+  constexpr int NWT = PRO == 2 ? (3 * D * kMaxConv + kIntraThreads - 1) / kIntraThreads : 1;
+  float cwv[NWT];
+  if constexpr (PRO == 2) {
+    const int W = kp.conv_w;
+#pragma unroll
+    for (int x = 0; x < NWT; ++x) {
+      const int idx = tid + kIntraThreads * x;
+      const int t = idx / (D * kMaxConv), c = (idx / kMaxConv) % D, j = idx % kMaxConv;
+      cwv[x] = idx < 3 * D * kMaxConv && j < W ? kp.cw[t][((size_t)h * D + c) * W + (W - 1 - j)] : 0.f;
+    }
+  }
   Raw8<float> graw[FPW];
   Raw8<in_t> qraw[FPW], kraw[FPW];
   float gscalar = 0.f;
@@ -778,19 +782,27 @@ __global__ __launch_bounds__(kIntraThreads, 4) void intra_chunk_kernel(KernelPtr
     float* cwq = reinterpret_cast<float*>(smem + L::oR0);
     float* cwk = cwq + D * kMaxConv;
     const int W = kp.conv_w;
-    stage_conv_weights(cwq, kp.cw[0] + (size_t)h * D * W, D, W);
-    stage_conv_weights(cwk, kp.cw[1] + (size_t)h * D * W, D, W);
-    stage_conv_weights(reinterpret_cast<float*>(smem + L::oCWv), kp.cw[2] + (size_t)h * D * W, D, W);
+    Raw8<in_t> qe[FPW], ke[FPW];
+#pragma unroll
+    for (int j = 0; j < FPW; ++j) {
+      load_halo<in_t, D>(qe[j], kp, 0, it, rt, lr, 32 * fkb[j] + 8 * lg, si.total_tokens);
+      load_halo<in_t, D>(ke[j], kp, 1, it, rt, lr, 32 * fkb[j] + 8 * lg, si.total_tokens);
+    }
+#pragma unroll
+    for (int x = 0; x < NWT; ++x) {
+      const int idx = tid + kIntraThreads * x;
+      if (idx < 3 * D * kMaxConv) {
+        const int t = idx / (D * kMaxConv);
+        (t == 0 ? cwq : t == 1 ? cwk : reinterpret_cast<float*>(smem + L::oCWv))[idx % (D * kMaxConv)] = cwv[x];
+      }
+    }
     __syncthreads();  // weights staged
 #pragma unroll
     for (int j = 0; j < FPW; ++j) {
       const int c0 = 32 * fkb[j] + 8 * lg;
-      Raw8<in_t> qe, ke;
-      load_halo<in_t, D>(qe, kp, 0, it, rt, lr, c0, si.total_tokens);
-      load_halo<in_t, D>(ke, kp, 1, it, rt, lr, c0, si.total_tokens);
       float kc[8];
-      conv8(qraw[j], qe, cwq + c0 * kMaxConv, W, lr, qc[j]);
-      conv8(kraw[j], ke, cwk + c0 * kMaxConv, W, lr, kc);
+      conv8(qraw[j], qe[j], cwq + c0 * kMaxConv, W, lr, qc[j]);
+      conv8(kraw[j], ke[j], cwk + c0 * kMaxConv, W, lr, kc);
 #pragma unroll
       for (int e = 0; e < 8; ++e) qc[j][e] = swishf(qc[j][e]);
       if constexpr (kPark) {
