@@ -1155,10 +1155,19 @@ __global__ __launch_bounds__(kIntraThreads, 4) void intra_chunk_kernel(KernelPtr
   // ---- step 6: X_a as chain operands; (K*gam)^T staged over A and P.  V
   // is fetched here for step 8 ----
   Raw8<in_t> vraw[FPW], vext[PRO == 2 ? FPW : 1];
+  {
+    // The row addresses are formed again from opaque copies of the item's
+    // fields: kept from step 1 they would be spilled to scratch and read
+    // back at memory latency.
+    Item iv = it;
+    int rr = r;
+    asm volatile("" : "+v"(iv.t0), "+v"(iv.len), "+v"(iv.bos), "+v"(iv.n), "+v"(iv.h), "+v"(rr));
+    const int tk = clampi(iv.t0 + (rr < iv.len ? rr : iv.len - 1), 0, si.total_tokens - 1);
 #pragma unroll
-  for (int j = 0; j < FPW; ++j) {
-    vraw[j].load(reinterpret_cast<const in_t*>(kp.v) + ((size_t)tok * H + h) * D + 32 * fkb[j] + 8 * lg);
-    if constexpr (PRO == 2) load_halo<in_t, D>(vext[j], kp, 2, it, rt, lr, 32 * fkb[j] + 8 * lg, si.total_tokens);
+    for (int j = 0; j < FPW; ++j) {
+      vraw[j].load(reinterpret_cast<const in_t*>(kp.v) + ((size_t)tk * H + iv.h) * D + 32 * fkb[j] + 8 * lg);
+      if constexpr (PRO == 2) load_halo<in_t, D>(vext[j], kp, 2, iv, rt, lr, 32 * fkb[j] + 8 * lg, si.total_tokens);
+    }
   }
   if (w < NRT) {
     float x[4];
