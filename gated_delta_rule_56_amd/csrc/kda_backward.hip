@@ -665,16 +665,19 @@ hipError_t launch_backward_t(const BackwardArgs& a) {
   e = hipFuncSetAttribute(reinterpret_cast<const void*>(&bwd_gram_kernel<D, C>),
                                      hipFuncAttributeMaxDynamicSharedMemorySize, (int)glds);
   if (e != hipSuccess) return e;
-  auto gemm = [&](auto kern, const float* A, const float* B, float* Cm, int M, int N, int K,
+  hipError_t gerr = hipSuccess;
+  auto gemm = [&](auto op, const float* A, const float* B, float* Cm, int M, int N, int K,
                   int lda, int ldb, size_t sa, size_t sb, float alpha, int acc_c, int mask) {
-    const dim3 grid((unsigned)NB, (N + 63) / 64, (M + 63) / 64);
-    hipLaunchKernelGGL(kern, grid, dim3(256), 0, a.stream, A, B, Cm, M, N, K, lda, ldb, N, sa, sb,
-                       (size_t)M * N, alpha, acc_c, mask);
+    typedef decltype(op) O;
+    const hipError_t e = launch_fp32_gemm<O::TA, O::TB>(A, B, Cm, M, N, K, lda, ldb, N, sa, sb,
+                                                         (size_t)M * N, alpha, acc_c, mask, NB,
+                                                         a.stream);
+    if (gerr == hipSuccess) gerr = e;
   };
   const size_t scd = (size_t)C * D, scc = (size_t)C * C, sdd = (size_t)D * D;
-  auto NT = fp32_gemm_kernel<false, true>;
-  auto NN = fp32_gemm_kernel<false, false>;
-  auto TN = fp32_gemm_kernel<true, false>;
+  const GemmNT NT;
+  const GemmNN NN;
+  const GemmTN TN;
   // Grams of the moderate-decay chunks, then the others pair by pair.
   gemm(NT, p.Kt, p.Kh, p.Bm, C, C, D, D, D, scd, scd, 1.f, 0, 2);  // strict_tril(Kt Kh^T)
   gemm(NT, p.Qt, p.Kh, p.P, C, C, D, D, D, scd, scd, 1.f, 0, 1);   // tril(Qt Kh^T)
@@ -698,6 +701,7 @@ hipError_t launch_backward_t(const BackwardArgs& a) {
   gemm(NN, p.dP, p.Kh, p.U, C, D, C, C, D, scc, scd, 1.f, 0, 0);    // Y2 = dP Kh
   gemm(TN, p.dBm, p.Kt, p.dU, C, D, C, C, D, scc, scd, 1.f, 0, 0);  // Y3 = dBm^T Kt
   gemm(TN, p.dP, p.Qt, p.dU, C, D, C, C, D, scc, scd, 1.f, 1, 0);   //    + dP^T Qt
+  if (gerr != hipSuccess) return gerr;
   hipLaunchKernelGGL((bwd_final_fast_kernel<D, C>), dim3(NB), dim3(D), 0, a.stream, p, geo, out);
   const size_t flds = final_lds<D, C>();
   e = hipFuncSetAttribute(reinterpret_cast<const void*>(&bwd_final_kernel<D, C>),

@@ -344,15 +344,18 @@ hipError_t launch_dplr_t(const DplrArgs& a) {
     DIn in{a.q, a.k, a.v, a.a, a.b, a.g, a.beta};
     hipLaunchKernelGGL((dplr_prep_kernel<in_t, D, C, TIED>), dim3(NB), dim3(256), 0, a.stream, in,
                        p, geo);
-    auto gemm = [&](auto kern, const float* A, const float* B, float* Cm, int M, int N, int K,
+    hipError_t gerr = hipSuccess;
+    auto gemm = [&](auto op, const float* A, const float* B, float* Cm, int M, int N, int K,
                     int lda, int ldb, size_t sa, size_t sb, float alpha, int mask) {
-      const dim3 grid((unsigned)NB, (N + 63) / 64, (M + 63) / 64);
-      hipLaunchKernelGGL(kern, grid, dim3(256), 0, a.stream, A, B, Cm, M, N, K, lda, ldb, N, sa,
-                         sb, (size_t)M * N, alpha, 0, mask);
+      typedef decltype(op) O;
+      const hipError_t e = launch_fp32_gemm<O::TA, O::TB>(A, B, Cm, M, N, K, lda, ldb, N, sa, sb,
+                                                           (size_t)M * N, alpha, 0, mask, NB,
+                                                           a.stream);
+      if (gerr == hipSuccess) gerr = e;
     };
     const size_t scd = (size_t)C * D, scc = (size_t)C * C;
-    auto NT = fp32_gemm_kernel<false, true>;
-    auto NN = fp32_gemm_kernel<false, false>;
+    const GemmNT NT;
+    const GemmNN NN;
     gemm(NT, p.Bt, p.Ah, p.Aba, C, C, D, D, D, scd, scd, 1.f, 2);  // strict_tril(Bt Ah^T)
     gemm(NT, p.Qt, p.Ah, p.Aqa, C, C, D, D, D, scd, scd, 1.f, 1);  // tril(Qt Ah^T)
     if (!TIED) {
@@ -370,6 +373,7 @@ hipError_t launch_dplr_t(const DplrArgs& a) {
       gemm(NN, p.M, p.X, p.Y, C, D, C, C, D, scc, scd, -1.f, 0);     // Y = -M X
       gemm(NN, p.Aqk, p.V, p.OV, C, D, C, C, D, scc, scd, 1.f, 0);   // OV = Aqk V
     }
+    if (gerr != hipSuccess) return gerr;
   }
   if (serial > 0)
     hipLaunchKernelGGL((dplr_states_kernel<D, C, TIED>), dim3(serial), dim3(kStThreads), slds, a.stream,

@@ -100,9 +100,15 @@ __device__ __forceinline__ f32x4 mfma4(float a, float b, f32x4 c) {
 // Batched C = alpha op(A) op(B) (+ C when acc) with op(A) [M x K] stored as
 // A[m][k] (TA = false) or A[k][m] (TA = true), op(B) [K x N] stored as B[k][n]
 // (TB = false) or B[n][k] (TB = true), leading dimensions lda, ldb, ldc, and
-// an optional mask on C (1: keep n <= m, 2: keep n < m).  64 x 64 tile, 256
-// threads with 4 x 4 outputs each; the tile loads stay coalesced for either
-// storage; K a multiple of 16.
+// an optional mask on C (1: keep n <= m, 2: keep n < m).  One 64 x 64 tile of
+// C per workgroup of 256 threads, 4 x 4 outputs each; K, M and N multiples
+// of 4.  K runs in stages of 64: a stage of op(A)'s and op(B)'s tiles is
+// loaded with 16-byte loads along each matrix's contiguous dimension (all of
+// a thread's loads issued together), written to LDS, and the next stage's
+// loads are issued before this stage's products, so they overlap.
+constexpr int kGemmKStage = 64, kGemmLd = 64 + 4;
+constexpr size_t kGemmLds = (size_t)2 * kGemmKStage * kGemmLd * sizeof(float);
+
 template <bool TA, bool TB>
 __global__ __launch_bounds__(256) void fp32_gemm_kernel(const float* __restrict__ A,
                                                        const float* __restrict__ B,
@@ -110,40 +116,87 @@ __global__ __launch_bounds__(256) void fp32_gemm_kernel(const float* __restrict_
                                                        int lda, int ldb, int ldc, size_t sa,
                                                        size_t sb, size_t sc, float alpha, int acc_c,
                                                        int mask) {
-  __shared__ float As[16][64 + 4];
-  __shared__ float Bs[16][64 + 4];
+  __shared__ __attribute__((aligned(16))) float As[kGemmKStage * kGemmLd];  // As[k][m]
+  __shared__ __attribute__((aligned(16))) float Bs[kGemmKStage * kGemmLd];  // Bs[k][n]
+  constexpr int LD = kGemmLd, NV = kGemmKStage * 16 / 256;  // vectors per thread and matrix
   const int bt = blockIdx.x;  // batch on x: up to 2^31 - 1 blocks
   const int m0 = blockIdx.z * 64, n0 = blockIdx.y * 64;
   const float* a = A + bt * sa;
   const float* bb = B + bt * sb;
-  const int tx = threadIdx.x % 16, ty = threadIdx.x / 16;
-  float acc[4][4] = {};
-  for (int k0 = 0; k0 < K; k0 += 16) {
-    for (int idx = threadIdx.x; idx < 64 * 16; idx += 256) {
-      int mm, kk;
-      if (TA) { kk = idx / 64; mm = idx % 64; } else { mm = idx / 16; kk = idx % 16; }
-      As[kk][mm] = m0 + mm < M ? (TA ? a[(size_t)(k0 + kk) * lda + m0 + mm]
-                                     : a[(size_t)(m0 + mm) * lda + k0 + kk]) : 0.f;
-      int nn;
-      if (TB) { nn = idx / 16; kk = idx % 16; } else { kk = idx / 64; nn = idx % 64; }
-      Bs[kk][nn] = n0 + nn < N ? (TB ? bb[(size_t)(n0 + nn) * ldb + k0 + kk]
-                                     : bb[(size_t)(k0 + kk) * ldb + n0 + nn]) : 0.f;
-    }
-    __syncthreads();
+  const int tid = threadIdx.x;
+  f32x4 xa[NV], xb[NV];
+  // Vector v of stage k0 (ks = its k extent): for a matrix stored with k as
+  // its row (TA for A, !TB for B) row k0 + v / 16, columns 4 (v % 16) ..;
+  // otherwise row v / (ks / 4) of the 64, k0 + 4 (v % (ks / 4)) ...
+  auto fetch = [&](int k0, int ks) {
 #pragma unroll
-    for (int kk = 0; kk < 16; ++kk) {
-      float av[4], bv[4];
-#pragma unroll
-      for (int x = 0; x < 4; ++x) {
-        av[x] = As[kk][ty * 4 + x];
-        bv[x] = Bs[kk][tx * 4 + x];
+    for (int x = 0; x < NV; ++x) {
+      const int v = tid + 256 * x;
+      xa[x] = f32x4{0, 0, 0, 0};
+      xb[x] = f32x4{0, 0, 0, 0};
+      if (v < ks * 16) {
+        if (TA) {
+          const int mm = 4 * (v % 16);
+          if (m0 + mm < M) xa[x] = *reinterpret_cast<const f32x4*>(a + (size_t)(k0 + v / 16) * lda + m0 + mm);
+        } else {
+          const int mm = v / (ks / 4);
+          if (m0 + mm < M)
+            xa[x] = *reinterpret_cast<const f32x4*>(a + (size_t)(m0 + mm) * lda + k0 + 4 * (v % (ks / 4)));
+        }
+        if (!TB) {
+          const int nn = 4 * (v % 16);
+          if (n0 + nn < N) xb[x] = *reinterpret_cast<const f32x4*>(bb + (size_t)(k0 + v / 16) * ldb + n0 + nn);
+        } else {
+          const int nn = v / (ks / 4);
+          if (n0 + nn < N)
+            xb[x] = *reinterpret_cast<const f32x4*>(bb + (size_t)(n0 + nn) * ldb + k0 + 4 * (v % (ks / 4)));
+        }
       }
+    }
+  };
+  auto stage = [&](int ks) {
+#pragma unroll
+    for (int x = 0; x < NV; ++x) {
+      const int v = tid + 256 * x;
+      if (v < ks * 16) {
+        if (TA) {
+          *reinterpret_cast<f32x4*>(As + (v / 16) * LD + 4 * (v % 16)) = xa[x];
+        } else {
+          const int mm = v / (ks / 4), k = 4 * (v % (ks / 4));
+#pragma unroll
+          for (int e = 0; e < 4; ++e) As[(k + e) * LD + mm] = xa[x][e];
+        }
+        if (!TB) {
+          *reinterpret_cast<f32x4*>(Bs + (v / 16) * LD + 4 * (v % 16)) = xb[x];
+        } else {
+          const int nn = v / (ks / 4), k = 4 * (v % (ks / 4));
+#pragma unroll
+          for (int e = 0; e < 4; ++e) Bs[(k + e) * LD + nn] = xb[x][e];
+        }
+      }
+    }
+  };
+  const int tx = tid % 16, ty = tid / 16;
+  float acc[4][4] = {};
+  fetch(0, K < kGemmKStage ? K : kGemmKStage);
+  for (int k0 = 0; k0 < K; k0 += kGemmKStage) {
+    const int ks = K - k0 < kGemmKStage ? K - k0 : kGemmKStage;
+    if (k0 > 0) __syncthreads();  // the previous stage's reads are done
+    stage(ks);
+    __syncthreads();
+    if (k0 + kGemmKStage < K) {
+      const int k1 = k0 + kGemmKStage;
+      fetch(k1, K - k1 < kGemmKStage ? K - k1 : kGemmKStage);
+    }
+#pragma unroll 4
+    for (int kk = 0; kk < ks; ++kk) {
+      const f32x4 av = *reinterpret_cast<const f32x4*>(As + kk * LD + ty * 4);
+      const f32x4 bv = *reinterpret_cast<const f32x4*>(Bs + kk * LD + tx * 4);
 #pragma unroll
       for (int x = 0; x < 4; ++x)
 #pragma unroll
         for (int y = 0; y < 4; ++y) acc[x][y] += av[x] * bv[y];
     }
-    __syncthreads();
   }
   float* c = Cm + bt * sc;
 #pragma unroll
@@ -157,6 +210,23 @@ __global__ __launch_bounds__(256) void fp32_gemm_kernel(const float* __restrict_
         c[(size_t)m * ldc + nn] = acc_c ? c[(size_t)m * ldc + nn] + v : v;
       }
     }
+}
+
+// Operand orientations of fp32_gemm_kernel, as tags for launch_fp32_gemm.
+struct GemmNN { static constexpr bool TA = false, TB = false; };
+struct GemmNT { static constexpr bool TA = false, TB = true; };
+struct GemmTN { static constexpr bool TA = true, TB = false; };
+
+// Launch of fp32_gemm_kernel over NB batch items.
+template <bool TA, bool TB>
+inline hipError_t launch_fp32_gemm(const float* A, const float* B, float* Cm, int M, int N, int K,
+                                   int lda, int ldb, int ldc, size_t sa, size_t sb, size_t sc,
+                                   float alpha, int acc_c, int mask, size_t NB, hipStream_t stream) {
+  if (K % 4 || M % 4 || N % 4) return hipErrorInvalidValue;
+  const dim3 grid((unsigned)NB, (N + 63) / 64, (M + 63) / 64);
+  hipLaunchKernelGGL((fp32_gemm_kernel<TA, TB>), grid, dim3(256), 0, stream, A, B, Cm, M, N, K, lda,
+                     ldb, ldc, sa, sb, sc, alpha, acc_c, mask);
+  return hipGetLastError();
 }
 
 // Register-staged copy of a ROWS x COLS fp32 block (row-major in global
