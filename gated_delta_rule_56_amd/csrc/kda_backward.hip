@@ -103,9 +103,20 @@ struct BwdIn {
 };
 
 // Padded fp32 copies of the chunk's inputs, Gamma = cumsum(g), Qt, Kt, Kb.
+// Four consecutive input elements as fp32.
+__device__ __forceinline__ f32x4 load4(const bf16* p) {
+  const bf16x4 v = *reinterpret_cast<const bf16x4*>(p);
+  return f32x4{(float)v[0], (float)v[1], (float)v[2], (float)v[3]};
+}
+__device__ __forceinline__ f32x4 load4(const float* p) { return *reinterpret_cast<const f32x4*>(p); }
+
+// Four consecutive channels per thread and item: 16-byte stores of every
+// plane; q and k stay in registers between the two passes.
 template <class in_t, int D, int C>
 __global__ __launch_bounds__(256) void bwd_prep_kernel(BwdIn in, Planes p, Geo geo) {
-  __shared__ float G[C][D + 1];
+  constexpr int SG = D + 4, NV = C * D / 4 / 256;
+  static_assert(NV * 256 * 4 == C * D, "whole vectors per thread");
+  __shared__ __attribute__((aligned(16))) float G[C][SG];
   const int b = blockIdx.x, H = geo.H;
   const int gch = b / H, h = b % H;
   int n, t0, len;
@@ -114,15 +125,23 @@ __global__ __launch_bounds__(256) void bwd_prep_kernel(BwdIn in, Planes p, Geo g
   const in_t* q = reinterpret_cast<const in_t*>(in.q);
   const in_t* k = reinterpret_cast<const in_t*>(in.k);
   const in_t* v = reinterpret_cast<const in_t*>(in.v);
-  for (int idx = threadIdx.x; idx < C * D; idx += 256) {
+  f32x4 qv[NV], kv[NV];
+#pragma unroll
+  for (int x = 0; x < NV; ++x) {
+    const int idx = 4 * ((int)threadIdx.x + 256 * x);
     const int r = idx / D, c = idx % D;
     const bool ok = r < len;
-    const size_t ti = ((size_t)(t0 + r) * H + h) * D + c;
-    p.Q[pcd + idx] = ok ? (float)q[ti] : 0.f;
-    p.K[pcd + idx] = ok ? (float)k[ti] : 0.f;
-    p.V[pcd + idx] = ok ? (float)v[ti] : 0.f;
-    p.dO[pcd + idx] = ok ? in.dout[ti] : 0.f;
-    G[r][c] = ok ? in.g[ti] : 0.f;
+    const size_t ti = ((size_t)(t0 + (ok ? r : 0)) * H + h) * D + c;
+    const f32x4 z = {0, 0, 0, 0};
+    qv[x] = ok ? load4(q + ti) : z;
+    kv[x] = ok ? load4(k + ti) : z;
+    const f32x4 vv = ok ? load4(v + ti) : z, dv = ok ? load4(in.dout + ti) : z;
+    const f32x4 gv = ok ? load4(in.g + ti) : z;
+    *reinterpret_cast<f32x4*>(p.Q + pcd + idx) = qv[x];
+    *reinterpret_cast<f32x4*>(p.K + pcd + idx) = kv[x];
+    *reinterpret_cast<f32x4*>(p.V + pcd + idx) = vv;
+    *reinterpret_cast<f32x4*>(p.dO + pcd + idx) = dv;
+    *reinterpret_cast<f32x4*>(&G[r][c]) = gv;
   }
   if (threadIdx.x < C) {
     const int r = threadIdx.x;
@@ -145,15 +164,26 @@ __global__ __launch_bounds__(256) void bwd_prep_kernel(BwdIn in, Planes p, Geo g
     big = __any(big);
     if (threadIdx.x == 0) p.fast[b] = big ? 0 : 1;
   }
-  for (int idx = threadIdx.x; idx < C * D; idx += 256) {
+#pragma unroll
+  for (int x = 0; x < NV; ++x) {
+    const int idx = 4 * ((int)threadIdx.x + 256 * x);
     const int r = idx / D, c = idx % D;
-    const float gm = G[r][c], ga = __expf(gm);
-    const float kv = p.K[pcd + idx];
-    p.Gam[pcd + idx] = gm;
-    p.Qt[pcd + idx] = p.Q[pcd + idx] * ga;
-    p.Kt[pcd + idx] = kv * ga;
-    p.Kb[pcd + idx] = kv * __expf(G[C - 1][c] - gm);
-    p.Kh[pcd + idx] = kv * __expf(-gm);  // finite where the chunk is factored
+    const f32x4 gm = *reinterpret_cast<const f32x4*>(&G[r][c]);
+    const f32x4 gl = *reinterpret_cast<const f32x4*>(&G[C - 1][c]);
+    f32x4 qt, kt, kb, kh;
+#pragma unroll
+    for (int e = 0; e < 4; ++e) {
+      const float ga = __expf(gm[e]);
+      qt[e] = qv[x][e] * ga;
+      kt[e] = kv[x][e] * ga;
+      kb[e] = kv[x][e] * __expf(gl[e] - gm[e]);
+      kh[e] = kv[x][e] * __expf(-gm[e]);  // finite where the chunk is factored
+    }
+    *reinterpret_cast<f32x4*>(p.Gam + pcd + idx) = gm;
+    *reinterpret_cast<f32x4*>(p.Qt + pcd + idx) = qt;
+    *reinterpret_cast<f32x4*>(p.Kt + pcd + idx) = kt;
+    *reinterpret_cast<f32x4*>(p.Kb + pcd + idx) = kb;
+    *reinterpret_cast<f32x4*>(p.Kh + pcd + idx) = kh;
   }
 }
 
@@ -597,15 +627,31 @@ __global__ __launch_bounds__(D) void bwd_final_fast_kernel(Planes p, Geo geo, Bw
   const float* Y1 = p.R + pcd;
   const float* Y2 = p.U + pcd;
   const float* Y3 = p.dU + pcd;
-  float dgn = 0.f, kbsum = 0.f;
+  // dgam_n[c] = rowsum(dS' * S)[c]: each wave reduces whole rows, its lanes
+  // reading them contiguously, and parks the sums in LDS.
+  __shared__ float rowsum[D];
   {
-    const float* S = p.S + ((size_t)b * D + c) * D;
-    const float* dS = p.dSn + ((size_t)b * D + c) * D;
-    for (int j = 0; j < D; ++j) dgn += S[j] * dS[j];
+    constexpr int NWV = D / 64, PL = D / 64;  // waves; elements per lane and row
+    const int w = c >> 6, l = c & 63;
+    const float* S = p.S + (size_t)b * D * D;
+    const float* dS = p.dSn + (size_t)b * D * D;
+    for (int i = w; i < D; i += NWV) {
+      float t = 0.f;
+#pragma unroll
+      for (int e = 0; e < PL; ++e) t += S[(size_t)i * D + 64 * e + l] * dS[(size_t)i * D + 64 * e + l];
+#pragma unroll
+      for (int off = 32; off > 0; off >>= 1) t += __shfl_xor(t, off);
+      if (l == 0) rowsum[i] = t;
+    }
   }
+  float kbsum = 0.f;
+#pragma unroll 8
   for (int r = 0; r < C; ++r) kbsum += p.dKb[pcd + r * D + c] * p.Kb[pcd + r * D + c];
+  __syncthreads();
+  const float dgn = rowsum[c];
   const float gl = p.Gam[pcd + (C - 1) * D + c];
   float run = kbsum + dgn * p.gn[(size_t)b * D + c];  // dGamma_n lands on the last row
+#pragma unroll 4
   for (int r = C - 1; r >= 0; --r) {
     const size_t e0 = pcd + r * D + c;
     const float gr = p.Gam[e0], ga = __expf(gr);
