@@ -35,6 +35,8 @@
 #include "kda_fp32_chunks.hpp"
 #include "kda_launch.hpp"
 
+#include <type_traits>
+
 namespace kda {
 namespace {
 
@@ -77,35 +79,50 @@ struct DIn {
 // Padded fp32 inputs, Gamma, the decayed operands and the span verdict.
 template <class in_t, int D, int C, bool TIED>
 __global__ __launch_bounds__(256) void dplr_prep_kernel(DIn in, DPlanes p, Geo geo) {
-  __shared__ float Gs[C][D + 1];
+  // Four consecutive channels per thread: 16-byte loads and stores.
+  constexpr int SG = D + 4;
+  __shared__ __attribute__((aligned(16))) float Gs[C][SG];
   const int b = blockIdx.x, H = geo.H;
   const int gch = b / H, h = b % H;
   int n, t0, len;
   chunk_of<C>(geo, gch, n, t0, len);
   const size_t pcd = (size_t)b * C * D;
-  auto ld = [&](const void* ptr, size_t ti) { return (float)reinterpret_cast<const in_t*>(ptr)[ti]; };
-  for (int idx = threadIdx.x; idx < C * D; idx += 256) {
-    const int r = idx / D, c = idx % D;
+  auto ld4 = [&](const void* ptr, size_t ti) -> f32x4 {
+    if constexpr (std::is_same<in_t, float>::value) {
+      return *reinterpret_cast<const f32x4*>(reinterpret_cast<const float*>(ptr) + ti);
+    } else {
+      const bf16x4 v = *reinterpret_cast<const bf16x4*>(reinterpret_cast<const in_t*>(ptr) + ti);
+      return f32x4{(float)v[0], (float)v[1], (float)v[2], (float)v[3]};
+    }
+  };
+  auto st4 = [&](float* plane, int idx, f32x4 x) { *reinterpret_cast<f32x4*>(plane + pcd + idx) = x; };
+  auto ld4p = [&](const float* plane, int idx) { return *reinterpret_cast<const f32x4*>(plane + pcd + idx); };
+  for (int v4 = threadIdx.x; v4 < C * D / 4; v4 += 256) {
+    const int idx = 4 * v4, r = idx / D, c = idx % D;
     const bool ok = r < len;
-    const size_t ti = ((size_t)(t0 + r) * H + h) * D + c;
-    const float kv = ok ? ld(in.k, ti) : 0.f;
-    const float gv = ok ? in.g[ti] : 0.f;
-    float av, bv;
+    const size_t ti = ((size_t)(t0 + (ok ? r : 0)) * H + h) * D + c;
+    const f32x4 z = {0, 0, 0, 0};
+    const f32x4 kv = ok ? ld4(in.k, ti) : z;
+    const f32x4 gv = ok ? *reinterpret_cast<const f32x4*>(in.g + ti) : z;
+    f32x4 av, bv;
     if (TIED) {
       const float be = ok ? in.beta[(size_t)(t0 + r) * H + h] : 0.f;
-      av = be * kv;                 // a = write key = beta k
-      bv = __expf(gv) * kv;         // b = alpha k
+#pragma unroll
+      for (int e = 0; e < 4; ++e) {
+        av[e] = be * kv[e];               // a = write key = beta k
+        bv[e] = __expf(gv[e]) * kv[e];    // b = alpha k
+      }
     } else {
-      av = ok ? ld(in.a, ti) : 0.f;
-      bv = ok ? ld(in.b, ti) : 0.f;
+      av = ok ? ld4(in.a, ti) : z;
+      bv = ok ? ld4(in.b, ti) : z;
     }
-    p.Q[pcd + idx] = ok ? ld(in.q, ti) : 0.f;
-    p.K[pcd + idx] = TIED ? av : kv;  // the key that writes v
-    p.V[pcd + idx] = ok ? ld(in.v, ti) : 0.f;
-    p.A[pcd + idx] = av;
-    p.B[pcd + idx] = bv;
-    p.G[pcd + idx] = gv;
-    Gs[r][c] = gv;
+    st4(p.Q, idx, ok ? ld4(in.q, ti) : z);
+    st4(p.K, idx, TIED ? av : kv);  // the key that writes v
+    st4(p.V, idx, ok ? ld4(in.v, ti) : z);
+    st4(p.A, idx, av);
+    st4(p.B, idx, bv);
+    st4(p.G, idx, gv);
+    *reinterpret_cast<f32x4*>(&Gs[r][c]) = gv;
   }
   __syncthreads();
   if (threadIdx.x < D) {
@@ -124,18 +141,30 @@ __global__ __launch_bounds__(256) void dplr_prep_kernel(DIn in, DPlanes p, Geo g
     big = __any(big);
     if (threadIdx.x == 0) p.fast[b] = big ? 0 : 1;
   }
-  for (int idx = threadIdx.x; idx < C * D; idx += 256) {
-    const int r = idx / D, c = idx % D;
-    const float gm = Gs[r][c], gl = Gs[C - 1][c];
-    const float ea = __expf(gm), eh = __expf(-gm), eb = __expf(gl - gm);
-    const float av = p.A[pcd + idx], kv = p.K[pcd + idx];
-    p.Gam[pcd + idx] = gm;
-    p.Qt[pcd + idx] = p.Q[pcd + idx] * ea;
-    p.Bt[pcd + idx] = p.B[pcd + idx] * __expf(gm - p.G[pcd + idx]);
-    p.Ah[pcd + idx] = av * eh;  // finite where the chunk is factored
-    p.Kh[pcd + idx] = kv * eh;
-    p.Ab[pcd + idx] = av * eb;
-    p.Kb[pcd + idx] = kv * eb;
+  for (int v4 = threadIdx.x; v4 < C * D / 4; v4 += 256) {
+    const int idx = 4 * v4, r = idx / D, c = idx % D;
+    const f32x4 gm = *reinterpret_cast<const f32x4*>(&Gs[r][c]);
+    const f32x4 gl = *reinterpret_cast<const f32x4*>(&Gs[C - 1][c]);
+    const f32x4 av = ld4p(p.A, idx), kv = ld4p(p.K, idx), qv = ld4p(p.Q, idx);
+    const f32x4 bv = ld4p(p.B, idx), gv = ld4p(p.G, idx);
+    f32x4 qt, bt, ah, kh, ab, kb;
+#pragma unroll
+    for (int e = 0; e < 4; ++e) {
+      const float ea = __expf(gm[e]), eh = __expf(-gm[e]), eb = __expf(gl[e] - gm[e]);
+      qt[e] = qv[e] * ea;
+      bt[e] = bv[e] * __expf(gm[e] - gv[e]);
+      ah[e] = av[e] * eh;  // finite where the chunk is factored
+      kh[e] = kv[e] * eh;
+      ab[e] = av[e] * eb;
+      kb[e] = kv[e] * eb;
+    }
+    st4(p.Gam, idx, gm);
+    st4(p.Qt, idx, qt);
+    st4(p.Bt, idx, bt);
+    st4(p.Ah, idx, ah);
+    st4(p.Kh, idx, kh);
+    st4(p.Ab, idx, ab);
+    st4(p.Kb, idx, kb);
   }
 }
 
