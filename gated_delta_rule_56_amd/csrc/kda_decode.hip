@@ -75,14 +75,34 @@ __global__ __launch_bounds__(256) void decode_step_kernel(
   const float ag = SG ? __expf(gp[0]) : 0.f;
   float* sp = state + tok * (size_t)DK * DV;
 
-  float kk[RPT], qq[RPT];
+  float kk[RPT], qq[RPT], ga[RPT];
   f32x4 s[RPT];
-  // Issue the state loads first: they are the long pole.
+  // Without the layer's prologue every per-token input is requested before
+  // the state: then each state row is decayed and reduced as soon as it
+  // arrives, and no small load is left to wait for between the reduction and
+  // the write-back (a late v or beta load cost 3 % of the step).  The
+  // scheduling barrier keeps the compiler from sinking these loads to their
+  // first uses.
+  const float b_in = beta[tok];
+  float v_in[4];
+  if (!LAYER) {
+    const in_t* vp0 = v + tok * DV + 4 * cg;
+#pragma unroll
+    for (int c = 0; c < 4; ++c) v_in[c] = (float)vp0[c];
+#pragma unroll
+    for (int m = 0; m < RPT; ++m) {
+      const int i = rg + RG * m;
+      kk[m] = (float)kp[i];
+      qq[m] = (float)qp[i];
+      ga[m] = SG ? 0.f : gp[i];
+    }
+  }
 #pragma unroll
   for (int m = 0; m < RPT; ++m) {
     const int i = rg + RG * m;
     s[m] = __builtin_nontemporal_load(reinterpret_cast<const f32x4*>(sp + (size_t)i * DV + 4 * cg));
   }
+  if constexpr (!LAYER) __builtin_amdgcn_sched_barrier(0);
   float r[4] = {0, 0, 0, 0}, p[4] = {0, 0, 0, 0}, kq = 0.f, nq = 0.f, nk = 0.f;
   const int W1 = LAYER ? lp.conv_w - 1 : -1;
   // Short convolution: each (tensor, channel) of this (n, h) is convolved by
@@ -117,11 +137,13 @@ __global__ __launch_bounds__(256) void decode_step_kernel(
     __syncthreads();
   }
   const bool conv = LAYER && W1 >= 0;
+  if constexpr (LAYER) {
 #pragma unroll
-  for (int m = 0; m < RPT; ++m) {
-    const int i = rg + RG * m;
-    kk[m] = conv ? cv[LAYER ? 1 : 0][i] : (float)kp[i];
-    qq[m] = conv ? cv[0][i] : (float)qp[i];
+    for (int m = 0; m < RPT; ++m) {
+      const int i = rg + RG * m;
+      kk[m] = conv ? cv[1][i] : (float)kp[i];
+      qq[m] = conv ? cv[0][i] : (float)qp[i];
+    }
   }
 #pragma unroll
   for (int m = 0; m < RPT; ++m) {
@@ -132,7 +154,7 @@ __global__ __launch_bounds__(256) void decode_step_kernel(
       nk += kk[m] * kk[m];
       nq += qq[m] * qq[m];
     }
-    const float a = SG ? ag : __expf(gp[i]);
+    const float a = SG ? ag : __expf(LAYER ? gp[i] : ga[m]);
 #pragma unroll
     for (int c = 0; c < 4; ++c) {
       s[m][c] *= a;
@@ -161,7 +183,7 @@ __global__ __launch_bounds__(256) void decode_step_kernel(
   const in_t* vp = v + tok * DV + 4 * cg;
   float vv[4];
 #pragma unroll
-  for (int c = 0; c < 4; ++c) vv[c] = conv ? cv[LAYER ? 2 : 0][4 * cg + c] : (float)vp[c];
+  for (int c = 0; c < 4; ++c) vv[c] = !LAYER ? v_in[c] : conv ? cv[LAYER ? 2 : 0][4 * cg + c] : (float)vp[c];
   const int w = t >> 6;
   if ((t & 63) < TPR) {
 #pragma unroll
@@ -183,7 +205,7 @@ __global__ __launch_bounds__(256) void decode_step_kernel(
   }
   kq = red[0][cg][8] + red[1][cg][8] + red[2][cg][8] + red[3][cg][8];
 
-  float b = beta[tok];
+  float b = b_in;
   if (LAYER && lp.prologue) {
     // L2 normalisation: scale the reductions by 1/|q|, 1/|k| (floored).
     nq = red[0][cg][9] + red[1][cg][9] + red[2][cg][9] + red[3][cg][9];
