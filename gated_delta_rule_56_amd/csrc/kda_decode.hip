@@ -50,6 +50,28 @@ struct LayerPtrs {
 __device__ __forceinline__ float swish_d(float x) { return x / (1.f + __expf(-x)); }
 __device__ __forceinline__ float sigmoid_d(float x) { return 1.f / (1.f + __expf(-x)); }
 
+// An input element kept as loaded, widened to 32 bits (a bf16 in the low
+// half): 16-bit values held this way are not packed in pairs, which would make
+// the compiler wait for the loads where they are issued.
+__device__ __forceinline__ unsigned raw32(const bf16* p) {
+  return *reinterpret_cast<const unsigned short*>(p);
+}
+__device__ __forceinline__ unsigned raw32(const float* p) { return __builtin_bit_cast(unsigned, *p); }
+template <typename T>
+__device__ __forceinline__ float raw_to_f(unsigned u) {
+  if constexpr (sizeof(T) == 2)
+    return __builtin_bit_cast(float, u << 16);  // bf16 is the high half of an fp32
+  else
+    return __builtin_bit_cast(float, u);
+}
+template <typename T>
+__device__ __forceinline__ T raw_to_t(unsigned u) {
+  if constexpr (sizeof(T) == 2)
+    return __builtin_bit_cast(T, (unsigned short)u);
+  else
+    return __builtin_bit_cast(T, u);
+}
+
 // SG: scalar gate (Gated DeltaNet): g holds one log-decay per (n, h).
 template <typename in_t, int DK, int DV, bool OUT_BF16, bool SG, bool LAYER>
 __global__ __launch_bounds__(256) void decode_step_kernel(
@@ -59,7 +81,6 @@ __global__ __launch_bounds__(256) void decode_step_kernel(
   constexpr int TPR = DV / 4;          // threads per state row
   constexpr int RG = 256 / TPR;        // row groups
   constexpr int RPT = DK / RG;         // rows per thread
-  constexpr int RG_PER_WAVE = 64 / TPR;
   static_assert(RPT * RG == DK, "row split");
 
   const int nh = blockIdx.x;
@@ -77,84 +98,125 @@ __global__ __launch_bounds__(256) void decode_step_kernel(
 
   float kk[RPT], qq[RPT], ga[RPT];
   f32x4 s[RPT];
-  // Without the layer's prologue every per-token input is requested before
-  // the state: then each state row is decayed and reduced as soon as it
-  // arrives, and no small load is left to wait for between the reduction and
-  // the write-back (a late v or beta load cost 3 % of the step).  The
-  // scheduling barrier keeps the compiler from sinking these loads to their
-  // first uses.
-  const float b_in = beta[tok];
-  float v_in[4];
-  if (!LAYER) {
-    const in_t* vp0 = v + tok * DV + 4 * cg;
-#pragma unroll
-    for (int c = 0; c < 4; ++c) v_in[c] = (float)vp0[c];
+  const int W1 = LAYER ? lp.conv_w - 1 : -1;
+  const bool conv = LAYER && W1 >= 0;
+  auto load_state = [&]() {
 #pragma unroll
     for (int m = 0; m < RPT; ++m) {
       const int i = rg + RG * m;
-      kk[m] = (float)kp[i];
-      qq[m] = (float)qp[i];
-      ga[m] = SG ? 0.f : gp[i];
+      s[m] = __builtin_nontemporal_load(reinterpret_cast<const f32x4*>(sp + (size_t)i * DV + 4 * cg));
+    }
+  };
+  // Every per-token input is requested with the state and before any wait:
+  // a small load issued after a wait (the compiler had put v after the state
+  // had arrived and beta after the cross-wave barrier) is a memory round trip
+  // of its own between the reduction and the write-back, 3 % of the step.
+  // Without the layer's convolution the inputs go first, so each state row is
+  // decayed and reduced as soon as it arrives.  Values are kept as loaded
+  // (raw32), addresses are clamped instead of branched on, and the scheduling
+  // barrier keeps the compiler from sinking the loads to their first uses.
+  if constexpr (LAYER) load_state();
+  const float b_in = beta[tok];
+  unsigned kraw[RPT], qraw[RPT], vraw[4];
+#pragma unroll
+  for (int m = 0; m < RPT; ++m) ga[m] = SG ? 0.f : gp[rg + RG * m];
+  {  // unused after the convolution, but unconditional (see below)
+    const in_t* vp0 = v + tok * DV + 4 * cg;
+#pragma unroll
+    for (int c = 0; c < 4; ++c) vraw[c] = raw32(vp0 + c);
+#pragma unroll
+    for (int m = 0; m < RPT; ++m) {
+      kraw[m] = raw32(kp + rg + RG * m);
+      qraw[m] = raw32(qp + rg + RG * m);
     }
   }
-#pragma unroll
-  for (int m = 0; m < RPT; ++m) {
-    const int i = rg + RG * m;
-    s[m] = __builtin_nontemporal_load(reinterpret_cast<const f32x4*>(sp + (size_t)i * DV + 4 * cg));
-  }
-  if constexpr (!LAYER) __builtin_amdgcn_sched_barrier(0);
-  float r[4] = {0, 0, 0, 0}, p[4] = {0, 0, 0, 0}, kq = 0.f, nq = 0.f, nk = 0.f;
-  const int W1 = LAYER ? lp.conv_w - 1 : -1;
   // Short convolution: each (tensor, channel) of this (n, h) is convolved by
   // one thread, which also shifts that channel's carried inputs (it alone
-  // reads them), and published through LDS.
-  __shared__ float cv[LAYER ? 3 : 1][LAYER ? DK : 1];
-  if (LAYER && W1 >= 0) {
-    const int hh = nh % lp.H;
-    for (int item = t; item < 3 * DK; item += 256) {
+  // reads them), and published through LDS.  Its inputs: the new value, the
+  // W weights and the W-1 carried inputs of each of the thread's items.
+  // The layer's loads are unconditional, from a valid stand-in address where
+  // an input is absent: a load under a branch leaves the other path waiting
+  // for it, and for every load issued before it, wherever that path reuses
+  // its register.
+  constexpr int NIT = LAYER ? (3 * DK + 255) / 256 : 1;
+  unsigned xr[NIT], ol[NIT][3], gt_in[4];
+  float wv[NIT][4], nw_in[4];
+  if constexpr (LAYER) {
+    const int hh = nh % lp.H, w1c = W1 > 0 ? W1 : 0;
+#pragma unroll
+    for (int it = 0; it < NIT; ++it) {
+      // clamped: an item past the end repeats the last one and is not used
+      const int item = min(t + 256 * it, 3 * DK - 1);
       const int x = item / DK, i = item % DK;
-      const in_t* src = (x == 0 ? q : x == 1 ? k : v) + tok * DK;
-      const float xn = (float)src[i];
-      const float* wr = lp.cw[x] + ((size_t)hh * DK + i) * (W1 + 1);
-      const in_t* in = reinterpret_cast<const in_t*>(lp.cs_in[x]);
-      in_t* out = reinterpret_cast<in_t*>(lp.cs_out[x]);
-      const size_t b0 = (size_t)nh * W1 * DK + i;
-      float old[3];
+      xr[it] = raw32((x == 0 ? q : x == 1 ? k : v) + tok * DK + i);
+      const float* wr = conv ? (x == 0 ? lp.cw[0] : x == 1 ? lp.cw[1] : lp.cw[2]) +
+                                   ((size_t)hh * DK + i) * (W1 + 1)
+                             : gp;
 #pragma unroll
-      for (int j = 0; j < 3; ++j) old[j] = (j < W1 && in) ? (float)in[b0 + (size_t)j * DK] : 0.f;
-      float acc = wr[W1] * xn;
+      for (int j = 0; j < 4; ++j) wv[it][j] = wr[j <= W1 ? j : w1c];
+      // carried inputs j < W1 (nullptr: zeros)
+      const in_t* in = reinterpret_cast<const in_t*>(x == 0 ? lp.cs_in[0] : x == 1 ? lp.cs_in[1] : lp.cs_in[2]);
+      const bool has_in = conv && in != nullptr && W1 > 0;
+      const in_t* ib = has_in ? in + (size_t)nh * W1 * DK + i : q + tok * DK;
 #pragma unroll
-      for (int j = 0; j < 3; ++j)
-        if (j < W1) acc += wr[j] * old[j];
-      cv[x][i] = acc;
-      if (out && W1 > 0) {
+      for (int j = 0; j < 3; ++j) ol[it][j] = raw32(ib + (has_in && j < W1 ? (size_t)j * DK : 0));
+    }
+    // the epilogue's gate and RMSNorm weight (used by the threads of row group 0)
+    const in_t* gt = lp.gate ? reinterpret_cast<const in_t*>(lp.gate) + tok * DV + 4 * cg : q + tok * DK;
+    const float* nw = lp.gate ? lp.norm_weight + 4 * cg : gp;
 #pragma unroll
-        for (int j = 0; j < 2; ++j)
-          if (j + 1 < W1) out[b0 + (size_t)j * DK] = (in_t)old[j + 1];  // exact: old came from in_t
-        out[b0 + (size_t)(W1 - 1) * DK] = src[i];
+    for (int c = 0; c < 4; ++c) {
+      gt_in[c] = raw32(gt + (lp.gate ? c : 0));
+      nw_in[c] = nw[lp.gate ? c : 0];
+    }
+  }
+  if constexpr (!LAYER) load_state();
+  __builtin_amdgcn_sched_barrier(0);
+  float r[4] = {0, 0, 0, 0}, p[4] = {0, 0, 0, 0}, kq = 0.f, nq = 0.f, nk = 0.f;
+  __shared__ float cv[LAYER ? 3 : 1][LAYER ? DK : 1];
+  if (conv) {
+#pragma unroll
+    for (int it = 0; it < NIT; ++it) {
+      const int item = t + 256 * it;
+      if (item < 3 * DK) {
+        const int x = item / DK, i = item % DK;
+        float wl = 0.f;  // the weight on the new value, W - 1
+#pragma unroll
+        for (int j = 0; j < 4; ++j)
+          if (j == W1) wl = wv[it][j];
+        const in_t* in = reinterpret_cast<const in_t*>(x == 0 ? lp.cs_in[0] : x == 1 ? lp.cs_in[1] : lp.cs_in[2]);
+        float acc = wl * raw_to_f<in_t>(xr[it]);
+#pragma unroll
+        for (int j = 0; j < 3; ++j)
+          if (j < W1) acc += wv[it][j] * (in ? raw_to_f<in_t>(ol[it][j]) : 0.f);
+        cv[LAYER ? x : 0][LAYER ? i : 0] = acc;
+        in_t* out = reinterpret_cast<in_t*>(x == 0 ? lp.cs_out[0] : x == 1 ? lp.cs_out[1] : lp.cs_out[2]);
+        if (out && W1 > 0) {
+          const size_t b0 = (size_t)nh * W1 * DK + i;
+#pragma unroll
+          for (int j = 0; j < 2; ++j)
+            if (j + 1 < W1) out[b0 + (size_t)j * DK] = in ? raw_to_t<in_t>(ol[it][j + 1]) : in_t(0.f);
+          out[b0 + (size_t)(W1 - 1) * DK] = raw_to_t<in_t>(xr[it]);
+        }
       }
     }
     __syncthreads();
   }
-  const bool conv = LAYER && W1 >= 0;
-  if constexpr (LAYER) {
-#pragma unroll
-    for (int m = 0; m < RPT; ++m) {
-      const int i = rg + RG * m;
-      kk[m] = conv ? cv[1][i] : (float)kp[i];
-      qq[m] = conv ? cv[0][i] : (float)qp[i];
-    }
-  }
 #pragma unroll
   for (int m = 0; m < RPT; ++m) {
     const int i = rg + RG * m;
+    kk[m] = conv ? cv[LAYER ? 1 : 0][LAYER ? i : 0] : raw_to_f<in_t>(kraw[m]);
+    qq[m] = conv ? cv[0][LAYER ? i : 0] : raw_to_f<in_t>(qraw[m]);
+  }
+#pragma unroll
+  for (int m = 0; m < RPT; ++m) {
     if (LAYER && lp.prologue) {
       kk[m] = swish_d(kk[m]);
       qq[m] = swish_d(qq[m]);
       nk += kk[m] * kk[m];
       nq += qq[m] * qq[m];
     }
-    const float a = SG ? ag : __expf(LAYER ? gp[i] : ga[m]);
+    const float a = SG ? ag : __expf(ga[m]);
 #pragma unroll
     for (int c = 0; c < 4; ++c) {
       s[m][c] *= a;
@@ -180,10 +242,9 @@ __global__ __launch_bounds__(256) void decode_step_kernel(
   }
   constexpr int NRED = LAYER ? 11 : 9;
   __shared__ float red[4][TPR][NRED];
-  const in_t* vp = v + tok * DV + 4 * cg;
   float vv[4];
 #pragma unroll
-  for (int c = 0; c < 4; ++c) vv[c] = !LAYER ? v_in[c] : conv ? cv[LAYER ? 2 : 0][4 * cg + c] : (float)vp[c];
+  for (int c = 0; c < 4; ++c) vv[c] = conv ? cv[LAYER ? 2 : 0][LAYER ? 4 * cg + c : 0] : raw_to_f<in_t>(vraw[c]);
   const int w = t >> 6;
   if ((t & 63) < TPR) {
 #pragma unroll
@@ -243,10 +304,8 @@ __global__ __launch_bounds__(256) void decode_step_kernel(
 #pragma unroll
       for (int off = 1; off < TPR; off <<= 1) ss += __shfl_xor(ss, off);
       const float inv = 1.f / sqrtf(ss / DV + lp.norm_eps);
-      const in_t* gt = reinterpret_cast<const in_t*>(lp.gate) + tok * DV + 4 * cg;
 #pragma unroll
-      for (int c = 0; c < 4; ++c)
-        y[c] = y[c] * inv * lp.norm_weight[4 * cg + c] * sigmoid_d((float)gt[c]);
+      for (int c = 0; c < 4; ++c) y[c] = y[c] * inv * nw_in[c] * sigmoid_d(raw_to_f<in_t>(gt_in[c]));
     }
     if constexpr (OUT_BF16) {
       bf16x4 ov;
@@ -262,10 +321,19 @@ __global__ __launch_bounds__(256) void decode_step_kernel(
   }
 }
 
+// The plain step at d = 128 streams the state fastest with two workgroups per
+// compute unit: 176 us per step at two against 193 at three, 198 at four (its
+// 123 registers allow four) and 186-196 at one, for 256 sequences x 32 heads.
+// An unused dynamic LDS allocation of more than a third of the unit's 160 KB
+// caps it at two.  The layer step (152 registers, three per unit) and other
+// widths keep the occupancy their registers give.
+constexpr unsigned kDecodeLdsPad = 56 * 1024;
+
 template <typename in_t, int D, bool OUT_BF16, bool LAYER>
 static void launch_decode_l(const DecodeArgs& a) {
   const int NH = a.N * a.H;
   dim3 grid(NH), block(256);
+  const unsigned pad = !LAYER && D == 128 ? kDecodeLdsPad : 0;
   LayerPtrs lp{a.layer.prologue ? 1 : 0, a.layer.gate, a.layer.norm_weight, a.layer.norm_eps,
                a.layer.prologue ? a.layer.conv_w : 0, a.H};
   for (int x = 0; x < 3; ++x) {
@@ -274,11 +342,11 @@ static void launch_decode_l(const DecodeArgs& a) {
     lp.cs_out[x] = a.layer.conv_state_out[x];
   }
   if (a.scalar_g)
-    hipLaunchKernelGGL((decode_step_kernel<in_t, D, D, OUT_BF16, true, LAYER>), grid, block, 0,
+    hipLaunchKernelGGL((decode_step_kernel<in_t, D, D, OUT_BF16, true, LAYER>), grid, block, pad,
                        a.stream, (const in_t*)a.q, (const in_t*)a.k, (const in_t*)a.v, a.g, a.beta,
                        a.state, a.o, NH, lp);
   else
-    hipLaunchKernelGGL((decode_step_kernel<in_t, D, D, OUT_BF16, false, LAYER>), grid, block, 0,
+    hipLaunchKernelGGL((decode_step_kernel<in_t, D, D, OUT_BF16, false, LAYER>), grid, block, pad,
                        a.stream, (const in_t*)a.q, (const in_t*)a.k, (const in_t*)a.v, a.g, a.beta,
                        a.state, a.o, NH, lp);
 }
