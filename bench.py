@@ -64,7 +64,7 @@ def decode_algorithmic_bytes(N=D_N, H=D_H, d=D_D):
 # values it was measured on.
 TRAFFIC = {
     "prefill": {"sources": "5a37ecc13cc819bd", "bytes": 836909440},
-    "decode": {"sources": "18352391e83cf0b2", "bytes": 1089360800},
+    "decode": {"sources": "83eebaf2c2207190", "bytes": 1089116640},
 }
 
 
