@@ -101,11 +101,13 @@ __device__ __forceinline__ f32x4 mfma4(float a, float b, f32x4 c) {
 // A[m][k] (TA = false) or A[k][m] (TA = true), op(B) [K x N] stored as B[k][n]
 // (TB = false) or B[n][k] (TB = true), leading dimensions lda, ldb, ldc, and
 // an optional mask on C (1: keep n <= m, 2: keep n < m).  One 64 x 64 tile of
-// C per workgroup of 256 threads, 4 x 4 outputs each; K, M and N multiples
-// of 4.  K runs in stages of 64: a stage of op(A)'s and op(B)'s tiles is
-// loaded with 16-byte loads along each matrix's contiguous dimension (all of
-// a thread's loads issued together), written to LDS, and the next stage's
-// loads are issued before this stage's products, so they overlap.
+// C per workgroup of 256 threads; each wave computes a 32 x 32 quarter as
+// four 16 x 16 tiles on v_mfma_f32_16x16x4f32 (fp32 operands, fp32
+// accumulation); K, M and N multiples of 4.  K runs in stages of 64: a stage
+// of op(A)'s and op(B)'s tiles is loaded with 16-byte loads along each
+// matrix's contiguous dimension (all of a thread's loads issued together),
+// written to LDS, and the next stage's loads are issued before this stage's
+// products, so they overlap.
 constexpr int kGemmKStage = 64, kGemmLd = 64 + 4;
 constexpr size_t kGemmLds = (size_t)2 * kGemmKStage * kGemmLd * sizeof(float);
 
@@ -176,8 +178,16 @@ __global__ __launch_bounds__(256) void fp32_gemm_kernel(const float* __restrict_
       }
     }
   };
-  const int tx = tid % 16, ty = tid / 16;
-  float acc[4][4] = {};
+  // MFMA operands: lane l holds A[m = l % 16][k + l / 16] and
+  // B[k + l / 16][n = l % 16]; output register i is row 4 (l / 16) + i,
+  // column l % 16 of the tile.
+  const int l = tid & 63, lm = l & 15, lg = l >> 4;
+  const int wm = (tid >> 7) * 32, wn = ((tid >> 6) & 1) * 32;  // this wave's quarter
+  f32x4 acc[2][2];
+#pragma unroll
+  for (int i = 0; i < 2; ++i)
+#pragma unroll
+    for (int j = 0; j < 2; ++j) acc[i][j] = f32x4{0.f, 0.f, 0.f, 0.f};
   fetch(0, K < kGemmKStage ? K : kGemmKStage);
   for (int k0 = 0; k0 < K; k0 += kGemmKStage) {
     const int ks = K - k0 < kGemmKStage ? K - k0 : kGemmKStage;
@@ -188,28 +198,36 @@ __global__ __launch_bounds__(256) void fp32_gemm_kernel(const float* __restrict_
       const int k1 = k0 + kGemmKStage;
       fetch(k1, K - k1 < kGemmKStage ? K - k1 : kGemmKStage);
     }
-#pragma unroll 4
-    for (int kk = 0; kk < ks; ++kk) {
-      const f32x4 av = *reinterpret_cast<const f32x4*>(As + kk * LD + ty * 4);
-      const f32x4 bv = *reinterpret_cast<const f32x4*>(Bs + kk * LD + tx * 4);
+    auto kstep = [&](int kk) {
+      const float* ar = As + (kk + lg) * LD + wm + lm;
+      const float* br = Bs + (kk + lg) * LD + wn + lm;
+      const float a0 = ar[0], a1 = ar[16], b0 = br[0], b1 = br[16];
+      acc[0][0] = mfma4(a0, b0, acc[0][0]);
+      acc[0][1] = mfma4(a0, b1, acc[0][1]);
+      acc[1][0] = mfma4(a1, b0, acc[1][0]);
+      acc[1][1] = mfma4(a1, b1, acc[1][1]);
+    };
+    if (ks == kGemmKStage) {
 #pragma unroll
-      for (int x = 0; x < 4; ++x)
-#pragma unroll
-        for (int y = 0; y < 4; ++y) acc[x][y] += av[x] * bv[y];
+      for (int kk = 0; kk < kGemmKStage; kk += 4) kstep(kk);
+    } else {
+      for (int kk = 0; kk < ks; kk += 4) kstep(kk);
     }
   }
   float* c = Cm + bt * sc;
 #pragma unroll
-  for (int x = 0; x < 4; ++x)
+  for (int ti = 0; ti < 2; ++ti)
 #pragma unroll
-    for (int y = 0; y < 4; ++y) {
-      const int m = m0 + ty * 4 + x, nn = n0 + tx * 4 + y;
-      if (m < M && nn < N) {
-        const bool keep = mask == 0 || (mask == 1 ? nn <= m : nn < m);
-        const float v = keep ? alpha * acc[x][y] : 0.f;
-        c[(size_t)m * ldc + nn] = acc_c ? c[(size_t)m * ldc + nn] + v : v;
+    for (int tj = 0; tj < 2; ++tj)
+#pragma unroll
+      for (int i = 0; i < 4; ++i) {
+        const int m = m0 + wm + 16 * ti + 4 * lg + i, nn = n0 + wn + 16 * tj + lm;
+        if (m < M && nn < N) {
+          const bool keep = mask == 0 || (mask == 1 ? nn <= m : nn < m);
+          const float v = keep ? alpha * acc[ti][tj][i] : 0.f;
+          c[(size_t)m * ldc + nn] = acc_c ? c[(size_t)m * ldc + nn] + v : v;
+        }
       }
-    }
 }
 
 // Operand orientations of fp32_gemm_kernel, as tags for launch_fp32_gemm.
