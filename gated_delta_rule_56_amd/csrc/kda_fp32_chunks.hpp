@@ -103,11 +103,15 @@ __device__ __forceinline__ f32x4 mfma4(float a, float b, f32x4 c) {
 // an optional mask on C (1: keep n <= m, 2: keep n < m).  One 64 x 64 tile of
 // C per workgroup of 256 threads; each wave computes a 32 x 32 quarter as
 // four 16 x 16 tiles on v_mfma_f32_16x16x4f32 (fp32 operands, fp32
-// accumulation); K, M and N multiples of 4.  K runs in stages of 64: a stage
-// of op(A)'s and op(B)'s tiles is loaded with 16-byte loads along each
+// accumulation); K a multiple of 16, M and N of 4.  K runs in stages of 64:
+// a stage of op(A)'s and op(B)'s tiles is loaded with 16-byte loads along each
 // matrix's contiguous dimension (all of a thread's loads issued together),
-// written to LDS, and the next stage's loads are issued before this stage's
-// products, so they overlap.
+// written to LDS as As[m][k] and Bs[n][k], and the next stage's loads are
+// issued before this stage's products, so they overlap.  Within each block of
+// 16 k the lanes of group g (lanes 16 g .. 16 g + 15) take k = 4 g .. 4 g + 3
+// in four successive MFMAs, so one 16-byte LDS read per operand and tile feeds
+// four products; with 68-float rows the reads of eight lanes cover the 32
+// banks once.
 constexpr int kGemmKStage = 64, kGemmLd = 64 + 4;
 constexpr size_t kGemmLds = (size_t)2 * kGemmKStage * kGemmLd * sizeof(float);
 
@@ -118,8 +122,8 @@ __global__ __launch_bounds__(256) void fp32_gemm_kernel(const float* __restrict_
                                                        int lda, int ldb, int ldc, size_t sa,
                                                        size_t sb, size_t sc, float alpha, int acc_c,
                                                        int mask) {
-  __shared__ __attribute__((aligned(16))) float As[kGemmKStage * kGemmLd];  // As[k][m]
-  __shared__ __attribute__((aligned(16))) float Bs[kGemmKStage * kGemmLd];  // Bs[k][n]
+  __shared__ __attribute__((aligned(16))) float As[64 * kGemmLd];  // As[m][k]
+  __shared__ __attribute__((aligned(16))) float Bs[64 * kGemmLd];  // Bs[n][k]
   constexpr int LD = kGemmLd, NV = kGemmKStage * 16 / 256;  // vectors per thread and matrix
   const int bt = blockIdx.x;  // batch on x: up to 2^31 - 1 blocks
   const int m0 = blockIdx.z * 64, n0 = blockIdx.y * 64;
@@ -127,27 +131,27 @@ __global__ __launch_bounds__(256) void fp32_gemm_kernel(const float* __restrict_
   const float* bb = B + bt * sb;
   const int tid = threadIdx.x;
   f32x4 xa[NV], xb[NV];
-  // Vector v of stage k0 (ks = its k extent): for a matrix stored with k as
-  // its row (TA for A, !TB for B) row k0 + v / 16, columns 4 (v % 16) ..;
-  // otherwise row v / (ks / 4) of the 64, k0 + 4 (v % (ks / 4)) ...
+  // Vector v = tid + 256 x of stage k0 (ks = its k extent): for a matrix
+  // stored with k as its row (TA for A, !TB for B) row k0 + 16 x + tid % 16,
+  // columns 4 (tid / 16) ..; otherwise row v / (ks / 4) of the 64, columns
+  // k0 + 4 (v % (ks / 4)) ...  (In the first case sixteen consecutive threads
+  // take sixteen rows, so their transposing LDS writes hit distinct banks.)
   auto fetch = [&](int k0, int ks) {
 #pragma unroll
     for (int x = 0; x < NV; ++x) {
-      const int v = tid + 256 * x;
+      const int v = tid + 256 * x, kr = 16 * x + tid % 16, c4 = 4 * (tid / 16);
       xa[x] = f32x4{0, 0, 0, 0};
       xb[x] = f32x4{0, 0, 0, 0};
       if (v < ks * 16) {
         if (TA) {
-          const int mm = 4 * (v % 16);
-          if (m0 + mm < M) xa[x] = *reinterpret_cast<const f32x4*>(a + (size_t)(k0 + v / 16) * lda + m0 + mm);
+          if (m0 + c4 < M) xa[x] = *reinterpret_cast<const f32x4*>(a + (size_t)(k0 + kr) * lda + m0 + c4);
         } else {
           const int mm = v / (ks / 4);
           if (m0 + mm < M)
             xa[x] = *reinterpret_cast<const f32x4*>(a + (size_t)(m0 + mm) * lda + k0 + 4 * (v % (ks / 4)));
         }
         if (!TB) {
-          const int nn = 4 * (v % 16);
-          if (n0 + nn < N) xb[x] = *reinterpret_cast<const f32x4*>(bb + (size_t)(k0 + v / 16) * ldb + n0 + nn);
+          if (n0 + c4 < N) xb[x] = *reinterpret_cast<const f32x4*>(bb + (size_t)(k0 + kr) * ldb + n0 + c4);
         } else {
           const int nn = v / (ks / 4);
           if (n0 + nn < N)
@@ -159,28 +163,26 @@ __global__ __launch_bounds__(256) void fp32_gemm_kernel(const float* __restrict_
   auto stage = [&](int ks) {
 #pragma unroll
     for (int x = 0; x < NV; ++x) {
-      const int v = tid + 256 * x;
+      const int v = tid + 256 * x, kr = 16 * x + tid % 16, c4 = 4 * (tid / 16);
       if (v < ks * 16) {
         if (TA) {
-          *reinterpret_cast<f32x4*>(As + (v / 16) * LD + 4 * (v % 16)) = xa[x];
-        } else {
-          const int mm = v / (ks / 4), k = 4 * (v % (ks / 4));
 #pragma unroll
-          for (int e = 0; e < 4; ++e) As[(k + e) * LD + mm] = xa[x][e];
+          for (int e = 0; e < 4; ++e) As[(c4 + e) * LD + kr] = xa[x][e];
+        } else {
+          *reinterpret_cast<f32x4*>(As + (v / (ks / 4)) * LD + 4 * (v % (ks / 4))) = xa[x];
         }
         if (!TB) {
-          *reinterpret_cast<f32x4*>(Bs + (v / 16) * LD + 4 * (v % 16)) = xb[x];
-        } else {
-          const int nn = v / (ks / 4), k = 4 * (v % (ks / 4));
 #pragma unroll
-          for (int e = 0; e < 4; ++e) Bs[(k + e) * LD + nn] = xb[x][e];
+          for (int e = 0; e < 4; ++e) Bs[(c4 + e) * LD + kr] = xb[x][e];
+        } else {
+          *reinterpret_cast<f32x4*>(Bs + (v / (ks / 4)) * LD + 4 * (v % (ks / 4))) = xb[x];
         }
       }
     }
   };
-  // MFMA operands: lane l holds A[m = l % 16][k + l / 16] and
-  // B[k + l / 16][n = l % 16]; output register i is row 4 (l / 16) + i,
-  // column l % 16 of the tile.
+  // MFMA operands: lane l = 16 g + i holds row i of the A tile and column i
+  // of the B tile at the k this step gives group g; output register r is row
+  // 4 g + r, column i of the tile.
   const int l = tid & 63, lm = l & 15, lg = l >> 4;
   const int wm = (tid >> 7) * 32, wn = ((tid >> 6) & 1) * 32;  // this wave's quarter
   f32x4 acc[2][2];
@@ -198,20 +200,25 @@ __global__ __launch_bounds__(256) void fp32_gemm_kernel(const float* __restrict_
       const int k1 = k0 + kGemmKStage;
       fetch(k1, K - k1 < kGemmKStage ? K - k1 : kGemmKStage);
     }
-    auto kstep = [&](int kk) {
-      const float* ar = As + (kk + lg) * LD + wm + lm;
-      const float* br = Bs + (kk + lg) * LD + wn + lm;
-      const float a0 = ar[0], a1 = ar[16], b0 = br[0], b1 = br[16];
-      acc[0][0] = mfma4(a0, b0, acc[0][0]);
-      acc[0][1] = mfma4(a0, b1, acc[0][1]);
-      acc[1][0] = mfma4(a1, b0, acc[1][0]);
-      acc[1][1] = mfma4(a1, b1, acc[1][1]);
+    auto kblock = [&](int kb) {  // k = 16 kb .. 16 kb + 15 of the stage
+      const int ko = 16 * kb + 4 * lg;
+      const f32x4 a0 = *reinterpret_cast<const f32x4*>(As + (wm + lm) * LD + ko);
+      const f32x4 a1 = *reinterpret_cast<const f32x4*>(As + (wm + 16 + lm) * LD + ko);
+      const f32x4 b0 = *reinterpret_cast<const f32x4*>(Bs + (wn + lm) * LD + ko);
+      const f32x4 b1 = *reinterpret_cast<const f32x4*>(Bs + (wn + 16 + lm) * LD + ko);
+#pragma unroll
+      for (int s = 0; s < 4; ++s) {
+        acc[0][0] = mfma4(a0[s], b0[s], acc[0][0]);
+        acc[0][1] = mfma4(a0[s], b1[s], acc[0][1]);
+        acc[1][0] = mfma4(a1[s], b0[s], acc[1][0]);
+        acc[1][1] = mfma4(a1[s], b1[s], acc[1][1]);
+      }
     };
     if (ks == kGemmKStage) {
 #pragma unroll
-      for (int kk = 0; kk < kGemmKStage; kk += 4) kstep(kk);
+      for (int kb = 0; kb < kGemmKStage / 16; ++kb) kblock(kb);
     } else {
-      for (int kk = 0; kk < ks; kk += 4) kstep(kk);
+      for (int kb = 0; kb < ks / 16; ++kb) kblock(kb);
     }
   }
   float* c = Cm + bt * sc;
@@ -240,7 +247,7 @@ template <bool TA, bool TB>
 inline hipError_t launch_fp32_gemm(const float* A, const float* B, float* Cm, int M, int N, int K,
                                    int lda, int ldb, int ldc, size_t sa, size_t sb, size_t sc,
                                    float alpha, int acc_c, int mask, size_t NB, hipStream_t stream) {
-  if (K % 4 || M % 4 || N % 4) return hipErrorInvalidValue;
+  if (K % 16 || M % 4 || N % 4) return hipErrorInvalidValue;
   const dim3 grid((unsigned)NB, (N + 63) / 64, (M + 63) / 64);
   hipLaunchKernelGGL((fp32_gemm_kernel<TA, TB>), grid, dim3(256), 0, stream, A, B, Cm, M, N, K, lda,
                      ldb, ldc, sa, sb, sc, alpha, acc_c, mask);
