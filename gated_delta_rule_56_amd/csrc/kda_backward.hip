@@ -472,32 +472,86 @@ __global__ __launch_bounds__(kSerThreads) void bwd_bwd_states_kernel(Planes p, G
 // dA = strict_tril(-M^T dM M^T); dBm = Diag(beta) dA.
 template <int C>
 __global__ __launch_bounds__(256) void bwd_cc_kernel(Planes p) {
-  __shared__ float Ms[C][C + 1];
-  __shared__ float dMs[C][C + 1];
-  __shared__ float Xs[C][C + 1];
+  // Both products on v_mfma_f32_16x16x4f32, one 16 x 16 tile per
+  // accumulator: wave w owns tiles w, w + 4, ... of the NT x NT grid.  Rows of
+  // 68 floats let a lane read four consecutive k in one 16-byte LDS read (lane
+  // group g takes k = 4 g .. 4 g + 3 of each block of 16) with the eight lanes
+  // served together on distinct banks.
+  constexpr int LDC = C + 4, NT = C / 16, TPW = (NT * NT + 3) / 4;
+  __shared__ __attribute__((aligned(16))) float Ms[C][LDC];   // M
+  __shared__ __attribute__((aligned(16))) float MTs[C][LDC];  // M^T
+  __shared__ __attribute__((aligned(16))) float dMs[C][LDC];  // dM = dT Diag(beta), later dA * Bm
+  __shared__ __attribute__((aligned(16))) float Xs[C][LDC];   // X = dM M^T
   const int b = blockIdx.x, tid = threadIdx.x;
   const size_t pcc = (size_t)b * C * C;
   const float* beta = p.beta + (size_t)b * C;
   for (int idx = tid; idx < C * C; idx += 256) {
     const int r = idx / C, i = idx % C;
-    Ms[r][i] = p.M[pcc + idx];
+    const float m = p.M[pcc + idx];
+    Ms[r][i] = m;
+    MTs[i][r] = m;
     dMs[r][i] = p.dT[pcc + idx] * beta[i];
   }
   __syncthreads();
-  for (int idx = tid; idx < C * C; idx += 256) {  // X = dM M^T
-    const int r = idx / C, i = idx % C;
-    float s = 0.f;
-    for (int l = 0; l < C; ++l) s += dMs[r][l] * Ms[i][l];
-    Xs[r][i] = s;
+  const int w = tid >> 6, l = tid & 63, lm = l & 15, lg = l >> 4;
+  f32x4 acc[TPW];
+  // X = dM M^T: A[r][l] = dM[r][l], B[l][i] = M[i][l]
+#pragma unroll
+  for (int j = 0; j < TPW; ++j) acc[j] = f32x4{0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+  for (int k = 0; k < C; k += 16) {
+#pragma unroll
+    for (int j = 0; j < TPW; ++j) {
+      const int t = w + 4 * j;
+      if (t < NT * NT) {
+        const int r0 = 16 * (t / NT), c0 = 16 * (t % NT);
+        const f32x4 a = *reinterpret_cast<const f32x4*>(&dMs[r0 + lm][k + 4 * lg]);
+        const f32x4 bq = *reinterpret_cast<const f32x4*>(&Ms[c0 + lm][k + 4 * lg]);
+#pragma unroll
+        for (int q = 0; q < 4; ++q) acc[j] = mfma4(a[q], bq[q], acc[j]);
+      }
+    }
+  }
+#pragma unroll
+  for (int j = 0; j < TPW; ++j) {
+    const int t = w + 4 * j;
+    if (t < NT * NT) {
+      const int r0 = 16 * (t / NT), c0 = 16 * (t % NT);
+#pragma unroll
+      for (int v = 0; v < 4; ++v) Xs[r0 + 4 * lg + v][c0 + lm] = acc[j][v];
+    }
   }
   __syncthreads();
-  for (int idx = tid; idx < C * C; idx += 256) {  // dA = -M^T X, strictly lower
-    const int r = idx / C, i = idx % C;
-    float s = 0.f;
-    if (i < r)
-      for (int l = 0; l < C; ++l) s -= Ms[l][r] * Xs[l][i];
-    p.dBm[pcc + idx] = beta[r] * s;
-    dMs[r][i] = s * p.Bm[pcc + idx];  // dA * Bm, for the row sums
+  // dA = -M^T X, strictly lower: A[r][l] = M^T[r][l], B[l][i] = X[l][i]
+  // (tiles wholly above the diagonal are zero and skip the products)
+#pragma unroll
+  for (int j = 0; j < TPW; ++j) acc[j] = f32x4{0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+  for (int k = 0; k < C; k += 16) {
+#pragma unroll
+    for (int j = 0; j < TPW; ++j) {
+      const int t = w + 4 * j;
+      const int r0 = 16 * (t / NT), c0 = 16 * (t % NT);
+      if (t < NT * NT && c0 <= r0) {
+        const f32x4 a = *reinterpret_cast<const f32x4*>(&MTs[r0 + lm][k + 4 * lg]);
+#pragma unroll
+        for (int q = 0; q < 4; ++q) acc[j] = mfma4(a[q], Xs[k + 4 * lg + q][c0 + lm], acc[j]);
+      }
+    }
+  }
+#pragma unroll
+  for (int j = 0; j < TPW; ++j) {
+    const int t = w + 4 * j;
+    if (t < NT * NT) {
+      const int r0 = 16 * (t / NT), c0 = 16 * (t % NT);
+#pragma unroll
+      for (int v = 0; v < 4; ++v) {
+        const int r = r0 + 4 * lg + v, i = c0 + lm;
+        const float sv = i < r ? -acc[j][v] : 0.f;
+        p.dBm[pcc + r * C + i] = beta[r] * sv;
+        dMs[r][i] = sv * p.Bm[pcc + r * C + i];  // dA * Bm, for the row sums
+      }
+    }
   }
   __syncthreads();
   if (tid < C) {
