@@ -750,7 +750,10 @@ __global__ __launch_bounds__(kIntraThreads, 4) void intra_chunk_kernel(KernelPtr
     for (int x = 0; x < NWT; ++x) {
       const int idx = tid + kIntraThreads * x;
       const int t = idx / (D * kMaxConv), c = (idx / kMaxConv) % D, j = idx % kMaxConv;
-      cwv[x] = idx < 3 * D * kMaxConv && j < W ? kp.cw[t][((size_t)h * D + c) * W + (W - 1 - j)] : 0.f;
+      // selected, not indexed: a per-lane index into the argument block
+      // would load the pointer from memory and wait for it first
+      const float* wt = t == 0 ? kp.cw[0] : t == 1 ? kp.cw[1] : kp.cw[2];
+      cwv[x] = idx < 3 * D * kMaxConv && j < W ? wt[((size_t)h * D + c) * W + (W - 1 - j)] : 0.f;
     }
   }
   Raw8<float> graw[FPW];
@@ -764,11 +767,17 @@ __global__ __launch_bounds__(kIntraThreads, 4) void intra_chunk_kernel(KernelPtr
     qraw[j].load(reinterpret_cast<const in_t*>(kp.q) + base);
     kraw[j].load(reinterpret_cast<const in_t*>(kp.k) + base);
   }
-  if (tid < KC) {
-    const int tb = clampi(t0 + (tid < len ? tid : 0), 0, si.total_tokens - 1);
-    const float bv = kp.beta[(size_t)tb * H + h];
-    beta_s[tid] = tid < len ? (PRO ? sigmoidf(bv) : bv) : 0.f;
-  }
+  // beta (the sigmoid of its logit with the prologue) into LDS.  Its store
+  // waits for the load, so with the convolution it comes after the halo
+  // loads below: issued first, it would hold them back by a round trip.
+  auto stage_beta = [&]() {
+    if (tid < KC) {
+      const int tb = clampi(t0 + (tid < len ? tid : 0), 0, si.total_tokens - 1);
+      const float bv = kp.beta[(size_t)tb * H + h];
+      beta_s[tid] = tid < len ? (PRO ? sigmoidf(bv) : bv) : 0.f;
+    }
+  };
+  if constexpr (PRO != 2) stage_beta();
   // Layer prologue: Swish of q and k, after their short convolution when
   // PRO == 2.  Where the Gram region (unused until step 4) holds 32 B per
   // lane and fragment, the convolved, activated k waits there instead of in
@@ -788,6 +797,7 @@ __global__ __launch_bounds__(kIntraThreads, 4) void intra_chunk_kernel(KernelPtr
       load_halo<in_t, D>(qe[j], kp, 0, it, rt, lr, 32 * fkb[j] + 8 * lg, si.total_tokens);
       load_halo<in_t, D>(ke[j], kp, 1, it, rt, lr, 32 * fkb[j] + 8 * lg, si.total_tokens);
     }
+    stage_beta();
 #pragma unroll
     for (int x = 0; x < NWT; ++x) {
       const int idx = tid + kIntraThreads * x;
