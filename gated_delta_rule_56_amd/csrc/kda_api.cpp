@@ -5,6 +5,7 @@
 #include <hip/hip_runtime.h>
 
 #include <math.h>
+#include <stdint.h>
 
 #include "kda_launch.hpp"
 
@@ -76,9 +77,22 @@ kda::Layer make_layer(const kda_layer_params* p) {
   return L;
 }
 
+// Options of kda_prefill_ex as the launcher's tuning (NULL: automatic).
+kda_status make_tuning(const kda_prefill_options* o, kda::PrefillTuning* t) {
+  *t = kda::PrefillTuning();
+  if (!o) return KDA_OK;
+  if (o->segment_chunks < 0) return KDA_ERR_INVALID_ARG;
+  if (o->value_block != 0 && o->value_block != 16 && o->value_block != 32)
+    return KDA_ERR_INVALID_ARG;
+  t->segment_chunks = o->segment_chunks;
+  t->segment_bytes = o->segment_bytes;
+  t->value_block = o->value_block;
+  return KDA_OK;
+}
+
 kda_status workspace_size(int B, int T, int H, int Dk, int Dv, int num_seqs,
                           const int32_t* cu_seqlens_host, int chunk_size, kda_dtype in_dtype,
-                          bool epilogue, size_t* bytes) {
+                          bool epilogue, const kda::PrefillTuning& tuning, size_t* bytes) {
   if (bytes == nullptr || H < 1 || !valid_dtype(in_dtype)) return KDA_ERR_INVALID_ARG;
   if (!supported_head(Dk, Dv) || !supported_chunk(chunk_size)) return KDA_ERR_UNSUPPORTED;
   int64_t chunks = 0;
@@ -87,7 +101,7 @@ kda_status workspace_size(int B, int T, int H, int Dk, int Dv, int num_seqs,
   kda_status st = seq_layout(B, T, num_seqs, cu_dev, cu_seqlens_host, chunk_size, &chunks);
   if (st != KDA_OK) return st;
   *bytes = kda::prefill_workspace_bytes(num_seqs, cu_seqlens_host, cu_seqlens_host ? 0 : T, H, Dk,
-                                        chunk_size, in_dtype == KDA_BF16, epilogue);
+                                        chunk_size, in_dtype == KDA_BF16, epilogue, tuning);
   return KDA_OK;
 }
 
@@ -112,7 +126,7 @@ kda_status kda_prefill_workspace_size(int B, int T, int H, int Dk, int Dv, int n
                                       const int32_t* cu_seqlens_host, int chunk_size,
                                       kda_dtype in_dtype, size_t* bytes) {
   return workspace_size(B, T, H, Dk, Dv, num_seqs, cu_seqlens_host, chunk_size, in_dtype, false,
-                        bytes);
+                        kda::PrefillTuning(), bytes);
 }
 
 kda_status kda_prefill_layer_workspace_size(int B, int T, int H, int Dk, int Dv, int num_seqs,
@@ -120,7 +134,7 @@ kda_status kda_prefill_layer_workspace_size(int B, int T, int H, int Dk, int Dv,
                                             kda_dtype in_dtype, const kda_layer_params* layer,
                                             size_t* bytes) {
   return workspace_size(B, T, H, Dk, Dv, num_seqs, cu_seqlens_host, chunk_size, in_dtype,
-                        layer != nullptr && layer->gate != nullptr, bytes);
+                        layer != nullptr && layer->gate != nullptr, kda::PrefillTuning(), bytes);
 }
 
 static kda_status prefill_impl(bool scalar_g, const kda::Layer& layer, const void* q, const void* k, const void* v,
@@ -129,7 +143,8 @@ static kda_status prefill_impl(bool scalar_g, const kda::Layer& layer, const voi
                                const int32_t* cu_seqlens, const int32_t* cu_seqlens_host,
                                int B, int T, int H, int Dk, int Dv, int num_seqs,
                                int chunk_size, kda_dtype in_dtype, kda_dtype out_dtype,
-                               void* workspace, size_t workspace_bytes, void* stream) {
+                               const kda::PrefillTuning& tuning, void* workspace,
+                               size_t workspace_bytes, void* stream) {
   if (H < 1 || !valid_dtype(in_dtype) || !valid_dtype(out_dtype)) return KDA_ERR_INVALID_ARG;
   if (!supported_head(Dk, Dv) || !supported_chunk(chunk_size)) return KDA_ERR_UNSUPPORTED;
   if (check_layer(layer) != KDA_OK) return KDA_ERR_INVALID_ARG;
@@ -141,9 +156,10 @@ static kda_status prefill_impl(bool scalar_g, const kda::Layer& layer, const voi
   if (st != KDA_OK) return st;
   // Token tensors may be empty (and then NULL) only when there are no tokens.
   if ((int64_t)B * T > 0 && (!q || !k || !v || !g || !beta || !o)) return KDA_ERR_INVALID_ARG;
-  const size_t need =
-      kda::prefill_workspace_bytes(num_seqs, cu_seqlens_host, cu_seqlens ? 0 : T, H, Dk,
-                                   chunk_size, in_dtype == KDA_BF16, layer.gate != nullptr);
+  const size_t need = kda::prefill_workspace_bytes(num_seqs, cu_seqlens_host, cu_seqlens ? 0 : T,
+                                                   H, Dk, chunk_size, in_dtype == KDA_BF16,
+                                                   layer.gate != nullptr, tuning);
+  if (need == SIZE_MAX) return KDA_ERR_WORKSPACE;
   if (need > 0 && (workspace == nullptr || workspace_bytes < need)) return KDA_ERR_WORKSPACE;
   if (workspace && !aligned(workspace, 256)) return KDA_ERR_INVALID_ARG;
 
@@ -168,6 +184,7 @@ static kda_status prefill_impl(bool scalar_g, const kda::Layer& layer, const voi
   a.out_bf16 = out_dtype == KDA_BF16;
   a.scalar_g = scalar_g;
   a.layer = layer;
+  a.tuning = tuning;
   a.workspace = workspace;
   a.stream = reinterpret_cast<hipStream_t>(stream);
   return kda::launch_prefill(a) == hipSuccess ? KDA_OK : KDA_ERR_HIP;
@@ -213,7 +230,7 @@ kda_status kda_prefill(const void* q, const void* k, const void* v, const float*
                        void* workspace, size_t workspace_bytes, void* stream) {
   return prefill_impl(false, kda::Layer(), q, k, v, g, beta, o, initial_state, final_state,
                       cu_seqlens, cu_seqlens_host, B, T, H, Dk, Dv, num_seqs, chunk_size,
-                      in_dtype, out_dtype, workspace, workspace_bytes, stream);
+                      in_dtype, out_dtype, kda::PrefillTuning(), workspace, workspace_bytes, stream);
 }
 
 kda_status gdn_prefill(const void* q, const void* k, const void* v, const float* g,
@@ -224,7 +241,43 @@ kda_status gdn_prefill(const void* q, const void* k, const void* v, const float*
                        void* workspace, size_t workspace_bytes, void* stream) {
   return prefill_impl(true, kda::Layer(), q, k, v, g, beta, o, initial_state, final_state,
                       cu_seqlens, cu_seqlens_host, B, T, H, Dk, Dv, num_seqs, chunk_size,
-                      in_dtype, out_dtype, workspace, workspace_bytes, stream);
+                      in_dtype, out_dtype, kda::PrefillTuning(), workspace, workspace_bytes, stream);
+}
+
+kda_status kda_prefill_workspace_size_ex(int form, int B, int T, int H, int Dk, int Dv,
+                                         int num_seqs, const int32_t* cu_seqlens_host,
+                                         int chunk_size, kda_dtype in_dtype, const void* layer,
+                                         const kda_prefill_options* options, size_t* bytes) {
+  if (form != KDA_FORM_KDA && form != KDA_FORM_GDN && form != KDA_FORM_LAYER)
+    return KDA_ERR_INVALID_ARG;
+  kda::PrefillTuning t;
+  const kda_status st = make_tuning(options, &t);
+  if (st != KDA_OK) return st;
+  const kda_layer_params* lp = static_cast<const kda_layer_params*>(layer);
+  const bool epi = form == KDA_FORM_LAYER && lp != nullptr && lp->gate != nullptr;
+  return workspace_size(B, T, H, Dk, Dv, num_seqs, cu_seqlens_host, chunk_size, in_dtype, epi, t,
+                        bytes);
+}
+
+kda_status kda_prefill_ex(int form, const void* q, const void* k, const void* v, const float* g,
+                          const float* beta, const void* layer, void* o,
+                          const float* initial_state, float* final_state,
+                          const int32_t* cu_seqlens, const int32_t* cu_seqlens_host, int B, int T,
+                          int H, int Dk, int Dv, int num_seqs, int chunk_size,
+                          kda_dtype in_dtype, kda_dtype out_dtype,
+                          const kda_prefill_options* options, void* workspace,
+                          size_t workspace_bytes, void* stream) {
+  if (form != KDA_FORM_KDA && form != KDA_FORM_GDN && form != KDA_FORM_LAYER)
+    return KDA_ERR_INVALID_ARG;
+  kda::PrefillTuning t;
+  const kda_status st = make_tuning(options, &t);
+  if (st != KDA_OK) return st;
+  const kda::Layer L = form == KDA_FORM_LAYER
+                           ? make_layer(static_cast<const kda_layer_params*>(layer))
+                           : kda::Layer();
+  return prefill_impl(form == KDA_FORM_GDN, L, q, k, v, g, beta, o, initial_state, final_state,
+                      cu_seqlens, cu_seqlens_host, B, T, H, Dk, Dv, num_seqs, chunk_size,
+                      in_dtype, out_dtype, t, workspace, workspace_bytes, stream);
 }
 
 kda_status kda_decode_step(const void* q, const void* k, const void* v, const float* g,
@@ -251,8 +304,8 @@ kda_status kda_prefill_layer(const void* q_pre, const void* k_pre, const void* v
                              void* stream) {
   return prefill_impl(false, make_layer(layer), q_pre, k_pre, v_pre, g, beta_logit, o,
                       initial_state, final_state, cu_seqlens, cu_seqlens_host, B, T, H, Dk, Dv,
-                      num_seqs, chunk_size, in_dtype, out_dtype, workspace, workspace_bytes,
-                      stream);
+                      num_seqs, chunk_size, in_dtype, out_dtype, kda::PrefillTuning(), workspace,
+                      workspace_bytes, stream);
 }
 
 kda_status kda_decode_step_layer(const void* q_pre, const void* k_pre, const void* v_pre,

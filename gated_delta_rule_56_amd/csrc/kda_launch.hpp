@@ -45,6 +45,14 @@ struct DecodeArgs {
 
 hipError_t launch_decode(const DecodeArgs& a);
 
+// Choices the prefill normally makes itself; zero fields mean automatic.
+struct PrefillTuning {
+  int segment_chunks = 0;    // local chunks per segment (>= 1), or 0
+  size_t segment_bytes = 0;  // operand budget of one segment, or 0
+  int value_block = 0;       // value columns per carry-pass workgroup (16 or 32), or 0
+  size_t workspace_cap = 0;  // the whole workspace must fit this many bytes, or 0 (no cap)
+};
+
 struct PrefillArgs {
   const void* q;
   const void* k;
@@ -63,6 +71,7 @@ struct PrefillArgs {
   bool in_bf16, out_bf16;
   bool scalar_g;              // g holds one log-decay per (token, head)
   Layer layer;
+  PrefillTuning tuning;
   void* workspace;
   hipStream_t stream;
 };
@@ -76,13 +85,16 @@ struct SegmentPlan {
   int nseg = 1;       // segments (at least one inter-chunk pass runs)
   int max_slots = 0;  // (sequence, chunk) slots of the largest segment, the first
 };
+// With tuning.workspace_cap set, a plan whose workspace exceeds the cap has
+// L = 0 and nseg = 0 (the call cannot run within it).
 SegmentPlan plan_segments(int num_seqs, const int32_t* cu_host, int seq_len, int H, int D,
-                          int chunk, bool in_bf16);
+                          int chunk, bool in_bf16, bool epilogue, const PrefillTuning& tuning);
 // Total workspace bytes (segment slot table, state carry between segments,
 // one segment's operands, and with the layer epilogue one segment's raw
-// fp32 output), 256-byte aligned pieces.
+// fp32 output), 256-byte aligned pieces; SIZE_MAX when no plan fits the cap.
 size_t prefill_workspace_bytes(int num_seqs, const int32_t* cu_host, int seq_len, int H, int D,
-                               int chunk, bool in_bf16, bool epilogue);
+                               int chunk, bool in_bf16, bool epilogue,
+                               const PrefillTuning& tuning);
 hipError_t launch_prefill(const PrefillArgs& a);
 
 struct BackwardArgs {

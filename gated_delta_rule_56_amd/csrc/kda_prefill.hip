@@ -40,7 +40,7 @@
 #include "kda_device.hpp"
 #include "kda_launch.hpp"
 
-#include <stdlib.h>
+#include <stdint.h>
 
 namespace kda {
 
@@ -101,21 +101,12 @@ size_t prefill_chunk_bytes(int D, int chunk, bool in_bf16) {
 // only add start-up and tail time, and the budget is 8 GiB, which only bounds
 // the workspace.  L is the largest length (at least 16 chunks, to amortise
 // the passes' start-up) whose operands fit the budget, then evened out over
-// the segments.  KDA_PREFILL_SEGMENT_KB (>= 1) overrides the budget
-// and KDA_PREFILL_SEGMENT_CHUNKS (>= 1) fixes L instead; both are read at
-// every call, and a workspace must be sized under the same settings as the
-// call that uses it.
-static size_t segment_budget_bytes(long long inter_workgroups) {
-  const char* e = getenv("KDA_PREFILL_SEGMENT_KB");
-  const long long v = e ? atoll(e) : 0;
-  if (v >= 1) return (size_t)v << 10;
+// the segments.  The caller's tuning may fix the budget or L instead; with a
+// workspace cap, L is the largest length (any, down to one chunk) whose whole
+// workspace fits the cap.
+static size_t segment_budget_bytes(long long inter_workgroups, const PrefillTuning& t) {
+  if (t.segment_bytes >= 1) return t.segment_bytes;
   return inter_workgroups <= 512 ? (size_t)160 << 20 : (size_t)8 << 30;
-}
-
-static int segment_chunks_override() {
-  const char* e = getenv("KDA_PREFILL_SEGMENT_CHUNKS");
-  const long long v = e ? atoll(e) : 0;
-  return v >= 1 && v <= (1 << 30) ? (int)v : 0;
 }
 
 namespace {
@@ -139,34 +130,6 @@ struct SeqCounts {  // chunk counts of the sequences, on the host
 };
 }  // namespace
 
-SegmentPlan plan_segments(int num_seqs, const int32_t* cu_host, int seq_len, int H, int D,
-                          int chunk, bool in_bf16) {
-  const SeqCounts sc{num_seqs, cu_host, seq_len, chunk};
-  int max_nch = 0;
-  for (int n = 0; n < num_seqs; ++n) max_nch = max_nch > sc.nch(n) ? max_nch : sc.nch(n);
-  SegmentPlan p;
-  if (max_nch == 0) return p;  // one pass of the inter kernel settles the states
-  const size_t per = (size_t)H * prefill_chunk_bytes(D, chunk, in_bf16);
-  // inter-chunk workgroups at 16 value columns each
-  const size_t budget = segment_budget_bytes((long long)num_seqs * H * (D / 16));
-  int lo = max_nch < 16 ? max_nch : 16, hi = max_nch;
-  if (const int fixed = segment_chunks_override()) {
-    lo = fixed < max_nch ? fixed : max_nch;
-  } else if ((size_t)sc.slots(0, lo) * per <= budget) {
-    while (lo < hi) {  // largest L that fits (slots grow with L)
-      const int mid = lo + (hi - lo + 1) / 2;
-      if ((size_t)sc.slots(0, mid) * per <= budget)
-        lo = mid;
-      else
-        hi = mid - 1;
-    }
-  }
-  p.nseg = (max_nch + lo - 1) / lo;
-  p.L = (max_nch + p.nseg - 1) / p.nseg;
-  p.max_slots = sc.slots(0, p.L);
-  return p;
-}
-
 // The slot table exists for varlen input only.
 static size_t table_bytes(int num_seqs, bool varlen) {
   return varlen ? align256(sizeof(int32_t) * (size_t)(num_seqs + 1)) : 0;
@@ -181,12 +144,88 @@ static size_t raw_o_bytes(const SegmentPlan& p, int H, int D, int chunk, bool ep
   return epilogue ? align256((size_t)p.max_slots * H * chunk * D * sizeof(float)) : 0;
 }
 
-size_t prefill_workspace_bytes(int num_seqs, const int32_t* cu_host, int seq_len, int H, int D,
-                               int chunk, bool in_bf16, bool epilogue) {
-  const SegmentPlan p = plan_segments(num_seqs, cu_host, seq_len, H, D, chunk, in_bf16);
-  return table_bytes(num_seqs, cu_host != nullptr) + carry_bytes(p, num_seqs, H, D) +
+static size_t plan_bytes(const SegmentPlan& p, int num_seqs, bool varlen, int H, int D, int chunk,
+                         bool in_bf16, bool epilogue) {
+  return table_bytes(num_seqs, varlen) + carry_bytes(p, num_seqs, H, D) +
          (size_t)p.max_slots * H * prefill_chunk_bytes(D, chunk, in_bf16) +
          raw_o_bytes(p, H, D, chunk, epilogue);
+}
+
+SegmentPlan plan_segments(int num_seqs, const int32_t* cu_host, int seq_len, int H, int D,
+                          int chunk, bool in_bf16, bool epilogue, const PrefillTuning& tuning) {
+  const SeqCounts sc{num_seqs, cu_host, seq_len, chunk};
+  int max_nch = 0;
+  for (int n = 0; n < num_seqs; ++n) max_nch = max_nch > sc.nch(n) ? max_nch : sc.nch(n);
+  SegmentPlan p;
+  if (max_nch == 0) {  // one pass of the inter kernel settles the states
+    if (tuning.workspace_cap &&
+        plan_bytes(p, num_seqs, cu_host != nullptr, H, D, chunk, in_bf16, epilogue) >
+            tuning.workspace_cap)
+      p.nseg = 0;
+    return p;
+  }
+  auto make = [&](int L) {
+    SegmentPlan q;
+    q.nseg = (max_nch + L - 1) / L;
+    q.L = (max_nch + q.nseg - 1) / q.nseg;
+    q.max_slots = (int)sc.slots(0, q.L);
+    return q;
+  };
+  const size_t per = (size_t)H * prefill_chunk_bytes(D, chunk, in_bf16);
+  int lo;
+  if (tuning.segment_chunks >= 1) {
+    lo = tuning.segment_chunks < max_nch ? tuning.segment_chunks : max_nch;
+  } else {
+    // inter-chunk workgroups at 16 value columns each
+    const size_t budget = segment_budget_bytes((long long)num_seqs * H * (D / 16), tuning);
+    lo = max_nch < 16 ? max_nch : 16;
+    int hi = max_nch;
+    if ((size_t)sc.slots(0, lo) * per <= budget) {
+      while (lo < hi) {  // largest L that fits (slots grow with L)
+        const int mid = lo + (hi - lo + 1) / 2;
+        if ((size_t)sc.slots(0, mid) * per <= budget)
+          lo = mid;
+        else
+          hi = mid - 1;
+      }
+    }
+  }
+  p = make(lo);
+  if (tuning.workspace_cap) {
+    auto fits = [&](int L) {
+      return plan_bytes(make(L), num_seqs, cu_host != nullptr, H, D, chunk, in_bf16, epilogue) <=
+             tuning.workspace_cap;
+    };
+    if (!fits(lo)) {
+      // The whole workspace of L = 1..lo grows with L (more slots, and the
+      // carry buffer once there are two segments): take the largest that fits.
+      int a = 1, b = lo;
+      if (!fits(1)) {
+        p.L = 0;
+        p.nseg = 0;
+        p.max_slots = 0;
+        return p;
+      }
+      while (a < b) {
+        const int mid = a + (b - a + 1) / 2;
+        if (fits(mid))
+          a = mid;
+        else
+          b = mid - 1;
+      }
+      p = make(a);
+    }
+  }
+  return p;
+}
+
+size_t prefill_workspace_bytes(int num_seqs, const int32_t* cu_host, int seq_len, int H, int D,
+                               int chunk, bool in_bf16, bool epilogue,
+                               const PrefillTuning& tuning) {
+  const SegmentPlan p =
+      plan_segments(num_seqs, cu_host, seq_len, H, D, chunk, in_bf16, epilogue, tuning);
+  if (p.nseg == 0) return SIZE_MAX;
+  return plan_bytes(p, num_seqs, cu_host != nullptr, H, D, chunk, in_bf16, epilogue);
 }
 
 // ---------------------------------------------------------------------------
@@ -1782,18 +1821,11 @@ __global__ __launch_bounds__(D) void conv_state_kernel(ConvStateArgs ca, SeqInfo
 // Value-column block width of the inter-chunk pass: wide blocks cut the
 // per-chunk operand traffic (each block re-reads the chunk's operands),
 // narrow ones give more workgroups.  32 columns once there are enough
-// (sequence, head) pairs to fill the chip twice over with them.
-// KDA_PREFILL_DVB (16 or 32) overrides it, for tuning.
-static int choose_nct(int pairs, int D) {
-  static int env = -1;
-  if (env < 0) {
-    const char* e = getenv("KDA_PREFILL_DVB");
-    const int v = e ? atoi(e) : 0;
-    env = (v == 16 || v == 32) ? v / 16 : 0;
-  }
-  int nct = env;
-  if (nct == 0) nct = (long long)pairs * (D / 32) >= 512 ? 2 : 1;
-  return nct;
+// (sequence, head) pairs to fill the chip twice over with them, unless the
+// caller's tuning fixes the width.
+static int choose_nct(int pairs, int D, const PrefillTuning& t) {
+  if (t.value_block == 16 || t.value_block == 32) return t.value_block / 16;
+  return (long long)pairs * (D / 32) >= 512 ? 2 : 1;
 }
 
 template <class M, int D, int C, int NCT>
@@ -1816,8 +1848,10 @@ template <class M, int D, int C, bool SDEC>
 static hipError_t launch_prefill_t(const PrefillArgs& a) {
   typedef Layout<M, D, C> LY;
   char* ws = reinterpret_cast<char*>(a.workspace);
-  const SegmentPlan plan =
-      plan_segments(a.num_seqs, a.cu_seqlens_host, a.seq_len, a.H, D, C, a.in_bf16);
+  const bool epi = a.layer.gate != nullptr;
+  const SegmentPlan plan = plan_segments(a.num_seqs, a.cu_seqlens_host, a.seq_len, a.H, D, C,
+                                         a.in_bf16, epi, a.tuning);
+  if (plan.nseg == 0) return hipErrorInvalidValue;  // checked before, on the host
   const SeqCounts sc{a.num_seqs, a.cu_seqlens_host, a.seq_len, C};
   SeqInfo si;
   si.cu = a.cu_seqlens;
@@ -1841,7 +1875,6 @@ static hipError_t launch_prefill_t(const PrefillArgs& a) {
   kp.carry = carry ? reinterpret_cast<float*>(after_table) : nullptr;
   kp.ops = after_table + carry;
   kp.H = a.H;
-  const bool epi = a.layer.gate != nullptr;
   kp.o_slots = epi ? reinterpret_cast<float*>(kp.ops + (size_t)plan.max_slots * a.H * LY::kBytes)
                    : nullptr;
   kp.gate = a.layer.gate;
@@ -1868,7 +1901,7 @@ static hipError_t launch_prefill_t(const PrefillArgs& a) {
     hipError_t e = hipFuncSetAttribute(intra_fn, hipFuncAttributeMaxDynamicSharedMemorySize, (int)lds);
     if (e != hipSuccess) return e;
   }
-  const int nct = choose_nct(a.num_seqs * a.H, D);
+  const int nct = choose_nct(a.num_seqs * a.H, D, a.tuning);
   for (int s = 0; s < plan.nseg; ++s) {
     si.c0 = s * plan.L;
     const long long slots = sc.slots(si.c0, plan.L);

@@ -34,6 +34,28 @@ class LayerParams(ctypes.Structure):
                 ("conv_state_out", ctypes.c_void_p * 3)]
 
 
+class PrefillOptions(ctypes.Structure):
+    """``kda_prefill_options`` of include/kda.h (zero fields: automatic)."""
+    _fields_ = [("segment_chunks", ctypes.c_int), ("segment_bytes", ctypes.c_size_t),
+                ("value_block", ctypes.c_int)]
+
+
+FORM_KDA, FORM_GDN, FORM_LAYER = 0, 1, 2
+
+
+def _options(options) -> Optional[PrefillOptions]:
+    """A dict with any of segment_chunks, segment_bytes, value_block (or
+    None) as the C struct."""
+    if options is None:
+        return None
+    unknown = set(options) - {"segment_chunks", "segment_bytes", "value_block"}
+    if unknown:
+        raise KDAError(f"unknown prefill options {sorted(unknown)}")
+    return PrefillOptions(int(options.get("segment_chunks", 0)),
+                          int(options.get("segment_bytes", 0)),
+                          int(options.get("value_block", 0)))
+
+
 def load() -> ctypes.CDLL:
     """Load libkda.so (built in-tree by gated_delta_rule_56_amd.build)."""
     global _lib
@@ -85,6 +107,13 @@ def load() -> ctypes.CDLL:
     lib.kda_prefill_chunk_fp32.restype = i32
     lib.dplr_decode_step.argtypes = [vp] * 8 + [i32] * 6 + [vp]
     lib.dplr_decode_step.restype = i32
+    op = ctypes.POINTER(PrefillOptions)
+    lib.kda_prefill_workspace_size_ex.argtypes = [i32, i32, i32, i32, i32, i32, i32, vp, i32, i32,
+                                                  vp, op, ctypes.POINTER(sz)]
+    lib.kda_prefill_workspace_size_ex.restype = i32
+    lib.kda_prefill_ex.argtypes = [i32, vp, vp, vp, vp, vp, vp, vp, vp, vp, vp, vp,
+                                   i32, i32, i32, i32, i32, i32, i32, i32, i32, op, vp, sz, vp]
+    lib.kda_prefill_ex.restype = i32
     _lib = lib
     return lib
 
@@ -116,6 +145,45 @@ def _ptr(t) -> Optional[int]:
     return None if t is None else t.data_ptr()
 
 
+def _on_device(dev, named):
+    """Every tensor handed to the C ABI must live on q's GPU: the kernels
+    dereference the raw pointers on that device."""
+    for name, t in named:
+        if t is None:
+            continue
+        if not t.is_cuda or t.device != dev:
+            raise KDAError(f"{name} must be a GPU tensor on the device of q ({dev}), "
+                           f"got {t.device}")
+
+
+def _out_dtype(o, out_dtype):
+    """The dtype written to o: o's own when o is given (out_dtype, if also
+    given, must agree), else out_dtype, else float32.  A given o must be
+    contiguous: the kernels write it densely."""
+    torch = _torch()
+    if o is not None:
+        if out_dtype is not None and out_dtype != o.dtype:
+            raise KDAError(f"o has dtype {o.dtype} but out_dtype is {out_dtype}")
+        if not o.is_contiguous():
+            raise KDAError("o must be contiguous")
+        _dtype_code(o.dtype)
+        return o.dtype
+    return out_dtype or torch.float32
+
+
+def _workspace(ws, nbytes, dev):
+    """A caller's workspace when it is a large enough contiguous byte buffer
+    on the device, else a new one."""
+    torch = _torch()
+    if ws is not None:
+        if ws.dtype != torch.uint8 or not ws.is_contiguous():
+            raise KDAError("workspace must be a contiguous uint8 tensor")
+        _on_device(dev, [("workspace", ws)])
+        if ws.numel() >= nbytes:
+            return ws
+    return torch.empty(max(nbytes, 256), dtype=torch.uint8, device=dev)
+
+
 def _stream_ptr(device) -> int:
     torch = _torch()
     return torch.cuda.current_stream(device).cuda_stream
@@ -129,12 +197,23 @@ def _host_cu(cu_seqlens, cu_seqlens_host) -> np.ndarray:
 
 def workspace_size(B: int, T: int, H: int, D: int, num_seqs: int, chunk_size: int,
                    in_dtype: int, cu_seqlens_host: Optional[np.ndarray] = None,
-                   layer_gate: Optional[bool] = None) -> int:
+                   layer_gate: Optional[bool] = None, options=None, form=None) -> int:
     """Workspace bytes of kda_prefill (``layer_gate`` None) or of
-    kda_prefill_layer with (True) or without (False) the gated epilogue."""
+    kda_prefill_layer with (True) or without (False) the gated epilogue;
+    with ``options`` (see :func:`prefill`) those of kda_prefill_ex."""
     out = ctypes.c_size_t(0)
     cu_p = None if cu_seqlens_host is None else cu_seqlens_host.ctypes.data
-    if layer_gate is None:
+    if options is not None:
+        if form is None:
+            form = FORM_KDA if layer_gate is None else FORM_LAYER
+        lp = LayerParams()
+        lp.gate = 1 << 20 if layer_gate else None  # only its presence is read
+        opts = _options(options)
+        _check(load().kda_prefill_workspace_size_ex(form, B, T, H, D, D, num_seqs, cu_p,
+                                                    chunk_size, in_dtype, ctypes.addressof(lp),
+                                                    ctypes.byref(opts), ctypes.byref(out)),
+               "kda_prefill_workspace_size_ex")
+    elif layer_gate is None:
         _check(load().kda_prefill_workspace_size(B, T, H, D, D, num_seqs, cu_p, chunk_size,
                                                  in_dtype, ctypes.byref(out)),
                "kda_prefill_workspace_size")
@@ -156,7 +235,7 @@ def _expect(name, t, shape):
 def prefill(q, k, v, g, beta, initial_state=None, cu_seqlens=None, *,
             cu_seqlens_host: Optional[Union[Sequence[int], np.ndarray]] = None,
             chunk_size: int = 64, out_dtype=None, output_final_state: bool = True,
-            final_state=None, o=None, workspace=None):
+            final_state=None, o=None, workspace=None, options=None):
     """Chunked KDA forward (``kda_prefill``).
 
     Shapes: q, k, g ``[B, T, H, Dk]``; v ``[B, T, H, Dv]``; beta ``[B, T, H]``.
@@ -165,10 +244,13 @@ def prefill(q, k, v, g, beta, initial_state=None, cu_seqlens=None, *,
     (int32 device tensor ``[N+1]``), B must be 1 and the N packed sequences
     share the T axis.  ``initial_state`` ``[N, H, Dk, Dv]`` float32 or None.
     Returns ``(o, final_state)`` (final_state None unless requested).
-    ``final_state`` may be passed (it may alias initial_state).
+    ``final_state`` may be passed (it may alias initial_state).  A given
+    ``o`` sets the output dtype.  ``options`` (a dict of
+    ``kda_prefill_options`` fields: segment_chunks, segment_bytes,
+    value_block) calls ``kda_prefill_ex`` with them.
     """
     return _prefill(q, k, v, g, beta, initial_state, cu_seqlens, cu_seqlens_host, chunk_size,
-                    out_dtype, output_final_state, final_state, o, workspace, None)
+                    out_dtype, output_final_state, final_state, o, workspace, None, options)
 
 
 def layer_prefill(q_pre, k_pre, v_pre, g, beta_logit, gate=None, norm_weight=None,
@@ -176,7 +258,7 @@ def layer_prefill(q_pre, k_pre, v_pre, g, beta_logit, gate=None, norm_weight=Non
                   conv_weight=None, conv_state=None, conv_state_out=None,
                   cu_seqlens_host: Optional[Union[Sequence[int], np.ndarray]] = None,
                   chunk_size: int = 64, out_dtype=None, output_final_state: bool = True,
-                  final_state=None, o=None, workspace=None):
+                  final_state=None, o=None, workspace=None, options=None):
     """KDA layer forward with the fused prologue and epilogue
     (``kda_prefill_layer``): the short convolution of q, k, v when
     ``conv_weight`` = (w_q, w_k, w_v) ``[H, D, W]`` float32 is given (carried
@@ -191,7 +273,7 @@ def layer_prefill(q_pre, k_pre, v_pre, g, beta_logit, gate=None, norm_weight=Non
     layer = _Layer(gate, norm_weight, norm_eps, conv_weight, conv_state, conv_state_out)
     o, fin = _prefill(q_pre, k_pre, v_pre, g, beta_logit, initial_state, cu_seqlens,
                       cu_seqlens_host, chunk_size, out_dtype, output_final_state, final_state, o,
-                      workspace, layer)
+                      workspace, layer, options)
     return (o, fin) if conv_weight is None else (o, fin, layer.conv_state_out)
 
 
@@ -213,6 +295,7 @@ class _Layer:
             _expect("norm_weight", self.weight, (out_shape[-1],))
             if self.weight.dtype != torch.float32 or not self.weight.is_contiguous():
                 raise KDAError("norm_weight must be contiguous float32")
+            _on_device(q.device, [("gate", self.gate), ("norm_weight", self.weight)])
         if self.conv_weight is None:
             return
         if len(self.conv_weight) != 3:
@@ -234,6 +317,9 @@ class _Layer:
                 _expect(name, t, (N, H, W - 1, D))
                 if t.dtype != q.dtype or not t.is_contiguous():
                     raise KDAError(f"{name} must be contiguous with the dtype of q")
+        _on_device(q.device, [("conv_weight", t) for t in self.conv_weight] +
+                   [("conv_state", t) for t in (self.conv_state or ())] +
+                   [("conv_state_out", t) for t in (self.conv_state_out or ())])
         if self.conv_state_out is None:
             self.conv_state_out = tuple(torch.empty((N, H, W - 1, D), dtype=q.dtype,
                                                     device=q.device) for _ in range(3))
@@ -254,7 +340,7 @@ class _Layer:
 
 
 def _prefill(q, k, v, g, beta, initial_state, cu_seqlens, cu_seqlens_host, chunk_size,
-             out_dtype, output_final_state, final_state, o, workspace, layer):
+             out_dtype, output_final_state, final_state, o, workspace, layer, options=None):
     torch = _torch()
     if q.dim() != 4:
         raise KDAError("q must be [B, T, H, D]")
@@ -277,39 +363,49 @@ def _prefill(q, k, v, g, beta, initial_state, cu_seqlens, cu_seqlens_host, chunk
         if not t.is_contiguous():
             raise KDAError(f"{name} must be contiguous")
     if cu_seqlens is not None:
+        if cu_seqlens.dtype != torch.int32 or not cu_seqlens.is_contiguous():
+            raise KDAError("cu_seqlens must be contiguous int32")
+        _on_device(q.device, [("q", q), ("cu_seqlens", cu_seqlens)])
         cu_h = _host_cu(cu_seqlens, cu_seqlens_host)
         N = len(cu_h) - 1
-        if cu_seqlens.dtype != torch.int32:
-            raise KDAError("cu_seqlens must be int32")
     else:
         cu_h = None
         N = B
-    out_dtype = out_dtype or torch.float32
+    out_dtype = _out_dtype(o, out_dtype)
     out_code = _dtype_code(out_dtype)
+    _expect("o", o, (B, T, H, Dv))
+    if not output_final_state:
+        final_state = None
+    for name, t in (("initial_state", initial_state), ("final_state", final_state)):
+        _expect(name, t, (N, H, D, Dv))
+        if t is not None and (t.dtype != torch.float32 or not t.is_contiguous()):
+            raise KDAError(f"{name} must be contiguous float32")
+    if layer is not None:
+        layer.check(q, (B, T, H, Dv), N, H, D)
+    _on_device(q.device, [("q", q), ("k", k), ("v", v), ("g", g), ("beta", beta), ("o", o),
+                          ("initial_state", initial_state), ("final_state", final_state)])
+    opts = _options(options)
+    gate = None if layer is None else layer.gate is not None
+    ws_bytes = workspace_size(B, T, H, D, N, chunk_size, in_code, cu_h, gate, options,
+                              FORM_LAYER if layer is not None else
+                              FORM_GDN if scalar_g else FORM_KDA)
+    workspace = _workspace(workspace, ws_bytes, q.device)
     if o is None:
         o = torch.empty((B, T, H, Dv), dtype=out_dtype, device=q.device)
     if output_final_state and final_state is None:
         final_state = torch.empty((N, H, D, Dv), dtype=torch.float32, device=q.device)
-    if not output_final_state:
-        final_state = None
-    if initial_state is not None and (initial_state.dtype != torch.float32
-                                      or not initial_state.is_contiguous()):
-        raise KDAError("initial_state must be contiguous float32")
-    _expect("o", o, (B, T, H, Dv))
-    _expect("initial_state", initial_state, (N, H, D, Dv))
-    _expect("final_state", final_state, (N, H, D, Dv))
-    if final_state is not None and (final_state.dtype != torch.float32
-                                    or not final_state.is_contiguous()):
-        raise KDAError("final_state must be contiguous float32")
-    if layer is not None:
-        layer.check(q, (B, T, H, Dv), N, H, D)
-    ws_bytes = workspace_size(B, T, H, D, N, chunk_size, in_code, cu_h,
-                              None if layer is None else layer.gate is not None)
-    if workspace is None or workspace.numel() < ws_bytes:
-        workspace = torch.empty(max(ws_bytes, 1), dtype=torch.uint8, device=q.device)
     cu_hp = None if cu_h is None else cu_h.ctypes.data
+    lp = layer.params() if layer is not None else None
+    if opts is not None:
+        form = FORM_LAYER if layer is not None else FORM_GDN if scalar_g else FORM_KDA
+        _check(load().kda_prefill_ex(
+            form, _ptr(q), _ptr(k), _ptr(v), _ptr(g), _ptr(beta),
+            None if lp is None else ctypes.addressof(lp), _ptr(o), _ptr(initial_state),
+            _ptr(final_state), _ptr(cu_seqlens), cu_hp, B, T, H, D, Dv, N, chunk_size, in_code,
+            out_code, ctypes.byref(opts), _ptr(workspace), workspace.numel(),
+            _stream_ptr(q.device)), "kda_prefill_ex")
+        return o, final_state
     if layer is not None:
-        lp = layer.params()
         _check(load().kda_prefill_layer(
             _ptr(q), _ptr(k), _ptr(v), _ptr(g), _ptr(beta), ctypes.byref(lp),
             _ptr(o), _ptr(initial_state), _ptr(final_state), _ptr(cu_seqlens), cu_hp,
@@ -354,6 +450,8 @@ def layer_decode_step(q_pre, k_pre, v_pre, g, beta_logit, state, gate=None, norm
 
 def _decode(q, k, v, g, beta, state, out_dtype, o, layer):
     torch = _torch()
+    if q.dim() != 3:
+        raise KDAError("q must be [N, H, D]")
     N, H, D = q.shape
     Dv = v.shape[-1]
     scalar_g = g.dim() == 2
@@ -366,17 +464,23 @@ def _decode(q, k, v, g, beta, state, out_dtype, o, layer):
     _expect("state", state, (N, H, D, Dv))
     _expect("o", o, (N, H, Dv))
     in_code = _dtype_code(q.dtype)
-    out_dtype = out_dtype or torch.float32
+    for name, t in (("k", k), ("v", v)):
+        if t.dtype != q.dtype:
+            raise KDAError(f"{name} must have the dtype of q")
+    out_dtype = _out_dtype(o, out_dtype)
     out_code = _dtype_code(out_dtype)
     for name, t in (("q", q), ("k", k), ("v", v), ("g", g), ("beta", beta), ("state", state)):
         if not t.is_contiguous():
             raise KDAError(f"{name} must be contiguous")
     if state.dtype != torch.float32 or g.dtype != torch.float32 or beta.dtype != torch.float32:
         raise KDAError("state, g and beta must be float32")
+    if layer is not None:
+        layer.check(q, (N, H, Dv), N, H, D)
+    _on_device(q.device, [("q", q), ("k", k), ("v", v), ("g", g), ("beta", beta),
+                          ("state", state), ("o", o)])
     if o is None:
         o = torch.empty((N, H, Dv), dtype=out_dtype, device=q.device)
     if layer is not None:
-        layer.check(q, (N, H, Dv), N, H, D)
         lp = layer.params()
         _check(load().kda_decode_step_layer(
             _ptr(q), _ptr(k), _ptr(v), _ptr(g), _ptr(beta), ctypes.byref(lp),
@@ -442,6 +546,12 @@ def backward(q, k, v, g, beta, d_o, initial_state=None, d_final_state=None, cu_s
         _expect(name, t, (N, H, D, Dv))
         if t is not None and (t.dtype != torch.float32 or not t.is_contiguous()):
             raise KDAError(f"{name} must be contiguous float32")
+    if out is not None:
+        for name, t in zip(("dq", "dk", "dv", "dg", "dbeta", "d_initial_state"), out):
+            _on_device(q.device, [(name, t)])
+    _on_device(q.device, [("q", q), ("k", k), ("v", v), ("g", g), ("beta", beta), ("d_o", d_o),
+                          ("initial_state", initial_state), ("d_final_state", d_final_state),
+                          ("cu_seqlens", cu_seqlens)])
     if out is None:
         f32 = dict(dtype=torch.float32, device=q.device)
         out = (torch.empty((B, T, H, D), **f32), torch.empty((B, T, H, D), **f32),
@@ -456,8 +566,7 @@ def backward(q, k, v, g, beta, d_o, initial_state=None, d_final_state=None, cu_s
         if t is not None and (t.dtype != torch.float32 or not t.is_contiguous()):
             raise KDAError(f"{name} must be contiguous float32")
     ws_bytes = backward_workspace_size(B, T, H, D, N, chunk_size, cu_h)
-    if workspace is None or workspace.numel() < ws_bytes:
-        workspace = torch.empty(max(ws_bytes, 256), dtype=torch.uint8, device=q.device)
+    workspace = _workspace(workspace, ws_bytes, q.device)
     cu_hp = None if cu_h is None else cu_h.ctypes.data
     _check(load().kda_backward(
         _ptr(q), _ptr(k), _ptr(v), _ptr(g), _ptr(beta), _ptr(initial_state), _ptr(d_o),
@@ -508,10 +617,6 @@ def _dplr_call(tied, q, k, v, a, b, g, beta, initial_state, cu_seqlens, cu_seqle
     else:
         cu_h = None
         N = B
-    if o is None:
-        o = torch.empty((B, T, H, Dv), dtype=torch.float32, device=q.device)
-    if output_final_state and final_state is None:
-        final_state = torch.empty((N, H, D, Dv), dtype=torch.float32, device=q.device)
     if not output_final_state:
         final_state = None
     for name, t in (("o", o), ("initial_state", initial_state), ("final_state", final_state)):
@@ -520,9 +625,14 @@ def _dplr_call(tied, q, k, v, a, b, g, beta, initial_state, cu_seqlens, cu_seqle
     _expect("o", o, (B, T, H, Dv))
     _expect("initial_state", initial_state, (N, H, D, Dv))
     _expect("final_state", final_state, (N, H, D, Dv))
+    _on_device(q.device, named + f32s + [("o", o), ("initial_state", initial_state),
+                                         ("final_state", final_state), ("cu_seqlens", cu_seqlens)])
     ws_bytes = dplr_workspace_size(B, T, H, D, N, chunk_size, cu_h)
-    if workspace is None or workspace.numel() < ws_bytes:
-        workspace = torch.empty(max(ws_bytes, 256), dtype=torch.uint8, device=q.device)
+    workspace = _workspace(workspace, ws_bytes, q.device)
+    if o is None:
+        o = torch.empty((B, T, H, Dv), dtype=torch.float32, device=q.device)
+    if output_final_state and final_state is None:
+        final_state = torch.empty((N, H, D, Dv), dtype=torch.float32, device=q.device)
     cu_hp = None if cu_h is None else cu_h.ctypes.data
     if tied:
         code = load().kda_prefill_chunk_fp32(
@@ -579,10 +689,12 @@ def dplr_decode_step(q, k, v, a, b, g, state, *, out_dtype=None, o=None):
     for name, t in (("g", g), ("state", state)):
         if t.dtype != torch.float32 or not t.is_contiguous():
             raise KDAError(f"{name} must be contiguous float32")
-    out_dtype = out_dtype or torch.float32
+    _expect("o", o, (N, H, Dv))
+    out_dtype = _out_dtype(o, out_dtype)
+    _on_device(q.device, [("q", q), ("k", k), ("v", v), ("a", a), ("b", b), ("g", g),
+                          ("state", state), ("o", o)])
     if o is None:
         o = torch.empty((N, H, Dv), dtype=out_dtype, device=q.device)
-    _expect("o", o, (N, H, Dv))
     _check(load().dplr_decode_step(
         _ptr(q), _ptr(k), _ptr(v), _ptr(a), _ptr(b), _ptr(g), _ptr(state), _ptr(o),
         N, H, D, Dv, _dtype_code(q.dtype), _dtype_code(out_dtype), _stream_ptr(q.device)),

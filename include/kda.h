@@ -72,11 +72,9 @@ int kda_version(void);
  * at Dk = Dv = 128, C = 64; about 160 MiB per segment when there are few
  * (sequence, head) pairs, up to 8 GiB otherwise) and, when there is more
  * than one segment, the fp32 state carried between them (num_seqs * H * Dk *
- * Dv * 4 bytes).  So the size is bounded for any sequence length.  The
- * environment variables KDA_PREFILL_SEGMENT_KB (operand budget) and
- * KDA_PREFILL_SEGMENT_CHUNKS (segment length) override the choice; a
- * workspace must be sized under the same settings as the kda_prefill call
- * that uses it.
+ * Dv * 4 bytes).  So the size is bounded for any sequence length.  The size
+ * depends only on the arguments: kda_prefill_ex with non-default options
+ * needs kda_prefill_workspace_size_ex with the same options.
  */
 kda_status kda_prefill_workspace_size(int B, int T, int H, int Dk, int Dv,
                                       int num_seqs,
@@ -132,6 +130,59 @@ kda_status kda_prefill(const void* q, const void* k, const void* v,
                        int chunk_size, kda_dtype in_dtype, kda_dtype out_dtype,
                        void* workspace, size_t workspace_bytes,
                        void* stream /* hipStream_t */);
+
+/*
+ * Choices kda_prefill normally makes itself, for callers that tune the
+ * launch or need to exercise a particular configuration.  Every field left
+ * at zero keeps the automatic choice; results are identical for every
+ * setting (they change only how the work is split).
+ *   segment_chunks  local chunks of every sequence per segment (>= 1); each
+ *                   segment is one intra-chunk pass and one carry pass, and
+ *                   the state is carried between segments in the workspace
+ *   segment_bytes   operand budget of one segment in bytes (segment_chunks
+ *                   then follows from it); ignored when segment_chunks is set
+ *   value_block     value columns per workgroup of the carry pass: 16 or 32
+ * Invalid values (negative, value_block not 0/16/32) give
+ * KDA_ERR_INVALID_ARG.
+ */
+typedef struct {
+  int segment_chunks;
+  size_t segment_bytes;
+  int value_block;
+} kda_prefill_options;
+
+/* The three chunked forward forms that share the prefill kernels. */
+typedef enum {
+  KDA_FORM_KDA = 0,   /* kda_prefill */
+  KDA_FORM_GDN = 1,   /* gdn_prefill: g is [B*T, H] */
+  KDA_FORM_LAYER = 2  /* kda_prefill_layer: inputs before their activations */
+} kda_prefill_form;
+
+/*
+ * kda_prefill, gdn_prefill or kda_prefill_layer (selected by `form`) with
+ * explicit options (NULL: automatic, the same as the plain entry points).
+ * `layer` (a kda_layer_params*, declared below) is read for KDA_FORM_LAYER
+ * only, and may be NULL there as in kda_prefill_layer.  The workspace must be
+ * sized by kda_prefill_workspace_size_ex with the same form, layer and
+ * options.  An unknown form gives KDA_ERR_INVALID_ARG.
+ */
+kda_status kda_prefill_workspace_size_ex(int form, int B, int T, int H, int Dk,
+                                         int Dv, int num_seqs,
+                                         const int32_t* cu_seqlens_host,
+                                         int chunk_size, kda_dtype in_dtype,
+                                         const void* layer,
+                                         const kda_prefill_options* options,
+                                         size_t* bytes);
+
+kda_status kda_prefill_ex(int form, const void* q, const void* k, const void* v,
+                          const float* g, const float* beta, const void* layer,
+                          void* o, const float* initial_state,
+                          float* final_state, const int32_t* cu_seqlens,
+                          const int32_t* cu_seqlens_host, int B, int T, int H,
+                          int Dk, int Dv, int num_seqs, int chunk_size,
+                          kda_dtype in_dtype, kda_dtype out_dtype,
+                          const kda_prefill_options* options, void* workspace,
+                          size_t workspace_bytes, void* stream /* hipStream_t */);
 
 /*
  * One recurrent KDA step for N independent sequences (generation).

@@ -96,8 +96,6 @@ def test_workspace_size(lib):
     # (a 160 MiB budget: at most 35 chunks, so 2 equal segments of 32) and the
     # fp32 state carried between segments (32 x 128 x 128 x 4 B); fixed-length
     # input needs no slot table.
-    if "KDA_PREFILL_SEGMENT_KB" in os.environ:
-        pytest.skip("segment budget overridden")
     n = kda.workspace_size(1, 4096, 32, 128, 1, 64, kda.KDA_BF16)
     assert n == 32 * 32 * 147968 + 32 * 128 * 128 * 4
     # one segment: no carry buffer
@@ -114,17 +112,26 @@ def test_workspace_size(lib):
         kda.workspace_size(1, 300, 4, 80, 3, 16, kda.KDA_F32, cu)
 
 
-def test_workspace_segments(monkeypatch):
+def test_workspace_segments(lib):
     # Segments hold at least 16 local chunks: with a 1000 KB budget (less
     # than 16 chunks of one head, 2.37 MB), T=4096 (64 chunks) runs as 4
     # segments of 16, plus the carried state.
-    monkeypatch.setenv("KDA_PREFILL_SEGMENT_KB", "1000")
-    n = kda.workspace_size(1, 4096, 1, 128, 1, 64, kda.KDA_BF16)
+    n = kda.workspace_size(1, 4096, 1, 128, 1, 64, kda.KDA_BF16,
+                           options={"segment_bytes": 1000 << 10})
     assert n == 16 * 147968 + 128 * 128 * 4
     # 4000 KB fits 27 chunks: 3 segments, evened out to 22 chunks each.
-    monkeypatch.setenv("KDA_PREFILL_SEGMENT_KB", "4000")
-    n = kda.workspace_size(1, 4096, 1, 128, 1, 64, kda.KDA_BF16)
+    n = kda.workspace_size(1, 4096, 1, 128, 1, 64, kda.KDA_BF16,
+                           options={"segment_bytes": 4000 << 10})
     assert n == 22 * 147968 + 128 * 128 * 4
+    # A fixed segment length of 5 chunks: 13 segments, evened out to 5.
+    n = kda.workspace_size(1, 4096, 1, 128, 1, 64, kda.KDA_BF16, options={"segment_chunks": 5})
+    assert n == 5 * 147968 + 128 * 128 * 4
+    # Options that only split the work differently leave plain calls alone.
+    assert kda.workspace_size(1, 4096, 1, 128, 1, 64, kda.KDA_BF16, options={}) == \
+        kda.workspace_size(1, 4096, 1, 128, 1, 64, kda.KDA_BF16)
+    assert kda.workspace_size(1, 4096, 1, 128, 1, 64, kda.KDA_BF16,
+                              options={"value_block": 32}) == \
+        kda.workspace_size(1, 4096, 1, 128, 1, 64, kda.KDA_BF16)
 
 
 def test_decode_validation(lib):
@@ -144,8 +151,6 @@ def test_layer_workspace_size(lib):
     # Without the gate the layer call needs exactly the plain workspace; with
     # it, one segment's raw fp32 output as well: 32 slots x 32 heads x 64 x
     # 128 x 4 B at T=4096 (two segments of 32 chunks).
-    if "KDA_PREFILL_SEGMENT_KB" in os.environ or "KDA_PREFILL_SEGMENT_CHUNKS" in os.environ:
-        pytest.skip("segment plan overridden")
     plain = kda.workspace_size(1, 4096, 32, 128, 1, 64, kda.KDA_BF16)
     assert kda.workspace_size(1, 4096, 32, 128, 1, 64, kda.KDA_BF16, layer_gate=False) == plain
     gated = kda.workspace_size(1, 4096, 32, 128, 1, 64, kda.KDA_BF16, layer_gate=True)
@@ -197,3 +202,100 @@ def test_layer_validation(lib):
     assert d(_params(cw=7)) == INVALID
     assert d(_params(), state=None) == INVALID
     assert d(_params(), Dk=32, Dv=32) == UNSUPPORTED
+
+
+def _prefill_ex(lib, form=0, opts=None, layer=None, **kw):
+    a = dict(q=FAKE, k=FAKE, v=FAKE, g=FAKE, beta=FAKE, o=FAKE, s0=None, s1=None,
+             cu=None, cu_host=None, B=1, T=128, H=2, Dk=128, Dv=128, N=1, C=64,
+             ind=0, outd=1, ws=FAKE, wsb=1 << 40, stream=None)
+    a.update(kw)
+    op = None if opts is None else ctypes.byref(opts)
+    lp = None if layer is None else ctypes.addressof(layer)
+    return lib.kda_prefill_ex(form, a["q"], a["k"], a["v"], a["g"], a["beta"], lp, a["o"],
+                              a["s0"], a["s1"], a["cu"], a["cu_host"], a["B"], a["T"], a["H"],
+                              a["Dk"], a["Dv"], a["N"], a["C"], a["ind"], a["outd"], op,
+                              a["ws"], a["wsb"], a["stream"])
+
+
+def test_prefill_ex_validation(lib):
+    P = kda.PrefillOptions
+    assert _prefill_ex(lib, form=3, ws=None) == INVALID                # unknown form
+    assert _prefill_ex(lib, form=-1, ws=None) == INVALID
+    assert _prefill_ex(lib, opts=P(0, 0, 24), ws=None) == INVALID      # value block 16 or 32
+    assert _prefill_ex(lib, opts=P(-1, 0, 0), ws=None) == INVALID      # negative segment length
+    # valid options: the call gets as far as the workspace check
+    for form in (0, 1, 2):
+        assert _prefill_ex(lib, form=form, opts=P(3, 0, 32), ws=None) == WORKSPACE
+        assert _prefill_ex(lib, form=form, ws=None) == WORKSPACE
+    assert _prefill_ex(lib, form=2, layer=_params(w=None), ws=None) == INVALID
+    out = ctypes.c_size_t(0)
+    assert lib.kda_prefill_workspace_size_ex(7, 1, 128, 2, 128, 128, 1, None, 64, 0, None, None,
+                                             ctypes.byref(out)) == INVALID
+    assert lib.kda_prefill_workspace_size_ex(0, 1, 128, 2, 128, 128, 1, None, 64, 0, None,
+                                             ctypes.byref(P(0, 0, 8)),
+                                             ctypes.byref(out)) == INVALID
+
+
+def test_workspace_size_ex_forms(lib):
+    # The GDN form and the layer form without a gate need the plain
+    # workspace; the gated layer form adds one segment's raw output.
+    plain = kda.workspace_size(1, 4096, 32, 128, 1, 64, kda.KDA_BF16)
+    opts = {"segment_chunks": 0}
+    assert kda.workspace_size(1, 4096, 32, 128, 1, 64, kda.KDA_BF16, options=opts,
+                              form=kda.FORM_GDN) == plain
+    assert kda.workspace_size(1, 4096, 32, 128, 1, 64, kda.KDA_BF16, layer_gate=False,
+                              options=opts) == plain
+    assert kda.workspace_size(1, 4096, 32, 128, 1, 64, kda.KDA_BF16, layer_gate=True,
+                              options=opts) == \
+        kda.workspace_size(1, 4096, 32, 128, 1, 64, kda.KDA_BF16, layer_gate=True)
+    with pytest.raises(kda.KDAError):
+        kda.workspace_size(1, 4096, 32, 128, 1, 64, kda.KDA_BF16, options={"chunks": 2})
+
+
+# --- binding misuse: every case raises KDAError before anything is allocated
+# on a GPU or launched (these run without one) ---
+
+def _tok(torch, B=1, T=8, H=2, D=64, dt=None, device="cpu"):
+    dt = dt or torch.bfloat16
+    z = lambda *s, d=dt: torch.zeros(*s, dtype=d, device=device)
+    return (z(B, T, H, D), z(B, T, H, D), z(B, T, H, D), z(B, T, H, D, d=torch.float32),
+            z(B, T, H, d=torch.float32))
+
+
+def test_binding_rejects_host_tensors():
+    torch = pytest.importorskip("torch")
+    q, k, v, g, b = _tok(torch)
+    with pytest.raises(kda.KDAError, match="GPU tensor"):
+        kda.prefill(q, k, v, g, b)
+    with pytest.raises(kda.KDAError, match="GPU tensor"):
+        kda.decode_step(q[0], k[0], v[0], g[0], b[0],
+                        torch.zeros(8, 2, 64, 64, dtype=torch.float32))
+    with pytest.raises(kda.KDAError, match="GPU tensor"):
+        kda.backward(q, k, v, g, b, torch.zeros(1, 8, 2, 64, dtype=torch.float32))
+    with pytest.raises(kda.KDAError, match="GPU tensor"):
+        kda.prefill_chunk_fp32(q, k, v, g, b)
+
+
+def test_binding_output_dtype_and_layout():
+    torch = pytest.importorskip("torch")
+    q, k, v, g, b = _tok(torch)
+    # o's dtype decides what is written; a disagreeing out_dtype is an error
+    o16 = torch.zeros(1, 8, 2, 64, dtype=torch.bfloat16)
+    with pytest.raises(kda.KDAError, match="out_dtype"):
+        kda.prefill(q, k, v, g, b, o=o16, out_dtype=torch.float32)
+    assert kda._out_dtype(o16, None) == torch.bfloat16
+    assert kda._out_dtype(None, None) == torch.float32
+    assert kda._out_dtype(None, torch.bfloat16) == torch.bfloat16
+    # a strided o (a transposed view) is rejected
+    ot = torch.zeros(1, 8, 64, 2, dtype=torch.float32).transpose(2, 3)
+    with pytest.raises(kda.KDAError, match="contiguous"):
+        kda.prefill(q, k, v, g, b, o=ot)
+    st = torch.zeros(8, 2, 64, 64, dtype=torch.float32)
+    with pytest.raises(kda.KDAError, match="out_dtype"):
+        kda.decode_step(q[0], k[0], v[0], g[0], b[0], st, o=o16[0], out_dtype=torch.float32)
+    with pytest.raises(kda.KDAError, match="contiguous"):
+        kda.decode_step(q[0], k[0], v[0], g[0], b[0], st,
+                        o=torch.zeros(8, 64, 2, dtype=torch.float32).transpose(1, 2))
+    # a workspace must be a contiguous byte buffer
+    with pytest.raises(kda.KDAError, match="GPU tensor|workspace"):
+        kda.prefill(q, k, v, g, b, workspace=torch.zeros(16, dtype=torch.float32))

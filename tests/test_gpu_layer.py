@@ -87,12 +87,11 @@ def test_layer_prefill_matches_oracle(kda, dtype, D, C, T, gate):
 
 
 @pytest.mark.parametrize("seg", [None, 1])
-def test_layer_prefill_varlen_segments(kda, monkeypatch, seg):
+def test_layer_prefill_varlen_segments(kda, seg):
     """Packed sequences (one empty) with the gated epilogue, in one pass or in
     segments of one local chunk each (the raw output buffer is reused by
     every segment)."""
-    if seg is not None:
-        monkeypatch.setenv("KDA_PREFILL_SEGMENT_CHUNKS", str(seg))
+    opts = None if seg is None else {"segment_chunks": seg}
     say(f"layer prefill varlen segments={seg}")
     lens = [37, 0, 130, 5, 200, 64]
     cu = np.concatenate([[0], np.cumsum(lens)]).astype(np.int32)
@@ -105,7 +104,7 @@ def test_layer_prefill_varlen_segments(kda, monkeypatch, seg):
     st = torch.from_numpy(s0.copy()).to(DEV)
     cud = torch.from_numpy(cu).to(DEV)
     o, _ = kda.layer_prefill(q, k, v, g, b, gt, tdev(x.norm_weight, torch.float32), EPS, st, cud,
-                             cu_seqlens_host=cu, chunk_size=64, final_state=st)
+                             cu_seqlens_host=cu, chunk_size=64, final_state=st, options=opts)
     torch.cuda.synchronize()
     eo_, es_ = rel(host(o)[0], eo), rel(host(st), ef)
     say(f"  o err {eo_:.2e}  state err {es_:.2e}")
@@ -238,12 +237,11 @@ def test_layer_prefill_conv_matches_oracle(kda, dtype, D, C, T, W, with_state):
 
 
 @pytest.mark.parametrize("seg", [None, 1])
-def test_layer_prefill_conv_varlen_in_place(kda, monkeypatch, seg):
+def test_layer_prefill_conv_varlen_in_place(kda, seg):
     """Packed sequences, some shorter than the convolution's reach (0, 1 and
     2 tokens), carried inputs and recurrent state updated in place, in one
     pass or in one-chunk segments."""
-    if seg is not None:
-        monkeypatch.setenv("KDA_PREFILL_SEGMENT_CHUNKS", str(seg))
+    opts = None if seg is None else {"segment_chunks": seg}
     say(f"layer prefill conv varlen in place segments={seg}")
     lens = [37, 0, 130, 1, 200, 2, 64]
     cu = np.concatenate([[0], np.cumsum(lens)]).astype(np.int32)
@@ -260,7 +258,7 @@ def test_layer_prefill_conv_varlen_in_place(kda, monkeypatch, seg):
     cud = torch.from_numpy(cu).to(DEV)
     o, _, cs = kda.layer_prefill(q, k, v, g, b, gt, tdev(x.norm_weight, torch.float32), EPS, st,
                                  cud, conv_weight=wd, conv_state=sd, conv_state_out=sd,
-                                 cu_seqlens_host=cu, chunk_size=64, final_state=st)
+                                 cu_seqlens_host=cu, chunk_size=64, final_state=st, options=opts)
     torch.cuda.synchronize()
     eo_, es_ = rel(host(o)[0], eo), rel(host(st), ef)
     say(f"  o err {eo_:.2e}  state err {es_:.2e}")

@@ -237,13 +237,12 @@ def test_prefill_varlen(kda, C):
 
 
 @pytest.mark.parametrize("dtype,C,seg", [("bf16", 16, 1), ("f32", 32, 2), ("bf16", 64, 3)])
-def test_prefill_segments(kda, monkeypatch, dtype, C, seg):
+def test_prefill_segments(kda, dtype, C, seg):
     """Short segments (1, 2 or 3 local chunks of every sequence per pass) make
     the prefill run as many intra/inter passes, each sequence's state carried
     between passes: packed sequences of different lengths finish in different
     segments, one is empty, and the final state is written over the initial
     state."""
-    monkeypatch.setenv("KDA_PREFILL_SEGMENT_CHUNKS", str(seg))
     say(f"prefill segments dtype={dtype} C={C} segment={seg} chunks")
     lens = [37, 0, 130, 5, 200, 64]
     cu = np.concatenate([[0], np.cumsum(lens)]).astype(np.int32)
@@ -255,7 +254,8 @@ def test_prefill_segments(kda, monkeypatch, dtype, C, seg):
     q, k, v, g, b = tok_to_dev(x)
     st = torch.from_numpy(s0.copy()).to(DEV)
     cud = torch.from_numpy(cu).to(DEV)
-    o, _ = kda.prefill(q, k, v, g, b, st, cud, cu_seqlens_host=cu, chunk_size=C, final_state=st)
+    o, _ = kda.prefill(q, k, v, g, b, st, cud, cu_seqlens_host=cu, chunk_size=C, final_state=st,
+                       options={"segment_chunks": seg})
     torch.cuda.synchronize()
     eo_, es_ = rel(host(o)[0], eo), rel(host(st), ef)
     say(f"  o err {eo_:.2e}  state err {es_:.2e}")
@@ -263,9 +263,8 @@ def test_prefill_segments(kda, monkeypatch, dtype, C, seg):
     np.testing.assert_array_equal(host(st)[1], s0[1])
 
 
-def test_prefill_fixed_length_segments(kda, monkeypatch):
+def test_prefill_fixed_length_segments(kda):
     """B=3 equal sequences (no cu_seqlens) in segments of 2 chunks, fp32."""
-    monkeypatch.setenv("KDA_PREFILL_SEGMENT_CHUNKS", "2")
     say("prefill fixed-length segments B=3")
     B, T, H = 3, 150, 2
     rng = np.random.default_rng(22)
@@ -274,7 +273,8 @@ def test_prefill_fixed_length_segments(kda, monkeypatch):
     cu = np.arange(B + 1, dtype=np.int32) * T
     eo, ef = oracle.kda_recurrent(x.q, x.k, x.v, x.g, x.beta, s0, cu_seqlens=cu)
     q, k, v, g, b = tok_to_dev(x, B=B)
-    o, fin = kda.prefill(q, k, v, g, b, torch.from_numpy(s0).to(DEV), chunk_size=32)
+    o, fin = kda.prefill(q, k, v, g, b, torch.from_numpy(s0).to(DEV), chunk_size=32,
+                         options={"segment_chunks": 2})
     torch.cuda.synchronize()
     eo_, es_ = rel(host(o).reshape(B * T, H, 64), eo), rel(host(fin), ef)
     say(f"  o err {eo_:.2e}  state err {es_:.2e}")
