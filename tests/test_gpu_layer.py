@@ -51,6 +51,17 @@ def host(t):
     return t.float().cpu().numpy()
 
 
+def pair_rel(x, y, pair_axes):
+    """Worst per-(sequence, head) error: max |x - y| / max |y| over the
+    elements of each pair, then the maximum over pairs."""
+    x = np.asarray(x, dtype=np.float64)
+    y = np.asarray(y, dtype=np.float64)
+    red = tuple(a for a in range(x.ndim) if a not in pair_axes)
+    num = np.abs(x - y).max(axis=red)
+    den = np.maximum(np.abs(y).max(axis=red), 1e-30)
+    return float((num / den).max())
+
+
 def layer_to_dev(x: I.LayerInputs, lead=(1,)):
     dt = torch.bfloat16 if x.dtype == "bf16" else torch.float32
     shp = lambda a: a.reshape(lead + a.shape[1:]) if len(lead) > 1 else a[None]
@@ -128,20 +139,90 @@ def test_layer_prefill_strong_decay(kda):
     assert eo_ <= TOL["f32"] and es_ <= TOL["f32"]
 
 
-def test_layer_prefill_bf16_output(kda):
-    """bf16 output is the fp32 output rounded once."""
-    say("layer prefill bf16 output")
-    rng = np.random.default_rng(34)
-    T, H, D = 100, 2, 128
+@pytest.mark.parametrize("conv", [False, True])
+def test_layer_prefill_bf16_output(kda, conv):
+    """bf16 output against the oracle: one bf16 rounding of y can reach
+    2^-9 of its magnitude, so the gate is 8e-3 (ungated mode)."""
+    say(f"layer prefill bf16 output conv={conv}")
+    rng = np.random.default_rng([34, int(conv)])
+    T, H, D, W = 100, 2, 128, 4
     x = I.draw_layer_tokens(rng, T, H, D, D, "bf16")
     q, k, v, g, b, gt = layer_to_dev(x)
     w = tdev(x.norm_weight, torch.float32)
-    o32, _ = kda.layer_prefill(q, k, v, g, b, gt, w, EPS, chunk_size=64)
-    o16, _ = kda.layer_prefill(q, k, v, g, b, gt, w, EPS, chunk_size=64,
-                               out_dtype=torch.bfloat16)
+    if conv:
+        ws, ss = I.draw_conv(rng, 1, H, D, W, "bf16")
+        eo, _, _ = oracle.kda_layer_conv(x.q_pre, x.k_pre, x.v_pre, x.g, x.beta_logit, ws, ss,
+                                         x.gate, x.norm_weight, EPS)
+        wd, sd = conv_to_dev(ws, ss, torch.bfloat16)
+        o16, _, _ = kda.layer_prefill(q, k, v, g, b, gt, w, EPS, conv_weight=wd, conv_state=sd,
+                                      chunk_size=64, out_dtype=torch.bfloat16)
+    else:
+        eo, _ = oracle_layer(x)
+        o16, _ = kda.layer_prefill(q, k, v, g, b, gt, w, EPS, chunk_size=64,
+                                   out_dtype=torch.bfloat16)
     torch.cuda.synchronize()
     assert o16.dtype == torch.bfloat16
-    assert rel(host(o16), host(o32)) <= 8e-3
+    e = rel(host(o16)[0], eo)
+    say(f"  o err {e:.2e}")
+    assert e <= 8e-3
+
+
+def test_layer_prefill_full_size(kda):
+    """The fused layer at B=1, H=32, T=4096, d=128, bf16, chunk 64, with the
+    width-4 convolution from carried inputs, an initial state and the gated
+    RMSNorm: every output, the final state and the carried inputs against the
+    oracle, per tensor and per head."""
+    say("layer prefill full size T=4096 H=32")
+    rng = np.random.default_rng(40)
+    T, H, D, W = 4096, 32, 128, 4
+    x = I.draw_layer_tokens(rng, T, H, D, D, "bf16")
+    s0 = I.draw_states(rng, 1, H, D, D)
+    ws, ss = I.draw_conv(rng, 1, H, D, W, "bf16")
+    eo, ef, ecs = oracle.kda_layer_conv(x.q_pre, x.k_pre, x.v_pre, x.g, x.beta_logit, ws, ss,
+                                        x.gate, x.norm_weight, EPS, s0)
+    q, k, v, g, b, gt = layer_to_dev(x)
+    wd, sd = conv_to_dev(ws, ss, torch.bfloat16)
+    o, fin, cs = kda.layer_prefill(q, k, v, g, b, gt, tdev(x.norm_weight, torch.float32), EPS,
+                                   torch.from_numpy(s0).to(DEV), conv_weight=wd, conv_state=sd,
+                                   chunk_size=64)
+    torch.cuda.synchronize()
+    o, fin = host(o)[0], host(fin)
+    eo_, es_ = rel(o, eo), rel(fin, ef)
+    po, ps = pair_rel(o, eo, (1,)), pair_rel(fin, ef, (0, 1))
+    say(f"  o err {eo_:.2e} (per head {po:.2e})  state err {es_:.2e} (per head {ps:.2e})")
+    assert eo_ <= TOL["bf16"] and es_ <= TOL["bf16"]
+    assert po <= TOL["bf16"] and ps <= TOL["bf16"]
+    for a, e in zip(cs, ecs):
+        np.testing.assert_array_equal(host(a), e.astype(np.float32))
+
+
+@pytest.mark.parametrize("dtype,D,C", [(dt, D, C) for dt in ("bf16", "f32") for D in (64, 128)
+                                       for C in (16, 32, 64)])
+def test_layer_prefill_value_block_32(kda, dtype, D, C):
+    """The layer path (raw output through the workspace, then the epilogue)
+    with 32 value columns per carry-pass workgroup, for every (dtype, head
+    size, chunk): packed sequences with a convolution and carried inputs."""
+    say(f"layer prefill value_block=32 dtype={dtype} D={D} C={C}")
+    lens = [2 * C + 3, 0, C, 5]
+    cu = np.concatenate([[0], np.cumsum(lens)]).astype(np.int32)
+    N, H, W = len(lens), 2, 4
+    rng = np.random.default_rng([41, D, C])
+    x = I.draw_layer_tokens(rng, int(cu[-1]), H, D, D, dtype)
+    s0 = I.draw_states(rng, N, H, D, D)
+    ws, ss = I.draw_conv(rng, N, H, D, W, dtype)
+    eo, ef, _ = oracle.kda_layer_conv(x.q_pre, x.k_pre, x.v_pre, x.g, x.beta_logit, ws, ss,
+                                      x.gate, x.norm_weight, EPS, s0, cu)
+    dt = torch.bfloat16 if dtype == "bf16" else torch.float32
+    q, k, v, g, b, gt = layer_to_dev(x)
+    wd, sd = conv_to_dev(ws, ss, dt)
+    o, fin, _ = kda.layer_prefill(q, k, v, g, b, gt, tdev(x.norm_weight, torch.float32), EPS,
+                                  torch.from_numpy(s0).to(DEV), torch.from_numpy(cu).to(DEV),
+                                  conv_weight=wd, conv_state=sd, cu_seqlens_host=cu,
+                                  chunk_size=C, options={"value_block": 32})
+    torch.cuda.synchronize()
+    eo_, es_ = rel(host(o)[0], eo), rel(host(fin), ef)
+    say(f"  o err {eo_:.2e}  state err {es_:.2e}")
+    assert eo_ <= TOL[dtype] and es_ <= TOL[dtype]
 
 
 @pytest.mark.parametrize("dtype,D,gate", [("bf16", 128, True), ("f32", 64, True),

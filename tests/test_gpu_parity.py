@@ -53,6 +53,29 @@ def rel(x, y):
     return float(np.abs(x - y).max() / max(np.abs(y).max(), 1e-30))
 
 
+def pair_rel(x, y, pair_axes):
+    """Worst per-(sequence, head) error: max |x - y| / max |y| taken over the
+    elements of each pair (the axes not in ``pair_axes``), then the maximum
+    over pairs.  A pair whose outputs are small cannot hide behind a larger
+    one, as it can in the per-tensor figure."""
+    x = np.asarray(x, dtype=np.float64)
+    y = np.asarray(y, dtype=np.float64)
+    red = tuple(a for a in range(x.ndim) if a not in pair_axes)
+    num = np.abs(x - y).max(axis=red)
+    den = np.maximum(np.abs(y).max(axis=red), 1e-30)
+    return float((num / den).max())
+
+
+def varlen_pair_rel(o, eo, cu):
+    """Worst per-(sequence, head) error of packed outputs [tokens, H, D]."""
+    worst = 0.0
+    for n in range(len(cu) - 1):
+        a, b = int(cu[n]), int(cu[n + 1])
+        if b > a:
+            worst = max(worst, pair_rel(o[a:b], eo[a:b], (1,)))
+    return worst
+
+
 def host(t):
     return t.float().cpu().numpy()
 
@@ -109,33 +132,71 @@ def test_decode_bf16_output(kda):
     assert rel(host(o), eo) <= 8e-3   # one bf16 rounding of o
 
 
-def test_decode_workload4_sampled(kda):
-    """256 sequences x 32 heads, d=128, bf16; 100 steps; sampled (n, h) pairs
-    replayed by the oracle at steps 1, 10, 100 and the state after 100."""
+@pytest.mark.slow
+def test_decode_workload4_full(kda):
+    """256 sequences x 32 heads, d=128, bf16, state [256, 32, 128, 128] ~
+    N(0, 0.1): all 1000 steps on the GPU.  The oracle replays every (sequence,
+    head) pair over the same 1000 tokens; o is compared at steps 1, 10, 100
+    and 1000 and the whole state after step 1000, per tensor and per pair."""
+    from concurrent.futures import ThreadPoolExecutor
     w = I.WORKLOADS[4]
-    say("decode workload 4 (100 steps, sampled pairs)")
-    N, H, D = w.decode_N, w.H, w.Dk
+    N, H, D, steps = w.decode_N, w.H, w.Dk, w.decode_steps
+    checks = (1, 10, 100, 1000)
+    say(f"decode workload 4: {steps} steps, N={N}, H={H}")
     s0 = I.draw_states(np.random.default_rng([4, 2]), N, H, D, D)
-    pairs = [(0, 0), (17, 5), (128, 31), (255, 12), (99, 20)]
     state = torch.from_numpy(s0).to(DEV)
-    sam_s = {p: s0[p][None, None].astype(np.float64) for p in pairs}
-    worst = 0.0
-    for step in range(100):
-        x = I.decode_step_inputs(w, step)
-        q, k, v, g, b = (a[0] for a in tok_to_dev(x))
-        o = kda.decode_step(q, k, v, g, b, state)
-        if step + 1 in (1, 10, 100):
-            oh = host(o)
-        for (n, h) in pairs:
-            eo, sam_s[(n, h)] = oracle.kda_recurrent(
-                x.q[n:n + 1, h:h + 1], x.k[n:n + 1, h:h + 1], x.v[n:n + 1, h:h + 1],
-                x.g[n:n + 1, h:h + 1], x.beta[n:n + 1, h:h + 1], sam_s[(n, h)])
-            if step + 1 in (1, 10, 100):
-                worst = max(worst, rel(oh[n, h], eo[0, 0]))
+    # host copies of every step's inputs for the oracle, [step, N, H, D]
+    hq = np.empty((steps, N, H, D), np.float32)
+    hk, hv, hg = np.empty_like(hq), np.empty_like(hq), np.empty_like(hq)
+    hb = np.empty((steps, N, H), np.float32)
+    o_chk = {}
+    with ThreadPoolExecutor(8) as ex:
+        futs = [ex.submit(I.decode_step_inputs, w, s) for s in range(min(16, steps))]
+        for step in range(steps):
+            x = futs[step].result()
+            futs[step] = None
+            if step + 16 < steps:
+                futs.append(ex.submit(I.decode_step_inputs, w, step + 16))
+            hq[step], hk[step], hv[step], hg[step], hb[step] = x.q, x.k, x.v, x.g, x.beta
+            q, k, v, g, b = (a[0] for a in tok_to_dev(x))
+            o = kda.decode_step(q, k, v, g, b, state)
+            if step + 1 in checks:
+                o_chk[step + 1] = host(o)
+            if (step + 1) % 200 == 0:
+                say(f"  step {step + 1}/{steps}")
+    torch.cuda.synchronize()
     st = host(state)
-    es = max(rel(st[n, h], sam_s[(n, h)][0, 0]) for (n, h) in pairs)
-    say(f"  o err {worst:.2e}  state err {es:.2e}")
-    assert worst <= TOL["bf16"] and es <= TOL["bf16"]
+    say("  oracle over every pair, 16 sequences at a time")
+    cu = np.arange(17, dtype=np.int64) * steps
+    worst_o_pair = worst_s_pair = 0.0
+    seq_major = lambda a, n0: np.ascontiguousarray(
+        a[:, n0:n0 + 16].swapaxes(0, 1).reshape((16 * steps,) + a.shape[2:]))
+    max_o = {c: 0.0 for c in checks}
+    err_o = {c: 0.0 for c in checks}
+    max_s = err_s = 0.0
+    for n0 in range(0, N, 16):
+        eo, ef = oracle.kda_recurrent(seq_major(hq, n0), seq_major(hk, n0), seq_major(hv, n0),
+                                      seq_major(hg, n0), seq_major(hb, n0), s0[n0:n0 + 16],
+                                      cu_seqlens=cu)
+        eo = eo.reshape(16, steps, H, D)
+        for c in checks:
+            x, y = o_chk[c][n0:n0 + 16], eo[:, c - 1]
+            err_o[c] = max(err_o[c], float(np.abs(x - y).max()))
+            max_o[c] = max(max_o[c], float(np.abs(y).max()))
+            worst_o_pair = max(worst_o_pair, pair_rel(x, y, (0, 1)))
+        x = st[n0:n0 + 16]
+        err_s = max(err_s, float(np.abs(x - ef).max()))
+        max_s = max(max_s, float(np.abs(ef).max()))
+        worst_s_pair = max(worst_s_pair, pair_rel(x, ef, (0, 1)))
+        if n0 % 64 == 0:
+            say(f"  oracle sequences {n0}..{n0 + 15}")
+    worst_o = max(err_o[c] / max_o[c] for c in checks)
+    worst_s = err_s / max_s
+    say("  o err " + " ".join(f"step{c} {err_o[c] / max_o[c]:.2e}" for c in checks) +
+        f"  per pair {worst_o_pair:.2e}")
+    say(f"  state err {worst_s:.2e}  per pair {worst_s_pair:.2e}")
+    assert worst_o <= TOL["bf16"] and worst_s <= TOL["bf16"]
+    assert worst_o_pair <= TOL["bf16"] and worst_s_pair <= TOL["bf16"]
 
 
 # --------------------------------------------------------------------------
@@ -175,20 +236,52 @@ def test_prefill_ragged_with_state(kda, dtype, D, C, T):
 @pytest.mark.parametrize("dtype", ["bf16", "f32"])
 @pytest.mark.parametrize("D", [64, 128])
 @pytest.mark.parametrize("C", [16, 32, 64])
-def test_prefill_every_variant_multichunk(kda, dtype, D, C):
+@pytest.mark.parametrize("vb", [16, 32])
+def test_prefill_every_variant_multichunk(kda, dtype, D, C, vb):
     """Every built (dtype, head size, chunk) variant over several chunks with a
-    ragged tail and an initial state: exercises the inter-chunk pipeline
-    (operands fetched one and two chunks ahead) for each instantiation."""
+    ragged tail and an initial state, with 16 and with 32 value columns per
+    carry-pass workgroup: exercises the inter-chunk pipeline (operands
+    fetched one and two chunks ahead) for each instantiation."""
     T = 3 * C + 5
-    say(f"prefill variant dtype={dtype} D={D} C={C} T={T}")
+    say(f"prefill variant dtype={dtype} D={D} C={C} T={T} value_block={vb}")
     rng = np.random.default_rng([19, D, C])
     x = I.draw_tokens(rng, T, 2, D, D, dtype)
     s0 = I.draw_states(rng, 1, 2, D, D)
     eo, ef = oracle.kda_recurrent(x.q, x.k, x.v, x.g, x.beta, s0)
-    o, fin = run_prefill(kda, x, C, s0=s0)
+    q, k, v, g, b = tok_to_dev(x)
+    o, fin = kda.prefill(q, k, v, g, b, torch.from_numpy(s0).to(DEV), chunk_size=C,
+                         options={"value_block": vb})
+    torch.cuda.synchronize()
+    o, fin = host(o)[0], host(fin)
     eo_, es_ = rel(o, eo), rel(fin, ef)
     say(f"  o err {eo_:.2e}  state err {es_:.2e}")
     assert eo_ <= TOL[dtype] and es_ <= TOL[dtype]
+
+
+@pytest.mark.parametrize("dtype,D,C", [(dt, D, C) for dt in ("bf16", "f32") for D in (64, 128)
+                                       for C in (16, 32, 64)])
+def test_prefill_many_pairs_automatic_block(kda, dtype, D, C):
+    """Enough (sequence, head) pairs (80 packed sequences x 4 heads) for the
+    automatic choice to take 32 value columns per carry-pass workgroup, for
+    every (dtype, head size, chunk): ragged lengths, an empty sequence,
+    initial states; per-(sequence, head) errors reported and gated."""
+    rng = np.random.default_rng([25, D, C])
+    lens = rng.integers(0, 3 * C + 9, 80)
+    lens[7] = 0
+    cu = np.concatenate([[0], np.cumsum(lens)]).astype(np.int32)
+    H = 4
+    assert len(lens) * H * (D // 32) >= 512
+    say(f"prefill many pairs dtype={dtype} D={D} C={C} tokens={int(cu[-1])}")
+    x = I.draw_tokens(rng, int(cu[-1]), H, D, D, dtype)
+    s0 = I.draw_states(rng, len(lens), H, D, D)
+    eo, ef = oracle.kda_recurrent(x.q, x.k, x.v, x.g, x.beta, s0, cu_seqlens=cu)
+    o, fin = run_prefill(kda, x, C, s0=s0, cu=cu)
+    eo_, es_ = rel(o, eo), rel(fin, ef)
+    po, ps = varlen_pair_rel(o, eo, cu), pair_rel(fin, ef, (0, 1))
+    say(f"  o err {eo_:.2e} (per pair {po:.2e})  state err {es_:.2e} (per pair {ps:.2e})")
+    assert eo_ <= TOL[dtype] and es_ <= TOL[dtype]
+    assert po <= TOL[dtype] and ps <= TOL[dtype]
+    np.testing.assert_array_equal(fin[7], s0[7])
 
 
 @pytest.mark.parametrize("dtype", ["bf16", "f32"])
@@ -293,24 +386,33 @@ def test_prefill_workload1_full(kda):
     assert eo_ <= TOL["bf16"] and es_ <= TOL["bf16"]
 
 
-def test_prefill_workload2_sampled_heads(kda):
+def test_prefill_workload2_all_heads(kda):
     """16 packed sequences (68,645 tokens), H=32, initial states N(0, 0.1):
-    the GPU runs everything; the oracle checks heads 0, 13 and 31."""
-    say("prefill workload 2 (sampled heads)")
+    every output and final state against the oracle, per tensor and per
+    (sequence, head)."""
+    say("prefill workload 2 (all heads)")
     w = I.WORKLOADS[2]
     cu = I.cu_seqlens_from_lengths(I.varlen_lengths(w))
     x = I.workload_tokens(w)
     s0 = I.workload_states(w, w.num_seqs)
     o, fin = run_prefill(kda, x, 64, s0=s0, cu=cu)
-    worst_o = worst_s = 0.0
-    for h in (0, 13, 31):
-        sl = slice(h, h + 1)
-        eo, ef = oracle.kda_recurrent(x.q[:, sl], x.k[:, sl], x.v[:, sl], x.g[:, sl],
-                                      x.beta[:, sl], s0[:, sl], cu_seqlens=cu)
-        worst_o = max(worst_o, rel(o[:, sl], eo))
-        worst_s = max(worst_s, rel(fin[:, sl], ef))
-    say(f"  o err {worst_o:.2e}  state err {worst_s:.2e}")
-    assert worst_o <= TOL["bf16"] and worst_s <= TOL["bf16"]
+    eo, ef = oracle.kda_recurrent(x.q, x.k, x.v, x.g, x.beta, s0, cu_seqlens=cu)
+    eo_, es_ = rel(o, eo), rel(fin, ef)
+    po, ps = varlen_pair_rel(o, eo, cu), pair_rel(fin, ef, (0, 1))
+    say(f"  o err {eo_:.2e} (per pair {po:.2e})  state err {es_:.2e} (per pair {ps:.2e})")
+    assert eo_ <= TOL["bf16"] and es_ <= TOL["bf16"]
+    assert po <= TOL["bf16"] and ps <= TOL["bf16"]
+
+
+def test_prefill_workload1_per_pair(kda):
+    """The T=4096, H=32 workload with a final state: the worst head."""
+    say("prefill workload 1 per head")
+    x = I.workload_tokens(I.WORKLOADS[1])
+    eo, ef = oracle.kda_recurrent(x.q, x.k, x.v, x.g, x.beta)
+    o, fin = run_prefill(kda, x, 64)
+    po, ps = pair_rel(o, eo, (1,)), pair_rel(fin, ef, (0, 1))
+    say(f"  per head: o {po:.2e}  state {ps:.2e}")
+    assert po <= TOL["bf16"] and ps <= TOL["bf16"]
 
 
 def test_prefill_bf16_output(kda):
@@ -396,10 +498,12 @@ def _scalar_gate(x, rng):
 
 
 @pytest.mark.parametrize("dtype,C", [("bf16", 64), ("f32", 16), ("bf16", 32)])
-def test_gdn_prefill_matches_oracle(kda, dtype, C):
+@pytest.mark.parametrize("vb", [16, 32])
+def test_gdn_prefill_matches_oracle(kda, dtype, C, vb):
     """gdn_prefill (g [T, H]) equals the recurrence with g broadcast over the
-    key channels: varlen packing, initial states, a ragged tail."""
-    say(f"gdn prefill dtype={dtype} C={C}")
+    key channels: varlen packing, initial states, a ragged tail; 16 and 32
+    value columns per carry-pass workgroup."""
+    say(f"gdn prefill dtype={dtype} C={C} value_block={vb}")
     lens = [3 * C + 7, 0, 50, 2 * C]
     cu = np.concatenate([[0], np.cumsum(lens)]).astype(np.int32)
     rng = np.random.default_rng([23, C])
@@ -412,7 +516,7 @@ def test_gdn_prefill_matches_oracle(kda, dtype, C):
     g = torch.from_numpy(gs).to(DEV)[None]
     cud = torch.from_numpy(cu).to(DEV)
     o, fin = kda.prefill(q, k, v, g, b, torch.from_numpy(s0).to(DEV), cud, cu_seqlens_host=cu,
-                         chunk_size=C)
+                         chunk_size=C, options={"value_block": vb})
     torch.cuda.synchronize()
     eo_, es_ = rel(host(o)[0], eo), rel(host(fin), ef)
     say(f"  o err {eo_:.2e}  state err {es_:.2e}")
