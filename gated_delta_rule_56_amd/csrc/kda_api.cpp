@@ -7,6 +7,8 @@
 #include <math.h>
 #include <stdint.h>
 
+#include <mutex>
+
 #include "kda_launch.hpp"
 
 namespace {
@@ -103,6 +105,31 @@ kda_status workspace_size(int B, int T, int H, int Dk, int Dv, int num_seqs,
   *bytes = kda::prefill_workspace_bytes(num_seqs, cu_seqlens_host, cu_seqlens_host ? 0 : T, H, Dk,
                                         chunk_size, in_dtype == KDA_BF16, epilogue, tuning);
   return KDA_OK;
+}
+
+// Static scratch of kda_prefill_noalloc: the prefill's workspace for callers
+// that cannot allocate.  Each GPU the library runs on holds its own copy of
+// this array until the process ends.  Host code never passes the array's
+// name to a kernel (on the host it is only a stand-in); it uses the device
+// address that hipGetSymbolAddress returns, looked up once per device.
+constexpr size_t kScratchBytes = KDA_PREFILL_NOALLOC_SCRATCH_BYTES;
+static __device__ __align__(256) char scratch[kScratchBytes];
+
+constexpr int kMaxDevices = 64;
+std::mutex scratch_mu;
+void* scratch_ptr[kMaxDevices] = {};
+
+// The current device's address of `scratch`, or nullptr on a HIP error.
+void* scratch_address() {
+  int dev = -1;
+  if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= kMaxDevices) return nullptr;
+  std::lock_guard<std::mutex> lock(scratch_mu);
+  if (!scratch_ptr[dev]) {
+    void* p = nullptr;
+    if (hipGetSymbolAddress(&p, HIP_SYMBOL(scratch)) != hipSuccess || !p) return nullptr;
+    scratch_ptr[dev] = p;
+  }
+  return scratch_ptr[dev];
 }
 
 }  // namespace
@@ -231,6 +258,41 @@ kda_status kda_prefill(const void* q, const void* k, const void* v, const float*
   return prefill_impl(false, kda::Layer(), q, k, v, g, beta, o, initial_state, final_state,
                       cu_seqlens, cu_seqlens_host, B, T, H, Dk, Dv, num_seqs, chunk_size,
                       in_dtype, out_dtype, kda::PrefillTuning(), workspace, workspace_bytes, stream);
+}
+
+kda_status kda_prefill_noalloc(const void* q, const void* k, const void* v, const float* g,
+                               const float* beta, void* o, const float* initial_state,
+                               float* final_state, const int32_t* cu_seqlens,
+                               const int32_t* cu_seqlens_host, int B, int T, int H, int Dk,
+                               int Dv, int num_seqs, int chunk_size, kda_dtype in_dtype,
+                               kda_dtype out_dtype, void* stream) {
+  // The segment plan is the longest whose whole workspace fits the scratch
+  // array; prefill_impl returns KDA_ERR_WORKSPACE when even one-chunk
+  // segments do not fit.  Every argument is checked before the scratch
+  // address is looked up.
+  kda::PrefillTuning t;
+  t.workspace_cap = kScratchBytes;
+  if (H < 1 || !valid_dtype(in_dtype) || !valid_dtype(out_dtype)) return KDA_ERR_INVALID_ARG;
+  if (!supported_head(Dk, Dv) || !supported_chunk(chunk_size)) return KDA_ERR_UNSUPPORTED;
+  int64_t chunks = 0;
+  const kda_status st = seq_layout(B, T, num_seqs, cu_seqlens, cu_seqlens_host, chunk_size, &chunks);
+  if (st != KDA_OK) return st;
+  const size_t need = kda::prefill_workspace_bytes(num_seqs, cu_seqlens_host, cu_seqlens ? 0 : T,
+                                                   H, Dk, chunk_size, in_dtype == KDA_BF16, false,
+                                                   t);
+  if (need == SIZE_MAX) return KDA_ERR_WORKSPACE;
+  const void* ptrs[] = {q, k, v, g, beta, o, initial_state, final_state, cu_seqlens};
+  for (const void* p : ptrs)
+    if (p && !aligned(p, 16)) return KDA_ERR_INVALID_ARG;
+  if ((int64_t)B * T > 0 && (!q || !k || !v || !g || !beta || !o)) return KDA_ERR_INVALID_ARG;
+  void* ws = nullptr;
+  if (need > 0) {
+    ws = scratch_address();
+    if (!ws) return KDA_ERR_HIP;
+  }
+  return prefill_impl(false, kda::Layer(), q, k, v, g, beta, o, initial_state, final_state,
+                      cu_seqlens, cu_seqlens_host, B, T, H, Dk, Dv, num_seqs, chunk_size,
+                      in_dtype, out_dtype, t, ws, kScratchBytes, stream);
 }
 
 kda_status gdn_prefill(const void* q, const void* k, const void* v, const float* g,

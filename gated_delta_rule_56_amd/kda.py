@@ -64,6 +64,10 @@ def load() -> ctypes.CDLL:
     if not os.path.exists(LIB_PATH):
         raise KDAError(f"{LIB_PATH} is missing: build it with "
                        "`python -m gated_delta_rule_56_amd.build` first")
+    # torch's HIP runtime and the one libkda.so links share a soname, so the
+    # first loaded serves the whole process.  Load torch's first: the device
+    # pointers and streams handed to the library come from it.
+    _torch()
     lib = ctypes.CDLL(LIB_PATH)
     vp, i32, sz = ctypes.c_void_p, ctypes.c_int, ctypes.c_size_t
     lib.kda_status_string.argtypes = [i32]
@@ -114,6 +118,8 @@ def load() -> ctypes.CDLL:
     lib.kda_prefill_ex.argtypes = [i32, vp, vp, vp, vp, vp, vp, vp, vp, vp, vp, vp,
                                    i32, i32, i32, i32, i32, i32, i32, i32, i32, op, vp, sz, vp]
     lib.kda_prefill_ex.restype = i32
+    lib.kda_prefill_noalloc.argtypes = [vp] * 10 + [i32] * 9 + [vp]
+    lib.kda_prefill_noalloc.restype = i32
     _lib = lib
     return lib
 
@@ -251,6 +257,59 @@ def prefill(q, k, v, g, beta, initial_state=None, cu_seqlens=None, *,
     """
     return _prefill(q, k, v, g, beta, initial_state, cu_seqlens, cu_seqlens_host, chunk_size,
                     out_dtype, output_final_state, final_state, o, workspace, None, options)
+
+
+def prefill_noalloc(q, k, v, g, beta, o, initial_state=None, final_state=None, cu_seqlens=None,
+                    *, cu_seqlens_host=None, chunk_size: int = 64):
+    """``kda_prefill_noalloc``: :func:`prefill` without a workspace, for
+    callers that cannot allocate.  The caller passes every output (``o``,
+    and ``final_state`` or None); with ``cu_seqlens`` the host copy
+    ``cu_seqlens_host`` is required too.  Nothing is allocated here or in the
+    library (its intermediates live in a static device array), and calls that
+    overlap on one GPU race.  Returns ``(o, final_state)``."""
+    torch = _torch()
+    if q.dim() != 4:
+        raise KDAError("q must be [B, T, H, D]")
+    B, T, H, D = q.shape
+    Dv = v.shape[-1]
+    _expect("k", k, (B, T, H, D))
+    _expect("v", v, (B, T, H, Dv))
+    _expect("g", g, (B, T, H, D))
+    _expect("beta", beta, (B, T, H))
+    _expect("o", o, (B, T, H, Dv))
+    in_code = _dtype_code(q.dtype)
+    for name, t in (("k", k), ("v", v)):
+        if t.dtype != q.dtype:
+            raise KDAError(f"{name} must have the dtype of q")
+    if g.dtype != torch.float32 or beta.dtype != torch.float32:
+        raise KDAError("g and beta must be float32")
+    for name, t in (("q", q), ("k", k), ("v", v), ("g", g), ("beta", beta)):
+        if not t.is_contiguous():
+            raise KDAError(f"{name} must be contiguous")
+    out_code = _dtype_code(_out_dtype(o, None))
+    if cu_seqlens is not None:
+        if cu_seqlens_host is None:
+            raise KDAError("cu_seqlens_host is required with cu_seqlens")
+        if cu_seqlens.dtype != torch.int32 or not cu_seqlens.is_contiguous():
+            raise KDAError("cu_seqlens must be contiguous int32")
+        cu_h = np.ascontiguousarray(np.asarray(cu_seqlens_host), dtype=np.int32)
+        N = len(cu_h) - 1
+    else:
+        cu_h = None
+        N = B
+    for name, t in (("initial_state", initial_state), ("final_state", final_state)):
+        _expect(name, t, (N, H, D, Dv))
+        if t is not None and (t.dtype != torch.float32 or not t.is_contiguous()):
+            raise KDAError(f"{name} must be contiguous float32")
+    _on_device(q.device, [("q", q), ("k", k), ("v", v), ("g", g), ("beta", beta), ("o", o),
+                          ("initial_state", initial_state), ("final_state", final_state),
+                          ("cu_seqlens", cu_seqlens)])
+    cu_hp = None if cu_h is None else cu_h.ctypes.data
+    _check(load().kda_prefill_noalloc(
+        _ptr(q), _ptr(k), _ptr(v), _ptr(g), _ptr(beta), _ptr(o), _ptr(initial_state),
+        _ptr(final_state), _ptr(cu_seqlens), cu_hp, B, T, H, D, Dv, N, chunk_size, in_code,
+        out_code, _stream_ptr(q.device)), "kda_prefill_noalloc")
+    return o, final_state
 
 
 def layer_prefill(q_pre, k_pre, v_pre, g, beta_logit, gate=None, norm_weight=None,

@@ -132,6 +132,38 @@ kda_status kda_prefill(const void* q, const void* k, const void* v,
                        void* stream /* hipStream_t */);
 
 /*
+ * kda_prefill for callers that cannot allocate device memory: code under HIP
+ * graph capture, serving loops that forbid allocation, and harnesses that
+ * forbid hipMalloc.  Same arguments and results as kda_prefill, without the
+ * workspace: the intermediate data lives in a static device array of
+ * KDA_PREFILL_NOALLOC_SCRATCH_BYTES (128 MiB) that each GPU the library runs
+ * on holds until the process ends.  The call allocates and frees nothing.
+ *
+ * The prefill runs in segments whose whole workspace fits that array (the
+ * segments are shorter than kda_prefill's when the problem is large, so the
+ * call may take longer; results are the same).  A problem that does not fit
+ * even with one-chunk segments -- the fp32 state carried between segments,
+ * num_seqs * H * Dk * Dv * 4 bytes, plus one chunk of every sequence's
+ * operands -- returns KDA_ERR_WORKSPACE before anything is enqueued.
+ *
+ * Every call on one GPU uses that GPU's one array: calls that overlap in time
+ * on one GPU (other streams, other host threads) race and corrupt each
+ * other's results.  Serialise them.  Nothing in the array needs clearing
+ * between calls.
+ */
+#define KDA_PREFILL_NOALLOC_SCRATCH_BYTES ((size_t)128 << 20)
+
+kda_status kda_prefill_noalloc(const void* q, const void* k, const void* v,
+                               const float* g, const float* beta, void* o,
+                               const float* initial_state, float* final_state,
+                               const int32_t* cu_seqlens,
+                               const int32_t* cu_seqlens_host, int B, int T,
+                               int H, int Dk, int Dv, int num_seqs,
+                               int chunk_size, kda_dtype in_dtype,
+                               kda_dtype out_dtype,
+                               void* stream /* hipStream_t */);
+
+/*
  * Choices kda_prefill normally makes itself, for callers that tune the
  * launch or need to exercise a particular configuration.  Every field left
  * at zero keeps the automatic choice; results are identical for every
