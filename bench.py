@@ -139,6 +139,27 @@ def other_workloads(torch, kda, I, dev):
                                              / BF16_PEAK_TFLOPS, 4)}
     del q, k, v, g, b, o, ws, fin
     torch.cuda.empty_cache()
+    # mixed decay: the T=4096, H=32 workload with half the key channels of
+    # every head at alpha near 0.1 per token (and near 0.01, where the
+    # diagonal Gram blocks of those tiles are evaluated pair by pair), timed
+    # beside the workload itself
+    mixed = {}
+    for alpha in (0.1, 0.01):
+        rng = np.random.default_rng([5, int(round(-np.log10(alpha)))])
+        x = I.draw_mixed_decay_tokens(rng, P_T, P_H, P_D, P_D, "bf16", alpha=alpha)
+        bf = lambda a: torch.from_numpy(a).to(torch.bfloat16).to(dev)[None]
+        f32 = lambda a: torch.from_numpy(np.ascontiguousarray(a)).to(dev)[None]
+        args = (bf(x.q), bf(x.k), bf(x.v), f32(x.g), f32(x.beta), None)
+        t = time_prefill(torch, kda, args, 10, chunk_size=P_C)
+        mixed[f"alpha_{alpha}_us_per_call"] = round(t * 1e6, 2)
+    x = I.workload_tokens(I.WORKLOADS[1])
+    args = (bf(x.q), bf(x.k), bf(x.v), f32(x.g), f32(x.beta), None)
+    t0 = time_prefill(torch, kda, args, 10, chunk_size=P_C)
+    mixed["workload_us_per_call"] = round(t0 * 1e6, 2)
+    for alpha in (0.1, 0.01):
+        mixed[f"alpha_{alpha}_over_workload"] = round(mixed[f"alpha_{alpha}_us_per_call"] / 1e6 / t0, 3)
+    out["mixed_decay"] = {"workload": "kda_prefill B=1 H=32 T=4096 d=128 chunk 64 bf16, half of the "
+                                      "key channels at alpha near 0.1 (or 0.01) per token", **mixed}
     # long context: one sequence of 1,048,576 tokens
     w = I.WORKLOADS[3]
     q, k, v, g, b = I.device_tokens(torch, w.T, w.H, w.Dk, w.Dv, 3003, dev)

@@ -31,12 +31,19 @@
 //                      the serial loop over the sequence's chunks, with the
 //                      state block held in MFMA accumulator registers.
 //
-// Decay factorisation.  The Grams need exp(Gamma_r - Gamma_i).  When the
-// total decay inside a chunk is moderate (max over channels of -Gamma_n <=
-// kSpanLimit), the kernel factors it as exp(Gamma_r) * exp(-Gamma_i) and runs
-// both Grams on MFMA; every factor then stays well inside the fp32/bf16
-// exponent range.  Otherwise the Grams are evaluated pair by pair with the
-// exact exponent of the difference (slow, but only strong decay reaches it).
+// Decay factorisation (secondary chunking; greeksharifa.github.io summary,
+// section 3.2 "Efficiency Analysis").  The Grams need exp(Gamma_r -
+// Gamma_i) for i <= r.  The chunk is cut into 16-row tiles; for rows r of
+// tile a and columns i of tile b <= a the factor is split as
+//   exp(Gamma_r - Gamma_s) * exp(Gamma_s - Gamma_e) * exp(Gamma_e - Gamma_i)
+// with s the row before tile a and e the last row of tile b: the row operand
+// (tile-local decay of row r), a per-channel factor of the block, and the
+// column operand (decay from row i to the end of its tile).  Off the
+// diagonal (b < a, so s >= e) all three are <= 1: a factor that underflows
+// belongs to a term below exp(-87).  On the diagonal the middle factor is
+// exp(span of tile a) >= 1; a tile whose span on some channel exceeds
+// kTileSpanLimit has its diagonal block evaluated pair by pair with the
+// exact exponent of each difference instead.  Every block runs on MFMA.
 #include "kda_device.hpp"
 #include "kda_launch.hpp"
 
@@ -44,7 +51,7 @@
 
 namespace kda {
 
-constexpr float kSpanLimit = 40.f;
+constexpr float kTileSpanLimit = 64.f;  // largest tile span on the diagonal's product path
 constexpr int kIntraThreads = 512;
 
 // ---------------------------------------------------------------------------
@@ -336,8 +343,8 @@ __device__ __forceinline__ f32x4 chain_mma(ModeF32, const char* p, f32x4 y, f32x
 
 // ---------------------------------------------------------------------------
 // LDS plan of the intra-chunk kernel: two regions that the phases reuse,
-//   R0: K-bar^T staging (precise [D x KC])  ->  K/gam fragments (precise, in
-//       fragment order; on the strong-decay path Gamma fp32 [C x (D+1)])
+//   R0: K-bar^T staging (precise [D x KC])  ->  the Gram column operands
+//       (precise, in fragment order)
 //       ->  the solve's operands: inverses of the diagonal blocks of I + A
 //       (fp32 [NRT][16][17]) and the chain operands (the blocks A_am below
 //       the diagonal, then the inverses)
@@ -358,29 +365,26 @@ struct IntraLds {
   static constexpr int NOFF = NRT * (NRT - 1) / 2;  // blocks below the diagonal
   static constexpr int SK = KC + kPad;  // row stride of [D x KC] staging
   static constexpr int SF = KC + 1;     // row stride of fp32 [C x KC] matrices
-  static constexpr int SG = D + 1;      // row stride of the fp32 Gamma array
   static constexpr size_t kStPlain = ((size_t)D * SK * sizeof(plain_t) + 15) / 16 * 16;
   static constexpr size_t kStPrecise = M::kSplit ? 2 * kStPlain : kStPlain;
   static constexpr size_t kKhFrags = (size_t)NRT * (D / 32) * M::kPFragBytes;
-  static constexpr size_t kGamma = ((size_t)C * SG * 4 + 15) / 16 * 16;
   static constexpr size_t kFMat = ((size_t)C * SF * 4 + 15) / 16 * 16;
   static constexpr size_t kXD = ((size_t)NRT * 16 * 17 * 4 + 15) / 16 * 16;
   static constexpr size_t kSolve = kXD + (size_t)(NOFF + NRT) * 1024;
-  static constexpr size_t kR0 = cmax(cmax(kStPrecise, kKhFrags), cmax(kGamma, kSolve));
+  static constexpr size_t kR0 = cmax(cmax(kStPrecise, kKhFrags), kSolve);
   static constexpr size_t kR1 = cmax(2 * kFMat, kStPrecise);
   static constexpr size_t oR0 = 0, oR1 = kR0;
   static constexpr size_t oTot = kR0 + kR1;              // fp32 [NRT][D]
   static constexpr size_t oBeta = oTot + (size_t)NRT * D * 4;
   static constexpr size_t oNrm = oBeta + (size_t)KC * 4;      // fp32 [8 waves][16][2]
-  static constexpr size_t oRn = oNrm + 8 * 16 * 2 * 4;         // fp32 [C][2]
-  static constexpr size_t kTotal = oRn + (size_t)C * 2 * 4;
+  static constexpr size_t kTotal = oNrm + 8 * 16 * 2 * 4;
   // With the convolution: v's weights, [D][kMaxConv] fp32, taps from the
   // current row back (q's and k's sit in R0 while the prologue runs).
   static constexpr size_t oCWv = kTotal;
   static constexpr size_t kTotalConv = oCWv + (size_t)D * kMaxConv * 4;
   // offsets inside the regions
   static constexpr size_t oKbS = oR0;                    // staging
-  static constexpr size_t oKh = oR0, oG = oR0;           // Gram operands / Gamma
+  static constexpr size_t oKh = oR0;                      // Gram column operands
   static constexpr size_t oA = oR1, oP = oR1 + kFMat;    // Grams
   static constexpr size_t oXD = oR0, oCF = oR0 + kXD;    // solve
   static constexpr size_t oKtT = oR1;                    // W
@@ -454,6 +458,16 @@ struct LdsPrecise<ModeF32> {
     for (int e = 0; e < 4; ++e) x[e] = t[e];
   }
 };
+
+// The eight values of a lane's precise fragment.
+__device__ __forceinline__ void pfrag_values(const ModeBF16::PFrag& f, float* x) {
+#pragma unroll
+  for (int e = 0; e < 8; ++e) x[e] = bf2f(f.hi[e]) + bf2f(f.lo[e]);
+}
+__device__ __forceinline__ void pfrag_values(const ModeF32::PFrag& f, float* x) {
+#pragma unroll
+  for (int e = 0; e < 8; ++e) x[e] = f.v[e];
+}
 
 // Write eight consecutive-k fp32 values of one lane into a global fragment.
 // `lane` is the lane that owns (row, k-group) in the fragment.
@@ -743,7 +757,7 @@ __global__ __launch_bounds__(kIntraThreads, 4) void intra_chunk_kernel(KernelPtr
   typedef IntraLds<M, D, C> L;
   typedef typename L::plain_t plain_t;
   constexpr int NRT = LY::NRT, KC = LY::KC, NKC = LY::NKC, NKD = LY::NKD, NDT = LY::NDT;
-  constexpr int SK = L::SK, SF = L::SF, SG = L::SG;
+  constexpr int SK = L::SK, SF = L::SF;
   constexpr int NW = kIntraThreads / 64;
   constexpr int NFRAG = NRT * NKD;            // fragments of a [C x D] matrix
   constexpr int FPW = (NFRAG + NW - 1) / NW;  // fragments per wave
@@ -934,77 +948,127 @@ __global__ __launch_bounds__(kIntraThreads, 4) void intra_chunk_kernel(KernelPtr
     }
     iq = 1.f / fmaxf(sqrtf(sq), kL2Floor);
     ik = 1.f / fmaxf(sqrtf(sk), kL2Floor);
-    // per-token factors for the strong-decay path, which re-reads q and k
-    float* rn = reinterpret_cast<float*>(smem + L::oRn);
-    if (w < NRT && lg == 0) {
-      rn[r * 2] = iq;
-      rn[r * 2 + 1] = ik;
-    }
   }
-  float Gn[FPW][8];
+  // G stays the decay accumulated within the row tile (from the row before
+  // it).  The full cumulative decay adds the totals of the earlier tiles,
+  // read per fragment from `tot` where they are used.
+  // Per-channel sums of tile totals for the lane's eight channels of
+  // fragment j: tiles [t0, t1).
+  auto tot_sum = [&](int j, int t0, int t1, float* out) {
 #pragma unroll
-  for (int j = 0; j < FPW; ++j)
-#pragma unroll
-    for (int e = 0; e < 8; ++e) Gn[j][e] = 0.f;
-#pragma unroll
-  for (int t = 0; t < NRT; ++t) {
-#pragma unroll
-    for (int j = 0; j < FPW; ++j) {
+    for (int e = 0; e < 8; ++e) out[e] = 0.f;
+    for (int t = t0; t < t1; ++t) {
       const f32x4 a = *reinterpret_cast<const f32x4*>(tot + t * D + 32 * fkb[j] + 8 * lg);
       const f32x4 b = *reinterpret_cast<const f32x4*>(tot + t * D + 32 * fkb[j] + 8 * lg + 4);
-      const float m = t < rt ? 1.f : 0.f;
 #pragma unroll
       for (int e = 0; e < 4; ++e) {
-        G[j][e] += m * a[e];
-        G[j][4 + e] += m * b[e];
-        Gn[j][e] += a[e];
-        Gn[j][4 + e] += b[e];
+        out[e] += a[e];
+        out[4 + e] += b[e];
       }
     }
-  }
-  // Span check over all channels (every wave reaches the same verdict).
+  };
+  // Span check of this wave's row tile over all channels.
   bool big = false;
-  for (int c = l; c < D; c += 64) {
-    float s = 0.f;
-#pragma unroll
-    for (int t = 0; t < NRT; ++t) s += tot[t * D + c];
-    big |= s < -kSpanLimit;
-  }
-  const bool fast = !__any(big);
+  for (int c = l; c < D; c += 64) big |= tot[rt * D + c] < -kTileSpanLimit;
+  const bool bad_tile = __any(big);
+  // inputs after the prologue
+  auto kin = [&](int j, int e) { return rv ? (PRO ? kact(j, e) * ik : kraw[j].get(e)) : 0.f; };
+  auto qin = [&](int j, int e) { return rv ? (PRO ? qact(j, e) * iq : qraw[j].get(e)) : 0.f; };
 
-  // ---- step 3: decayed operands.  Q*gam leaves as whole fragments; K*gam
-  // and K/gam stay in registers; K-bar^T is staged transposed ----
-  PFrag qtf[FPW], ktf[FPW], khf[FPW];
-  LdsPrecise<M> KbS(smem + L::oKbS, L::kStPlain);
+  // The diagonal block of a tile whose span is too large for the product
+  // path, pair by pair with the exact exponent, in the accumulator layout of
+  // the products (lane (lr, lg), element x: row R = 4 lg + x, column I =
+  // lr).  A lane of lane group g holds row lr's values on channel set g, so
+  // for every target lane group t it forms the partial sum of pair
+  // (R = 4 t + x, I = lr) over set g, fetching row R from lane R + 16 g; the
+  // four sets' partials for each target are then summed across the lane
+  // groups, and the lane of group t keeps its own.  The result merges with
+  // the other waves' channel parts as the products do.
+  f32x4 accAd = {0, 0, 0, 0}, accPd = {0, 0, 0, 0};
+  if (bad_tile) {
+    float kvv[FPW][8], qvv[FPW][8];
 #pragma unroll
-  for (int j = 0; j < FPW; ++j) {
-    float qt[8], kt[8], kh[8];
+    for (int j = 0; j < FPW; ++j)
 #pragma unroll
-    for (int e = 0; e < 8; ++e) {
-      const float kv = rv ? (PRO ? kact(j, e) * ik : kraw[j].get(e)) : 0.f;
-      const float qv = rv ? (PRO ? qact(j, e) * iq : qraw[j].get(e)) : 0.f;
-      const float gm = __expf(G[j][e]);
-      qt[e] = qv * gm;
-      kt[e] = kv * gm;
-      kh[e] = fast ? kv * __expf(-G[j][e]) : 0.f;
-      const int c = 32 * fkb[j] + 8 * lg + e;
-      if (fv[j]) {
-        KbS.store(c * SK + r, kv * __expf(Gn[j][e] - G[j][e]));
+      for (int e = 0; e < 8; ++e) {
+        kvv[j][e] = fv[j] ? kin(j, e) : 0.f;
+        qvv[j][e] = fv[j] ? qin(j, e) : 0.f;
       }
+#pragma unroll 1
+    for (int x = 0; x < 4; ++x) {
+      float pa[4], pp[4];
+#pragma unroll
+      for (int t = 0; t < 4; ++t) {
+        const int R = 4 * t + x;
+        const int src = R + 16 * lg;
+        float sa = 0.f, sp = 0.f;
+#pragma unroll
+        for (int j = 0; j < FPW; ++j)
+#pragma unroll
+          for (int e = 0; e < 8; ++e) {
+            const float kR = __shfl(kvv[j][e], src), qR = __shfl(qvv[j][e], src);
+            const float gR = __shfl(G[j][e], src);
+            const float ex = lr <= R ? __expf(gR - G[j][e]) : 0.f;  // exp(Gamma_R - Gamma_I), I <= R
+            sa += kR * kvv[j][e] * ex;
+            sp += qR * kvv[j][e] * ex;
+          }
+        sa += __shfl_xor(sa, 16);
+        sp += __shfl_xor(sp, 16);
+        sa += __shfl_xor(sa, 32);
+        sp += __shfl_xor(sp, 32);
+        pa[t] = sa;
+        pp[t] = sp;
+      }
+      const float va = lg == 0 ? pa[0] : lg == 1 ? pa[1] : lg == 2 ? pa[2] : pa[3];
+      const float vp = lg == 0 ? pp[0] : lg == 1 ? pp[1] : lg == 2 ? pp[2] : pp[3];
+      if (x == 0) { accAd[0] = va; accPd[0] = vp; }
+      else if (x == 1) { accAd[1] = va; accPd[1] = vp; }
+      else if (x == 2) { accAd[2] = va; accPd[2] = vp; }
+      else { accAd[3] = va; accPd[3] = vp; }
     }
-    qtf[j] = make_pfrag(M{}, qt);
-    ktf[j] = make_pfrag(M{}, kt);
-    khf[j] = make_pfrag(M{}, kh);
-    if (fv[j]) st_pfrag(M{}, blk + LY::kQt + (size_t)(rt * NKD + fkb[j]) * LY::PF, qtf[j]);
+  }
+
+  // ---- step 3: decayed operands.  Q*gam leaves as whole fragments;
+  // K-bar^T is staged transposed; the Gram operands stay in registers: rows
+  // q and k times their tile-local decay exp(G), and the column operand
+  // k exp(tot_rt - G), the decay from the row to the end of its tile ----
+  PFrag qrf[FPW], krf[FPW], khf[FPW];
+  LdsPrecise<M> KbS(smem + L::oKbS, L::kStPlain);
+  {
+    // tile references: rows x exp(G), columns k exp(tot_rt - G)
+#pragma unroll
+    for (int j = 0; j < FPW; ++j) {
+      float qt[8], qr[8], kr[8], kh[8], gsa[8], trt[8], gn[8];
+      tot_sum(j, 0, rt, gsa);
+      tot_sum(j, rt, rt + 1, trt);
+      tot_sum(j, 0, NRT, gn);
+#pragma unroll
+      for (int e = 0; e < 8; ++e) {
+        const float kv = kin(j, e), qv = qin(j, e);
+        const float gf = G[j][e] + gsa[e];  // cumulative decay of the row
+        const float ew = __expf(G[j][e]);
+        qt[e] = qv * __expf(gf);
+        qr[e] = qv * ew;
+        kr[e] = kv * ew;
+        kh[e] = kv * __expf(trt[e] - G[j][e]);
+        if (fv[j]) KbS.store((32 * fkb[j] + 8 * lg + e) * SK + r, kv * __expf(gn[e] - gf));
+      }
+      qrf[j] = make_pfrag(M{}, qr);
+      krf[j] = make_pfrag(M{}, kr);
+      khf[j] = make_pfrag(M{}, kh);
+      if (fv[j]) st_pfrag(M{}, blk + LY::kQt + (size_t)(rt * NKD + fkb[j]) * LY::PF, make_pfrag(M{}, qt));
+    }
   }
   if (any_frag && rt == 0 && lr == 0) {
     // gam_n: channels 32 kb + 8 lg .. + 7 of each fragment of row tile 0
 #pragma unroll
     for (int j = 0; j < FPW; ++j)
       if (fv[j]) {
+        float gn[8];
+        tot_sum(j, 0, NRT, gn);
 #pragma unroll
         for (int e = 0; e < 8; ++e)
-          reinterpret_cast<float*>(blk + LY::kGam)[32 * fkb[j] + 8 * lg + e] = __expf(Gn[j][e]);
+          reinterpret_cast<float*>(blk + LY::kGam)[32 * fkb[j] + 8 * lg + e] = __expf(gn[e]);
       }
   }
   if (KC > C) {  // zero the padded tokens
@@ -1027,85 +1091,50 @@ __global__ __launch_bounds__(kIntraThreads, 4) void intra_chunk_kernel(KernelPtr
   float* Ps = reinterpret_cast<float*>(smem + L::oP);
   for (int idx = 4 * tid; idx < 2 * (int)(L::kFMat / 4); idx += 4 * kIntraThreads)
     *reinterpret_cast<f32x4*>(As + idx) = f32x4{0, 0, 0, 0};  // A and P are adjacent
-  if (fast) {
 #pragma unroll
-    for (int j = 0; j < FPW; ++j)
-      if (fv[j]) lds_st_pfrag(M{}, smem + L::oKh + (size_t)(rt * NKD + fkb[j]) * LY::PF, khf[j]);
-  } else {
-    float* Gs = reinterpret_cast<float*>(smem + L::oG);
-#pragma unroll
-    for (int j = 0; j < FPW; ++j)
-      if (fv[j]) {
-#pragma unroll
-        for (int e = 0; e < 8; ++e) Gs[r * SG + 32 * fkb[j] + 8 * lg + e] = G[j][e];
-      }
-  }
-  __syncthreads();  // B4: K/gam fragments (or Gamma), zeroed A and P
+  for (int j = 0; j < FPW; ++j)
+    if (fv[j]) lds_st_pfrag(M{}, smem + L::oKh + (size_t)(rt * NKD + fkb[j]) * LY::PF, khf[j]);
+  __syncthreads();  // B4: column operands staged, zeroed A and P
   // Partial Grams over this wave's channel blocks for every tile b <= rt.
+  // Column tile b's operand is multiplied, per channel, by the block's
+  // factor exp(Gamma_s - Gamma_e): 1 for b = rt - 1, exp(sum of the totals of
+  // tiles b+1 .. rt-1) (<= 1) below that, exp(-tot_rt) on the diagonal.
   // The NC waves that share a row tile add their parts into A and P in turn,
   // one barrier apart (LDS float atomics are far slower).
   constexpr int NC = (NFRAG < NW ? NFRAG : NW) / NRT;
   f32x4 accA[NRT], accP[NRT];
 #pragma unroll
   for (int b = 0; b < NRT; ++b) { accA[b] = f32x4{0, 0, 0, 0}; accP[b] = accA[b]; }
-  if (fast) {
-    if (any_frag) {
+  if (any_frag) {
 #pragma unroll
-      for (int b = 0; b < NRT; ++b) {
-        if (b > rt) break;
-#pragma unroll
-        for (int j = 0; j < FPW; ++j) {
-          if (!fv[j]) continue;
-          const PFrag kbf = ld_pfrag(M{}, smem + L::oKh + (size_t)(b * NKD + fkb[j]) * LY::PF);
-          accP[b] = mma_pp(qtf[j], kbf, accP[b]);
-          accA[b] = mma_pp(ktf[j], kbf, accA[b]);
-        }
+    for (int b = 0; b < NRT; ++b) {
+      if (b > rt) break;
+      if (b == rt && bad_tile) {
+        accA[b] = accAd;
+        accP[b] = accPd;
+        continue;
       }
-    }
-  } else {
-    // Strong decay: exact pairwise evaluation.  Thread tid owns row
-    // rr = tid / 8 and columns i = tid % 8, +8, ... <= rr.
-    const float* Gs = reinterpret_cast<const float*>(smem + L::oG);
-    const in_t* qg = reinterpret_cast<const in_t*>(kp.q);
-    const in_t* kg = reinterpret_cast<const in_t*>(kp.k);
-    const float* rn = reinterpret_cast<const float*>(smem + L::oRn);
-    // token t of the chunk, channel c of q (x = 0) or k (x = 1), after the
-    // prologue scaled by the token's norm factor f
-    auto in = [&](const in_t* p, int x, int t, int c, float f) {
-      float y = 0.f;
-      if constexpr (PRO == 2) {
-        const int W = kp.conv_w;
-        const float* wr = kp.cw[x] + ((size_t)h * D + c) * W;
-        for (int i = 0; i < W; ++i) {
-          const int s = t0 + t - (W - 1) + i;
-          float xv = 0.f;
-          if (s >= it.bos) {
-            xv = (float)p[((size_t)s * H + h) * D + c];
-          } else if (kp.cs[x] && (W - 1) + (s - it.bos) >= 0) {
-            xv = (float)reinterpret_cast<const in_t*>(kp.cs[x])
-                     [(((size_t)it.n * H + h) * (W - 1) + (W - 1) + (s - it.bos)) * D + c];
+#pragma unroll
+      for (int j = 0; j < FPW; ++j) {
+        if (!fv[j]) continue;
+        PFrag kbf = ld_pfrag(M{}, smem + L::oKh + (size_t)(b * NKD + fkb[j]) * LY::PF);
+        if (b != rt - 1) {
+          float ex[8];
+          if (b == rt) {
+            tot_sum(j, rt, rt + 1, ex);
+#pragma unroll
+            for (int e = 0; e < 8; ++e) ex[e] = -ex[e];
+          } else {
+            tot_sum(j, b + 1, rt, ex);
           }
-          y += wr[i] * xv;
+          float x[8];
+          pfrag_values(kbf, x);
+#pragma unroll
+          for (int e = 0; e < 8; ++e) x[e] *= __expf(ex[e]);
+          kbf = make_pfrag(M{}, x);
         }
-      } else {
-        y = (float)p[((size_t)(t0 + t) * H + h) * D + c];
-      }
-      return PRO ? swishf(y) * f : y;
-    };
-    const int rr = tid >> 3;
-    if (rr < len) {
-      for (int i = tid & 7; i <= rr; i += 8) {
-        float sa = 0.f, sp = 0.f;
-        for (int c = 0; c < D; ++c) {
-          const float kr = in(kg, 1, rr, c, rn[rr * 2 + 1]);
-          const float ki = in(kg, 1, i, c, rn[i * 2 + 1]);
-          const float qr = in(qg, 0, rr, c, rn[rr * 2]);
-          const float ex = __expf(Gs[rr * SG + c] - Gs[i * SG + c]);
-          sa += kr * ki * ex;
-          sp += qr * ki * ex;
-        }
-        if (i < rr) As[rr * SF + i] = beta_s[rr] * sa;
-        Ps[rr * SF + i] = sp;
+        accP[b] = mma_pp(qrf[j], kbf, accP[b]);
+        accA[b] = mma_pp(krf[j], kbf, accA[b]);
       }
     }
   }
@@ -1115,7 +1144,7 @@ __global__ __launch_bounds__(kIntraThreads, 4) void intra_chunk_kernel(KernelPtr
   const int cix = w / NRT;  // this wave's turn among those sharing the row tile
 #pragma unroll
   for (int c = 0; c < NC; ++c) {
-    if (fast && any_frag && cix == c) {
+    if (any_frag && cix == c) {
       // all reads of earlier contributions first, then the writes
       float po[NRT][4], ao[NRT][4];
 #pragma unroll
@@ -1224,12 +1253,17 @@ __global__ __launch_bounds__(kIntraThreads, 4) void intra_chunk_kernel(KernelPtr
     for (int e = 0; e < 4; ++e) x[e] = XD[(16 * w + lr) * 17 + 4 * lg + e];
     cfrag_store(M{}, CF + (size_t)(NOFF + w) * 1024, x);
   }
+  // K*gam = (k exp(G)) exp(Gsa): the row operand times the decay of the
+  // earlier tiles (both factors <= 1, so an underflow is a true zero).
   LdsPrecise<M> KtT(smem + L::oKtT, L::kStPlain);
 #pragma unroll
   for (int j = 0; j < FPW; ++j)
     if (fv[j]) {
+      float x[8], gs[8];
+      pfrag_values(krf[j], x);
+      tot_sum(j, 0, rt, gs);
 #pragma unroll
-      for (int e = 0; e < 8; ++e) KtT.put((32 * fkb[j] + 8 * lg + e) * SK + r, ktf[j], e);
+      for (int e = 0; e < 8; ++e) KtT.store((32 * fkb[j] + 8 * lg + e) * SK + r, x[e] * __expf(gs[e]));
     }
   if (KC > C) {
     for (int idx = tid; idx < D * (KC - C); idx += kIntraThreads) {

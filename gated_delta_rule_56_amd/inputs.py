@@ -113,6 +113,23 @@ def draw_tokens(rng: np.random.Generator, T: int, H: int, Dk: int, Dv: int,
     return TokenInputs(q, k, v, g.astype(np.float32), beta.astype(np.float32), dtype)
 
 
+def draw_mixed_decay_tokens(rng: np.random.Generator, T: int, H: int, Dk: int, Dv: int,
+                            dtype: str = "bf16", alpha: float = 0.1,
+                            frac: float = 0.5) -> TokenInputs:
+    """Tokens as :func:`draw_tokens`, but on the last ``frac`` of the key
+    channels of every head the decay is fast: g = log(alpha) (1 + 0.1 N(0, 1)),
+    clipped to <= 0, i.e. alpha near ``alpha`` per token.  The other channels
+    keep the workload recipe.  (Channel-wise forgetting at different rates is
+    what the per-channel gate is for: the "Kimi Linear" notes, docsaid.org,
+    section "KDA: Splitting the Decay Across Channels", illustrate it with a
+    channel at alpha = 0.1.)"""
+    x = draw_tokens(rng, T, H, Dk, Dv, dtype)
+    c0 = Dk - int(round(frac * Dk))
+    fast = np.log(alpha) * (1.0 + 0.1 * rng.standard_normal((T, H, Dk - c0)))
+    x.g[:, :, c0:] = np.minimum(fast, 0.0).astype(np.float32)
+    return x
+
+
 @dataclasses.dataclass
 class LayerInputs:
     """Inputs of the fused layer: the projections before their activations.

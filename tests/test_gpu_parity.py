@@ -299,6 +299,44 @@ def test_prefill_strong_decay(kda, dtype):
     assert eo_ <= TOL[dtype] and es_ <= TOL[dtype]
 
 
+@pytest.mark.parametrize("dtype,alpha,C", [("bf16", 0.1, 64), ("f32", 0.1, 64), ("bf16", 0.1, 16),
+                                           ("bf16", 0.01, 64), ("f32", 0.01, 32),
+                                           ("bf16", 1e-20, 64)])
+def test_prefill_mixed_decay(kda, dtype, alpha, C):
+    """Half the key channels decay at alpha near 0.1 per token (a 16-token
+    tile spans about 37 in log-decay: products only), near 0.01 (about 74:
+    the diagonal blocks of those tiles are evaluated pair by pair) or 1e-20
+    (each token wipes those channels), the other half at the workload rate;
+    packed sequences with initial states and ragged tails."""
+    say(f"prefill mixed decay dtype={dtype} alpha={alpha} C={C}")
+    lens = [3 * C + 9, 0, 2 * C, 37]
+    cu = np.concatenate([[0], np.cumsum(lens)]).astype(np.int32)
+    rng = np.random.default_rng([26, C, int(-np.log10(alpha))])
+    H = 3
+    x = I.draw_mixed_decay_tokens(rng, int(cu[-1]), H, 128, 128, dtype, alpha=alpha)
+    s0 = I.draw_states(rng, len(lens), H, 128, 128)
+    eo, ef = oracle.kda_recurrent(x.q, x.k, x.v, x.g, x.beta, s0, cu_seqlens=cu)
+    o, fin = run_prefill(kda, x, C, s0=s0, cu=cu)
+    eo_, es_ = rel(o, eo), rel(fin, ef)
+    po, ps = varlen_pair_rel(o, eo, cu), pair_rel(fin, ef, (0, 1))
+    say(f"  o err {eo_:.2e} (per pair {po:.2e})  state err {es_:.2e} (per pair {ps:.2e})")
+    assert eo_ <= TOL[dtype] and es_ <= TOL[dtype]
+    assert po <= TOL[dtype] and ps <= TOL[dtype]
+
+
+def test_prefill_mixed_decay_full_size(kda):
+    """The T=4096, H=32 workload with half the channels at alpha near 0.1."""
+    say("prefill mixed decay T=4096 H=32")
+    rng = np.random.default_rng(27)
+    x = I.draw_mixed_decay_tokens(rng, 4096, 32, 128, 128, "bf16", alpha=0.1)
+    eo, ef = oracle.kda_recurrent(x.q, x.k, x.v, x.g, x.beta)
+    o, fin = run_prefill(kda, x, 64)
+    eo_, es_ = rel(o, eo), rel(fin, ef)
+    po, ps = pair_rel(o, eo, (1,)), pair_rel(fin, ef, (0, 1))
+    say(f"  o err {eo_:.2e} (per head {po:.2e})  state err {es_:.2e} (per head {ps:.2e})")
+    assert max(eo_, es_, po, ps) <= TOL["bf16"]
+
+
 def test_prefill_weak_decay(kda):
     """g scaled x0.01: long memory, errors could accumulate across chunks."""
     say("prefill weak decay")
