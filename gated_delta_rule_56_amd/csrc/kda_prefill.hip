@@ -44,6 +44,16 @@
 // exp(span of tile a) >= 1; a tile whose span on some channel exceeds
 // kTileSpanLimit has its diagonal block evaluated pair by pair with the
 // exact exponent of each difference instead.  Every block runs on MFMA.
+//
+// Most chunks need none of this: while no channel decays by more than
+// exp(-kChunkSpanLimit) over the whole chunk, one factorisation per chunk
+// (rows exp(Gamma_r) <= 1, columns exp(-Gamma_i) <= exp(kChunkSpanLimit)) is
+// exact to rounding and needs no per-block factors.  So the intra pass runs
+// twice per segment: the chunk-wide pass (TILE = false) handles those
+// chunks and only flags the others in their block; the tile pass (TILE =
+// true) exits at once for unflagged blocks.  The two code paths live in two
+// kernels so that the common one keeps its registers (as one kernel, the
+// tile path's values spilled in both).
 #include "kda_device.hpp"
 #include "kda_launch.hpp"
 
@@ -52,6 +62,7 @@
 namespace kda {
 
 constexpr float kTileSpanLimit = 64.f;  // largest tile span on the diagonal's product path
+constexpr float kChunkSpanLimit = 40.f;  // largest chunk span of the chunk-wide factoring
 constexpr int kIntraThreads = 512;
 
 // ---------------------------------------------------------------------------
@@ -74,7 +85,10 @@ struct Layout {
   // tile): lane l holds rows 4(l>>4)..+3 of column l&15, 16 B per lane.
   static constexpr size_t kU0 = kP + (size_t)NRT * NKC * PF;
   static constexpr size_t kGam = kU0 + (size_t)NRT * NDT * 1024;      // fp32 [D]
-  static constexpr size_t kBytes = ((kGam + D * 4) + 255) / 256 * 256;
+  // int: 1 when the chunk's decay needs tile-local factors (set by the
+  // chunk-wide intra pass, which then leaves the block to the tile pass)
+  static constexpr size_t kFlag = kGam + (size_t)D * 4;
+  static constexpr size_t kBytes = ((kFlag + 4) + 255) / 256 * 256;
 };
 
 static size_t align256(size_t x) { return (x + 255) / 256 * 256; }
@@ -749,7 +763,7 @@ __device__ __forceinline__ void conv8(const Raw8<T>& own, const Raw8<T>& ext, co
 // is applied to the inputs as they are read: 1 = Swish + L2 norm of q and k,
 // Swish of v, sigmoid of beta; 2 = the same after the short convolution of
 // q, k and v.
-template <class M, int D, int C, bool SDEC, int PRO>
+template <class M, int D, int C, bool SDEC, int PRO, bool TILE>
 __global__ __launch_bounds__(kIntraThreads, 4) void intra_chunk_kernel(KernelPtrs kp, SeqInfo si) {
   typedef typename M::in_t in_t;
   typedef typename M::PFrag PFrag;
@@ -769,6 +783,9 @@ __global__ __launch_bounds__(kIntraThreads, 4) void intra_chunk_kernel(KernelPtr
   const Item it = intra_item<C>(si, kp, blockIdx.x * H + blockIdx.y, LY::kBytes);
   const int h = it.h, t0 = it.t0, len = it.len;
   char* blk = it.blk;
+  if constexpr (TILE) {  // only the blocks the chunk-wide pass left
+    if (*reinterpret_cast<const int*>(blk + LY::kFlag) == 0) return;
+  }
   const int tid = threadIdx.x;
   const int w = wave_id(), l = lane_id();
   const int lr = l & 15, lg = l >> 4;
@@ -967,10 +984,24 @@ __global__ __launch_bounds__(kIntraThreads, 4) void intra_chunk_kernel(KernelPtr
       }
     }
   };
-  // Span check of this wave's row tile over all channels.
-  bool big = false;
-  for (int c = l; c < D; c += 64) big |= tot[rt * D + c] < -kTileSpanLimit;
+  // Span checks over all channels: this wave's row tile, and the chunk (the
+  // same verdict in every wave).
+  bool big = false, wide = false;
+  for (int c = l; c < D; c += 64) {
+    big |= tot[rt * D + c] < -kTileSpanLimit;
+    float span = 0.f;
+#pragma unroll
+    for (int t = 0; t < NRT; ++t) span += tot[t * D + c];
+    wide |= span < -kChunkSpanLimit;
+  }
   const bool bad_tile = __any(big);
+  constexpr bool tile_mode = TILE;
+  if constexpr (!TILE) {
+    // every wave reaches the same verdict; the tile pass takes the block
+    const bool leave = __any(wide);
+    if (tid == 0) *reinterpret_cast<int*>(blk + LY::kFlag) = leave ? 1 : 0;
+    if (leave) return;
+  }
   // inputs after the prologue
   auto kin = [&](int j, int e) { return rv ? (PRO ? kact(j, e) * ik : kraw[j].get(e)) : 0.f; };
   auto qin = [&](int j, int e) { return rv ? (PRO ? qact(j, e) * iq : qraw[j].get(e)) : 0.f; };
@@ -985,7 +1016,7 @@ __global__ __launch_bounds__(kIntraThreads, 4) void intra_chunk_kernel(KernelPtr
   // groups, and the lane of group t keeps its own.  The result merges with
   // the other waves' channel parts as the products do.
   f32x4 accAd = {0, 0, 0, 0}, accPd = {0, 0, 0, 0};
-  if (bad_tile) {
+  if (TILE && bad_tile) {
     float kvv[FPW][8], qvv[FPW][8];
 #pragma unroll
     for (int j = 0; j < FPW; ++j)
@@ -1035,7 +1066,8 @@ __global__ __launch_bounds__(kIntraThreads, 4) void intra_chunk_kernel(KernelPtr
   PFrag qrf[FPW], krf[FPW], khf[FPW];
   LdsPrecise<M> KbS(smem + L::oKbS, L::kStPlain);
   {
-    // tile references: rows x exp(G), columns k exp(tot_rt - G)
+    // references: per tile (rows x exp(G), columns k exp(tot_rt - G)), or
+    // for the whole chunk (rows x exp(Gamma), columns k exp(-Gamma))
 #pragma unroll
     for (int j = 0; j < FPW; ++j) {
       float qt[8], qr[8], kr[8], kh[8], gsa[8], trt[8], gn[8];
@@ -1046,11 +1078,11 @@ __global__ __launch_bounds__(kIntraThreads, 4) void intra_chunk_kernel(KernelPtr
       for (int e = 0; e < 8; ++e) {
         const float kv = kin(j, e), qv = qin(j, e);
         const float gf = G[j][e] + gsa[e];  // cumulative decay of the row
-        const float ew = __expf(G[j][e]);
+        const float ew = __expf(tile_mode ? G[j][e] : gf);
         qt[e] = qv * __expf(gf);
         qr[e] = qv * ew;
         kr[e] = kv * ew;
-        kh[e] = kv * __expf(trt[e] - G[j][e]);
+        kh[e] = kv * __expf(tile_mode ? trt[e] - G[j][e] : -gf);
         if (fv[j]) KbS.store((32 * fkb[j] + 8 * lg + e) * SK + r, kv * __expf(gn[e] - gf));
       }
       qrf[j] = make_pfrag(M{}, qr);
@@ -1109,7 +1141,7 @@ __global__ __launch_bounds__(kIntraThreads, 4) void intra_chunk_kernel(KernelPtr
 #pragma unroll
     for (int b = 0; b < NRT; ++b) {
       if (b > rt) break;
-      if (b == rt && bad_tile) {
+      if (TILE && b == rt && bad_tile) {
         accA[b] = accAd;
         accP[b] = accPd;
         continue;
@@ -1118,7 +1150,7 @@ __global__ __launch_bounds__(kIntraThreads, 4) void intra_chunk_kernel(KernelPtr
       for (int j = 0; j < FPW; ++j) {
         if (!fv[j]) continue;
         PFrag kbf = ld_pfrag(M{}, smem + L::oKh + (size_t)(b * NKD + fkb[j]) * LY::PF);
-        if (b != rt - 1) {
+        if (tile_mode && b != rt - 1) {
           float ex[8];
           if (b == rt) {
             tot_sum(j, rt, rt + 1, ex);
@@ -1253,18 +1285,28 @@ __global__ __launch_bounds__(kIntraThreads, 4) void intra_chunk_kernel(KernelPtr
     for (int e = 0; e < 4; ++e) x[e] = XD[(16 * w + lr) * 17 + 4 * lg + e];
     cfrag_store(M{}, CF + (size_t)(NOFF + w) * 1024, x);
   }
-  // K*gam = (k exp(G)) exp(Gsa): the row operand times the decay of the
-  // earlier tiles (both factors <= 1, so an underflow is a true zero).
+  // K*gam: the Gram row operand k exp(Gamma) itself with chunk-wide
+  // factoring; per tile, (k exp(G)) exp(Gsa), the row operand times the decay
+  // of the earlier tiles (both factors <= 1, so an underflow is a true zero).
   LdsPrecise<M> KtT(smem + L::oKtT, L::kStPlain);
+  if constexpr (!TILE) {
 #pragma unroll
-  for (int j = 0; j < FPW; ++j)
-    if (fv[j]) {
-      float x[8], gs[8];
-      pfrag_values(krf[j], x);
-      tot_sum(j, 0, rt, gs);
+    for (int j = 0; j < FPW; ++j)
+      if (fv[j]) {
 #pragma unroll
-      for (int e = 0; e < 8; ++e) KtT.store((32 * fkb[j] + 8 * lg + e) * SK + r, x[e] * __expf(gs[e]));
-    }
+        for (int e = 0; e < 8; ++e) KtT.put((32 * fkb[j] + 8 * lg + e) * SK + r, krf[j], e);
+      }
+  } else {
+#pragma unroll
+    for (int j = 0; j < FPW; ++j)
+      if (fv[j]) {
+        float x[8], gs[8];
+        pfrag_values(krf[j], x);
+        tot_sum(j, 0, rt, gs);
+#pragma unroll
+        for (int e = 0; e < 8; ++e) KtT.store((32 * fkb[j] + 8 * lg + e) * SK + r, x[e] * __expf(gs[e]));
+      }
+  }
   if (KC > C) {
     for (int idx = tid; idx < D * (KC - C); idx += kIntraThreads) {
       const int c = idx / (KC - C), i = C + idx % (KC - C);
@@ -1927,13 +1969,18 @@ static hipError_t launch_prefill_t(const PrefillArgs& a) {
   if (SDEC && a.layer.prologue) return hipErrorInvalidValue;
   const int pro = !a.layer.prologue ? 0 : a.layer.conv_w > 0 ? 2 : 1;
   const size_t lds = pro == 2 ? lds_conv : lds0;
-  const void* intra_fn =
-      pro == 2   ? reinterpret_cast<const void*>(&intra_chunk_kernel<M, D, C, SDEC, P2>)
-      : pro == 1 ? reinterpret_cast<const void*>(&intra_chunk_kernel<M, D, C, SDEC, P1>)
-                 : reinterpret_cast<const void*>(&intra_chunk_kernel<M, D, C, SDEC, 0>);
+  const void* intra_fn[2] = {
+      pro == 2   ? reinterpret_cast<const void*>(&intra_chunk_kernel<M, D, C, SDEC, P2, false>)
+      : pro == 1 ? reinterpret_cast<const void*>(&intra_chunk_kernel<M, D, C, SDEC, P1, false>)
+                 : reinterpret_cast<const void*>(&intra_chunk_kernel<M, D, C, SDEC, 0, false>),
+      pro == 2   ? reinterpret_cast<const void*>(&intra_chunk_kernel<M, D, C, SDEC, P2, true>)
+      : pro == 1 ? reinterpret_cast<const void*>(&intra_chunk_kernel<M, D, C, SDEC, P1, true>)
+                 : reinterpret_cast<const void*>(&intra_chunk_kernel<M, D, C, SDEC, 0, true>)};
   if (plan.max_slots > 0) {
-    hipError_t e = hipFuncSetAttribute(intra_fn, hipFuncAttributeMaxDynamicSharedMemorySize, (int)lds);
-    if (e != hipSuccess) return e;
+    for (const void* fn : intra_fn) {
+      hipError_t e = hipFuncSetAttribute(fn, hipFuncAttributeMaxDynamicSharedMemorySize, (int)lds);
+      if (e != hipSuccess) return e;
+    }
   }
   const int nct = choose_nct(a.num_seqs * a.H, D, a.tuning);
   for (int s = 0; s < plan.nseg; ++s) {
@@ -1948,16 +1995,15 @@ static hipError_t launch_prefill_t(const PrefillArgs& a) {
       const int c = sc.nch(0) - si.c0;
       si.slot_cnt = c <= 0 ? 0 : (c < plan.L ? c : plan.L);
     }
+    // the chunk-wide intra pass, then the tile pass for the blocks it left
     const dim3 igrid((unsigned)slots, a.H);
-    if (slots > 0 && pro == 2)
-      hipLaunchKernelGGL((intra_chunk_kernel<M, D, C, SDEC, P2>), igrid, dim3(kIntraThreads), lds,
-                         a.stream, kp, si);
-    else if (slots > 0 && pro == 1)
-      hipLaunchKernelGGL((intra_chunk_kernel<M, D, C, SDEC, P1>), igrid, dim3(kIntraThreads), lds,
-                         a.stream, kp, si);
-    else if (slots > 0)
-      hipLaunchKernelGGL((intra_chunk_kernel<M, D, C, SDEC, 0>), igrid, dim3(kIntraThreads), lds,
-                         a.stream, kp, si);
+    if (slots > 0) {
+      for (const void* fn : intra_fn) {
+        void* args[] = {&kp, &si};
+        hipError_t e = hipLaunchKernel(fn, igrid, dim3(kIntraThreads), args, lds, a.stream);
+        if (e != hipSuccess) return e;
+      }
+    }
     if (nct == 2)
       launch_inter<M, D, C, 2>(a, kp, si);
     else

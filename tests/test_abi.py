@@ -89,25 +89,30 @@ def test_prefill_varlen_validation(lib):
     assert _prefill(lib, cu=FAKE, cu_host=hp(good), N=3, wsb=16) == WORKSPACE
 
 
+# One (chunk, head) operand block at D=128, C=64, bf16: Q*gam 32 KB, W 32 KB,
+# K-bar 32 KB, P 16 KB as bf16 hi + lo; U0 = T V 32 KB fp32; gam_n 512 B; the
+# tile-pass flag, padded to 256 B.
+BLOCK = 3 * 32768 + 16384 + 32768 + 512 + 256
+
+
 def test_workspace_size(lib):
-    # B=1, T=4096, H=32, D=128, C=64, bf16: 64 chunks of 32 heads x 147968 B
-    # (Q*gam 32 KB, W 32 KB, K-bar 32 KB, P 16 KB as bf16 hi + lo; U0 = T V
-    # 32 KB fp32; gam_n 512 B).  The workspace holds one segment of chunks
+    # B=1, T=4096, H=32, D=128, C=64, bf16: 64 chunks of 32 heads x BLOCK
+    # bytes.  The workspace holds one segment of chunks
     # (a 160 MiB budget: at most 35 chunks, so 2 equal segments of 32) and the
     # fp32 state carried between segments (32 x 128 x 128 x 4 B); fixed-length
     # input needs no slot table.
     n = kda.workspace_size(1, 4096, 32, 128, 1, 64, kda.KDA_BF16)
-    assert n == 32 * 32 * 147968 + 32 * 128 * 128 * 4
+    assert n == 32 * 32 * BLOCK + 32 * 128 * 128 * 4
     # one segment: no carry buffer
     n1 = kda.workspace_size(1, 2048, 32, 128, 1, 64, kda.KDA_BF16)
-    assert n1 == 32 * 32 * 147968
+    assert n1 == 32 * 32 * BLOCK
     # varlen, fp32, D=64, C=16, H=4: lengths 100, 0, 200 -> 7, 0, 13 chunks,
-    # one segment of 13 local chunks holding 7 + 13 slots of 4 x 22784 B
-    # (Q*gam 4 KB, W 4 KB, K-bar 8 KB, P 2 KB, U0 4 KB, gam_n 256 B, a
-    # multiple of 256 B), plus the 256-byte slot table.
+    # one segment of 13 local chunks holding 7 + 13 slots of 4 x 23040 B
+    # (Q*gam 4 KB, W 4 KB, K-bar 8 KB, P 2 KB, U0 4 KB, gam_n 256 B, the flag
+    # padded to 256 B), plus the 256-byte slot table.
     cu = np.array([0, 100, 100, 300], dtype=np.int32)
     m = kda.workspace_size(1, 300, 4, 64, 3, 16, kda.KDA_F32, cu)
-    assert m == 20 * 4 * 22784 + 256
+    assert m == 20 * 4 * 23040 + 256
     with pytest.raises(kda.KDAError):
         kda.workspace_size(1, 300, 4, 80, 3, 16, kda.KDA_F32, cu)
 
@@ -118,14 +123,14 @@ def test_workspace_segments(lib):
     # segments of 16, plus the carried state.
     n = kda.workspace_size(1, 4096, 1, 128, 1, 64, kda.KDA_BF16,
                            options={"segment_bytes": 1000 << 10})
-    assert n == 16 * 147968 + 128 * 128 * 4
+    assert n == 16 * BLOCK + 128 * 128 * 4
     # 4000 KB fits 27 chunks: 3 segments, evened out to 22 chunks each.
     n = kda.workspace_size(1, 4096, 1, 128, 1, 64, kda.KDA_BF16,
                            options={"segment_bytes": 4000 << 10})
-    assert n == 22 * 147968 + 128 * 128 * 4
+    assert n == 22 * BLOCK + 128 * 128 * 4
     # A fixed segment length of 5 chunks: 13 segments, evened out to 5.
     n = kda.workspace_size(1, 4096, 1, 128, 1, 64, kda.KDA_BF16, options={"segment_chunks": 5})
-    assert n == 5 * 147968 + 128 * 128 * 4
+    assert n == 5 * BLOCK + 128 * 128 * 4
     # Options that only split the work differently leave plain calls alone.
     assert kda.workspace_size(1, 4096, 1, 128, 1, 64, kda.KDA_BF16, options={}) == \
         kda.workspace_size(1, 4096, 1, 128, 1, 64, kda.KDA_BF16)
