@@ -763,8 +763,10 @@ __device__ __forceinline__ void conv8(const Raw8<T>& own, const Raw8<T>& ext, co
 // is applied to the inputs as they are read: 1 = Swish + L2 norm of q and k,
 // Swish of v, sigmoid of beta; 2 = the same after the short convolution of
 // q, k and v.
+// The work of one (chunk slot, head) item; smem is the workgroup's dynamic
+// LDS.  Every wave of the workgroup calls it for the same item.
 template <class M, int D, int C, bool SDEC, int PRO, bool TILE>
-__global__ __launch_bounds__(kIntraThreads, 4) void intra_chunk_kernel(KernelPtrs kp, SeqInfo si) {
+__device__ __forceinline__ void intra_item_body(const KernelPtrs& kp, const SeqInfo& si, int item, char* smem) {
   typedef typename M::in_t in_t;
   typedef typename M::PFrag PFrag;
   typedef Layout<M, D, C> LY;
@@ -777,10 +779,9 @@ __global__ __launch_bounds__(kIntraThreads, 4) void intra_chunk_kernel(KernelPtr
   constexpr int FPW = (NFRAG + NW - 1) / NW;  // fragments per wave
   static_assert(NW % NRT == 0, "a wave's fragments share one row tile");
   static_assert(NDT <= NW, "one wave per column tile in the solve");
-  extern __shared__ __attribute__((aligned(16))) char smem[];
 
   const int H = kp.H;
-  const Item it = intra_item<C>(si, kp, blockIdx.x * H + blockIdx.y, LY::kBytes);
+  const Item it = intra_item<C>(si, kp, item, LY::kBytes);
   const int h = it.h, t0 = it.t0, len = it.len;
   char* blk = it.blk;
   if constexpr (TILE) {  // only the blocks the chunk-wide pass left
@@ -1391,6 +1392,27 @@ __global__ __launch_bounds__(kIntraThreads, 4) void intra_chunk_kernel(KernelPtr
   }
 }
 
+// The chunk-wide pass: one workgroup per item, grid (segment slots, H).
+template <class M, int D, int C, bool SDEC, int PRO>
+__global__ __launch_bounds__(kIntraThreads, 4) void intra_chunk_kernel(KernelPtrs kp, SeqInfo si) {
+  extern __shared__ __attribute__((aligned(16))) char smem[];
+  intra_item_body<M, D, C, SDEC, PRO, false>(kp, si, blockIdx.x * kp.H + blockIdx.y, smem);
+}
+
+// The tile pass: each workgroup looks at two items and works on the ones the
+// chunk-wide pass flagged, so a segment without any costs one launch of half
+// the size (at T = 4096, H = 32, one round of two workgroups per CU).  Two
+// written-out calls, not a loop: in a loop the compiler keeps per-lane
+// values live across the body and spills hundreds of bytes.
+template <class M, int D, int C, bool SDEC, int PRO>
+__global__ __launch_bounds__(kIntraThreads, 4) void intra_tile_kernel(KernelPtrs kp, SeqInfo si, int items) {
+  extern __shared__ __attribute__((aligned(16))) char smem[];
+  intra_item_body<M, D, C, SDEC, PRO, true>(kp, si, 2 * blockIdx.x, smem);
+  __syncthreads();  // the first item's last LDS reads before the second's writes
+  if (2 * (int)blockIdx.x + 1 < items)
+    intra_item_body<M, D, C, SDEC, PRO, true>(kp, si, 2 * blockIdx.x + 1, smem);
+}
+
 // ---------------------------------------------------------------------------
 // Inter-chunk kernel: one workgroup per (sequence, head, block of value
 // columns), 512 threads in two roles that share the chunk loop:
@@ -1970,12 +1992,12 @@ static hipError_t launch_prefill_t(const PrefillArgs& a) {
   const int pro = !a.layer.prologue ? 0 : a.layer.conv_w > 0 ? 2 : 1;
   const size_t lds = pro == 2 ? lds_conv : lds0;
   const void* intra_fn[2] = {
-      pro == 2   ? reinterpret_cast<const void*>(&intra_chunk_kernel<M, D, C, SDEC, P2, false>)
-      : pro == 1 ? reinterpret_cast<const void*>(&intra_chunk_kernel<M, D, C, SDEC, P1, false>)
-                 : reinterpret_cast<const void*>(&intra_chunk_kernel<M, D, C, SDEC, 0, false>),
-      pro == 2   ? reinterpret_cast<const void*>(&intra_chunk_kernel<M, D, C, SDEC, P2, true>)
-      : pro == 1 ? reinterpret_cast<const void*>(&intra_chunk_kernel<M, D, C, SDEC, P1, true>)
-                 : reinterpret_cast<const void*>(&intra_chunk_kernel<M, D, C, SDEC, 0, true>)};
+      pro == 2   ? reinterpret_cast<const void*>(&intra_chunk_kernel<M, D, C, SDEC, P2>)
+      : pro == 1 ? reinterpret_cast<const void*>(&intra_chunk_kernel<M, D, C, SDEC, P1>)
+                 : reinterpret_cast<const void*>(&intra_chunk_kernel<M, D, C, SDEC, 0>),
+      pro == 2   ? reinterpret_cast<const void*>(&intra_tile_kernel<M, D, C, SDEC, P2>)
+      : pro == 1 ? reinterpret_cast<const void*>(&intra_tile_kernel<M, D, C, SDEC, P1>)
+                 : reinterpret_cast<const void*>(&intra_tile_kernel<M, D, C, SDEC, 0>)};
   if (plan.max_slots > 0) {
     for (const void* fn : intra_fn) {
       hipError_t e = hipFuncSetAttribute(fn, hipFuncAttributeMaxDynamicSharedMemorySize, (int)lds);
@@ -1998,11 +2020,14 @@ static hipError_t launch_prefill_t(const PrefillArgs& a) {
     // the chunk-wide intra pass, then the tile pass for the blocks it left
     const dim3 igrid((unsigned)slots, a.H);
     if (slots > 0) {
-      for (const void* fn : intra_fn) {
-        void* args[] = {&kp, &si};
-        hipError_t e = hipLaunchKernel(fn, igrid, dim3(kIntraThreads), args, lds, a.stream);
-        if (e != hipSuccess) return e;
-      }
+      void* args[] = {&kp, &si};
+      hipError_t e = hipLaunchKernel(intra_fn[0], igrid, dim3(kIntraThreads), args, lds, a.stream);
+      if (e != hipSuccess) return e;
+      int items = (int)(slots * a.H);
+      void* targs[] = {&kp, &si, &items};
+      e = hipLaunchKernel(intra_fn[1], dim3((unsigned)((items + 1) / 2)), dim3(kIntraThreads), targs, lds,
+                          a.stream);
+      if (e != hipSuccess) return e;
     }
     if (nct == 2)
       launch_inter<M, D, C, 2>(a, kp, si);
