@@ -379,27 +379,47 @@ kda_status kda_decode_step_layer(const void* q_pre, const void* k_pre, const voi
                      H, Dk, Dv, in_dtype, out_dtype, stream);
 }
 
-kda_status kda_backward_workspace_size(int B, int T, int H, int Dk, int Dv, int num_seqs,
-                                       const int32_t* cu_seqlens_host, int chunk_size,
-                                       size_t* bytes) {
+static kda_status backward_size_impl(int B, int T, int H, int Dk, int Dv, int num_seqs,
+                                     const int32_t* cu_seqlens_host, int chunk_size,
+                                     const kda_prefill_options* options, size_t* bytes) {
   if (bytes == nullptr || H < 1) return KDA_ERR_INVALID_ARG;
   if (!supported_head(Dk, Dv) || !supported_chunk(chunk_size)) return KDA_ERR_UNSUPPORTED;
+  kda::PrefillTuning t;
+  if (make_tuning(options, &t) != KDA_OK || t.value_block != 0) return KDA_ERR_INVALID_ARG;
   int64_t chunks = 0;
   kda_status st = seq_layout(B, T, num_seqs, cu_seqlens_host, cu_seqlens_host, chunk_size, &chunks);
   if (st != KDA_OK) return st;
-  *bytes = kda::backward_workspace_bytes(chunks, num_seqs, H, Dk, chunk_size);
+  const size_t n = kda::backward_workspace_bytes(num_seqs, cu_seqlens_host, cu_seqlens_host ? 0 : T, H, Dk,
+                                                 chunk_size, t);
+  if (n == SIZE_MAX) return KDA_ERR_INVALID_ARG;
+  *bytes = n;
   return KDA_OK;
 }
 
-kda_status kda_backward(const void* q, const void* k, const void* v, const float* g,
-                        const float* beta, const float* initial_state, const float* d_o,
-                        const float* d_final_state, float* dq, float* dk, float* dv, float* dg,
-                        float* dbeta, float* d_initial_state, const int32_t* cu_seqlens,
-                        const int32_t* cu_seqlens_host, int B, int T, int H, int Dk, int Dv,
-                        int num_seqs, int chunk_size, kda_dtype in_dtype, void* workspace,
-                        size_t workspace_bytes, void* stream) {
+kda_status kda_backward_workspace_size(int B, int T, int H, int Dk, int Dv, int num_seqs,
+                                       const int32_t* cu_seqlens_host, int chunk_size,
+                                       size_t* bytes) {
+  return backward_size_impl(B, T, H, Dk, Dv, num_seqs, cu_seqlens_host, chunk_size, nullptr, bytes);
+}
+
+kda_status kda_backward_workspace_size_ex(int B, int T, int H, int Dk, int Dv, int num_seqs,
+                                          const int32_t* cu_seqlens_host, int chunk_size,
+                                          const kda_prefill_options* options, size_t* bytes) {
+  return backward_size_impl(B, T, H, Dk, Dv, num_seqs, cu_seqlens_host, chunk_size, options, bytes);
+}
+
+static kda_status backward_impl(const void* q, const void* k, const void* v, const float* g,
+                                const float* beta, const float* initial_state, const float* d_o,
+                                const float* d_final_state, float* dq, float* dk, float* dv,
+                                float* dg, float* dbeta, float* d_initial_state,
+                                const int32_t* cu_seqlens, const int32_t* cu_seqlens_host, int B,
+                                int T, int H, int Dk, int Dv, int num_seqs, int chunk_size,
+                                kda_dtype in_dtype, const kda_prefill_options* options,
+                                void* workspace, size_t workspace_bytes, void* stream) {
   if (H < 1 || !valid_dtype(in_dtype)) return KDA_ERR_INVALID_ARG;
   if (!supported_head(Dk, Dv) || !supported_chunk(chunk_size)) return KDA_ERR_UNSUPPORTED;
+  kda::PrefillTuning t;
+  if (make_tuning(options, &t) != KDA_OK || t.value_block != 0) return KDA_ERR_INVALID_ARG;
   const void* ptrs[] = {q, k, v, g, beta, initial_state, d_o, d_final_state, dq, dk, dv, dg,
                         dbeta, d_initial_state, cu_seqlens};
   for (const void* p : ptrs)
@@ -411,7 +431,9 @@ kda_status kda_backward(const void* q, const void* k, const void* v, const float
       (!q || !k || !v || !g || !beta || !d_o || !dq || !dk || !dv || !dg || !dbeta))
     return KDA_ERR_INVALID_ARG;
   if (chunks * (int64_t)H > INT32_MAX) return KDA_ERR_INVALID_ARG;
-  const size_t need = kda::backward_workspace_bytes(chunks, num_seqs, H, Dk, chunk_size);
+  const size_t need = kda::backward_workspace_bytes(num_seqs, cu_seqlens_host, cu_seqlens ? 0 : T, H, Dk,
+                                                    chunk_size, t);
+  if (need == SIZE_MAX) return KDA_ERR_INVALID_ARG;
   if (workspace == nullptr || workspace_bytes < need) return KDA_ERR_WORKSPACE;
   if (!aligned(workspace, 256)) return KDA_ERR_INVALID_ARG;
   kda::BackwardArgs a;
@@ -430,6 +452,7 @@ kda_status kda_backward(const void* q, const void* k, const void* v, const float
   a.dbeta = dbeta;
   a.d_initial_state = d_initial_state;
   a.cu_seqlens = cu_seqlens;
+  a.cu_seqlens_host = cu_seqlens ? cu_seqlens_host : nullptr;
   a.num_seqs = num_seqs;
   a.seq_len = cu_seqlens ? 0 : T;
   a.total_tokens = B * T;
@@ -438,9 +461,35 @@ kda_status kda_backward(const void* q, const void* k, const void* v, const float
   a.D = Dk;
   a.chunk = chunk_size;
   a.in_bf16 = in_dtype == KDA_BF16;
+  a.tuning = t;
   a.workspace = workspace;
   a.stream = reinterpret_cast<hipStream_t>(stream);
   return kda::launch_backward(a) == hipSuccess ? KDA_OK : KDA_ERR_HIP;
+}
+
+kda_status kda_backward(const void* q, const void* k, const void* v, const float* g,
+                        const float* beta, const float* initial_state, const float* d_o,
+                        const float* d_final_state, float* dq, float* dk, float* dv, float* dg,
+                        float* dbeta, float* d_initial_state, const int32_t* cu_seqlens,
+                        const int32_t* cu_seqlens_host, int B, int T, int H, int Dk, int Dv,
+                        int num_seqs, int chunk_size, kda_dtype in_dtype, void* workspace,
+                        size_t workspace_bytes, void* stream) {
+  return backward_impl(q, k, v, g, beta, initial_state, d_o, d_final_state, dq, dk, dv, dg, dbeta,
+                       d_initial_state, cu_seqlens, cu_seqlens_host, B, T, H, Dk, Dv, num_seqs,
+                       chunk_size, in_dtype, nullptr, workspace, workspace_bytes, stream);
+}
+
+kda_status kda_backward_ex(const void* q, const void* k, const void* v, const float* g,
+                           const float* beta, const float* initial_state, const float* d_o,
+                           const float* d_final_state, float* dq, float* dk, float* dv, float* dg,
+                           float* dbeta, float* d_initial_state, const int32_t* cu_seqlens,
+                           const int32_t* cu_seqlens_host, int B, int T, int H, int Dk, int Dv,
+                           int num_seqs, int chunk_size, kda_dtype in_dtype,
+                           const kda_prefill_options* options, void* workspace,
+                           size_t workspace_bytes, void* stream) {
+  return backward_impl(q, k, v, g, beta, initial_state, d_o, d_final_state, dq, dk, dv, dg, dbeta,
+                       d_initial_state, cu_seqlens, cu_seqlens_host, B, T, H, Dk, Dv, num_seqs,
+                       chunk_size, in_dtype, options, workspace, workspace_bytes, stream);
 }
 
 kda_status dplr_prefill_workspace_size(int B, int T, int H, int Dk, int Dv, int num_seqs,

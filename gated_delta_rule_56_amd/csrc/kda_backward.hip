@@ -244,7 +244,8 @@ constexpr int kSerThreads = 512;
 // chunk's Kt, Kb, T are loaded into registers while this chunk computes.
 template <int D, int C>
 __global__ __launch_bounds__(kSerThreads) void bwd_fwd_states_kernel(Planes p, Geo geo,
-                                                                     const float* __restrict__ s0) {
+                                                                     const float* __restrict__ s0,
+                                                                     float* __restrict__ s_out) {
   extern __shared__ float sm[];
   FwdLds<D, C>& L = *reinterpret_cast<FwdLds<D, C>*>(sm);
   constexpr int NVB = D / kCols, NT = kSerThreads, NW = NT / 64;
@@ -252,9 +253,9 @@ __global__ __launch_bounds__(kSerThreads) void bwd_fwd_states_kernel(Planes p, G
   const int vb = blockIdx.x % NVB, nh = blockIdx.x / NVB;
   const int n = nh / H, h = nh % H, col0 = vb * kCols;
   const int tid = threadIdx.x, w = tid >> 6, l = tid & 63, m = l & 15, g = l >> 4;
-  int bos, eos, base;
+  int bos, eos, base, lo, hi;
   seq_of<C>(geo, n, bos, eos, base);
-  const int nch = (eos - bos + C - 1) / C;
+  seg_range<C>(geo, bos, eos, lo, hi);
   for (int idx = tid; idx < D * kCols; idx += NT) {
     const int i = idx / kCols, j = idx % kCols;
     L.S[i][j] = s0 ? s0[(((size_t)n * H + h) * D + i) * D + col0 + j] : 0.f;
@@ -263,7 +264,7 @@ __global__ __launch_bounds__(kSerThreads) void bwd_fwd_states_kernel(Planes p, G
   Prefetch<C, C, NT> pT;
   Prefetch<C, kCols, NT, D> pV;  // this workgroup's value columns
   Prefetch<1, D, NT> pG;         // gam_n
-  auto blk = [&](int ci) { return (size_t)(base + ci) * H + h; };
+  auto blk = [&](int ci) { return (size_t)(base + ci - geo.c0) * H + h; };
   auto fetch = [&](size_t b) {
     pKt.load(p.Kt + b * C * D);
     pKb.load(p.Kb + b * C * D);
@@ -271,8 +272,8 @@ __global__ __launch_bounds__(kSerThreads) void bwd_fwd_states_kernel(Planes p, G
     pV.load(p.V + b * C * D + col0);
     pG.load(p.gn + b * D);
   };
-  if (nch > 0) fetch(blk(0));
-  for (int ci = 0; ci < nch; ++ci) {
+  if (lo < hi) fetch(blk(lo));
+  for (int ci = lo; ci < hi; ++ci) {
     const size_t b = blk(ci);
     const size_t pcd = b * C * D;
     __syncthreads();
@@ -286,7 +287,7 @@ __global__ __launch_bounds__(kSerThreads) void bwd_fwd_states_kernel(Planes p, G
       p.S[(b * D + i) * D + col0 + j] = L.S[i][j];
     }
     __syncthreads();
-    if (ci + 1 < nch) fetch(blk(ci + 1));
+    if (ci + 1 < hi) fetch(blk(ci + 1));
     for (int rt = w; rt < C / 16; rt += NW) {  // R = V - Kt S
       f32x4 acc = {0, 0, 0, 0}, acc1 = {0, 0, 0, 0};
 #pragma unroll 8
@@ -330,6 +331,13 @@ __global__ __launch_bounds__(kSerThreads) void bwd_fwd_states_kernel(Planes p, G
       for (int i = 0; i < 4; ++i) L.S[16 * t + 4 * g + i][m] = acc[i] + acc1[i];
     }
   }
+  if (s_out) {  // the state after the pass's last chunk
+    __syncthreads();
+    for (int idx = tid; idx < D * kCols; idx += NT) {
+      const int i = idx / kCols, j = idx % kCols;
+      s_out[(((size_t)n * H + h) * D + i) * D + col0 + j] = L.S[i][j];
+    }
+  }
 }
 
 template <int D, int C>
@@ -367,9 +375,9 @@ __global__ __launch_bounds__(kSerThreads) void bwd_bwd_states_kernel(Planes p, G
   const int vb = blockIdx.x % NVB, nh = blockIdx.x / NVB;
   const int n = nh / H, h = nh % H, col0 = vb * kCols;
   const int tid = threadIdx.x, w = tid >> 6, l = tid & 63, m = l & 15, g = l >> 4;
-  int bos, eos, base;
+  int bos, eos, base, lo, hi;
   seq_of<C>(geo, n, bos, eos, base);
-  const int nch = (eos - bos + C - 1) / C;
+  seg_range<C>(geo, bos, eos, lo, hi);
   for (int idx = tid; idx < D * kCols; idx += NT) {
     const int i = idx / kCols, j = idx % kCols;
     L.X[i][j] = dfin ? dfin[(((size_t)n * H + h) * D + i) * D + col0 + j] : 0.f;
@@ -378,7 +386,7 @@ __global__ __launch_bounds__(kSerThreads) void bwd_bwd_states_kernel(Planes p, G
   Prefetch<C, D, NT> pKb, pQt, pKt;
   Prefetch<C, kCols, NT, D> pdO;  // this workgroup's value columns
   Prefetch<1, D, NT> pG;          // gam_n
-  auto blk = [&](int ci) { return (size_t)(base + ci) * H + h; };
+  auto blk = [&](int ci) { return (size_t)(base + ci - geo.c0) * H + h; };
   // P, T, K-bar, dO and gam_n of a chunk load a step ahead, Q*gam and K*gam
   // half a step ahead (after the previous chunk's copies are stored).
   auto fetch_a = [&](size_t b) {
@@ -392,11 +400,11 @@ __global__ __launch_bounds__(kSerThreads) void bwd_bwd_states_kernel(Planes p, G
     pQt.load(p.Qt + b * C * D);
     pKt.load(p.Kt + b * C * D);
   };
-  if (nch > 0) {
-    fetch_a(blk(nch - 1));
-    fetch_b(blk(nch - 1));
+  if (lo < hi) {
+    fetch_a(blk(hi - 1));
+    fetch_b(blk(hi - 1));
   }
-  for (int ci = nch - 1; ci >= 0; --ci) {
+  for (int ci = hi - 1; ci >= lo; --ci) {
     const size_t b = blk(ci);
     const size_t pcd = b * C * D;
     __syncthreads();
@@ -410,7 +418,7 @@ __global__ __launch_bounds__(kSerThreads) void bwd_bwd_states_kernel(Planes p, G
       p.dSn[(b * D + i) * D + col0 + j] = L.X[i][j];
     }
     __syncthreads();
-    if (ci > 0) fetch_a(blk(ci - 1));
+    if (ci > lo) fetch_a(blk(ci - 1));
     for (int rt = w; rt < C / 16; rt += NW) {  // dU = P^T dO + Kb dS'
       f32x4 acc = {0, 0, 0, 0}, acc1 = {0, 0, 0, 0};
       for (int k0 = 16 * rt; k0 < C; k0 += 4) acc = mfma4(L.u.a.P[k0 + g][16 * rt + m], L.dO[k0 + g][m], acc);
@@ -441,7 +449,7 @@ __global__ __launch_bounds__(kSerThreads) void bwd_bwd_states_kernel(Planes p, G
     __syncthreads();
     pQt.template store<D + 16>(&L.u.b.Qt[0][0]);
     pKt.template store<D + 16>(&L.u.b.Kt[0][0]);
-    if (ci > 0) fetch_b(blk(ci - 1));
+    if (ci > lo) fetch_b(blk(ci - 1));
     __syncthreads();
     for (int t = w; t < D / 16; t += NW) {  // dS = gam_n dS' + Qt^T dO - Kt^T dR
       f32x4 acc, acc1 = {0, 0, 0, 0};
@@ -727,9 +735,86 @@ __global__ __launch_bounds__(D) void bwd_final_fast_kernel(Planes p, Geo geo, Bw
 template <int D, int C>
 size_t final_lds() { return ((size_t)4 * C * D + 2 * C * C) * sizeof(float); }
 
+// Chunk counts of the sequences, on the host.
+struct BwdCounts {
+  int num_seqs;
+  const int32_t* cu;  // host cu_seqlens or nullptr
+  int seq_len, C;
+  int nch(int n) const {
+    const long long len = cu ? (long long)cu[n + 1] - cu[n] : seq_len;
+    return (int)((len + C - 1) / C);
+  }
+  long long slots(int c0, int L) const {  // plane slots of the segment at c0
+    long long t = 0;
+    for (int n = 0; n < num_seqs; ++n) {
+      const int c = nch(n) - c0;
+      t += c <= 0 ? 0 : (c < L ? c : L);
+    }
+    return t;
+  }
+  int max_nch() const {
+    int m = 0;
+    for (int n = 0; n < num_seqs; ++n) m = nch(n) > m ? nch(n) : m;
+    return m;
+  }
+};
+
+// The backward runs in segments of L local chunks of every sequence, like the
+// forward prefill: a forward sweep over the segments keeps only the state
+// entering each one, and the backward sweep, last segment first, recomputes a
+// segment's forward planes from that state before its gradients.  The planes
+// of one segment fit the budget (4 GiB unless the caller's tuning says
+// otherwise), so the workspace is bounded for any length; an input that fits
+// in one segment runs exactly as one pass.
+struct BwdPlan {
+  int L = 0, nseg = 0;
+  long long max_slots = 0;
+};
+
+BwdPlan plan_backward(int num_seqs, const int32_t* cu_host, int seq_len, int H, int D, int C,
+                      const PrefillTuning& t) {
+  const BwdCounts sc{num_seqs, cu_host, seq_len, C};
+  const int maxc = sc.max_nch();
+  BwdPlan p;
+  auto finish = [&](int L) {
+    p.L = L < 1 ? 1 : L;
+    p.nseg = maxc == 0 ? 1 : (maxc + p.L - 1) / p.L;
+    p.max_slots = 0;
+    for (int s = 0; s < p.nseg; ++s) {
+      const long long x = sc.slots(s * p.L, p.L);
+      p.max_slots = x > p.max_slots ? x : p.max_slots;
+    }
+  };
+  if (t.segment_chunks >= 1) {
+    finish(t.segment_chunks);
+    return p;
+  }
+  const size_t budget = t.segment_bytes >= 1 ? t.segment_bytes : (size_t)4 << 30;
+  // the largest L whose planes fit, at least one chunk; then even out
+  int lo = 1, hi = maxc > 0 ? maxc : 1;
+  while (lo < hi) {
+    const int mid = lo + (hi - lo + 1) / 2;
+    if (plane_bytes((size_t)sc.slots(0, mid) * H, C, D) <= budget)
+      lo = mid;
+    else
+      hi = mid - 1;
+  }
+  const int nseg = maxc == 0 ? 1 : (maxc + lo - 1) / lo;
+  finish(maxc == 0 ? 1 : (maxc + nseg - 1) / nseg);
+  return p;
+}
+
+size_t bwd_bytes(const BwdPlan& p, int num_seqs, bool varlen, int H, int D, int C) {
+  const size_t nhdd = (size_t)num_seqs * H * D * D * sizeof(float);
+  return (varlen ? a256(sizeof(int32_t) * (size_t)(num_seqs + 1)) : 0) +
+         (p.nseg > 1 ? a256((size_t)p.nseg * nhdd) : 0) + plane_bytes((size_t)p.max_slots * H, C, D);
+}
+
 template <class in_t, int D, int C>
 hipError_t launch_backward_t(const BackwardArgs& a) {
-  const size_t NB = (size_t)a.total_chunks * a.H;
+  const BwdPlan plan = plan_backward(a.num_seqs, a.cu_seqlens_host, a.seq_len, a.H, D, C, a.tuning);
+  const BwdCounts sc{a.num_seqs, a.cu_seqlens_host, a.seq_len, C};
+  const size_t nhdd = (size_t)a.num_seqs * a.H * D * D;
   char* ws = reinterpret_cast<char*>(a.workspace);
   Geo geo;
   geo.cu = a.cu_seqlens;
@@ -738,11 +823,16 @@ hipError_t launch_backward_t(const BackwardArgs& a) {
   geo.seq_len = a.seq_len;
   geo.total_tokens = a.total_tokens;
   geo.H = a.H;
-  geo.nchunks = a.total_chunks;
-  Planes p = carve(ws + a256(sizeof(int32_t) * (a.num_seqs + 1)), NB, C, D);
-  if (a.cu_seqlens)
-    hipLaunchKernelGGL(chunk_table_kernel, dim3(1), dim3(1024), 0, a.stream, a.cu_seqlens,
-                       const_cast<int32_t*>(geo.off), a.num_seqs, a.total_tokens, C);
+  geo.L = plan.L;
+  char* after_table = ws + (a.cu_seqlens ? a256(sizeof(int32_t) * (a.num_seqs + 1)) : 0);
+  // States entering segments 1 .. nseg-1, then the carried dS, then planes.
+  float* ckpt = reinterpret_cast<float*>(after_table);
+  float* dcarry = ckpt + (plan.nseg > 1 ? (size_t)(plan.nseg - 1) * nhdd : 0);
+  char* planes = after_table + (plan.nseg > 1 ? a256((size_t)plan.nseg * nhdd * sizeof(float)) : 0);
+  const size_t NBmax = (size_t)plan.max_slots * a.H;
+  Planes p = carve(planes, NBmax, C, D);
+  auto state_in = [&](int s) { return s == 0 ? a.initial_state : ckpt + (size_t)(s - 1) * nhdd; };
+
   const int serial = a.num_seqs * a.H * (D / kCols);
   const size_t flds_s = sizeof(FwdLds<D, C>), blds_s = sizeof(BwdLds<D, C>);
   hipError_t e = hipFuncSetAttribute(reinterpret_cast<const void*>(&bwd_fwd_states_kernel<D, C>),
@@ -751,21 +841,19 @@ hipError_t launch_backward_t(const BackwardArgs& a) {
   e = hipFuncSetAttribute(reinterpret_cast<const void*>(&bwd_bwd_states_kernel<D, C>),
                           hipFuncAttributeMaxDynamicSharedMemorySize, (int)blds_s);
   if (e != hipSuccess) return e;
-  if (NB == 0) {
-    // No tokens: dS0 = dS_N.
-    if (a.d_initial_state && serial > 0)
-      hipLaunchKernelGGL((bwd_bwd_states_kernel<D, C>), dim3(serial), dim3(kSerThreads), blds_s, a.stream,
-                         p, geo, a.d_final_state, a.d_initial_state);
-    return hipGetLastError();
-  }
-  BwdIn in{a.q, a.k, a.v, a.g, a.beta, a.d_o};
-  BwdOut out{a.dq, a.dk, a.dv, a.dg, a.dbeta};
-  hipLaunchKernelGGL((bwd_prep_kernel<in_t, D, C>), dim3(NB), dim3(256), 0, a.stream, in, p, geo);
   const size_t glds = (size_t)3 * C * (D + 1) * sizeof(float);
   e = hipFuncSetAttribute(reinterpret_cast<const void*>(&bwd_gram_kernel<D, C>),
-                                     hipFuncAttributeMaxDynamicSharedMemorySize, (int)glds);
+                          hipFuncAttributeMaxDynamicSharedMemorySize, (int)glds);
   if (e != hipSuccess) return e;
+  const size_t flds = final_lds<D, C>();
+  e = hipFuncSetAttribute(reinterpret_cast<const void*>(&bwd_final_kernel<D, C>),
+                          hipFuncAttributeMaxDynamicSharedMemorySize, (int)flds);
+  if (e != hipSuccess) return e;
+
+  BwdIn in{a.q, a.k, a.v, a.g, a.beta, a.d_o};
+  BwdOut out{a.dq, a.dk, a.dv, a.dg, a.dbeta};
   hipError_t gerr = hipSuccess;
+  size_t NB = 0;
   auto gemm = [&](auto op, const float* A, const float* B, float* Cm, int M, int N, int K,
                   int lda, int ldb, size_t sa, size_t sb, float alpha, int acc_c, int mask) {
     typedef decltype(op) O;
@@ -778,36 +866,70 @@ hipError_t launch_backward_t(const BackwardArgs& a) {
   const GemmNT NT;
   const GemmNN NN;
   const GemmTN TN;
-  // Grams of the moderate-decay chunks, then the others pair by pair.
-  gemm(NT, p.Kt, p.Kh, p.Bm, C, C, D, D, D, scd, scd, 1.f, 0, 2);  // strict_tril(Kt Kh^T)
-  gemm(NT, p.Qt, p.Kh, p.P, C, C, D, D, D, scd, scd, 1.f, 0, 1);   // tril(Qt Kh^T)
-  hipLaunchKernelGGL((bwd_gram_kernel<D, C>), dim3(NB), dim3(256), glds, a.stream, p, (int)NB);
-  hipLaunchKernelGGL((unit_lower_inverse_kernel<C>), dim3(NB), dim3(256), 0, a.stream, p.Bm, p.beta,
-                     p.M, p.T);
-  hipLaunchKernelGGL((bwd_fwd_states_kernel<D, C>), dim3(serial), dim3(kSerThreads), flds_s, a.stream, p,
-                     geo, a.initial_state);
-  hipLaunchKernelGGL((bwd_bwd_states_kernel<D, C>), dim3(serial), dim3(kSerThreads), blds_s, a.stream, p,
-                     geo, a.d_final_state, a.d_initial_state);
-  // p.S and p.dSn are [D][D] per chunk and head: the B operand "rows" are the
-  // key channels, contracted over the value columns.
-  gemm(NT, p.dO, p.S, p.dQt, C, D, D, D, D, scd, sdd, 1.f, 0, 0);   // dQt = dO S^T
-  gemm(NT, p.U, p.dSn, p.dKb, C, D, D, D, D, scd, sdd, 1.f, 0, 0);  // dKb = U dS'^T
-  gemm(NT, p.dR, p.S, p.dKt, C, D, D, D, D, scd, sdd, -1.f, 0, 0);  // dKt = -dR S^T
-  gemm(NT, p.dU, p.R, p.dT, C, C, D, D, D, scd, scd, 1.f, 0, 0);    // dT = dU R^T
-  gemm(NT, p.dO, p.U, p.dP, C, C, D, D, D, scd, scd, 1.f, 0, 1);    // dP = tril(dO U^T)
-  hipLaunchKernelGGL((bwd_cc_kernel<C>), dim3(NB), dim3(256), 0, a.stream, p);
-  // Pairwise gradient terms of the moderate-decay chunks (R, U, dU are free).
-  gemm(NN, p.dBm, p.Kh, p.R, C, D, C, C, D, scc, scd, 1.f, 0, 0);   // Y1 = dBm Kh
-  gemm(NN, p.dP, p.Kh, p.U, C, D, C, C, D, scc, scd, 1.f, 0, 0);    // Y2 = dP Kh
-  gemm(TN, p.dBm, p.Kt, p.dU, C, D, C, C, D, scc, scd, 1.f, 0, 0);  // Y3 = dBm^T Kt
-  gemm(TN, p.dP, p.Qt, p.dU, C, D, C, C, D, scc, scd, 1.f, 1, 0);   //    + dP^T Qt
+  // Segment s: its geometry, then prep, the Grams, the inverse (through the
+  // forward operands of the serial pass); `grams_p` adds P.
+  auto segment_setup = [&](int s, bool grams_p) {
+    geo.c0 = s * plan.L;
+    const long long slots = sc.slots(geo.c0, plan.L);
+    NB = (size_t)slots * a.H;
+    geo.nchunks = (int)slots;
+    if (a.cu_seqlens) {
+      hipLaunchKernelGGL(chunk_table_kernel, dim3(1), dim3(1024), 0, a.stream, a.cu_seqlens,
+                         const_cast<int32_t*>(geo.off), a.num_seqs, a.total_tokens, C, geo.c0, plan.L);
+      geo.slot_cnt = 0;
+    } else {
+      const int c = sc.nch(0) - geo.c0;
+      geo.slot_cnt = c <= 0 ? 0 : (c < plan.L ? c : plan.L);
+    }
+    if (NB == 0) return;
+    hipLaunchKernelGGL((bwd_prep_kernel<in_t, D, C>), dim3(NB), dim3(256), 0, a.stream, in, p, geo);
+    // Grams of the moderate-decay chunks, then the others pair by pair.
+    gemm(NT, p.Kt, p.Kh, p.Bm, C, C, D, D, D, scd, scd, 1.f, 0, 2);    // strict_tril(Kt Kh^T)
+    if (grams_p) gemm(NT, p.Qt, p.Kh, p.P, C, C, D, D, D, scd, scd, 1.f, 0, 1);  // tril(Qt Kh^T)
+    hipLaunchKernelGGL((bwd_gram_kernel<D, C>), dim3(NB), dim3(256), glds, a.stream, p, (int)NB);
+    hipLaunchKernelGGL((unit_lower_inverse_kernel<C>), dim3(NB), dim3(256), 0, a.stream, p.Bm, p.beta,
+                       p.M, p.T);
+  };
+  // Forward sweep: the state entering every segment after the first (only
+  // the serial forward pass of each segment is needed for it).
+  for (int s = 0; s + 1 < plan.nseg; ++s) {
+    segment_setup(s, false);
+    if (serial > 0)
+      hipLaunchKernelGGL((bwd_fwd_states_kernel<D, C>), dim3(serial), dim3(kSerThreads), flds_s, a.stream,
+                         p, geo, state_in(s), ckpt + (size_t)s * nhdd);
+  }
+  // Backward sweep, last segment first; dS crosses segments in dcarry.
+  for (int s = plan.nseg - 1; s >= 0; --s) {
+    segment_setup(s, true);
+    const float* ds_in = s == plan.nseg - 1 ? a.d_final_state : dcarry;
+    float* ds_out = s == 0 ? a.d_initial_state : dcarry;
+    if (serial > 0) {
+      if (NB > 0)
+        hipLaunchKernelGGL((bwd_fwd_states_kernel<D, C>), dim3(serial), dim3(kSerThreads), flds_s, a.stream,
+                           p, geo, state_in(s), static_cast<float*>(nullptr));
+      // (with no chunk in the segment this only hands dS through)
+      hipLaunchKernelGGL((bwd_bwd_states_kernel<D, C>), dim3(serial), dim3(kSerThreads), blds_s, a.stream,
+                         p, geo, ds_in, ds_out);
+    }
+    if (NB == 0) continue;
+    // p.S and p.dSn are [D][D] per chunk and head: the B operand "rows" are
+    // the key channels, contracted over the value columns.
+    gemm(NT, p.dO, p.S, p.dQt, C, D, D, D, D, scd, sdd, 1.f, 0, 0);   // dQt = dO S^T
+    gemm(NT, p.U, p.dSn, p.dKb, C, D, D, D, D, scd, sdd, 1.f, 0, 0);  // dKb = U dS'^T
+    gemm(NT, p.dR, p.S, p.dKt, C, D, D, D, D, scd, sdd, -1.f, 0, 0);  // dKt = -dR S^T
+    gemm(NT, p.dU, p.R, p.dT, C, C, D, D, D, scd, scd, 1.f, 0, 0);    // dT = dU R^T
+    gemm(NT, p.dO, p.U, p.dP, C, C, D, D, D, scd, scd, 1.f, 0, 1);    // dP = tril(dO U^T)
+    hipLaunchKernelGGL((bwd_cc_kernel<C>), dim3(NB), dim3(256), 0, a.stream, p);
+    // Pairwise gradient terms of the moderate-decay chunks (R, U, dU are free).
+    gemm(NN, p.dBm, p.Kh, p.R, C, D, C, C, D, scc, scd, 1.f, 0, 0);   // Y1 = dBm Kh
+    gemm(NN, p.dP, p.Kh, p.U, C, D, C, C, D, scc, scd, 1.f, 0, 0);    // Y2 = dP Kh
+    gemm(TN, p.dBm, p.Kt, p.dU, C, D, C, C, D, scc, scd, 1.f, 0, 0);  // Y3 = dBm^T Kt
+    gemm(TN, p.dP, p.Qt, p.dU, C, D, C, C, D, scc, scd, 1.f, 1, 0);   //    + dP^T Qt
+    if (gerr != hipSuccess) return gerr;
+    hipLaunchKernelGGL((bwd_final_fast_kernel<D, C>), dim3(NB), dim3(D), 0, a.stream, p, geo, out);
+    hipLaunchKernelGGL((bwd_final_kernel<D, C>), dim3(NB), dim3(2 * D), flds, a.stream, p, geo, out);
+  }
   if (gerr != hipSuccess) return gerr;
-  hipLaunchKernelGGL((bwd_final_fast_kernel<D, C>), dim3(NB), dim3(D), 0, a.stream, p, geo, out);
-  const size_t flds = final_lds<D, C>();
-  e = hipFuncSetAttribute(reinterpret_cast<const void*>(&bwd_final_kernel<D, C>),
-                          hipFuncAttributeMaxDynamicSharedMemorySize, (int)flds);
-  if (e != hipSuccess) return e;
-  hipLaunchKernelGGL((bwd_final_kernel<D, C>), dim3(NB), dim3(2 * D), flds, a.stream, p, geo, out);
   return hipGetLastError();
 }
 
@@ -825,9 +947,11 @@ hipError_t launch_backward_i(const BackwardArgs& a) {
 
 }  // namespace
 
-size_t backward_workspace_bytes(long long total_chunks, int num_seqs, int H, int D, int chunk) {
-  return a256(sizeof(int32_t) * (size_t)(num_seqs + 1)) +
-         plane_bytes((size_t)total_chunks * H, chunk, D);
+size_t backward_workspace_bytes(int num_seqs, const int32_t* cu_host, int seq_len, int H, int D, int chunk,
+                                const PrefillTuning& tuning) {
+  const BwdPlan plan = plan_backward(num_seqs, cu_host, seq_len, H, D, chunk, tuning);
+  if (plan.nseg == 0) return SIZE_MAX;
+  return bwd_bytes(plan, num_seqs, cu_host != nullptr, H, D, chunk);
 }
 
 hipError_t launch_backward(const BackwardArgs& a) {

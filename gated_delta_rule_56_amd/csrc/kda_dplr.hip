@@ -360,10 +360,13 @@ hipError_t launch_dplr_t(const DplrArgs& a) {
   geo.total_tokens = a.total_tokens;
   geo.H = a.H;
   geo.nchunks = a.total_chunks;
+  geo.c0 = 0;  // one pass over every chunk
+  geo.L = INT32_MAX / 2;
+  geo.slot_cnt = a.cu_seqlens ? 0 : (a.seq_len + C - 1) / C;
   DPlanes p = dcarve(ws + a256(sizeof(int32_t) * (a.num_seqs + 1)), NB, C, D);
   if (a.cu_seqlens)
     hipLaunchKernelGGL(chunk_table_kernel, dim3(1), dim3(1024), 0, a.stream, a.cu_seqlens,
-                       const_cast<int32_t*>(geo.off), a.num_seqs, a.total_tokens, C);
+                       const_cast<int32_t*>(geo.off), a.num_seqs, a.total_tokens, C, 0, INT32_MAX / 2);
   const int serial = a.num_seqs * a.H * (D / kColsD);
   const size_t slds = sizeof(StLds<D, C>);
   hipError_t e = hipFuncSetAttribute(reinterpret_cast<const void*>(&dplr_states_kernel<D, C, TIED>),

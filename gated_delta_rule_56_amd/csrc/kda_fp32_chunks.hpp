@@ -11,12 +11,17 @@ namespace {
 
 size_t a256(size_t x) { return (x + 255) / 256 * 256; }
 
-// Sequence geometry.  Fixed length: num_seqs sequences of seq_len tokens;
-// varlen: cu (device) and off[n] = first global chunk of sequence n.
+// Sequence geometry of a pass over the local chunks [c0, c0 + L) of every
+// sequence (a segment; c0 = 0 and L past every sequence's length for a whole
+// pass).  The pass's planes hold those chunks in order: sequence n's chunk
+// ci sits at plane slot base(n) + ci - c0, with base(n) = off[n] (varlen:
+// cu on the device, off from chunk_table_kernel) or n * slot_cnt (fixed
+// length: num_seqs sequences of seq_len tokens).
 struct Geo {
   const int32_t* cu;
   const int32_t* off;  // varlen only
   int num_seqs, seq_len, total_tokens, H, nchunks;
+  int c0, L, slot_cnt;
 };
 
 __device__ __forceinline__ int clampi(int x, int lo, int hi) { return x < lo ? lo : (x > hi ? hi : x); }
@@ -30,11 +35,19 @@ __device__ __forceinline__ void seq_of(const Geo& g, int n, int& bos, int& eos, 
   } else {
     bos = n * g.seq_len;
     eos = bos + g.seq_len;
-    base = n * ((g.seq_len + C - 1) / C);
+    base = n * g.slot_cnt;
   }
 }
 
-// Global chunk -> (sequence, first token, length).
+// The pass's chunks [lo, hi) of the sequence [bos, eos).
+template <int C>
+__device__ __forceinline__ void seg_range(const Geo& g, int bos, int eos, int& lo, int& hi) {
+  const int nch = (eos - bos + C - 1) / C;
+  lo = min(g.c0, nch);
+  hi = min(g.c0 + g.L, nch);
+}
+
+// Plane slot -> (sequence, first token, length).
 template <int C>
 __device__ __forceinline__ void chunk_of(const Geo& g, int gch, int& n, int& t0, int& len) {
   if (g.cu) {
@@ -48,25 +61,26 @@ __device__ __forceinline__ void chunk_of(const Geo& g, int gch, int& n, int& t0,
     }
     n = lo;
   } else {
-    n = clampi(gch / ((g.seq_len + C - 1) / C), 0, g.num_seqs - 1);
+    n = clampi(gch / max(g.slot_cnt, 1), 0, g.num_seqs - 1);
   }
   int bos, eos, base;
   seq_of<C>(g, n, bos, eos, base);
-  t0 = clampi(bos + (gch - base) * C, bos, eos);
+  t0 = clampi(bos + (g.c0 + gch - base) * C, bos, eos);
   len = clampi(eos - t0, 0, C);
 }
 
-// off[n] = sum of the chunk counts of the sequences before n (block scan).
+// off[n] = the pass's chunk counts of the sequences before n (block scan):
+// sequence n contributes its local chunks in [c0, c0 + L).
 __global__ __launch_bounds__(1024) void chunk_table_kernel(const int32_t* __restrict__ cu,
                                                          int32_t* __restrict__ off, int num_seqs,
-                                                         int total_tokens, int C) {
+                                                         int total_tokens, int C, int c0, int L) {
   __shared__ int part[1024];
   const int t = threadIdx.x;
   const int per = (num_seqs + 1023) / 1024;
   const int n0 = t * per, n1 = min(n0 + per, num_seqs);
   auto nch = [&](int n) {
     const int b = clampi(cu[n], 0, total_tokens), e = clampi(cu[n + 1], b, total_tokens);
-    return (e - b + C - 1) / C;
+    return clampi((e - b + C - 1) / C - c0, 0, L);
   };
   int s = 0;
   for (int n = n0; n < n1; ++n) s += nch(n);

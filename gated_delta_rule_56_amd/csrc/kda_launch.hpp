@@ -109,16 +109,21 @@ struct BackwardArgs {
   float *dq, *dk, *dv, *dg, *dbeta;
   float* d_initial_state;      // or nullptr (not written)
   const int32_t* cu_seqlens;   // device, or nullptr => num_seqs sequences of seq_len
+  const int32_t* cu_seqlens_host;  // host copy (varlen), for the segment plan
   int num_seqs, seq_len, total_tokens, total_chunks;
   int H, D, chunk;
   bool in_bf16;
+  PrefillTuning tuning;  // segment_chunks / segment_bytes (value_block unused)
   void* workspace;
   hipStream_t stream;
 };
 
-// Workspace of the backward pass: the first chunk of each sequence, then the
-// fp32 per-(chunk, head) planes of every chunk (no segmenting).
-size_t backward_workspace_bytes(long long total_chunks, int num_seqs, int H, int D, int chunk);
+// Workspace of the backward pass, which runs in segments of local chunks:
+// the segment's slot table (varlen), the states entering segments 1.. and
+// the carried dS (more than one segment), and one segment's fp32
+// per-(chunk, head) planes.  SIZE_MAX if no plan fits.
+size_t backward_workspace_bytes(int num_seqs, const int32_t* cu_host, int seq_len, int H, int D, int chunk,
+                                const PrefillTuning& tuning);
 hipError_t launch_backward(const BackwardArgs& a);
 
 // General DPLR forward (fp32 chunk pipeline); tied = KDA through the same

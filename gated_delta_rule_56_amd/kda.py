@@ -112,6 +112,11 @@ def load() -> ctypes.CDLL:
     lib.dplr_decode_step.argtypes = [vp] * 8 + [i32] * 6 + [vp]
     lib.dplr_decode_step.restype = i32
     op = ctypes.POINTER(PrefillOptions)
+    lib.kda_backward_workspace_size_ex.argtypes = [i32, i32, i32, i32, i32, i32, vp, i32, op,
+                                                   ctypes.POINTER(sz)]
+    lib.kda_backward_workspace_size_ex.restype = i32
+    lib.kda_backward_ex.argtypes = [vp] * 16 + [i32] * 8 + [op, vp, sz, vp]
+    lib.kda_backward_ex.restype = i32
     lib.kda_prefill_workspace_size_ex.argtypes = [i32, i32, i32, i32, i32, i32, i32, vp, i32, i32,
                                                   vp, op, ctypes.POINTER(sz)]
     lib.kda_prefill_workspace_size_ex.restype = i32
@@ -555,18 +560,26 @@ def _decode(q, k, v, g, beta, state, out_dtype, o, layer):
 
 
 def backward_workspace_size(B: int, T: int, H: int, D: int, num_seqs: int, chunk_size: int,
-                            cu_seqlens_host: Optional[np.ndarray] = None) -> int:
+                            cu_seqlens_host: Optional[np.ndarray] = None, options=None) -> int:
+    """Bytes of ``kda_backward``'s workspace; ``options`` (segment_chunks,
+    segment_bytes) as for :func:`backward`."""
     out = ctypes.c_size_t(0)
     cu_p = None if cu_seqlens_host is None else cu_seqlens_host.ctypes.data
-    _check(load().kda_backward_workspace_size(B, T, H, D, D, num_seqs, cu_p, chunk_size,
-                                              ctypes.byref(out)), "kda_backward_workspace_size")
+    if options is None:
+        _check(load().kda_backward_workspace_size(B, T, H, D, D, num_seqs, cu_p, chunk_size,
+                                                  ctypes.byref(out)), "kda_backward_workspace_size")
+    else:
+        o = _options(options)
+        _check(load().kda_backward_workspace_size_ex(B, T, H, D, D, num_seqs, cu_p, chunk_size,
+                                                     ctypes.byref(o), ctypes.byref(out)),
+               "kda_backward_workspace_size_ex")
     return out.value
 
 
 def backward(q, k, v, g, beta, d_o, initial_state=None, d_final_state=None, cu_seqlens=None, *,
              cu_seqlens_host: Optional[Union[Sequence[int], np.ndarray]] = None,
              chunk_size: int = 64, output_d_initial_state: bool = True, workspace=None,
-             out=None):
+             out=None, options=None):
     """Backward of :func:`prefill` (``kda_backward``): gradients of
     ``sum(d_o * o) + sum(d_final_state * final_state)`` with respect to q, k,
     v, g, beta and the initial state.  Shapes as in :func:`prefill`; d_o
@@ -624,14 +637,18 @@ def backward(q, k, v, g, beta, d_o, initial_state=None, d_final_state=None, cu_s
         _expect(name, t, shp)
         if t is not None and (t.dtype != torch.float32 or not t.is_contiguous()):
             raise KDAError(f"{name} must be contiguous float32")
-    ws_bytes = backward_workspace_size(B, T, H, D, N, chunk_size, cu_h)
+    ws_bytes = backward_workspace_size(B, T, H, D, N, chunk_size, cu_h, options)
     workspace = _workspace(workspace, ws_bytes, q.device)
     cu_hp = None if cu_h is None else cu_h.ctypes.data
-    _check(load().kda_backward(
-        _ptr(q), _ptr(k), _ptr(v), _ptr(g), _ptr(beta), _ptr(initial_state), _ptr(d_o),
-        _ptr(d_final_state), _ptr(dq), _ptr(dk), _ptr(dv), _ptr(dg), _ptr(db), _ptr(ds0),
-        _ptr(cu_seqlens), cu_hp, B, T, H, D, Dv, N, chunk_size, in_code,
-        _ptr(workspace), workspace.numel(), _stream_ptr(q.device)), "kda_backward")
+    args = (_ptr(q), _ptr(k), _ptr(v), _ptr(g), _ptr(beta), _ptr(initial_state), _ptr(d_o),
+            _ptr(d_final_state), _ptr(dq), _ptr(dk), _ptr(dv), _ptr(dg), _ptr(db), _ptr(ds0),
+            _ptr(cu_seqlens), cu_hp, B, T, H, D, Dv, N, chunk_size, in_code)
+    tail = (_ptr(workspace), workspace.numel(), _stream_ptr(q.device))
+    if options is None:
+        _check(load().kda_backward(*args, *tail), "kda_backward")
+    else:
+        o = _options(options)
+        _check(load().kda_backward_ex(*args, ctypes.byref(o), *tail), "kda_backward_ex")
     return dq, dk, dv, dg, db, ds0
 
 

@@ -376,9 +376,21 @@ kda_status kda_decode_step_layer(const void* q_pre, const void* k_pre,
  *   dbeta          [B*T, H] float32 (written)
  *   d_initial_state [num_seqs, H, Dk, Dv] float32, or NULL (not written)
  *   workspace      at least kda_backward_workspace_size bytes, 256-byte
- *                  aligned: about 737 KB of fp32 intermediates per chunk and
- *                  head at Dk = Dv = 128, C = 64, for every chunk (the
- *                  backward does not run in segments).
+ *                  aligned.  The backward runs in segments of local chunks
+ *                  of every sequence, as kda_prefill does: a forward sweep
+ *                  keeps only the state entering each segment, and the
+ *                  backward sweep (last segment first) recomputes one
+ *                  segment's fp32 intermediates (about 737 KB per chunk and
+ *                  head at Dk = Dv = 128, C = 64) before its gradients.  The
+ *                  segment length is chosen so that those fit 4 GiB; the
+ *                  workspace adds the per-segment states (num_seqs x H x Dk
+ *                  x Dv fp32 each) when there is more than one segment.  An
+ *                  input that fits one segment runs as one pass.
+ *
+ * kda_backward_ex / kda_backward_workspace_size_ex take a
+ * kda_prefill_options (NULL = automatic): segment_chunks fixes the segment
+ * length, segment_bytes the budget of one segment's intermediates;
+ * value_block must be 0.  The workspace size depends only on the arguments.
  */
 kda_status kda_backward_workspace_size(int B, int T, int H, int Dk, int Dv,
                                        int num_seqs,
@@ -395,6 +407,26 @@ kda_status kda_backward(const void* q, const void* k, const void* v,
                         int Dk, int Dv, int num_seqs, int chunk_size,
                         kda_dtype in_dtype, void* workspace,
                         size_t workspace_bytes, void* stream /* hipStream_t */);
+
+kda_status kda_backward_workspace_size_ex(int B, int T, int H, int Dk, int Dv,
+                                          int num_seqs,
+                                          const int32_t* cu_seqlens_host,
+                                          int chunk_size,
+                                          const kda_prefill_options* options,
+                                          size_t* bytes);
+
+kda_status kda_backward_ex(const void* q, const void* k, const void* v,
+                           const float* g, const float* beta,
+                           const float* initial_state, const float* d_o,
+                           const float* d_final_state, float* dq, float* dk,
+                           float* dv, float* dg, float* dbeta,
+                           float* d_initial_state, const int32_t* cu_seqlens,
+                           const int32_t* cu_seqlens_host, int B, int T, int H,
+                           int Dk, int Dv, int num_seqs, int chunk_size,
+                           kda_dtype in_dtype,
+                           const kda_prefill_options* options, void* workspace,
+                           size_t workspace_bytes,
+                           void* stream /* hipStream_t */);
 
 /*
  * General diagonal-plus-low-rank (DPLR) recurrence, chunked forward pass:

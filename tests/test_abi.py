@@ -304,3 +304,41 @@ def test_binding_output_dtype_and_layout():
     # a workspace must be a contiguous byte buffer
     with pytest.raises(kda.KDAError, match="GPU tensor|workspace"):
         kda.prefill(q, k, v, g, b, workspace=torch.zeros(16, dtype=torch.float32))
+
+
+def _a256(x):
+    return (x + 255) // 256 * 256
+
+
+def _bwd_planes(nb, C, D):
+    # fp32 per-(chunk, head) planes of one backward segment: sixteen [C x D],
+    # seven [C x C], two [D x D], two [C], one [D] and one flag each
+    return (16 * _a256(nb * C * D * 4) + 7 * _a256(nb * C * C * 4) + 2 * _a256(nb * D * D * 4)
+            + 2 * _a256(nb * C * 4) + _a256(nb * D * 4) + _a256(nb * 4))
+
+
+def test_backward_workspace_segments(lib):
+    # T=4096, H=32, D=128, C=64: 64 chunks x 32 heads of planes fit one 4 GiB
+    # segment, so the backward is one pass with no stored states.
+    n = kda.backward_workspace_size(1, 4096, 32, 128, 1, 64)
+    assert n == _bwd_planes(64 * 32, 64, 128)
+    # forced 16-chunk segments: four segments, the states entering segments
+    # 1..3 and the carried dS (4 x 32 x 128 x 128 fp32), one segment's planes
+    n = kda.backward_workspace_size(1, 4096, 32, 128, 1, 64, options={"segment_chunks": 16})
+    assert n == 4 * 32 * 128 * 128 * 4 + _bwd_planes(16 * 32, 64, 128)
+    # T=65536, H=8: 1024 chunks; the largest segment whose planes fit 4 GiB,
+    # evened out: two segments of 512 chunks
+    n = kda.backward_workspace_size(1, 65536, 8, 128, 1, 64)
+    assert n == 2 * 8 * 128 * 128 * 4 + _bwd_planes(512 * 8, 64, 128)
+    assert _bwd_planes(512 * 8, 64, 128) <= 4 << 30 < _bwd_planes(1024 * 8, 64, 128)
+    # a budget of one chunk's planes per head and sequence: 1-chunk segments
+    one = _bwd_planes(8, 64, 128)
+    n = kda.backward_workspace_size(1, 640, 8, 128, 1, 64, options={"segment_bytes": one})
+    assert n == 10 * 8 * 128 * 128 * 4 + one
+    # varlen: lengths 100, 0, 200 at C=16 -> 7, 0, 13 chunks; 5-chunk segments
+    # hold at most 5 + 5 slots; three segments; plus the slot table
+    cu = np.array([0, 100, 100, 300], dtype=np.int32)
+    n = kda.backward_workspace_size(1, 300, 4, 64, 3, 16, cu, options={"segment_chunks": 5})
+    assert n == 256 + _a256(3 * 3 * 4 * 64 * 64 * 4) + _bwd_planes(10 * 4, 16, 64)
+    with pytest.raises(kda.KDAError):
+        kda.backward_workspace_size(1, 4096, 32, 128, 1, 64, options={"value_block": 16})
