@@ -265,12 +265,22 @@ def backward_workload(torch, kda, I, dev):
     # inputs q, k, v bf16, g, beta, d_o fp32; outputs dq, dk, dv, dg, dbeta
     # fp32; initial state, final-state gradient and its result
     by = T * H * (3 * 2 * d + 4 * d + 4 + 4 * d + 4 * 4 * d + 4) + 3 * H * d * d * 4
+    # the same with half the key channels decaying at alpha near 0.1 per token
+    rng = np.random.default_rng(5006)
+    x = I.draw_mixed_decay_tokens(rng, T, H, d, d, "bf16", alpha=0.1)
+    qm, km, vm = (torch.from_numpy(np.ascontiguousarray(a)).to(dev).to(torch.bfloat16)[None]
+                  for a in (x.q, x.k, x.v))
+    gm, bm = (torch.from_numpy(np.ascontiguousarray(a)).to(dev)[None] for a in (x.g, x.beta))
+    tm = time_calls(torch, lambda: kda.backward(qm, km, vm, gm, bm, do, s0, dF, chunk_size=P_C,
+                                                workspace=ws, out=outs), 3)
     return {"workload": f"kda_backward B=1 H={H} T={T} d={d} chunk {P_C}, bf16 q/k/v, fp32 "
                         "gradients, initial state and final-state gradient",
             "ms_per_call": round(t * 1e3, 3), "tokens_per_s": round(T / t, 1),
             "algorithmic_GBps": round(by / t / 1e9, 1),
             "hbm_frac": round(by / t / 1e9 / HBM_PEAK_GBS, 4),
-            "workspace_bytes": int(ws.numel())}
+            "workspace_bytes": int(ws.numel()),
+            "mixed_decay_alpha_0.1_ms_per_call": round(tm * 1e3, 3),
+            "mixed_decay_over_workload": round(tm / t, 3)}
 
 
 def layer_workloads(torch, kda, I, dev):

@@ -32,8 +32,9 @@
 // holds to rounding in fp32, and every pairwise sum is a product with
 // Kh = K*exp(-Gamma): Bm = strict_tril(Kt Kh^T), P = tril(Qt Kh^T), and the
 // pairwise gradient terms come from Y1 = dBm Kh, Y2 = dP Kh and
-// Y3 = dBm^T Kt + dP^T Qt.  Other chunks evaluate every pair with the exact
-// exponent of its difference.
+// Y3 = dBm^T Kt + dP^T Qt.  Other chunks are factored per 16-row tile, with
+// one per-channel factor bridging each pair of tiles (see
+// bwd_gram_tile_kernel), still on the matrix units.
 //
 // Kernels (one launch each, in order):
 //   chunk_table_kernel    first global chunk of each packed sequence
@@ -41,16 +42,16 @@
 //                         Kb, Kh and the span verdict
 //   fp32_gemm_kernel      batched fp32 products (Grams, contractions over value
 //                         columns, pairwise gradient terms)
-//   bwd_gram_kernel       per strong-decay (chunk, head): Bm and P pair by pair
+//   bwd_gram_tile_kernel  per strong-decay (chunk, head): Bm and P, tile-factored
 //   unit_lower_inverse_kernel per (chunk, head): M = (I + Diag(beta) Bm)^-1, T
 //   bwd_fwd_states_kernel per (sequence, head, 16 value columns), serial over
 //                         chunks: the entering state S of every chunk, R, U
 //   bwd_bwd_states_kernel the same, reverse: dS' of every chunk, dU, dR, dS0
 //   bwd_cc_kernel         per (chunk, head): the C x C algebra of M and A
-//   bwd_final_fast_kernel per moderate-decay (chunk, head): decays, reverse
-//                         cumsum, scatter to the token-major outputs
-//   bwd_final_kernel      the same for strong-decay chunks, with the pairwise
-//                         gradient terms evaluated pair by pair
+//   bwd_pairs_tile_kernel per strong-decay (chunk, head): the pairwise
+//                         gradient terms, tile-factored
+//   bwd_final_fast_kernel per (chunk, head): decays, reverse cumsum, scatter
+//                         to the token-major outputs
 #include "kda_device.hpp"
 #include "kda_fp32_chunks.hpp"
 #include "kda_launch.hpp"
@@ -187,43 +188,218 @@ __global__ __launch_bounds__(256) void bwd_prep_kernel(BwdIn in, Planes p, Geo g
   }
 }
 
-// Bm (strictly lower) and P (lower) with the exact exponent of every pair,
-// for strong-decay chunks.
-// Lane = row r; the four waves step through the columns i.
+// Strong-decay chunks (span > kSpan) are factored per 16-row tile, as the
+// forward prefill does.  With Gamma_s(a) the cumulative decay before tile a
+// and Gamma_e(b) at the end of tile b, for rows r of tile a and columns i of
+// tile b <= a,
+//   exp(Gamma_r - Gamma_i) = exp(Gamma_r - Gamma_s(a)) f_ab exp(Gamma_e(b) - Gamma_i),
+//   f_ab = exp(Gamma_s(a) - Gamma_e(b)),
+// all three factors <= 1 off the diagonal; on the diagonal f_aa =
+// exp(-(span of tile a)) >= 1, which stays in range up to a tile span of
+// kTileSpan; a diagonal block beyond that is summed pair by pair with the
+// exact exponent.  The tile operands, in LDS:
+//   Kr, Qr  rows scaled by exp(Gamma_r - Gamma_s(a))   [C][D + 4]
+//   Kc      K scaled by exp(Gamma_e(b) - Gamma_i)      [C][D + 4]
+constexpr float kTileSpan = 64.f;
+
 template <int D, int C>
-__global__ __launch_bounds__(256) void bwd_gram_kernel(Planes p, int NB) {
-  extern __shared__ float sm[];
-  float* Ks = sm;                  // [C][D + 1]
-  float* Qs = Ks + C * (D + 1);
-  float* Gs = Qs + C * (D + 1);
-  const int b = blockIdx.x;
-  if (p.fast[b]) return;  // formed as a product
-  const size_t pcd = (size_t)b * C * D;
-  for (int idx = threadIdx.x; idx < C * D; idx += 256) {
-    const int r = idx / D, c = idx % D;
-    Ks[r * (D + 1) + c] = p.K[pcd + idx];
-    Qs[r * (D + 1) + c] = p.Q[pcd + idx];
-    Gs[r * (D + 1) + c] = p.Gam[pcd + idx];
+struct TileLds {
+  static constexpr int NT = C / 16, SD = D + 4, SC = C + 4;
+  float Kr[C][SD], Qr[C][SD], Kc[C][SD];
+  float Gs[NT][D], Ge[NT][D];  // Gamma before tile t and at its end
+  float dBm[C][SC], dP[C][SC];  // the final stage only
+};
+
+// The tile operands of item b, and whether each diagonal tile spans more
+// than kTileSpan on some channel (bad[t], wave-uniform after the barrier).
+template <int D, int C>
+__device__ __forceinline__ void tile_operands(const Planes& p, size_t b, TileLds<D, C>& L, bool* bad) {
+  constexpr int NT = C / 16;
+  const size_t pcd = b * C * D;
+  for (int idx = threadIdx.x; idx < NT * D; idx += 256) {
+    const int t = idx / D, c = idx % D;
+    L.Gs[t][c] = t == 0 ? 0.f : p.Gam[pcd + (size_t)(16 * t - 1) * D + c];
+    L.Ge[t][c] = p.Gam[pcd + (size_t)(16 * t + 15) * D + c];
   }
   __syncthreads();
-  const int r = threadIdx.x & 63, w = threadIdx.x >> 6;
-  if (r >= C) return;
-  const size_t pcc = (size_t)b * C * C;
-  for (int i = w; i < C; i += 4) {
-    float sb = 0.f, sp = 0.f;
-    if (i <= r) {
-      for (int c = 0; c < D; ++c) {
-        const float e = __expf(Gs[r * (D + 1) + c] - Gs[i * (D + 1) + c]);
-        const float ki = Ks[i * (D + 1) + c] * e;
-        sb += Ks[r * (D + 1) + c] * ki;
-        sp += Qs[r * (D + 1) + c] * ki;
+  for (int idx = threadIdx.x; idx < C * D; idx += 256) {
+    const int r = idx / D, c = idx % D, t = r / 16;
+    const float g = p.Gam[pcd + idx], k = p.K[pcd + idx], q = p.Q[pcd + idx];
+    const float er = __expf(g - L.Gs[t][c]);
+    L.Kr[r][c] = k * er;
+    L.Qr[r][c] = q * er;
+    L.Kc[r][c] = k * __expf(L.Ge[t][c] - g);
+  }
+  // Every thread reads the tile spans itself (same verdict in every wave).
+  for (int t = 0; t < NT; ++t) {
+    bool big = false;
+    for (int c = lane_id(); c < D; c += 64) big |= L.Ge[t][c] - L.Gs[t][c] < -kTileSpan;
+    bad[t] = __any(big);
+  }
+  __syncthreads();
+}
+
+// Bm (strictly lower) and P (lower) of the strong-decay chunks, block by
+// block on v_mfma_f32_16x16x4f32: the column operand of block (a, b) is Kc
+// of tile b times f_ab per channel.  Four waves share the blocks.
+template <int D, int C>
+__global__ __launch_bounds__(256) void bwd_gram_tile_kernel(Planes p) {
+  extern __shared__ float sm[];
+  TileLds<D, C>& L = *reinterpret_cast<TileLds<D, C>*>(sm);
+  constexpr int NT = C / 16, NBLK = NT * (NT + 1) / 2;
+  const size_t b = blockIdx.x;
+  if (p.fast[b]) return;  // formed as a product
+  bool bad[NT];
+  tile_operands<D, C>(p, b, L, bad);
+  const int w = wave_id(), l = lane_id(), m = l & 15, g = l >> 4;
+  const size_t pcc = b * C * C;
+  for (int blk = w; blk < NBLK; blk += 4) {
+    int ta = 0;
+    while ((ta + 1) * (ta + 2) / 2 <= blk) ++ta;
+    const int tb = blk - ta * (ta + 1) / 2;  // tb <= ta
+    f32x4 accB = {0, 0, 0, 0}, accP = {0, 0, 0, 0};
+    if (tb < ta || !bad[ta]) {
+#pragma unroll 4
+      for (int k0 = 0; k0 < D; k0 += 4) {
+        const int c = k0 + g;
+        const float kc = L.Kc[16 * tb + m][c] * __expf(L.Gs[ta][c] - L.Ge[tb][c]);
+        accB = mfma4(L.Kr[16 * ta + m][c], kc, accB);
+        accP = mfma4(L.Qr[16 * ta + m][c], kc, accP);
+      }
+    } else {
+      // tile span beyond kTileSpan: each pair with its exact exponent
+#pragma unroll
+      for (int x = 0; x < 4; ++x) {
+        const size_t rr = 16 * ta + 4 * g + x, ii = 16 * tb + m;
+        float sb = 0.f, sp = 0.f;
+        if (ii <= rr) {
+          for (int c = 0; c < D; ++c) {
+            const float e = __expf(p.Gam[(b * C + rr) * D + c] - p.Gam[(b * C + ii) * D + c]);
+            const float ki = p.K[(b * C + ii) * D + c] * e;
+            sb += p.K[(b * C + rr) * D + c] * ki;
+            sp += p.Q[(b * C + rr) * D + c] * ki;
+          }
+        }
+        accB[x] = sb;
+        accP[x] = sp;
       }
     }
-    p.Bm[pcc + r * C + i] = i < r ? sb : 0.f;
-    p.P[pcc + r * C + i] = i <= r ? sp : 0.f;
+    // lane (m, g) holds rows 4 g + x of column m of the block
+#pragma unroll
+    for (int x = 0; x < 4; ++x) {
+      const int r = 16 * ta + 4 * g + x, i = 16 * tb + m;
+      p.Bm[pcc + r * C + i] = i < r ? accB[x] : 0.f;
+      p.P[pcc + r * C + i] = i <= r ? accP[x] : 0.f;
+    }
+  }
+  // blocks above the diagonal
+  for (int idx = threadIdx.x; idx < C * C; idx += 256) {
+    const int r = idx / C, i = idx % C;
+    if (i / 16 > r / 16) {
+      p.Bm[pcc + idx] = 0.f;
+      p.P[pcc + idx] = 0.f;
+    }
   }
 }
 
+// The pairwise gradient terms of the strong-decay chunks, as the exact sums
+//   Z1[r,c] = sum_{i<r} dBm[r,i] k_ic e_ric,  Z2[r,c] = sum_{i<=r} dP[r,i] k_ic e_ric,
+//   Z3[i,c] = sum_{r>=i} (dBm[r,i] k_rc + dP[r,i] q_rc) e_ric,  e_ric = exp(Gamma_rc - Gamma_ic),
+// into the planes that hold Y1, Y2, Y3 for the factored chunks (R, U, dU).
+// Per output tile: the block products of the tile operands, each block's
+// result scaled column by column by f_ab, then the row factor of the
+// output's own tile.  Four waves share the output tiles.
+template <int D, int C>
+__global__ __launch_bounds__(256) void bwd_pairs_tile_kernel(Planes p) {
+  extern __shared__ float sm[];
+  TileLds<D, C>& L = *reinterpret_cast<TileLds<D, C>*>(sm);
+  constexpr int NT = C / 16, NCT = D / 16;
+  const size_t b = blockIdx.x;
+  if (p.fast[b]) return;  // the products Y1, Y2, Y3
+  const size_t pcc = b * C * C, pcd = b * C * D;
+  for (int idx = threadIdx.x; idx < C * C; idx += 256) {
+    const int r = idx / C, i = idx % C;
+    L.dBm[r][i] = p.dBm[pcc + idx];
+    L.dP[r][i] = p.dP[pcc + idx];
+  }
+  bool bad[NT];
+  tile_operands<D, C>(p, b, L, bad);
+  const int w = wave_id(), l = lane_id(), m = l & 15, g = l >> 4;
+  for (int ot = w; ot < NT * NCT; ot += 4) {
+    const int ta = ot / NCT, ct = ot % NCT;
+    const int c = 16 * ct + m;  // this lane's output channel
+    // Z1, Z2 for rows of tile ta: blocks tb <= ta
+    // z: factored sums (times the row factor at the end); zd: a diagonal
+    // tile summed with exact exponents
+    f32x4 z1 = {0, 0, 0, 0}, z2 = {0, 0, 0, 0}, z1d = {0, 0, 0, 0}, z2d = {0, 0, 0, 0};
+    for (int tb = 0; tb <= ta; ++tb) {
+      if (tb < ta || !bad[ta]) {
+        const float f = __expf(L.Gs[ta][c] - L.Ge[tb][c]);
+        f32x4 y1 = {0, 0, 0, 0}, y2 = {0, 0, 0, 0};
+#pragma unroll
+        for (int k0 = 0; k0 < 16; k0 += 4) {
+          const float kc = L.Kc[16 * tb + k0 + g][c];
+          y1 = mfma4(L.dBm[16 * ta + m][16 * tb + k0 + g], kc, y1);
+          y2 = mfma4(L.dP[16 * ta + m][16 * tb + k0 + g], kc, y2);
+        }
+#pragma unroll
+        for (int x = 0; x < 4; ++x) {
+          z1[x] += f * y1[x];
+          z2[x] += f * y2[x];
+        }
+      } else {
+#pragma unroll
+        for (int x = 0; x < 4; ++x) {
+          const int r = 16 * ta + 4 * g + x;
+          const float gr = p.Gam[pcd + (size_t)r * D + c];
+          for (int i = 16 * tb; i <= r; ++i) {
+            const float ki = p.K[pcd + (size_t)i * D + c] * __expf(gr - p.Gam[pcd + (size_t)i * D + c]);
+            z1d[x] += L.dBm[r][i] * ki;
+            z2d[x] += L.dP[r][i] * ki;
+          }
+        }
+      }
+    }
+#pragma unroll
+    for (int x = 0; x < 4; ++x) {
+      const int r = 16 * ta + 4 * g + x;
+      const float rf = __expf(p.Gam[pcd + (size_t)r * D + c] - L.Gs[ta][c]);
+      p.R[pcd + (size_t)r * D + c] = z1[x] * rf + z1d[x];
+      p.U[pcd + (size_t)r * D + c] = z2[x] * rf + z2d[x];
+    }
+    // Z3 for columns (tokens) of tile ta: blocks tr >= ta (rows r of tile tr)
+    f32x4 z3 = {0, 0, 0, 0}, z3d = {0, 0, 0, 0};
+    for (int tr = ta; tr < NT; ++tr) {
+      if (tr > ta || !bad[ta]) {
+        const float f = __expf(L.Gs[tr][c] - L.Ge[ta][c]);
+        f32x4 y = {0, 0, 0, 0};
+#pragma unroll
+        for (int k0 = 0; k0 < 16; k0 += 4) {
+          const int r = 16 * tr + k0 + g;
+          y = mfma4(L.dBm[r][16 * ta + m], L.Kr[r][c], y);
+          y = mfma4(L.dP[r][16 * ta + m], L.Qr[r][c], y);
+        }
+#pragma unroll
+        for (int x = 0; x < 4; ++x) z3[x] += f * y[x];
+      } else {
+#pragma unroll
+        for (int x = 0; x < 4; ++x) {
+          const int i = 16 * ta + 4 * g + x;
+          const float gi = p.Gam[pcd + (size_t)i * D + c];
+          for (int r = i; r < 16 * tr + 16; ++r) {
+            const float e = __expf(p.Gam[pcd + (size_t)r * D + c] - gi);
+            z3d[x] += (L.dBm[r][i] * p.K[pcd + (size_t)r * D + c] + L.dP[r][i] * p.Q[pcd + (size_t)r * D + c]) * e;
+          }
+        }
+      }
+    }
+#pragma unroll
+    for (int x = 0; x < 4; ++x) {
+      const int i = 16 * ta + 4 * g + x;
+      p.dU[pcd + (size_t)i * D + c] = z3[x] * __expf(L.Ge[ta][c] - p.Gam[pcd + (size_t)i * D + c]) + z3d[x];
+    }
+  }
+}
 
 template <int D, int C>
 struct FwdLds {
@@ -574,114 +750,17 @@ struct BwdOut {
   float *dq, *dk, *dv, *dg, *dbeta;
 };
 
-// The pairwise terms of Bm and P, the decays, the reverse cumulative sum of
-// dGamma, and the scatter to token-major outputs.  2 D threads: thread c < D
-// walks the pairs (r, i <= r) row by row and keeps the row-r terms of channel
-// c in registers; thread D + c walks them column by column and keeps the
-// row-i terms, which it hands over through LDS (the row-i term of dGamma is
-// minus that of dk times k_i).  Each exponent is evaluated by both.
-template <int D, int C>
-__global__ __launch_bounds__(2 * D) void bwd_final_kernel(Planes p, Geo geo, BwdOut out) {
-  extern __shared__ float sm[];
-  float* Ks = sm;               // [C][D]
-  float* Gs = Ks + C * D;       // [C][D]
-  float* Qs = Gs + C * D;       // [C][D]
-  float* xK = Qs + C * D;       // [C][D] row-i terms of dk
-  float* dBm = xK + C * D;      // [C][C]
-  float* dP = dBm + C * C;      // [C][C]
-  const int b = blockIdx.x, H = geo.H;
-  if (p.fast[b]) return;  // bwd_final_fast_kernel
-  const int c = threadIdx.x % D, half = threadIdx.x / D;
-  const int gch = b / H, h = b % H;
-  int n, t0, len;
-  chunk_of<C>(geo, gch, n, t0, len);
-  const size_t pcd = (size_t)b * C * D, pcc = (size_t)b * C * C;
-  for (int idx = threadIdx.x; idx < C * D; idx += 2 * D) {
-    Ks[idx] = p.K[pcd + idx];
-    Gs[idx] = p.Gam[pcd + idx];
-    Qs[idx] = p.Q[pcd + idx];
-  }
-  for (int idx = threadIdx.x; idx < C * C; idx += 2 * D) {
-    dBm[idx] = p.dBm[pcc + idx];
-    dP[idx] = p.dP[pcc + idx];
-  }
-  __syncthreads();
-  if (half == 1) {
-    // column i: dk_i += sum_{r >= i} (dBm[r,i] k_r + dP[r,i] q_r) e_ri,
-    // dGamma_i -= sum_{r >= i} (dBm[r,i] k_r + dP[r,i] q_r) k_i e_ri
-    for (int i = 0; i < C; ++i) {
-      const float gi = Gs[i * D + c];
-      float ak0 = 0.f, ak1 = 0.f;
-      int r = i;
-      for (; r + 1 < C; r += 2) {
-        ak0 += (dBm[r * C + i] * Ks[r * D + c] + dP[r * C + i] * Qs[r * D + c]) *
-               __expf(Gs[r * D + c] - gi);
-        ak1 += (dBm[(r + 1) * C + i] * Ks[(r + 1) * D + c] + dP[(r + 1) * C + i] * Qs[(r + 1) * D + c]) *
-               __expf(Gs[(r + 1) * D + c] - gi);
-      }
-      if (r < C) ak0 += (dBm[r * C + i] * Ks[r * D + c] + dP[r * C + i] * Qs[r * D + c]) * __expf(Gs[r * D + c] - gi);
-      xK[i * D + c] = ak0 + ak1;
-    }
-  }
-  // Row-r terms go to dk and dg of the token (padded rows carry none), and
-  // are completed after the barrier by the same thread.
-  float kbsum = 0.f, dgn = 0.f;
-  if (half == 0) {
-    {
-      const float* S = p.S + ((size_t)b * D + c) * D;
-      const float* dS = p.dSn + ((size_t)b * D + c) * D;
-      for (int j = 0; j < D; ++j) dgn += S[j] * dS[j];
-    }
-    for (int r = 0; r < C; ++r) {
-      const float kr = Ks[r * D + c], qr = Qs[r * D + c], gr = Gs[r * D + c];
-      float dkr = 0.f, dqr = 0.f, dgr = 0.f;
-      for (int i = 0; i <= r; ++i) {
-        const float e = __expf(gr - Gs[i * D + c]);
-        const float ki = Ks[i * D + c];
-        const float wb = dBm[r * C + i] * e, wp = dP[r * C + i] * e;
-        dkr += wb * ki;
-        dqr += wp * ki;
-        dgr += (wb * kr + wp * qr) * ki;
-      }
-      const float ga = __expf(gr);
-      const size_t e0 = pcd + r * D + c;
-      const float dqt = p.dQt[e0], dkt = p.dKt[e0], dkb = p.dKb[e0];
-      const float kb = p.Kb[e0];
-      kbsum += dkb * kb;
-      if (r < len) {
-        const size_t ti = ((size_t)(t0 + r) * H + h) * D + c;
-        out.dq[ti] = dqt * ga + dqr;
-        out.dk[ti] = dkr + dkt * ga + dkb * __expf(Gs[(C - 1) * D + c] - gr);
-        out.dg[ti] = dgr + dqt * p.Qt[e0] + dkt * p.Kt[e0] - dkb * kb;
-      }
-    }
-  }
-  __syncthreads();
-  if (half == 0) {
-    const float gn = p.gn[(size_t)b * D + c];
-    float run = kbsum + dgn * gn;  // dGamma_n lands on the last row
-    for (int r = C - 1; r >= 0; --r) {
-      run -= xK[r * D + c] * Ks[r * D + c];
-      if (r < len) {
-        const size_t ti = ((size_t)(t0 + r) * H + h) * D + c;
-        run += out.dg[ti];
-        out.dg[ti] = run;
-        out.dk[ti] += xK[r * D + c];
-        out.dv[ti] = p.dR[pcd + r * D + c];
-      }
-    }
-    if (c < len) out.dbeta[(size_t)(t0 + c) * H + h] = p.db[(size_t)b * C + c];
-  }
-}
-
-// Moderate-decay chunks: the pairwise gradient terms are the products
-// Y1 = dBm Kh, Y2 = dP Kh, Y3 = dBm^T Kt + dP^T Qt (in the R, U, dU planes):
-// dq += gam Y2, dk += gam Y1 + exp(-Gamma) Y3, dGamma += Kt Y1 + Qt Y2 - Kh Y3.
-// One thread per channel.
+// The decays, the reverse cumulative sum of dGamma and the scatter to the
+// token-major outputs.  The pairwise gradient terms sit in the R, U, dU
+// planes: for factored chunks the products Y1 = dBm Kh, Y2 = dP Kh,
+// Y3 = dBm^T Kt + dP^T Qt, with dq += gam Y2, dk += gam Y1 + exp(-Gamma) Y3,
+// dGamma += Kt Y1 + Qt Y2 - Kh Y3; for strong-decay chunks the sums Z1, Z2,
+// Z3 themselves (bwd_pairs_tile_kernel), with dq += Z2, dk += Z1 + Z3,
+// dGamma += k (Z1 - Z3) + q Z2.  One thread per channel.
 template <int D, int C>
 __global__ __launch_bounds__(D) void bwd_final_fast_kernel(Planes p, Geo geo, BwdOut out) {
   const int b = blockIdx.x, c = threadIdx.x, H = geo.H;
-  if (!p.fast[b]) return;  // bwd_final_kernel
+  const bool fast = p.fast[b] != 0;
   const int gch = b / H, h = b % H;
   int n, t0, len;
   chunk_of<C>(geo, gch, n, t0, len);
@@ -719,12 +798,13 @@ __global__ __launch_bounds__(D) void bwd_final_fast_kernel(Planes p, Geo geo, Bw
     const float gr = p.Gam[e0], ga = __expf(gr);
     const float dqt = p.dQt[e0], dkt = p.dKt[e0], dkb = p.dKb[e0];
     const float y1 = Y1[r * D + c], y2 = Y2[r * D + c], y3 = Y3[r * D + c];
-    run += dqt * p.Qt[e0] + dkt * p.Kt[e0] - dkb * p.Kb[e0] + p.Kt[e0] * y1 + p.Qt[e0] * y2 -
-           p.Kh[e0] * y3;
+    run += dqt * p.Qt[e0] + dkt * p.Kt[e0] - dkb * p.Kb[e0] +
+           (fast ? p.Kt[e0] * y1 + p.Qt[e0] * y2 - p.Kh[e0] * y3 : p.K[e0] * (y1 - y3) + p.Q[e0] * y2);
     if (r < len) {
       const size_t ti = ((size_t)(t0 + r) * H + h) * D + c;
-      out.dq[ti] = (dqt + y2) * ga;
-      out.dk[ti] = (dkt + y1) * ga + dkb * __expf(gl - gr) + __expf(-gr) * y3;
+      out.dq[ti] = fast ? (dqt + y2) * ga : dqt * ga + y2;
+      out.dk[ti] = fast ? (dkt + y1) * ga + dkb * __expf(gl - gr) + __expf(-gr) * y3
+                        : dkt * ga + y1 + dkb * __expf(gl - gr) + y3;
       out.dg[ti] = run;
       out.dv[ti] = p.dR[e0];
     }
@@ -732,8 +812,6 @@ __global__ __launch_bounds__(D) void bwd_final_fast_kernel(Planes p, Geo geo, Bw
   if (c < len) out.dbeta[(size_t)(t0 + c) * H + h] = p.db[(size_t)b * C + c];
 }
 
-template <int D, int C>
-size_t final_lds() { return ((size_t)4 * C * D + 2 * C * C) * sizeof(float); }
 
 // Chunk counts of the sequences, on the host.
 struct BwdCounts {
@@ -841,13 +919,13 @@ hipError_t launch_backward_t(const BackwardArgs& a) {
   e = hipFuncSetAttribute(reinterpret_cast<const void*>(&bwd_bwd_states_kernel<D, C>),
                           hipFuncAttributeMaxDynamicSharedMemorySize, (int)blds_s);
   if (e != hipSuccess) return e;
-  const size_t glds = (size_t)3 * C * (D + 1) * sizeof(float);
-  e = hipFuncSetAttribute(reinterpret_cast<const void*>(&bwd_gram_kernel<D, C>),
-                          hipFuncAttributeMaxDynamicSharedMemorySize, (int)glds);
+  const size_t tlds = sizeof(TileLds<D, C>);
+  static_assert(sizeof(TileLds<D, C>) <= 160 * 1024, "tile operands fit LDS");
+  e = hipFuncSetAttribute(reinterpret_cast<const void*>(&bwd_gram_tile_kernel<D, C>),
+                          hipFuncAttributeMaxDynamicSharedMemorySize, (int)tlds);
   if (e != hipSuccess) return e;
-  const size_t flds = final_lds<D, C>();
-  e = hipFuncSetAttribute(reinterpret_cast<const void*>(&bwd_final_kernel<D, C>),
-                          hipFuncAttributeMaxDynamicSharedMemorySize, (int)flds);
+  e = hipFuncSetAttribute(reinterpret_cast<const void*>(&bwd_pairs_tile_kernel<D, C>),
+                          hipFuncAttributeMaxDynamicSharedMemorySize, (int)tlds);
   if (e != hipSuccess) return e;
 
   BwdIn in{a.q, a.k, a.v, a.g, a.beta, a.d_o};
@@ -886,7 +964,7 @@ hipError_t launch_backward_t(const BackwardArgs& a) {
     // Grams of the moderate-decay chunks, then the others pair by pair.
     gemm(NT, p.Kt, p.Kh, p.Bm, C, C, D, D, D, scd, scd, 1.f, 0, 2);    // strict_tril(Kt Kh^T)
     if (grams_p) gemm(NT, p.Qt, p.Kh, p.P, C, C, D, D, D, scd, scd, 1.f, 0, 1);  // tril(Qt Kh^T)
-    hipLaunchKernelGGL((bwd_gram_kernel<D, C>), dim3(NB), dim3(256), glds, a.stream, p, (int)NB);
+    hipLaunchKernelGGL((bwd_gram_tile_kernel<D, C>), dim3(NB), dim3(256), tlds, a.stream, p);
     hipLaunchKernelGGL((unit_lower_inverse_kernel<C>), dim3(NB), dim3(256), 0, a.stream, p.Bm, p.beta,
                        p.M, p.T);
   };
@@ -926,8 +1004,8 @@ hipError_t launch_backward_t(const BackwardArgs& a) {
     gemm(TN, p.dBm, p.Kt, p.dU, C, D, C, C, D, scc, scd, 1.f, 0, 0);  // Y3 = dBm^T Kt
     gemm(TN, p.dP, p.Qt, p.dU, C, D, C, C, D, scc, scd, 1.f, 1, 0);   //    + dP^T Qt
     if (gerr != hipSuccess) return gerr;
+    hipLaunchKernelGGL((bwd_pairs_tile_kernel<D, C>), dim3(NB), dim3(256), tlds, a.stream, p);
     hipLaunchKernelGGL((bwd_final_fast_kernel<D, C>), dim3(NB), dim3(D), 0, a.stream, p, geo, out);
-    hipLaunchKernelGGL((bwd_final_kernel<D, C>), dim3(NB), dim3(2 * D), flds, a.stream, p, geo, out);
   }
   if (gerr != hipSuccess) return gerr;
   return hipGetLastError();

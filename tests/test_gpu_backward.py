@@ -242,3 +242,19 @@ def test_backward_long_sampled_heads(kda):
         say("  " + "  ".join(f"{k} {v:.2e}" for k, v in errs.items()))
         assert max(errs.values()) <= TOL["bf16"], errs
         del got
+
+
+@pytest.mark.parametrize("dtype,C,alpha", [("bf16", 64, 0.1), ("f32", 64, 0.1), ("f32", 32, 0.01),
+                                           ("bf16", 16, 0.1), ("f32", 64, 1e-20)])
+def test_backward_mixed_decay(kda, dtype, C, alpha):
+    """Half the key channels at alpha per token: every chunk is past the
+    chunk-wide span, so Bm, P and the pairwise gradient terms go through the
+    tile-factored kernels (alpha = 0.01 and 1e-20: diagonal tiles past the
+    tile span as well, summed with exact exponents)."""
+    say(f"backward mixed decay dtype={dtype} C={C} alpha={alpha}")
+    rng = np.random.default_rng([60, C, int(-np.log10(alpha))])
+    T, H, D = 3 * C + 21, 2, 128
+    x = I.draw_mixed_decay_tokens(rng, T, H, D, D, dtype, alpha=alpha)
+    s0 = I.draw_states(rng, 1, H, D, D)
+    errs = run_case(kda, x, C, s0=s0, seed=C)
+    assert max(errs.values()) <= TOL[dtype], errs
