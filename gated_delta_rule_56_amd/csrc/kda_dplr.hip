@@ -24,11 +24,11 @@
 // general form's extra work.
 //
 // Grams of chunks whose decay span (max -Gamma_{C-1}) is at most 40 are
-// products of the factored operands; others are evaluated pair by pair with
-// the exact exponent of each difference.
+// products of the factored operands; others are factored per 16-row tile
+// (dplr_gram_tile_kernel), still on the matrix units.
 //
 // Kernels: chunk_table_kernel (varlen), dplr_prep_kernel, fp32_gemm_kernel
-// (Grams, then Wb = M Bt, the V terms), dplr_gram_kernel (strong decay),
+// (Grams, then Wb = M Bt, the V terms), dplr_gram_tile_kernel (strong decay),
 // unit_lower_inverse_kernel (M), dplr_states_kernel (serial over chunks per
 // (sequence, head, 16 value columns), fp32 MFMA, writes o and the final state).
 #include "kda_device.hpp"
@@ -170,43 +170,118 @@ __global__ __launch_bounds__(256) void dplr_prep_kernel(DIn in, DPlanes p, Geo g
 
 // Strong-decay chunks: the four (tied: two) Grams pair by pair with the
 // exact exponent of each difference.  Lane = row r; waves step through i.
+// Strong-decay chunks (span > kSpanD), factored per 16-row tile: with
+// Gamma_s(a) the cumulative decay before tile a and Gamma_e(b) at the end of
+// tile b, for rows r of tile a and columns i of tile b <= a
+//   exp(X_r - Gamma_i) = exp(X_r - Gamma_s(a)) f_ab exp(Gamma_e(b) - Gamma_i),
+//   f_ab = exp(Gamma_s(a) - Gamma_e(b)),
+// where X_r is Gamma_r (rows of Q) or Gamma'_r = Gamma_r - g_r (rows of B):
+// every factor <= 1 off the diagonal; on the diagonal f_aa = exp(span of
+// tile a), in range up to a span of kTileSpanD, beyond which the diagonal
+// block is summed pair by pair.  Blocks run on v_mfma_f32_16x16x4f32 with the
+// bridge factor on the column operand, channel by channel.
+constexpr float kTileSpanD = 64.f;
+
+template <int D, int C>
+struct DTileLds {
+  static constexpr int NT = C / 16, SD = D + 4;
+  float Br[C][SD], Qr[C][SD], Ac[C][SD], Kc[C][SD];
+  float Gs[NT][D], Ge[NT][D];
+};
+
 template <int D, int C, bool TIED>
-__global__ __launch_bounds__(256) void dplr_gram_kernel(DPlanes p) {
-  const int b = blockIdx.x;
-  if (p.fast[b]) return;
-  const size_t pcd = (size_t)b * C * D, pcc = (size_t)b * C * C;
-  const int r = threadIdx.x & 63, w = threadIdx.x >> 6;
-  if (r >= C) return;
-  const float* Q = p.Q + pcd;
-  const float* K = p.K + pcd;
-  const float* A = p.A + pcd;
-  const float* Bv = p.B + pcd;
-  const float* G = p.Gam + pcd;
-  const float* g = p.G + pcd;
-  for (int i = w; i < C; i += 4) {
-    float ba = 0.f, bk = 0.f, qa = 0.f, qk = 0.f;
-    if (i <= r) {
-      for (int c = 0; c < D; ++c) {
-        const float gi = G[i * D + c], gr = G[r * D + c];
-        const float eq = __expf(gr - gi), eb = __expf(gr - g[r * D + c] - gi);
-        const float ai = A[i * D + c], ki = K[i * D + c];
-        ba += Bv[r * D + c] * ai * eb;
-        qa += Q[r * D + c] * ai * eq;
+__global__ __launch_bounds__(256) void dplr_gram_tile_kernel(DPlanes p) {
+  extern __shared__ float sm[];
+  DTileLds<D, C>& L = *reinterpret_cast<DTileLds<D, C>*>(sm);
+  constexpr int NT = C / 16, NBLK = NT * (NT + 1) / 2;
+  const size_t b = blockIdx.x;
+  if (p.fast[b]) return;  // formed as products
+  const size_t pcd = b * C * D, pcc = b * C * C;
+  for (int idx = threadIdx.x; idx < NT * D; idx += 256) {
+    const int t = idx / D, c = idx % D;
+    L.Gs[t][c] = t == 0 ? 0.f : p.Gam[pcd + (size_t)(16 * t - 1) * D + c];
+    L.Ge[t][c] = p.Gam[pcd + (size_t)(16 * t + 15) * D + c];
+  }
+  __syncthreads();
+  for (int idx = threadIdx.x; idx < C * D; idx += 256) {
+    const int r = idx / D, c = idx % D, t = r / 16;
+    const float gm = p.Gam[pcd + idx], gs = L.Gs[t][c], ce = __expf(L.Ge[t][c] - gm);
+    L.Qr[r][c] = p.Q[pcd + idx] * __expf(gm - gs);
+    L.Br[r][c] = p.B[pcd + idx] * __expf(gm - p.G[pcd + idx] - gs);
+    L.Ac[r][c] = p.A[pcd + idx] * ce;
+    if (!TIED) L.Kc[r][c] = p.K[pcd + idx] * ce;
+  }
+  bool bad[NT];
+  for (int t = 0; t < NT; ++t) {
+    bool big = false;
+    for (int c = lane_id(); c < D; c += 64) big |= L.Ge[t][c] - L.Gs[t][c] < -kTileSpanD;
+    bad[t] = __any(big);
+  }
+  __syncthreads();
+  const int w = wave_id(), l = lane_id(), m = l & 15, g = l >> 4;
+  for (int blk = w; blk < NBLK; blk += 4) {
+    int ta = 0;
+    while ((ta + 1) * (ta + 2) / 2 <= blk) ++ta;
+    const int tb = blk - ta * (ta + 1) / 2;
+    f32x4 ba = {0, 0, 0, 0}, qa = ba, bk = ba, qk = ba;
+    if (tb < ta || !bad[ta]) {
+#pragma unroll 4
+      for (int k0 = 0; k0 < D; k0 += 4) {
+        const int c = k0 + g;
+        const float f = __expf(L.Gs[ta][c] - L.Ge[tb][c]);
+        const float ac = L.Ac[16 * tb + m][c] * f;
+        ba = mfma4(L.Br[16 * ta + m][c], ac, ba);
+        qa = mfma4(L.Qr[16 * ta + m][c], ac, qa);
         if (!TIED) {
-          bk += Bv[r * D + c] * ki * eb;
-          qk += Q[r * D + c] * ki * eq;
+          const float kc = L.Kc[16 * tb + m][c] * f;
+          bk = mfma4(L.Br[16 * ta + m][c], kc, bk);
+          qk = mfma4(L.Qr[16 * ta + m][c], kc, qk);
+        }
+      }
+    } else {
+      // tile span beyond kTileSpanD: each pair with its exact exponents
+#pragma unroll
+      for (int x = 0; x < 4; ++x) {
+        const size_t rr = 16 * ta + 4 * g + x, ii = 16 * tb + m;
+        if (ii > rr) continue;
+        for (int c = 0; c < D; ++c) {
+          const float gi = p.Gam[pcd + ii * D + c], gr = p.Gam[pcd + rr * D + c];
+          const float eq = __expf(gr - gi), eb = __expf(gr - p.G[pcd + rr * D + c] - gi);
+          const float ai = p.A[pcd + ii * D + c];
+          ba[x] += p.B[pcd + rr * D + c] * ai * eb;
+          qa[x] += p.Q[pcd + rr * D + c] * ai * eq;
+          if (!TIED) {
+            const float ki = p.K[pcd + ii * D + c];
+            bk[x] += p.B[pcd + rr * D + c] * ki * eb;
+            qk[x] += p.Q[pcd + rr * D + c] * ki * eq;
+          }
         }
       }
     }
-    p.Aba[pcc + r * C + i] = i < r ? ba : 0.f;
-    p.Aqa[pcc + r * C + i] = i <= r ? qa : 0.f;
-    if (!TIED) {
-      p.Abk[pcc + r * C + i] = i < r ? bk : 0.f;
-      p.Aqk[pcc + r * C + i] = i <= r ? qk : 0.f;
+    // lane (m, g) holds rows 4 g + x of column m of the block
+#pragma unroll
+    for (int x = 0; x < 4; ++x) {
+      const int r = 16 * ta + 4 * g + x, i = 16 * tb + m;
+      p.Aba[pcc + r * C + i] = i < r ? ba[x] : 0.f;
+      p.Aqa[pcc + r * C + i] = i <= r ? qa[x] : 0.f;
+      if (!TIED) {
+        p.Abk[pcc + r * C + i] = i < r ? bk[x] : 0.f;
+        p.Aqk[pcc + r * C + i] = i <= r ? qk[x] : 0.f;
+      }
+    }
+  }
+  for (int idx = threadIdx.x; idx < C * C; idx += 256) {  // blocks above the diagonal
+    const int r = idx / C, i = idx % C;
+    if (i / 16 > r / 16) {
+      p.Aba[pcc + idx] = 0.f;
+      p.Aqa[pcc + idx] = 0.f;
+      if (!TIED) {
+        p.Abk[pcc + idx] = 0.f;
+        p.Aqk[pcc + idx] = 0.f;
+      }
     }
   }
 }
-
 
 template <int D, int C>
 struct StLds {
@@ -372,6 +447,10 @@ hipError_t launch_dplr_t(const DplrArgs& a) {
   hipError_t e = hipFuncSetAttribute(reinterpret_cast<const void*>(&dplr_states_kernel<D, C, TIED>),
                                      hipFuncAttributeMaxDynamicSharedMemorySize, (int)slds);
   if (e != hipSuccess) return e;
+  static_assert(sizeof(DTileLds<D, C>) <= 160 * 1024, "tile operands fit LDS");
+  e = hipFuncSetAttribute(reinterpret_cast<const void*>(&dplr_gram_tile_kernel<D, C, TIED>),
+                          hipFuncAttributeMaxDynamicSharedMemorySize, (int)sizeof(DTileLds<D, C>));
+  if (e != hipSuccess) return e;
   if (NB > 0) {
     DIn in{a.q, a.k, a.v, a.a, a.b, a.g, a.beta};
     hipLaunchKernelGGL((dplr_prep_kernel<in_t, D, C, TIED>), dim3(NB), dim3(256), 0, a.stream, in,
@@ -394,7 +473,8 @@ hipError_t launch_dplr_t(const DplrArgs& a) {
       gemm(NT, p.Bt, p.Kh, p.Abk, C, C, D, D, D, scd, scd, 1.f, 2);  // strict_tril(Bt Kh^T)
       gemm(NT, p.Qt, p.Kh, p.Aqk, C, C, D, D, D, scd, scd, 1.f, 1);  // tril(Qt Kh^T)
     }
-    hipLaunchKernelGGL((dplr_gram_kernel<D, C, TIED>), dim3(NB), dim3(256), 0, a.stream, p);
+    hipLaunchKernelGGL((dplr_gram_tile_kernel<D, C, TIED>), dim3(NB), dim3(256), sizeof(DTileLds<D, C>),
+                       a.stream, p);
     hipLaunchKernelGGL((unit_lower_inverse_kernel<C>), dim3(NB), dim3(256), 0, a.stream, p.Aba,
                        (const float*)nullptr, p.M, (float*)nullptr);
     gemm(NN, p.M, p.Bt, p.Wb, C, D, C, C, D, scc, scd, 1.f, 0);      // Wb = M Bt

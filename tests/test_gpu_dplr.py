@@ -184,3 +184,43 @@ def test_dplr_no_tokens(kda):
     torch.cuda.synchronize()
     np.testing.assert_array_equal(host(fin), s0)
     assert o.numel() == 0
+
+
+@pytest.mark.parametrize("dtype,C,alpha", [("bf16", 64, 0.1), ("f32", 32, 0.01), ("f32", 64, 1e-20)])
+def test_dplr_mixed_decay(kda, dtype, C, alpha):
+    """General DPLR with half the channels decaying at alpha per token: every
+    chunk is past the chunk-wide span, so the four Grams take the
+    tile-factored kernel (alpha = 0.01 and 1e-20: diagonal tiles past the tile
+    span too, summed with exact exponents)."""
+    say(f"dplr mixed decay dtype={dtype} C={C} alpha={alpha}")
+    rng = np.random.default_rng([63, C, int(-np.log10(alpha))])
+    T, H, D = 3 * C + 11, 2, 128
+    q, k, v, a, b, g = I.draw_dplr_tokens(rng, T, H, D, D, dtype)
+    g = np.array(g, dtype=np.float32)
+    half = rng.standard_normal((T, H, D - D // 2))
+    g[:, :, D // 2:] = np.minimum(np.log(alpha) * (1.0 + 0.1 * half), 0.0).astype(np.float32)
+    x = (q, k, v, a, b, g)
+    s0 = I.draw_states(rng, 1, H, D, D)
+    eo, ef = oracle.dplr_recurrent(*x, s0)
+    o, fin = run_dplr(kda, x, dtype, C, s0)
+    eo_, es_ = rel(o, eo), rel(fin, ef)
+    say(f"  o err {eo_:.2e}  state err {es_:.2e}")
+    assert eo_ <= TOL[dtype] and es_ <= TOL[dtype]
+
+
+@pytest.mark.parametrize("dtype,C,alpha", [("bf16", 64, 0.1), ("f32", 16, 0.01)])
+def test_kda_chunk_fp32_mixed_decay(kda, dtype, C, alpha):
+    """KDA through the fp32 pipeline on mixed decay (the tied tile kernel)."""
+    say(f"kda chunk fp32 mixed decay dtype={dtype} C={C} alpha={alpha}")
+    rng = np.random.default_rng([64, C, int(-np.log10(alpha))])
+    T, H, D = 3 * C + 5, 2, 128
+    x = I.draw_mixed_decay_tokens(rng, T, H, D, D, dtype, alpha=alpha)
+    s0 = I.draw_states(rng, 1, H, D, D)
+    eo, ef = oracle.kda_recurrent(x.q, x.k, x.v, x.g, x.beta, s0)
+    dt = torch.bfloat16 if dtype == "bf16" else torch.float32
+    o, fin = kda.prefill_chunk_fp32(tdev(x.q, dt)[None], tdev(x.k, dt)[None], tdev(x.v, dt)[None],
+                                    tdev(x.g)[None], tdev(x.beta)[None], tdev(s0), chunk_size=C)
+    torch.cuda.synchronize()
+    eo_, es_ = rel(host(o)[0], eo), rel(host(fin), ef)
+    say(f"  o err {eo_:.2e}  state err {es_:.2e}")
+    assert eo_ <= TOL[dtype] and es_ <= TOL[dtype]
