@@ -47,8 +47,10 @@ struct LayerPtrs {
   void* cs_out[3];
 };
 
-__device__ __forceinline__ float swish_d(float x) { return x / (1.f + __expf(-x)); }
-__device__ __forceinline__ float sigmoid_d(float x) { return 1.f / (1.f + __expf(-x)); }
+// Hardware reciprocal (about 1 ulp) instead of a correctly rounded
+// division; 1 / inf is 0, so large |x| give the limits.
+__device__ __forceinline__ float sigmoid_d(float x) { return __builtin_amdgcn_rcpf(1.f + __expf(-x)); }
+__device__ __forceinline__ float swish_d(float x) { return x * sigmoid_d(x); }
 
 // An input element kept as loaded, widened to 32 bits (a bf16 in the low
 // half): 16-bit values held this way are not packed in pairs, which would make

@@ -565,8 +565,11 @@ struct KernelPtrs {
 
 // Layer prologue pieces (the "Kimi Linear" notes, docsaid.org, section
 // "Other Components"): Swish of the projected q, k, v; sigmoid of beta.
-__device__ __forceinline__ float swishf(float x) { return x / (1.f + __expf(-x)); }
-__device__ __forceinline__ float sigmoidf(float x) { return 1.f / (1.f + __expf(-x)); }
+// The reciprocal is the hardware's (about 1 ulp), not a correctly rounded
+// division: both stay within a few fp32 ulp, and large |x| give the limits
+// (x or 0, 1 or 0) since 1 / inf is 0.
+__device__ __forceinline__ float sigmoidf(float x) { return __builtin_amdgcn_rcpf(1.f + __expf(-x)); }
+__device__ __forceinline__ float swishf(float x) { return x * sigmoidf(x); }
 constexpr float kL2Floor = 1e-12f;  // L2 norms below this count as this
 
 // Eight input elements of one row held as loaded (bf16 or fp32).
@@ -670,10 +673,11 @@ __device__ __forceinline__ void load_halo(Raw8<T>& ext, const KernelPtrs& kp, in
 
 // Rotate a value right by N lanes within each 16-lane row (DPP row_ror):
 // lane lr receives the value of lane (lr - N) mod 16 of its row.
+// Every lane has a source, so no old value is needed.
 template <int N>
 __device__ __forceinline__ float row_ror(float x) {
-  return __builtin_bit_cast(float, __builtin_amdgcn_update_dpp(0, __builtin_bit_cast(int, x),
-                                                               0x120 + N, 0xF, 0xF, false));
+  return __builtin_bit_cast(float, __builtin_amdgcn_mov_dpp(__builtin_bit_cast(int, x), 0x120 + N, 0xF, 0xF,
+                                                            true));
 }
 
 // Shift a value right by N lanes within each 16-lane row (DPP row_shr): lane
@@ -720,28 +724,37 @@ __device__ __forceinline__ float row_scan16(float x) {
 
 // Convolved values of one lane's 8 channels (c0 .. c0 + 7) of row 16 rt + lr,
 // from the lane's own row and the halo rows of lanes 13..15 of its 16-lane
-// group: tap j reads row lr - j, the own value of lane lr - j, or for
-// lr < j the halo value of lane lr - j + 16 (both one row rotation).  w4
-// holds the channels' weights in LDS, [8][kMaxConv], w4[4e + j] the weight
-// of row lr - j; taps at or past the width W are skipped.
+// group.  w4 holds the channels' weights in LDS, [8][kMaxConv], w4[4e + j]
+// the weight of row lr - j.  Tap j needs lane lr - j's own value, or for
+// lr < j the halo value of lane lr - j + 16: each source lane s first picks
+// its halo value when s >= 16 - j, and one row rotation by j delivers it.
+// Full width (the usual case) runs every tap with no test; a narrower width
+// skips the taps at or past W, whose rows must not be read (a non-finite
+// input there would leak through a zero weight).
 template <class T>
 __device__ __forceinline__ void conv8(const Raw8<T>& own, const Raw8<T>& ext, const float* w4,
                                       int W, int lr, float out[8]) {
   static_assert(kMaxConv == 4, "three taps before the current row");
+  if (W == kMaxConv) {
 #pragma unroll
-  for (int e = 0; e < 8; ++e) {
-    const float xo = own.get(e), xe = ext.get(e);
-    float acc = w4[4 * e] * xo;
-    // Both rotations run on every lane (a conditional operator would run
-    // only one, under a divergent branch, and read inactive lanes).
-    const float o1 = row_ror<1>(xo), e1 = row_ror<1>(xe);
-    const float o2 = row_ror<2>(xo), e2 = row_ror<2>(xe);
-    const float o3 = row_ror<3>(xo), e3 = row_ror<3>(xe);
-    const float t1 = lr >= 1 ? o1 : e1, t2 = lr >= 2 ? o2 : e2, t3 = lr >= 3 ? o3 : e3;
-    if (W > 1) acc += w4[4 * e + 1] * t1;
-    if (W > 2) acc += w4[4 * e + 2] * t2;
-    if (W > 3) acc += w4[4 * e + 3] * t3;
-    out[e] = acc;
+    for (int e = 0; e < 8; ++e) {
+      const float xo = own.get(e), xe = ext.get(e);
+      const f32x4 wv = *reinterpret_cast<const f32x4*>(w4 + 4 * e);
+      float acc = wv[0] * xo;
+      acc += wv[1] * row_ror<1>(lr >= 15 ? xe : xo);
+      acc += wv[2] * row_ror<2>(lr >= 14 ? xe : xo);
+      acc += wv[3] * row_ror<3>(lr >= 13 ? xe : xo);
+      out[e] = acc;
+    }
+  } else {
+#pragma unroll
+    for (int e = 0; e < 8; ++e) {
+      const float xo = own.get(e), xe = ext.get(e);
+      float acc = w4[4 * e] * xo;
+      if (W > 1) acc += w4[4 * e + 1] * row_ror<1>(lr >= 15 ? xe : xo);
+      if (W > 2) acc += w4[4 * e + 2] * row_ror<2>(lr >= 14 ? xe : xo);
+      out[e] = acc;
+    }
   }
 }
 
@@ -1782,41 +1795,61 @@ __device__ __forceinline__ void inter_o_role(const KernelPtrs& kp, const InterGe
 // head, y = o / sqrt(mean_c o_c^2 + eps) * weight * sigmoid(gate).  The norm
 // spans all D value columns, which the inter-chunk pass splits over
 // workgroups, so it runs after that pass, per segment, on the raw o it left
-// in the workspace.  One workgroup per (slot, head); one wave per token row,
-// D/64 columns per lane.
+// in the workspace.  One workgroup of four waves per (slot, head), C / 4 rows
+// per wave.  D / 4 consecutive lanes hold one row, four columns each, so a
+// wave's 16-byte loads cover whole rows (two for d = 128); every row's loads
+// are issued before the first use, and the mean square is summed over the
+// row's lanes.
 // ---------------------------------------------------------------------------
 template <class M, int D, int C, bool OUT_BF16>
 __global__ __launch_bounds__(256) void layer_epilogue_kernel(KernelPtrs kp, SeqInfo si) {
   typedef typename M::in_t in_t;
-  constexpr int CPL = D / 64;  // columns per lane
+  constexpr int LPR = D / 4;       // lanes per row
+  constexpr int RPI = 64 / LPR;    // rows per wave and pass
+  constexpr int NI = C / 4 / RPI;  // passes per wave
+  static_assert(NI >= 1 && C % (4 * RPI) == 0, "whole passes per wave");
   const Item it = intra_item<C>(si, kp, blockIdx.x, 0);
+  if (it.len <= 0) return;
   const int slot = blockIdx.x / kp.H;
-  const int w = wave_id(), l = lane_id();
+  const int l = lane_id();
+  const int c0 = 4 * (l % LPR);
+  const int rb = (C / 4) * wave_id() + l / LPR;
   const in_t* gate = reinterpret_cast<const in_t*>(kp.gate);
-  float wt[CPL];
+  const f32x4 wt = *reinterpret_cast<const f32x4*>(kp.norm_weight + c0);
+  f32x4 x[NI], gv[NI];
 #pragma unroll
-  for (int e = 0; e < CPL; ++e) wt[e] = kp.norm_weight[CPL * l + e];
-  for (int row = w; row < it.len; row += 4) {
-    const float* src = kp.o_slots + (((size_t)slot * kp.H + it.h) * C + row) * D + CPL * l;
-    const size_t ti = ((size_t)(it.t0 + row) * kp.H + it.h) * D + CPL * l;
-    float x[CPL], gv[CPL];
-    float ss = 0.f;
-#pragma unroll
-    for (int e = 0; e < CPL; ++e) {
-      x[e] = src[e];
-      gv[e] = (float)gate[ti + e];
-      ss += x[e] * x[e];
+  for (int i = 0; i < NI; ++i) {
+    const int row = rb + RPI * i;
+    const int rr = row < it.len ? row : 0;  // rows past the chunk read row 0 and store nothing
+    x[i] = *reinterpret_cast<const f32x4*>(kp.o_slots + (((size_t)slot * kp.H + it.h) * C + rr) * D + c0);
+    const size_t ti = ((size_t)(it.t0 + rr) * kp.H + it.h) * D + c0;
+    if constexpr (sizeof(in_t) == 2) {
+      const bf16x4 g4 = *reinterpret_cast<const bf16x4*>(gate + ti);
+      gv[i] = f32x4{(float)g4[0], (float)g4[1], (float)g4[2], (float)g4[3]};
+    } else {
+      gv[i] = *reinterpret_cast<const f32x4*>(gate + ti);
     }
+  }
 #pragma unroll
-    for (int off = 32; off > 0; off >>= 1) ss += __shfl_xor(ss, off);
+  for (int i = 0; i < NI; ++i) {
+    const int row = rb + RPI * i;
+    float ss = x[i][0] * x[i][0] + x[i][1] * x[i][1] + x[i][2] * x[i][2] + x[i][3] * x[i][3];
+#pragma unroll
+    for (int off = LPR / 2; off > 0; off >>= 1) ss += __shfl_xor(ss, off);
     const float inv = 1.f / sqrtf(ss / D + kp.norm_eps);
+    if (row < it.len) {
+      const size_t ti = ((size_t)(it.t0 + row) * kp.H + it.h) * D + c0;
+      f32x4 y;
 #pragma unroll
-    for (int e = 0; e < CPL; ++e) {
-      const float y = x[e] * inv * wt[e] * sigmoidf(gv[e]);
-      if constexpr (OUT_BF16)
-        reinterpret_cast<bf16*>(kp.o)[ti + e] = f2bf(y);
-      else
-        reinterpret_cast<float*>(kp.o)[ti + e] = y;
+      for (int e = 0; e < 4; ++e) y[e] = x[i][e] * inv * wt[e] * sigmoidf(gv[i][e]);
+      if constexpr (OUT_BF16) {
+        bf16x4 yb;
+#pragma unroll
+        for (int e = 0; e < 4; ++e) yb[e] = f2bf(y[e]);
+        *reinterpret_cast<bf16x4*>(reinterpret_cast<bf16*>(kp.o) + ti) = yb;
+      } else {
+        *reinterpret_cast<f32x4*>(reinterpret_cast<float*>(kp.o) + ti) = y;
+      }
     }
   }
 }
