@@ -401,254 +401,435 @@ __global__ __launch_bounds__(256) void bwd_pairs_tile_kernel(Planes p) {
   }
 }
 
-template <int D, int C>
-struct FwdLds {
-  float Kt[C][D + 4];
-  float Kb[C][D + 16];
-  float T[C][C + 4];
-  float S[D][kCols];
-  float R[C][kCols];
-  float U[C][kCols];
-  float V[C][kCols];
-  float gn[D];
-};
-
 constexpr int kSerThreads = 512;
 
+// Serial passes over a sequence's chunks, one workgroup per (sequence, head,
+// 16 value columns), eight waves.  The carried 16-column block (S forward,
+// dS' backward) stays in the MFMA accumulators of waves 0 .. D/16 - 1, one
+// 16 x 16 tile each.  Every product is cut into 16 x 16 tiles on
+// v_mfma_f32_16x16x4f32, whose lane l supplies A[l & 15][k] and B[k][l & 15]
+// for k = l >> 4 and ends with rows 4 (l >> 4) .. + 3 of column l & 15.  A
+// tile's contraction is spread over several waves where the tiles are fewer
+// than the waves, each wave's share ending as a partial tile in LDS that the
+// next stage sums while reading it.  Within a share, lane group g takes a
+// contiguous run of the contraction index, so a lane's A values are
+// consecutive in memory where the plane's rows run along that index.  Every
+// operand a stage takes from global memory is loaded into registers one chunk
+// ahead, right after its last use.
+template <int D, int C>
+struct SerGeom {
+  static constexpr int NW = kSerThreads / 64;
+  static constexpr int NRT = C / 16;   // 16-row tiles of a chunk
+  static constexpr int NST = D / 16;   // 16-row tiles of the carried block
+  static constexpr int KS = NW / NRT;  // waves sharing a row tile's D-long contraction
+  static constexpr int DK = D / KS;    // channels per share
+  static constexpr int RJ = DK / 4;    // products per share
+  static constexpr int SJ = C / 4;     // products of a C-long contraction
+  static constexpr int TJ = C / 8;     // most products of a half of a triangular one
+  static constexpr int FIN = (C * 16 + kSerThreads - 1) / kSerThreads;  // C x 16 elements per thread
+  static_assert(NW % NRT == 0 && D % (4 * KS) == 0 && NST <= NW, "work split");
+};
+
+// N consecutive floats (16-byte aligned when N % 4 == 0, 8-byte when even).
+template <int N>
+__device__ __forceinline__ void ld_run(float (&d)[N], const float* src) {
+  if constexpr (N % 4 == 0) {
+#pragma unroll
+    for (int x = 0; x < N / 4; ++x) {
+      const f32x4 v = *reinterpret_cast<const f32x4*>(src + 4 * x);
+#pragma unroll
+      for (int e = 0; e < 4; ++e) d[4 * x + e] = v[e];
+    }
+  } else if constexpr (N % 2 == 0) {
+#pragma unroll
+    for (int x = 0; x < N / 2; ++x) {
+      const float2 v = *reinterpret_cast<const float2*>(src + 2 * x);
+      d[2 * x] = v.x;
+      d[2 * x + 1] = v.y;
+    }
+  } else {
+#pragma unroll
+    for (int x = 0; x < N; ++x) d[x] = src[x];
+  }
+}
+
+// A 16-column slab of a chunk plane (rows r0 .. r0 + nr - 1 of [C][ld], columns
+// c0 .. c0 + 15) moved through one wave: fetch() loads it with 16-byte loads
+// (C / 16 per lane; rows past nr re-read the last one), put() writes it
+// transposed into the wave's own LDS tile [16][C + 4], so that lane (m, g)
+// then reads a contiguous run of rows of column m.  The tile belongs to one
+// wave, so no barrier separates put() from the reads that follow it.
+template <int C>
+struct Slab {
+  static constexpr int NU = C / 16;
+  f32x4 v[NU];
+  __device__ __forceinline__ void fetch(const float* plane, int ld, int r0, int nr, int c0, int l) {
+#pragma unroll
+    for (int x = 0; x < NU; ++x) {
+      const int u = l + 64 * x, r = (u >> 2) < nr ? (u >> 2) : nr - 1;
+      v[x] = *reinterpret_cast<const f32x4*>(plane + (size_t)(r0 + r) * ld + c0 + 4 * (u & 3));
+    }
+  }
+  __device__ __forceinline__ void put(float* tile, int nr, int l) const {
+#pragma unroll
+    for (int x = 0; x < NU; ++x) {
+      const int u = l + 64 * x, r = (u >> 2) < nr ? (u >> 2) : nr - 1;
+#pragma unroll
+      for (int e = 0; e < 4; ++e) tile[(4 * (u & 3) + e) * (C + 4) + r] = v[x][e];
+    }
+  }
+};
+
+// Requests every 128-byte line of one chunk's operand blocks ahead of their
+// loads, so those loads find them in L2 rather than in HBM: each of the NVB
+// workgroups of a (sequence, head), which share an L2, takes every NVB-th
+// line, one per lane of each wave (lanes past the lines touch the first one
+// again).  Returns the 4-byte value read; the caller keeps it until the next
+// step and then marks it used (touch_done), so nothing waits for it sooner.
+template <int NS>
+__device__ __forceinline__ float l2_touch(const float* const (&base)[NS], const int (&lines)[NS], int vb,
+                                          int nvb, int w, int nw, int l) {
+  int line = vb + nvb * (64 * w + l);
+  const float* ptr = base[0];
+#pragma unroll
+  for (int x = 0; x < NS; ++x) {
+    if (line >= 0 && line < lines[x]) ptr = base[x] + 32 * line;
+    line -= lines[x];
+  }
+  (void)nw;
+  return *ptr;
+}
+// Marks a touch value as used without any instruction (its load must have
+// completed here).
+__device__ __forceinline__ void touch_done(float x) { asm volatile("" ::"v"(x)); }
+
+template <int D, int C>
+struct FwdLds {
+  float St[16][D + 4];                          // S^T: [value column][channel]
+  float Rp[SerGeom<D, C>::KS][16][C + 4];       // shares of Kt S - V, transposed
+  float Up[2][16][C + 4];                       // halves of T R, transposed
+  float Kw[SerGeom<D, C>::NW][16][C + 4];       // each wave's Kb slab, transposed
+};
+
 // Serial forward over a sequence's chunks for 16 value columns: the state
-// entering every chunk, R = V - Kt S and U = T R.  Eight waves; the next
-// chunk's Kt, Kb, T are loaded into registers while this chunk computes.
+// entering every chunk, R = V - Kt S and U = T R, and S' = gam_n S + Kb^T U.
+// R stage: wave w takes row tile w % NRT and channel share w / NRT.  U stage:
+// waves w < 2 NRT take row tile w % NRT and half w / NRT of its k < 16 (rt+1).
+// S stage: wave t < D/16 updates its state tile.
 template <int D, int C>
 __global__ __launch_bounds__(kSerThreads) void bwd_fwd_states_kernel(Planes p, Geo geo,
                                                                      const float* __restrict__ s0,
                                                                      float* __restrict__ s_out) {
+  typedef SerGeom<D, C> G;
+  constexpr int NVB = D / kCols, NRT = G::NRT, NST = G::NST, DK = G::DK, RJ = G::RJ, SJ = G::SJ;
+  constexpr int UJM = 2 * NRT;  // most U-stage products per lane
+  constexpr int kFin = G::FIN;
   extern __shared__ float sm[];
   FwdLds<D, C>& L = *reinterpret_cast<FwdLds<D, C>*>(sm);
-  constexpr int NVB = D / kCols, NT = kSerThreads, NW = NT / 64;
   const int H = geo.H;
-  const int vb = blockIdx.x % NVB, nh = blockIdx.x / NVB;
+  int nh, vb;
+  if (!serial_slot<NVB>(geo.num_seqs * H, nh, vb)) return;
   const int n = nh / H, h = nh % H, col0 = vb * kCols;
-  const int tid = threadIdx.x, w = tid >> 6, l = tid & 63, m = l & 15, g = l >> 4;
+  const int tid = threadIdx.x, w = __builtin_amdgcn_readfirstlane(tid >> 6), l = tid & 63;
+  const int m = l & 15, g = l >> 4;
   int bos, eos, base, lo, hi;
   seq_of<C>(geo, n, bos, eos, base);
   seg_range<C>(geo, bos, eos, lo, hi);
-  for (int idx = tid; idx < D * kCols; idx += NT) {
-    const int i = idx / kCols, j = idx % kCols;
-    L.S[i][j] = s0 ? s0[(((size_t)n * H + h) * D + i) * D + col0 + j] : 0.f;
-  }
-  Prefetch<C, D, NT> pKt, pKb;
-  Prefetch<C, C, NT> pT;
-  Prefetch<C, kCols, NT, D> pV;  // this workgroup's value columns
-  Prefetch<1, D, NT> pG;         // gam_n
+  const int rrt = w % NRT, rks = w / NRT;                       // R stage
+  const int urt = w % NRT, uhs = (w / NRT) & 1;                 // U stage (w < 2 NRT)
+  const int ulh = 8 * (urt + 1), uj = ulh / 4;                  // its half's length, products
+  const int st = w < NST ? w : NST - 1;                         // S stage tile
   auto blk = [&](int ci) { return (size_t)(base + ci - geo.c0) * H + h; };
-  auto fetch = [&](size_t b) {
-    pKt.load(p.Kt + b * C * D);
-    pKb.load(p.Kb + b * C * D);
-    pT.load(p.T + b * C * C);
-    pV.load(p.V + b * C * D + col0);
-    pG.load(p.gn + b * D);
+
+  float ra[RJ], rv[4], ta[UJM], sreg[4];
+  Slab<C> kb;
+  f32x4 gam;
+  auto load_r = [&](size_t b) {
+    ld_run<RJ>(ra, p.Kt + (b * C + 16 * rrt + m) * D + rks * DK + g * RJ);
+#pragma unroll
+    for (int i = 0; i < 4; ++i) rv[i] = p.V[(b * C + 16 * rrt + 4 * g + i) * D + col0 + m];
   };
-  if (lo < hi) fetch(blk(lo));
-  for (int ci = lo; ci < hi; ++ci) {
-    const size_t b = blk(ci);
-    const size_t pcd = b * C * D;
-    __syncthreads();
-    pKt.template store<D + 4>(&L.Kt[0][0]);
-    pKb.template store<D + 16>(&L.Kb[0][0]);
-    pT.template store<C + 4>(&L.T[0][0]);
-    pV.template store<kCols>(&L.V[0][0]);
-    pG.template store<D>(&L.gn[0]);
-    for (int idx = tid; idx < D * kCols; idx += NT) {
-      const int i = idx / kCols, j = idx % kCols;
-      p.S[(b * D + i) * D + col0 + j] = L.S[i][j];
-    }
-    __syncthreads();
-    if (ci + 1 < hi) fetch(blk(ci + 1));
-    for (int rt = w; rt < C / 16; rt += NW) {  // R = V - Kt S
-      f32x4 acc = {0, 0, 0, 0}, acc1 = {0, 0, 0, 0};
-#pragma unroll 8
-      for (int k0 = 0; k0 < D; k0 += 8) {
-        acc = mfma4(L.Kt[16 * rt + m][k0 + g], L.S[k0 + g][m], acc);
-        acc1 = mfma4(L.Kt[16 * rt + m][k0 + 4 + g], L.S[k0 + 4 + g][m], acc1);
-      }
+  auto load_u = [&](size_t b) {  // uj is even, and so is the run's offset
+    const float* src = p.T + (b * C + 16 * urt + m) * C + uhs * ulh + g * uj;
 #pragma unroll
-      for (int i = 0; i < 4; ++i) {
-        const int r = 16 * rt + 4 * g + i;
-        const float x = L.V[r][m] - acc[i] - acc1[i];
-        L.R[r][m] = x;
-        p.R[pcd + r * D + col0 + m] = x;
-      }
+    for (int j = 0; j < UJM; j += 2) {
+      const float2 x = *reinterpret_cast<const float2*>(src + (j < uj ? j : 0));
+      ta[j] = x.x;
+      ta[j + 1] = x.y;
     }
-    __syncthreads();
-    for (int rt = w; rt < C / 16; rt += NW) {  // U = T R (T lower triangular)
-      f32x4 acc = {0, 0, 0, 0};
-      for (int k0 = 0; k0 < 16 * (rt + 1); k0 += 4) acc = mfma4(L.T[16 * rt + m][k0 + g], L.R[k0 + g][m], acc);
+  };
+  auto load_s = [&](size_t b) {
+    kb.fetch(p.Kb + b * C * D, D, 0, C, 16 * st, l);
+    gam = *reinterpret_cast<const f32x4*>(p.gn + b * D + 16 * st + 4 * g);
+  };
 #pragma unroll
-      for (int i = 0; i < 4; ++i) {
-        const int r = 16 * rt + 4 * g + i;
-        L.U[r][m] = acc[i];
-        p.U[pcd + r * D + col0 + m] = acc[i];
-      }
-    }
-    __syncthreads();
-    for (int t = w; t < D / 16; t += NW) {  // S = gam_n S + Kb^T U, one tile per wave
-      f32x4 acc, acc1 = {0, 0, 0, 0};
-#pragma unroll
-      for (int i = 0; i < 4; ++i) {
-        const int c = 16 * t + 4 * g + i;
-        acc[i] = L.gn[c] * L.S[c][m];
-      }
-#pragma unroll 8
-      for (int k0 = 0; k0 < C; k0 += 8) {
-        acc = mfma4(L.Kb[k0 + g][16 * t + m], L.U[k0 + g][m], acc);
-        acc1 = mfma4(L.Kb[k0 + 4 + g][16 * t + m], L.U[k0 + 4 + g][m], acc1);
-      }
-#pragma unroll
-      for (int i = 0; i < 4; ++i) L.S[16 * t + 4 * g + i][m] = acc[i] + acc1[i];
-    }
+  for (int i = 0; i < 4; ++i)
+    sreg[i] = s0 ? s0[(((size_t)n * H + h) * D + 16 * st + 4 * g + i) * D + col0 + m] : 0.f;
+  // The initial state in full before any prefetch: left pending, it would
+  // make the compiler's waits in the loop count every later load.
+  __builtin_amdgcn_s_waitcnt(0);
+  float tch = 0.f;  // the last L2 request's value
+  if (lo < hi) {
+    load_r(blk(lo));
+    load_u(blk(lo));
+    load_s(blk(lo));
   }
-  if (s_out) {  // the state after the pass's last chunk
-    __syncthreads();
-    for (int idx = tid; idx < D * kCols; idx += NT) {
-      const int i = idx / kCols, j = idx % kCols;
-      s_out[(((size_t)n * H + h) * D + i) * D + col0 + j] = L.S[i][j];
+  // R and U of a chunk go out at the top of the next step (and of the last
+  // chunk after the loop), so every step issues the same memory operations
+  // in the same order, the first one included (its store goes to the first
+  // chunk's rows, which the second step then overwrites); the compiler's
+  // waits for the operands loaded a step earlier then cover nothing newer.
+  auto put_ru = [&](size_t b) {
+    const size_t pcd = b * C * D;
+#pragma unroll
+    for (int xf = 0; xf < kFin; ++xf) {
+      const int e = tid + kSerThreads * xf, nn = e & 15, r = e >> 4;
+      if (C * 16 % kSerThreads != 0 && e >= C * 16) break;
+      float x = 0.f;
+#pragma unroll
+      for (int k = 0; k < G::KS; ++k) x += L.Rp[k][nn][r];
+      p.R[pcd + r * D + col0 + nn] = -x;  // R = -(sum of the shares)
+      p.U[pcd + r * D + col0 + nn] = L.Up[0][nn][r] + L.Up[1][nn][r];
     }
+  };
+  for (int ci = lo; ci < hi; ++ci) {
+    const size_t b = blk(ci), bn = blk(ci + 1 < hi ? ci + 1 : ci);
+    put_ru(blk(ci > lo ? ci - 1 : ci));
+    if (NST == G::NW || w < NST) {  // publish the entering state (every wave at d = 128)
+      *reinterpret_cast<f32x4*>(&L.St[m][16 * w + 4 * g]) = f32x4{sreg[0], sreg[1], sreg[2], sreg[3]};
+#pragma unroll
+      for (int i = 0; i < 4; ++i) p.S[(b * D + 16 * w + 4 * g + i) * D + col0 + m] = sreg[i];
+    }
+    __syncthreads();
+    {  // chunk ci + 2's operands into L2
+      static_assert(NVB * kSerThreads >= (3 * C * D + C * C) / 32 + D / 32, "one line per lane covers them");
+      const size_t b2 = blk(ci + 2 < hi ? ci + 2 : hi - 1);
+      const float* const bp[5] = {p.Kt + b2 * C * D, p.Kb + b2 * C * D, p.V + b2 * C * D, p.T + b2 * C * C,
+                                  p.gn + b2 * D};
+      const int ln[5] = {C * D / 32, C * D / 32, C * D / 32, C * C / 32, D / 32};
+      touch_done(tch);
+      tch = l2_touch<5>(bp, ln, vb, NVB, w, G::NW, l);
+    }
+    {  // share rks of Kt S (minus V in share 0) for row tile rrt
+      f32x4 acc = rks == 0 ? f32x4{-rv[0], -rv[1], -rv[2], -rv[3]} : f32x4{0, 0, 0, 0};
+      float sb[RJ];
+      ld_run<RJ>(sb, &L.St[m][rks * DK + g * RJ]);
+#pragma unroll
+      for (int j = 0; j < RJ; ++j) acc = mfma4(ra[j], sb[j], acc);
+      *reinterpret_cast<f32x4*>(&L.Rp[rks][m][16 * rrt + 4 * g]) = acc;
+    }
+    load_r(bn);
+    __builtin_amdgcn_sched_barrier(0);  // keep the loads where they are
+    __syncthreads();
+    if (2 * NRT == G::NW || w < 2 * NRT) {  // half uhs of T R for row tile urt
+      f32x4 acc = {0, 0, 0, 0};
+      const int k0 = uhs * ulh + g * uj;
+#pragma unroll
+      for (int j = 0; j < UJM; ++j)
+        if (j < uj) {
+          float x = 0.f;
+#pragma unroll
+          for (int k = 0; k < G::KS; ++k) x += L.Rp[k][m][k0 + j];
+          acc = mfma4(ta[j], -x, acc);
+        }
+      *reinterpret_cast<f32x4*>(&L.Up[uhs][m][16 * urt + 4 * g]) = acc;
+    }
+    load_u(bn);
+    __builtin_amdgcn_sched_barrier(0);  // keep the loads where they are
+    __syncthreads();
+    if (NST == G::NW || w < NST) {  // S' = gam_n S + Kb^T U for state tile w
+      float* kw = &L.Kw[w][0][0];
+      kb.put(kw, C, l);
+      f32x4 acc = {gam[0] * sreg[0], gam[1] * sreg[1], gam[2] * sreg[2], gam[3] * sreg[3]};
+      float a[SJ], u0[SJ], u1[SJ];
+      ld_run<SJ>(a, kw + m * (C + 4) + g * SJ);
+      ld_run<SJ>(u0, &L.Up[0][m][g * SJ]);
+      ld_run<SJ>(u1, &L.Up[1][m][g * SJ]);
+#pragma unroll
+      for (int j = 0; j < SJ; ++j) acc = mfma4(a[j], u0[j] + u1[j], acc);
+#pragma unroll
+      for (int i = 0; i < 4; ++i) sreg[i] = acc[i];
+    }
+    load_s(bn);
+    __builtin_amdgcn_sched_barrier(0);  // keep the loads where they are
+  }
+  if (lo < hi) put_ru(blk(hi - 1));
+  if (s_out && w < NST) {  // the state after the pass's last chunk
+#pragma unroll
+    for (int i = 0; i < 4; ++i) s_out[(((size_t)n * H + h) * D + 16 * w + 4 * g + i) * D + col0 + m] = sreg[i];
   }
 }
 
 template <int D, int C>
 struct BwdLds {
-  union {
-    struct {
-      float P[C][C + 16];   // read transposed
-      float T[C][C + 16];   // read transposed
-      float Kb[C][D + 4];
-    } a;
-    struct {
-      float Qt[C][D + 16];  // read transposed
-      float Kt[C][D + 16];  // read transposed
-    } b;
-  } u;
-  float X[D][kCols];     // dS'
-  float dO[C][kCols];
-  float dU[C][kCols];
-  float ndR[C][kCols];   // -dR
-  float gn[D];
+  float Xt[16][D + 4];                          // dS'^T: [value column][channel]
+  float Up[SerGeom<D, C>::KS][16][C + 4];       // shares of dU, transposed
+  float Rp[2][16][C + 4];                       // halves of dR, transposed
+  float dOt[2][16][C + 4];                      // dO slice, transposed; by chunk parity
+  float Wt[SerGeom<D, C>::NW][2][16][C + 4];    // each wave's slabs, transposed
 };
 
 // Serial backward over a sequence's chunks for 16 value columns: dS' of
 // every chunk, dU = P^T dO + Kb dS', dR = T^T dU, and the carried
-// dS = gam_n dS' + Qt^T dO - Kt^T dR; the last one is dS0.  Eight waves; the
-// next chunk's P, T, Kb and this chunk's Qt, Kt load while earlier work runs.
+// dS = gam_n dS' + Qt^T dO - Kt^T dR; the last one is dS0.  dU stage: wave w
+// takes row tile w % NRT and channel share w / NRT of Kb dS' (share 0 adds
+// P^T dO, over k >= 16 rt).  dR stage: waves w < 2 NRT take row tile w % NRT
+// and half w / NRT of its k >= 16 rt.  dS stage: wave t < D/16 updates its
+// tile of the carried gradient.
 template <int D, int C>
 __global__ __launch_bounds__(kSerThreads) void bwd_bwd_states_kernel(Planes p, Geo geo,
                                                                      const float* __restrict__ dfin,
                                                                      float* __restrict__ ds0) {
+  typedef SerGeom<D, C> G;
+  constexpr int NVB = D / kCols, NRT = G::NRT, NST = G::NST, DK = G::DK, RJ = G::RJ, SJ = G::SJ,
+                TJ = G::TJ, kFin = G::FIN;
   extern __shared__ float sm[];
   BwdLds<D, C>& L = *reinterpret_cast<BwdLds<D, C>*>(sm);
-  constexpr int NVB = D / kCols, NT = kSerThreads, NW = NT / 64;
   const int H = geo.H;
-  const int vb = blockIdx.x % NVB, nh = blockIdx.x / NVB;
+  int nh, vb;
+  if (!serial_slot<NVB>(geo.num_seqs * H, nh, vb)) return;
   const int n = nh / H, h = nh % H, col0 = vb * kCols;
-  const int tid = threadIdx.x, w = tid >> 6, l = tid & 63, m = l & 15, g = l >> 4;
+  const int tid = threadIdx.x, w = __builtin_amdgcn_readfirstlane(tid >> 6), l = tid & 63;
+  const int m = l & 15, g = l >> 4;
   int bos, eos, base, lo, hi;
   seq_of<C>(geo, n, bos, eos, base);
   seg_range<C>(geo, bos, eos, lo, hi);
-  for (int idx = tid; idx < D * kCols; idx += NT) {
-    const int i = idx / kCols, j = idx % kCols;
-    L.X[i][j] = dfin ? dfin[(((size_t)n * H + h) * D + i) * D + col0 + j] : 0.f;
-  }
-  Prefetch<C, C, NT> pP, pT;
-  Prefetch<C, D, NT> pKb, pQt, pKt;
-  Prefetch<C, kCols, NT, D> pdO;  // this workgroup's value columns
-  Prefetch<1, D, NT> pG;          // gam_n
+  const int urt = w % NRT, uks = w / NRT;                 // dU stage
+  const int pn = C - 16 * urt, pj = pn / 4;               // its P^T part (share 0): k >= 16 urt
+  const int rrt = w % NRT, rhs = (w / NRT) & 1;           // dR stage (w < 2 NRT)
+  const int rn = C - 16 * rrt, rj = rn / 8;               // k >= 16 rrt, in two halves
+  const int st = w < NST ? w : NST - 1;                   // dS stage tile
   auto blk = [&](int ci) { return (size_t)(base + ci - geo.c0) * H + h; };
-  // P, T, K-bar, dO and gam_n of a chunk load a step ahead, Q*gam and K*gam
-  // half a step ahead (after the previous chunk's copies are stored).
-  auto fetch_a = [&](size_t b) {
-    pP.load(p.P + b * C * C);
-    pT.load(p.T + b * C * C);
-    pKb.load(p.Kb + b * C * D);
-    pdO.load(p.dO + b * C * D + col0);
-    pG.load(p.gn + b * D);
+  float* w0 = &L.Wt[w][0][0][0];
+  float* w1 = &L.Wt[w][1][0][0];
+
+  float ua[RJ], xreg[4];
+  Slab<C> ps, ts, qs, ks;
+  f32x4 dov, gam;
+  const int du = tid < 4 * C ? tid : 4 * C - 1;  // this thread's 16 bytes of the dO slice
+  // The dO slice is requested first: it goes to LDS at the top of the next
+  // step, so a late request would hold that step back by a memory round trip.
+  auto load_u = [&](size_t b) {
+    dov = *reinterpret_cast<const f32x4*>(p.dO + (b * C + (du >> 2)) * D + col0 + 4 * (du & 3));
+    ld_run<RJ>(ua, p.Kb + (b * C + 16 * urt + m) * D + uks * DK + g * RJ);
+    ps.fetch(p.P + b * C * C, C, 16 * urt, pn, 16 * urt, l);
   };
-  auto fetch_b = [&](size_t b) {
-    pQt.load(p.Qt + b * C * D);
-    pKt.load(p.Kt + b * C * D);
+  auto load_r = [&](size_t b) { ts.fetch(p.T + b * C * C, C, 16 * rrt, rn, 16 * rrt, l); };
+  auto load_s = [&](size_t b) {
+    qs.fetch(p.Qt + b * C * D, D, 0, C, 16 * st, l);
+    ks.fetch(p.Kt + b * C * D, D, 0, C, 16 * st, l);
+    gam = *reinterpret_cast<const f32x4*>(p.gn + b * D + 16 * st + 4 * g);
   };
+#pragma unroll
+  for (int i = 0; i < 4; ++i)
+    xreg[i] = dfin ? dfin[(((size_t)n * H + h) * D + 16 * st + 4 * g + i) * D + col0 + m] : 0.f;
+  __builtin_amdgcn_s_waitcnt(0);  // as in the forward pass
+  float tch = 0.f;  // the last L2 request's value
   if (lo < hi) {
-    fetch_a(blk(hi - 1));
-    fetch_b(blk(hi - 1));
+    load_u(blk(hi - 1));
+    load_r(blk(hi - 1));
+    load_s(blk(hi - 1));
   }
-  for (int ci = hi - 1; ci >= lo; --ci) {
-    const size_t b = blk(ci);
+  // dU and dR of a chunk go out at the top of the next step (and of the last
+  // one after the loop), as in the forward pass.
+  auto put_ur = [&](size_t b) {
     const size_t pcd = b * C * D;
-    __syncthreads();
-    pP.template store<C + 16>(&L.u.a.P[0][0]);
-    pT.template store<C + 16>(&L.u.a.T[0][0]);
-    pKb.template store<D + 4>(&L.u.a.Kb[0][0]);
-    pdO.template store<kCols>(&L.dO[0][0]);
-    pG.template store<D>(&L.gn[0]);
-    for (int idx = tid; idx < D * kCols; idx += NT) {
-      const int i = idx / kCols, j = idx % kCols;
-      p.dSn[(b * D + i) * D + col0 + j] = L.X[i][j];
-    }
-    __syncthreads();
-    if (ci > lo) fetch_a(blk(ci - 1));
-    for (int rt = w; rt < C / 16; rt += NW) {  // dU = P^T dO + Kb dS'
-      f32x4 acc = {0, 0, 0, 0}, acc1 = {0, 0, 0, 0};
-      for (int k0 = 16 * rt; k0 < C; k0 += 4) acc = mfma4(L.u.a.P[k0 + g][16 * rt + m], L.dO[k0 + g][m], acc);
-#pragma unroll 8
-      for (int k0 = 0; k0 < D; k0 += 8) {
-        acc1 = mfma4(L.u.a.Kb[16 * rt + m][k0 + g], L.X[k0 + g][m], acc1);
-        acc = mfma4(L.u.a.Kb[16 * rt + m][k0 + 4 + g], L.X[k0 + 4 + g][m], acc);
-      }
-      acc += acc1;
 #pragma unroll
-      for (int i = 0; i < 4; ++i) {
-        const int r = 16 * rt + 4 * g + i;
-        L.dU[r][m] = acc[i];
-        p.dU[pcd + r * D + col0 + m] = acc[i];
-      }
+    for (int xf = 0; xf < kFin; ++xf) {
+      const int e = tid + kSerThreads * xf, nn = e & 15, r = e >> 4;
+      if (C * 16 % kSerThreads != 0 && e >= C * 16) break;
+      float x = 0.f;
+#pragma unroll
+      for (int k = 0; k < G::KS; ++k) x += L.Up[k][nn][r];
+      p.dU[pcd + r * D + col0 + nn] = x;
+      p.dR[pcd + r * D + col0 + nn] = L.Rp[0][nn][r] + L.Rp[1][nn][r];
+    }
+  };
+  for (int ci = hi - 1; ci >= lo; --ci) {
+    const size_t b = blk(ci), bn = blk(ci > lo ? ci - 1 : ci);
+    put_ur(blk(ci < hi - 1 ? ci + 1 : ci));
+    float* dot = &L.dOt[ci & 1][0][0];
+    if (tid < 4 * C) {  // this chunk's dO slice, transposed
+#pragma unroll
+      for (int e = 0; e < 4; ++e) dot[(4 * (du & 3) + e) * (C + 4) + (du >> 2)] = dov[e];
+    }
+    if (NST == G::NW || w < NST) {  // publish dS'
+      *reinterpret_cast<f32x4*>(&L.Xt[m][16 * w + 4 * g]) = f32x4{xreg[0], xreg[1], xreg[2], xreg[3]};
+#pragma unroll
+      for (int i = 0; i < 4; ++i) p.dSn[(b * D + 16 * w + 4 * g + i) * D + col0 + m] = xreg[i];
     }
     __syncthreads();
-    for (int rt = w; rt < C / 16; rt += NW) {  // dR = T^T dU
+    {  // chunk ci - 2's operands into L2
+      static_assert(NVB * kSerThreads >= (4 * C * D + 2 * C * C) / 32 + D / 32, "one line per lane covers them");
+      const size_t b2 = blk(ci - 2 >= lo ? ci - 2 : lo);
+      const float* const bp[7] = {p.Kb + b2 * C * D, p.Qt + b2 * C * D, p.Kt + b2 * C * D, p.dO + b2 * C * D,
+                                  p.P + b2 * C * C, p.T + b2 * C * C, p.gn + b2 * D};
+      const int ln[7] = {C * D / 32, C * D / 32, C * D / 32, C * D / 32, C * C / 32, C * C / 32, D / 32};
+      touch_done(tch);
+      tch = l2_touch<7>(bp, ln, vb, NVB, w, G::NW, l);
+    }
+    {  // share uks of Kb dS' (plus P^T dO in share 0) for row tile urt
       f32x4 acc = {0, 0, 0, 0};
-      for (int k0 = 16 * rt; k0 < C; k0 += 4) acc = mfma4(L.u.a.T[k0 + g][16 * rt + m], L.dU[k0 + g][m], acc);
+      float xb[RJ];
+      ld_run<RJ>(xb, &L.Xt[m][uks * DK + g * RJ]);
 #pragma unroll
-      for (int i = 0; i < 4; ++i) {
-        const int r = 16 * rt + 4 * g + i;
-        L.ndR[r][m] = -acc[i];
-        p.dR[pcd + r * D + col0 + m] = acc[i];
+      for (int j = 0; j < RJ; ++j) acc = mfma4(ua[j], xb[j], acc);
+      if (uks == 0) {
+        ps.put(w0, pn, l);
+        float a[SJ], d[SJ];
+        ld_run<SJ>(a, w0 + m * (C + 4) + g * pj);       // P[16 urt + g pj + j][16 urt + m]
+        ld_run<SJ>(d, dot + m * (C + 4) + 16 * urt + g * pj);  // dO[16 urt + g pj + j][m]
+#pragma unroll
+        for (int j = 0; j < SJ; ++j)
+          if (j < pj) acc = mfma4(a[j], d[j], acc);
       }
+      *reinterpret_cast<f32x4*>(&L.Up[uks][m][16 * urt + 4 * g]) = acc;
     }
+    load_u(bn);
+    __builtin_amdgcn_sched_barrier(0);  // keep the loads where they are
     __syncthreads();
-    pQt.template store<D + 16>(&L.u.b.Qt[0][0]);
-    pKt.template store<D + 16>(&L.u.b.Kt[0][0]);
-    if (ci > lo) fetch_b(blk(ci - 1));
-    __syncthreads();
-    for (int t = w; t < D / 16; t += NW) {  // dS = gam_n dS' + Qt^T dO - Kt^T dR
-      f32x4 acc, acc1 = {0, 0, 0, 0};
+    if (2 * NRT == G::NW || w < 2 * NRT) {  // half rhs of T^T dU for row tile rrt
+      ts.put(w0, rn, l);
+      const int k0 = rhs * (rn / 2) + g * rj;  // relative to row 16 rrt
+      f32x4 acc = {0, 0, 0, 0};
 #pragma unroll
-      for (int i = 0; i < 4; ++i) {
-        const int c = 16 * t + 4 * g + i;
-        acc[i] = L.gn[c] * L.X[c][m];
-      }
-#pragma unroll 8
-      for (int k0 = 0; k0 < C; k0 += 4) {
-        acc = mfma4(L.u.b.Qt[k0 + g][16 * t + m], L.dO[k0 + g][m], acc);
-        acc1 = mfma4(L.u.b.Kt[k0 + g][16 * t + m], L.ndR[k0 + g][m], acc1);
-      }
+      for (int j = 0; j < TJ; ++j)
+        if (j < rj) {
+          float x = 0.f;
 #pragma unroll
-      for (int i = 0; i < 4; ++i) L.X[16 * t + 4 * g + i][m] = acc[i] + acc1[i];
+          for (int k = 0; k < G::KS; ++k) x += L.Up[k][m][16 * rrt + k0 + j];
+          acc = mfma4(w0[m * (C + 4) + k0 + j], x, acc);
+        }
+      *reinterpret_cast<f32x4*>(&L.Rp[rhs][m][16 * rrt + 4 * g]) = acc;
     }
+    load_r(bn);
+    __builtin_amdgcn_sched_barrier(0);  // keep the loads where they are
+    __syncthreads();
+    if (NST == G::NW || w < NST) {  // dS = gam_n dS' + Qt^T dO - Kt^T dR for tile w
+      qs.put(w0, C, l);
+      ks.put(w1, C, l);
+      f32x4 acc = {gam[0] * xreg[0], gam[1] * xreg[1], gam[2] * xreg[2], gam[3] * xreg[3]};
+      float qa[SJ], ka[SJ], d[SJ], r0[SJ], r1[SJ];
+      ld_run<SJ>(qa, w0 + m * (C + 4) + g * SJ);
+      ld_run<SJ>(ka, w1 + m * (C + 4) + g * SJ);
+      ld_run<SJ>(d, dot + m * (C + 4) + g * SJ);
+      ld_run<SJ>(r0, &L.Rp[0][m][g * SJ]);
+      ld_run<SJ>(r1, &L.Rp[1][m][g * SJ]);
+#pragma unroll
+      for (int j = 0; j < SJ; ++j) {
+        acc = mfma4(qa[j], d[j], acc);
+        acc = mfma4(ka[j], -(r0[j] + r1[j]), acc);
+      }
+#pragma unroll
+      for (int i = 0; i < 4; ++i) xreg[i] = acc[i];
+    }
+    load_s(bn);
+    __builtin_amdgcn_sched_barrier(0);  // keep the loads where they are
   }
-  __syncthreads();
-  if (ds0) {
-    for (int idx = tid; idx < D * kCols; idx += NT) {
-      const int i = idx / kCols, j = idx % kCols;
-      ds0[(((size_t)n * H + h) * D + i) * D + col0 + j] = L.X[i][j];
-    }
+  if (lo < hi) put_ur(blk(lo));
+  if (ds0 && w < NST) {
+#pragma unroll
+    for (int i = 0; i < 4; ++i) ds0[(((size_t)n * H + h) * D + 16 * w + 4 * g + i) * D + col0 + m] = xreg[i];
   }
 }
 
@@ -911,7 +1092,7 @@ hipError_t launch_backward_t(const BackwardArgs& a) {
   Planes p = carve(planes, NBmax, C, D);
   auto state_in = [&](int s) { return s == 0 ? a.initial_state : ckpt + (size_t)(s - 1) * nhdd; };
 
-  const int serial = a.num_seqs * a.H * (D / kCols);
+  const int serial = serial_blocks(a.num_seqs * a.H, D / kCols);
   const size_t flds_s = sizeof(FwdLds<D, C>), blds_s = sizeof(BwdLds<D, C>);
   hipError_t e = hipFuncSetAttribute(reinterpret_cast<const void*>(&bwd_fwd_states_kernel<D, C>),
                                      hipFuncAttributeMaxDynamicSharedMemorySize, (int)flds_s);

@@ -320,7 +320,8 @@ __global__ __launch_bounds__(kStThreads) void dplr_states_kernel(DPlanes p, Geo 
   StLds<D, C>& L = *reinterpret_cast<StLds<D, C>*>(sm);
   constexpr int NVB = D / kColsD, NT = kStThreads, NW = NT / 64;
   const int H = geo.H;
-  const int vb = blockIdx.x % NVB, nh = blockIdx.x / NVB;
+  int nh, vb;
+  if (!serial_slot<NVB>(geo.num_seqs * H, nh, vb)) return;
   const int n = nh / H, h = nh % H, col0 = vb * kColsD;
   const int tid = threadIdx.x, w = tid >> 6, l = tid & 63, m = l & 15, g = l >> 4;
   int bos, eos, base;
@@ -442,7 +443,7 @@ hipError_t launch_dplr_t(const DplrArgs& a) {
   if (a.cu_seqlens)
     hipLaunchKernelGGL(chunk_table_kernel, dim3(1), dim3(1024), 0, a.stream, a.cu_seqlens,
                        const_cast<int32_t*>(geo.off), a.num_seqs, a.total_tokens, C, 0, INT32_MAX / 2);
-  const int serial = a.num_seqs * a.H * (D / kColsD);
+  const int serial = serial_blocks(a.num_seqs * a.H, D / kColsD);
   const size_t slds = sizeof(StLds<D, C>);
   hipError_t e = hipFuncSetAttribute(reinterpret_cast<const void*>(&dplr_states_kernel<D, C, TIED>),
                                      hipFuncAttributeMaxDynamicSharedMemorySize, (int)slds);

@@ -26,6 +26,21 @@ struct Geo {
 
 __device__ __forceinline__ int clampi(int x, int lo, int hi) { return x < lo ? lo : (x > hi ? hi : x); }
 
+// Placement of the serial passes' workgroups, one per (sequence, head) and
+// block of NVB value columns.  Consecutive block ids rotate over the chip's
+// eight XCDs, so the NVB column blocks of one (sequence, head) take ids on
+// the same XCD and share its L2 for the chunk operands that all of them
+// read.  Launch serial_blocks(pairs, NVB) workgroups; serial_slot gives a
+// workgroup its pair nh and column block vb, false for the padding ids.
+inline int serial_blocks(int pairs, int nvb) { return (pairs + 7) / 8 * 8 * nvb; }
+template <int NVB>
+__device__ __forceinline__ bool serial_slot(int pairs, int& nh, int& vb) {
+  const int bid = blockIdx.x, xcd = bid & 7, slot = bid >> 3;
+  nh = (slot / NVB) * 8 + xcd;
+  vb = slot % NVB;
+  return nh < pairs;
+}
+
 template <int C>
 __device__ __forceinline__ void seq_of(const Geo& g, int n, int& bos, int& eos, int& base) {
   if (g.cu) {
@@ -279,12 +294,14 @@ struct Prefetch {
   static constexpr int C4 = COLS / 4, N = (ROWS * C4 + NT - 1) / NT;
   static_assert(COLS % 4 == 0 && SLD % 4 == 0, "float4 rows");
   f32x4 v[N];
+  // Every thread loads, those past the block its last vector again (their
+  // stores are skipped): a load under a branch would make the code after the
+  // branch wait for every load issued before it.
   __device__ __forceinline__ void load(const float* __restrict__ src) {
 #pragma unroll
     for (int x = 0; x < N; ++x) {
-      const int idx = threadIdx.x + NT * x;
-      if (idx < ROWS * C4)
-        v[x] = *reinterpret_cast<const f32x4*>(src + (size_t)(idx / C4) * SLD + 4 * (idx % C4));
+      const int i = threadIdx.x + NT * x, idx = i < ROWS * C4 ? i : ROWS * C4 - 1;
+      v[x] = *reinterpret_cast<const f32x4*>(src + (size_t)(idx / C4) * SLD + 4 * (idx % C4));
     }
   }
   template <int LD>
