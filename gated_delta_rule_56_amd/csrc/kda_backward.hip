@@ -72,12 +72,14 @@ struct Planes {
   float *S, *dSn;                                                                 // [D][D]
   float *beta, *db;                                                               // [C]
   float *gn;                                                                      // [D]
+  float *dgp;  // [D/16][D]: rowsum(dS' * S) over each serial workgroup's 16 value columns
   int32_t* fast;                                                                  // [1] per (chunk, head)
 };
 
 size_t plane_bytes(size_t NB, int C, int D) {
   const size_t cd = a256(NB * C * D * 4), cc = a256(NB * C * C * 4), dd = a256(NB * D * D * 4);
-  return 16 * cd + 7 * cc + 2 * dd + 2 * a256(NB * C * 4) + a256(NB * D * 4) + a256(NB * 4);
+  return 16 * cd + 7 * cc + 2 * dd + 2 * a256(NB * C * 4) + a256(NB * D * 4) + a256(NB * (D / 16) * D * 4) +
+         a256(NB * 4);
 }
 
 Planes carve(char* p, size_t NB, int C, int D) {
@@ -94,6 +96,8 @@ Planes carve(char* p, size_t NB, int C, int D) {
   x.db = reinterpret_cast<float*>(p); p += a256(NB * C * 4);
   x.gn = reinterpret_cast<float*>(p);
   p += a256(NB * D * 4);
+  x.dgp = reinterpret_cast<float*>(p);
+  p += a256(NB * (D / 16) * D * 4);
   x.fast = reinterpret_cast<int32_t*>(p);
   return x;
 }
@@ -430,6 +434,16 @@ struct SerGeom {
   static_assert(NW % NRT == 0 && D % (4 * KS) == 0 && NST <= NW, "work split");
 };
 
+// Sum over the 16 lanes of each row of the wave (DPP row rotations; every
+// lane ends with its row's sum).
+__device__ __forceinline__ float row_sum16(float x) {
+  x += __builtin_bit_cast(float, __builtin_amdgcn_mov_dpp(__builtin_bit_cast(int, x), 0x128, 0xF, 0xF, true));
+  x += __builtin_bit_cast(float, __builtin_amdgcn_mov_dpp(__builtin_bit_cast(int, x), 0x124, 0xF, 0xF, true));
+  x += __builtin_bit_cast(float, __builtin_amdgcn_mov_dpp(__builtin_bit_cast(int, x), 0x122, 0xF, 0xF, true));
+  x += __builtin_bit_cast(float, __builtin_amdgcn_mov_dpp(__builtin_bit_cast(int, x), 0x121, 0xF, 0xF, true));
+  return x;
+}
+
 // N consecutive floats (16-byte aligned when N % 4 == 0, 8-byte when even).
 template <int N>
 __device__ __forceinline__ void ld_run(float (&d)[N], const float* src) {
@@ -706,11 +720,15 @@ __global__ __launch_bounds__(kSerThreads) void bwd_bwd_states_kernel(Planes p, G
   float ua[RJ], xreg[4];
   Slab<C> ps, ts, qs, ks;
   f32x4 dov, gam;
+  float sv[4];  // S entering the chunk: rows 16 st + 4 g .. + 3, this lane's value column
   const int du = tid < 4 * C ? tid : 4 * C - 1;  // this thread's 16 bytes of the dO slice
-  // The dO slice is requested first: it goes to LDS at the top of the next
-  // step, so a late request would hold that step back by a memory round trip.
+  // The dO slice and the S slice are requested first: both are used at the top
+  // of the next step, so a late request would hold that step back by a
+  // memory round trip.
   auto load_u = [&](size_t b) {
     dov = *reinterpret_cast<const f32x4*>(p.dO + (b * C + (du >> 2)) * D + col0 + 4 * (du & 3));
+#pragma unroll
+    for (int i = 0; i < 4; ++i) sv[i] = p.S[(b * D + 16 * st + 4 * g + i) * D + col0 + m];
     ld_run<RJ>(ua, p.Kb + (b * C + 16 * urt + m) * D + uks * DK + g * RJ);
     ps.fetch(p.P + b * C * C, C, 16 * urt, pn, 16 * urt, l);
   };
@@ -753,20 +771,27 @@ __global__ __launch_bounds__(kSerThreads) void bwd_bwd_states_kernel(Planes p, G
 #pragma unroll
       for (int e = 0; e < 4; ++e) dot[(4 * (du & 3) + e) * (C + 4) + (du >> 2)] = dov[e];
     }
-    if (NST == G::NW || w < NST) {  // publish dS'
+    if (NST == G::NW || w < NST) {  // publish dS'; this block's share of rowsum(dS' * S)
       *reinterpret_cast<f32x4*>(&L.Xt[m][16 * w + 4 * g]) = f32x4{xreg[0], xreg[1], xreg[2], xreg[3]};
 #pragma unroll
       for (int i = 0; i < 4; ++i) p.dSn[(b * D + 16 * w + 4 * g + i) * D + col0 + m] = xreg[i];
+      float t[4];
+#pragma unroll
+      for (int i = 0; i < 4; ++i) t[i] = row_sum16(xreg[i] * sv[i]);  // over the 16 columns
+      // every lane stores (lanes m and m + 4k store the same value)
+      const int i4 = m & 3;
+      p.dgp[(b * NVB + vb) * D + 16 * w + 4 * g + i4] = i4 == 0 ? t[0] : i4 == 1 ? t[1] : i4 == 2 ? t[2] : t[3];
     }
     __syncthreads();
     {  // chunk ci - 2's operands into L2
-      static_assert(NVB * kSerThreads >= (4 * C * D + 2 * C * C) / 32 + D / 32, "one line per lane covers them");
+      static_assert(NVB * kSerThreads >= (4 * C * D + 2 * C * C + D * D) / 32 + D / 32,
+                    "one line per lane covers them");
       const size_t b2 = blk(ci - 2 >= lo ? ci - 2 : lo);
-      const float* const bp[7] = {p.Kb + b2 * C * D, p.Qt + b2 * C * D, p.Kt + b2 * C * D, p.dO + b2 * C * D,
-                                  p.P + b2 * C * C, p.T + b2 * C * C, p.gn + b2 * D};
-      const int ln[7] = {C * D / 32, C * D / 32, C * D / 32, C * D / 32, C * C / 32, C * C / 32, D / 32};
+      const float* const bp[8] = {p.Kb + b2 * C * D, p.Qt + b2 * C * D, p.Kt + b2 * C * D, p.dO + b2 * C * D,
+                                  p.P + b2 * C * C, p.T + b2 * C * C, p.S + b2 * D * D, p.gn + b2 * D};
+      const int ln[8] = {C * D / 32, C * D / 32, C * D / 32, C * D / 32, C * C / 32, C * C / 32, D * D / 32, D / 32};
       touch_done(tch);
-      tch = l2_touch<7>(bp, ln, vb, NVB, w, G::NW, l);
+      tch = l2_touch<8>(bp, ln, vb, NVB, w, G::NW, l);
     }
     {  // share uks of Kb dS' (plus P^T dO in share 0) for row tile urt
       f32x4 acc = {0, 0, 0, 0};
@@ -937,60 +962,71 @@ struct BwdOut {
 // Y3 = dBm^T Kt + dP^T Qt, with dq += gam Y2, dk += gam Y1 + exp(-Gamma) Y3,
 // dGamma += Kt Y1 + Qt Y2 - Kh Y3; for strong-decay chunks the sums Z1, Z2,
 // Z3 themselves (bwd_pairs_tile_kernel), with dq += Z2, dk += Z1 + Z3,
-// dGamma += k (Z1 - Z3) + q Z2.  One thread per channel.
+// dGamma += k (Z1 - Z3) + q Z2.  256 threads per (chunk, head), D/4 threads
+// per row with four consecutive channels each, so every plane is read with
+// 16-byte loads and every output row written with 16-byte stores; the rows'
+// dGamma terms wait in LDS for the reverse cumulative sum, one thread per
+// channel.
 template <int D, int C>
-__global__ __launch_bounds__(D) void bwd_final_fast_kernel(Planes p, Geo geo, BwdOut out) {
-  const int b = blockIdx.x, c = threadIdx.x, H = geo.H;
+__global__ __launch_bounds__(256) void bwd_final_fast_kernel(Planes p, Geo geo, BwdOut out) {
+  constexpr int TPR = D / 4, RPP = 256 / TPR;  // threads per row, rows per pass
+  static_assert(C % RPP == 0 && D % RPP == 0, "whole passes");
+  __shared__ __attribute__((aligned(16))) float term[C][D + 4];
+  __shared__ __attribute__((aligned(16))) float kbp[RPP][D];
+  const int b = blockIdx.x, tid = threadIdx.x, H = geo.H;
+  const int c0 = 4 * (tid % TPR), rs = tid / TPR;
   const bool fast = p.fast[b] != 0;
   const int gch = b / H, h = b % H;
   int n, t0, len;
   chunk_of<C>(geo, gch, n, t0, len);
   const size_t pcd = (size_t)b * C * D;
-  const float* Y1 = p.R + pcd;
-  const float* Y2 = p.U + pcd;
-  const float* Y3 = p.dU + pcd;
-  // dgam_n[c] = rowsum(dS' * S)[c]: each wave reduces whole rows, its lanes
-  // reading them contiguously, and parks the sums in LDS.
-  __shared__ float rowsum[D];
-  {
-    constexpr int NWV = D / 64, PL = D / 64;  // waves; elements per lane and row
-    const int w = c >> 6, l = c & 63;
-    const float* S = p.S + (size_t)b * D * D;
-    const float* dS = p.dSn + (size_t)b * D * D;
-    for (int i = w; i < D; i += NWV) {
-      float t = 0.f;
+  auto ld4 = [](const float* x) { return *reinterpret_cast<const f32x4*>(x); };
+  // The pairwise terms' operands: Kt, Qt, Kh when factored, else K, Q, K.
+  const float* a1 = fast ? p.Kt : p.K;
+  const float* a2 = fast ? p.Qt : p.Q;
+  const float* a3 = fast ? p.Kh : p.K;
+  const f32x4 gl = ld4(p.Gam + pcd + (size_t)(C - 1) * D + c0);
+  f32x4 kb = {0, 0, 0, 0};
+  for (int r = rs; r < C; r += RPP) {
+    const size_t e0 = pcd + (size_t)r * D + c0;
+    const f32x4 gr = ld4(p.Gam + e0), dqt = ld4(p.dQt + e0), dkt = ld4(p.dKt + e0), dkb = ld4(p.dKb + e0);
+    const f32x4 kbv = ld4(p.Kb + e0), qt = ld4(p.Qt + e0), kt = ld4(p.Kt + e0), dr = ld4(p.dR + e0);
+    const f32x4 y1 = ld4(p.R + e0), y2 = ld4(p.U + e0), y3 = ld4(p.dU + e0);
+    const f32x4 x1 = ld4(a1 + e0), x2 = ld4(a2 + e0), x3 = ld4(a3 + e0);
+    f32x4 tv, dq, dk;
 #pragma unroll
-      for (int e = 0; e < PL; ++e) t += S[(size_t)i * D + 64 * e + l] * dS[(size_t)i * D + 64 * e + l];
-#pragma unroll
-      for (int off = 32; off > 0; off >>= 1) t += __shfl_xor(t, off);
-      if (l == 0) rowsum[i] = t;
+    for (int e = 0; e < 4; ++e) {
+      tv[e] = dqt[e] * qt[e] + dkt[e] * kt[e] - dkb[e] * kbv[e] + x1[e] * y1[e] + x2[e] * y2[e] - x3[e] * y3[e];
+      kb[e] += dkb[e] * kbv[e];
+      const float ga = __expf(gr[e]), gb = dkb[e] * __expf(gl[e] - gr[e]);
+      dq[e] = fast ? (dqt[e] + y2[e]) * ga : dqt[e] * ga + y2[e];
+      dk[e] = fast ? (dkt[e] + y1[e]) * ga + gb + __expf(-gr[e]) * y3[e] : dkt[e] * ga + y1[e] + gb + y3[e];
     }
-  }
-  float kbsum = 0.f;
-#pragma unroll 8
-  for (int r = 0; r < C; ++r) kbsum += p.dKb[pcd + r * D + c] * p.Kb[pcd + r * D + c];
-  __syncthreads();
-  const float dgn = rowsum[c];
-  const float gl = p.Gam[pcd + (C - 1) * D + c];
-  float run = kbsum + dgn * p.gn[(size_t)b * D + c];  // dGamma_n lands on the last row
-#pragma unroll 4
-  for (int r = C - 1; r >= 0; --r) {
-    const size_t e0 = pcd + r * D + c;
-    const float gr = p.Gam[e0], ga = __expf(gr);
-    const float dqt = p.dQt[e0], dkt = p.dKt[e0], dkb = p.dKb[e0];
-    const float y1 = Y1[r * D + c], y2 = Y2[r * D + c], y3 = Y3[r * D + c];
-    run += dqt * p.Qt[e0] + dkt * p.Kt[e0] - dkb * p.Kb[e0] +
-           (fast ? p.Kt[e0] * y1 + p.Qt[e0] * y2 - p.Kh[e0] * y3 : p.K[e0] * (y1 - y3) + p.Q[e0] * y2);
+    *reinterpret_cast<f32x4*>(&term[r][c0]) = tv;
     if (r < len) {
-      const size_t ti = ((size_t)(t0 + r) * H + h) * D + c;
-      out.dq[ti] = fast ? (dqt + y2) * ga : dqt * ga + y2;
-      out.dk[ti] = fast ? (dkt + y1) * ga + dkb * __expf(gl - gr) + __expf(-gr) * y3
-                        : dkt * ga + y1 + dkb * __expf(gl - gr) + y3;
-      out.dg[ti] = run;
-      out.dv[ti] = p.dR[e0];
+      const size_t ti = ((size_t)(t0 + r) * H + h) * D + c0;
+      *reinterpret_cast<f32x4*>(out.dq + ti) = dq;
+      *reinterpret_cast<f32x4*>(out.dk + ti) = dk;
+      *reinterpret_cast<f32x4*>(out.dv + ti) = dr;
     }
   }
-  if (c < len) out.dbeta[(size_t)(t0 + c) * H + h] = p.db[(size_t)b * C + c];
+  *reinterpret_cast<f32x4*>(&kbp[rs][c0]) = kb;
+  __syncthreads();
+  if (tid < D) {  // dg = reverse cumulative sum of dGamma; dGamma_n lands on the last row
+    const int c = tid;
+    float dgn = 0.f;  // rowsum(dS' * S)[c], from the serial pass's per-block shares
+#pragma unroll
+    for (int v = 0; v < D / 16; ++v) dgn += p.dgp[((size_t)b * (D / 16) + v) * D + c];
+    float run = dgn * p.gn[(size_t)b * D + c];
+#pragma unroll
+    for (int j = 0; j < RPP; ++j) run += kbp[j][c];
+#pragma unroll 8
+    for (int r = C - 1; r >= 0; --r) {
+      run += term[r][c];
+      if (r < len) out.dg[((size_t)(t0 + r) * H + h) * D + c] = run;
+    }
+  }
+  if (tid < len) out.dbeta[(size_t)(t0 + tid) * H + h] = p.db[(size_t)b * C + tid];
 }
 
 
@@ -1186,7 +1222,7 @@ hipError_t launch_backward_t(const BackwardArgs& a) {
     gemm(TN, p.dP, p.Qt, p.dU, C, D, C, C, D, scc, scd, 1.f, 1, 0);   //    + dP^T Qt
     if (gerr != hipSuccess) return gerr;
     hipLaunchKernelGGL((bwd_pairs_tile_kernel<D, C>), dim3(NB), dim3(256), tlds, a.stream, p);
-    hipLaunchKernelGGL((bwd_final_fast_kernel<D, C>), dim3(NB), dim3(D), 0, a.stream, p, geo, out);
+    hipLaunchKernelGGL((bwd_final_fast_kernel<D, C>), dim3(NB), dim3(256), 0, a.stream, p, geo, out);
   }
   if (gerr != hipSuccess) return gerr;
   return hipGetLastError();

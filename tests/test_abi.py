@@ -312,9 +312,10 @@ def _a256(x):
 
 def _bwd_planes(nb, C, D):
     # fp32 per-(chunk, head) planes of one backward segment: sixteen [C x D],
-    # seven [C x C], two [D x D], two [C], one [D] and one flag each
+    # seven [C x C], two [D x D], two [C], one [D], one [D/16 x D] and one flag each
     return (16 * _a256(nb * C * D * 4) + 7 * _a256(nb * C * C * 4) + 2 * _a256(nb * D * D * 4)
-            + 2 * _a256(nb * C * 4) + _a256(nb * D * 4) + _a256(nb * 4))
+            + 2 * _a256(nb * C * 4) + _a256(nb * D * 4) + _a256(nb * (D // 16) * D * 4)
+            + _a256(nb * 4))
 
 
 def test_backward_workspace_segments(lib):
