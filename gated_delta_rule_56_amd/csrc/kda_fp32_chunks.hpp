@@ -150,12 +150,19 @@ __global__ __launch_bounds__(256) void fp32_gemm_kernel(const float* __restrict_
                                                        float* __restrict__ Cm, int M, int N, int K,
                                                        int lda, int ldb, int ldc, size_t sa,
                                                        size_t sb, size_t sc, float alpha, int acc_c,
-                                                       int mask) {
+                                                       int mask, size_t nb) {
   __shared__ __attribute__((aligned(16))) float As[64 * kGemmLd];  // As[m][k]
   __shared__ __attribute__((aligned(16))) float Bs[64 * kGemmLd];  // Bs[n][k]
   constexpr int LD = kGemmLd, NV = kGemmKStage * 16 / 256;  // vectors per thread and matrix
-  const int bt = blockIdx.x;  // batch on x: up to 2^31 - 1 blocks
-  const int m0 = blockIdx.z * 64, n0 = blockIdx.y * 64;
+  // Items in groups of eight, the tiles of a group's items interleaved: item
+  // j of a group and tile t take block 8 t + j of the group, so an item's
+  // tiles (which share an operand) run close together on one XCD, since
+  // consecutive block ids go to the chip's eight XCDs in turn.
+  const int ntn = (N + 63) / 64, ntiles = ntn * ((M + 63) / 64);
+  const int grp = blockIdx.x / (8 * ntiles), rem = blockIdx.x % (8 * ntiles);
+  const int bt = 8 * grp + rem % 8, tile = rem / 8;
+  if ((size_t)bt >= nb) return;
+  const int m0 = (tile / ntn) * 64, n0 = (tile % ntn) * 64;
   const float* a = A + bt * sa;
   const float* bb = B + bt * sb;
   const int tid = threadIdx.x;
@@ -277,9 +284,11 @@ inline hipError_t launch_fp32_gemm(const float* A, const float* B, float* Cm, in
                                    int lda, int ldb, int ldc, size_t sa, size_t sb, size_t sc,
                                    float alpha, int acc_c, int mask, size_t NB, hipStream_t stream) {
   if (K % 16 || M % 4 || N % 4) return hipErrorInvalidValue;
-  const dim3 grid((unsigned)NB, (N + 63) / 64, (M + 63) / 64);
-  hipLaunchKernelGGL((fp32_gemm_kernel<TA, TB>), grid, dim3(256), 0, stream, A, B, Cm, M, N, K, lda,
-                     ldb, ldc, sa, sb, sc, alpha, acc_c, mask);
+  const size_t blocks = (NB + 7) / 8 * 8 * (size_t)((N + 63) / 64) * ((M + 63) / 64);
+  if (blocks == 0) return hipSuccess;
+  if (blocks > 0x7fffffff) return hipErrorInvalidValue;
+  hipLaunchKernelGGL((fp32_gemm_kernel<TA, TB>), dim3((unsigned)blocks), dim3(256), 0, stream, A, B, Cm, M, N,
+                     K, lda, ldb, ldc, sa, sb, sc, alpha, acc_c, mask, NB);
   return hipGetLastError();
 }
 
