@@ -303,14 +303,12 @@ struct Prefetch {
   static constexpr int C4 = COLS / 4, N = (ROWS * C4 + NT - 1) / NT;
   static_assert(COLS % 4 == 0 && SLD % 4 == 0, "float4 rows");
   f32x4 v[N];
-  // Every thread loads, those past the block its last vector again (their
-  // stores are skipped): a load under a branch would make the code after the
-  // branch wait for every load issued before it.
   __device__ __forceinline__ void load(const float* __restrict__ src) {
 #pragma unroll
     for (int x = 0; x < N; ++x) {
-      const int i = threadIdx.x + NT * x, idx = i < ROWS * C4 ? i : ROWS * C4 - 1;
-      v[x] = *reinterpret_cast<const f32x4*>(src + (size_t)(idx / C4) * SLD + 4 * (idx % C4));
+      const int idx = threadIdx.x + NT * x;
+      if (idx < ROWS * C4)
+        v[x] = *reinterpret_cast<const f32x4*>(src + (size_t)(idx / C4) * SLD + 4 * (idx % C4));
     }
   }
   template <int LD>
