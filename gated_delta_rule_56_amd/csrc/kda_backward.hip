@@ -52,6 +52,8 @@
 //                         gradient terms, tile-factored
 //   bwd_final_fast_kernel per (chunk, head): decays, reverse cumsum, scatter
 //                         to the token-major outputs
+#include <type_traits>
+
 #include "kda_device.hpp"
 #include "kda_fp32_chunks.hpp"
 #include "kda_launch.hpp"
@@ -1157,6 +1159,17 @@ hipError_t launch_backward_t(const BackwardArgs& a) {
                                                          a.stream);
     if (gerr == hipSuccess) gerr = e;
   };
+  // Two products in one launch: kGemmDual (second A and C, same B) or
+  // kGemmCat (second A and B, summed into C).
+  auto gemm2 = [&](auto op, auto mode, const float* A, const float* B, float* Cm, int M, int N, int K,
+                   int lda, int ldb, size_t sa, size_t sb, float alpha, int mask, GemmX x2) {
+    typedef decltype(op) O;
+    const hipError_t e = launch_fp32_gemm<O::TA, O::TB, decltype(mode)::value>(
+        A, B, Cm, M, N, K, lda, ldb, N, sa, sb, (size_t)M * N, alpha, 0, mask, NB, a.stream, x2);
+    if (gerr == hipSuccess) gerr = e;
+  };
+  const std::integral_constant<int, kGemmDual> dual;
+  const std::integral_constant<int, kGemmCat> cat;
   const size_t scd = (size_t)C * D, scc = (size_t)C * C, sdd = (size_t)D * D;
   const GemmNT NT;
   const GemmNN NN;
@@ -1179,8 +1192,15 @@ hipError_t launch_backward_t(const BackwardArgs& a) {
     if (NB == 0) return;
     hipLaunchKernelGGL((bwd_prep_kernel<in_t, D, C>), dim3(NB), dim3(256), 0, a.stream, in, p, geo);
     // Grams of the moderate-decay chunks, then the others pair by pair.
-    gemm(NT, p.Kt, p.Kh, p.Bm, C, C, D, D, D, scd, scd, 1.f, 0, 2);    // strict_tril(Kt Kh^T)
-    if (grams_p) gemm(NT, p.Qt, p.Kh, p.P, C, C, D, D, D, scd, scd, 1.f, 0, 1);  // tril(Qt Kh^T)
+    if (grams_p) {  // strict_tril(Kt Kh^T) and tril(Qt Kh^T), Kh read once
+      GemmX x2;
+      x2.A2 = p.Qt;
+      x2.C2 = p.P;
+      x2.mask2 = 1;
+      gemm2(NT, dual, p.Kt, p.Kh, p.Bm, C, C, D, D, D, scd, scd, 1.f, 2, x2);
+    } else {
+      gemm(NT, p.Kt, p.Kh, p.Bm, C, C, D, D, D, scd, scd, 1.f, 0, 2);  // strict_tril(Kt Kh^T)
+    }
     hipLaunchKernelGGL((bwd_gram_tile_kernel<D, C>), dim3(NB), dim3(256), tlds, a.stream, p);
     hipLaunchKernelGGL((unit_lower_inverse_kernel<C>), dim3(NB), dim3(256), 0, a.stream, p.Bm, p.beta,
                        p.M, p.T);
@@ -1209,17 +1229,31 @@ hipError_t launch_backward_t(const BackwardArgs& a) {
     if (NB == 0) continue;
     // p.S and p.dSn are [D][D] per chunk and head: the B operand "rows" are
     // the key channels, contracted over the value columns.
-    gemm(NT, p.dO, p.S, p.dQt, C, D, D, D, D, scd, sdd, 1.f, 0, 0);   // dQt = dO S^T
+    {  // dQt = dO S^T and dKt = -dR S^T, S read once
+      GemmX x2;
+      x2.A2 = p.dR;
+      x2.C2 = p.dKt;
+      x2.alpha2 = -1.f;
+      gemm2(NT, dual, p.dO, p.S, p.dQt, C, D, D, D, D, scd, sdd, 1.f, 0, x2);
+    }
     gemm(NT, p.U, p.dSn, p.dKb, C, D, D, D, D, scd, sdd, 1.f, 0, 0);  // dKb = U dS'^T
-    gemm(NT, p.dR, p.S, p.dKt, C, D, D, D, D, scd, sdd, -1.f, 0, 0);  // dKt = -dR S^T
     gemm(NT, p.dU, p.R, p.dT, C, C, D, D, D, scd, scd, 1.f, 0, 0);    // dT = dU R^T
     gemm(NT, p.dO, p.U, p.dP, C, C, D, D, D, scd, scd, 1.f, 0, 1);    // dP = tril(dO U^T)
     hipLaunchKernelGGL((bwd_cc_kernel<C>), dim3(NB), dim3(256), 0, a.stream, p);
     // Pairwise gradient terms of the moderate-decay chunks (R, U, dU are free).
-    gemm(NN, p.dBm, p.Kh, p.R, C, D, C, C, D, scc, scd, 1.f, 0, 0);   // Y1 = dBm Kh
-    gemm(NN, p.dP, p.Kh, p.U, C, D, C, C, D, scc, scd, 1.f, 0, 0);    // Y2 = dP Kh
-    gemm(TN, p.dBm, p.Kt, p.dU, C, D, C, C, D, scc, scd, 1.f, 0, 0);  // Y3 = dBm^T Kt
-    gemm(TN, p.dP, p.Qt, p.dU, C, D, C, C, D, scc, scd, 1.f, 1, 0);   //    + dP^T Qt
+    {  // Y1 = dBm Kh and Y2 = dP Kh, Kh read once
+      GemmX x2;
+      x2.A2 = p.dP;
+      x2.C2 = p.U;
+      gemm2(NN, dual, p.dBm, p.Kh, p.R, C, D, C, C, D, scc, scd, 1.f, 0, x2);
+    }
+    {  // Y3 = dBm^T Kt + dP^T Qt, written once
+      GemmX x2;
+      x2.A2 = p.dP;
+      x2.B2 = p.Qt;
+      x2.K2 = C;
+      gemm2(TN, cat, p.dBm, p.Kt, p.dU, C, D, C, C, D, scc, scd, 1.f, 0, x2);
+    }
     if (gerr != hipSuccess) return gerr;
     hipLaunchKernelGGL((bwd_pairs_tile_kernel<D, C>), dim3(NB), dim3(256), tlds, a.stream, p);
     hipLaunchKernelGGL((bwd_final_fast_kernel<D, C>), dim3(NB), dim3(256), 0, a.stream, p, geo, out);

@@ -465,15 +465,26 @@ hipError_t launch_dplr_t(const DplrArgs& a) {
                                                            a.stream);
       if (gerr == hipSuccess) gerr = e;
     };
+    // Two products sharing B (and its load) in one launch.
+    auto gemm_dual = [&](auto op, const float* A, const float* B, float* Cm, int M, int N, int K, int lda,
+                         int ldb, size_t sa, size_t sb, int mask, const float* A2, float* C2, int mask2) {
+      typedef decltype(op) O;
+      GemmX x2;
+      x2.A2 = A2;
+      x2.C2 = C2;
+      x2.mask2 = mask2;
+      const hipError_t e = launch_fp32_gemm<O::TA, O::TB, kGemmDual>(A, B, Cm, M, N, K, lda, ldb, N, sa, sb,
+                                                                     (size_t)M * N, 1.f, 0, mask, NB,
+                                                                     a.stream, x2);
+      if (gerr == hipSuccess) gerr = e;
+    };
     const size_t scd = (size_t)C * D, scc = (size_t)C * C;
     const GemmNT NT;
     const GemmNN NN;
-    gemm(NT, p.Bt, p.Ah, p.Aba, C, C, D, D, D, scd, scd, 1.f, 2);  // strict_tril(Bt Ah^T)
-    gemm(NT, p.Qt, p.Ah, p.Aqa, C, C, D, D, D, scd, scd, 1.f, 1);  // tril(Qt Ah^T)
-    if (!TIED) {
-      gemm(NT, p.Bt, p.Kh, p.Abk, C, C, D, D, D, scd, scd, 1.f, 2);  // strict_tril(Bt Kh^T)
-      gemm(NT, p.Qt, p.Kh, p.Aqk, C, C, D, D, D, scd, scd, 1.f, 1);  // tril(Qt Kh^T)
-    }
+    // strict_tril(Bt Ah^T) and tril(Qt Ah^T)
+    gemm_dual(NT, p.Bt, p.Ah, p.Aba, C, C, D, D, D, scd, scd, 2, p.Qt, p.Aqa, 1);
+    if (!TIED)  // strict_tril(Bt Kh^T) and tril(Qt Kh^T)
+      gemm_dual(NT, p.Bt, p.Kh, p.Abk, C, C, D, D, D, scd, scd, 2, p.Qt, p.Aqk, 1);
     hipLaunchKernelGGL((dplr_gram_tile_kernel<D, C, TIED>), dim3(NB), dim3(256), sizeof(DTileLds<D, C>),
                        a.stream, p);
     hipLaunchKernelGGL((unit_lower_inverse_kernel<C>), dim3(NB), dim3(256), 0, a.stream, p.Aba,
@@ -482,9 +493,8 @@ hipError_t launch_dplr_t(const DplrArgs& a) {
     if (TIED) {
       gemm(NN, p.M, p.V, p.Y, C, D, C, C, D, scc, scd, 1.f, 0);      // Y = M V
     } else {
-      gemm(NN, p.Abk, p.V, p.X, C, D, C, C, D, scc, scd, 1.f, 0);    // X = Abk V
+      gemm_dual(NN, p.Abk, p.V, p.X, C, D, C, C, D, scc, scd, 0, p.Aqk, p.OV, 0);  // X = Abk V, OV = Aqk V
       gemm(NN, p.M, p.X, p.Y, C, D, C, C, D, scc, scd, -1.f, 0);     // Y = -M X
-      gemm(NN, p.Aqk, p.V, p.OV, C, D, C, C, D, scc, scd, 1.f, 0);   // OV = Aqk V
     }
     if (gerr != hipSuccess) return gerr;
   }

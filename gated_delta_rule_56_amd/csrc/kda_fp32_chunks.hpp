@@ -144,15 +144,31 @@ __device__ __forceinline__ f32x4 mfma4(float a, float b, f32x4 c) {
 constexpr int kGemmKStage = 64, kGemmLd = 64 + 4;
 constexpr size_t kGemmLds = (size_t)2 * kGemmKStage * kGemmLd * sizeof(float);
 
-template <bool TA, bool TB>
+// A second product in the same launch (X modes of fp32_gemm_kernel):
+// kGemmDual: C2 = alpha2 op(A2) op(B), same B, shapes and strides as the
+// first, mask2 on C2 (two outputs, B read once); kGemmCat: C = alpha (op(A)
+// op(B) + op(A2) op(B2)) with A2, B2 laid out like A, B and K2 more k (one
+// output, written once).
+constexpr int kGemmOne = 0, kGemmDual = 1, kGemmCat = 2;
+struct GemmX {
+  const float* A2 = nullptr;
+  const float* B2 = nullptr;
+  float* C2 = nullptr;
+  int K2 = 0;
+  float alpha2 = 1.f;
+  int mask2 = 0;
+};
+
+template <bool TA, bool TB, int X>
 __global__ __launch_bounds__(256) void fp32_gemm_kernel(const float* __restrict__ A,
                                                        const float* __restrict__ B,
                                                        float* __restrict__ Cm, int M, int N, int K,
                                                        int lda, int ldb, int ldc, size_t sa,
                                                        size_t sb, size_t sc, float alpha, int acc_c,
-                                                       int mask, size_t nb) {
-  __shared__ __attribute__((aligned(16))) float As[64 * kGemmLd];  // As[m][k]
-  __shared__ __attribute__((aligned(16))) float Bs[64 * kGemmLd];  // Bs[n][k]
+                                                       int mask, size_t nb, GemmX x2) {
+  constexpr bool DUAL = X == kGemmDual;
+  __shared__ __attribute__((aligned(16))) float As[(DUAL ? 2 : 1) * 64 * kGemmLd];  // As[m][k] (then A2's)
+  __shared__ __attribute__((aligned(16))) float Bs[64 * kGemmLd];                   // Bs[n][k]
   constexpr int LD = kGemmLd, NV = kGemmKStage * 16 / 256;  // vectors per thread and matrix
   // Items in groups of eight, the tiles of a group's items interleaved: item
   // j of a group and tile t take block 8 t + j of the group, so an item's
@@ -165,35 +181,66 @@ __global__ __launch_bounds__(256) void fp32_gemm_kernel(const float* __restrict_
   const int m0 = (tile / ntn) * 64, n0 = (tile % ntn) * 64;
   const float* a = A + bt * sa;
   const float* bb = B + bt * sb;
+  const float* a2 = X != kGemmOne ? x2.A2 + bt * sa : nullptr;
+  const float* b2 = X == kGemmCat ? x2.B2 + bt * sb : nullptr;
+  // Stages of up to kGemmKStage k: the first product's, then (kGemmCat) the
+  // second's, so no stage mixes the two.
+  const int ns1 = (K + kGemmKStage - 1) / kGemmKStage;
+  const int nst = ns1 + (X == kGemmCat ? (x2.K2 + kGemmKStage - 1) / kGemmKStage : 0);
+  auto stage_at = [&](int si, bool& second, int& kk, int& ks) {
+    second = X == kGemmCat && si >= ns1;
+    kk = kGemmKStage * (second ? si - ns1 : si);
+    const int kend = second ? x2.K2 : K;
+    ks = kend - kk < kGemmKStage ? kend - kk : kGemmKStage;
+  };
   const int tid = threadIdx.x;
-  f32x4 xa[NV], xb[NV];
+  f32x4 xa[NV], xb[NV], xc[DUAL ? NV : 1];
   // Vector v = tid + 256 x of stage k0 (ks = its k extent): for a matrix
   // stored with k as its row (TA for A, !TB for B) row k0 + 16 x + tid % 16,
   // columns 4 (tid / 16) ..; otherwise row v / (ks / 4) of the 64, columns
   // k0 + 4 (v % (ks / 4)) ...  (In the first case sixteen consecutive threads
   // take sixteen rows, so their transposing LDS writes hit distinct banks.)
-  auto fetch = [&](int k0, int ks) {
+  auto ldA = [&](const float* src, int k0, int x, int v, int kr, int c4, int ks) -> f32x4 {
+    if (TA) {
+      if (m0 + c4 < M) return *reinterpret_cast<const f32x4*>(src + (size_t)(k0 + kr) * lda + m0 + c4);
+    } else {
+      const int mm = v / (ks / 4);
+      if (m0 + mm < M) return *reinterpret_cast<const f32x4*>(src + (size_t)(m0 + mm) * lda + k0 + 4 * (v % (ks / 4)));
+    }
+    (void)x;
+    return f32x4{0, 0, 0, 0};
+  };
+  auto fetch = [&](int si) {
+    bool second;
+    int kk, ks;
+    stage_at(si, second, kk, ks);
+    const float* sa_ = second ? a2 : a;
+    const float* sb_ = second ? b2 : bb;
 #pragma unroll
     for (int x = 0; x < NV; ++x) {
       const int v = tid + 256 * x, kr = 16 * x + tid % 16, c4 = 4 * (tid / 16);
       xa[x] = f32x4{0, 0, 0, 0};
       xb[x] = f32x4{0, 0, 0, 0};
+      if constexpr (DUAL) xc[x] = f32x4{0, 0, 0, 0};
       if (v < ks * 16) {
-        if (TA) {
-          if (m0 + c4 < M) xa[x] = *reinterpret_cast<const f32x4*>(a + (size_t)(k0 + kr) * lda + m0 + c4);
-        } else {
-          const int mm = v / (ks / 4);
-          if (m0 + mm < M)
-            xa[x] = *reinterpret_cast<const f32x4*>(a + (size_t)(m0 + mm) * lda + k0 + 4 * (v % (ks / 4)));
-        }
+        xa[x] = ldA(sa_, kk, x, v, kr, c4, ks);
+        if constexpr (DUAL) xc[x] = ldA(a2, kk, x, v, kr, c4, ks);
         if (!TB) {
-          if (n0 + c4 < N) xb[x] = *reinterpret_cast<const f32x4*>(bb + (size_t)(k0 + kr) * ldb + n0 + c4);
+          if (n0 + c4 < N) xb[x] = *reinterpret_cast<const f32x4*>(sb_ + (size_t)(kk + kr) * ldb + n0 + c4);
         } else {
           const int nn = v / (ks / 4);
           if (n0 + nn < N)
-            xb[x] = *reinterpret_cast<const f32x4*>(bb + (size_t)(n0 + nn) * ldb + k0 + 4 * (v % (ks / 4)));
+            xb[x] = *reinterpret_cast<const f32x4*>(sb_ + (size_t)(n0 + nn) * ldb + kk + 4 * (v % (ks / 4)));
         }
       }
+    }
+  };
+  auto stA = [&](float* dst, const f32x4& val, int v, int kr, int c4, int ks) {
+    if (TA) {
+#pragma unroll
+      for (int e = 0; e < 4; ++e) dst[(c4 + e) * LD + kr] = val[e];
+    } else {
+      *reinterpret_cast<f32x4*>(dst + (v / (ks / 4)) * LD + 4 * (v % (ks / 4))) = val;
     }
   };
   auto stage = [&](int ks) {
@@ -201,12 +248,8 @@ __global__ __launch_bounds__(256) void fp32_gemm_kernel(const float* __restrict_
     for (int x = 0; x < NV; ++x) {
       const int v = tid + 256 * x, kr = 16 * x + tid % 16, c4 = 4 * (tid / 16);
       if (v < ks * 16) {
-        if (TA) {
-#pragma unroll
-          for (int e = 0; e < 4; ++e) As[(c4 + e) * LD + kr] = xa[x][e];
-        } else {
-          *reinterpret_cast<f32x4*>(As + (v / (ks / 4)) * LD + 4 * (v % (ks / 4))) = xa[x];
-        }
+        stA(As, xa[x], v, kr, c4, ks);
+        if constexpr (DUAL) stA(As + 64 * LD, xc[x], v, kr, c4, ks);
         if (!TB) {
 #pragma unroll
           for (int e = 0; e < 4; ++e) Bs[(c4 + e) * LD + kr] = xb[x][e];
@@ -221,21 +264,28 @@ __global__ __launch_bounds__(256) void fp32_gemm_kernel(const float* __restrict_
   // 4 g + r, column i of the tile.
   const int l = tid & 63, lm = l & 15, lg = l >> 4;
   const int wm = (tid >> 7) * 32, wn = ((tid >> 6) & 1) * 32;  // this wave's quarter
-  f32x4 acc[2][2];
+  f32x4 acc[2][2], acc2[DUAL ? 2 : 1][DUAL ? 2 : 1];
 #pragma unroll
   for (int i = 0; i < 2; ++i)
 #pragma unroll
     for (int j = 0; j < 2; ++j) acc[i][j] = f32x4{0.f, 0.f, 0.f, 0.f};
-  fetch(0, K < kGemmKStage ? K : kGemmKStage);
-  for (int k0 = 0; k0 < K; k0 += kGemmKStage) {
-    const int ks = K - k0 < kGemmKStage ? K - k0 : kGemmKStage;
-    if (k0 > 0) __syncthreads();  // the previous stage's reads are done
+  if constexpr (DUAL) {
+#pragma unroll
+    for (int i = 0; i < 2; ++i)
+#pragma unroll
+      for (int j = 0; j < 2; ++j) acc2[i][j] = f32x4{0.f, 0.f, 0.f, 0.f};
+  }
+  fetch(0);
+  for (int si = 0; si < nst; ++si) {
+    bool second;
+    int kk, ks;
+    stage_at(si, second, kk, ks);
+    (void)second;
+    (void)kk;
+    if (si > 0) __syncthreads();  // the previous stage's reads are done
     stage(ks);
     __syncthreads();
-    if (k0 + kGemmKStage < K) {
-      const int k1 = k0 + kGemmKStage;
-      fetch(k1, K - k1 < kGemmKStage ? K - k1 : kGemmKStage);
-    }
+    if (si + 1 < nst) fetch(si + 1);
     auto kblock = [&](int kb) {  // k = 16 kb .. 16 kb + 15 of the stage
       const int ko = 16 * kb + 4 * lg;
       const f32x4 a0 = *reinterpret_cast<const f32x4*>(As + (wm + lm) * LD + ko);
@@ -249,6 +299,17 @@ __global__ __launch_bounds__(256) void fp32_gemm_kernel(const float* __restrict_
         acc[1][0] = mfma4(a1[s], b0[s], acc[1][0]);
         acc[1][1] = mfma4(a1[s], b1[s], acc[1][1]);
       }
+      if constexpr (DUAL) {
+        const f32x4 c0 = *reinterpret_cast<const f32x4*>(As + (64 + wm + lm) * LD + ko);
+        const f32x4 c1 = *reinterpret_cast<const f32x4*>(As + (64 + wm + 16 + lm) * LD + ko);
+#pragma unroll
+        for (int s = 0; s < 4; ++s) {
+          acc2[0][0] = mfma4(c0[s], b0[s], acc2[0][0]);
+          acc2[0][1] = mfma4(c0[s], b1[s], acc2[0][1]);
+          acc2[1][0] = mfma4(c1[s], b0[s], acc2[1][0]);
+          acc2[1][1] = mfma4(c1[s], b1[s], acc2[1][1]);
+        }
+      }
     };
     if (ks == kGemmKStage) {
 #pragma unroll
@@ -257,20 +318,24 @@ __global__ __launch_bounds__(256) void fp32_gemm_kernel(const float* __restrict_
       for (int kb = 0; kb < ks / 16; ++kb) kblock(kb);
     }
   }
-  float* c = Cm + bt * sc;
+  auto put = [&](float* cm, const f32x4 (&ac)[2][2], float al, int mk) {
+    float* c = cm + bt * sc;
 #pragma unroll
-  for (int ti = 0; ti < 2; ++ti)
+    for (int ti = 0; ti < 2; ++ti)
 #pragma unroll
-    for (int tj = 0; tj < 2; ++tj)
+      for (int tj = 0; tj < 2; ++tj)
 #pragma unroll
-      for (int i = 0; i < 4; ++i) {
-        const int m = m0 + wm + 16 * ti + 4 * lg + i, nn = n0 + wn + 16 * tj + lm;
-        if (m < M && nn < N) {
-          const bool keep = mask == 0 || (mask == 1 ? nn <= m : nn < m);
-          const float v = keep ? alpha * acc[ti][tj][i] : 0.f;
-          c[(size_t)m * ldc + nn] = acc_c ? c[(size_t)m * ldc + nn] + v : v;
+        for (int i = 0; i < 4; ++i) {
+          const int m = m0 + wm + 16 * ti + 4 * lg + i, nn = n0 + wn + 16 * tj + lm;
+          if (m < M && nn < N) {
+            const bool keep = mk == 0 || (mk == 1 ? nn <= m : nn < m);
+            const float v = keep ? al * ac[ti][tj][i] : 0.f;
+            c[(size_t)m * ldc + nn] = acc_c ? c[(size_t)m * ldc + nn] + v : v;
+          }
         }
-      }
+  };
+  put(Cm, acc, alpha, mask);
+  if constexpr (DUAL) put(x2.C2, acc2, x2.alpha2, x2.mask2);
 }
 
 // Operand orientations of fp32_gemm_kernel, as tags for launch_fp32_gemm.
@@ -278,17 +343,21 @@ struct GemmNN { static constexpr bool TA = false, TB = false; };
 struct GemmNT { static constexpr bool TA = false, TB = true; };
 struct GemmTN { static constexpr bool TA = true, TB = false; };
 
-// Launch of fp32_gemm_kernel over NB batch items.
-template <bool TA, bool TB>
+// Launch of fp32_gemm_kernel over NB batch items (x2: the second product of
+// kGemmDual or kGemmCat).
+template <bool TA, bool TB, int X = kGemmOne>
 inline hipError_t launch_fp32_gemm(const float* A, const float* B, float* Cm, int M, int N, int K,
                                    int lda, int ldb, int ldc, size_t sa, size_t sb, size_t sc,
-                                   float alpha, int acc_c, int mask, size_t NB, hipStream_t stream) {
+                                   float alpha, int acc_c, int mask, size_t NB, hipStream_t stream,
+                                   GemmX x2 = GemmX{}) {
   if (K % 16 || M % 4 || N % 4) return hipErrorInvalidValue;
+  if (X == kGemmCat && (x2.K2 % 16 || !x2.A2 || !x2.B2)) return hipErrorInvalidValue;
+  if (X == kGemmDual && (!x2.A2 || !x2.C2)) return hipErrorInvalidValue;
   const size_t blocks = (NB + 7) / 8 * 8 * (size_t)((N + 63) / 64) * ((M + 63) / 64);
   if (blocks == 0) return hipSuccess;
   if (blocks > 0x7fffffff) return hipErrorInvalidValue;
-  hipLaunchKernelGGL((fp32_gemm_kernel<TA, TB>), dim3((unsigned)blocks), dim3(256), 0, stream, A, B, Cm, M, N,
-                     K, lda, ldb, ldc, sa, sb, sc, alpha, acc_c, mask, NB);
+  hipLaunchKernelGGL((fp32_gemm_kernel<TA, TB, X>), dim3((unsigned)blocks), dim3(256), 0, stream, A, B, Cm, M,
+                     N, K, lda, ldb, ldc, sa, sb, sc, alpha, acc_c, mask, NB, x2);
   return hipGetLastError();
 }
 
