@@ -41,7 +41,7 @@
 //   bwd_prep_kernel       per (chunk, head): padded fp32 copies, Gamma, Qt, Kt,
 //                         Kb, Kh and the span verdict
 //   fp32_gemm_kernel      batched fp32 products (Grams, contractions over value
-//                         columns, pairwise gradient terms)
+//                         columns)
 //   bwd_gram_tile_kernel  per strong-decay (chunk, head): Bm and P, tile-factored
 //   unit_lower_inverse_kernel per (chunk, head): M = (I + Diag(beta) Bm)^-1, T
 //   bwd_fwd_states_kernel per (sequence, head, 16 value columns), serial over
@@ -50,8 +50,9 @@
 //   bwd_cc_kernel         per (chunk, head): the C x C algebra of M and A
 //   bwd_pairs_tile_kernel per strong-decay (chunk, head): the pairwise
 //                         gradient terms, tile-factored
-//   bwd_final_fast_kernel per (chunk, head): decays, reverse cumsum, scatter
-//                         to the token-major outputs
+//   bwd_final_prod_kernel per (chunk, head, 64 channels): the pairwise
+//                         gradient terms of the factored chunks, decays,
+//                         reverse cumsum, scatter to the token-major outputs
 #include <type_traits>
 
 #include "kda_device.hpp"
@@ -640,13 +641,25 @@ __global__ __launch_bounds__(kSerThreads) void bwd_fwd_states_kernel(Planes p, G
     if (2 * NRT == G::NW || w < 2 * NRT) {  // half uhs of T R for row tile urt
       f32x4 acc = {0, 0, 0, 0};
       const int k0 = uhs * ulh + g * uj;
+      // R^T in pairs (8-byte reads: one lane's run is contiguous in the
+      // transposed shares; single floats put lanes 16 apart on one bank)
+      float2 rx[UJM / 2];
 #pragma unroll
-      for (int j = 0; j < UJM; ++j)
+      for (int j = 0; j < UJM; j += 2) {
+        const int jj = j < uj ? j : 0;
+        rx[j / 2] = float2{0.f, 0.f};
+#pragma unroll
+        for (int k = 0; k < G::KS; ++k) {
+          const float2 v = *reinterpret_cast<const float2*>(&L.Rp[k][m][k0 + jj]);
+          rx[j / 2].x += v.x;
+          rx[j / 2].y += v.y;
+        }
+      }
+#pragma unroll
+      for (int j = 0; j < UJM; j += 2)
         if (j < uj) {
-          float x = 0.f;
-#pragma unroll
-          for (int k = 0; k < G::KS; ++k) x += L.Rp[k][m][k0 + j];
-          acc = mfma4(ta[j], -x, acc);
+          acc = mfma4(ta[j], -rx[j / 2].x, acc);
+          acc = mfma4(ta[j + 1], -rx[j / 2].y, acc);
         }
       *reinterpret_cast<f32x4*>(&L.Up[uhs][m][16 * urt + 4 * g]) = acc;
     }
@@ -819,13 +832,25 @@ __global__ __launch_bounds__(kSerThreads) void bwd_bwd_states_kernel(Planes p, G
       ts.put(w0, rn, l);
       const int k0 = rhs * (rn / 2) + g * rj;  // relative to row 16 rrt
       f32x4 acc = {0, 0, 0, 0};
+      // both operands in pairs (rj and k0 are even), as in the forward U stage
+      float2 tx[TJ / 2], ux[TJ / 2];
 #pragma unroll
-      for (int j = 0; j < TJ; ++j)
+      for (int j = 0; j < TJ; j += 2) {
+        const int jj = j < rj ? j : 0;
+        tx[j / 2] = *reinterpret_cast<const float2*>(w0 + m * (C + 4) + k0 + jj);
+        ux[j / 2] = float2{0.f, 0.f};
+#pragma unroll
+        for (int k = 0; k < G::KS; ++k) {
+          const float2 v = *reinterpret_cast<const float2*>(&L.Up[k][m][16 * rrt + k0 + jj]);
+          ux[j / 2].x += v.x;
+          ux[j / 2].y += v.y;
+        }
+      }
+#pragma unroll
+      for (int j = 0; j < TJ; j += 2)
         if (j < rj) {
-          float x = 0.f;
-#pragma unroll
-          for (int k = 0; k < G::KS; ++k) x += L.Up[k][m][16 * rrt + k0 + j];
-          acc = mfma4(w0[m * (C + 4) + k0 + j], x, acc);
+          acc = mfma4(tx[j / 2].x, ux[j / 2].x, acc);
+          acc = mfma4(tx[j / 2].y, ux[j / 2].y, acc);
         }
       *reinterpret_cast<f32x4*>(&L.Rp[rhs][m][16 * rrt + 4 * g]) = acc;
     }
@@ -958,79 +983,191 @@ struct BwdOut {
   float *dq, *dk, *dv, *dg, *dbeta;
 };
 
-// The decays, the reverse cumulative sum of dGamma and the scatter to the
-// token-major outputs.  The pairwise gradient terms sit in the R, U, dU
-// planes: for factored chunks the products Y1 = dBm Kh, Y2 = dP Kh,
-// Y3 = dBm^T Kt + dP^T Qt, with dq += gam Y2, dk += gam Y1 + exp(-Gamma) Y3,
-// dGamma += Kt Y1 + Qt Y2 - Kh Y3; for strong-decay chunks the sums Z1, Z2,
-// Z3 themselves (bwd_pairs_tile_kernel), with dq += Z2, dk += Z1 + Z3,
-// dGamma += k (Z1 - Z3) + q Z2.  256 threads per (chunk, head), D/4 threads
-// per row with four consecutive channels each, so every plane is read with
-// 16-byte loads and every output row written with 16-byte stores; the rows'
-// dGamma terms wait in LDS for the reverse cumulative sum, one thread per
-// channel.
+// The final pass: the pairwise gradient terms, the decays, the reverse
+// cumulative sum of dGamma and the scatter to the token-major outputs, for
+// one (chunk, head) and 64 channels.  For factored chunks the pairwise terms
+// are the products Y1 = dBm Kh, Y2 = dP Kh, Y3 = dBm^T Kt + dP^T Qt, formed
+// here on v_mfma_f32_16x16x4f32 (each wave 16 channels and every row tile of
+// the chunk), with dq += gam Y2, dk += gam Y1 + exp(-Gamma) Y3, dGamma +=
+// Kt Y1 + Qt Y2 - Kh Y3 taken straight from the accumulators; for
+// strong-decay chunks they are the sums Z1, Z2, Z3 that bwd_pairs_tile_kernel
+// left in the R, U, dU planes, with dq += Z2, dk += Z1 + Z3, dGamma +=
+// k (Z1 - Z3) + q Z2.  The contraction index of every product is
+// k = 16 q + 4 g + s for lane group g, so the B-operand registers (column c
+// of Kh, Kt, Qt at those rows) are also the values the combine needs at rows
+// 16 a + 4 g + i of the accumulators.  dBm and dP (zero above, resp. on and
+// above, the diagonal) are staged in LDS; blocks of them that are zero skip
+// their products.  Items in groups of eight with the tiles of a group's
+// items interleaved, so both tiles of an item run on one XCD.
 template <int D, int C>
-__global__ __launch_bounds__(256) void bwd_final_fast_kernel(Planes p, Geo geo, BwdOut out) {
-  constexpr int TPR = D / 4, RPP = 256 / TPR;  // threads per row, rows per pass
-  static_assert(C % RPP == 0 && D % RPP == 0, "whole passes");
-  __shared__ __attribute__((aligned(16))) float term[C][D + 4];
-  __shared__ __attribute__((aligned(16))) float kbp[RPP][D];
-  const int b = blockIdx.x, tid = threadIdx.x, H = geo.H;
-  const int c0 = 4 * (tid % TPR), rs = tid / TPR;
+__global__ __launch_bounds__(256) void bwd_final_prod_kernel(Planes p, Geo geo, BwdOut out, int nb) {
+  constexpr int NRT = C / 16, NQ = C / 16, NCT = D / 64, LDX = C + 4, LDT = 64 + 4;
+  __shared__ __attribute__((aligned(16))) float Xb[C][LDX];   // dBm
+  __shared__ __attribute__((aligned(16))) float Xp[C][LDX];   // dP
+  __shared__ __attribute__((aligned(16))) float term[C][LDT];  // dGamma terms of the tile
+  __shared__ float kbp[4][64];                                  // partial sums of dKb Kb per lane group
+  const int grp = blockIdx.x / (8 * NCT), rem = blockIdx.x % (8 * NCT);
+  const int b = 8 * grp + rem % 8, ct = rem / 8;
+  if (b >= nb) return;
+  const int tid = threadIdx.x, w = tid >> 6, l = tid & 63, m = l & 15, g = l >> 4, H = geo.H;
+  const int cl = 16 * w + m, c = 64 * ct + cl;  // this lane's channel (local, global)
   const bool fast = p.fast[b] != 0;
   const int gch = b / H, h = b % H;
   int n, t0, len;
   chunk_of<C>(geo, gch, n, t0, len);
-  const size_t pcd = (size_t)b * C * D;
-  auto ld4 = [](const float* x) { return *reinterpret_cast<const f32x4*>(x); };
-  // The pairwise terms' operands: Kt, Qt, Kh when factored, else K, Q, K.
-  const float* a1 = fast ? p.Kt : p.K;
-  const float* a2 = fast ? p.Qt : p.Q;
-  const float* a3 = fast ? p.Kh : p.K;
-  const f32x4 gl = ld4(p.Gam + pcd + (size_t)(C - 1) * D + c0);
-  f32x4 kb = {0, 0, 0, 0};
-  for (int r = rs; r < C; r += RPP) {
-    const size_t e0 = pcd + (size_t)r * D + c0;
-    const f32x4 gr = ld4(p.Gam + e0), dqt = ld4(p.dQt + e0), dkt = ld4(p.dKt + e0), dkb = ld4(p.dKb + e0);
-    const f32x4 kbv = ld4(p.Kb + e0), qt = ld4(p.Qt + e0), kt = ld4(p.Kt + e0), dr = ld4(p.dR + e0);
-    const f32x4 y1 = ld4(p.R + e0), y2 = ld4(p.U + e0), y3 = ld4(p.dU + e0);
-    const f32x4 x1 = ld4(a1 + e0), x2 = ld4(a2 + e0), x3 = ld4(a3 + e0);
-    f32x4 tv, dq, dk;
+  const size_t pcd = (size_t)b * C * D, pcc = (size_t)b * C * C;
+  // (the item's plane base is uniform, the in-plane offset 32-bit)
+  auto at = [&](const float* x, int r) { return (x + pcd)[r * D + c]; };
+  // Every load of the product phase is issued first and unconditionally
+  // (all addresses are valid; a strong-decay chunk ignores what it does not
+  // use): dBm and dP for the LDS staging, then column c of Kh, Kt, Qt at rows
+  // 16 q + 4 g + s.
+  constexpr int NSTG = (C * C / 4 + 255) / 256;  // 16-byte pieces of dBm (and dP) per thread
+  f32x4 sb[NSTG], sp[NSTG];
 #pragma unroll
-    for (int e = 0; e < 4; ++e) {
-      tv[e] = dqt[e] * qt[e] + dkt[e] * kt[e] - dkb[e] * kbv[e] + x1[e] * y1[e] + x2[e] * y2[e] - x3[e] * y3[e];
-      kb[e] += dkb[e] * kbv[e];
-      const float ga = __expf(gr[e]), gb = dkb[e] * __expf(gl[e] - gr[e]);
-      dq[e] = fast ? (dqt[e] + y2[e]) * ga : dqt[e] * ga + y2[e];
-      dk[e] = fast ? (dkt[e] + y1[e]) * ga + gb + __expf(-gr[e]) * y3[e] : dkt[e] * ga + y1[e] + gb + y3[e];
+  for (int x = 0; x < NSTG; ++x) {
+    const int idx = min(tid + 256 * x, C * C / 4 - 1), r = idx / (C / 4), k4 = 4 * (idx % (C / 4));
+    sb[x] = *reinterpret_cast<const f32x4*>(p.dBm + pcc + (size_t)r * C + k4);
+    sp[x] = *reinterpret_cast<const f32x4*>(p.dP + pcc + (size_t)r * C + k4);
+  }
+  float bt[4 * NQ], bq[4 * NQ], bh[4 * NQ];
+#pragma unroll
+  for (int q = 0; q < NQ; ++q)
+#pragma unroll
+    for (int s2 = 0; s2 < 4; ++s2) {
+      const int r = 16 * q + 4 * g + s2;
+      bt[4 * q + s2] = at(p.Kt, r);
+      bq[4 * q + s2] = at(p.Qt, r);
+      bh[4 * q + s2] = at(p.Kh, r);
     }
-    *reinterpret_cast<f32x4*>(&term[r][c0]) = tv;
-    if (r < len) {
-      const size_t ti = ((size_t)(t0 + r) * H + h) * D + c0;
-      *reinterpret_cast<f32x4*>(out.dq + ti) = dq;
-      *reinterpret_cast<f32x4*>(out.dk + ti) = dk;
-      *reinterpret_cast<f32x4*>(out.dv + ti) = dr;
+  __builtin_amdgcn_sched_barrier(0);  // keep the loads ahead of the staging writes
+  f32x4 y1[NRT], y2[NRT], y3[NRT];
+#pragma unroll
+  for (int a = 0; a < NRT; ++a) {
+    y1[a] = f32x4{0.f, 0.f, 0.f, 0.f};
+    y2[a] = y1[a];
+    y3[a] = y1[a];
+  }
+  if (fast) {
+#pragma unroll
+    for (int x = 0; x < NSTG; ++x) {
+      const int idx = tid + 256 * x, r = idx / (C / 4), k4 = 4 * (idx % (C / 4));
+      if (C * C / 4 % 256 == 0 || idx < C * C / 4) {
+        *reinterpret_cast<f32x4*>(&Xb[r][k4]) = sb[x];
+        *reinterpret_cast<f32x4*>(&Xp[r][k4]) = sp[x];
+      }
+    }
+    __syncthreads();
+#pragma unroll
+    for (int a = 0; a < NRT; ++a) {
+      // Y1, Y2 (rows 16 a + .., k <= 16 a + 15)
+#pragma unroll
+      for (int q = 0; q <= a; ++q) {
+        const f32x4 xb = *reinterpret_cast<const f32x4*>(&Xb[16 * a + m][16 * q + 4 * g]);
+        const f32x4 xp = *reinterpret_cast<const f32x4*>(&Xp[16 * a + m][16 * q + 4 * g]);
+#pragma unroll
+        for (int s2 = 0; s2 < 4; ++s2) {
+          y1[a] = mfma4(xb[s2], bh[4 * q + s2], y1[a]);
+          y2[a] = mfma4(xp[s2], bh[4 * q + s2], y2[a]);
+        }
+      }
+      // Y3 (columns 16 a + .. of dBm, dP; k >= 16 a)
+#pragma unroll
+      for (int q = a; q < NQ; ++q)
+#pragma unroll
+        for (int s2 = 0; s2 < 4; ++s2) {
+          const int k = 16 * q + 4 * g + s2;
+          y3[a] = mfma4(Xb[k][16 * a + m], bt[4 * q + s2], y3[a]);
+          y3[a] = mfma4(Xp[k][16 * a + m], bq[4 * q + s2], y3[a]);
+        }
     }
   }
-  *reinterpret_cast<f32x4*>(&kbp[rs][c0]) = kb;
+  // Combine: lane (m, g) holds rows 16 a + 4 g + i of column c.  A row
+  // tile's plane values are loaded before the previous tile's outputs are
+  // stored (the compiler may not move a load above a store that could alias
+  // it), so one memory round trip per tile overlaps the previous tile's work.
+  // Two copies, for the factored and the strong-decay chunks, so that no load
+  // sits under a branch.
+  const float gl = at(p.Gam, C - 1);
+  float kbsum = 0.f;
+  auto combine = [&](auto fc) {
+    constexpr bool F = decltype(fc)::value;
+    constexpr int NV = F ? 6 : 11;  // planes read per row
+    auto load_tile = [&](int a, float (&t)[NV][4]) {
+#pragma unroll
+      for (int i = 0; i < 4; ++i) {
+        const int r = 16 * a + 4 * g + i;
+        t[0][i] = at(p.Gam, r);
+        t[1][i] = at(p.dQt, r);
+        t[2][i] = at(p.dKt, r);
+        t[3][i] = at(p.dKb, r);
+        t[4][i] = at(p.Kb, r);
+        t[5][i] = at(p.dR, r);
+        if constexpr (!F) {
+          t[6][i] = at(p.R, r);
+          t[7][i] = at(p.U, r);
+          t[8][i] = at(p.dU, r);
+          t[9][i] = at(p.K, r);
+          t[10][i] = at(p.Q, r);
+        }
+      }
+    };
+    float tv[2][NV][4];
+    load_tile(0, tv[0]);
+#pragma unroll
+    for (int a = 0; a < NRT; ++a) {
+      if (a + 1 < NRT) load_tile(a + 1, tv[(a + 1) & 1]);
+      const float(&t)[NV][4] = tv[a & 1];
+#pragma unroll
+      for (int i = 0; i < 4; ++i) {
+        const int r = 16 * a + 4 * g + i;
+        const float gr = t[0][i], dqt = t[1][i], dkt = t[2][i], dkb = t[3][i], kbv = t[4][i];
+        const float qt = bq[4 * a + i], kt = bt[4 * a + i];
+        const float ga = __expf(gr), gb = dkb * __expf(gl - gr);
+        float dq, dk, tm;
+        if constexpr (F) {
+          const float v1 = y1[a][i], v2 = y2[a][i], v3 = y3[a][i];
+          tm = dqt * qt + dkt * kt - dkb * kbv + kt * v1 + qt * v2 - bh[4 * a + i] * v3;
+          dq = (dqt + v2) * ga;
+          dk = (dkt + v1) * ga + gb + __expf(-gr) * v3;
+        } else {
+          const float v1 = t[6][i], v2 = t[7][i], v3 = t[8][i], x1 = t[9][i], x2 = t[10][i];
+          tm = dqt * qt + dkt * kt - dkb * kbv + x1 * v1 + x2 * v2 - x1 * v3;
+          dq = dqt * ga + v2;
+          dk = dkt * ga + v1 + gb + v3;
+        }
+        term[r][cl] = tm;
+        kbsum += dkb * kbv;
+        touch_done(t[5][i]);  // dR is stored only for rows < len: keep its load out of that branch
+        if (r < len) {
+          const size_t ti = ((size_t)(t0 + r) * H + h) * D + c;
+          out.dq[ti] = dq;
+          out.dk[ti] = dk;
+          out.dv[ti] = t[5][i];
+        }
+      }
+    }
+  };
+  if (fast)
+    combine(std::true_type{});
+  else
+    combine(std::false_type{});
+  kbp[g][cl] = kbsum;
   __syncthreads();
-  if (tid < D) {  // dg = reverse cumulative sum of dGamma; dGamma_n lands on the last row
-    const int c = tid;
-    float dgn = 0.f;  // rowsum(dS' * S)[c], from the serial pass's per-block shares
+  if (tid < 64) {  // dg = reverse cumulative sum of dGamma; dGamma_n lands on the last row
+    const int cc = 64 * ct + tid;
+    float dgn = 0.f;  // rowsum(dS' * S)[cc], from the serial pass's per-block shares
 #pragma unroll
-    for (int v = 0; v < D / 16; ++v) dgn += p.dgp[((size_t)b * (D / 16) + v) * D + c];
-    float run = dgn * p.gn[(size_t)b * D + c];
-#pragma unroll
-    for (int j = 0; j < RPP; ++j) run += kbp[j][c];
+    for (int v = 0; v < D / 16; ++v) dgn += p.dgp[((size_t)b * (D / 16) + v) * D + cc];
+    float run = dgn * p.gn[(size_t)b * D + cc] + kbp[0][tid] + kbp[1][tid] + kbp[2][tid] + kbp[3][tid];
 #pragma unroll 8
     for (int r = C - 1; r >= 0; --r) {
-      run += term[r][c];
-      if (r < len) out.dg[((size_t)(t0 + r) * H + h) * D + c] = run;
+      run += term[r][tid];
+      if (r < len) out.dg[((size_t)(t0 + r) * H + h) * D + cc] = run;
     }
   }
-  if (tid < len) out.dbeta[(size_t)(t0 + tid) * H + h] = p.db[(size_t)b * C + tid];
+  if (ct == 0 && tid < len) out.dbeta[(size_t)(t0 + tid) * H + h] = p.db[(size_t)b * C + tid];
 }
-
 
 // Chunk counts of the sequences, on the host.
 struct BwdCounts {
@@ -1169,11 +1306,8 @@ hipError_t launch_backward_t(const BackwardArgs& a) {
     if (gerr == hipSuccess) gerr = e;
   };
   const std::integral_constant<int, kGemmDual> dual;
-  const std::integral_constant<int, kGemmCat> cat;
-  const size_t scd = (size_t)C * D, scc = (size_t)C * C, sdd = (size_t)D * D;
+  const size_t scd = (size_t)C * D, sdd = (size_t)D * D;
   const GemmNT NT;
-  const GemmNN NN;
-  const GemmTN TN;
   // Segment s: its geometry, then prep, the Grams, the inverse (through the
   // forward operands of the serial pass); `grams_p` adds P.
   auto segment_setup = [&](int s, bool grams_p) {
@@ -1240,23 +1374,13 @@ hipError_t launch_backward_t(const BackwardArgs& a) {
     gemm(NT, p.dU, p.R, p.dT, C, C, D, D, D, scd, scd, 1.f, 0, 0);    // dT = dU R^T
     gemm(NT, p.dO, p.U, p.dP, C, C, D, D, D, scd, scd, 1.f, 0, 1);    // dP = tril(dO U^T)
     hipLaunchKernelGGL((bwd_cc_kernel<C>), dim3(NB), dim3(256), 0, a.stream, p);
-    // Pairwise gradient terms of the moderate-decay chunks (R, U, dU are free).
-    {  // Y1 = dBm Kh and Y2 = dP Kh, Kh read once
-      GemmX x2;
-      x2.A2 = p.dP;
-      x2.C2 = p.U;
-      gemm2(NN, dual, p.dBm, p.Kh, p.R, C, D, C, C, D, scc, scd, 1.f, 0, x2);
-    }
-    {  // Y3 = dBm^T Kt + dP^T Qt, written once
-      GemmX x2;
-      x2.A2 = p.dP;
-      x2.B2 = p.Qt;
-      x2.K2 = C;
-      gemm2(TN, cat, p.dBm, p.Kt, p.dU, C, D, C, C, D, scc, scd, 1.f, 0, x2);
-    }
     if (gerr != hipSuccess) return gerr;
+    // Pairwise gradient terms: Z1..Z3 of the strong-decay chunks into the R,
+    // U, dU planes (free by now), then the final pass, which forms those of
+    // the other chunks itself.
     hipLaunchKernelGGL((bwd_pairs_tile_kernel<D, C>), dim3(NB), dim3(256), tlds, a.stream, p);
-    hipLaunchKernelGGL((bwd_final_fast_kernel<D, C>), dim3(NB), dim3(256), 0, a.stream, p, geo, out);
+    hipLaunchKernelGGL((bwd_final_prod_kernel<D, C>), dim3((NB + 7) / 8 * 8 * (D / 64)), dim3(256), 0, a.stream,
+                       p, geo, out, (int)NB);
   }
   if (gerr != hipSuccess) return gerr;
   return hipGetLastError();
