@@ -170,33 +170,15 @@ __global__ __launch_bounds__(256) void fp32_gemm_kernel(const float* __restrict_
   __shared__ __attribute__((aligned(16))) float As[(DUAL ? 2 : 1) * 64 * kGemmLd];  // As[m][k] (then A2's)
   __shared__ __attribute__((aligned(16))) float Bs[64 * kGemmLd];                   // Bs[n][k]
   constexpr int LD = kGemmLd, NV = kGemmKStage * 16 / 256;  // vectors per thread and matrix
-  // Work units (item, 64 x 64 tile of C): items in groups of eight, the tiles
-  // of a group's items interleaved (item j of a group and tile t are unit
-  // 8 t + j of the group), so an item's tiles, which share an operand, run
-  // close together on one XCD: consecutive workgroups go to the chip's eight
-  // XCDs in turn, and a workgroup takes units blockIdx.x, + gridDim.x, ...
-  // (gridDim.x a multiple of eight), the next unit's first loads issued
-  // before the current unit's last products.
+  // Items in groups of eight, the tiles of a group's items interleaved: item
+  // j of a group and tile t take block 8 t + j of the group, so an item's
+  // tiles (which share an operand) run close together on one XCD, since
+  // consecutive block ids go to the chip's eight XCDs in turn.
   const int ntn = (N + 63) / 64, ntiles = ntn * ((M + 63) / 64);
-  const size_t nunits = (nb + 7) / 8 * 8 * (size_t)ntiles;
-  struct Unit {
-    size_t bt;
-    int m0, n0;
-  };
-  auto next_unit = [&](size_t u, Unit& t) {  // first unit at or after u of this workgroup's (nunits: none)
-    for (; u < nunits; u += gridDim.x) {
-      const size_t grp = u / (8 * (size_t)ntiles), rem = u % (8 * (size_t)ntiles);
-      t.bt = 8 * grp + rem % 8;
-      const int tile = (int)(rem / 8);
-      t.m0 = (tile / ntn) * 64;
-      t.n0 = (tile % ntn) * 64;
-      if (t.bt < nb) break;  // else a padding item of the last group
-    }
-    return u;
-  };
-  Unit cur, nxt;
-  size_t u = next_unit(blockIdx.x, cur);
-  if (u >= nunits) return;
+  const int grp = blockIdx.x / (8 * ntiles), rem = blockIdx.x % (8 * ntiles);
+  const int bt = 8 * grp + rem % 8, tile = rem / 8;
+  if ((size_t)bt >= nb) return;
+  const int m0 = (tile / ntn) * 64, n0 = (tile % ntn) * 64;
   // Stages of up to kGemmKStage k: the first product's, then (kGemmCat) the
   // second's, so no stage mixes the two.
   const int ns1 = (K + kGemmKStage - 1) / kGemmKStage;
@@ -216,26 +198,26 @@ __global__ __launch_bounds__(256) void fp32_gemm_kernel(const float* __restrict_
   // threads take sixteen rows, so their transposing LDS writes hit distinct
   // banks.)  Rows and columns past M or N are loaded from the last ones and
   // zeroed when written to LDS, so the loads take no branch.
-  auto fetch = [&](const Unit& t, int si) {
+  auto fetch = [&](int si) {
     bool second;
     int kk, ks;
     stage_at(si, second, kk, ks);
-    const float* sa_ = (second ? x2.A2 : A) + t.bt * sa;
-    const float* sb_ = (second ? x2.B2 : B) + t.bt * sb;
-    const float* sc_ = X == kGemmDual ? x2.A2 + t.bt * sa : nullptr;
+    const float* sa_ = (second ? x2.A2 : A) + (size_t)bt * sa;
+    const float* sb_ = (second ? x2.B2 : B) + (size_t)bt * sb;
+    const float* sc_ = X == kGemmDual ? x2.A2 + (size_t)bt * sa : nullptr;
 #pragma unroll
     for (int x = 0; x < NV; ++x) {
       if (x >= ks / 16) break;
       const int v = tid + 256 * x, kr = 16 * x + tid % 16, c4 = 4 * (tid / 16);
       const int q = ks / 4, rv = v / q, cv = kk + 4 * (v % q);
       size_t oa;
-      if (TA) oa = (size_t)(kk + kr) * lda + min(t.m0 + c4, M - 4);
-      else oa = (size_t)min(t.m0 + rv, M - 1) * lda + cv;
+      if (TA) oa = (size_t)(kk + kr) * lda + min(m0 + c4, M - 4);
+      else oa = (size_t)min(m0 + rv, M - 1) * lda + cv;
       xa[x] = *reinterpret_cast<const f32x4*>(sa_ + oa);
       if constexpr (DUAL) xc[x] = *reinterpret_cast<const f32x4*>(sc_ + oa);
       size_t ob;
-      if (!TB) ob = (size_t)(kk + kr) * ldb + min(t.n0 + c4, N - 4);
-      else ob = (size_t)min(t.n0 + rv, N - 1) * ldb + cv;
+      if (!TB) ob = (size_t)(kk + kr) * ldb + min(n0 + c4, N - 4);
+      else ob = (size_t)min(n0 + rv, N - 1) * ldb + cv;
       xb[x] = *reinterpret_cast<const f32x4*>(sb_ + ob);
     }
   };
@@ -252,7 +234,7 @@ __global__ __launch_bounds__(256) void fp32_gemm_kernel(const float* __restrict_
     for (int x = 0; x < NV; ++x) {
       if (x >= ks / 16) break;
       const int v = tid + 256 * x, kr = 16 * x + tid % 16, c4 = 4 * (tid / 16), rv = v / (ks / 4);
-      const bool ina = (TA ? cur.m0 + c4 : cur.m0 + rv) < M, inb = (TB ? cur.n0 + rv : cur.n0 + c4) < N;
+      const bool ina = (TA ? m0 + c4 : m0 + rv) < M, inb = (TB ? n0 + rv : n0 + c4) < N;
       const f32x4 z = {0.f, 0.f, 0.f, 0.f};
       stA(As, ina ? xa[x] : z, v, kr, c4, ks);
       if constexpr (DUAL) stA(As + 64 * LD, ina ? xc[x] : z, v, kr, c4, ks);
@@ -271,15 +253,68 @@ __global__ __launch_bounds__(256) void fp32_gemm_kernel(const float* __restrict_
   const int l = tid & 63, lm = l & 15, lg = l >> 4;
   const int wm = (tid >> 7) * 32, wn = ((tid >> 6) & 1) * 32;  // this wave's quarter
   f32x4 acc[2][2], acc2[DUAL ? 2 : 1][DUAL ? 2 : 1];
+#pragma unroll
+  for (int i = 0; i < 2; ++i)
+#pragma unroll
+    for (int j = 0; j < 2; ++j) acc[i][j] = f32x4{0.f, 0.f, 0.f, 0.f};
+  if constexpr (DUAL) {
+#pragma unroll
+    for (int i = 0; i < 2; ++i)
+#pragma unroll
+      for (int j = 0; j < 2; ++j) acc2[i][j] = f32x4{0.f, 0.f, 0.f, 0.f};
+  }
+  fetch(0);
+  for (int si = 0; si < nst; ++si) {
+    bool second;
+    int kk, ks;
+    stage_at(si, second, kk, ks);
+    (void)second;
+    (void)kk;
+    if (si > 0) __syncthreads();  // the previous stage's reads are done
+    stage(ks);
+    __syncthreads();
+    if (si + 1 < nst) fetch(si + 1);
+    auto kblock = [&](int kb) {  // k = 16 kb .. 16 kb + 15 of the stage
+      const int ko = 16 * kb + 4 * lg;
+      const f32x4 a0 = *reinterpret_cast<const f32x4*>(As + (wm + lm) * LD + ko);
+      const f32x4 a1 = *reinterpret_cast<const f32x4*>(As + (wm + 16 + lm) * LD + ko);
+      const f32x4 b0 = *reinterpret_cast<const f32x4*>(Bs + (wn + lm) * LD + ko);
+      const f32x4 b1 = *reinterpret_cast<const f32x4*>(Bs + (wn + 16 + lm) * LD + ko);
+#pragma unroll
+      for (int s = 0; s < 4; ++s) {
+        acc[0][0] = mfma4(a0[s], b0[s], acc[0][0]);
+        acc[0][1] = mfma4(a0[s], b1[s], acc[0][1]);
+        acc[1][0] = mfma4(a1[s], b0[s], acc[1][0]);
+        acc[1][1] = mfma4(a1[s], b1[s], acc[1][1]);
+      }
+      if constexpr (DUAL) {
+        const f32x4 c0 = *reinterpret_cast<const f32x4*>(As + (64 + wm + lm) * LD + ko);
+        const f32x4 c1 = *reinterpret_cast<const f32x4*>(As + (64 + wm + 16 + lm) * LD + ko);
+#pragma unroll
+        for (int s = 0; s < 4; ++s) {
+          acc2[0][0] = mfma4(c0[s], b0[s], acc2[0][0]);
+          acc2[0][1] = mfma4(c0[s], b1[s], acc2[0][1]);
+          acc2[1][0] = mfma4(c1[s], b0[s], acc2[1][0]);
+          acc2[1][1] = mfma4(c1[s], b1[s], acc2[1][1]);
+        }
+      }
+    };
+    if (ks == kGemmKStage) {
+#pragma unroll
+      for (int kb = 0; kb < kGemmKStage / 16; ++kb) kblock(kb);
+    } else {
+      for (int kb = 0; kb < ks / 16; ++kb) kblock(kb);
+    }
+  }
   auto put = [&](float* cm, const f32x4 (&ac)[2][2], float al, int mk) {
-    float* c = cm + cur.bt * sc;
+    float* c = cm + bt * sc;
 #pragma unroll
     for (int ti = 0; ti < 2; ++ti)
 #pragma unroll
       for (int tj = 0; tj < 2; ++tj)
 #pragma unroll
         for (int i = 0; i < 4; ++i) {
-          const int m = cur.m0 + wm + 16 * ti + 4 * lg + i, nn = cur.n0 + wn + 16 * tj + lm;
+          const int m = m0 + wm + 16 * ti + 4 * lg + i, nn = n0 + wn + 16 * tj + lm;
           if (m < M && nn < N) {
             const bool keep = mk == 0 || (mk == 1 ? nn <= m : nn < m);
             const float v = keep ? al * ac[ti][tj][i] : 0.f;
@@ -287,72 +322,8 @@ __global__ __launch_bounds__(256) void fp32_gemm_kernel(const float* __restrict_
           }
         }
   };
-  fetch(cur, 0);
-  for (bool first = true;; first = false) {
-#pragma unroll
-    for (int i = 0; i < 2; ++i)
-#pragma unroll
-      for (int j = 0; j < 2; ++j) acc[i][j] = f32x4{0.f, 0.f, 0.f, 0.f};
-    if constexpr (DUAL) {
-#pragma unroll
-      for (int i = 0; i < 2; ++i)
-#pragma unroll
-        for (int j = 0; j < 2; ++j) acc2[i][j] = f32x4{0.f, 0.f, 0.f, 0.f};
-    }
-    size_t un = nunits;
-    for (int si = 0; si < nst; ++si) {
-      bool second;
-      int kk, ks;
-      stage_at(si, second, kk, ks);
-      (void)second;
-      (void)kk;
-      if (!first || si > 0) __syncthreads();  // the previous stage's reads are done
-      stage(ks);
-      __syncthreads();
-      if (si + 1 < nst) {
-        fetch(cur, si + 1);
-      } else {
-        un = next_unit(u + gridDim.x, nxt);
-        if (un < nunits) fetch(nxt, 0);
-      }
-      auto kblock = [&](int kb) {  // k = 16 kb .. 16 kb + 15 of the stage
-        const int ko = 16 * kb + 4 * lg;
-        const f32x4 a0 = *reinterpret_cast<const f32x4*>(As + (wm + lm) * LD + ko);
-        const f32x4 a1 = *reinterpret_cast<const f32x4*>(As + (wm + 16 + lm) * LD + ko);
-        const f32x4 b0 = *reinterpret_cast<const f32x4*>(Bs + (wn + lm) * LD + ko);
-        const f32x4 b1 = *reinterpret_cast<const f32x4*>(Bs + (wn + 16 + lm) * LD + ko);
-#pragma unroll
-        for (int s = 0; s < 4; ++s) {
-          acc[0][0] = mfma4(a0[s], b0[s], acc[0][0]);
-          acc[0][1] = mfma4(a0[s], b1[s], acc[0][1]);
-          acc[1][0] = mfma4(a1[s], b0[s], acc[1][0]);
-          acc[1][1] = mfma4(a1[s], b1[s], acc[1][1]);
-        }
-        if constexpr (DUAL) {
-          const f32x4 c0 = *reinterpret_cast<const f32x4*>(As + (64 + wm + lm) * LD + ko);
-          const f32x4 c1 = *reinterpret_cast<const f32x4*>(As + (64 + wm + 16 + lm) * LD + ko);
-#pragma unroll
-          for (int s = 0; s < 4; ++s) {
-            acc2[0][0] = mfma4(c0[s], b0[s], acc2[0][0]);
-            acc2[0][1] = mfma4(c0[s], b1[s], acc2[0][1]);
-            acc2[1][0] = mfma4(c1[s], b0[s], acc2[1][0]);
-            acc2[1][1] = mfma4(c1[s], b1[s], acc2[1][1]);
-          }
-        }
-      };
-      if (ks == kGemmKStage) {
-#pragma unroll
-        for (int kb = 0; kb < kGemmKStage / 16; ++kb) kblock(kb);
-      } else {
-        for (int kb = 0; kb < ks / 16; ++kb) kblock(kb);
-      }
-    }
-    put(Cm, acc, alpha, mask);
-    if constexpr (DUAL) put(x2.C2, acc2, x2.alpha2, x2.mask2);
-    if (un >= nunits) break;
-    u = un;
-    cur = nxt;
-  }
+  put(Cm, acc, alpha, mask);
+  if constexpr (DUAL) put(x2.C2, acc2, x2.alpha2, x2.mask2);
 }
 
 // Operand orientations of fp32_gemm_kernel, as tags for launch_fp32_gemm.
@@ -370,23 +341,8 @@ inline hipError_t launch_fp32_gemm(const float* A, const float* B, float* Cm, in
   if (K % 16 || M % 4 || N % 4) return hipErrorInvalidValue;
   if (X == kGemmCat && (x2.K2 % 16 || !x2.A2 || !x2.B2)) return hipErrorInvalidValue;
   if (X == kGemmDual && (!x2.A2 || !x2.C2)) return hipErrorInvalidValue;
-  const size_t units = (NB + 7) / 8 * 8 * (size_t)((N + 63) / 64) * ((M + 63) / 64);
-  if (units == 0) return hipSuccess;
-  // As many workgroups as the device holds at once (a multiple of eight),
-  // each looping over its share of the units.
-  static const int per_cu = [] {
-    int n = 0;
-    if (hipOccupancyMaxActiveBlocksPerMultiprocessor(&n, reinterpret_cast<const void*>(&fp32_gemm_kernel<TA, TB, X>),
-                                                     256, 0) != hipSuccess || n < 1)
-      n = 1;
-    return n;
-  }();
-  int dev = 0, cus = 0;
-  hipError_t e = hipGetDevice(&dev);
-  if (e == hipSuccess) e = hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev);
-  if (e != hipSuccess) return e;
-  const size_t slots = (size_t)(cus > 0 ? cus : 1) * per_cu / 8 * 8;
-  const size_t blocks = units < slots || slots == 0 ? units : slots;
+  const size_t blocks = (NB + 7) / 8 * 8 * (size_t)((N + 63) / 64) * ((M + 63) / 64);
+  if (blocks == 0) return hipSuccess;
   if (blocks > 0x7fffffff) return hipErrorInvalidValue;
   hipLaunchKernelGGL((fp32_gemm_kernel<TA, TB, X>), dim3((unsigned)blocks), dim3(256), 0, stream, A, B, Cm, M,
                      N, K, lda, ldb, ldc, sa, sb, sc, alpha, acc_c, mask, NB, x2);
