@@ -133,18 +133,33 @@ __global__ __launch_bounds__(256) void bwd_prep_kernel(BwdIn in, Planes p, Geo g
   const in_t* q = reinterpret_cast<const in_t*>(in.q);
   const in_t* k = reinterpret_cast<const in_t*>(in.k);
   const in_t* v = reinterpret_cast<const in_t*>(in.v);
-  f32x4 qv[NV], kv[NV];
+  // Inputs are loaded unconditionally (rows past the chunk re-read its first
+  // row) and zeroed after, and each vector's loads are issued before the
+  // previous vector's stores: a load under the row test made every one wait
+  // for the last, and the compiler may not move a load above a store that
+  // could alias it.
+  f32x4 qv[NV], kv[NV], vr[2], dr[2], gr[2];
+  auto fetch = [&](int x) {
+    const int idx = 4 * ((int)threadIdx.x + 256 * x), r = idx / D, c = idx % D;
+    const size_t ti = ((size_t)(t0 + (r < len ? r : 0)) * H + h) * D + c;
+    qv[x] = load4(q + ti);
+    kv[x] = load4(k + ti);
+    vr[x & 1] = load4(v + ti);
+    dr[x & 1] = load4(in.dout + ti);
+    gr[x & 1] = load4(in.g + ti);
+  };
+  fetch(0);
 #pragma unroll
   for (int x = 0; x < NV; ++x) {
+    if (x + 1 < NV) fetch(x + 1);
     const int idx = 4 * ((int)threadIdx.x + 256 * x);
     const int r = idx / D, c = idx % D;
     const bool ok = r < len;
-    const size_t ti = ((size_t)(t0 + (ok ? r : 0)) * H + h) * D + c;
     const f32x4 z = {0, 0, 0, 0};
-    qv[x] = ok ? load4(q + ti) : z;
-    kv[x] = ok ? load4(k + ti) : z;
-    const f32x4 vv = ok ? load4(v + ti) : z, dv = ok ? load4(in.dout + ti) : z;
-    const f32x4 gv = ok ? load4(in.g + ti) : z;
+    qv[x] = ok ? qv[x] : z;
+    kv[x] = ok ? kv[x] : z;
+    const f32x4 vv = ok ? vr[x & 1] : z, dv = ok ? dr[x & 1] : z;
+    const f32x4 gv = ok ? gr[x & 1] : z;
     *reinterpret_cast<f32x4*>(p.Q + pcd + idx) = qv[x];
     *reinterpret_cast<f32x4*>(p.K + pcd + idx) = kv[x];
     *reinterpret_cast<f32x4*>(p.V + pcd + idx) = vv;

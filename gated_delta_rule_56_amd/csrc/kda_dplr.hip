@@ -97,28 +97,53 @@ __global__ __launch_bounds__(256) void dplr_prep_kernel(DIn in, DPlanes p, Geo g
   };
   auto st4 = [&](float* plane, int idx, f32x4 x) { *reinterpret_cast<f32x4*>(plane + pcd + idx) = x; };
   auto ld4p = [&](const float* plane, int idx) { return *reinterpret_cast<const f32x4*>(plane + pcd + idx); };
-  for (int v4 = threadIdx.x; v4 < C * D / 4; v4 += 256) {
-    const int idx = 4 * v4, r = idx / D, c = idx % D;
+  // Inputs are loaded unconditionally (rows past the chunk re-read its first
+  // row) and zeroed after, and each vector's loads are issued before the
+  // previous vector's stores: a load under the row test made every one wait
+  // for the last, and the compiler may not move a load above a store that
+  // could alias it.
+  constexpr int NV = C * D / 4 / 256;
+  static_assert(NV * 256 * 4 == C * D, "whole vectors per thread");
+  f32x4 kl[2], gl4[2], ql[2], vl[2], al[2], bl[2];
+  float bel[2];
+  auto fetch = [&](int x) {
+    const int idx = 4 * ((int)threadIdx.x + 256 * x), r = idx / D, c = idx % D;
+    const int rr = r < len ? r : 0, s2 = x & 1;
+    const size_t ti = ((size_t)(t0 + rr) * H + h) * D + c;
+    kl[s2] = ld4(in.k, ti);
+    gl4[s2] = *reinterpret_cast<const f32x4*>(in.g + ti);
+    ql[s2] = ld4(in.q, ti);
+    vl[s2] = ld4(in.v, ti);
+    if (TIED) {
+      bel[s2] = in.beta[(size_t)(t0 + rr) * H + h];
+    } else {
+      al[s2] = ld4(in.a, ti);
+      bl[s2] = ld4(in.b, ti);
+    }
+  };
+  fetch(0);
+#pragma unroll
+  for (int x = 0; x < NV; ++x) {
+    if (x + 1 < NV) fetch(x + 1);
+    const int idx = 4 * ((int)threadIdx.x + 256 * x), r = idx / D, c = idx % D, s2 = x & 1;
     const bool ok = r < len;
-    const size_t ti = ((size_t)(t0 + (ok ? r : 0)) * H + h) * D + c;
     const f32x4 z = {0, 0, 0, 0};
-    const f32x4 kv = ok ? ld4(in.k, ti) : z;
-    const f32x4 gv = ok ? *reinterpret_cast<const f32x4*>(in.g + ti) : z;
+    const f32x4 kv = ok ? kl[s2] : z, gv = ok ? gl4[s2] : z;
     f32x4 av, bv;
     if (TIED) {
-      const float be = ok ? in.beta[(size_t)(t0 + r) * H + h] : 0.f;
+      const float be = ok ? bel[s2] : 0.f;
 #pragma unroll
       for (int e = 0; e < 4; ++e) {
         av[e] = be * kv[e];               // a = write key = beta k
         bv[e] = __expf(gv[e]) * kv[e];    // b = alpha k
       }
     } else {
-      av = ok ? ld4(in.a, ti) : z;
-      bv = ok ? ld4(in.b, ti) : z;
+      av = ok ? al[s2] : z;
+      bv = ok ? bl[s2] : z;
     }
-    st4(p.Q, idx, ok ? ld4(in.q, ti) : z);
+    st4(p.Q, idx, ok ? ql[s2] : z);
     st4(p.K, idx, TIED ? av : kv);  // the key that writes v
-    st4(p.V, idx, ok ? ld4(in.v, ti) : z);
+    st4(p.V, idx, ok ? vl[s2] : z);
     st4(p.A, idx, av);
     st4(p.B, idx, bv);
     st4(p.G, idx, gv);
