@@ -914,18 +914,45 @@ __global__ __launch_bounds__(256) void bwd_cc_kernel(Planes p) {
   __shared__ __attribute__((aligned(16))) float MTs[C][LDC];  // M^T
   __shared__ __attribute__((aligned(16))) float dMs[C][LDC];  // dM = dT Diag(beta), later dA * Bm
   __shared__ __attribute__((aligned(16))) float Xs[C][LDC];   // X = dM M^T
+  constexpr int NS = C * C / 256, CP = 256 / C;  // elements per thread; threads per column
+  static_assert(NS * 256 == C * C, "whole elements per thread");
+  __shared__ float colp[CP][C];  // partial column sums of M * dT
   const int b = blockIdx.x, tid = threadIdx.x;
   const size_t pcc = (size_t)b * C * C;
   const float* beta = p.beta + (size_t)b * C;
-  for (int idx = tid; idx < C * C; idx += 256) {
-    const int r = idx / C, i = idx % C;
-    const float m = p.M[pcc + idx];
-    Ms[r][i] = m;
-    MTs[i][r] = m;
-    dMs[r][i] = p.dT[pcc + idx] * beta[i];
-  }
-  __syncthreads();
   const int w = tid >> 6, l = tid & 63, lm = l & 15, lg = l >> 4;
+  // Every global load is issued here, before the first wait: M and dT (this
+  // thread's column i = tid % C, rows tid / C + CP x), beta_i, and the Bm
+  // values and beta rows of this lane's accumulator positions for the last
+  // stage (whose stores the compiler may not move those loads past).
+  float mv[NS], tv[NS], bmv[TPW][4], brv[TPW][4];
+#pragma unroll
+  for (int x = 0; x < NS; ++x) {
+    mv[x] = p.M[pcc + tid + 256 * x];
+    tv[x] = p.dT[pcc + tid + 256 * x];
+  }
+  const float bi = beta[tid % C];
+#pragma unroll
+  for (int j = 0; j < TPW; ++j) {
+    const int t = min(w + 4 * j, NT * NT - 1);
+    const int r0 = 16 * (t / NT), c0 = 16 * (t % NT);
+#pragma unroll
+    for (int v = 0; v < 4; ++v) {
+      bmv[j][v] = p.Bm[pcc + (size_t)(r0 + 4 * lg + v) * C + c0 + lm];
+      brv[j][v] = beta[r0 + 4 * lg + v];
+    }
+  }
+  float cs = 0.f;
+#pragma unroll
+  for (int x = 0; x < NS; ++x) {
+    const int idx = tid + 256 * x, r = idx / C, i = idx % C;
+    Ms[r][i] = mv[x];
+    MTs[i][r] = mv[x];
+    dMs[r][i] = tv[x] * bi;
+    cs += mv[x] * tv[x];
+  }
+  colp[tid / C][tid % C] = cs;
+  __syncthreads();
   f32x4 acc[TPW];
   // X = dM M^T: A[r][l] = dM[r][l], B[l][i] = M[i][l]
 #pragma unroll
@@ -980,8 +1007,8 @@ __global__ __launch_bounds__(256) void bwd_cc_kernel(Planes p) {
       for (int v = 0; v < 4; ++v) {
         const int r = r0 + 4 * lg + v, i = c0 + lm;
         const float sv = i < r ? -acc[j][v] : 0.f;
-        p.dBm[pcc + r * C + i] = beta[r] * sv;
-        dMs[r][i] = sv * p.Bm[pcc + r * C + i];  // dA * Bm, for the row sums
+        p.dBm[pcc + r * C + i] = brv[j][v] * sv;
+        dMs[r][i] = sv * bmv[j][v];  // dA * Bm, for the row sums
       }
     }
   }
@@ -989,7 +1016,9 @@ __global__ __launch_bounds__(256) void bwd_cc_kernel(Planes p) {
   if (tid < C) {
     const int j = tid;
     float s = 0.f;
-    for (int r = 0; r < C; ++r) s += Ms[r][j] * p.dT[pcc + r * C + j] + dMs[j][r];
+#pragma unroll
+    for (int x = 0; x < CP; ++x) s += colp[x][j];  // colsum(M * dT)
+    for (int r = 0; r < C; ++r) s += dMs[j][r];     // rowsum(dA * Bm)
     p.db[(size_t)b * C + j] = s;
   }
 }
