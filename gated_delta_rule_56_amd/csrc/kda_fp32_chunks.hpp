@@ -397,9 +397,21 @@ __global__ __launch_bounds__(256) void unit_lower_inverse_kernel(const float* __
   const int b = blockIdx.x, tid = threadIdx.x;
   const size_t pcc = (size_t)b * C * C;
   const float* r = rs ? rs + (size_t)b * C : nullptr;
-  for (int idx = tid; idx < C * C; idx += 256) {
-    const int i = idx / C, j = idx % C;
-    As[i][j] = j < i ? (r ? r[i] : 1.f) * A[pcc + idx] : 0.f;
+  // Every load of the staging first (a loop that waited for each element's
+  // load before its LDS write took most of the kernel's time).
+  constexpr int NS = C * C / 256;
+  static_assert(NS * 256 == C * C, "whole elements per thread");
+  float av[NS], rv[NS];
+#pragma unroll
+  for (int x = 0; x < NS; ++x) {
+    const int idx = tid + 256 * x;
+    av[x] = A[pcc + idx];
+    rv[x] = r ? r[idx / C] : 1.f;
+  }
+#pragma unroll
+  for (int x = 0; x < NS; ++x) {
+    const int idx = tid + 256 * x, i = idx / C, j = idx % C;
+    As[i][j] = j < i ? rv[x] * av[x] : 0.f;
     Xs[i][j] = 0.f;
   }
   __syncthreads();
