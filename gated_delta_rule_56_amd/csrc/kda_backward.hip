@@ -234,19 +234,56 @@ struct TileLds {
 
 // The tile operands of item b, and whether each diagonal tile spans more
 // than kTileSpan on some channel (bad[t], wave-uniform after the barrier).
-template <int D, int C>
+template <int D, int C, bool PAIRS = false>
 __device__ __forceinline__ void tile_operands(const Planes& p, size_t b, TileLds<D, C>& L, bool* bad) {
-  constexpr int NT = C / 16;
-  const size_t pcd = b * C * D;
-  for (int idx = threadIdx.x; idx < NT * D; idx += 256) {
-    const int t = idx / D, c = idx % D;
-    L.Gs[t][c] = t == 0 ? 0.f : p.Gam[pcd + (size_t)(16 * t - 1) * D + c];
-    L.Ge[t][c] = p.Gam[pcd + (size_t)(16 * t + 15) * D + c];
+  constexpr int NT = C / 16, NI = C * D / 256, NG = (NT * D + 255) / 256, NCC = PAIRS ? C * C / 256 : 0;
+  static_assert(NI * 256 == C * D && (!PAIRS || NCC * 256 == C * C), "whole elements per thread");
+  const size_t pcd = b * C * D, pcc = b * C * C;
+  const int tid = threadIdx.x;
+  // Every global load first (a loop that waited for each element's loads
+  // before its LDS writes took most of these kernels' time): Gamma, K, Q of
+  // the thread's elements, Gamma before and at the end of each tile, and
+  // (PAIRS) dBm and dP.
+  float gv[NI], kv[NI], qv[NI], gsv[NG], gev[NG], bmv[NCC > 0 ? NCC : 1], dpv[NCC > 0 ? NCC : 1];
+#pragma unroll
+  for (int x = 0; x < NI; ++x) {
+    const size_t e = pcd + tid + 256 * x;
+    gv[x] = p.Gam[e];
+    kv[x] = p.K[e];
+    qv[x] = p.Q[e];
+  }
+#pragma unroll
+  for (int x = 0; x < NG; ++x) {
+    const int idx = min(tid + 256 * x, NT * D - 1), t = idx / D, c = idx % D;
+    gsv[x] = p.Gam[pcd + (size_t)(t == 0 ? 0 : 16 * t - 1) * D + c];
+    gev[x] = p.Gam[pcd + (size_t)(16 * t + 15) * D + c];
+  }
+#pragma unroll
+  for (int x = 0; x < NCC; ++x) {
+    bmv[x] = p.dBm[pcc + tid + 256 * x];
+    dpv[x] = p.dP[pcc + tid + 256 * x];
+  }
+#pragma unroll
+  for (int x = 0; x < NG; ++x) {
+    const int idx = tid + 256 * x, t = idx / D, c = idx % D;
+    if (NT * D % 256 == 0 || idx < NT * D) {
+      L.Gs[t][c] = t == 0 ? 0.f : gsv[x];
+      L.Ge[t][c] = gev[x];
+    }
+  }
+  if constexpr (PAIRS) {
+#pragma unroll
+    for (int x = 0; x < NCC; ++x) {
+      const int idx = tid + 256 * x, r = idx / C, i = idx % C;
+      L.dBm[r][i] = bmv[x];
+      L.dP[r][i] = dpv[x];
+    }
   }
   __syncthreads();
-  for (int idx = threadIdx.x; idx < C * D; idx += 256) {
-    const int r = idx / D, c = idx % D, t = r / 16;
-    const float g = p.Gam[pcd + idx], k = p.K[pcd + idx], q = p.Q[pcd + idx];
+#pragma unroll
+  for (int x = 0; x < NI; ++x) {
+    const int idx = tid + 256 * x, r = idx / D, c = idx % D, t = r / 16;
+    const float g = gv[x], k = kv[x], q = qv[x];
     const float er = __expf(g - L.Gs[t][c]);
     L.Kr[r][c] = k * er;
     L.Qr[r][c] = q * er;
@@ -338,14 +375,9 @@ __global__ __launch_bounds__(256) void bwd_pairs_tile_kernel(Planes p) {
   constexpr int NT = C / 16, NCT = D / 16;
   const size_t b = blockIdx.x;
   if (p.fast[b]) return;  // the products Y1, Y2, Y3
-  const size_t pcc = b * C * C, pcd = b * C * D;
-  for (int idx = threadIdx.x; idx < C * C; idx += 256) {
-    const int r = idx / C, i = idx % C;
-    L.dBm[r][i] = p.dBm[pcc + idx];
-    L.dP[r][i] = p.dP[pcc + idx];
-  }
+  const size_t pcd = b * C * D;
   bool bad[NT];
-  tile_operands<D, C>(p, b, L, bad);
+  tile_operands<D, C, true>(p, b, L, bad);  // with dBm and dP
   const int w = wave_id(), l = lane_id(), m = l & 15, g = l >> 4;
   for (int ot = w; ot < NT * NCT; ot += 4) {
     const int ta = ot / NCT, ct = ot % NCT;
