@@ -166,12 +166,25 @@ __global__ __launch_bounds__(256) void dplr_prep_kernel(DIn in, DPlanes p, Geo g
     big = __any(big);
     if (threadIdx.x == 0) p.fast[b] = big ? 0 : 1;
   }
-  for (int v4 = threadIdx.x; v4 < C * D / 4; v4 += 256) {
-    const int idx = 4 * v4, r = idx / D, c = idx % D;
+  // The planes written above are read back (from L2) a vector ahead of the
+  // stores that could alias them, as in the first loop.
+  f32x4 rav[2], rkv[2], rqv[2], rbv[2], rgv[2];
+  auto refetch = [&](int x) {
+    const int idx = 4 * ((int)threadIdx.x + 256 * x), s2 = x & 1;
+    rav[s2] = ld4p(p.A, idx);
+    rkv[s2] = ld4p(p.K, idx);
+    rqv[s2] = ld4p(p.Q, idx);
+    rbv[s2] = ld4p(p.B, idx);
+    rgv[s2] = ld4p(p.G, idx);
+  };
+  refetch(0);
+#pragma unroll
+  for (int x = 0; x < NV; ++x) {
+    if (x + 1 < NV) refetch(x + 1);
+    const int idx = 4 * ((int)threadIdx.x + 256 * x), r = idx / D, c = idx % D, s2 = x & 1;
     const f32x4 gm = *reinterpret_cast<const f32x4*>(&Gs[r][c]);
     const f32x4 gl = *reinterpret_cast<const f32x4*>(&Gs[C - 1][c]);
-    const f32x4 av = ld4p(p.A, idx), kv = ld4p(p.K, idx), qv = ld4p(p.Q, idx);
-    const f32x4 bv = ld4p(p.B, idx), gv = ld4p(p.G, idx);
+    const f32x4 av = rav[s2], kv = rkv[s2], qv = rqv[s2], bv = rbv[s2], gv = rgv[s2];
     f32x4 qt, bt, ah, kh, ab, kb;
 #pragma unroll
     for (int e = 0; e < 4; ++e) {
@@ -222,19 +235,45 @@ __global__ __launch_bounds__(256) void dplr_gram_tile_kernel(DPlanes p) {
   const size_t b = blockIdx.x;
   if (p.fast[b]) return;  // formed as products
   const size_t pcd = b * C * D, pcc = b * C * C;
-  for (int idx = threadIdx.x; idx < NT * D; idx += 256) {
-    const int t = idx / D, c = idx % D;
-    L.Gs[t][c] = t == 0 ? 0.f : p.Gam[pcd + (size_t)(16 * t - 1) * D + c];
-    L.Ge[t][c] = p.Gam[pcd + (size_t)(16 * t + 15) * D + c];
+  // Every staging load before the first LDS write (a loop that waited for
+  // each element's loads took most of the kernel's time).
+  constexpr int NI = C * D / 256, NG = (NT * D + 255) / 256;
+  static_assert(NI * 256 == C * D, "whole elements per thread");
+  const int tid = threadIdx.x;
+  float gmv[NI], qv[NI], bv[NI], gv[NI], av[NI], kv[NI], gsv[NG], gev[NG];
+#pragma unroll
+  for (int x = 0; x < NI; ++x) {
+    const size_t e = pcd + tid + 256 * x;
+    gmv[x] = p.Gam[e];
+    qv[x] = p.Q[e];
+    bv[x] = p.B[e];
+    gv[x] = p.G[e];
+    av[x] = p.A[e];
+    kv[x] = TIED ? 0.f : p.K[e];
+  }
+#pragma unroll
+  for (int x = 0; x < NG; ++x) {
+    const int idx = min(tid + 256 * x, NT * D - 1), t = idx / D, c = idx % D;
+    gsv[x] = p.Gam[pcd + (size_t)(t == 0 ? 0 : 16 * t - 1) * D + c];
+    gev[x] = p.Gam[pcd + (size_t)(16 * t + 15) * D + c];
+  }
+#pragma unroll
+  for (int x = 0; x < NG; ++x) {
+    const int idx = tid + 256 * x, t = idx / D, c = idx % D;
+    if (NT * D % 256 == 0 || idx < NT * D) {
+      L.Gs[t][c] = t == 0 ? 0.f : gsv[x];
+      L.Ge[t][c] = gev[x];
+    }
   }
   __syncthreads();
-  for (int idx = threadIdx.x; idx < C * D; idx += 256) {
-    const int r = idx / D, c = idx % D, t = r / 16;
-    const float gm = p.Gam[pcd + idx], gs = L.Gs[t][c], ce = __expf(L.Ge[t][c] - gm);
-    L.Qr[r][c] = p.Q[pcd + idx] * __expf(gm - gs);
-    L.Br[r][c] = p.B[pcd + idx] * __expf(gm - p.G[pcd + idx] - gs);
-    L.Ac[r][c] = p.A[pcd + idx] * ce;
-    if (!TIED) L.Kc[r][c] = p.K[pcd + idx] * ce;
+#pragma unroll
+  for (int x = 0; x < NI; ++x) {
+    const int idx = tid + 256 * x, r = idx / D, c = idx % D, t = r / 16;
+    const float gm = gmv[x], gs = L.Gs[t][c], ce = __expf(L.Ge[t][c] - gm);
+    L.Qr[r][c] = qv[x] * __expf(gm - gs);
+    L.Br[r][c] = bv[x] * __expf(gm - gv[x] - gs);
+    L.Ac[r][c] = av[x] * ce;
+    if (!TIED) L.Kc[r][c] = kv[x] * ce;
   }
   bool bad[NT];
   for (int t = 0; t < NT; ++t) {
