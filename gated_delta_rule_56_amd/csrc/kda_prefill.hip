@@ -165,9 +165,15 @@ static size_t raw_o_bytes(const SegmentPlan& p, int H, int D, int chunk, bool ep
   return epilogue ? align256((size_t)p.max_slots * H * chunk * D * sizeof(float)) : 0;
 }
 
+// With the layer epilogue and several segments, segment s's epilogue runs in
+// segment s + 1's chunk-wide launch, after the slot table of s + 1 is made:
+// the varlen slot tables of consecutive segments then alternate between two
+// copies.
+static int table_copies(const SegmentPlan& p, bool epilogue) { return epilogue && p.nseg > 1 ? 2 : 1; }
+
 static size_t plan_bytes(const SegmentPlan& p, int num_seqs, bool varlen, int H, int D, int chunk,
                          bool in_bf16, bool epilogue) {
-  return table_bytes(num_seqs, varlen) + carry_bytes(p, num_seqs, H, D) +
+  return table_copies(p, epilogue) * table_bytes(num_seqs, varlen) + carry_bytes(p, num_seqs, H, D) +
          (size_t)p.max_slots * H * prefill_chunk_bytes(D, chunk, in_bf16) +
          raw_o_bytes(p, H, D, chunk, epilogue);
 }
@@ -1405,11 +1411,106 @@ __device__ __forceinline__ void intra_item_body(const KernelPtrs& kp, const SeqI
   }
 }
 
-// The chunk-wide pass: one workgroup per item, grid (segment slots, H).
+// ---------------------------------------------------------------------------
+// Layer epilogue (the "Kimi Linear" notes, docsaid.org, section "Other
+// Components"; greeksharifa.github.io summary, section 4): per token and
+// head, y = o / sqrt(mean_c o_c^2 + eps) * weight * sigmoid(gate).  The norm
+// spans all D value columns, which the inter-chunk pass splits over
+// workgroups, so it runs after that pass, per segment, on the raw o it left
+// in the workspace.  Four waves per (slot, head), C / 4 rows per wave.
+// D / 4 consecutive lanes hold one row, four columns each, so a wave's
+// 16-byte loads cover whole rows (two for d = 128); every row's loads are
+// issued before the first use, and the mean square is summed over the row's
+// lanes.  No barrier: a wave may leave early.  With the convolution, every
+// segment's epilogue but the last runs in the next segment's chunk-wide intra
+// launch, as workgroups after its items (two items each): the raw o is
+// untouched until that segment's carry pass, and this HBM-bound work fills
+// compute units beside the VALU-bound intra items.  The last segment's runs as
+// a launch of its own.
+// ---------------------------------------------------------------------------
+template <class M, int D, int C, bool OUT_BF16>
+__device__ __forceinline__ void layer_epilogue_item(const KernelPtrs& kp, const SeqInfo& si, int item,
+                                                    int wave) {
+  typedef typename M::in_t in_t;
+  constexpr int LPR = D / 4;       // lanes per row
+  constexpr int RPI = 64 / LPR;    // rows per wave and pass
+  constexpr int NI = C / 4 / RPI;  // passes per wave
+  static_assert(NI >= 1 && C % (4 * RPI) == 0, "whole passes per wave");
+  const Item it = intra_item<C>(si, kp, item, 0);
+  if (it.len <= 0) return;
+  const int slot = item / kp.H;
+  const int l = lane_id();
+  const int c0 = 4 * (l % LPR);
+  const int rb = (C / 4) * wave + l / LPR;
+  const in_t* gate = reinterpret_cast<const in_t*>(kp.gate);
+  const f32x4 wt = *reinterpret_cast<const f32x4*>(kp.norm_weight + c0);
+  f32x4 x[NI], gv[NI];
+#pragma unroll
+  for (int i = 0; i < NI; ++i) {
+    const int row = rb + RPI * i;
+    const int rr = row < it.len ? row : 0;  // rows past the chunk read row 0 and store nothing
+    x[i] = *reinterpret_cast<const f32x4*>(kp.o_slots + (((size_t)slot * kp.H + it.h) * C + rr) * D + c0);
+    const size_t ti = ((size_t)(it.t0 + rr) * kp.H + it.h) * D + c0;
+    if constexpr (sizeof(in_t) == 2) {
+      const bf16x4 g4 = *reinterpret_cast<const bf16x4*>(gate + ti);
+      gv[i] = f32x4{(float)g4[0], (float)g4[1], (float)g4[2], (float)g4[3]};
+    } else {
+      gv[i] = *reinterpret_cast<const f32x4*>(gate + ti);
+    }
+  }
+#pragma unroll
+  for (int i = 0; i < NI; ++i) {
+    const int row = rb + RPI * i;
+    float ss = x[i][0] * x[i][0] + x[i][1] * x[i][1] + x[i][2] * x[i][2] + x[i][3] * x[i][3];
+#pragma unroll
+    for (int off = LPR / 2; off > 0; off >>= 1) ss += __shfl_xor(ss, off);
+    const float inv = 1.f / sqrtf(ss / D + kp.norm_eps);
+    if (row < it.len) {
+      const size_t ti = ((size_t)(it.t0 + row) * kp.H + it.h) * D + c0;
+      f32x4 y;
+#pragma unroll
+      for (int e = 0; e < 4; ++e) y[e] = x[i][e] * inv * wt[e] * sigmoidf(gv[i][e]);
+      if constexpr (OUT_BF16) {
+        bf16x4 yb;
+#pragma unroll
+        for (int e = 0; e < 4; ++e) yb[e] = f2bf(y[e]);
+        *reinterpret_cast<bf16x4*>(reinterpret_cast<bf16*>(kp.o) + ti) = yb;
+      } else {
+        *reinterpret_cast<f32x4*>(reinterpret_cast<float*>(kp.o) + ti) = y;
+      }
+    }
+  }
+}
+
+// The previous segment's layer epilogue, carried by a chunk-wide launch.
+struct EpiJob {
+  SeqInfo si;    // the previous segment
+  int items;     // its (slot, head) items; 0: none
+  int out_bf16;  // y in bf16 (else fp32)
+};
+
+// The chunk-wide pass: one workgroup per item (item = slot * H + head), then
+// with the layer prologue and its convolution the workgroups of the previous
+// segment's epilogue.  (Without the convolution the branch would cost the
+// item path a spill; there every segment's epilogue has a launch of its own.)
 template <class M, int D, int C, bool SDEC, int PRO>
-__global__ __launch_bounds__(kIntraThreads, 4) void intra_chunk_kernel(KernelPtrs kp, SeqInfo si) {
+__global__ __launch_bounds__(kIntraThreads, 4) void intra_chunk_kernel(KernelPtrs kp, SeqInfo si, int items,
+                                                                       EpiJob ej) {
   extern __shared__ __attribute__((aligned(16))) char smem[];
-  intra_item_body<M, D, C, SDEC, PRO, false>(kp, si, blockIdx.x * kp.H + blockIdx.y, smem);
+  const int b = blockIdx.x;
+  if constexpr (PRO == 2) {
+    if (b >= items) {
+      const int e = 2 * (b - items) + (wave_id() >> 2);
+      if (e < ej.items) {
+        if (ej.out_bf16)
+          layer_epilogue_item<M, D, C, true>(kp, ej.si, e, wave_id() & 3);
+        else
+          layer_epilogue_item<M, D, C, false>(kp, ej.si, e, wave_id() & 3);
+      }
+      return;
+    }
+  }
+  intra_item_body<M, D, C, SDEC, PRO, false>(kp, si, b, smem);
 }
 
 // The tile pass: each workgroup looks at two items and works on the ones the
@@ -1789,69 +1890,9 @@ __device__ __forceinline__ void inter_o_role(const KernelPtrs& kp, const InterGe
   }
 }
 
-// ---------------------------------------------------------------------------
-// Layer epilogue (the "Kimi Linear" notes, docsaid.org, section "Other
-// Components"; greeksharifa.github.io summary, section 4): per token and
-// head, y = o / sqrt(mean_c o_c^2 + eps) * weight * sigmoid(gate).  The norm
-// spans all D value columns, which the inter-chunk pass splits over
-// workgroups, so it runs after that pass, per segment, on the raw o it left
-// in the workspace.  One workgroup of four waves per (slot, head), C / 4 rows
-// per wave.  D / 4 consecutive lanes hold one row, four columns each, so a
-// wave's 16-byte loads cover whole rows (two for d = 128); every row's loads
-// are issued before the first use, and the mean square is summed over the
-// row's lanes.
-// ---------------------------------------------------------------------------
 template <class M, int D, int C, bool OUT_BF16>
 __global__ __launch_bounds__(256) void layer_epilogue_kernel(KernelPtrs kp, SeqInfo si) {
-  typedef typename M::in_t in_t;
-  constexpr int LPR = D / 4;       // lanes per row
-  constexpr int RPI = 64 / LPR;    // rows per wave and pass
-  constexpr int NI = C / 4 / RPI;  // passes per wave
-  static_assert(NI >= 1 && C % (4 * RPI) == 0, "whole passes per wave");
-  const Item it = intra_item<C>(si, kp, blockIdx.x, 0);
-  if (it.len <= 0) return;
-  const int slot = blockIdx.x / kp.H;
-  const int l = lane_id();
-  const int c0 = 4 * (l % LPR);
-  const int rb = (C / 4) * wave_id() + l / LPR;
-  const in_t* gate = reinterpret_cast<const in_t*>(kp.gate);
-  const f32x4 wt = *reinterpret_cast<const f32x4*>(kp.norm_weight + c0);
-  f32x4 x[NI], gv[NI];
-#pragma unroll
-  for (int i = 0; i < NI; ++i) {
-    const int row = rb + RPI * i;
-    const int rr = row < it.len ? row : 0;  // rows past the chunk read row 0 and store nothing
-    x[i] = *reinterpret_cast<const f32x4*>(kp.o_slots + (((size_t)slot * kp.H + it.h) * C + rr) * D + c0);
-    const size_t ti = ((size_t)(it.t0 + rr) * kp.H + it.h) * D + c0;
-    if constexpr (sizeof(in_t) == 2) {
-      const bf16x4 g4 = *reinterpret_cast<const bf16x4*>(gate + ti);
-      gv[i] = f32x4{(float)g4[0], (float)g4[1], (float)g4[2], (float)g4[3]};
-    } else {
-      gv[i] = *reinterpret_cast<const f32x4*>(gate + ti);
-    }
-  }
-#pragma unroll
-  for (int i = 0; i < NI; ++i) {
-    const int row = rb + RPI * i;
-    float ss = x[i][0] * x[i][0] + x[i][1] * x[i][1] + x[i][2] * x[i][2] + x[i][3] * x[i][3];
-#pragma unroll
-    for (int off = LPR / 2; off > 0; off >>= 1) ss += __shfl_xor(ss, off);
-    const float inv = 1.f / sqrtf(ss / D + kp.norm_eps);
-    if (row < it.len) {
-      const size_t ti = ((size_t)(it.t0 + row) * kp.H + it.h) * D + c0;
-      f32x4 y;
-#pragma unroll
-      for (int e = 0; e < 4; ++e) y[e] = x[i][e] * inv * wt[e] * sigmoidf(gv[i][e]);
-      if constexpr (OUT_BF16) {
-        bf16x4 yb;
-#pragma unroll
-        for (int e = 0; e < 4; ++e) yb[e] = f2bf(y[e]);
-        *reinterpret_cast<bf16x4*>(reinterpret_cast<bf16*>(kp.o) + ti) = yb;
-      } else {
-        *reinterpret_cast<f32x4*>(reinterpret_cast<float*>(kp.o) + ti) = y;
-      }
-    }
-  }
+  layer_epilogue_item<M, D, C, OUT_BF16>(kp, si, blockIdx.x, wave_id());
 }
 
 // NCT = number of 16-column value tiles per workgroup (16 or 32 columns).
@@ -1927,10 +1968,8 @@ struct ConvStateArgs {
 };
 
 template <class T, int D>
-__global__ __launch_bounds__(D) void conv_state_kernel(ConvStateArgs ca, SeqInfo si) {
-  const int x = blockIdx.y;
-  if (!ca.out[x]) return;
-  const int n = blockIdx.x / ca.H, h = blockIdx.x % ca.H, c = threadIdx.x;
+__device__ __forceinline__ void conv_state_item(const ConvStateArgs& ca, const SeqInfo& si, int n, int h,
+                                                int x, int c) {
   int bos, eos;
   seq_bounds(si, n, bos, eos);
   const int W1 = ca.W - 1, len = eos - bos;
@@ -1947,6 +1986,31 @@ __global__ __launch_bounds__(D) void conv_state_kernel(ConvStateArgs ca, SeqInfo
       v = in ? in[sb + (size_t)(len + j) * D] : T(0.f);
     out[sb + (size_t)j * D] = v;
   }
+}
+
+template <class T, int D>
+__global__ __launch_bounds__(D) void conv_state_kernel(ConvStateArgs ca, SeqInfo si) {
+  const int x = blockIdx.y;
+  if (!ca.out[x]) return;
+  conv_state_item<T, D>(ca, si, blockIdx.x / ca.H, blockIdx.x % ca.H, x, threadIdx.x);
+}
+
+// The last segment's layer epilogue (items workgroups) and then the carried
+// convolution inputs (one workgroup per (sequence, head), the three tensors
+// over its threads) in one launch: it follows every pass that reads the old
+// carried inputs.
+template <class M, int D, int C, bool OUT_BF16>
+__global__ __launch_bounds__(256) void layer_epilogue_conv_kernel(KernelPtrs kp, SeqInfo si,
+                                                                  ConvStateArgs ca, int items) {
+  const int b = blockIdx.x;
+  if (b < items) {
+    layer_epilogue_item<M, D, C, OUT_BF16>(kp, si, b, wave_id());
+    return;
+  }
+  static_assert(256 % D == 0, "whole tensors per pass");
+  const int pair = b - items, c = threadIdx.x % D;
+  for (int x = threadIdx.x / D; x < 3; x += 256 / D)
+    if (ca.out[x]) conv_state_item<typename M::in_t, D>(ca, si, pair / ca.H, pair % ca.H, x, c);
 }
 
 // Value-column block width of the inter-chunk pass: wide blocks cut the
@@ -1989,7 +2053,11 @@ static hipError_t launch_prefill_t(const PrefillArgs& a) {
   si.num_seqs = a.num_seqs;
   si.seq_len = a.seq_len;
   si.total_tokens = a.total_tokens;
-  si.slot_off = reinterpret_cast<const int32_t*>(ws);
+  const size_t tbytes = table_bytes(a.num_seqs, a.cu_seqlens != nullptr);
+  const int ntab = table_copies(plan, epi);
+  const int32_t* tables[2] = {reinterpret_cast<const int32_t*>(ws),
+                              reinterpret_cast<const int32_t*>(ws + (ntab - 1) * tbytes)};
+  si.slot_off = tables[0];
   si.max_slots = plan.max_slots;
   si.L = plan.L;
   KernelPtrs kp;
@@ -2001,7 +2069,7 @@ static hipError_t launch_prefill_t(const PrefillArgs& a) {
   kp.o = a.o;
   kp.s0 = a.initial_state;
   kp.s1 = a.final_state;
-  char* after_table = ws + table_bytes(a.num_seqs, a.cu_seqlens != nullptr);
+  char* after_table = ws + ntab * tbytes;
   const size_t carry = carry_bytes(plan, a.num_seqs, a.H, D);
   kp.carry = carry ? reinterpret_cast<float*>(after_table) : nullptr;
   kp.ops = after_table + carry;
@@ -2038,8 +2106,20 @@ static hipError_t launch_prefill_t(const PrefillArgs& a) {
     }
   }
   const int nct = choose_nct(a.num_seqs * a.H, D, a.tuning);
+  auto launch_epilogue = [&](const SeqInfo& sq, int items) {
+    if (a.out_bf16)
+      hipLaunchKernelGGL((layer_epilogue_kernel<M, D, C, true>), dim3(items), dim3(256), 0, a.stream, kp, sq);
+    else
+      hipLaunchKernelGGL((layer_epilogue_kernel<M, D, C, false>), dim3(items), dim3(256), 0, a.stream, kp,
+                         sq);
+  };
+  EpiJob ej;  // the epilogue still to run: the previous segment's
+  ej.si = si;
+  ej.items = 0;
+  ej.out_bf16 = a.out_bf16 ? 1 : 0;
   for (int s = 0; s < plan.nseg; ++s) {
     si.c0 = s * plan.L;
+    si.slot_off = tables[s & 1];
     const long long slots = sc.slots(si.c0, plan.L);
     if (a.cu_seqlens) {
       hipLaunchKernelGGL(segment_table_kernel, dim3(1), dim3(1024), 0, a.stream, a.cu_seqlens,
@@ -2050,46 +2130,60 @@ static hipError_t launch_prefill_t(const PrefillArgs& a) {
       const int c = sc.nch(0) - si.c0;
       si.slot_cnt = c <= 0 ? 0 : (c < plan.L ? c : plan.L);
     }
-    // the chunk-wide intra pass, then the tile pass for the blocks it left
-    const dim3 igrid((unsigned)slots, a.H);
+    // the chunk-wide intra pass (with the previous segment's epilogue), then
+    // the tile pass for the blocks it left
     if (slots > 0) {
-      void* args[] = {&kp, &si};
+      int items = (int)(slots * a.H);
+      const dim3 igrid((unsigned)(items + (ej.items + 1) / 2));
+      void* args[] = {&kp, &si, &items, &ej};
       hipError_t e = hipLaunchKernel(intra_fn[0], igrid, dim3(kIntraThreads), args, lds, a.stream);
       if (e != hipSuccess) return e;
-      int items = (int)(slots * a.H);
+      ej.items = 0;
       void* targs[] = {&kp, &si, &items};
       e = hipLaunchKernel(intra_fn[1], dim3((unsigned)((items + 1) / 2)), dim3(kIntraThreads), targs, lds,
                           a.stream);
       if (e != hipSuccess) return e;
     }
+    // with no intra launch to carry it, the previous epilogue before the
+    // carry pass overwrites the raw o
+    if (ej.items > 0) launch_epilogue(ej.si, ej.items);
     if (nct == 2)
       launch_inter<M, D, C, 2>(a, kp, si);
     else
       launch_inter<M, D, C, 1>(a, kp, si);
-    if (epi && slots > 0) {
-      const dim3 grid((unsigned)(slots * a.H));
-      if (a.out_bf16)
-        hipLaunchKernelGGL((layer_epilogue_kernel<M, D, C, true>), grid, dim3(256), 0, a.stream, kp, si);
-      else
-        hipLaunchKernelGGL((layer_epilogue_kernel<M, D, C, false>), grid, dim3(256), 0, a.stream, kp,
-                           si);
+    if (epi && pro == 2) {  // carried by the next chunk-wide launch
+      ej.si = si;
+      ej.items = (int)(slots * a.H);
+    } else if (epi && slots > 0) {
+      launch_epilogue(si, (int)(slots * a.H));
     }
   }
   // The carried convolution inputs, after every pass that reads the old ones
-  // (they may share memory).
+  // (they may share memory); with the epilogue, in its last launch.
   const bool conv_out = a.layer.conv_state_out[0] || a.layer.conv_state_out[1] ||
                         a.layer.conv_state_out[2];
-  if (pro == 2 && a.layer.conv_w > 1 && conv_out && a.num_seqs > 0) {
-    ConvStateArgs ca;
-    ca.W = a.layer.conv_w;
-    ca.H = a.H;
-    for (int x = 0; x < 3; ++x) {
-      ca.x[x] = x == 0 ? a.q : x == 1 ? a.k : a.v;
-      ca.in[x] = a.layer.conv_state_in[x];
-      ca.out[x] = a.layer.conv_state_out[x];
-    }
-    hipLaunchKernelGGL((conv_state_kernel<typename M::in_t, D>), dim3(a.num_seqs * a.H, 3), dim3(D),
-                       0, a.stream, ca, si);
+  const bool conv_state = pro == 2 && a.layer.conv_w > 1 && conv_out && a.num_seqs > 0;
+  ConvStateArgs ca;
+  ca.W = a.layer.conv_w;
+  ca.H = a.H;
+  for (int x = 0; x < 3; ++x) {
+    ca.x[x] = x == 0 ? a.q : x == 1 ? a.k : a.v;
+    ca.in[x] = a.layer.conv_state_in[x];
+    ca.out[x] = a.layer.conv_state_out[x];
+  }
+  if (ej.items > 0 && conv_state) {  // the last segment's epilogue and the carried inputs
+    const dim3 grid((unsigned)(ej.items + a.num_seqs * a.H));
+    if (a.out_bf16)
+      hipLaunchKernelGGL((layer_epilogue_conv_kernel<M, D, C, true>), grid, dim3(256), 0, a.stream, kp, ej.si,
+                         ca, ej.items);
+    else
+      hipLaunchKernelGGL((layer_epilogue_conv_kernel<M, D, C, false>), grid, dim3(256), 0, a.stream, kp,
+                         ej.si, ca, ej.items);
+  } else {
+    if (ej.items > 0) launch_epilogue(ej.si, ej.items);  // the last segment's
+    if (conv_state)
+      hipLaunchKernelGGL((conv_state_kernel<typename M::in_t, D>), dim3(a.num_seqs * a.H, 3), dim3(D), 0,
+                         a.stream, ca, si);
   }
   return hipGetLastError();
 }

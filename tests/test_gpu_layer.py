@@ -196,6 +196,47 @@ def test_layer_prefill_full_size(kda):
         np.testing.assert_array_equal(host(a), e.astype(np.float32))
 
 
+@pytest.mark.parametrize("seg,out", [(1, "f32"), (2, "f32"), (2, "bf16"), (3, "bf16")])
+def test_layer_prefill_segment_epilogues(kda, seg, out):
+    """Fixed-length input (two sequences) in segments of 1-3 chunks with the
+    convolution and the gated epilogue, whose raw output buffer every segment
+    reuses.  Three calls in a row on a stream of the caller's own must give
+    the same output each time, and every output and the final state match
+    the oracle (bf16 output to its 8e-3 gate)."""
+    say(f"layer prefill segment epilogues seg={seg} out={out}")
+    rng = np.random.default_rng([42, seg])
+    B, T, H, D, W = 2, 300, 3, 128, 4
+    N = B
+    cu = np.arange(B + 1, dtype=np.int32) * T
+    x = I.draw_layer_tokens(rng, B * T, H, D, D, "bf16")
+    s0 = I.draw_states(rng, N, H, D, D)
+    ws, ss = I.draw_conv(rng, N, H, D, W, "bf16")
+    eo, ef, _ = oracle.kda_layer_conv(x.q_pre, x.k_pre, x.v_pre, x.g, x.beta_logit, ws, ss,
+                                      x.gate, x.norm_weight, EPS, s0, cu)
+    q, k, v, g, b, gt = layer_to_dev(x, lead=(B, T))
+    wd, sd = conv_to_dev(ws, ss, torch.bfloat16)
+    odt = torch.bfloat16 if out == "bf16" else torch.float32
+    side = torch.cuda.Stream(DEV)
+    side.wait_stream(torch.cuda.current_stream(DEV))
+    outs = []
+    with torch.cuda.stream(side):
+        for _ in range(3):
+            o, fin, _ = kda.layer_prefill(q, k, v, g, b, gt, tdev(x.norm_weight, torch.float32), EPS,
+                                          torch.from_numpy(s0).to(DEV), conv_weight=wd,
+                                          conv_state=sd, chunk_size=64, out_dtype=odt,
+                                          options={"segment_chunks": seg})
+            outs.append((o.float().cpu().numpy(), fin.cpu().numpy()))
+    side.synchronize()
+    o0, f0 = outs[0]
+    for o1, f1 in outs[1:]:
+        np.testing.assert_array_equal(o1, o0)
+        np.testing.assert_array_equal(f1, f0)
+    eo_ = rel(o0.reshape(eo.shape), eo)
+    es_ = rel(f0, ef)
+    say(f"  o err {eo_:.2e}  state err {es_:.2e}")
+    assert eo_ <= (8e-3 if out == "bf16" else TOL["bf16"]) and es_ <= TOL["bf16"]
+
+
 @pytest.mark.parametrize("dtype,D,C", [(dt, D, C) for dt in ("bf16", "f32") for D in (64, 128)
                                        for C in (16, 32, 64)])
 def test_layer_prefill_value_block_32(kda, dtype, D, C):
