@@ -1360,6 +1360,10 @@ hipError_t launch_backward_t(const BackwardArgs& a) {
                           hipFuncAttributeMaxDynamicSharedMemorySize, (int)tlds);
   if (e != hipSuccess) return e;
 
+  // With bf16 inputs the batched products run on split-bf16 operands (about
+  // 16 significant bits, as the forward pass's products); fp32 inputs keep
+  // fp32 products for their tighter bound.
+  constexpr bool kSplitGemm = sizeof(in_t) == 2;
   BwdIn in{a.q, a.k, a.v, a.g, a.beta, a.d_o};
   BwdOut out{a.dq, a.dk, a.dv, a.dg, a.dbeta};
   hipError_t gerr = hipSuccess;
@@ -1367,7 +1371,7 @@ hipError_t launch_backward_t(const BackwardArgs& a) {
   auto gemm = [&](auto op, const float* A, const float* B, float* Cm, int M, int N, int K,
                   int lda, int ldb, size_t sa, size_t sb, float alpha, int acc_c, int mask) {
     typedef decltype(op) O;
-    const hipError_t e = launch_fp32_gemm<O::TA, O::TB>(A, B, Cm, M, N, K, lda, ldb, N, sa, sb,
+    const hipError_t e = launch_fp32_gemm<O::TA, O::TB, kGemmOne, kSplitGemm>(A, B, Cm, M, N, K, lda, ldb, N, sa, sb,
                                                          (size_t)M * N, alpha, acc_c, mask, NB,
                                                          a.stream);
     if (gerr == hipSuccess) gerr = e;
@@ -1377,7 +1381,7 @@ hipError_t launch_backward_t(const BackwardArgs& a) {
   auto gemm2 = [&](auto op, auto mode, const float* A, const float* B, float* Cm, int M, int N, int K,
                    int lda, int ldb, size_t sa, size_t sb, float alpha, int mask, GemmX x2) {
     typedef decltype(op) O;
-    const hipError_t e = launch_fp32_gemm<O::TA, O::TB, decltype(mode)::value>(
+    const hipError_t e = launch_fp32_gemm<O::TA, O::TB, decltype(mode)::value, kSplitGemm>(
         A, B, Cm, M, N, K, lda, ldb, N, sa, sb, (size_t)M * N, alpha, 0, mask, NB, a.stream, x2);
     if (gerr == hipSuccess) gerr = e;
   };

@@ -516,6 +516,8 @@ hipError_t launch_dplr_t(const DplrArgs& a) {
   e = hipFuncSetAttribute(reinterpret_cast<const void*>(&dplr_gram_tile_kernel<D, C, TIED>),
                           hipFuncAttributeMaxDynamicSharedMemorySize, (int)sizeof(DTileLds<D, C>));
   if (e != hipSuccess) return e;
+  // bf16 inputs: batched products on split-bf16 operands; fp32 inputs: fp32.
+  constexpr bool kSplitGemm = sizeof(in_t) == 2;
   if (NB > 0) {
     DIn in{a.q, a.k, a.v, a.a, a.b, a.g, a.beta};
     hipLaunchKernelGGL((dplr_prep_kernel<in_t, D, C, TIED>), dim3(NB), dim3(256), 0, a.stream, in,
@@ -524,9 +526,8 @@ hipError_t launch_dplr_t(const DplrArgs& a) {
     auto gemm = [&](auto op, const float* A, const float* B, float* Cm, int M, int N, int K,
                     int lda, int ldb, size_t sa, size_t sb, float alpha, int mask) {
       typedef decltype(op) O;
-      const hipError_t e = launch_fp32_gemm<O::TA, O::TB>(A, B, Cm, M, N, K, lda, ldb, N, sa, sb,
-                                                           (size_t)M * N, alpha, 0, mask, NB,
-                                                           a.stream);
+      const hipError_t e = launch_fp32_gemm<O::TA, O::TB, kGemmOne, kSplitGemm>(
+          A, B, Cm, M, N, K, lda, ldb, N, sa, sb, (size_t)M * N, alpha, 0, mask, NB, a.stream);
       if (gerr == hipSuccess) gerr = e;
     };
     // Two products sharing B (and its load) in one launch.
@@ -537,9 +538,8 @@ hipError_t launch_dplr_t(const DplrArgs& a) {
       x2.A2 = A2;
       x2.C2 = C2;
       x2.mask2 = mask2;
-      const hipError_t e = launch_fp32_gemm<O::TA, O::TB, kGemmDual>(A, B, Cm, M, N, K, lda, ldb, N, sa, sb,
-                                                                     (size_t)M * N, 1.f, 0, mask, NB,
-                                                                     a.stream, x2);
+      const hipError_t e = launch_fp32_gemm<O::TA, O::TB, kGemmDual, kSplitGemm>(
+          A, B, Cm, M, N, K, lda, ldb, N, sa, sb, (size_t)M * N, 1.f, 0, mask, NB, a.stream, x2);
       if (gerr == hipSuccess) gerr = e;
     };
     const size_t scd = (size_t)C * D, scc = (size_t)C * C;

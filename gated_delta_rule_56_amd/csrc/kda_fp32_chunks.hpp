@@ -159,7 +159,7 @@ struct GemmX {
   int mask2 = 0;
 };
 
-template <bool TA, bool TB, int X>
+template <bool TA, bool TB, int X, bool SPLIT>
 __global__ __launch_bounds__(256) void fp32_gemm_kernel(const float* __restrict__ A,
                                                        const float* __restrict__ B,
                                                        float* __restrict__ Cm, int M, int N, int K,
@@ -299,11 +299,44 @@ __global__ __launch_bounds__(256) void fp32_gemm_kernel(const float* __restrict_
         }
       }
     };
-    if (ks == kGemmKStage) {
+    // SPLIT: each 32 k on v_mfma_f32_16x16x32_bf16 with split-bf16 operands
+    // (x = hi + lo, products hi hi + hi lo + lo hi, fp32 accumulation),
+    // formed from the same fp32 LDS tiles: lane group g takes the k of its
+    // 16-byte reads in two consecutive 16-blocks as its eight k, for A and B
+    // alike, so the 32 k of the pair are each summed once.
+    auto split8 = [&](const float* row, int ko, ModeBF16::PFrag& f) {
+      const f32x4 p = *reinterpret_cast<const f32x4*>(row + ko);
+      const f32x4 q = *reinterpret_cast<const f32x4*>(row + ko + 16);
+      const float v[8] = {p[0], p[1], p[2], p[3], q[0], q[1], q[2], q[3]};
+      f = make_pfrag(ModeBF16{}, v);
+    };
+    auto kpair = [&](int kb) {  // k = 16 kb .. 16 kb + 31 of the stage
+      const int ko = 16 * kb + 4 * lg;
+      ModeBF16::PFrag b0, b1, a;
+      split8(Bs + (wn + lm) * LD, ko, b0);
+      split8(Bs + (wn + 16 + lm) * LD, ko, b1);
+      // one A row tile at a time: three fragments live, not six
 #pragma unroll
-      for (int kb = 0; kb < kGemmKStage / 16; ++kb) kblock(kb);
+      for (int t = 0; t < (DUAL ? 4 : 2); ++t) {
+        split8(As + ((t >> 1) * 64 + wm + 16 * (t & 1) + lm) * LD, ko, a);
+        f32x4* ac = t < 2 ? acc[t & 1] : acc2[DUAL ? (t & 1) : 0];
+        ac[0] = mma_pp(a, b0, ac[0]);
+        ac[1] = mma_pp(a, b1, ac[1]);
+      }
+    };
+    if (ks == kGemmKStage) {
+      if constexpr (SPLIT) {
+#pragma unroll
+        for (int kb = 0; kb < kGemmKStage / 16; kb += 2) kpair(kb);
+      } else {
+#pragma unroll
+        for (int kb = 0; kb < kGemmKStage / 16; ++kb) kblock(kb);
+      }
     } else {
-      for (int kb = 0; kb < ks / 16; ++kb) kblock(kb);
+      int kb = 0;
+      if constexpr (SPLIT)
+        for (; kb + 1 < ks / 16; kb += 2) kpair(kb);
+      for (; kb < ks / 16; ++kb) kblock(kb);
     }
   }
   auto put = [&](float* cm, const f32x4 (&ac)[2][2], float al, int mk) {
@@ -333,7 +366,7 @@ struct GemmTN { static constexpr bool TA = true, TB = false; };
 
 // Launch of fp32_gemm_kernel over NB batch items (x2: the second product of
 // kGemmDual or kGemmCat).
-template <bool TA, bool TB, int X = kGemmOne>
+template <bool TA, bool TB, int X = kGemmOne, bool SPLIT = false>
 inline hipError_t launch_fp32_gemm(const float* A, const float* B, float* Cm, int M, int N, int K,
                                    int lda, int ldb, int ldc, size_t sa, size_t sb, size_t sc,
                                    float alpha, int acc_c, int mask, size_t NB, hipStream_t stream,
@@ -344,7 +377,7 @@ inline hipError_t launch_fp32_gemm(const float* A, const float* B, float* Cm, in
   const size_t blocks = (NB + 7) / 8 * 8 * (size_t)((N + 63) / 64) * ((M + 63) / 64);
   if (blocks == 0) return hipSuccess;
   if (blocks > 0x7fffffff) return hipErrorInvalidValue;
-  hipLaunchKernelGGL((fp32_gemm_kernel<TA, TB, X>), dim3((unsigned)blocks), dim3(256), 0, stream, A, B, Cm, M,
+  hipLaunchKernelGGL((fp32_gemm_kernel<TA, TB, X, SPLIT>), dim3((unsigned)blocks), dim3(256), 0, stream, A, B, Cm, M,
                      N, K, lda, ldb, ldc, sa, sb, sc, alpha, acc_c, mask, NB, x2);
   return hipGetLastError();
 }
