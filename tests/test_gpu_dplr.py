@@ -61,9 +61,11 @@ def run_dplr(kda, x, dtype, C, s0=None, cu=None):
     return host(o)[0], host(fin)
 
 
+# bf16 at C = 16 and 32: the batched products contracted over C run one
+# split-bf16 32-k pair (C = 32) or the fp32 16-k block alone (C = 16).
 @pytest.mark.parametrize("dtype,D,C,T,gs", [
     ("bf16", 128, 64, 300, 0.1), ("f32", 64, 16, 131, 0.1), ("f32", 128, 32, 77, 0.1),
-    ("f32", 128, 64, 150, 5.0)])
+    ("f32", 128, 64, 150, 5.0), ("bf16", 64, 32, 131, 0.1), ("bf16", 128, 16, 77, 0.1)])
 def test_dplr_matches_oracle(kda, dtype, D, C, T, gs):
     say(f"dplr dtype={dtype} D={D} C={C} T={T} g_scale={gs}")
     rng = np.random.default_rng([60, D, C, T])
@@ -94,7 +96,8 @@ def test_dplr_varlen(kda):
 
 
 @pytest.mark.parametrize("dtype,D,C,T,gs", [
-    ("bf16", 128, 64, 300, 0.1), ("f32", 64, 32, 131, 0.1), ("f32", 128, 64, 150, 5.0)])
+    ("bf16", 128, 64, 300, 0.1), ("f32", 64, 32, 131, 0.1), ("f32", 128, 64, 150, 5.0),
+    ("bf16", 64, 32, 131, 0.1)])
 def test_kda_chunk_fp32_matches_oracle(kda, dtype, D, C, T, gs):
     say(f"kda chunk fp32 dtype={dtype} D={D} C={C} T={T} g_scale={gs}")
     rng = np.random.default_rng([62, D, C, T])
