@@ -162,6 +162,25 @@ def test_layer_workspace_size(lib):
     assert gated == plain + 32 * 32 * 64 * 128 * 4
 
 
+def test_layer_workspace_size_varlen_segments(lib):
+    # Packed sequences in one-chunk segments with the gated epilogue: each
+    # segment's epilogue runs in the next segment's intra launch, after that
+    # segment's slot table is made, so the slot table has two copies (256 B
+    # each here) besides one segment's raw output (4 slots: the sequences
+    # with a chunk, x 2 heads x 64 x 128 x 4 B).  Without the gate, or in one
+    # segment, there is one copy.
+    cu = np.array([0, 37, 37, 167, 172, 372], dtype=np.int32)
+    one = {"segment_chunks": 1}
+    plain = kda.workspace_size(1, 372, 2, 128, 5, 64, kda.KDA_BF16, cu, options=one)
+    gated = kda.workspace_size(1, 372, 2, 128, 5, 64, kda.KDA_BF16, cu, layer_gate=True, options=one)
+    assert gated == plain + 256 + 4 * 2 * 64 * 128 * 4
+    whole = {"segment_chunks": 4}
+    plain1 = kda.workspace_size(1, 372, 2, 128, 5, 64, kda.KDA_BF16, cu, options=whole)
+    gated1 = kda.workspace_size(1, 372, 2, 128, 5, 64, kda.KDA_BF16, cu, layer_gate=True, options=whole)
+    # one segment of up to 4 chunks per sequence: 1 + 3 + 1 + 4 slots
+    assert gated1 == plain1 + 9 * 2 * 64 * 128 * 4
+
+
 def _params(gate=FAKE, w=FAKE, eps=1e-6, cw=0, cwt=(FAKE, FAKE, FAKE), csin=(None,) * 3,
             csout=(None,) * 3):
     lp = kda.LayerParams()
